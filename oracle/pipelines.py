@@ -1,0 +1,92 @@
+"""The five workloads run end to end on the oracle (test infrastructure only).
+
+Each driver calls the oracle steps in the order the method takes them:
+
+* SnapKV one-shot eviction (SparseEngine page, "How it works": selection and eviction after the last prompt
+  chunk): causal window scores -> top-K + protected tail -> whole-cache compaction -> one decode step over the
+  retained KV (no append: the decode query attends over the cache as it stands).
+* Kara periodic compression (KARA page, "Method" parts 1-3): at an event, bidirectional window scores -> top-K
+  candidates -> Token2Chunk -> trailing-window compaction; between events, decode steps that append their token
+  first and then attend.
+* Quest (SparseEngine page, "How it works": ``build_decode_selection``): page metadata -> page bounds -> top
+  pages plus the first and last -> decode over the selected pages.
+* H2O (SparseEngine page, "What it is"): per step append -> decode with cumulative-score accumulation ->
+  when over budget, evict the lowest score outside the recent positions.
+"""
+import numpy as np
+
+from .cache_ops import cache_append, compact_gather, evict_slots
+from .decode import decode_attn
+from .pages import page_bounds_build, page_bounds_score
+from .score import window_score_bidir, window_score_causal
+from .select import token2chunk, topk_largest, topk_smallest
+
+
+def snapkv_event(inp):
+    cfg, cache = inp["cfg"], inp["cache"]
+    scores = window_score_causal(cache, inp["q_win"], inp["q_pos"], inp["scale"])
+    keep = topk_largest(scores, cache, cfg.keep, protect=cfg.protect)
+    compacted = compact_gather(cache, keep)
+    out, _ = decode_attn(compacted, inp["q_dec"], inp["scale"])
+    return dict(scores=scores, keep=keep, cache=compacted, out=out)
+
+
+def kara_window_queries(inp, cache):
+    """The queries of each window slot's token, [B][hq][window][d], looked up by position (harness plumbing:
+    the workload keeps the query of every token since the first window)."""
+    cfg = inp["cfg"]
+    B, hq = cfg.B, cfg.hq
+    r = hq // cfg.hkv
+    q = np.zeros((B, hq, cfg.window, cfg.d), inp["q_all"].dtype)
+    for b in range(B):
+        for g in range(cfg.hkv):
+            n = int(cache.n_slots[b, g])
+            pos = cache.pos_map[b, g, n - cfg.window:n] - inp["q_first_pos"]
+            if np.any(pos < 0):
+                raise ValueError("window holds a token without a stored query")
+            q[b, g * r:(g + 1) * r] = inp["q_all"][b, g * r:(g + 1) * r][:, pos]
+    return q
+
+
+def kara_event(inp, cache):
+    cfg = inp["cfg"]
+    q_win = kara_window_queries(inp, cache)
+    scores = window_score_bidir(cache, q_win, inp["scale"], cfg.window, cfg.protect)
+    cand = topk_largest(scores, cache, cfg.n_cand, window=cfg.window, protect=cfg.protect)
+    scores32 = scores.astype(np.float32)
+    keep = token2chunk(cand, scores32, cache, max_gap=cfg.max_gap, budget=cfg.budget, window=cfg.window,
+                       protect=cfg.protect)
+    compacted = compact_gather(cache, keep, window=cfg.window)
+    return dict(q_win=q_win, scores=scores, cand=cand, keep=keep, cache=compacted)
+
+
+def kara_decode_step(inp, cache, step: int):
+    cfg = inp["cfg"]
+    pos = np.full((cfg.B,), cfg.N + step, np.int32)
+    cache, _ = cache_append(cache, inp["k_new"][step], inp["v_new"][step], pos)
+    q = np.ascontiguousarray(inp["q_all"][:, :, cfg.N + step - inp["q_first_pos"]])
+    out, _ = decode_attn(cache, q, inp["scale"])
+    return cache, out
+
+
+def quest_step(inp, cache=None):
+    cfg = inp["cfg"]
+    cache = inp["cache"] if cache is None else cache
+    meta = page_bounds_build(cache)
+    with_meta = cache.copy()
+    with_meta.page_meta = meta
+    pscores = page_bounds_score(with_meta, meta, inp["q_dec"])
+    pages = topk_largest(pscores, with_meta, cfg.top_pages, unit="page", forced_ends=True)
+    out, _ = decode_attn(with_meta, inp["q_dec"], inp["scale"], pages=pages)
+    return dict(meta=meta, page_scores=pscores, pages=pages, out=out, cache=with_meta)
+
+
+def h2o_step(inp, cache, step: int):
+    cfg = inp["cfg"]
+    pos = np.full((cfg.B,), cfg.N + step, np.int32)
+    cache, slots = cache_append(cache, inp["k_new"][step], inp["v_new"][step], pos)
+    out, cum = decode_attn(cache, inp["q_steps"][step], inp["scale"], accumulate=True)
+    cache.cum_score = cum
+    evict = topk_smallest(cum, cache, 1, budget=cfg.budget, recent=cfg.recent)
+    cache = evict_slots(cache, evict)
+    return cache, dict(out=out, evict=evict, slots=slots, cum=cum)
