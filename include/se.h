@@ -1,0 +1,228 @@
+/*
+ * se.h — sparse KV selection, eviction and sparse decode attention on MI355X (gfx950).
+ *
+ * C ABI of libse.so. The calls follow the lifecycle contract of the SparseEngine page
+ * (onedev.kr/papers/824, section "How it works"): a persistent cache state C owned by a cache manager
+ * (KV layout, position mapping, allocate / write / update / free, metadata kept beside the KV), a set of
+ * selected token or page ids I, a view View = BuildView(C, I) and o = Attention(q, View). Here C is an
+ * se_cache_t, I is an (idx, count) pair, BuildView is implicit in passing both to se_sparse_decode_attn.
+ *
+ * Conventions shared by every call
+ *  - Every pointer in a descriptor or argument is a DEVICE pointer unless stated otherwise; descriptor and
+ *    parameter structs themselves are host memory and are read before the call returns. The caller owns all
+ *    memory: pools, maps, scores, index lists, outputs and workspaces. The library allocates nothing and keeps
+ *    no per-cache state.
+ *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the default stream) and mutates its outputs
+ *    in stream order. Calls on different streams must not touch the same buffers concurrently.
+ *  - Return value: SE_OK, or a host-detected error (SE_ERR_*) in which case nothing was launched.
+ *  - Errors only the device can see (bad indices, exhausted free lists) are OR-ed into the caller's sticky
+ *    device word `status` (may be NULL to ignore them) as SE_DEV_* bits; read it with se_status_read.
+ *  - `ws`/`ws_bytes`: caller-provided device workspace of at least the size the matching *_workspace_size
+ *    function reports (NULL/0 when it reports 0). Its contents need not be initialised and are clobbered.
+ *
+ * Paged cache layout (se_cache_t): K and V live in pools of physical blocks; block p holds, for every KV
+ * head g, `page` consecutive slots of `d` elements: k_pool[p][g][i][e]. A sequence b maps logical block L to
+ * physical block block_table[b][L] (-1 = none; allocated entries form a prefix). Slot s of (b, g) is row
+ * s % page of block block_table[b][s / page]. pos_map[b][g][s] is the original token position held in slot s
+ * (-1 = free). Slots at or beyond n_slots[b][g] are unused (their pos_map entries are unspecified). Inside
+ * [0, n_slots) the free slots are exactly the entries of the (b, g) slot stack, and ctx_len counts the
+ * resident ones. All calls keep these invariants.
+ */
+#ifndef SE_H
+#define SE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------------------------------------------ */
+enum {
+  SE_OK = 0,
+  SE_ERR_NULL = 1,        /* a required pointer is NULL */
+  SE_ERR_SHAPE = 2,       /* sizes that do not fit together (strides, dims, group size) */
+  SE_ERR_DTYPE = 3,       /* unsupported element type or head dimension */
+  SE_ERR_PARAM = 4,       /* a parameter outside its domain */
+  SE_ERR_WORKSPACE = 5,   /* workspace missing or too small */
+  SE_ERR_UNSUPPORTED = 6, /* a combination this build does not implement */
+  SE_ERR_HIP = 7,         /* a HIP runtime call failed */
+  /* device status bits, OR-ed into *status */
+  SE_DEV_INDEX = 1 << 8,    /* an index list entry out of range, unsorted, duplicated or not resident */
+  SE_DEV_CAPACITY = 1 << 9  /* free block stack, slot stack or slot range exhausted */
+};
+
+enum { SE_DTYPE_F32 = 0, SE_DTYPE_BF16 = 1 };
+
+typedef void *se_stream_t; /* a hipStream_t */
+
+/* ---- the persistent cache state C ------------------------------------------------------------------------ */
+typedef struct se_cache {
+  void *k_pool, *v_pool;  /* [num_blocks][n_kv][page][d] of dtype */
+  int32_t *block_table;   /* [B][max_blocks] physical block id, -1 = none */
+  int32_t *pos_map;       /* [B][n_kv][max_blocks * page] original position, -1 = free slot */
+  int32_t *ctx_len;       /* [B][n_kv] resident tokens */
+  int32_t *n_slots;       /* [B][n_kv] high-water slot count */
+  int32_t *free_blocks;   /* [num_blocks] LIFO stack of free physical blocks */
+  int32_t *free_top;      /* [1] number of entries on free_blocks */
+  int32_t *slot_stack;    /* [B][n_kv][slot_cap] LIFO of free slots below n_slots (may be NULL if slot_cap = 0) */
+  int32_t *slot_top;      /* [B][n_kv] entries on each slot stack (may be NULL if slot_cap = 0) */
+  void *page_meta;        /* optional [B][n_kv][max_blocks][2][d] of dtype: per-page key min ([..][0][..]) and
+                             max ([..][1][..]) (Quest metadata) */
+  float *cum_score;       /* optional [B][n_kv][max_blocks * page] per-slot cumulative attention (H2O metadata) */
+  int32_t B, n_kv, n_q, d, page, num_blocks, max_blocks, slot_cap, dtype;
+} se_cache_t;
+
+/* ---- window scores ------------------------------------------------------------------------------------------
+ * SnapKV observation-window scoring (SparseEngine page, "How it works": selection after the last prompt
+ * chunk) and Kara's bidirectional window scoring (KARA page, gist.science/ko/paper/2607.01237, "Method"
+ * part 1). For every KV head g of sequence b and every query head h of its group (h / (n_q / n_kv) == g):
+ *   CAUSAL: q_win [B][n_q][n_query][d] are the queries of the window tokens, q_pos [B][n_query] their
+ *     positions. Each query row is a softmax over the resident slots s < n_slots with pos_map[s] <= q_pos.
+ *     scores[(b*n_kv+g)*score_stride + s] = sum over h, t of that row's weight on s, for s < n_slots
+ *     (0 where no query sees the slot).
+ *   BIDIR: the window is the last `window` slots [w0, n_slots), w0 = n_slots - window, and the region its first
+ *     window - protect slots. q_win [B][n_q][window][d] holds the queries of the window's tokens; q_pos is
+ *     unused. Each query row is a softmax over the resident region slots (no mask);
+ *     scores[(b*n_kv+g)*score_stride + (s - w0)] for s in the region.
+ * Arithmetic: products of stored values exact, fp32 accumulation, fp32 output.
+ */
+enum { SE_SCORE_CAUSAL = 0, SE_SCORE_BIDIR = 1 };
+typedef struct {
+  float scale;          /* logit scale, usually 1/sqrt(d) */
+  int32_t mode;         /* SE_SCORE_CAUSAL or SE_SCORE_BIDIR */
+  int32_t n_query;      /* queries per (sequence, head) in q_win; BIDIR requires n_query == window */
+  int32_t window;       /* BIDIR only */
+  int32_t protect;      /* BIDIR only: trailing window slots outside the key region */
+  int32_t score_stride; /* floats between consecutive (b, g) rows of scores */
+} se_window_params_t;
+
+size_t se_window_score_workspace_size(const se_cache_t *c, const se_window_params_t *p);
+int32_t se_window_score(const se_cache_t *c, const void *q_win, const int32_t *q_pos, const se_window_params_t *p,
+                        float *scores, int32_t *status, void *ws, size_t ws_bytes, se_stream_t stream);
+
+/* ---- top-K retention / bottom eviction ---------------------------------------------------------------------
+ * KARA page "Method" part 1 (top-K discrete pairs become candidates), SparseEngine page "How it works"
+ * (SnapKV selection; Quest build_decode_selection) and "What it is" (H2O eviction by continuous scores).
+ * Output per (b, g): idx[(b*n_kv+g)*out_stride + i], i < count[b*n_kv+g], ascending item ids.
+ *  LARGEST / SLOT: items are slots. Candidates are the resident slots of [base, n_slots - protect), with base = 0
+ *    (scores indexed by slot) or, if window > 0, base = n_slots - window (scores indexed by slot - base). The
+ *    min(k, #candidates) best by (score desc, position asc) are returned together with the resident slots of
+ *    the protected tail [n_slots - protect, n_slots).
+ *  LARGEST / PAGE: items are logical pages [0, ceil(n_slots/page)), scores indexed by page. With forced_ends
+ *    the first and last page are always returned and are not candidates. Order (score desc, page asc).
+ *  SMALLEST / SLOT: if ctx_len > budget, returns min(k, ctx_len - budget) slots with the lowest score among the
+ *    resident slots whose position is <= (max resident position - recent); order (score asc, position desc).
+ *    Otherwise count = 0.
+ * Scores must not be NaN.
+ */
+enum { SE_TOPK_LARGEST = 0, SE_TOPK_SMALLEST = 1 };
+enum { SE_UNIT_SLOT = 0, SE_UNIT_PAGE = 1 };
+typedef struct {
+  int32_t mode, unit, k;
+  int32_t window, protect; /* LARGEST / SLOT */
+  int32_t forced_ends;     /* LARGEST / PAGE */
+  int32_t budget, recent;  /* SMALLEST */
+  int32_t score_stride, out_stride;
+} se_topk_params_t;
+
+size_t se_topk_select_workspace_size(const se_cache_t *c, const se_topk_params_t *p);
+int32_t se_topk_select(const se_cache_t *c, const float *scores, const se_topk_params_t *p, int32_t *idx,
+                       int32_t *count, int32_t *status, void *ws, size_t ws_bytes, se_stream_t stream);
+
+/* ---- Token2Chunk -------------------------------------------------------------------------------------------
+ * KARA page, "Method" part 2. Input per (b, g): an ascending slot list (as returned by se_topk_select with a
+ * window): entries below n_slots - protect are the candidates c_1 < ... < c_m, the rest the protected tail.
+ * For consecutive candidates a < b with 1 <= b - a - 1 <= max_gap the gap's priority is the IEEE fp32 quotient
+ * (s_a + s_b) / (b - a), s read from scores[(b*n_kv+g)*score_stride + (slot - (n_slots - window))]. Gaps are
+ * taken by priority (ties: lower a); a gap is filled whole if the count of candidates plus filled slots stays
+ * <= budget, otherwise skipped; filling stops at the budget. Output: ascending candidates and fills, then the
+ * tail.
+ */
+typedef struct {
+  int32_t max_gap, budget, window, protect;
+  int32_t score_stride, in_stride, out_stride;
+} se_t2c_params_t;
+
+int32_t se_token2chunk(const se_cache_t *c, const int32_t *idx, const int32_t *count, const float *scores,
+                       const se_t2c_params_t *p, int32_t *idx_out, int32_t *count_out, int32_t *status, void *ws,
+                       size_t ws_bytes, se_stream_t stream);
+
+/* ---- physical compaction and slot eviction ------------------------------------------------------------------
+ * SparseEngine page, "How it works": physical eviction updates the retained slot mapping and the context
+ * length and returns discarded slots to the allocator. KARA page, "Method" part 3: trailing blocks are
+ * compacted periodically.
+ *  GATHER: per (b, g) the ascending, distinct, resident slots idx[..][0..count) inside [w0, n_slots) are kept,
+ *    w0 = 0 (window = 0) or n_slots - window. The j-th moves to slot w0 + j with its K, V, position and (if
+ *    present) cumulative score; n_slots = w0 + count; ctx_len drops the window's other resident slots; free
+ *    slots at or above w0 leave the slot stack. Sequence b keeps logical blocks [0, ceil(max_g n_slots / page))
+ *    (same physical ids); the rest of its allocated blocks are pushed on free_blocks in order of sequence, then
+ *    logical block, and their table entries become -1. In place; bit-exact.
+ *  EVICT_SLOTS: per (b, g) each listed resident slot is freed: position -1, cumulative score 0, pushed on the
+ *    slot stack, ctx_len - 1. No data moves.
+ */
+enum { SE_COMPACT_GATHER = 0, SE_COMPACT_EVICT_SLOTS = 1 };
+typedef struct {
+  int32_t mode, window, idx_stride;
+} se_compact_params_t;
+
+size_t se_compact_evict_workspace_size(const se_cache_t *c, const se_compact_params_t *p);
+int32_t se_compact_evict(se_cache_t *c, const int32_t *idx, const int32_t *count, const se_compact_params_t *p,
+                         int32_t *status, void *ws, size_t ws_bytes, se_stream_t stream);
+
+/* ---- append one decode token per (sequence, KV head) --------------------------------------------------------
+ * CacheManager allocate/write (SparseEngine page, "How it works"). Per (b, g): the slot is popped from the
+ * slot stack if it is not empty, else slot = n_slots++. When a slot lies in a logical block sequence b lacks,
+ * one block is popped from free_blocks for it (pops in sequence order). k_new, v_new [B][n_kv][d] of dtype are
+ * written, pos_map = pos[b] (pos: device [B]), ctx_len + 1, and the cumulative score (if present) set to 0. All or
+ * nothing: if the free stack or a sequence's slot range cannot serve the whole call, nothing changes and
+ * SE_DEV_CAPACITY is raised.
+ */
+int32_t se_cache_append(se_cache_t *c, const void *k_new, const void *v_new, const int32_t *pos, int32_t *status,
+                        void *ws, size_t ws_bytes, se_stream_t stream);
+
+/* ---- Quest page bounds ---------------------------------------------------------------------------------------
+ * SparseEngine page, "What it is"/"How it works": Quest's query-dependent page selection. Needs page_meta.
+ *  BUILD: page_meta[b][g][p][0][e] / [1][e] = min / max over the resident keys of page p (exact). Every page
+ *    p < max_blocks is written; pages without a resident key hold +inf / -inf.
+ *  SCORE: page_scores[(b*n_kv+g)*score_stride + p] = max over h in G(g) of sum_e max(q[b][h][e]*min_e,
+ *    q[b][h][e]*max_e) for p < ceil(n_slots/page) (fp32 accumulation; -inf for empty pages). q [B][n_q][d].
+ */
+enum { SE_PAGES_BUILD = 0, SE_PAGES_SCORE = 1 };
+int32_t se_page_bounds(se_cache_t *c, int32_t op, const void *q, float *page_scores, int32_t score_stride,
+                       int32_t *status, void *ws, size_t ws_bytes, se_stream_t stream);
+
+/* ---- decode attention over the view ---------------------------------------------------------------------------
+ * o = Attention(q, View), View = BuildView(C, I) (SparseEngine page, "How it works"). For each query head h of
+ * KV head g: out[b][h][e] = sum over slots s in View(b, g) of softmax_s(scale * q[b][h] . k_s) v_s[e], fp32
+ * output [B][n_q][d]. View(b, g) = the resident slots below n_slots, or, when sel_pages is given, the resident
+ * slots of the logical pages sel_pages[(b*n_kv+g)*sel_stride + i], i < sel_count[b*n_kv+g] (ascending,
+ * distinct, < ceil(n_slots/page)). An empty view gives 0. With accumulate != 0 (needs cum_score; H2O, the
+ * SparseEngine page "What it is"): cum_score[b][g][s] += sum over h in G(g) of that head's weight on s.
+ */
+typedef struct {
+  float scale;
+  int32_t sel_stride; /* ignored without sel_pages */
+  int32_t max_sel;    /* with sel_pages: upper bound on sel_count (sizes the launch); counts above it raise
+                         SE_DEV_CAPACITY and only the first max_sel pages are read */
+  int32_t max_slots;  /* without sel_pages: upper bound on n_slots (0 = max_blocks * page); larger n_slots raise
+                         SE_DEV_CAPACITY and only the first max_slots slots are read */
+  int32_t accumulate;
+} se_decode_params_t;
+
+size_t se_sparse_decode_attn_workspace_size(const se_cache_t *c, const se_decode_params_t *p, int32_t has_sel);
+int32_t se_sparse_decode_attn(se_cache_t *c, const void *q, const int32_t *sel_pages, const int32_t *sel_count,
+                              const se_decode_params_t *p, float *out, int32_t *status, void *ws, size_t ws_bytes,
+                              se_stream_t stream);
+
+/* ---- utilities ----------------------------------------------------------------------------------------------- */
+/* Synchronise `stream`, copy the device status word to *host_value and (if reset) clear it. */
+int32_t se_status_read(int32_t *status, int32_t *host_value, int32_t reset, se_stream_t stream);
+const char *se_error_string(int32_t code);
+const char *se_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SE_H */

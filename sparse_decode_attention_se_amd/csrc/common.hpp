@@ -1,0 +1,115 @@
+// Shared device and host helpers of libse (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/se.h"
+
+#define SE_DEV __device__ __forceinline__
+
+namespace se {
+
+constexpr int kWave = 64;
+
+// ---- element types --------------------------------------------------------------------------------------------
+// bf16 is carried as its 16-bit pattern; widening to fp32 is a shift.
+SE_DEV float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+SE_DEV float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+SE_DEV uint16_t f32_to_bf16_exact(float x) { return (uint16_t)(__float_as_uint(x) >> 16); }  // x already bf16
+
+// 16-byte vector load / store (global, through the vector memory path)
+struct alignas(16) u32x4 {
+  uint32_t x, y, z, w;
+};
+SE_DEV u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
+SE_DEV void st16(void *p, const u32x4 &v) { *reinterpret_cast<u32x4 *>(p) = v; }
+
+// ---- wave reductions ------------------------------------------------------------------------------------------
+// DPP row_ror:n rotates within a row of 16 lanes; four steps leave the row total in every lane of the row.
+template <int CTRL>
+SE_DEV float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+constexpr int kRowRor1 = 0x121, kRowRor2 = 0x122, kRowRor4 = 0x124, kRowRor8 = 0x128;
+
+SE_DEV float row16_sum(float x) {
+  x += dpp_f<kRowRor8>(x);
+  x += dpp_f<kRowRor4>(x);
+  x += dpp_f<kRowRor2>(x);
+  x += dpp_f<kRowRor1>(x);
+  return x;
+}
+SE_DEV float row16_max(float x) {
+  x = fmaxf(x, dpp_f<kRowRor8>(x));
+  x = fmaxf(x, dpp_f<kRowRor4>(x));
+  x = fmaxf(x, dpp_f<kRowRor2>(x));
+  x = fmaxf(x, dpp_f<kRowRor1>(x));
+  return x;
+}
+// sum over lanes with the same (lane % 16): the four rows of the wave
+SE_DEV float cross_row_sum(float x) {
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+SE_DEV float cross_row_max(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
+  x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+SE_DEV float wave_sum(float x) { return cross_row_sum(row16_sum(x)); }
+SE_DEV float wave_max(float x) { return cross_row_max(row16_max(x)); }
+
+SE_DEV int wave_sum_i(int x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+SE_DEV bool blk_ok(int32_t blk, int32_t num_blocks) { return blk >= 0 && blk < num_blocks; }
+
+// ---- status ---------------------------------------------------------------------------------------------------
+SE_DEV void raise(int32_t *status, int32_t bit) {
+  if (status) atomicOr(status, bit);
+}
+
+// ---- cache addressing -----------------------------------------------------------------------------------------
+struct CacheView {
+  const char *k, *v;
+  const int32_t *bt, *pos;
+  int32_t n_kv, d, page, max_blocks, row_bytes;
+  SE_DEV int64_t max_slots() const { return (int64_t)max_blocks * page; }
+  // byte offset of slot s of (b, g) in a pool, given the physical block
+  SE_DEV int64_t row_off(int32_t blk, int32_t g, int32_t s) const {
+    return (((int64_t)blk * n_kv + g) * page + (s % page)) * row_bytes;
+  }
+};
+
+inline int elem_bytes(int dtype) { return dtype == SE_DTYPE_BF16 ? 2 : 4; }
+
+}  // namespace se
+
+// ---- host-side validation shared by the entry points ---------------------------------------------------------
+namespace se_host {
+
+inline int32_t check_cache(const se_cache_t *c) {
+  if (!c) return SE_ERR_NULL;
+  if (!c->k_pool || !c->v_pool || !c->block_table || !c->pos_map || !c->ctx_len || !c->n_slots) return SE_ERR_NULL;
+  if (c->dtype != SE_DTYPE_F32 && c->dtype != SE_DTYPE_BF16) return SE_ERR_DTYPE;
+  if (c->B <= 0 || c->n_kv <= 0 || c->n_q <= 0 || c->d <= 0 || c->page <= 0 || c->num_blocks <= 0 ||
+      c->max_blocks <= 0 || c->slot_cap < 0)
+    return SE_ERR_SHAPE;
+  if (c->n_q % c->n_kv != 0) return SE_ERR_SHAPE;
+  if ((long long)c->max_blocks * c->page > (1ll << 30)) return SE_ERR_SHAPE;
+  return SE_OK;
+}
+
+inline int32_t launch_status() {
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? SE_OK : SE_ERR_HIP;
+}
+
+inline size_t align_up(size_t x, size_t a = 256) { return (x + a - 1) / a * a; }
+
+}  // namespace se_host

@@ -1,0 +1,567 @@
+// CacheManager state changes (SparseEngine page, "How it works": physical eviction updates the retained
+// slot mapping and context length and returns discarded slots to the allocator; KARA page, "Method" part 3:
+// periodic compaction of trailing blocks):
+//   se_compact_evict  GATHER       in-place keep-prefix compaction + block freeing
+//                     EVICT_SLOTS  slot eviction onto the per-head slot stack
+//   se_cache_append   one decode token per (sequence, KV head)
+//
+// In-place gather hazard. Output j of a (sequence, head) unit copies slot s_j to slot w0 + j, with s ascending
+// and s_j >= w0 + j. Writing slot w0 + j destroys a source only if some output k < j reads s_k = w0 + j. Let
+// h = #{j : s_j < w0 + cnt}; those outputs form a prefix, and so do the identity outputs (s_j = w0 + j,
+// nothing to move), [0, i0). The only conflicting pairs are (reader k in [i0, h), writer s_k - w0). Workgroup
+// 0 of each unit moves exactly that set S in ascending tiles (all reads of a tile before its writes); every
+// other output reads a slot >= w0 + cnt, which nobody writes, and writes a slot no reader needs, so the
+// remaining workgroups move them with no ordering at all. Bit-exact, deterministic, one pass over the data.
+#include "common.hpp"
+
+namespace se {
+namespace {
+
+constexpr int kMoveRows = 64;   // output rows per workgroup tile
+constexpr int kMoveThreads = 256;
+constexpr int kMaxBitmapWords = 2048;  // hazard bitmap: 65536 outputs per unit
+
+struct GatherArgs {
+  char *k, *v;
+  const int32_t *bt;
+  int32_t *pos;
+  float *cum;
+  const int32_t *n_slots, *idx, *count;
+  int32_t *status;
+  int32_t n_kv, page, max_blocks, num_blocks, row_bytes, window, idx_stride;
+};
+
+struct UnitPlan {
+  int n, cnt, w0, i0, h;
+  bool ok;
+};
+
+// first j in [0, cnt) with pred(j) true, for a monotone predicate (cnt if none)
+template <class F>
+SE_DEV int lower_bound_pred(int cnt, F pred) {
+  int lo = 0, hi = cnt;
+  while (lo < hi) {
+    int mid = (lo + hi) >> 1;
+    if (pred(mid)) hi = mid; else lo = mid + 1;
+  }
+  return lo;
+}
+
+SE_DEV UnitPlan plan_unit(const GatherArgs &a, int unit) {
+  UnitPlan u;
+  const int cap = a.max_blocks * a.page;
+  u.n = a.n_slots[unit];
+  u.cnt = a.count[unit];
+  u.w0 = a.window > 0 ? u.n - a.window : 0;
+  u.ok = u.n >= 0 && u.n <= cap && u.w0 >= 0 && u.cnt >= 0 && u.cnt <= u.n - u.w0 && u.cnt <= a.idx_stride;
+  if (!u.ok) {
+    u.cnt = 0;
+    u.i0 = u.h = 0;
+    return u;
+  }
+  const int32_t *s = a.idx + (int64_t)unit * a.idx_stride;
+  const int lim = u.w0 + u.cnt, w0 = u.w0;
+  u.h = lower_bound_pred(u.cnt, [&](int j) { return s[j] >= lim; });
+  u.i0 = lower_bound_pred(u.cnt, [&](int j) { return s[j] - j > w0; });
+  if (u.i0 > u.h) u.i0 = u.h;  // only possible for an invalid list, which is flagged below
+  return u;
+}
+
+// is slot w0 + j the source of a hazardous reader k in [i0, h)?
+SE_DEV bool is_hazard_dest(const int32_t *s, const UnitPlan &u, int j) {
+  int lo = u.i0, hi = u.h, want = u.w0 + j;
+  while (lo < hi) {
+    int mid = (lo + hi) >> 1;
+    if (s[mid] < want) lo = mid + 1; else hi = mid;
+  }
+  return lo < u.h && s[lo] == want;
+}
+
+// copy `nrows` rows (row r: source slot src[r] -> dest slot dst[r], -1 = skip) of one unit; reads complete
+// before any write
+SE_DEV void move_rows(const GatherArgs &a, int b, int g, int unit, const int *src, const int *dst, int nrows) {
+  const int cpr = a.row_bytes / 16;
+  const int total = nrows * cpr;
+  const int32_t *bt = a.bt + (int64_t)b * a.max_blocks;
+  int32_t *pos = a.pos + (int64_t)unit * a.max_blocks * a.page;
+  float *cum = a.cum ? a.cum + (int64_t)unit * a.max_blocks * a.page : nullptr;
+  constexpr int kPer = kMoveRows * 32 / kMoveThreads;  // up to 32 chunks per row (512-byte rows)
+  u32x4 kbuf[kPer], vbuf[kPer];
+  int32_t pbuf[kPer];
+  float cbuf[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    int t = threadIdx.x + i * kMoveThreads;
+    if (t < total && src[t / cpr] >= 0 && blk_ok(bt[src[t / cpr] / a.page], a.num_blocks) &&
+        blk_ok(bt[dst[t / cpr] / a.page], a.num_blocks)) {
+      int r = t / cpr, ch = t % cpr, ss = src[r];
+      int64_t off = (((int64_t)bt[ss / a.page] * a.n_kv + g) * a.page + ss % a.page) * a.row_bytes + ch * 16;
+      kbuf[i] = ld16(a.k + off);
+      vbuf[i] = ld16(a.v + off);
+      if (ch == 0) {
+        pbuf[i] = pos[ss];
+        if (cum) cbuf[i] = cum[ss];
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    int t = threadIdx.x + i * kMoveThreads;
+    if (t < total && src[t / cpr] >= 0 && blk_ok(bt[src[t / cpr] / a.page], a.num_blocks) &&
+        blk_ok(bt[dst[t / cpr] / a.page], a.num_blocks)) {
+      int r = t / cpr, ch = t % cpr, ds = dst[r];
+      int64_t off = (((int64_t)bt[ds / a.page] * a.n_kv + g) * a.page + ds % a.page) * a.row_bytes + ch * 16;
+      st16(a.k + off, kbuf[i]);
+      st16(a.v + off, vbuf[i]);
+      if (ch == 0) {
+        pos[ds] = pbuf[i];
+        if (cum) cum[ds] = cbuf[i];
+      }
+    }
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(kMoveThreads) void gather_move(GatherArgs a) {
+  const int unit = blockIdx.y;
+  const int b = unit / a.n_kv, g = unit % a.n_kv;
+  __shared__ UnitPlan s_plan;
+  __shared__ int s_src[kMoveRows], s_dst[kMoveRows];
+  __shared__ uint32_t s_bits[kMaxBitmapWords];
+  if (threadIdx.x == 0) s_plan = plan_unit(a, unit);
+  __syncthreads();
+  const UnitPlan u = s_plan;
+  if (!u.ok) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) raise(a.status, SE_DEV_INDEX);
+    return;
+  }
+  const int32_t *s = a.idx + (int64_t)unit * a.idx_stride;
+  const int32_t *pos = a.pos + (int64_t)unit * a.max_blocks * a.page;
+  const int lim = u.w0 + u.cnt;
+
+  if (blockIdx.x > 0) {
+    // free-running movers: outputs j >= h whose destination no hazardous reader needs
+    const int j0 = (blockIdx.x - 1) * kMoveRows;
+    if (j0 >= u.cnt) return;
+    if (threadIdx.x < kMoveRows) {
+      int j = j0 + threadIdx.x, src = -1;
+      if (j < u.cnt && j >= u.h) {
+        int sj = s[j];
+        bool valid = sj >= lim && sj < u.n && (j == 0 || s[j - 1] < sj) && pos[sj] >= 0;
+        if (!valid) raise(a.status, SE_DEV_INDEX);
+        else if (!is_hazard_dest(s, u, j)) src = sj;
+      }
+      s_src[threadIdx.x] = src;
+      s_dst[threadIdx.x] = u.w0 + j;
+    }
+    __syncthreads();
+    move_rows(a, b, g, unit, s_src, s_dst, kMoveRows);
+    return;
+  }
+
+  // workgroup 0: validate the prefix and move the hazard set S in ascending tiles
+  const int words = (u.cnt + 31) / 32;
+  for (int i = threadIdx.x; i < words; i += kMoveThreads) s_bits[i] = 0;
+  __syncthreads();
+  for (int j = threadIdx.x; j < u.h; j += kMoveThreads) {
+    int sj = s[j];
+    bool valid = sj >= u.w0 + j && sj < lim && (j == 0 || s[j - 1] < sj) && pos[sj] >= 0;
+    if (!valid) {
+      raise(a.status, SE_DEV_INDEX);
+      continue;
+    }
+    if (j >= u.i0 && sj != u.w0 + j) {
+      atomicOr(&s_bits[j >> 5], 1u << (j & 31));
+      int d = sj - u.w0;
+      atomicOr(&s_bits[d >> 5], 1u << (d & 31));
+    }
+  }
+  __syncthreads();
+  for (int t0 = (u.i0 / kMoveRows) * kMoveRows; t0 < u.cnt; t0 += kMoveRows) {
+    const uint32_t w_lo = s_bits[t0 >> 5], w_hi = (t0 + 32 < u.cnt) ? s_bits[(t0 >> 5) + 1] : 0u;
+    if ((w_lo | w_hi) == 0) continue;  // uniform across the workgroup
+    if (threadIdx.x < kMoveRows) {
+      int j = t0 + threadIdx.x;
+      bool mark = j < u.cnt && ((threadIdx.x < 32 ? w_lo : w_hi) >> (threadIdx.x & 31)) & 1u;
+      int sj = mark ? s[j] : -1;
+      s_src[threadIdx.x] = (mark && sj >= u.w0 && sj < u.n) ? sj : -1;
+      s_dst[threadIdx.x] = u.w0 + j;
+    }
+    __syncthreads();
+    move_rows(a, b, g, unit, s_src, s_dst, kMoveRows);
+  }
+}
+
+struct FinalArgs {
+  int32_t *bt, *n_slots, *ctx, *free_blocks, *free_top, *slot_stack, *slot_top;
+  const int32_t *count;
+  int32_t *status;
+  int32_t B, n_kv, page, max_blocks, num_blocks, slot_cap, window;
+};
+
+constexpr int kFinalThreads = 1024;
+constexpr int kMaxSeq = 4096;
+
+// single workgroup: per-(b,g) counters and slot stacks, then per-sequence block freeing in sequence order
+__global__ __launch_bounds__(kFinalThreads) void gather_finalize(FinalArgs a) {
+  __shared__ int s_new_ext[kMaxSeq];
+  __shared__ int s_freed[kMaxSeq];
+  __shared__ int s_scan[kFinalThreads];
+  const int units = a.B * a.n_kv;
+  const int cap = a.max_blocks * a.page;
+  // new n_slots per unit (computed, not yet stored, so that the per-sequence maximum can use them)
+  for (int b = threadIdx.x; b < a.B; b += kFinalThreads) {
+    int mx = 0;
+    for (int g = 0; g < a.n_kv; ++g) {
+      int unit = b * a.n_kv + g;
+      int n = a.n_slots[unit], cnt = a.count[unit];
+      int w0 = a.window > 0 ? n - a.window : 0;
+      bool ok = n >= 0 && n <= cap && w0 >= 0 && cnt >= 0 && cnt <= n - w0;
+      int nn = ok ? w0 + cnt : n;
+      mx = max(mx, nn);
+    }
+    s_new_ext[b] = (mx + a.page - 1) / a.page;
+  }
+  __syncthreads();
+  for (int unit = threadIdx.x; unit < units; unit += kFinalThreads) {
+    int n = a.n_slots[unit], cnt = a.count[unit];
+    int w0 = a.window > 0 ? n - a.window : 0;
+    bool ok = n >= 0 && n <= cap && w0 >= 0 && cnt >= 0 && cnt <= n - w0;
+    if (!ok) continue;
+    int holes = 0;
+    if (a.slot_cap > 0 && a.slot_stack) {
+      int top = a.slot_top[unit], kept = 0;
+      int32_t *st = a.slot_stack + (int64_t)unit * a.slot_cap;
+      for (int i = 0; i < top && i < a.slot_cap; ++i) {
+        int sl = st[i];
+        if (sl >= w0) ++holes; else st[kept++] = sl;
+      }
+      a.slot_top[unit] = kept;
+    }
+    a.ctx[unit] = a.ctx[unit] - ((n - w0) - holes) + cnt;
+    a.n_slots[unit] = w0 + cnt;
+  }
+  // blocks past the new extent, up to the end of the allocated prefix
+  for (int b = threadIdx.x; b < a.B; b += kFinalThreads) {
+    const int32_t *row = a.bt + (int64_t)b * a.max_blocks;
+    int e = s_new_ext[b], old = e;
+    while (old < a.max_blocks && row[old] >= 0) ++old;
+    s_freed[b] = old - e;
+  }
+  __syncthreads();
+  // exclusive scan of s_freed over sequences (chunks of kFinalThreads)
+  int carry = 0;
+  const int top0 = *a.free_top;
+  if (top0 < 0 || top0 > a.num_blocks) {
+    if (threadIdx.x == 0) raise(a.status, SE_DEV_CAPACITY);
+    return;
+  }
+  for (int base = 0; base < a.B; base += kFinalThreads) {
+    int b = base + threadIdx.x;
+    int v = b < a.B ? s_freed[b] : 0;
+    s_scan[threadIdx.x] = v;
+    __syncthreads();
+    for (int off = 1; off < kFinalThreads; off <<= 1) {
+      int x = threadIdx.x >= off ? s_scan[threadIdx.x - off] : 0;
+      __syncthreads();
+      s_scan[threadIdx.x] += x;
+      __syncthreads();
+    }
+    int excl = carry + s_scan[threadIdx.x] - v;
+    if (b < a.B && v > 0) {
+      int32_t *row = a.bt + (int64_t)b * a.max_blocks;
+      int e = s_new_ext[b];
+      int dst = top0 + excl;
+      if (dst + v > a.num_blocks) {
+        raise(a.status, SE_DEV_CAPACITY);
+      } else {
+        for (int i = 0; i < v; ++i) {
+          a.free_blocks[dst + i] = row[e + i];
+          row[e + i] = -1;
+        }
+      }
+    }
+    carry += s_scan[kFinalThreads - 1];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *a.free_top = min(top0 + carry, a.num_blocks);
+}
+
+// ---- slot eviction ------------------------------------------------------------------------------------------------
+struct EvictArgs {
+  int32_t *pos, *ctx, *slot_stack, *slot_top;
+  float *cum;
+  const int32_t *n_slots, *idx, *count;
+  int32_t *status;
+  int32_t units, max_slots, slot_cap, idx_stride;
+};
+
+__global__ void evict_slots_kernel(EvictArgs a) {
+  int unit = blockIdx.x * blockDim.x + threadIdx.x;
+  if (unit >= a.units) return;
+  int cnt = a.count[unit], n = a.n_slots[unit];
+  if (cnt < 0 || cnt > a.idx_stride) {
+    raise(a.status, SE_DEV_INDEX);
+    return;
+  }
+  int32_t *pos = a.pos + (int64_t)unit * a.max_slots;
+  int32_t *st = a.slot_stack + (int64_t)unit * a.slot_cap;
+  const int32_t *list = a.idx + (int64_t)unit * a.idx_stride;
+  int top = a.slot_top[unit];
+  if (top < 0 || top > a.slot_cap) {
+    raise(a.status, SE_DEV_CAPACITY);
+    return;
+  }
+  for (int i = 0; i < cnt; ++i) {
+    int s = list[i];
+    if (s < 0 || s >= n || s >= a.max_slots || pos[s] < 0) {
+      raise(a.status, SE_DEV_INDEX);
+      continue;
+    }
+    if (top >= a.slot_cap) {
+      raise(a.status, SE_DEV_CAPACITY);
+      break;
+    }
+    pos[s] = -1;
+    if (a.cum) a.cum[(int64_t)unit * a.max_slots + s] = 0.f;
+    st[top++] = s;
+    a.ctx[unit] -= 1;
+  }
+  a.slot_top[unit] = top;
+}
+
+// ---- append -------------------------------------------------------------------------------------------------------
+struct AppendArgs {
+  char *k, *v;
+  int32_t *bt, *pos, *ctx, *n_slots, *free_blocks, *free_top, *slot_stack, *slot_top;
+  float *cum;
+  const char *k_new, *v_new;
+  const int32_t *pos_new;
+  int32_t *status;
+  int32_t B, n_kv, page, max_blocks, num_blocks, slot_cap, row_bytes;
+};
+
+constexpr int kAppendThreads = 1024;
+constexpr int kMaxUnits = 4096;
+constexpr int kAppendMaxSeq = 2048;
+
+// single workgroup: decide every slot and block first, then commit only if the whole call fits
+__global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
+  __shared__ int s_slot[kMaxUnits];
+  __shared__ int s_blk[kMaxUnits];      // physical block of each unit's slot
+  __shared__ int s_lb[kAppendMaxSeq];   // logical block sequence b lacks (-1 = none)
+  __shared__ int s_pop[kAppendMaxSeq];  // free-stack index it pops from
+  __shared__ int s_scan[kAppendThreads];
+  __shared__ int s_fail;
+  const int units = a.B * a.n_kv;
+  const int cap = a.max_blocks * a.page;
+  if (threadIdx.x == 0) s_fail = 0;
+  __syncthreads();
+  for (int unit = threadIdx.x; unit < units; unit += kAppendThreads) {
+    int top = a.slot_cap > 0 ? a.slot_top[unit] : 0;
+    if (top < 0 || top > a.slot_cap) {
+      atomicOr(&s_fail, 1);
+      top = 0;
+    }
+    int slot = top > 0 ? a.slot_stack[(int64_t)unit * a.slot_cap + top - 1] : a.n_slots[unit];
+    if (slot < 0 || slot >= cap) {
+      atomicOr(&s_fail, 1);
+      slot = 0;
+    }
+    s_slot[unit] = slot;
+  }
+  __syncthreads();
+  // per sequence: the logical block its heads lack, if any (allocated entries form a prefix, so a single
+  // token per head can only enter one new block)
+  for (int b = threadIdx.x; b < a.B; b += kAppendThreads) {
+    int need = -1;
+    for (int g = 0; g < a.n_kv; ++g) {
+      int lb = s_slot[b * a.n_kv + g] / a.page;
+      int cur = a.bt[(int64_t)b * a.max_blocks + lb];
+      if (cur >= a.num_blocks) atomicOr(&s_fail, 1);
+      if (cur < 0) {
+        if (need >= 0 && need != lb) atomicOr(&s_fail, 2);
+        need = lb;
+      }
+    }
+    s_lb[b] = need;
+  }
+  __syncthreads();
+  // exclusive scan of the pops over sequences, in sequence order
+  int carry = 0;
+  const int top0 = *a.free_top;
+  if (top0 < 0 || top0 > a.num_blocks) {
+    if (threadIdx.x == 0) raise(a.status, SE_DEV_CAPACITY);
+    return;
+  }
+  for (int base = 0; base < a.B; base += kAppendThreads) {
+    int b = base + threadIdx.x;
+    int v = (b < a.B && s_lb[b] >= 0) ? 1 : 0;
+    s_scan[threadIdx.x] = v;
+    __syncthreads();
+    for (int off = 1; off < kAppendThreads; off <<= 1) {
+      int x = threadIdx.x >= off ? s_scan[threadIdx.x - off] : 0;
+      __syncthreads();
+      s_scan[threadIdx.x] += x;
+      __syncthreads();
+    }
+    if (v) {
+      int idx = top0 - 1 - (carry + s_scan[threadIdx.x] - 1);
+      int blk = idx >= 0 ? a.free_blocks[idx] : -1;
+      if (blk < 0 || blk >= a.num_blocks) atomicOr(&s_fail, 4);
+      s_pop[b] = blk;
+    }
+    carry += s_scan[kAppendThreads - 1];
+    __syncthreads();
+  }
+  if (s_fail) {
+    if (threadIdx.x == 0) raise(a.status, s_fail == 2 ? SE_DEV_INDEX : SE_DEV_CAPACITY);
+    return;  // all or nothing: nothing was written
+  }
+  for (int b = threadIdx.x; b < a.B; b += kAppendThreads)
+    if (s_lb[b] >= 0) a.bt[(int64_t)b * a.max_blocks + s_lb[b]] = s_pop[b];
+  __syncthreads();
+  if (threadIdx.x == 0) *a.free_top = top0 - carry;
+  for (int unit = threadIdx.x; unit < units; unit += kAppendThreads) {
+    int b = unit / a.n_kv;
+    int slot = s_slot[unit];
+    int top = a.slot_cap > 0 ? a.slot_top[unit] : 0;
+    if (top > 0) a.slot_top[unit] = top - 1; else a.n_slots[unit] = slot + 1;
+    a.pos[(int64_t)unit * cap + slot] = a.pos_new[b];
+    a.ctx[unit] += 1;
+    if (a.cum) a.cum[(int64_t)unit * cap + slot] = 0.f;
+    s_blk[unit] = a.bt[(int64_t)b * a.max_blocks + slot / a.page];
+  }
+  __syncthreads();
+  const int cpr = a.row_bytes / 16;
+  for (int t = threadIdx.x; t < units * cpr; t += kAppendThreads) {
+    int unit = t / cpr, ch = t % cpr;
+    int g = unit % a.n_kv, slot = s_slot[unit];
+    int64_t off = (((int64_t)s_blk[unit] * a.n_kv + g) * a.page + slot % a.page) * a.row_bytes + ch * 16;
+    int64_t src = (int64_t)unit * a.row_bytes + ch * 16;
+    st16(a.k + off, ld16(a.k_new + src));
+    st16(a.v + off, ld16(a.v_new + src));
+  }
+}
+
+}  // namespace
+}  // namespace se
+
+extern "C" size_t se_compact_evict_workspace_size(const se_cache_t *, const se_compact_params_t *) { return 0; }
+
+extern "C" int32_t se_compact_evict(se_cache_t *c, const int32_t *idx, const int32_t *count,
+                                    const se_compact_params_t *p, int32_t *status, void *ws, size_t ws_bytes,
+                                    se_stream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  int32_t rc = se_host::check_cache(c);
+  if (rc != SE_OK) return rc;
+  if (!idx || !count || !p) return SE_ERR_NULL;
+  if (p->idx_stride <= 0 || p->window < 0) return SE_ERR_PARAM;
+  hipStream_t st = (hipStream_t)stream;
+  const int units = c->B * c->n_kv;
+  const int row_bytes = c->d * se::elem_bytes(c->dtype);
+  if (row_bytes % 16 != 0 || row_bytes > 512) return SE_ERR_DTYPE;
+  if (p->mode == SE_COMPACT_GATHER) {
+    if (!c->free_blocks || !c->free_top) return SE_ERR_NULL;
+    if (p->idx_stride > 32 * se::kMaxBitmapWords) return SE_ERR_UNSUPPORTED;
+    if (c->B > se::kMaxSeq) return SE_ERR_UNSUPPORTED;
+    se::GatherArgs a;
+    a.k = (char *)c->k_pool;
+    a.v = (char *)c->v_pool;
+    a.bt = c->block_table;
+    a.pos = c->pos_map;
+    a.cum = c->cum_score;
+    a.n_slots = c->n_slots;
+    a.idx = idx;
+    a.count = count;
+    a.status = status;
+    a.n_kv = c->n_kv;
+    a.page = c->page;
+    a.max_blocks = c->max_blocks;
+    a.num_blocks = c->num_blocks;
+    a.row_bytes = row_bytes;
+    a.window = p->window;
+    a.idx_stride = p->idx_stride;
+    const int tiles = 1 + (p->idx_stride + se::kMoveRows - 1) / se::kMoveRows;
+    hipLaunchKernelGGL(se::gather_move, dim3(tiles, units), dim3(se::kMoveThreads), 0, st, a);
+    se::FinalArgs f;
+    f.bt = c->block_table;
+    f.n_slots = c->n_slots;
+    f.ctx = c->ctx_len;
+    f.free_blocks = c->free_blocks;
+    f.free_top = c->free_top;
+    f.slot_stack = c->slot_stack;
+    f.slot_top = c->slot_top;
+    f.count = count;
+    f.status = status;
+    f.B = c->B;
+    f.n_kv = c->n_kv;
+    f.page = c->page;
+    f.max_blocks = c->max_blocks;
+    f.num_blocks = c->num_blocks;
+    f.slot_cap = (c->slot_stack && c->slot_top) ? c->slot_cap : 0;
+    f.window = p->window;
+    hipLaunchKernelGGL(se::gather_finalize, dim3(1), dim3(se::kFinalThreads), 0, st, f);
+    return se_host::launch_status();
+  }
+  if (p->mode == SE_COMPACT_EVICT_SLOTS) {
+    if (!c->slot_stack || !c->slot_top || c->slot_cap <= 0) return SE_ERR_NULL;
+    se::EvictArgs a;
+    a.pos = c->pos_map;
+    a.ctx = c->ctx_len;
+    a.slot_stack = c->slot_stack;
+    a.slot_top = c->slot_top;
+    a.cum = c->cum_score;
+    a.n_slots = c->n_slots;
+    a.idx = idx;
+    a.count = count;
+    a.status = status;
+    a.units = units;
+    a.max_slots = c->max_blocks * c->page;
+    a.slot_cap = c->slot_cap;
+    a.idx_stride = p->idx_stride;
+    hipLaunchKernelGGL(se::evict_slots_kernel, dim3((units + 255) / 256), dim3(256), 0, st, a);
+    return se_host::launch_status();
+  }
+  return SE_ERR_PARAM;
+}
+
+extern "C" int32_t se_cache_append(se_cache_t *c, const void *k_new, const void *v_new, const int32_t *pos,
+                                   int32_t *status, void *ws, size_t ws_bytes, se_stream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  int32_t rc = se_host::check_cache(c);
+  if (rc != SE_OK) return rc;
+  if (!k_new || !v_new || !pos || !c->free_blocks || !c->free_top) return SE_ERR_NULL;
+  if (c->slot_cap > 0 && (!c->slot_stack || !c->slot_top)) return SE_ERR_NULL;
+  if (c->B * c->n_kv > se::kMaxUnits || c->B > se::kAppendMaxSeq) return SE_ERR_UNSUPPORTED;
+  const int row_bytes = c->d * se::elem_bytes(c->dtype);
+  if (row_bytes % 16 != 0) return SE_ERR_DTYPE;
+  se::AppendArgs a;
+  a.k = (char *)c->k_pool;
+  a.v = (char *)c->v_pool;
+  a.bt = c->block_table;
+  a.pos = c->pos_map;
+  a.ctx = c->ctx_len;
+  a.n_slots = c->n_slots;
+  a.free_blocks = c->free_blocks;
+  a.free_top = c->free_top;
+  a.slot_stack = c->slot_stack;
+  a.slot_top = c->slot_top;
+  a.cum = c->cum_score;
+  a.k_new = (const char *)k_new;
+  a.v_new = (const char *)v_new;
+  a.pos_new = pos;
+  a.status = status;
+  a.B = c->B;
+  a.n_kv = c->n_kv;
+  a.page = c->page;
+  a.max_blocks = c->max_blocks;
+  a.num_blocks = c->num_blocks;
+  a.slot_cap = c->slot_cap;
+  a.row_bytes = row_bytes;
+  hipLaunchKernelGGL(se::append_kernel, dim3(1), dim3(se::kAppendThreads), 0, (hipStream_t)stream, a);
+  return se_host::launch_status();
+}

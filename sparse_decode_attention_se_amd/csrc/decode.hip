@@ -1,0 +1,385 @@
+// Decode attention over a view of the paged cache: o = Attention(q, View), View = BuildView(C, I)
+// (SparseEngine page, "How it works"), optionally adding each step's softmax weights to per-slot cumulative
+// scores (H2O, SparseEngine page "What it is").
+//
+// The op is HBM-bound (each KV byte is used for one query group), so it runs on the vector ALU, not MFMA.
+// Split-K: workgroup (chunk, unit) streams `chunk_rows` view rows of one (sequence, KV head) unit. A row of
+// K or V is 256 bytes (bf16 d=128 or fp32 d=64) = 16 lanes x 16 B, so a wave reads four rows per load and the
+// per-row dot products reduce inside a 16-lane DPP row. Each lane-row keeps an online softmax (max, sum,
+// weighted V) for the R query heads of the group; lane-rows and waves merge at the end and the workgroup
+// writes one (m, l, acc[d]) partial per head. A second kernel merges the chunks and, when asked, turns the
+// stored logits into probabilities and adds them to cum_score.
+#include "common.hpp"
+
+namespace se {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 4;  // wave-loads in flight per lane-row
+
+template <int DTYPE>
+struct Vec;
+
+template <>
+struct Vec<SE_DTYPE_BF16> {
+  static constexpr int EPL = 8;  // elements per lane (16 B)
+  typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+  SE_DEV static float dot(const u32x4 &q, const u32x4 &k, float acc) {
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, q.x), __builtin_bit_cast(bf2, k.x), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, q.y), __builtin_bit_cast(bf2, k.y), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, q.z), __builtin_bit_cast(bf2, k.z), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, q.w), __builtin_bit_cast(bf2, k.w), acc, false);
+    return acc;
+  }
+  SE_DEV static void widen(const u32x4 &w, float *x) {
+    x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x); x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
+    x[4] = bf16_lo(w.z); x[5] = bf16_hi(w.z); x[6] = bf16_lo(w.w); x[7] = bf16_hi(w.w);
+  }
+};
+
+template <>
+struct Vec<SE_DTYPE_F32> {
+  static constexpr int EPL = 4;
+  SE_DEV static float dot(const u32x4 &q, const u32x4 &k, float acc) {
+    acc = fmaf(__uint_as_float(q.x), __uint_as_float(k.x), acc);
+    acc = fmaf(__uint_as_float(q.y), __uint_as_float(k.y), acc);
+    acc = fmaf(__uint_as_float(q.z), __uint_as_float(k.z), acc);
+    acc = fmaf(__uint_as_float(q.w), __uint_as_float(k.w), acc);
+    return acc;
+  }
+  SE_DEV static void widen(const u32x4 &w, float *x) {
+    x[0] = __uint_as_float(w.x); x[1] = __uint_as_float(w.y); x[2] = __uint_as_float(w.z); x[3] = __uint_as_float(w.w);
+  }
+};
+
+struct DecodeArgs {
+  const char *k, *v;
+  const int32_t *bt, *pos, *n_slots;
+  const char *q;
+  const int32_t *sel, *sel_count;
+  float *out, *part, *logits, *cum;
+  int32_t *status;
+  int32_t n_kv, page, max_blocks, num_blocks, sel_stride, rows_bound, chunk_rows, nchunk;
+  float scale_log2;
+};
+
+// number of view rows of a unit, and the slot of view row r (-1 if the row is not in the view)
+struct ViewMap {
+  const DecodeArgs &a;
+  int unit, n, rows;
+  SE_DEV ViewMap(const DecodeArgs &a_, int unit_) : a(a_), unit(unit_) {
+    n = a.n_slots[unit];
+    int cap = a.max_blocks * a.page;
+    n = n < 0 ? 0 : (n > cap ? cap : n);
+    if (a.sel) {
+      int cnt = a.sel_count[unit];
+      int bound = a.rows_bound / a.page;
+      rows = (cnt < 0 ? 0 : (cnt > bound ? bound : cnt)) * a.page;
+    } else {
+      rows = n < a.rows_bound ? n : a.rows_bound;
+    }
+  }
+  SE_DEV int slot(int r) const {
+    if (r >= rows) return -1;
+    if (!a.sel) return r;
+    const int32_t *list = a.sel + (int64_t)unit * a.sel_stride;
+    int i = r / a.page;
+    int p = list[i];
+    int n_pages = (n + a.page - 1) / a.page;
+    if (p < 0 || p >= n_pages || (i > 0 && list[i - 1] >= p)) return -2;  // invalid selection entry
+    int s = p * a.page + r % a.page;
+    return s < n ? s : -1;
+  }
+};
+
+template <int DTYPE, int R>
+__global__ __launch_bounds__(kThreads) void decode_partial(DecodeArgs a) {
+  using V = Vec<DTYPE>;
+  constexpr int EPL = V::EPL;
+  constexpr int D = 16 * EPL;
+  constexpr int RB = 256;  // row bytes
+  const int unit = blockIdx.y, chunk = blockIdx.x;
+  const int b = unit / a.n_kv, g = unit % a.n_kv;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lrow = lane >> 4, cl = lane & 15;
+  ViewMap vm(a, unit);
+  if (chunk == 0 && threadIdx.x == 0) {
+    if (!a.sel && vm.n > a.rows_bound) raise(a.status, SE_DEV_CAPACITY);
+    if (a.sel && a.sel_count[unit] * a.page > a.rows_bound) raise(a.status, SE_DEV_CAPACITY);
+  }
+
+  // the group's query heads, this lane's 16-byte slice of each
+  u32x4 q[R];
+#pragma unroll
+  for (int h = 0; h < R; ++h) q[h] = ld16(a.q + (((int64_t)b * a.n_kv + g) * R + h) * RB + cl * 16);
+
+  float m[R], l[R], acc[R][EPL];
+#pragma unroll
+  for (int h = 0; h < R; ++h) {
+    m[h] = -1e30f;
+    l[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
+  }
+
+  const int per_wave = a.chunk_rows / 4;
+  const int r_begin = chunk * a.chunk_rows + wave * per_wave;
+  const int r_end = min(r_begin + per_wave, vm.rows);
+  const int32_t *bt = a.bt + (int64_t)b * a.max_blocks;
+  const int32_t *pos = a.pos + (int64_t)unit * a.max_blocks * a.page;
+  bool bad = false;
+
+  for (int r0 = r_begin; r0 < r_end; r0 += 4 * kUnroll) {
+    u32x4 kv[kUnroll], vv[kUnroll];
+    int rows[kUnroll];
+    bool valid[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      int r = r0 + u * 4 + lrow;
+      rows[u] = r;
+      int s = r < r_end ? vm.slot(r) : -1;
+      bad |= (s == -2);
+      valid[u] = s >= 0 && pos[s] >= 0;
+      int blk = valid[u] ? bt[s / a.page] : -1;
+      if (valid[u] && (blk < 0 || blk >= a.num_blocks)) {
+        valid[u] = false;
+        bad = true;
+      }
+      if (valid[u]) {
+        int64_t off = (((int64_t)blk * a.n_kv + g) * a.page + (s % a.page)) * RB + cl * 16;
+        kv[u] = ld16(a.k + off);
+        vv[u] = ld16(a.v + off);
+      } else {
+        kv[u] = u32x4{0, 0, 0, 0};
+        vv[u] = u32x4{0, 0, 0, 0};
+      }
+    }
+    float sc[kUnroll][R];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+#pragma unroll
+      for (int h = 0; h < R; ++h) {
+        float d = row16_sum(V::dot(q[h], kv[u], 0.f));
+        sc[u][h] = valid[u] ? d * a.scale_log2 : -INFINITY;
+      }
+    }
+    if (a.logits) {
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        if (cl == 0 && rows[u] < r_end) {
+          float *dst = a.logits + ((int64_t)unit * a.rows_bound + rows[u]) * R;
+#pragma unroll
+          for (int h = 0; h < R; ++h) dst[h] = sc[u][h];
+        }
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < R; ++h) {
+      float mn = m[h];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) mn = fmaxf(mn, sc[u][h]);
+      float f = __builtin_amdgcn_exp2f(m[h] - mn);
+      m[h] = mn;
+      l[h] *= f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[h][e] *= f;
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      float x[EPL];
+      V::widen(vv[u], x);
+#pragma unroll
+      for (int h = 0; h < R; ++h) {
+        float p = __builtin_amdgcn_exp2f(sc[u][h] - m[h]);
+        l[h] += p;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(p, x[e], acc[h][e]);
+      }
+    }
+  }
+  if (bad) raise(a.status, SE_DEV_INDEX);
+
+  // merge the four lane-rows of the wave
+#pragma unroll
+  for (int off = 16; off <= 32; off <<= 1) {
+#pragma unroll
+    for (int h = 0; h < R; ++h) {
+      float mo = __shfl_xor(m[h], off), lo = __shfl_xor(l[h], off);
+      float mn = fmaxf(m[h], mo);
+      float fa = __builtin_amdgcn_exp2f(m[h] - mn), fb = __builtin_amdgcn_exp2f(mo - mn);
+      l[h] = l[h] * fa + lo * fb;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[h][e] = acc[h][e] * fa + __shfl_xor(acc[h][e], off) * fb;
+      m[h] = mn;
+    }
+  }
+  // merge the waves through LDS and write the chunk's partial
+  __shared__ float s_ml[4][R][2];
+  __shared__ float s_acc[4][R][D];
+  if (lane < 16) {
+#pragma unroll
+    for (int h = 0; h < R; ++h) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) s_acc[wave][h][cl * EPL + e] = acc[h][e];
+      if (lane == 0) {
+        s_ml[wave][h][0] = m[h];
+        s_ml[wave][h][1] = l[h];
+      }
+    }
+  }
+  __syncthreads();
+  float *part = a.part + ((int64_t)unit * a.nchunk + chunk) * R * (D + 2);
+  for (int i = threadIdx.x; i < R * D; i += kThreads) {
+    int h = i / D, e = i % D;
+    float mm = fmaxf(fmaxf(s_ml[0][h][0], s_ml[1][h][0]), fmaxf(s_ml[2][h][0], s_ml[3][h][0]));
+    float ll = 0.f, oo = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      float f = __builtin_amdgcn_exp2f(s_ml[w][h][0] - mm);
+      ll += s_ml[w][h][1] * f;
+      oo += s_acc[w][h][e] * f;
+    }
+    part[h * (D + 2) + 2 + e] = oo;
+    if (e == 0) {
+      part[h * (D + 2)] = mm;
+      part[h * (D + 2) + 1] = ll;
+    }
+  }
+}
+
+template <int DTYPE, int R>
+__global__ __launch_bounds__(kThreads) void decode_merge(DecodeArgs a) {
+  constexpr int D = 16 * Vec<DTYPE>::EPL;
+  const int unit = blockIdx.x;
+  const int b = unit / a.n_kv, g = unit % a.n_kv;
+  const float *part = a.part + (int64_t)unit * a.nchunk * R * (D + 2);
+  __shared__ float s_m[R], s_il[R];
+  for (int i = threadIdx.x; i < R * D; i += kThreads) {
+    int h = i / D, e = i % D;
+    float mm = -1e30f;
+    for (int c = 0; c < a.nchunk; ++c) mm = fmaxf(mm, part[(c * R + h) * (D + 2)]);
+    float ll = 0.f, oo = 0.f;
+    for (int c = 0; c < a.nchunk; ++c) {
+      const float *pc = part + (c * R + h) * (D + 2);
+      float f = __builtin_amdgcn_exp2f(pc[0] - mm);
+      ll += pc[1] * f;
+      oo += pc[2 + e] * f;
+    }
+    a.out[(((int64_t)b * a.n_kv + g) * R + h) * D + e] = ll > 0.f ? oo / ll : 0.f;
+    if (e == 0) {
+      s_m[h] = mm;
+      s_il[h] = ll > 0.f ? 1.f / ll : 0.f;
+    }
+  }
+  if (!a.cum) return;
+  __syncthreads();
+  ViewMap vm(a, unit);
+  float *cum = a.cum + (int64_t)unit * a.max_blocks * a.page;
+  for (int r = threadIdx.x; r < vm.rows; r += kThreads) {
+    int s = vm.slot(r);
+    if (s < 0) continue;
+    const float *lg = a.logits + ((int64_t)unit * a.rows_bound + r) * R;
+    if (lg[0] == -INFINITY) continue;  // free slot: not in the view
+    float sum = 0.f;
+#pragma unroll
+    for (int h = 0; h < R; ++h) sum += __builtin_amdgcn_exp2f(lg[h] - s_m[h]) * s_il[h];
+    cum[s] += sum;
+  }
+}
+
+struct Plan {
+  int rows_bound, chunk_rows, nchunk, units;
+  size_t part_bytes, logit_bytes;
+};
+
+Plan make_plan(const se_cache_t *c, const se_decode_params_t *p, int has_sel) {
+  Plan pl;
+  int cap = c->max_blocks * c->page;
+  if (has_sel) {
+    pl.rows_bound = p->max_sel * c->page;
+  } else {
+    pl.rows_bound = p->max_slots > 0 && p->max_slots < cap ? p->max_slots : cap;
+  }
+  pl.units = c->B * c->n_kv;
+  int ch = 512;
+  while (ch > 64 && (long long)pl.units * ((pl.rows_bound + ch - 1) / ch) < 2048) ch /= 2;
+  pl.chunk_rows = ch;
+  pl.nchunk = (pl.rows_bound + ch - 1) / ch;
+  if (pl.nchunk < 1) pl.nchunk = 1;
+  int R = c->n_q / c->n_kv;
+  pl.part_bytes = se_host::align_up((size_t)pl.units * pl.nchunk * R * (c->d + 2) * sizeof(float));
+  pl.logit_bytes = p->accumulate ? se_host::align_up((size_t)pl.units * pl.rows_bound * R * sizeof(float)) : 0;
+  return pl;
+}
+
+template <int DTYPE, int R>
+void launch(const DecodeArgs &a, int units, int nchunk, hipStream_t st) {
+  hipLaunchKernelGGL((decode_partial<DTYPE, R>), dim3(nchunk, units), dim3(kThreads), 0, st, a);
+  hipLaunchKernelGGL((decode_merge<DTYPE, R>), dim3(units), dim3(kThreads), 0, st, a);
+}
+
+template <int DTYPE>
+int32_t dispatch_r(int R, const DecodeArgs &a, int units, int nchunk, hipStream_t st) {
+  switch (R) {
+    case 1: launch<DTYPE, 1>(a, units, nchunk, st); break;
+    case 2: launch<DTYPE, 2>(a, units, nchunk, st); break;
+    case 4: launch<DTYPE, 4>(a, units, nchunk, st); break;
+    case 8: launch<DTYPE, 8>(a, units, nchunk, st); break;
+    default: return SE_ERR_UNSUPPORTED;
+  }
+  return se_host::launch_status();
+}
+
+}  // namespace
+}  // namespace se
+
+extern "C" size_t se_sparse_decode_attn_workspace_size(const se_cache_t *c, const se_decode_params_t *p,
+                                                        int32_t has_sel) {
+  if (se_host::check_cache(c) != SE_OK || !p) return 0;
+  se::Plan pl = se::make_plan(c, p, has_sel);
+  return pl.part_bytes + pl.logit_bytes;
+}
+
+extern "C" int32_t se_sparse_decode_attn(se_cache_t *c, const void *q, const int32_t *sel_pages,
+                                         const int32_t *sel_count, const se_decode_params_t *p, float *out,
+                                         int32_t *status, void *ws, size_t ws_bytes, se_stream_t stream) {
+  int32_t rc = se_host::check_cache(c);
+  if (rc != SE_OK) return rc;
+  if (!q || !out || !p) return SE_ERR_NULL;
+  const int has_sel = sel_pages != nullptr;
+  if (has_sel && !sel_count) return SE_ERR_NULL;
+  if (has_sel && (p->max_sel <= 0 || p->sel_stride < p->max_sel)) return SE_ERR_SHAPE;
+  if (p->max_slots < 0) return SE_ERR_PARAM;
+  if (p->accumulate && !c->cum_score) return SE_ERR_NULL;
+  const bool ok_shape = (c->dtype == SE_DTYPE_BF16 && c->d == 128) || (c->dtype == SE_DTYPE_F32 && c->d == 64);
+  if (!ok_shape) return SE_ERR_DTYPE;
+  se::Plan pl = se::make_plan(c, p, has_sel);
+  if (ws_bytes < pl.part_bytes + pl.logit_bytes || !ws) return SE_ERR_WORKSPACE;
+  se::DecodeArgs a;
+  a.k = (const char *)c->k_pool;
+  a.v = (const char *)c->v_pool;
+  a.bt = c->block_table;
+  a.pos = c->pos_map;
+  a.n_slots = c->n_slots;
+  a.q = (const char *)q;
+  a.sel = sel_pages;
+  a.sel_count = sel_count;
+  a.out = out;
+  a.part = (float *)ws;
+  a.logits = p->accumulate ? (float *)((char *)ws + pl.part_bytes) : nullptr;
+  a.cum = p->accumulate ? c->cum_score : nullptr;
+  a.status = status;
+  a.n_kv = c->n_kv;
+  a.page = c->page;
+  a.max_blocks = c->max_blocks;
+  a.num_blocks = c->num_blocks;
+  a.sel_stride = has_sel ? p->sel_stride : 0;
+  a.rows_bound = pl.rows_bound;
+  a.chunk_rows = pl.chunk_rows;
+  a.nchunk = pl.nchunk;
+  a.scale_log2 = p->scale * 1.4426950408889634f;
+  const int R = c->n_q / c->n_kv;
+  hipStream_t st = (hipStream_t)stream;
+  if (c->dtype == SE_DTYPE_BF16) return se::dispatch_r<SE_DTYPE_BF16>(R, a, pl.units, pl.nchunk, st);
+  return se::dispatch_r<SE_DTYPE_F32>(R, a, pl.units, pl.nchunk, st);
+}

@@ -1,0 +1,140 @@
+"""Host drivers that run the lifecycle steps of each method through libse, in the order the method takes them.
+
+They stand where the SparseEngine page ("How it works") puts its SparseController hooks: SnapKV selection and
+eviction after the last prompt chunk, Quest's build_decode_selection before decode attention, H2O's score
+accumulation and eviction every decode step; and where the KARA page ("Method" part 3) puts KvLLM's periodic
+compression of trailing blocks. Output buffers are allocated once per driver; every step is a libse call on
+the current stream, and nothing here synchronises.
+"""
+import torch
+
+from . import (SE_COMPACT_EVICT_SLOTS, SE_COMPACT_GATHER, SE_PAGES_BUILD, SE_PAGES_SCORE, SE_SCORE_BIDIR,
+               SE_SCORE_CAUSAL, SE_TOPK_LARGEST, SE_TOPK_SMALLEST, SE_UNIT_PAGE, SE_UNIT_SLOT, se_cache_append,
+               se_compact_evict, se_page_bounds, se_sparse_decode_attn, se_token2chunk, se_topk_select,
+               se_window_score)
+
+
+def _dims(cache):
+    B, G, S = cache.pos_map.shape
+    return B, G, S, cache.k_pool.shape[3]
+
+
+class SnapKVEvent:
+    """Causal window scores -> top-K + protected tail -> whole-cache compaction -> one decode step."""
+
+    def __init__(self, cache, *, wq, protect, keep, scale, status=None):
+        B, G, S, d = _dims(cache)
+        dev = cache.device
+        self.cache, self.wq, self.protect, self.keep, self.scale, self.status = cache, wq, protect, keep, scale, status
+        self.scores = torch.zeros((B, G, S), dtype=torch.float32, device=dev)
+        self.idx = torch.zeros((B, G, keep + protect), dtype=torch.int32, device=dev)
+        self.count = torch.zeros((B, G), dtype=torch.int32, device=dev)
+        self.out = torch.zeros((B, cache.n_q, d), dtype=torch.float32, device=dev)
+
+    def score(self, q_win, q_pos):
+        se_window_score(self.cache, q_win, q_pos, self.scores, scale=self.scale, mode=SE_SCORE_CAUSAL,
+                        n_query=self.wq, status=self.status)
+
+    def select(self):
+        se_topk_select(self.cache, self.scores, self.idx, self.count, mode=SE_TOPK_LARGEST, unit=SE_UNIT_SLOT,
+                       k=self.keep, protect=self.protect, status=self.status)
+
+    def compact(self):
+        se_compact_evict(self.cache, self.idx, self.count, mode=SE_COMPACT_GATHER, status=self.status)
+
+    def decode(self, q_dec):
+        se_sparse_decode_attn(self.cache, q_dec, self.out, scale=self.scale, max_slots=self.keep + self.protect,
+                              status=self.status)
+
+    def run(self, q_win, q_pos, q_dec):
+        self.score(q_win, q_pos)
+        self.select()
+        self.compact()
+        self.decode(q_dec)
+        return self.out
+
+
+class KaraEvent:
+    """Bidirectional scores of the trailing window -> top-K candidates -> Token2Chunk -> trailing compaction."""
+
+    def __init__(self, cache, *, window, protect, n_cand, budget, max_gap, scale, status=None):
+        B, G, S, d = _dims(cache)
+        dev = cache.device
+        self.cache, self.window, self.protect, self.n_cand, self.budget, self.max_gap = (
+            cache, window, protect, n_cand, budget, max_gap)
+        self.scale, self.status = scale, status
+        R = window - protect
+        self.scores = torch.zeros((B, G, R), dtype=torch.float32, device=dev)
+        self.cand = torch.zeros((B, G, n_cand + protect), dtype=torch.int32, device=dev)
+        self.cand_count = torch.zeros((B, G), dtype=torch.int32, device=dev)
+        self.keep = torch.zeros((B, G, max(budget, n_cand) + protect), dtype=torch.int32, device=dev)
+        self.keep_count = torch.zeros((B, G), dtype=torch.int32, device=dev)
+
+    def run(self, q_win):
+        se_window_score(self.cache, q_win, None, self.scores, scale=self.scale, mode=SE_SCORE_BIDIR,
+                        n_query=self.window, window=self.window, protect=self.protect, status=self.status)
+        se_topk_select(self.cache, self.scores, self.cand, self.cand_count, mode=SE_TOPK_LARGEST, unit=SE_UNIT_SLOT,
+                       k=self.n_cand, window=self.window, protect=self.protect, status=self.status)
+        se_token2chunk(self.cache, self.cand, self.cand_count, self.scores, self.keep, self.keep_count,
+                       max_gap=self.max_gap, budget=self.budget, window=self.window, protect=self.protect,
+                       status=self.status)
+        se_compact_evict(self.cache, self.keep, self.keep_count, mode=SE_COMPACT_GATHER, window=self.window,
+                         status=self.status)
+
+
+class DecodeStep:
+    """Append this step's token, then attend over every resident slot (optionally accumulating H2O scores)."""
+
+    def __init__(self, cache, *, scale, accumulate=False, status=None):
+        B, G, S, d = _dims(cache)
+        self.cache, self.scale, self.accumulate, self.status = cache, scale, accumulate, status
+        self.out = torch.zeros((B, cache.n_q, d), dtype=torch.float32, device=cache.device)
+
+    def run(self, k_new, v_new, pos, q):
+        se_cache_append(self.cache, k_new, v_new, pos, status=self.status)
+        se_sparse_decode_attn(self.cache, q, self.out, scale=self.scale, accumulate=self.accumulate,
+                              status=self.status)
+        return self.out
+
+
+class H2OStep(DecodeStep):
+    """Append -> decode with cumulative scores -> evict the lowest score outside the recent positions."""
+
+    def __init__(self, cache, *, scale, budget, recent, status=None):
+        super().__init__(cache, scale=scale, accumulate=True, status=status)
+        B, G, S, d = _dims(cache)
+        self.budget, self.recent = budget, recent
+        self.evict = torch.zeros((B, G, 1), dtype=torch.int32, device=cache.device)
+        self.evict_count = torch.zeros((B, G), dtype=torch.int32, device=cache.device)
+
+    def run(self, k_new, v_new, pos, q):
+        super().run(k_new, v_new, pos, q)
+        se_topk_select(self.cache, self.cache.cum_score, self.evict, self.evict_count, mode=SE_TOPK_SMALLEST,
+                       unit=SE_UNIT_SLOT, k=1, budget=self.budget, recent=self.recent, status=self.status)
+        se_compact_evict(self.cache, self.evict, self.evict_count, mode=SE_COMPACT_EVICT_SLOTS, status=self.status)
+        return self.out
+
+
+class QuestStep:
+    """Page bounds of the cache (built once) -> page scores -> top pages + first/last -> decode over them."""
+
+    def __init__(self, cache, *, top_pages, scale, status=None):
+        B, G, S, d = _dims(cache)
+        dev = cache.device
+        self.cache, self.top_pages, self.scale, self.status = cache, top_pages, scale, status
+        nb = cache.block_table.shape[1]
+        self.page_scores = torch.zeros((B, G, nb), dtype=torch.float32, device=dev)
+        self.pages = torch.zeros((B, G, top_pages + 2), dtype=torch.int32, device=dev)
+        self.count = torch.zeros((B, G), dtype=torch.int32, device=dev)
+        self.out = torch.zeros((B, cache.n_q, d), dtype=torch.float32, device=dev)
+
+    def build(self):
+        se_page_bounds(self.cache, SE_PAGES_BUILD, status=self.status)
+
+    def run(self, q):
+        se_page_bounds(self.cache, SE_PAGES_SCORE, q, self.page_scores, status=self.status)
+        se_topk_select(self.cache, self.page_scores, self.pages, self.count, mode=SE_TOPK_LARGEST, unit=SE_UNIT_PAGE,
+                       k=self.top_pages, forced_ends=1, status=self.status)
+        se_sparse_decode_attn(self.cache, q, self.out, scale=self.scale, sel_pages=self.pages, sel_count=self.count,
+                              status=self.status)
+        return self.out

@@ -1,0 +1,78 @@
+"""The C-ABI library loads and exports every entry point include/se.h declares; host-side validation answers
+without touching a device (no compute calls here)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from sparse_decode_attention_se_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_symbols():
+    text = open(os.path.join(ROOT, "include", "se.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(se_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    names = declared_symbols()
+    assert len(names) >= 14
+    for name in names:
+        assert hasattr(lib, name), name
+    # the binding declares the same set
+    assert set(names) == set(_lib.EXPORTS)
+
+
+def test_python_binding_names_match_c():
+    import sparse_decode_attention_se_amd as se
+
+    for name in ("se_window_score", "se_topk_select", "se_token2chunk", "se_compact_evict", "se_cache_append",
+                 "se_page_bounds", "se_sparse_decode_attn", "se_status_read", "se_version"):
+        assert callable(getattr(se, name))
+
+
+def test_host_validation_without_device():
+    lib = _lib.load()
+    assert lib.se_version().decode().startswith("libse")
+    assert lib.se_error_string(_lib.SE_ERR_NULL)
+    assert lib.se_error_string(_lib.SE_DEV_INDEX).startswith(b"device")
+    # null descriptor / params: rejected before any HIP call
+    assert lib.se_window_score(None, None, None, None, None, None, None, 0, None) == _lib.SE_ERR_NULL
+    assert lib.se_sparse_decode_attn(None, None, None, None, None, None, None, None, 0, None) == _lib.SE_ERR_NULL
+    c = _lib.se_cache_t()
+    c.k_pool = c.v_pool = c.block_table = c.pos_map = c.ctx_len = c.n_slots = 16  # fake non-null, never touched
+    c.B, c.n_kv, c.n_q, c.d, c.page, c.num_blocks, c.max_blocks, c.dtype = 1, 2, 3, 128, 16, 4, 4, 1
+    p = _lib.se_decode_params_t(0.1, 0, 0, 0, 0)
+    # n_q not a multiple of n_kv
+    assert lib.se_sparse_decode_attn(C.byref(c), 16, None, None, C.byref(p), 16, None, None, 0, None) == \
+        _lib.SE_ERR_SHAPE
+    c.n_q = 8
+    c.d = 96  # unsupported head dim
+    assert lib.se_sparse_decode_attn(C.byref(c), 16, None, None, C.byref(p), 16, None, None, 0, None) == \
+        _lib.SE_ERR_DTYPE
+    c.d = 128
+    # workspace missing
+    assert lib.se_sparse_decode_attn(C.byref(c), 16, None, None, C.byref(p), 16, None, None, 0, None) == \
+        _lib.SE_ERR_WORKSPACE
+    tp = _lib.se_topk_params_t(0, 0, -1, 0, 0, 0, 0, 0, 64, 64)
+    assert lib.se_topk_select(C.byref(c), 16, C.byref(tp), 16, 16, None, None, 0, None) == _lib.SE_ERR_PARAM
+    wp = _lib.se_window_params_t(0.1, 1, 512, 512, 600, 512)  # protect > window
+    assert lib.se_window_score(C.byref(c), 16, None, C.byref(wp), 16, None, None, 0, None) == _lib.SE_ERR_PARAM
+    cp = _lib.se_compact_params_t(7, 0, 8)  # unknown mode
+    c.free_blocks = c.free_top = 16
+    assert lib.se_compact_evict(C.byref(c), 16, 16, C.byref(cp), None, None, 0, None) == _lib.SE_ERR_PARAM
+
+
+def test_workspace_sizes_are_host_only():
+    lib = _lib.load()
+    c = _lib.se_cache_t()
+    c.k_pool = c.v_pool = c.block_table = c.pos_map = c.ctx_len = c.n_slots = 16
+    c.B, c.n_kv, c.n_q, c.d, c.page, c.num_blocks, c.max_blocks, c.dtype = 8, 8, 32, 128, 16, 16384, 2048, 1
+    p = _lib.se_decode_params_t(0.1, 0, 0, 2048, 1)
+    assert lib.se_sparse_decode_attn_workspace_size(C.byref(c), C.byref(p), 0) > 0
+    wp = _lib.se_window_params_t(0.1, 0, 64, 0, 0, 32768)
+    assert lib.se_window_score_workspace_size(C.byref(c), C.byref(wp)) > 0

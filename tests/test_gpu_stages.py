@@ -1,0 +1,348 @@
+"""Stage-isolated parity: each libse call against the oracle on the same seeded inputs (small sizes that still
+span several tiles and a ragged tail). Index, map and list results are bit-exact; floats within the stated
+tolerances (scores 1e-3 relative with a 1e-6 row-mass floor, decode outputs 2e-3 absolute)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_decode_attention_se_amd as se
+import workloads as W
+from gpu_util import (DEV, assert_scores_close, compare_cache, i32, lists_from, status_word, storage_tensor,
+                      to_device)
+
+pytestmark = pytest.mark.gpu
+
+
+def banner(name):
+    print(f"\n[case] {name}", flush=True)
+
+
+def snap_inputs(B=2, hq=8, hkv=2, d=128, N=1500, wq=64, protect=64, keep=200, dtype="bf16", seed=0, spikes=0.04):
+    cfg = W.SnapKV("t", B=B, hq=hq, hkv=hkv, d=d, N=N, wq=wq, protect=protect, keep=keep, dtype=dtype,
+                   spike_frac=spikes)
+    return W.gen_snapkv(cfg, seed=seed, threads=4)
+
+
+def punch_holes(state, frac, seed, slot_cap=8):
+    """Evict a few slots (oracle semantics) so the cache has free slots on its slot stacks."""
+    rs = np.random.default_rng(seed)
+    B, G = state.n_slots.shape
+    ev = [[np.sort(rs.choice(int(state.n_slots[b, g]), size=min(slot_cap, max(1, int(frac * state.n_slots[b, g]))),
+                             replace=False)).astype(np.int32) for g in range(G)] for b in range(B)]
+    return oracle.evict_slots(state, ev)
+
+
+# ------------------------------------------------------------------ decode --------------------------------------
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64)])
+def test_decode_all_slots(dtype, d):
+    banner(f"decode all slots {dtype}")
+    inp = snap_inputs(d=d, dtype=dtype, N=777)
+    st = punch_holes(inp["cache"], 0.01, 1)
+    ref, _ = oracle.decode_attn(st, inp["q_dec"], inp["scale"])
+    dc = to_device(st, 8)
+    out = torch.empty((2, 8, d), dtype=torch.float32, device=DEV)
+    status = status_word()
+    se.se_sparse_decode_attn(dc, storage_tensor(inp["q_dec"], dtype), out, scale=inp["scale"], status=status)
+    assert se.se_status_read(status) == 0
+    np.testing.assert_allclose(out.cpu().numpy(), ref, atol=2e-3, rtol=0)
+
+
+def test_decode_max_slots_bound_and_pages():
+    banner("decode page lists")
+    inp = snap_inputs(N=1000)
+    st = inp["cache"]
+    rs = np.random.default_rng(3)
+    n_pages = -(-1000 // 16)
+    pages = [[np.sort(rs.choice(n_pages, size=int(rs.integers(1, 20)), replace=False)).astype(np.int32)
+              for g in range(2)] for b in range(2)]
+    pages[0][0] = np.array([n_pages - 1], np.int32)  # ragged last page only
+    ref, _ = oracle.decode_attn(st, inp["q_dec"], inp["scale"], pages=pages)
+    sel, cnt = W.pack_lists(pages, 24)
+    dc = to_device(st, 8)
+    out = torch.empty((2, 8, 128), dtype=torch.float32, device=DEV)
+    status = status_word()
+    se.se_sparse_decode_attn(dc, storage_tensor(inp["q_dec"], "bf16"), out, scale=inp["scale"], sel_pages=i32(sel),
+                             sel_count=i32(cnt), status=status)
+    assert se.se_status_read(status) == 0
+    np.testing.assert_allclose(out.cpu().numpy(), ref, atol=2e-3, rtol=0)
+    # all pages selected == dense attention
+    allp = [[np.arange(n_pages, dtype=np.int32)] * 2] * 2
+    sel, cnt = W.pack_lists(allp, n_pages)
+    se.se_sparse_decode_attn(dc, storage_tensor(inp["q_dec"], "bf16"), out, scale=inp["scale"], sel_pages=i32(sel),
+                             sel_count=i32(cnt), status=status)
+    dense, _ = oracle.decode_attn(st, inp["q_dec"], inp["scale"])
+    np.testing.assert_allclose(out.cpu().numpy(), dense, atol=2e-3, rtol=0)
+    # an n_slots bound below the real size is reported
+    se.se_sparse_decode_attn(dc, storage_tensor(inp["q_dec"], "bf16"), out, scale=inp["scale"], max_slots=512,
+                             status=status)
+    assert se.se_status_read(status) & se.SE_DEV_CAPACITY
+
+
+def test_decode_accumulates_cumulative_scores():
+    banner("decode cum")
+    cfg = W.H2O("t", B=3, hq=8, hkv=2, d=128, N=900, budget=900, recent=32, steps=2, zipf=1.1)
+    inp = W.gen_h2o(cfg, seed=5, threads=4)
+    st = punch_holes(inp["cache"], 0.005, 2)
+    st.cum_score[:] = np.random.default_rng(0).random(st.cum_score.shape).astype(np.float32)
+    ref_out, ref_cum = oracle.decode_attn(st, inp["q_steps"][0], inp["scale"], accumulate=True)
+    dc = to_device(st, 8)
+    out = torch.empty((3, 8, 128), dtype=torch.float32, device=DEV)
+    se.se_sparse_decode_attn(dc, storage_tensor(inp["q_steps"][0], "bf16"), out, scale=inp["scale"],
+                             accumulate=True)
+    np.testing.assert_allclose(out.cpu().numpy(), ref_out, atol=2e-3, rtol=0)
+    cum = dc.cum_score.cpu().numpy()
+    for b in range(3):
+        for g in range(2):
+            n = int(st.n_slots[b, g])
+            res = st.pos_map[b, g, :n] >= 0
+            np.testing.assert_allclose(cum[b, g, :n][res], ref_cum[b, g, :n][res], rtol=1e-5, atol=1e-7)
+            np.testing.assert_array_equal(cum[b, g, :n][~res], st.cum_score[b, g, :n][~res])
+
+
+# ------------------------------------------------------------------ window scores -------------------------------
+@pytest.mark.parametrize("N", [1500, 700])
+def test_window_score_causal_bf16(N):
+    banner(f"window causal bf16 N={N}")
+    inp = snap_inputs(N=N)
+    st = punch_holes(inp["cache"], 0.002, 4)
+    ref = oracle.window_score_causal(st, inp["q_win"], inp["q_pos"], inp["scale"])
+    dc = to_device(st, 8)
+    S = st.pos_map.shape[2]
+    scores = torch.zeros((2, 2, S), dtype=torch.float32, device=DEV)
+    se.se_window_score(dc, storage_tensor(inp["q_win"], "bf16"), i32(inp["q_pos"]), scores, scale=inp["scale"],
+                       mode=se.SE_SCORE_CAUSAL, n_query=64)
+    got = scores.cpu().numpy()
+    assert_scores_close(got[:, :, :N], ref[:, :, :N], mass=np.full((2, 2), 4 * 64.0))
+    np.testing.assert_allclose(got.sum(axis=2), 256.0, rtol=1e-5)
+
+
+def test_window_score_causal_f32_c0():
+    banner("window causal f32 (tiny workload, full size)")
+    inp = W.gen_snapkv(W.C0, seed=0, threads=1)
+    st = inp["cache"]
+    ref = oracle.window_score_causal(st, inp["q_win"], inp["q_pos"], inp["scale"])
+    dc = to_device(st, 8)
+    scores = torch.zeros((1, 2, 1024), dtype=torch.float32, device=DEV)
+    se.se_window_score(dc, storage_tensor(inp["q_win"], "f32"), i32(inp["q_pos"]), scores, scale=inp["scale"],
+                       mode=se.SE_SCORE_CAUSAL, n_query=32)
+    assert_scores_close(scores.cpu().numpy(), ref, mass=np.full((1, 2), 4 * 32.0))
+
+
+def test_window_score_bidir():
+    banner("window bidir")
+    cfg = W.Kara("t", B=2, hq=8, hkv=2, d=128, N=700, window=512, protect=64, cand_frac=0.2, budget_frac=0.2,
+                 max_gap=8, period=4, events=1, rho=0.9)
+    inp = W.gen_kara(cfg, seed=3, threads=4)
+    st = inp["cache"]
+    from oracle.pipelines import kara_window_queries
+
+    qw = kara_window_queries(inp, st)
+    ref = oracle.window_score_bidir(st, qw, inp["scale"], 512, 64)
+    dc = to_device(st, 8)
+    scores = torch.zeros((2, 2, 448), dtype=torch.float32, device=DEV)
+    se.se_window_score(dc, storage_tensor(qw, "bf16"), None, scores, scale=inp["scale"], mode=se.SE_SCORE_BIDIR,
+                       n_query=512, window=512, protect=64)
+    got = scores.cpu().numpy()
+    assert_scores_close(got, ref, mass=np.full((2, 2), 4 * 512.0))
+    np.testing.assert_allclose(got.sum(axis=2), 2048.0, rtol=1e-5)
+
+
+# ------------------------------------------------------------------ top-K -----------------------------------------
+def _topk_cache(B=2, G=3, N=3000, page=16):
+    c = W.empty_cache(B, G, 128, page, -(-N // page), B * -(-N // page), "bf16")
+    W.layout_initial(c, N)
+    return c
+
+
+@pytest.mark.parametrize("levels,k,protect", [(0, 300, 64), (50, 300, 64), (7, 1000, 0), (0, 2936, 64),
+                                              (0, 0, 16)])
+def test_topk_largest_slots_exact(levels, k, protect):
+    banner(f"topk slots levels={levels} k={k}")
+    c = _topk_cache()
+    c.n_slots[1, 2] = 2500  # ragged
+    c.ctx_len[1, 2] = 2500
+    c.pos_map[0, 1, 100:110] = -1
+    scores = W.gen_scores(7, (2, 3, c.pos_map.shape[2]), levels=levels, tie_frac=0.05)
+    ref = oracle.topk_largest(scores, c, k, protect=protect)
+    dc = to_device(c, 12)
+    idx = torch.full((2, 3, 3000), -7, dtype=torch.int32, device=DEV)
+    cnt = torch.zeros((2, 3), dtype=torch.int32, device=DEV)
+    se.se_topk_select(dc, torch.from_numpy(scores).to(DEV), idx, cnt, mode=se.SE_TOPK_LARGEST, unit=se.SE_UNIT_SLOT,
+                      k=k, protect=protect)
+    got = lists_from(idx, cnt)
+    for b in range(2):
+        for g in range(3):
+            assert got[b][g].tolist() == ref[b][g].tolist(), (b, g)
+
+
+def test_topk_window_and_pages_and_smallest_exact():
+    banner("topk window/pages/smallest")
+    c = _topk_cache(N=2000)
+    scores = W.gen_scores(8, (2, 3, 448), levels=100)
+    ref = oracle.topk_largest(scores, c, 89, window=512, protect=64)
+    dc = to_device(c, 12)
+    idx = torch.zeros((2, 3, 160), dtype=torch.int32, device=DEV)
+    cnt = torch.zeros((2, 3), dtype=torch.int32, device=DEV)
+    se.se_topk_select(dc, torch.from_numpy(scores).to(DEV), idx, cnt, mode=se.SE_TOPK_LARGEST, unit=se.SE_UNIT_SLOT,
+                      k=89, window=512, protect=64)
+    assert [x.tolist() for r in lists_from(idx, cnt) for x in r] == [x.tolist() for r in ref for x in r]
+    # pages with forced ends
+    pscores = W.gen_scores(9, (2, 3, c.max_blocks), levels=30)
+    ref = oracle.topk_largest(pscores, c, 40, unit="page", forced_ends=True)
+    idx = torch.zeros((2, 3, 42), dtype=torch.int32, device=DEV)
+    se.se_topk_select(dc, torch.from_numpy(pscores).to(DEV), idx, cnt, mode=se.SE_TOPK_LARGEST, unit=se.SE_UNIT_PAGE,
+                      k=40, forced_ends=1)
+    assert [x.tolist() for r in lists_from(idx, cnt) for x in r] == [x.tolist() for r in ref for x in r]
+    # smallest with holes, ties and the recent window
+    c2 = punch_holes(c, 0.001, 9)
+    cum = W.gen_scores(10, (2, 3, c2.pos_map.shape[2]), levels=20)
+    for budget in (1990, 1000, 5000):
+        ref = oracle.topk_smallest(cum, c2, 3, budget=budget, recent=256)
+        dc2 = to_device(c2, 12)
+        idx = torch.zeros((2, 3, 3), dtype=torch.int32, device=DEV)
+        se.se_topk_select(dc2, torch.from_numpy(cum).to(DEV), idx, cnt, mode=se.SE_TOPK_SMALLEST,
+                          unit=se.SE_UNIT_SLOT, k=3, budget=budget, recent=256)
+        assert [x.tolist() for r in lists_from(idx, cnt) for x in r] == [x.tolist() for r in ref for x in r]
+
+
+# ------------------------------------------------------------------ Token2Chunk -----------------------------------
+def test_token2chunk_exact():
+    banner("token2chunk")
+    c = _topk_cache(B=4, G=2, N=1200)
+    scores = W.gen_scores(11, (4, 2, 448), levels=64)  # coarse levels -> tied priorities
+    cand = oracle.topk_largest(scores, c, 89, window=512, protect=64)
+    for budget in (89, 102, 140, 400):
+        ref = oracle.token2chunk(cand, scores, c, max_gap=8, budget=budget, window=512, protect=64)
+        dc = to_device(c, 8)
+        idx, cnt = W.pack_lists(cand, 160)
+        out = torch.full((4, 2, 470), -1, dtype=torch.int32, device=DEV)
+        ocnt = torch.zeros((4, 2), dtype=torch.int32, device=DEV)
+        status = status_word()
+        se.se_token2chunk(dc, i32(idx), i32(cnt), torch.from_numpy(scores).to(DEV), out, ocnt, max_gap=8,
+                          budget=budget, window=512, protect=64, status=status)
+        assert se.se_status_read(status) == 0
+        got = lists_from(out, ocnt)
+        for b in range(4):
+            for g in range(2):
+                assert got[b][g].tolist() == ref[b][g].tolist(), (budget, b, g)
+
+
+# ------------------------------------------------------------------ compaction / append ---------------------------
+@pytest.mark.parametrize("pattern", ["random", "prefix", "shift1", "tail"])
+def test_compact_gather_whole_bit_exact(pattern):
+    banner(f"compact whole {pattern}")
+    inp = snap_inputs(B=3, N=1337, d=128)
+    st = inp["cache"]
+    counts = np.array([[200, 1000], [0, 64], [1300, 17]], np.int32)
+    keep = W.gen_keep_sets(5, st.n_slots, counts, pattern=pattern)
+    ref = oracle.compact_gather(st, keep)
+    dc = to_device(st, 8)
+    idx, cnt = W.pack_lists(keep, 1337)
+    status = status_word()
+    se.se_compact_evict(dc, i32(idx), i32(cnt), mode=se.SE_COMPACT_GATHER, status=status)
+    assert se.se_status_read(status) == 0
+    compare_cache(dc.to_numpy(), ref)
+
+
+def test_compact_gather_trailing_with_holes_and_cum():
+    banner("compact trailing")
+    cfg = W.H2O("t", B=2, hq=8, hkv=2, d=128, N=1100, budget=2000, recent=8, steps=1, zipf=1.1)
+    inp = W.gen_h2o(cfg, seed=2, threads=4)
+    st = inp["cache"]
+    st.cum_score[:] = np.random.default_rng(1).random(st.cum_score.shape).astype(np.float32)
+    st = punch_holes(st, 0.004, 3)  # some holes inside and before the window
+    lo = st.n_slots - 512
+    keep = []
+    for b in range(2):
+        row = []
+        for g in range(2):
+            n = int(st.n_slots[b, g])
+            res = [s for s in range(n - 512, n) if st.pos_map[b, g, s] >= 0]
+            rs = np.random.default_rng(b * 2 + g)
+            row.append(np.sort(rs.choice(res, size=166, replace=False)).astype(np.int32))
+        keep.append(row)
+    ref = oracle.compact_gather(st, keep, window=512)
+    dc = to_device(st, 8)
+    idx, cnt = W.pack_lists(keep, 170)
+    status = status_word()
+    se.se_compact_evict(dc, i32(idx), i32(cnt), mode=se.SE_COMPACT_GATHER, window=512, status=status)
+    assert se.se_status_read(status) == 0
+    compare_cache(dc.to_numpy(), ref)
+
+
+def test_evict_append_sequence_bit_exact():
+    banner("evict/append")
+    cfg = W.H2O("t", B=3, hq=8, hkv=2, d=128, N=47, budget=100, recent=4, steps=40, zipf=1.1)
+    inp = W.gen_h2o(cfg, seed=4, threads=2)
+    st = inp["cache"]
+    ref = st.copy()
+    dc = to_device(st, 8)
+    status = status_word()
+    rs = np.random.default_rng(8)
+    for step in range(40):
+        if step % 3 == 0:  # evict one or two resident slots per head
+            ev = []
+            for b in range(3):
+                row = []
+                for g in range(2):
+                    res = np.where(ref.pos_map[b, g, :ref.n_slots[b, g]] >= 0)[0]
+                    row.append(np.sort(rs.choice(res, size=1 + (b + g + step) % 2, replace=False)).astype(np.int32))
+                ev.append(row)
+            ref = oracle.evict_slots(ref, ev)
+            idx, cnt = W.pack_lists(ev, 2)
+            se.se_compact_evict(dc, i32(idx), i32(cnt), mode=se.SE_COMPACT_EVICT_SLOTS, status=status)
+        pos = np.full((3,), 47 + step, np.int32)
+        ref, _ = oracle.cache_append(ref, inp["k_new"][step], inp["v_new"][step], pos)
+        se.se_cache_append(dc, storage_tensor(inp["k_new"][step], "bf16"), storage_tensor(inp["v_new"][step], "bf16"),
+                           i32(pos), status=status)
+    assert se.se_status_read(status) == 0
+    compare_cache(dc.to_numpy(), ref)
+
+
+def test_append_capacity_is_all_or_nothing():
+    banner("append capacity")
+    c = W.empty_cache(2, 2, 128, 16, 4, 8, "bf16")
+    W.layout_initial(c, 64)  # 4 blocks each: no spare block
+    dc = to_device(c, 8)
+    before = dc.to_numpy()
+    status = status_word()
+    z = torch.zeros((2, 2, 128), dtype=torch.bfloat16, device=DEV)
+    se.se_cache_append(dc, z, z, i32([64, 64]), status=status)
+    assert se.se_status_read(status) & se.SE_DEV_CAPACITY
+    after = dc.to_numpy()
+    for f in before:
+        np.testing.assert_array_equal(after[f], before[f])
+
+
+def test_compact_rejects_bad_indices():
+    banner("compact bad indices")
+    inp = snap_inputs(B=1, N=300)
+    dc = to_device(inp["cache"], 8)
+    idx, cnt = W.pack_lists([[np.array([5, 3, 9], np.int32), np.array([1, 400], np.int32)]], 4)
+    status = status_word()
+    se.se_compact_evict(dc, i32(idx), i32(cnt), mode=se.SE_COMPACT_GATHER, status=status)
+    assert se.se_status_read(status) & se.SE_DEV_INDEX
+
+
+# ------------------------------------------------------------------ page bounds -----------------------------------
+def test_page_bounds_build_exact_and_score():
+    banner("page bounds")
+    cfg = W.Quest("t", B=2, hq=8, hkv=2, d=128, N=2000, top_pages=16, shift_frac=0.05, shift=2.0)
+    inp = W.gen_quest(cfg, seed=6, threads=4)
+    st = punch_holes(inp["cache"], 0.003, 5)
+    meta = oracle.page_bounds_build(st)
+    dc = to_device(st, 8)
+    se.se_page_bounds(dc, se.SE_PAGES_BUILD)
+    got = dc.page_meta.view(torch.int16).cpu().numpy().view(np.uint16)
+    np.testing.assert_array_equal(got, meta)
+    u = oracle.page_bounds_score(st, meta, inp["q_dec"])
+    ps = torch.full((2, 2, st.max_blocks), 7.0, dtype=torch.float32, device=DEV)
+    se.se_page_bounds(dc, se.SE_PAGES_SCORE, storage_tensor(inp["q_dec"], "bf16"), ps)
+    n_pages = -(-2000 // 16)
+    g = ps.cpu().numpy()[:, :, :n_pages]
+    r = u[:, :, :n_pages]
+    assert np.all(np.isfinite(r))
+    np.testing.assert_allclose(g, r, rtol=1e-3, atol=1e-3)
