@@ -17,9 +17,12 @@
 namespace se {
 namespace {
 
-constexpr int kMoveRows = 64;   // output rows per workgroup tile
-constexpr int kMoveThreads = 256;
+constexpr int kMoveRowsMax = 256;  // output rows per workgroup tile (rows <= 256 B; 128 rows for 512-B rows)
+constexpr int kMoveThreads = 1024;
+constexpr int kMovePer = 4;        // 16-byte K and V chunks held per thread in a tile
 constexpr int kMaxBitmapWords = 2048;  // hazard bitmap: 65536 outputs per unit
+constexpr int kIdxLds = 4096;          // retained-index lists up to this length are searched in LDS
+constexpr int kWindowWords = 256;      // hazard outputs are listed 8192 at a time
 
 struct GatherArgs {
   char *k, *v;
@@ -47,7 +50,7 @@ SE_DEV int lower_bound_pred(int cnt, F pred) {
   return lo;
 }
 
-SE_DEV UnitPlan plan_unit(const GatherArgs &a, int unit) {
+SE_DEV UnitPlan plan_unit(const GatherArgs &a, int unit, const int32_t *s) {
   UnitPlan u;
   const int cap = a.max_blocks * a.page;
   u.n = a.n_slots[unit];
@@ -59,7 +62,6 @@ SE_DEV UnitPlan plan_unit(const GatherArgs &a, int unit) {
     u.i0 = u.h = 0;
     return u;
   }
-  const int32_t *s = a.idx + (int64_t)unit * a.idx_stride;
   const int lim = u.w0 + u.cnt, w0 = u.w0;
   u.h = lower_bound_pred(u.cnt, [&](int j) { return s[j] >= lim; });
   u.i0 = lower_bound_pred(u.cnt, [&](int j) { return s[j] - j > w0; });
@@ -77,66 +79,77 @@ SE_DEV bool is_hazard_dest(const int32_t *s, const UnitPlan &u, int j) {
   return lo < u.h && s[lo] == want;
 }
 
-// copy `nrows` rows (row r: source slot src[r] -> dest slot dst[r], -1 = skip) of one unit; reads complete
-// before any write
+// copy `nrows` rows (row r: source slot src[r] -> dest slot dst[r], -1 = skip) of one unit; every read of the
+// tile completes before its first write. nrows * row_bytes / 16 <= kMovePer * kMoveThreads.
 SE_DEV void move_rows(const GatherArgs &a, int b, int g, int unit, const int *src, const int *dst, int nrows) {
   const int cpr = a.row_bytes / 16;
   const int total = nrows * cpr;
   const int32_t *bt = a.bt + (int64_t)b * a.max_blocks;
   int32_t *pos = a.pos + (int64_t)unit * a.max_blocks * a.page;
   float *cum = a.cum ? a.cum + (int64_t)unit * a.max_blocks * a.page : nullptr;
-  constexpr int kPer = kMoveRows * 32 / kMoveThreads;  // up to 32 chunks per row (512-byte rows)
+  constexpr int kPer = kMovePer;
   u32x4 kbuf[kPer], vbuf[kPer];
   int32_t pbuf[kPer];
   float cbuf[kPer];
+  int64_t doff[kPer];
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
-    int t = threadIdx.x + i * kMoveThreads;
-    if (t < total && src[t / cpr] >= 0 && blk_ok(bt[src[t / cpr] / a.page], a.num_blocks) &&
-        blk_ok(bt[dst[t / cpr] / a.page], a.num_blocks)) {
-      int r = t / cpr, ch = t % cpr, ss = src[r];
-      int64_t off = (((int64_t)bt[ss / a.page] * a.n_kv + g) * a.page + ss % a.page) * a.row_bytes + ch * 16;
-      kbuf[i] = ld16(a.k + off);
-      vbuf[i] = ld16(a.v + off);
-      if (ch == 0) {
-        pbuf[i] = pos[ss];
-        if (cum) cbuf[i] = cum[ss];
-      }
+    const int t = threadIdx.x + i * kMoveThreads;
+    doff[i] = -1;
+    if (t >= total) continue;
+    const int r = t / cpr, ch = t % cpr, ss = src[r], ds = dst[r];
+    if (ss < 0) continue;
+    const int sb = bt[ss / a.page], db = bt[ds / a.page];
+    if (!blk_ok(sb, a.num_blocks) || !blk_ok(db, a.num_blocks)) continue;
+    const int64_t soff = (((int64_t)sb * a.n_kv + g) * a.page + ss % a.page) * a.row_bytes + ch * 16;
+    doff[i] = (((int64_t)db * a.n_kv + g) * a.page + ds % a.page) * a.row_bytes + ch * 16;
+    kbuf[i] = ld16(a.k + soff);
+    vbuf[i] = ld16(a.v + soff);
+    if (ch == 0) {
+      pbuf[i] = pos[ss];
+      if (cum) cbuf[i] = cum[ss];
     }
   }
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
-    int t = threadIdx.x + i * kMoveThreads;
-    if (t < total && src[t / cpr] >= 0 && blk_ok(bt[src[t / cpr] / a.page], a.num_blocks) &&
-        blk_ok(bt[dst[t / cpr] / a.page], a.num_blocks)) {
-      int r = t / cpr, ch = t % cpr, ds = dst[r];
-      int64_t off = (((int64_t)bt[ds / a.page] * a.n_kv + g) * a.page + ds % a.page) * a.row_bytes + ch * 16;
-      st16(a.k + off, kbuf[i]);
-      st16(a.v + off, vbuf[i]);
-      if (ch == 0) {
-        pos[ds] = pbuf[i];
-        if (cum) cum[ds] = cbuf[i];
-      }
+    if (doff[i] < 0) continue;
+    const int t = threadIdx.x + i * kMoveThreads;
+    const int r = t / cpr, ch = t % cpr;
+    st16(a.k + doff[i], kbuf[i]);
+    st16(a.v + doff[i], vbuf[i]);
+    if (ch == 0) {
+      pos[dst[r]] = pbuf[i];
+      if (cum) cum[dst[r]] = cbuf[i];
     }
   }
   __syncthreads();
 }
 
+template <int kMoveRows>
 __global__ __launch_bounds__(kMoveThreads) void gather_move(GatherArgs a) {
   const int unit = blockIdx.y;
   const int b = unit / a.n_kv, g = unit % a.n_kv;
   __shared__ UnitPlan s_plan;
-  __shared__ int s_src[kMoveRows], s_dst[kMoveRows];
+  __shared__ int s_idx[kIdxLds];
+  __shared__ int s_src[kMoveRowsMax], s_dst[kMoveRowsMax];
   __shared__ uint32_t s_bits[kMaxBitmapWords];
-  if (threadIdx.x == 0) s_plan = plan_unit(a, unit);
+  __shared__ int s_list[kWindowWords * 32];
+  __shared__ int s_scan[kWindowWords];
+  const int32_t *gidx = a.idx + (int64_t)unit * a.idx_stride;
+  const int cnt_raw = a.count[unit];
+  const bool in_lds = cnt_raw >= 0 && cnt_raw <= kIdxLds && cnt_raw <= a.idx_stride;
+  if (in_lds)
+    for (int j = threadIdx.x; j < cnt_raw; j += kMoveThreads) s_idx[j] = gidx[j];
+  __syncthreads();
+  const int32_t *s = in_lds ? s_idx : gidx;
+  if (threadIdx.x == 0) s_plan = plan_unit(a, unit, s);
   __syncthreads();
   const UnitPlan u = s_plan;
   if (!u.ok) {
     if (blockIdx.x == 0 && threadIdx.x == 0) raise(a.status, SE_DEV_INDEX);
     return;
   }
-  const int32_t *s = a.idx + (int64_t)unit * a.idx_stride;
   const int32_t *pos = a.pos + (int64_t)unit * a.max_blocks * a.page;
   const int lim = u.w0 + u.cnt;
 
@@ -160,7 +173,8 @@ __global__ __launch_bounds__(kMoveThreads) void gather_move(GatherArgs a) {
     return;
   }
 
-  // workgroup 0: validate the prefix and move the hazard set S in ascending tiles
+  // workgroup 0: validate the prefix, mark the hazard set S = readers [i0, h) and their destinations, then move
+  // S in ascending order, a tile of up to kMoveRows outputs at a time (reads of a tile before its writes)
   const int words = (u.cnt + 31) / 32;
   for (int i = threadIdx.x; i < words; i += kMoveThreads) s_bits[i] = 0;
   __syncthreads();
@@ -178,18 +192,38 @@ __global__ __launch_bounds__(kMoveThreads) void gather_move(GatherArgs a) {
     }
   }
   __syncthreads();
-  for (int t0 = (u.i0 / kMoveRows) * kMoveRows; t0 < u.cnt; t0 += kMoveRows) {
-    const uint32_t w_lo = s_bits[t0 >> 5], w_hi = (t0 + 32 < u.cnt) ? s_bits[(t0 >> 5) + 1] : 0u;
-    if ((w_lo | w_hi) == 0) continue;  // uniform across the workgroup
-    if (threadIdx.x < kMoveRows) {
-      int j = t0 + threadIdx.x;
-      bool mark = j < u.cnt && ((threadIdx.x < 32 ? w_lo : w_hi) >> (threadIdx.x & 31)) & 1u;
-      int sj = mark ? s[j] : -1;
-      s_src[threadIdx.x] = (mark && sj >= u.w0 && sj < u.n) ? sj : -1;
-      s_dst[threadIdx.x] = u.w0 + j;
+  for (int wbase = u.i0 >> 5; wbase < words; wbase += kWindowWords) {
+    // list the marked outputs of this window of words in ascending order
+    const int wi = wbase + threadIdx.x;
+    const uint32_t bits = (threadIdx.x < kWindowWords && wi < words) ? s_bits[wi] : 0u;
+    if (threadIdx.x < kWindowWords) s_scan[threadIdx.x] = __popc(bits);
+    __syncthreads();
+    for (int off = 1; off < kWindowWords; off <<= 1) {
+      int x = (threadIdx.x < kWindowWords && threadIdx.x >= off) ? s_scan[threadIdx.x - off] : 0;
+      __syncthreads();
+      if (threadIdx.x < kWindowWords) s_scan[threadIdx.x] += x;
+      __syncthreads();
+    }
+    const int nlist = s_scan[kWindowWords - 1];
+    if (threadIdx.x < kWindowWords) {
+      int o = s_scan[threadIdx.x] - __popc(bits);
+      for (uint32_t x = bits; x; x &= x - 1) s_list[o++] = wi * 32 + __ffs(x) - 1;
     }
     __syncthreads();
-    move_rows(a, b, g, unit, s_src, s_dst, kMoveRows);
+    for (int t0 = 0; t0 < nlist; t0 += kMoveRows) {
+      if (threadIdx.x < kMoveRows) {
+        int src = -1, j = 0;
+        if (t0 + threadIdx.x < nlist) {
+          j = s_list[t0 + threadIdx.x];
+          int sj = s[j];
+          if (sj >= u.w0 && sj < u.n) src = sj;
+        }
+        s_src[threadIdx.x] = src;
+        s_dst[threadIdx.x] = u.w0 + j;
+      }
+      __syncthreads();
+      move_rows(a, b, g, unit, s_src, s_dst, kMoveRows);
+    }
   }
 }
 
@@ -203,14 +237,20 @@ struct FinalArgs {
 constexpr int kFinalThreads = 1024;
 constexpr int kMaxSeq = 4096;
 
-// single workgroup: per-(b,g) counters and slot stacks, then per-sequence block freeing in sequence order
+// single workgroup: per-(b,g) counters and slot stacks, then the blocks past each sequence's new extent go to
+// the free stack in order of sequence, then logical block
 __global__ __launch_bounds__(kFinalThreads) void gather_finalize(FinalArgs a) {
   __shared__ int s_new_ext[kMaxSeq];
-  __shared__ int s_freed[kMaxSeq];
+  __shared__ int s_old_ext[kMaxSeq];
+  __shared__ int s_excl[kMaxSeq + 1];
   __shared__ int s_scan[kFinalThreads];
   const int units = a.B * a.n_kv;
   const int cap = a.max_blocks * a.page;
-  // new n_slots per unit (computed, not yet stored, so that the per-sequence maximum can use them)
+  const int top0 = *a.free_top;
+  if (top0 < 0 || top0 > a.num_blocks) {
+    if (threadIdx.x == 0) raise(a.status, SE_DEV_CAPACITY);
+    return;
+  }
   for (int b = threadIdx.x; b < a.B; b += kFinalThreads) {
     int mx = 0;
     for (int g = 0; g < a.n_kv; ++g) {
@@ -218,12 +258,17 @@ __global__ __launch_bounds__(kFinalThreads) void gather_finalize(FinalArgs a) {
       int n = a.n_slots[unit], cnt = a.count[unit];
       int w0 = a.window > 0 ? n - a.window : 0;
       bool ok = n >= 0 && n <= cap && w0 >= 0 && cnt >= 0 && cnt <= n - w0;
-      int nn = ok ? w0 + cnt : n;
-      mx = max(mx, nn);
+      mx = max(mx, ok ? w0 + cnt : min(max(n, 0), cap));
     }
     s_new_ext[b] = (mx + a.page - 1) / a.page;
+    s_old_ext[b] = a.max_blocks;
   }
   __syncthreads();
+  // end of each allocated prefix: first unallocated entry at or after the new extent
+  for (int i = threadIdx.x; i < a.B * a.max_blocks; i += kFinalThreads) {
+    const int b = i / a.max_blocks, j = i % a.max_blocks;
+    if (j >= s_new_ext[b] && a.bt[i] < 0) atomicMin(&s_old_ext[b], j);
+  }
   for (int unit = threadIdx.x; unit < units; unit += kFinalThreads) {
     int n = a.n_slots[unit], cnt = a.count[unit];
     int w0 = a.window > 0 ? n - a.window : 0;
@@ -231,9 +276,9 @@ __global__ __launch_bounds__(kFinalThreads) void gather_finalize(FinalArgs a) {
     if (!ok) continue;
     int holes = 0;
     if (a.slot_cap > 0 && a.slot_stack) {
-      int top = a.slot_top[unit], kept = 0;
+      int top = min(max(a.slot_top[unit], 0), a.slot_cap), kept = 0;
       int32_t *st = a.slot_stack + (int64_t)unit * a.slot_cap;
-      for (int i = 0; i < top && i < a.slot_cap; ++i) {
+      for (int i = 0; i < top; ++i) {
         int sl = st[i];
         if (sl >= w0) ++holes; else st[kept++] = sl;
       }
@@ -242,24 +287,12 @@ __global__ __launch_bounds__(kFinalThreads) void gather_finalize(FinalArgs a) {
     a.ctx[unit] = a.ctx[unit] - ((n - w0) - holes) + cnt;
     a.n_slots[unit] = w0 + cnt;
   }
-  // blocks past the new extent, up to the end of the allocated prefix
-  for (int b = threadIdx.x; b < a.B; b += kFinalThreads) {
-    const int32_t *row = a.bt + (int64_t)b * a.max_blocks;
-    int e = s_new_ext[b], old = e;
-    while (old < a.max_blocks && row[old] >= 0) ++old;
-    s_freed[b] = old - e;
-  }
   __syncthreads();
-  // exclusive scan of s_freed over sequences (chunks of kFinalThreads)
+  // exclusive scan of the freed counts over sequences
   int carry = 0;
-  const int top0 = *a.free_top;
-  if (top0 < 0 || top0 > a.num_blocks) {
-    if (threadIdx.x == 0) raise(a.status, SE_DEV_CAPACITY);
-    return;
-  }
   for (int base = 0; base < a.B; base += kFinalThreads) {
-    int b = base + threadIdx.x;
-    int v = b < a.B ? s_freed[b] : 0;
+    const int b = base + threadIdx.x;
+    const int v = b < a.B ? max(s_old_ext[b] - s_new_ext[b], 0) : 0;
     s_scan[threadIdx.x] = v;
     __syncthreads();
     for (int off = 1; off < kFinalThreads; off <<= 1) {
@@ -268,24 +301,29 @@ __global__ __launch_bounds__(kFinalThreads) void gather_finalize(FinalArgs a) {
       s_scan[threadIdx.x] += x;
       __syncthreads();
     }
-    int excl = carry + s_scan[threadIdx.x] - v;
-    if (b < a.B && v > 0) {
-      int32_t *row = a.bt + (int64_t)b * a.max_blocks;
-      int e = s_new_ext[b];
-      int dst = top0 + excl;
-      if (dst + v > a.num_blocks) {
-        raise(a.status, SE_DEV_CAPACITY);
-      } else {
-        for (int i = 0; i < v; ++i) {
-          a.free_blocks[dst + i] = row[e + i];
-          row[e + i] = -1;
-        }
-      }
-    }
+    if (b < a.B) s_excl[b] = carry + s_scan[threadIdx.x] - v;
     carry += s_scan[kFinalThreads - 1];
     __syncthreads();
   }
-  if (threadIdx.x == 0) *a.free_top = min(top0 + carry, a.num_blocks);
+  if (threadIdx.x == 0) s_excl[a.B] = carry;
+  __syncthreads();
+  if (top0 + carry > a.num_blocks) {
+    if (threadIdx.x == 0) raise(a.status, SE_DEV_CAPACITY);
+    return;
+  }
+  // push: freed block f belongs to the sequence b with s_excl[b] <= f < s_excl[b + 1]
+  for (int f = threadIdx.x; f < carry; f += kFinalThreads) {
+    int lo = 0, hi = a.B - 1;
+    while (lo < hi) {
+      int mid = (lo + hi + 1) >> 1;
+      if (s_excl[mid] <= f) lo = mid; else hi = mid - 1;
+    }
+    const int b = lo, j = s_new_ext[b] + (f - s_excl[b]);
+    int32_t *e = a.bt + (int64_t)b * a.max_blocks + j;
+    a.free_blocks[top0 + f] = *e;
+    *e = -1;
+  }
+  if (threadIdx.x == 0) *a.free_top = top0 + carry;
 }
 
 // ---- slot eviction ------------------------------------------------------------------------------------------------
@@ -484,8 +522,13 @@ extern "C" int32_t se_compact_evict(se_cache_t *c, const int32_t *idx, const int
     a.row_bytes = row_bytes;
     a.window = p->window;
     a.idx_stride = p->idx_stride;
-    const int tiles = 1 + (p->idx_stride + se::kMoveRows - 1) / se::kMoveRows;
-    hipLaunchKernelGGL(se::gather_move, dim3(tiles, units), dim3(se::kMoveThreads), 0, st, a);
+    if (row_bytes <= 256) {
+      const int tiles = 1 + (p->idx_stride + 255) / 256;
+      hipLaunchKernelGGL(se::gather_move<256>, dim3(tiles, units), dim3(se::kMoveThreads), 0, st, a);
+    } else {
+      const int tiles = 1 + (p->idx_stride + 127) / 128;
+      hipLaunchKernelGGL(se::gather_move<128>, dim3(tiles, units), dim3(se::kMoveThreads), 0, st, a);
+    }
     se::FinalArgs f;
     f.bt = c->block_table;
     f.n_slots = c->n_slots;

@@ -247,44 +247,77 @@ __global__ __launch_bounds__(kThreads) void decode_partial(DecodeArgs a) {
   }
 }
 
+constexpr int kMaxChunks = 4096;
+
+// (max, sum) of head h over the chunks of a unit, computed by one full wave; lanes stride over chunks. When w is
+// given, the per-chunk weights exp2(m_c - max) are stored there.
+SE_DEV void merge_ml(const float *part, int nchunk, int R, int D, int h, float &mm, float &ll, float *w) {
+  const int lane = threadIdx.x & 63;
+  mm = -1e30f;
+  for (int c = lane; c < nchunk; c += 64) mm = fmaxf(mm, part[(c * R + h) * (D + 2)]);
+  mm = wave_max(mm);
+  ll = 0.f;
+  for (int c = lane; c < nchunk; c += 64) {
+    const float wc = __builtin_amdgcn_exp2f(part[(c * R + h) * (D + 2)] - mm);
+    if (w) w[c] = wc;
+    ll += part[(c * R + h) * (D + 2) + 1] * wc;
+  }
+  ll = wave_sum(ll);
+}
+
+// one workgroup per (unit, head): merge the chunks' partial softmax states into the output row
 template <int DTYPE, int R>
-__global__ __launch_bounds__(kThreads) void decode_merge(DecodeArgs a) {
+__global__ __launch_bounds__(128) void decode_merge(DecodeArgs a) {
   constexpr int D = 16 * Vec<DTYPE>::EPL;
-  const int unit = blockIdx.x;
+  const int unit = blockIdx.x / R, h = blockIdx.x % R;
   const int b = unit / a.n_kv, g = unit % a.n_kv;
   const float *part = a.part + (int64_t)unit * a.nchunk * R * (D + 2);
+  __shared__ float s_w[kMaxChunks];
+  __shared__ float s_l;
+  if (threadIdx.x < 64) {
+    float mm, ll;
+    merge_ml(part, a.nchunk, R, D, h, mm, ll, s_w);
+    if (threadIdx.x == 0) s_l = ll;
+  }
+  __syncthreads();
+  const float inv = s_l > 0.f ? 1.f / s_l : 0.f;
+  for (int e = threadIdx.x; e < D; e += 128) {
+    float o = 0.f;
+#pragma unroll 4
+    for (int c = 0; c < a.nchunk; ++c) o += s_w[c] * part[(c * R + h) * (D + 2) + 2 + e];
+    a.out[(((int64_t)b * a.n_kv + g) * R + h) * D + e] = o * inv;
+  }
+}
+
+// cumulative scores: cum[slot] += sum over the group's heads of that head's softmax weight on the slot
+template <int DTYPE, int R>
+__global__ __launch_bounds__(kThreads) void decode_cum(DecodeArgs a) {
+  constexpr int D = 16 * Vec<DTYPE>::EPL;
+  const int unit = blockIdx.y;
+  const float *part = a.part + (int64_t)unit * a.nchunk * R * (D + 2);
   __shared__ float s_m[R], s_il[R];
-  for (int i = threadIdx.x; i < R * D; i += kThreads) {
-    int h = i / D, e = i % D;
-    float mm = -1e30f;
-    for (int c = 0; c < a.nchunk; ++c) mm = fmaxf(mm, part[(c * R + h) * (D + 2)]);
-    float ll = 0.f, oo = 0.f;
-    for (int c = 0; c < a.nchunk; ++c) {
-      const float *pc = part + (c * R + h) * (D + 2);
-      float f = __builtin_amdgcn_exp2f(pc[0] - mm);
-      ll += pc[1] * f;
-      oo += pc[2 + e] * f;
-    }
-    a.out[(((int64_t)b * a.n_kv + g) * R + h) * D + e] = ll > 0.f ? oo / ll : 0.f;
-    if (e == 0) {
-      s_m[h] = mm;
-      s_il[h] = ll > 0.f ? 1.f / ll : 0.f;
+  if (threadIdx.x < 64) {
+    for (int h = 0; h < R; ++h) {
+      float mm, ll;
+      merge_ml(part, a.nchunk, R, D, h, mm, ll, nullptr);
+      if (threadIdx.x == 0) {
+        s_m[h] = mm;
+        s_il[h] = ll > 0.f ? 1.f / ll : 0.f;
+      }
     }
   }
-  if (!a.cum) return;
   __syncthreads();
   ViewMap vm(a, unit);
-  float *cum = a.cum + (int64_t)unit * a.max_blocks * a.page;
-  for (int r = threadIdx.x; r < vm.rows; r += kThreads) {
-    int s = vm.slot(r);
-    if (s < 0) continue;
-    const float *lg = a.logits + ((int64_t)unit * a.rows_bound + r) * R;
-    if (lg[0] == -INFINITY) continue;  // free slot: not in the view
-    float sum = 0.f;
+  const int r = blockIdx.x * kThreads + threadIdx.x;
+  if (r >= vm.rows) return;
+  const int s = vm.slot(r);
+  if (s < 0) return;
+  const float *lg = a.logits + ((int64_t)unit * a.rows_bound + r) * R;
+  if (lg[0] == -INFINITY) return;  // free slot: not in the view
+  float sum = 0.f;
 #pragma unroll
-    for (int h = 0; h < R; ++h) sum += __builtin_amdgcn_exp2f(lg[h] - s_m[h]) * s_il[h];
-    cum[s] += sum;
-  }
+  for (int h = 0; h < R; ++h) sum += __builtin_amdgcn_exp2f(lg[h] - s_m[h]) * s_il[h];
+  a.cum[(int64_t)unit * a.max_blocks * a.page + s] += sum;
 }
 
 struct Plan {
@@ -303,6 +336,7 @@ Plan make_plan(const se_cache_t *c, const se_decode_params_t *p, int has_sel) {
   pl.units = c->B * c->n_kv;
   int ch = 512;
   while (ch > 64 && (long long)pl.units * ((pl.rows_bound + ch - 1) / ch) < 2048) ch /= 2;
+  while ((pl.rows_bound + ch - 1) / ch > kMaxChunks) ch *= 2;
   pl.chunk_rows = ch;
   pl.nchunk = (pl.rows_bound + ch - 1) / ch;
   if (pl.nchunk < 1) pl.nchunk = 1;
@@ -315,7 +349,10 @@ Plan make_plan(const se_cache_t *c, const se_decode_params_t *p, int has_sel) {
 template <int DTYPE, int R>
 void launch(const DecodeArgs &a, int units, int nchunk, hipStream_t st) {
   hipLaunchKernelGGL((decode_partial<DTYPE, R>), dim3(nchunk, units), dim3(kThreads), 0, st, a);
-  hipLaunchKernelGGL((decode_merge<DTYPE, R>), dim3(units), dim3(kThreads), 0, st, a);
+  hipLaunchKernelGGL((decode_merge<DTYPE, R>), dim3(units * R), dim3(128), 0, st, a);
+  if (a.cum)
+    hipLaunchKernelGGL((decode_cum<DTYPE, R>), dim3((a.rows_bound + kThreads - 1) / kThreads, units), dim3(kThreads),
+                       0, st, a);
 }
 
 template <int DTYPE>

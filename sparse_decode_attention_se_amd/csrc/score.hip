@@ -30,6 +30,7 @@ struct ScoreArgs {
   float *scores;
   float *stats;    // [units][nrg][nkc][256][2] (max, sum) in the log2 domain
   float *colpart;  // [units][nrg][key_span] when nrg > 1
+  float *mlog;     // [units][nrg][256] merged row statistics: max + log2(sum), +inf for empty rows
   int32_t *status;
   int32_t mode, n_kv, R, wq, page, max_blocks, num_blocks, window, protect, score_stride;
   int32_t nrg, nkc, kc, key_span;
@@ -62,42 +63,65 @@ SE_DEV const char *q_row(const ScoreArgs &a, int b, int g, int rho, int row_byte
   return a.q + ((((int64_t)b * a.n_kv + g) * a.R + h) * a.wq + t) * row_bytes;
 }
 
+// merge the per-chunk statistics of this workgroup's 256 rows into log2(sum) + max (or +inf for empty rows)
+SE_DEV float merge_row(const ScoreArgs &a, int unit, int rg, int r) {
+  const float *st = a.stats + (((int64_t)unit * a.nrg + rg) * a.nkc * kRowsPerWG + r) * 2;
+  float mm = -1e30f, ll = 0.f;
+  int c = 0;
+  for (; c + 8 <= a.nkc; c += 8) {  // eight independent loads in flight
+    float m8[8], l8[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      m8[i] = st[(int64_t)(c + i) * kRowsPerWG * 2];
+      l8[i] = st[(int64_t)(c + i) * kRowsPerWG * 2 + 1];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float mn = fmaxf(mm, m8[i]);
+      ll = ll * __builtin_amdgcn_exp2f(mm - mn) + l8[i] * __builtin_amdgcn_exp2f(m8[i] - mn);
+      mm = mn;
+    }
+  }
+  for (; c < a.nkc; ++c) {
+    const float m1 = st[(int64_t)c * kRowsPerWG * 2], l1 = st[(int64_t)c * kRowsPerWG * 2 + 1];
+    const float mn = fmaxf(mm, m1);
+    ll = ll * __builtin_amdgcn_exp2f(mm - mn) + l1 * __builtin_amdgcn_exp2f(m1 - mn);
+    mm = mn;
+  }
+  return ll > 0.f ? mm + __log2f(ll) : INFINITY;
+}
+
+SE_DEV void merge_stats(const ScoreArgs &a, int unit, int rg, float *s_mlog) {
+  s_mlog[threadIdx.x] = merge_row(a, unit, rg, threadIdx.x);
+}
+
+// one thread per query row: the merged statistics used by the column-sum pass
+__global__ __launch_bounds__(kRowsPerWG) void stats_merge(ScoreArgs a) {
+  const int unit = blockIdx.y, rg = blockIdx.x;
+  a.mlog[((int64_t)unit * a.nrg + rg) * kRowsPerWG + threadIdx.x] = merge_row(a, unit, rg, threadIdx.x);
+}
+
 // ---- MFMA path (bf16, d = 128) -------------------------------------------------------------------------------
 // S = Q K^T per 16x16 tile: A = 16 query rows x 32 dims, B = 32 dims x 16 keys; lane l holds A row l%16 and B
 // column l%16 with dims 8*(l/16)..+8 of each 32-dim step, and receives S rows 4*(l/16)..+4 of column l%16.
-struct KTile {
-  bf16x8 f[4];  // 4 k-steps of 32 dims
-  int pos;      // position of this lane's key, -1 if it is not a visible key
-};
-
-SE_DEV void load_ktile(const ScoreArgs &a, int b, int g, int key, int k1, KTile &kt) {
-  const int lane = threadIdx.x & 63;
-  const int32_t *pos = a.pos + ((int64_t)b * a.n_kv + g) * a.max_blocks * a.page;
-  kt.pos = -1;
-  if (key < k1) {
-    int p = pos[key];
-    int blk = a.bt[(int64_t)b * a.max_blocks + key / a.page];
-    if (p >= 0 && blk_ok(blk, a.num_blocks)) {
-      kt.pos = p;
-      const char *row = a.k + (((int64_t)blk * a.n_kv + g) * a.page + key % a.page) * 256 + (lane >> 4) * 16;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) kt.f[ks] = __builtin_bit_cast(bf16x8, ld16(row + ks * 64));
-      return;
-    }
-  }
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) kt.f[ks] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
-}
+// A workgroup owns one key chunk (<= 1024 keys): the chunk's block ids and positions are staged in LDS once,
+// and K fragments of the next 64 keys are loaded while the current 64 are multiplied. Logits stay unscaled;
+// the scale (times log2 e) is folded into the exp2 argument.
+constexpr int kSub = 64;
+constexpr int kMaxChunk = 2048;
+constexpr int kMThreads = 512;    // 8 waves x 32 query rows: two waves per SIMD overlap MFMA with VALU work
+constexpr int kMRowsPerWave = 32;
+constexpr int kRB = kMRowsPerWave / 16;  // 16-row MFMA blocks per wave
 
 struct QFrags {
-  bf16x8 f[4][4];  // [row block][k-step]
-  int lim[4][4];   // [row block][v]: position limit of S row 4*(l/16)+v of the block
+  bf16x8 f[kRB][4];  // [row block][k-step]
+  int lim[kRB][4];   // [row block][v]: position limit of S row 4*(l/16)+v of the block (-1: no such row)
 };
 
 SE_DEV void load_q(const ScoreArgs &a, int b, int g, int rho_wave, QFrags &qf) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb) {
+  for (int rb = 0; rb < kRB; ++rb) {
     int rho = rho_wave + rb * 16 + (lane & 15);
     bool ok = rho < a.R * a.wq;
     const char *row = ok ? q_row(a, b, g, rho, 256) + (lane >> 4) * 16 : nullptr;
@@ -109,144 +133,297 @@ SE_DEV void load_q(const ScoreArgs &a, int b, int g, int rho_wave, QFrags &qf) {
   }
 }
 
-SE_DEV floatx4 mfma_tile(const QFrags &qf, int rb, const KTile &kt) {
-  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf.f[rb][ks], kt.f[ks], acc, 0, 0, 0);
-  return acc;
-}
+struct Chunk {
+  int c0, c1, pbase, nsub;
+  bool fast;  // every key of the chunk exists, is resident and visible to every row of the workgroup
+};
 
-__global__ __launch_bounds__(kThreads) void stats_mfma(ScoreArgs a) {
-  const int unit = blockIdx.z, rg = blockIdx.y, kc = blockIdx.x;
-  const int b = unit / a.n_kv, g = unit % a.n_kv;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int k0, k1, n;
-  key_range(a, unit, k0, k1, n);
-  const int rho_wave = rg * kRowsPerWG + wave * kRowsPerWave;
-  QFrags qf;
-  load_q(a, b, g, rho_wave, qf);
-  float m[4][4], l[4][4];
-#pragma unroll
-  for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      m[rb][v] = -1e30f;
-      l[rb][v] = 0.f;
-    }
-  const int c0 = k0 + kc * a.kc, c1 = min(c0 + a.kc, k1);
-  for (int t0 = c0; t0 < c1; t0 += 64) {
-    KTile kt[4];
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) load_ktile(a, b, g, t0 + tt * 16 + (lane & 15), c1, kt[tt]);
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      floatx4 s[4];
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) s[tt] = mfma_tile(qf, rb, kt[tt]);
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        float x[4];
-        float mn = m[rb][v];
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-          bool vis = kt[tt].pos >= 0 && kt[tt].pos <= qf.lim[rb][v];
-          x[tt] = vis ? s[tt][v] * a.scale_log2 : -INFINITY;
-          mn = fmaxf(mn, x[tt]);
-        }
-        float acc = l[rb][v] * __builtin_amdgcn_exp2f(m[rb][v] - mn);
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) acc += __builtin_amdgcn_exp2f(x[tt] - mn);
-        l[rb][v] = acc;
-        m[rb][v] = mn;
-      }
-    }
+// stage the chunk's key positions and pool row indices in LDS; keys that cannot be read get position -1
+SE_DEV Chunk stage_chunk(const ScoreArgs &a, int b, int g, int c0, int c1, int rg, int *s_blk, int *s_pos,
+                         int *s_row, int *s_mm) {
+  Chunk ch;
+  ch.c0 = c0;
+  ch.c1 = c1;
+  ch.pbase = c0 / a.page;
+  ch.nsub = (c1 - c0 + kSub - 1) / kSub;
+  const int npg = c1 > c0 ? (c1 - 1) / a.page - ch.pbase + 1 : 0;
+  if (threadIdx.x == 0) {
+    s_mm[0] = 0x7fffffff;  // min position
+    s_mm[1] = -1;          // max position
+    s_mm[2] = 0x7fffffff;  // min row limit of the workgroup's rows
   }
-  // combine the 16 lanes (keys) that share each row, then write the chunk's (max, sum) per row
-  float *out = a.stats + ((((int64_t)unit * a.nrg + rg) * a.nkc + kc) * kRowsPerWG) * 2;
-#pragma unroll
-  for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      float mr = row16_max(m[rb][v]);
-      float lr = row16_sum(l[rb][v] * __builtin_amdgcn_exp2f(m[rb][v] - mr));
-      if ((lane & 15) == 0) {
-        int r = wave * kRowsPerWave + rb * 16 + (lane >> 4) * 4 + v;
-        out[r * 2] = mr;
-        out[r * 2 + 1] = lr;
-      }
-    }
-}
-
-// merge the per-chunk statistics of this workgroup's 256 rows into log2(sum) + max (or +inf for empty rows)
-SE_DEV void merge_stats(const ScoreArgs &a, int unit, int rg, float *s_mlog) {
-  const int r = threadIdx.x;
-  const float *st = a.stats + (((int64_t)unit * a.nrg + rg) * a.nkc * kRowsPerWG) * 2;
-  float mm = -1e30f;
-  for (int c = 0; c < a.nkc; ++c) mm = fmaxf(mm, st[(c * kRowsPerWG + r) * 2]);
-  float ll = 0.f;
-  for (int c = 0; c < a.nkc; ++c) {
-    const float *p = st + (c * kRowsPerWG + r) * 2;
-    ll += p[1] * __builtin_amdgcn_exp2f(p[0] - mm);
-  }
-  s_mlog[r] = ll > 0.f ? mm + __log2f(ll) : INFINITY;
-}
-
-SE_DEV void write_colsums(const ScoreArgs &a, int unit, int rg, int c0, int c1, int k0, const float (*s_col)[1024]) {
-  for (int j = threadIdx.x; j < c1 - c0; j += kThreads) {
-    float sum = s_col[0][j] + s_col[1][j] + s_col[2][j] + s_col[3][j];
-    int idx = c0 + j - k0;
-    if (a.nrg == 1) a.scores[(int64_t)unit * a.score_stride + idx] = sum;
-    else a.colpart[((int64_t)unit * a.nrg + rg) * a.key_span + idx] = sum;
-  }
-}
-
-__global__ __launch_bounds__(kThreads) void colsum_mfma(ScoreArgs a) {
-  const int unit = blockIdx.z, rg = blockIdx.y, kc = blockIdx.x;
-  const int b = unit / a.n_kv, g = unit % a.n_kv;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  __shared__ float s_mlog[kRowsPerWG];
-  __shared__ float s_col[4][1024];
-  int k0, k1, n;
-  key_range(a, unit, k0, k1, n);
-  const int c0 = k0 + kc * a.kc, c1 = min(c0 + a.kc, k1);
-  if (c0 >= c1) return;  // uniform: no keys in this chunk
-  merge_stats(a, unit, rg, s_mlog);
-  const int rho_wave = rg * kRowsPerWG + wave * kRowsPerWave;
-  QFrags qf;
-  load_q(a, b, g, rho_wave, qf);
+  for (int i = threadIdx.x; i < npg; i += kMThreads) s_blk[i] = a.bt[(int64_t)b * a.max_blocks + ch.pbase + i];
   __syncthreads();
-  float ml[4][4];
+  const int32_t *pos = a.pos + ((int64_t)b * a.n_kv + g) * a.max_blocks * a.page;
+  int mn = 0x7fffffff, mx = -1;
+  constexpr int kPer = kMaxChunk / kMThreads;
+  int pv[kPer];
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb)
+  for (int j = 0; j < kPer; ++j) {  // all position loads in flight at once
+    const int key = c0 + threadIdx.x + j * kMThreads;
+    pv[j] = key < c1 ? pos[key] : -1;
+  }
 #pragma unroll
-    for (int v = 0; v < 4; ++v) ml[rb][v] = s_mlog[wave * kRowsPerWave + rb * 16 + (lane >> 4) * 4 + v];
-  for (int t0 = c0; t0 < c1; t0 += 64) {
-    KTile kt[4];
+  for (int j = 0; j < kPer; ++j) {
+    const int i = threadIdx.x + j * kMThreads;
+    if (i >= ch.nsub * kSub) break;
+    const int key = c0 + i;
+    int p = pv[j], row = 0;
+    if (key < c1) {
+      const int blk = s_blk[key / a.page - ch.pbase];
+      if (p >= 0 && !blk_ok(blk, a.num_blocks)) p = -1;
+      if (p >= 0) row = (blk * a.n_kv + g) * a.page + key % a.page;
+      mn = min(mn, p);
+      mx = max(mx, p);
+    }
+    s_pos[i] = p;
+    s_row[i] = row;
+  }
+  atomicMin(&s_mm[0], mn);
+  atomicMax(&s_mm[1], mx);
+  if (threadIdx.x < kRowsPerWG) {
+    const int lim = row_limit(a, b, rg * kRowsPerWG + threadIdx.x);
+    if (lim >= 0) atomicMin(&s_mm[2], lim);
+  }
+  __syncthreads();
+  ch.fast = (c1 - c0 == ch.nsub * kSub) && s_mm[0] >= 0 && s_mm[1] <= s_mm[2];
+  return ch;
+}
+
+// K staging: 64-key sub-chunks (16 KiB) pass through registers into a double-buffered LDS tile, three
+// sub-chunks ahead of the one being multiplied. Thread t fetches 32 contiguous bytes of key t / 8. In LDS the 4
+// keys of each 1 KiB block are stored as 64 16-byte positions, piece c of key r at position r * 16 + (c ^ swz),
+// swz = 4 * (block % 4) + r: the 16 lanes of a B-fragment read (16 keys, one piece each) hit 16 distinct 16-byte
+// bank groups.
+constexpr int kSubBytes = kSub * 256;
+
+SE_DEV int swz(int r, int blk) { return ((blk & 3) << 2) | r; }
+
+struct Stage {
+  u32x4 v[2];
+};
+
+SE_DEV void load_stage(const ScoreArgs &a, const Chunk &ch, int sub, const int *s_row, Stage &st) {
+  // branch-free so that the compiler's wait counts stay exact: keys that are never read (free, past the chunk or
+  // past the last sub-chunk) fetch row 0 of the pool instead and are masked by position later
+  const int kt = threadIdx.x >> 3, q8 = threadIdx.x & 7;
+  const int row = sub < ch.nsub ? s_row[sub * kSub + kt] : 0;
+  const char *src = a.k + (int64_t)row * 256 + q8 * 32;
+  st.v[0] = ld16(src);
+  st.v[1] = ld16(src + 16);
+}
+
+SE_DEV void store_stage(const Stage &st, char *slot) {
+  const int kt = threadIdx.x >> 3, q8 = threadIdx.x & 7;
+  const int blk = kt >> 2, r = kt & 3;
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) load_ktile(a, b, g, t0 + tt * 16 + (lane & 15), c1, kt[tt]);
-    float col[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < 2; ++i) {
+    const int c = q8 * 2 + i;
+    *reinterpret_cast<u32x4 *>(slot + blk * 1024 + (r * 16 + (c ^ swz(r, blk))) * 16) = st.v[i];
+  }
+}
+
+// B fragment of key tile tt, k-step ks from a staged sub-chunk
+SE_DEV bf16x8 read_frag(const char *slot, int tt, int ks) {
+  const int lane = threadIdx.x & 63;
+  const int key = tt * 16 + (lane & 15);
+  const int blk = key >> 2, r = key & 3;
+  const int piece = ks * 4 + (lane >> 4);
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(slot + blk * 1024 + (r * 16 + (piece ^ swz(r, blk))) * 16));
+}
+
+// S tiles of the wave's row blocks x the sub-chunk's 4 key tiles; the k-step loop is outermost so each step
+// issues independent MFMAs
+SE_DEV void mfma_sub(const QFrags &qf, const char *slot, floatx4 (&s)[kRB][4]) {
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
+  for (int rb = 0; rb < kRB; ++rb)
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) s[rb][tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    bf16x8 k[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) k[tt] = read_frag(slot, tt, ks);
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb)
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+        s[rb][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf.f[rb][ks], k[tt], s[rb][tt], 0, 0, 0);
+  }
+}
+
+// pass 1 state: running max (unscaled logits) and sum of exp2((s - max) * c) per S row of the lane
+struct Stats {
+  float m[kRB][4], l[kRB][4];
+};
+
+template <bool FAST>
+SE_DEV void stats_valu_step(const ScoreArgs &a, const QFrags &qf, int sub, const int *s_pos, const floatx4 (&s)[kRB][4],
+                            Stats &st) {
+  const int lane = threadIdx.x & 63;
+  const float c = a.scale_log2;
+  int kp[4];
+  if (!FAST)
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) kp[tt] = s_pos[sub * kSub + tt * 16 + (lane & 15)];
+#pragma unroll
+  for (int rb = 0; rb < kRB; ++rb) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      float x[4];
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) {
-        floatx4 s = mfma_tile(qf, rb, kt[tt]);
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          bool vis = kt[tt].pos >= 0 && kt[tt].pos <= qf.lim[rb][v];
-          float p = __builtin_amdgcn_exp2f(s[v] * a.scale_log2 - ml[rb][v]);
-          col[tt] += vis ? p : 0.f;
-        }
+        x[tt] = s[rb][tt][v];
+        if (!FAST) x[tt] = (kp[tt] >= 0 && kp[tt] <= qf.lim[rb][v]) ? x[tt] : -INFINITY;
       }
-    }
+      const float mn = fmaxf(fmaxf(st.m[rb][v], fmaxf(x[0], x[1])), fmaxf(x[2], x[3]));
+      const float nmc = -mn * c;
+      float acc = st.l[rb][v] * __builtin_amdgcn_exp2f(fmaf(st.m[rb][v], c, nmc));
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      float cs = cross_row_sum(col[tt]);
-      int j = t0 + tt * 16 + lane - c0;
-      if (lane < 16 && t0 + tt * 16 + lane < c1) s_col[wave][j] = cs;
+      for (int tt = 0; tt < 4; ++tt) acc += __builtin_amdgcn_exp2f(fmaf(x[tt], c, nmc));
+      st.l[rb][v] = acc;
+      st.m[rb][v] = mn;
     }
   }
+}
+
+template <bool FAST>
+SE_DEV void colsum_valu_step(const ScoreArgs &a, const QFrags &qf, int sub, const int *s_pos,
+                             const floatx4 (&s)[kRB][4], const float (&ml)[kRB][4], float (*s_col)[kMaxChunk]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const float c = a.scale_log2;
+  int kp[4];
+  if (!FAST)
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) kp[tt] = s_pos[sub * kSub + tt * 16 + (lane & 15)];
+  float col[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int rb = 0; rb < kRB; ++rb) {
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        float p = __builtin_amdgcn_exp2f(fmaf(s[rb][tt][v], c, -ml[rb][v]));
+        if (!FAST) p = (kp[tt] >= 0 && kp[tt] <= qf.lim[rb][v]) ? p : 0.f;
+        col[tt] += p;
+      }
+    }
+  }
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) {
+    const float cs = cross_row_sum(col[tt]);
+    if (lane < 16) s_col[wave][sub * kSub + tt * 16 + lane] = cs;
+  }
+}
+
+template <int PASS>
+__global__ __launch_bounds__(kMThreads) void window_mfma(ScoreArgs a) {
+  constexpr int kWaves = kMThreads / 64;
+  const int unit = blockIdx.z, rg = blockIdx.y, kc = blockIdx.x;
+  const int b = unit / a.n_kv, g = unit % a.n_kv;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ __attribute__((aligned(1024))) char s_k[3][kSubBytes];
+  __shared__ int s_blk[kMaxChunk / 16 + 2];
+  __shared__ int s_pos[kMaxChunk];
+  __shared__ int s_row[kMaxChunk];
+  __shared__ int s_mm[3];
+  __shared__ float s_col[PASS == 2 ? kWaves : 1][PASS == 2 ? kMaxChunk : 1];
+  int k0, k1, n;
+  key_range(a, unit, k0, k1, n);
+  const int c0 = k0 + kc * a.kc, c1 = min(c0 + a.kc, k1);
+  if (PASS == 2 && c0 >= c1) return;  // uniform: nothing to score in this chunk
+  const Chunk ch = stage_chunk(a, b, g, c0, max(c0, c1), rg, s_blk, s_pos, s_row, s_mm);
+  // sub-chunks 0..2 in flight before anything else
+  Stage st0, st1, st2;
+  load_stage(a, ch, 0, s_row, st0);
+  load_stage(a, ch, 1, s_row, st1);
+  load_stage(a, ch, 2, s_row, st2);
+  const int rho_wave = rg * kRowsPerWG + wave * kMRowsPerWave;
+  QFrags qf;
+  load_q(a, b, g, rho_wave, qf);
+
+  Stats st;
+  float ml[kRB][4];
+  if (PASS == 1) {
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        st.m[rb][v] = -1e30f;
+        st.l[rb][v] = 0.f;
+      }
+  } else {
+    const float *mlog = a.mlog + ((int64_t)unit * a.nrg + rg) * kRowsPerWG;
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        ml[rb][v] = qf.lim[rb][v] >= 0 ? mlog[wave * kMRowsPerWave + rb * 16 + (lane >> 4) * 4 + v] : INFINITY;
+  }
+  // Sub-chunk j: fetched into stage j % 3 at step j - 3 (or up front), written to LDS buffer j % 3 at step j - 2,
+  // multiplied (MFMA) at step j - 1 and turned into softmax statistics / column sums (VALU) at step j. Issuing the
+  // MFMAs of the next sub-chunk before the VALU work of this one lets the matrix core run while the VALU works.
+  store_stage(st0, s_k[0]);
+  store_stage(st1, s_k[1]);
   __syncthreads();
-  write_colsums(a, unit, rg, c0, c1, k0, s_col);
+  load_stage(a, ch, 3, s_row, st0);
+  load_stage(a, ch, 4, s_row, st1);
+  floatx4 acc_a[kRB][4], acc_b[kRB][4];
+  mfma_sub(qf, s_k[0], acc_a);
+#define SE_STEP(FAST, SUB, CUR, NXT, NEXT_BUF, STORE_BUF, STAGE)                                                \
+  if ((SUB) < ch.nsub) {                                                                                       \
+    if ((SUB) + 1 < ch.nsub) mfma_sub(qf, s_k[NEXT_BUF], NXT);                                                 \
+    if constexpr (PASS == 1) stats_valu_step<FAST>(a, qf, (SUB), s_pos, CUR, st);                              \
+    else colsum_valu_step<FAST>(a, qf, (SUB), s_pos, CUR, ml, s_col);                                          \
+  }                                                                                                            \
+  store_stage(STAGE, s_k[STORE_BUF]);                                                                          \
+  __syncthreads();                                                                                             \
+  load_stage(a, ch, (SUB) + 5, s_row, STAGE);
+  // step s: MFMA buffer (s + 1) % 3, store buffer / stage (s + 2) % 3; accumulators alternate
+#define SE_SIX(FAST)                                                                                            \
+  for (int sub = 0; sub < ch.nsub; sub += 6) {                                                                 \
+    SE_STEP(FAST, sub, acc_a, acc_b, 1, 2, st2)                                                                \
+    SE_STEP(FAST, sub + 1, acc_b, acc_a, 2, 0, st0)                                                            \
+    SE_STEP(FAST, sub + 2, acc_a, acc_b, 0, 1, st1)                                                            \
+    SE_STEP(FAST, sub + 3, acc_b, acc_a, 1, 2, st2)                                                            \
+    SE_STEP(FAST, sub + 4, acc_a, acc_b, 2, 0, st0)                                                            \
+    SE_STEP(FAST, sub + 5, acc_b, acc_a, 0, 1, st1)                                                            \
+  }
+  if (ch.fast) {
+    SE_SIX(true)
+  } else {
+    SE_SIX(false)
+  }
+#undef SE_SIX
+#undef SE_STEP
+
+  if constexpr (PASS == 1) {
+    // combine the 16 lanes (keys) of each row; write the chunk's (max, sum) per row in the log2 domain
+    float *out = a.stats + ((((int64_t)unit * a.nrg + rg) * a.nkc + kc) * kRowsPerWG) * 2;
+    const float c = a.scale_log2;
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float mr = row16_max(st.m[rb][v]);
+        const float lr = row16_sum(st.l[rb][v] * __builtin_amdgcn_exp2f((st.m[rb][v] - mr) * c));
+        if ((lane & 15) == 0) {
+          const int r = wave * kMRowsPerWave + rb * 16 + (lane >> 4) * 4 + v;
+          out[r * 2] = mr * c;
+          out[r * 2 + 1] = lr;
+        }
+      }
+  } else {
+    __syncthreads();
+    for (int j = threadIdx.x; j < c1 - c0; j += kMThreads) {
+      float sum = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) sum += s_col[w][j];
+      const int idx = c0 + j - k0;
+      if (a.nrg == 1) a.scores[(int64_t)unit * a.score_stride + idx] = sum;
+      else a.colpart[((int64_t)unit * a.nrg + rg) * a.key_span + idx] = sum;
+    }
+  }
 }
 
 // ---- VALU path (fp32 inputs, or any d that fits) ---------------------------------------------------------------
@@ -346,7 +523,7 @@ __global__ void colsum_reduce(ScoreArgs a) {
 
 struct Plan {
   int nrg, nkc, kc, key_span;
-  size_t stats_bytes, col_bytes;
+  size_t stats_bytes, col_bytes, mlog_bytes;
 };
 
 Plan make_plan(const se_cache_t *c, const se_window_params_t *p) {
@@ -357,12 +534,13 @@ Plan make_plan(const se_cache_t *c, const se_window_params_t *p) {
   const int max_slots = c->max_blocks * c->page;
   pl.key_span = p->mode == SE_SCORE_CAUSAL ? max_slots : p->window - p->protect;
   const int span64 = (pl.key_span + 63) / 64 * 64;
-  pl.kc = span64 < 1024 ? span64 : 1024;
+  pl.kc = span64 < kMaxChunk ? span64 : kMaxChunk;
   if (pl.kc < 64) pl.kc = 64;
   pl.nkc = (pl.key_span + pl.kc - 1) / pl.kc;
   const size_t units = (size_t)c->B * c->n_kv;
   pl.stats_bytes = se_host::align_up(units * pl.nrg * pl.nkc * kRowsPerWG * 2 * sizeof(float));
   pl.col_bytes = pl.nrg > 1 ? se_host::align_up(units * pl.nrg * pl.key_span * sizeof(float)) : 0;
+  pl.mlog_bytes = se_host::align_up(units * pl.nrg * kRowsPerWG * sizeof(float));
   return pl;
 }
 
@@ -372,7 +550,7 @@ Plan make_plan(const se_cache_t *c, const se_window_params_t *p) {
 extern "C" size_t se_window_score_workspace_size(const se_cache_t *c, const se_window_params_t *p) {
   if (se_host::check_cache(c) != SE_OK || !p) return 0;
   se::Plan pl = se::make_plan(c, p);
-  return pl.stats_bytes + pl.col_bytes;
+  return pl.stats_bytes + pl.col_bytes + pl.mlog_bytes;
 }
 
 extern "C" int32_t se_window_score(const se_cache_t *c, const void *q_win, const int32_t *q_pos,
@@ -396,7 +574,7 @@ extern "C" int32_t se_window_score(const se_cache_t *c, const void *q_win, const
   const bool valu = c->dtype == SE_DTYPE_F32 && c->d == 64;
   if (!mfma && !valu) return SE_ERR_DTYPE;
   se::Plan pl = se::make_plan(c, p);
-  if (!ws || ws_bytes < pl.stats_bytes + pl.col_bytes) return SE_ERR_WORKSPACE;
+  if (!ws || ws_bytes < pl.stats_bytes + pl.col_bytes + pl.mlog_bytes) return SE_ERR_WORKSPACE;
   se::ScoreArgs a;
   a.k = (const char *)c->k_pool;
   a.bt = c->block_table;
@@ -407,6 +585,7 @@ extern "C" int32_t se_window_score(const se_cache_t *c, const void *q_win, const
   a.scores = scores;
   a.stats = (float *)ws;
   a.colpart = pl.col_bytes ? (float *)((char *)ws + pl.stats_bytes) : nullptr;
+  a.mlog = (float *)((char *)ws + pl.stats_bytes + pl.col_bytes);
   a.status = status;
   a.mode = p->mode;
   a.n_kv = c->n_kv;
@@ -427,8 +606,9 @@ extern "C" int32_t se_window_score(const se_cache_t *c, const void *q_win, const
   const dim3 grid(pl.nkc, pl.nrg, units);
   hipStream_t st = (hipStream_t)stream;
   if (mfma) {
-    hipLaunchKernelGGL(se::stats_mfma, grid, dim3(se::kThreads), 0, st, a);
-    hipLaunchKernelGGL(se::colsum_mfma, grid, dim3(se::kThreads), 0, st, a);
+    hipLaunchKernelGGL(se::window_mfma<1>, grid, dim3(se::kMThreads), 0, st, a);
+    hipLaunchKernelGGL(se::stats_merge, dim3(pl.nrg, units), dim3(se::kRowsPerWG), 0, st, a);
+    hipLaunchKernelGGL(se::window_mfma<2>, grid, dim3(se::kMThreads), 0, st, a);
   } else {
     hipLaunchKernelGGL((se::stats_valu<SE_DTYPE_F32, 64>), grid, dim3(se::kThreads), 0, st, a);
     hipLaunchKernelGGL((se::colsum_valu<SE_DTYPE_F32, 64>), grid, dim3(se::kThreads), 0, st, a);
