@@ -1,16 +1,26 @@
-"""Benchmark of the sparse-KV hot path on one MI355X.
+"""Benchmark of the sparse-KV hot path on one MI355X. Prints one JSON line.
 
-A step is one SnapKV-style prefill-end eviction event over a batch of 8 Llama-3.1-8B-shaped sequences of 32768
-tokens (32 query / 8 KV heads, d = 128, bf16, page 16): causal window scores of the last 64 queries, top-1984
-+ 64 protected keys per KV head, in-place compaction with block freeing, and one decode step over the retained
-KV. Every step works on its own pristine copy of the cache, resident in HBM before timing starts (compaction is
-destructive). Prints one JSON line.
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c1|c2|c3|c4] [--no-cpu-baseline]
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+A step is one pass of the workload's hot path over its batch, with every input resident in HBM before timing:
+
+  c1 (default, the headline) SnapKV-style prefill-end eviction on 8 Llama-3.1-8B-shaped sequences x 32768 tokens
+     (32 q / 8 KV heads, d 128, bf16, page 16): causal window scores of the last 64 queries, top-1984 + 64
+     protected keys per KV head, in-place compaction with block freeing, one decode step over the retained KV.
+  c2 Kara periodic compression on 128 Qwen3-4B-shaped sequences x 16384 tokens: bidirectional scores of the
+     trailing 512-token window, top-20% candidates, Token2Chunk, trailing-block compaction, then one decode step
+     (append + attention over the whole cache).
+  c3 Quest decode on 2 sequences x 131072 tokens: page bounds against the query, top-256 pages + first/last,
+     decode attention over the 258 selected pages (page metadata built once, outside the step).
+  c4 H2O continuous eviction on 64 sequences at the 8192-token budget: append, decode with cumulative scores,
+     bottom-1 eviction outside the 256 most recent positions (the step loop of the workload itself).
+
+Steps that change the cache destructively, or whose working set would stay in the 256 MB Infinity Cache between
+steps, run each on a pristine copy of the cache (c1, c2, c3). Per-call times come from HIP events on the stream
+the calls are launched on.
 """
 import argparse
 import json
-import math
 import os
 import sys
 import time
@@ -28,22 +38,166 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def algorithmic(cfg):
-    """Algorithmic bytes and flops of each call of one event (what the method must move or compute)."""
-    B, G, N, d, r = cfg.B, cfg.hkv, cfg.N, cfg.d, cfg.hq // cfg.hkv
+def to_dev_bf16(x, dev):
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev).view(torch.bfloat16)
+
+
+def device_cache(se, cfg, c, dev):
+    return se.DeviceCache.from_arrays(cfg.hq, cfg.dtype, dev, **{f: getattr(c, f) for f in se.DeviceCache.FIELDS
+                                                                  if getattr(c, f, None) is not None})
+
+
+# ---------------------------------------------------------------------------------------------------------------
+# workloads: each returns (cfg, steps[list of list of (call name, fn)], tokens per step, algorithmic bytes per call,
+# dominant call, inputs for the CPU baseline)
+# ---------------------------------------------------------------------------------------------------------------
+
+
+def setup_c1(se, WF, W, copies, dev):
+    cfg = W.C1
+    inp = W.gen_snapkv(cfg, seed=0, threads=16)
+    base = device_cache(se, cfg, inp["cache"], dev)
+    caches = [base] + [base.clone() for _ in range(copies - 1)]
+    import torch
+
+    q_win, q_dec = to_dev_bf16(inp["q_win"], dev), to_dev_bf16(inp["q_dec"], dev)
+    q_pos = torch.from_numpy(inp["q_pos"]).to(dev)
+    evs = [WF.SnapKVEvent(c, wq=cfg.wq, protect=cfg.protect, keep=cfg.keep, scale=inp["scale"]) for c in caches]
+    steps = [[("se_window_score", lambda e=e: e.score(q_win, q_pos)), ("se_topk_select", e.select),
+              ("se_compact_evict", e.compact), ("se_sparse_decode_attn", lambda e=e: e.decode(q_dec))] for e in evs]
+    B, G, N, r, row = cfg.B, cfg.hkv, cfg.N, cfg.hq // cfg.hkv, cfg.d * 2
     keep = cfg.keep + cfg.protect
-    row = d * 2
-    return {
+    alg = {
         "se_window_score": {"bytes": B * G * N * row + B * cfg.hq * cfg.wq * row + B * G * N * 4,
-                            "flops": 2.0 * B * G * r * cfg.wq * N * d},
-        "se_topk_select": {"bytes": B * G * N * 4 * 2 + B * G * keep * 4, "flops": 0.0},
-        "se_compact_evict": {"bytes": 2 * (B * G * keep * row * 2) + 2 * B * G * keep * 4, "flops": 0.0},
-        "se_sparse_decode_attn": {"bytes": B * G * keep * row * 2 + B * cfg.hq * d * (2 + 4), "flops": 0.0},
+                            "flops": 2.0 * B * G * r * cfg.wq * N * cfg.d},
+        "se_topk_select": {"bytes": B * G * N * 4 * 2 + B * G * keep * 4},
+        "se_compact_evict": {"bytes": 2 * (B * G * keep * row * 2) + 2 * B * G * keep * 4},
+        "se_sparse_decode_attn": {"bytes": B * G * keep * row * 2 + B * cfg.hq * cfg.d * (2 + 4)},
     }
+    return cfg, steps, B * N, alg, inp
+
+
+def setup_c2(se, WF, W, copies, dev):
+    cfg = W.scaled(W.C2, period=1, events=1)
+    inp = W.gen_kara(cfg, seed=0, threads=16)
+    base = device_cache(se, cfg, inp["cache"], dev)
+    caches = [base] + [base.clone() for _ in range(copies - 1)]
+    import torch
+
+    # the fresh cache's trailing window holds positions N - window .. N - 1, the first queries the workload keeps
+    assert inp["q_first_pos"] == cfg.N - cfg.window
+    q_win = to_dev_bf16(np.ascontiguousarray(inp["q_all"][:, :, :cfg.window]), dev)
+    k_new, v_new = to_dev_bf16(inp["k_new"][0], dev), to_dev_bf16(inp["v_new"][0], dev)
+    q = to_dev_bf16(np.ascontiguousarray(inp["q_all"][:, :, cfg.N - inp["q_first_pos"]]), dev)
+    pos = torch.full((cfg.B,), cfg.N, dtype=torch.int32, device=dev)
+    steps = []
+    for c in caches:
+        ev = WF.KaraEvent(c, window=cfg.window, protect=cfg.protect, n_cand=cfg.n_cand, budget=cfg.budget,
+                          max_gap=cfg.max_gap, scale=inp["scale"])
+        dec = WF.DecodeStep(c, scale=inp["scale"])
+        steps.append([
+            ("se_window_score", lambda ev=ev: se.se_window_score(
+                ev.cache, q_win, None, ev.scores, scale=ev.scale, mode=se.SE_SCORE_BIDIR, n_query=cfg.window,
+                window=cfg.window, protect=cfg.protect)),
+            ("se_topk_select", lambda ev=ev: se.se_topk_select(
+                ev.cache, ev.scores, ev.cand, ev.cand_count, mode=se.SE_TOPK_LARGEST, unit=se.SE_UNIT_SLOT,
+                k=cfg.n_cand, window=cfg.window, protect=cfg.protect)),
+            ("se_token2chunk", lambda ev=ev: se.se_token2chunk(
+                ev.cache, ev.cand, ev.cand_count, ev.scores, ev.keep, ev.keep_count, max_gap=cfg.max_gap,
+                budget=cfg.budget, window=cfg.window, protect=cfg.protect)),
+            ("se_compact_evict", lambda ev=ev: se.se_compact_evict(
+                ev.cache, ev.keep, ev.keep_count, mode=se.SE_COMPACT_GATHER, window=cfg.window)),
+            ("se_cache_append", lambda dec=dec: se.se_cache_append(dec.cache, k_new, v_new, pos)),
+            ("se_sparse_decode_attn", lambda dec=dec: se.se_sparse_decode_attn(dec.cache, q, dec.out,
+                                                                               scale=dec.scale)),
+        ])
+    B, G, N, r, row, W_ = cfg.B, cfg.hkv, cfg.N, cfg.hq // cfg.hkv, cfg.d * 2, cfg.window
+    R = W_ - cfg.protect
+    kept = cfg.budget + cfg.protect  # upper bound of the retained window
+    after = N - W_ + kept + 1
+    alg = {
+        "se_window_score": {"bytes": B * G * R * row + B * cfg.hq * W_ * row + B * G * R * 4,
+                            "flops": 2.0 * B * G * r * W_ * R * cfg.d},
+        "se_topk_select": {"bytes": B * G * (R * 4 + W_ * 4)},
+        "se_token2chunk": {"bytes": B * G * (R * 4 + 2 * kept * 4)},
+        "se_compact_evict": {"bytes": 2 * B * G * kept * (2 * row + 4)},
+        "se_cache_append": {"bytes": 2 * B * G * row * 2},
+        "se_sparse_decode_attn": {"bytes": B * G * after * (2 * row + 4) + B * cfg.hq * cfg.d * (2 + 4)},
+    }
+    return cfg, steps, B * W_, alg, None
+
+
+def setup_c3(se, WF, W, copies, dev):
+    cfg = W.C3
+    inp = W.gen_quest(cfg, seed=0, threads=16)
+    base = device_cache(se, cfg, inp["cache"], dev)
+    q = to_dev_bf16(inp["q_dec"], dev)
+    QS = WF.QuestStep(base, top_pages=cfg.top_pages, scale=inp["scale"])
+    QS.build()  # page metadata: built once for the cache, then carried by every copy
+    caches = [base] + [base.clone() for _ in range(copies - 1)]
+    steps = []
+    for c in caches:
+        qs = WF.QuestStep(c, top_pages=cfg.top_pages, scale=inp["scale"])
+        steps.append([
+            ("se_page_bounds", lambda qs=qs: se.se_page_bounds(qs.cache, se.SE_PAGES_SCORE, q, qs.page_scores)),
+            ("se_topk_select", lambda qs=qs: se.se_topk_select(
+                qs.cache, qs.page_scores, qs.pages, qs.count, mode=se.SE_TOPK_LARGEST, unit=se.SE_UNIT_PAGE,
+                k=cfg.top_pages, forced_ends=1)),
+            ("se_sparse_decode_attn", lambda qs=qs: se.se_sparse_decode_attn(
+                qs.cache, q, qs.out, scale=qs.scale, sel_pages=qs.pages, sel_count=qs.count)),
+        ])
+    B, G, N, row = cfg.B, cfg.hkv, cfg.N, cfg.d * 2
+    P_ = N // cfg.page
+    sel = cfg.top_pages + 2
+    alg = {
+        "se_page_bounds": {"bytes": B * G * P_ * 2 * row + B * G * P_ * 4 + B * cfg.hq * row},
+        "se_topk_select": {"bytes": B * G * P_ * 4 + B * G * sel * 4},
+        "se_sparse_decode_attn": {"bytes": B * G * sel * cfg.page * (2 * row + 4) + B * cfg.hq * cfg.d * (2 + 4)},
+    }
+    return cfg, steps, B * N, alg, None
+
+
+def setup_c4(se, WF, W, copies, dev):
+    cfg = W.scaled(W.C4, steps=copies)
+    inp = W.gen_h2o(cfg, seed=0, threads=16)
+    c = device_cache(se, cfg, inp["cache"], dev)
+    import torch
+
+    h2o = WF.H2OStep(c, scale=inp["scale"], budget=cfg.budget, recent=cfg.recent)
+    k_new = [to_dev_bf16(inp["k_new"][s], dev) for s in range(copies)]
+    v_new = [to_dev_bf16(inp["v_new"][s], dev) for s in range(copies)]
+    q = [to_dev_bf16(inp["q_steps"][s], dev) for s in range(copies)]
+    pos = [torch.full((cfg.B,), cfg.N + s, dtype=torch.int32, device=dev) for s in range(copies)]
+    steps = []
+    for s in range(copies):
+        steps.append([
+            ("se_cache_append", lambda s=s: se.se_cache_append(c, k_new[s], v_new[s], pos[s])),
+            ("se_sparse_decode_attn", lambda s=s: se.se_sparse_decode_attn(c, q[s], h2o.out, scale=h2o.scale,
+                                                                           accumulate=True)),
+            ("se_topk_select", lambda: se.se_topk_select(c, c.cum_score, h2o.evict, h2o.evict_count,
+                                                         mode=se.SE_TOPK_SMALLEST, unit=se.SE_UNIT_SLOT, k=1,
+                                                         budget=cfg.budget, recent=cfg.recent)),
+            ("se_compact_evict", lambda: se.se_compact_evict(c, h2o.evict, h2o.evict_count,
+                                                             mode=se.SE_COMPACT_EVICT_SLOTS)),
+        ])
+    B, G, row = cfg.B, cfg.hkv, cfg.d * 2
+    n = cfg.budget + 1
+    alg = {
+        "se_cache_append": {"bytes": 2 * B * G * row * 2},
+        "se_sparse_decode_attn": {"bytes": B * G * n * (2 * row + 4 + 8) + B * cfg.hq * cfg.d * (2 + 4)},
+        "se_topk_select": {"bytes": B * G * n * 8},
+        "se_compact_evict": {"bytes": B * G * 16},
+    }
+    return cfg, steps, B * n, alg, None
+
+
+SETUPS = {"c1": setup_c1, "c2": setup_c2, "c3": setup_c3, "c4": setup_c4}
 
 
 def cpu_baseline(inp, n_seq):
-    """The oracle (as it stands) on the first n_seq sequences of the same workload, timed on the host cores."""
+    """The oracle (as it stands) on the first n_seq sequences of the SnapKV workload, timed on the host cores."""
     import oracle.pipelines as P
     import workloads as W
 
@@ -76,7 +230,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--workload", default="c1", choices=sorted(SETUPS))
     ap.add_argument("--cpu-seqs", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -86,7 +240,7 @@ def main():
         sys.exit(2)
     copies = args.steps + args.warmup
     if copies > 64:
-        print("steps + warmup must be <= 64 (one pristine 1 GiB cache copy is kept per step)", file=sys.stderr)
+        print("steps + warmup must be <= 64 (one pristine cache copy is kept per step)", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -96,74 +250,50 @@ def main():
     from sparse_decode_attention_se_amd import workflows as WF
 
     dev = "cuda:0"
-    cfg = W.C1
     t0 = time.time()
-    inp = W.gen_snapkv(cfg, seed=args.seed, threads=16)
-    log(f"generated {cfg.name} inputs in {time.time() - t0:.1f} s")
-    c = inp["cache"]
-    base = se.DeviceCache.from_arrays(cfg.hq, cfg.dtype, dev, **{f: getattr(c, f) for f in se.DeviceCache.FIELDS
-                                                                  if getattr(c, f, None) is not None})
-    caches = [base] + [base.clone() for _ in range(copies - 1)]
-    q_win = torch.from_numpy(inp["q_win"].view(np.int16)).to(dev).view(torch.bfloat16)
-    q_pos = torch.from_numpy(inp["q_pos"]).to(dev)
-    q_dec = torch.from_numpy(inp["q_dec"].view(np.int16)).to(dev).view(torch.bfloat16)
-    status = torch.zeros(1, dtype=torch.int32, device=dev)
-    events = [WF.SnapKVEvent(cc, wq=cfg.wq, protect=cfg.protect, keep=cfg.keep, scale=inp["scale"], status=status)
-              for cc in caches]
+    cfg, steps, tokens, alg, inp = SETUPS[args.workload](se, WF, W, copies, dev)
     torch.cuda.synchronize()
-    log(f"{copies} cache copies resident ({torch.cuda.memory_allocated() / 2**30:.1f} GiB)")
-
-    calls = ["se_window_score", "se_topk_select", "se_compact_evict", "se_sparse_decode_attn"]
-
-    def run_step(ev, marks=None):
-        stages = [lambda: ev.score(q_win, q_pos), ev.select, ev.compact, lambda: ev.decode(q_dec)]
-        for name, fn in zip(calls, stages):
-            if marks is not None:
-                marks[name][0].record()
-            fn()
-            if marks is not None:
-                marks[name][1].record()
+    log(f"{cfg.name}: inputs ready in {time.time() - t0:.1f} s, {torch.cuda.memory_allocated() / 2**30:.1f} GiB "
+        f"resident")
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    calls = [name for name, _ in steps[0]]
 
     for i in range(args.warmup):
-        run_step(events[i])
+        for _, fn in steps[i]:
+            fn()
     torch.cuda.synchronize()
-    if se.se_status_read(status) != 0:
-        raise SystemExit("device status error during warmup")
-    marks = [{n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for n in calls}
+    marks = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in calls]
              for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(args.steps):
-        run_step(events[args.warmup + i], marks[i])
+        for (name, fn), (e0, e1) in zip(steps[args.warmup + i], marks[i]):
+            e0.record()
+            fn()
+            e1.record()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
-    st = se.se_status_read(status)
-    if st != 0:
-        raise SystemExit(f"device status error {st}")
-    per_call_ms = {n: float(np.mean([m[n][0].elapsed_time(m[n][1]) for m in marks])) for n in calls}
+    if se.se_status_read(status) != 0:
+        raise SystemExit("device status error")
+    per_call_ms = {n: float(np.mean([m[j][0].elapsed_time(m[j][1]) for m in marks])) for j, n in enumerate(calls)}
     log("per call ms: " + ", ".join(f"{k} {v:.4f}" for k, v in per_call_ms.items()))
     ms_per_step = elapsed * 1e3 / args.steps
-    tokens = cfg.B * cfg.N
-    alg = algorithmic(cfg)
 
-    def roof(name, bound):
+    def roof(name):
         t = per_call_ms[name] * 1e-3
-        if bound == "hbm":
-            a = alg[name]["bytes"] / t / 1e9
-            return {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(a / HBM_PEAK_GBS, 4)}
-        a = alg[name]["flops"] / t / 1e12
-        return {"bound": "mfma", "achieved": round(a, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(a / MFMA_BF16_PEAK_TFLOPS, 4)}
+        a = alg[name]["bytes"] / t / 1e9
+        return {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(a / HBM_PEAK_GBS, 4)}
 
     dominant = max(per_call_ms, key=per_call_ms.get)
-    roofline = roof(dominant, "hbm")
+    roofline = roof(dominant)
     roofline["kernel"] = dominant
     roofline["traffic"] = None
-    breakdown = {n: dict(ms=round(per_call_ms[n], 4), **{k: v for k, v in roof(n, "hbm").items() if k != "bound"})
+    breakdown = {n: dict(ms=round(per_call_ms[n], 4), **{k: v for k, v in roof(n).items() if k != "bound"})
                  for n in calls}
-    breakdown["se_window_score"]["mfma_tflops_one_pass"] = roof("se_window_score", "mfma")["achieved"]
-
+    for n in calls:
+        if "flops" in alg[n]:
+            breakdown[n]["mfma_tflops_one_pass"] = round(alg[n]["flops"] / (per_call_ms[n] * 1e-3) / 1e12, 1)
     result = {
         "metric": "KV tokens scored+compacted/s",
         "value": round(tokens / (ms_per_step * 1e-3), 1),
@@ -178,13 +308,12 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": cfg.name, "batch": cfg.B, "seq_len": cfg.N, "q_heads": cfg.hq, "kv_heads": cfg.hkv,
-                   "head_dim": cfg.d, "window_queries": cfg.wq, "protect": cfg.protect, "keep": cfg.keep + cfg.protect,
-                   "page": cfg.page, "parallelism": "single GPU"},
+                   "head_dim": cfg.d, "page": cfg.page, "parallelism": "single GPU"},
         "roofline": roofline,
         "calls": breakdown,
     }
-    if not args.no_cpu_baseline:
-        del caches, events, base
+    if args.workload == "c1" and not args.no_cpu_baseline:
+        del steps
         torch.cuda.empty_cache()
         log("timing the oracle on the host")
         result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seqs)

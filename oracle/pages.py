@@ -23,14 +23,16 @@ def page_bounds_build(cache):
     for b in range(B):
         for g in range(n_kv):
             n = int(cache.n_slots[b, g])
-            for p in range(-(-n // page)):
-                blk = cache.block_table[b, p]
-                rows = [i for i in range(page) if p * page + i < n and cache.pos_map[b, g, p * page + i] >= 0]
-                if not rows:
-                    continue
-                k = widen(cache.k_pool[blk, g, rows], cache.dtype)
-                meta[b, g, p, 0] = k.min(axis=0)
-                meta[b, g, p, 1] = k.max(axis=0)
+            n_pages = -(-n // page)
+            slots = np.arange(n_pages * page)
+            inside = slots < n
+            resident = np.zeros(slots.size, bool)
+            resident[inside] = cache.pos_map[b, g, slots[inside]] >= 0
+            blocks = cache.block_table[b, slots // page]
+            k = widen(cache.k_pool[blocks, g, slots % page], cache.dtype).reshape(n_pages, page, d)
+            keep = resident.reshape(n_pages, page, 1)
+            meta[b, g, :n_pages, 0] = np.where(keep, k, np.inf).min(axis=1)
+            meta[b, g, :n_pages, 1] = np.where(keep, k, -np.inf).max(axis=1)
     if cache.dtype == "f32":
         return meta.astype(f)
     # min/max of bf16 values are bf16 values: narrow exactly back to bit patterns

@@ -108,20 +108,30 @@ __global__ __launch_bounds__(kRowsPerWG) void stats_merge(ScoreArgs a) {
 // and K fragments of the next 64 keys are loaded while the current 64 are multiplied. Logits stay unscaled;
 // the scale (times log2 e) is folded into the exp2 argument.
 constexpr int kSub = 64;
-constexpr int kMaxChunk = 2048;
-constexpr int kMThreads = 512;    // 8 waves x 32 query rows: two waves per SIMD overlap MFMA with VALU work
-constexpr int kMRowsPerWave = 32;
-constexpr int kRB = kMRowsPerWave / 16;  // 16-row MFMA blocks per wave
+constexpr int kMaxChunk = 2048;  // keys per workgroup
 
-struct QFrags {
-  bf16x8 f[kRB][4];  // [row block][k-step]
-  int lim[kRB][4];   // [row block][v]: position limit of S row 4*(l/16)+v of the block (-1: no such row)
+// Workgroup shape: NW waves x RPW query rows (NW * RPW = 256). RPW = 64 halves the LDS reads per key (every wave
+// reads the whole K sub-chunk) and keeps a workgroup under 256 VGPRs and ~56 KiB LDS, so two workgroups share a
+// CU and their barrier phases drift apart, overlapping one's LDS/memory phase with the other's VALU phase.
+template <int RPW>
+struct Shape {
+  static constexpr int RB = RPW / 16;           // 16-row MFMA blocks per wave
+  static constexpr int NW = kRowsPerWG / RPW;   // waves per workgroup
+  static constexpr int NT = NW * 64;            // threads
+  static constexpr int SPT = kSub * 16 / NT;    // 16-byte pieces of a sub-chunk fetched per thread
 };
 
-SE_DEV void load_q(const ScoreArgs &a, int b, int g, int rho_wave, QFrags &qf) {
+template <int RB>
+struct QFrags {
+  bf16x8 f[RB][4];  // [row block][k-step]
+  int lim[RB][4];   // [row block][v]: position limit of S row 4*(l/16)+v of the block (-1: no such row)
+};
+
+template <int RB>
+SE_DEV void load_q(const ScoreArgs &a, int b, int g, int rho_wave, QFrags<RB> &qf) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int rb = 0; rb < kRB; ++rb) {
+  for (int rb = 0; rb < RB; ++rb) {
     int rho = rho_wave + rb * 16 + (lane & 15);
     bool ok = rho < a.R * a.wq;
     const char *row = ok ? q_row(a, b, g, rho, 256) + (lane >> 4) * 16 : nullptr;
@@ -139,6 +149,7 @@ struct Chunk {
 };
 
 // stage the chunk's key positions and pool row indices in LDS; keys that cannot be read get position -1
+template <int NT>
 SE_DEV Chunk stage_chunk(const ScoreArgs &a, int b, int g, int c0, int c1, int rg, int *s_blk, int *s_pos,
                          int *s_row, int *s_mm) {
   Chunk ch;
@@ -152,20 +163,20 @@ SE_DEV Chunk stage_chunk(const ScoreArgs &a, int b, int g, int c0, int c1, int r
     s_mm[1] = -1;          // max position
     s_mm[2] = 0x7fffffff;  // min row limit of the workgroup's rows
   }
-  for (int i = threadIdx.x; i < npg; i += kMThreads) s_blk[i] = a.bt[(int64_t)b * a.max_blocks + ch.pbase + i];
+  for (int i = threadIdx.x; i < npg; i += NT) s_blk[i] = a.bt[(int64_t)b * a.max_blocks + ch.pbase + i];
   __syncthreads();
   const int32_t *pos = a.pos + ((int64_t)b * a.n_kv + g) * a.max_blocks * a.page;
   int mn = 0x7fffffff, mx = -1;
-  constexpr int kPer = kMaxChunk / kMThreads;
+  constexpr int kPer = kMaxChunk / NT;
   int pv[kPer];
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {  // all position loads in flight at once
-    const int key = c0 + threadIdx.x + j * kMThreads;
+    const int key = c0 + threadIdx.x + j * NT;
     pv[j] = key < c1 ? pos[key] : -1;
   }
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
-    const int i = threadIdx.x + j * kMThreads;
+    const int i = threadIdx.x + j * NT;
     if (i >= ch.nsub * kSub) break;
     const int key = c0 + i;
     int p = pv[j], row = 0;
@@ -181,8 +192,8 @@ SE_DEV Chunk stage_chunk(const ScoreArgs &a, int b, int g, int c0, int c1, int r
   }
   atomicMin(&s_mm[0], mn);
   atomicMax(&s_mm[1], mx);
-  if (threadIdx.x < kRowsPerWG) {
-    const int lim = row_limit(a, b, rg * kRowsPerWG + threadIdx.x);
+  for (int r = threadIdx.x; r < kRowsPerWG; r += NT) {
+    const int lim = row_limit(a, b, rg * kRowsPerWG + r);
     if (lim >= 0) atomicMin(&s_mm[2], lim);
   }
   __syncthreads();
@@ -191,34 +202,39 @@ SE_DEV Chunk stage_chunk(const ScoreArgs &a, int b, int g, int c0, int c1, int r
 }
 
 // K staging: 64-key sub-chunks (16 KiB) pass through registers into a double-buffered LDS tile, three
-// sub-chunks ahead of the one being multiplied. Thread t fetches 32 contiguous bytes of key t / 8. In LDS the 4
-// keys of each 1 KiB block are stored as 64 16-byte positions, piece c of key r at position r * 16 + (c ^ swz),
-// swz = 4 * (block % 4) + r: the 16 lanes of a B-fragment read (16 keys, one piece each) hit 16 distinct 16-byte
-// bank groups.
+// sub-chunks ahead of the one being multiplied. Thread t fetches SPT consecutive 16-byte pieces of one key. In LDS
+// the 4 keys of each 1 KiB block are stored as 64 16-byte positions, piece c of key r at position r * 16 + (c ^
+// swz), swz = 4 * (block % 4) + r: the 16 lanes of a B-fragment read (16 keys, one piece each) hit 16 distinct
+// 16-byte bank groups.
 constexpr int kSubBytes = kSub * 256;
 
 SE_DEV int swz(int r, int blk) { return ((blk & 3) << 2) | r; }
 
+template <int SPT>
 struct Stage {
-  u32x4 v[2];
+  u32x4 v[SPT];
 };
 
-SE_DEV void load_stage(const ScoreArgs &a, const Chunk &ch, int sub, const int *s_row, Stage &st) {
+template <int SPT>
+SE_DEV void load_stage(const ScoreArgs &a, const Chunk &ch, int sub, const int *s_row, Stage<SPT> &st) {
   // branch-free so that the compiler's wait counts stay exact: keys that are never read (free, past the chunk or
   // past the last sub-chunk) fetch row 0 of the pool instead and are masked by position later
-  const int kt = threadIdx.x >> 3, q8 = threadIdx.x & 7;
+  constexpr int TPK = 16 / SPT;  // threads per key
+  const int kt = threadIdx.x / TPK, q = threadIdx.x % TPK;
   const int row = sub < ch.nsub ? s_row[sub * kSub + kt] : 0;
-  const char *src = a.k + (int64_t)row * 256 + q8 * 32;
-  st.v[0] = ld16(src);
-  st.v[1] = ld16(src + 16);
+  const char *src = a.k + (int64_t)row * 256 + q * SPT * 16;
+#pragma unroll
+  for (int i = 0; i < SPT; ++i) st.v[i] = ld16(src + i * 16);
 }
 
-SE_DEV void store_stage(const Stage &st, char *slot) {
-  const int kt = threadIdx.x >> 3, q8 = threadIdx.x & 7;
+template <int SPT>
+SE_DEV void store_stage(const Stage<SPT> &st, char *slot) {
+  constexpr int TPK = 16 / SPT;
+  const int kt = threadIdx.x / TPK, q = threadIdx.x % TPK;
   const int blk = kt >> 2, r = kt & 3;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int c = q8 * 2 + i;
+  for (int i = 0; i < SPT; ++i) {
+    const int c = q * SPT + i;
     *reinterpret_cast<u32x4 *>(slot + blk * 1024 + (r * 16 + (c ^ swz(r, blk))) * 16) = st.v[i];
   }
 }
@@ -232,11 +248,12 @@ SE_DEV bf16x8 read_frag(const char *slot, int tt, int ks) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(slot + blk * 1024 + (r * 16 + (piece ^ swz(r, blk))) * 16));
 }
 
-// S tiles of the wave's row blocks x the sub-chunk's 4 key tiles; the k-step loop is outermost so each step
-// issues independent MFMAs
-SE_DEV void mfma_sub(const QFrags &qf, const char *slot, floatx4 (&s)[kRB][4]) {
+// S tiles of the wave's row blocks x the sub-chunk's 4 key tiles; k-step outermost so each step issues RB*4
+// independent MFMAs
+template <int RB>
+SE_DEV void mfma_sub(const QFrags<RB> &qf, const char *slot, floatx4 (&s)[RB][4]) {
 #pragma unroll
-  for (int rb = 0; rb < kRB; ++rb)
+  for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) s[rb][tt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -245,7 +262,7 @@ SE_DEV void mfma_sub(const QFrags &qf, const char *slot, floatx4 (&s)[kRB][4]) {
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) k[tt] = read_frag(slot, tt, ks);
 #pragma unroll
-    for (int rb = 0; rb < kRB; ++rb)
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt)
         s[rb][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf.f[rb][ks], k[tt], s[rb][tt], 0, 0, 0);
@@ -253,13 +270,18 @@ SE_DEV void mfma_sub(const QFrags &qf, const char *slot, floatx4 (&s)[kRB][4]) {
 }
 
 // pass 1 state: running max (unscaled logits) and sum of exp2((s - max) * c) per S row of the lane
+template <int RB>
 struct Stats {
-  float m[kRB][4], l[kRB][4];
+  float m[RB][4], l[RB][4];
 };
 
-template <bool FAST>
-SE_DEV void stats_valu_step(const ScoreArgs &a, const QFrags &qf, int sub, const int *s_pos, const floatx4 (&s)[kRB][4],
-                            Stats &st) {
+// Pass 1 VALU: the running max is only moved (and the sum rescaled) when a logit exceeds it by more than
+// kLazy / c in log2 units; until then terms are exp2 of values up to kLazy, which fp32 holds exactly enough.
+constexpr float kLazy = 8.f;
+
+template <bool FAST, int RB>
+SE_DEV void stats_valu_step(const ScoreArgs &a, const QFrags<RB> &qf, int sub, const int *s_pos,
+                            const floatx4 (&s)[RB][4], Stats<RB> &st) {
   const int lane = threadIdx.x & 63;
   const float c = a.scale_log2;
   int kp[4];
@@ -267,7 +289,7 @@ SE_DEV void stats_valu_step(const ScoreArgs &a, const QFrags &qf, int sub, const
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) kp[tt] = s_pos[sub * kSub + tt * 16 + (lane & 15)];
 #pragma unroll
-  for (int rb = 0; rb < kRB; ++rb) {
+  for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       float x[4];
@@ -276,20 +298,27 @@ SE_DEV void stats_valu_step(const ScoreArgs &a, const QFrags &qf, int sub, const
         x[tt] = s[rb][tt][v];
         if (!FAST) x[tt] = (kp[tt] >= 0 && kp[tt] <= qf.lim[rb][v]) ? x[tt] : -INFINITY;
       }
-      const float mn = fmaxf(fmaxf(st.m[rb][v], fmaxf(x[0], x[1])), fmaxf(x[2], x[3]));
-      const float nmc = -mn * c;
-      float acc = st.l[rb][v] * __builtin_amdgcn_exp2f(fmaf(st.m[rb][v], c, nmc));
+      const float xm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+#ifdef SE_NO_LAZY
+      if (xm > st.m[rb][v]) {
+#else
+      if (__builtin_expect((xm - st.m[rb][v]) * c > kLazy, 0)) {  // rare: move the reference and rescale
+#endif
+        st.l[rb][v] *= __builtin_amdgcn_exp2f((st.m[rb][v] - xm) * c);
+        st.m[rb][v] = xm;
+      }
+      const float nmc = -st.m[rb][v] * c;
+      float acc = st.l[rb][v];
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) acc += __builtin_amdgcn_exp2f(fmaf(x[tt], c, nmc));
       st.l[rb][v] = acc;
-      st.m[rb][v] = mn;
     }
   }
 }
 
-template <bool FAST>
-SE_DEV void colsum_valu_step(const ScoreArgs &a, const QFrags &qf, int sub, const int *s_pos,
-                             const floatx4 (&s)[kRB][4], const float (&ml)[kRB][4], float (*s_col)[kMaxChunk]) {
+template <bool FAST, int RB, int NW>
+SE_DEV void colsum_valu_step(const ScoreArgs &a, const QFrags<RB> &qf, int sub, const int *s_pos,
+                             const floatx4 (&s)[RB][4], const float (&ml)[RB][4], float (*s_col)[kMaxChunk]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const float c = a.scale_log2;
   int kp[4];
@@ -298,7 +327,7 @@ SE_DEV void colsum_valu_step(const ScoreArgs &a, const QFrags &qf, int sub, cons
     for (int tt = 0; tt < 4; ++tt) kp[tt] = s_pos[sub * kSub + tt * 16 + (lane & 15)];
   float col[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int rb = 0; rb < kRB; ++rb) {
+  for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
 #pragma unroll
@@ -316,37 +345,38 @@ SE_DEV void colsum_valu_step(const ScoreArgs &a, const QFrags &qf, int sub, cons
   }
 }
 
-template <int PASS>
-__global__ __launch_bounds__(kMThreads) void window_mfma(ScoreArgs a) {
-  constexpr int kWaves = kMThreads / 64;
+template <int PASS, int RPW>
+__global__ __launch_bounds__(Shape<RPW>::NT) void window_mfma(ScoreArgs a) {
+  using S = Shape<RPW>;
+  constexpr int RB = S::RB, NW = S::NW, NT = S::NT, SPT = S::SPT;
   const int unit = blockIdx.z, rg = blockIdx.y, kc = blockIdx.x;
   const int b = unit / a.n_kv, g = unit % a.n_kv;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  __shared__ __attribute__((aligned(1024))) char s_k[3][kSubBytes];
+  __shared__ __attribute__((aligned(1024))) char s_k[2][kSubBytes];
   __shared__ int s_blk[kMaxChunk / 16 + 2];
   __shared__ int s_pos[kMaxChunk];
   __shared__ int s_row[kMaxChunk];
   __shared__ int s_mm[3];
-  __shared__ float s_col[PASS == 2 ? kWaves : 1][PASS == 2 ? kMaxChunk : 1];
+  __shared__ float s_col[PASS == 2 ? NW : 1][PASS == 2 ? kMaxChunk : 1];
   int k0, k1, n;
   key_range(a, unit, k0, k1, n);
   const int c0 = k0 + kc * a.kc, c1 = min(c0 + a.kc, k1);
   if (PASS == 2 && c0 >= c1) return;  // uniform: nothing to score in this chunk
-  const Chunk ch = stage_chunk(a, b, g, c0, max(c0, c1), rg, s_blk, s_pos, s_row, s_mm);
+  const Chunk ch = stage_chunk<NT>(a, b, g, c0, max(c0, c1), rg, s_blk, s_pos, s_row, s_mm);
   // sub-chunks 0..2 in flight before anything else
-  Stage st0, st1, st2;
+  Stage<SPT> st0, st1, st2;
   load_stage(a, ch, 0, s_row, st0);
   load_stage(a, ch, 1, s_row, st1);
   load_stage(a, ch, 2, s_row, st2);
-  const int rho_wave = rg * kRowsPerWG + wave * kMRowsPerWave;
-  QFrags qf;
+  const int rho_wave = rg * kRowsPerWG + wave * RPW;
+  QFrags<RB> qf;
   load_q(a, b, g, rho_wave, qf);
 
-  Stats st;
-  float ml[kRB][4];
+  Stats<RB> st;
+  float ml[RB][4];
   if (PASS == 1) {
 #pragma unroll
-    for (int rb = 0; rb < kRB; ++rb)
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         st.m[rb][v] = -1e30f;
@@ -355,46 +385,39 @@ __global__ __launch_bounds__(kMThreads) void window_mfma(ScoreArgs a) {
   } else {
     const float *mlog = a.mlog + ((int64_t)unit * a.nrg + rg) * kRowsPerWG;
 #pragma unroll
-    for (int rb = 0; rb < kRB; ++rb)
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int v = 0; v < 4; ++v)
-        ml[rb][v] = qf.lim[rb][v] >= 0 ? mlog[wave * kMRowsPerWave + rb * 16 + (lane >> 4) * 4 + v] : INFINITY;
+        ml[rb][v] = qf.lim[rb][v] >= 0 ? mlog[wave * RPW + rb * 16 + (lane >> 4) * 4 + v] : INFINITY;
   }
-  // Sub-chunk j: fetched into stage j % 3 at step j - 3 (or up front), written to LDS buffer j % 3 at step j - 2,
-  // multiplied (MFMA) at step j - 1 and turned into softmax statistics / column sums (VALU) at step j. Issuing the
-  // MFMAs of the next sub-chunk before the VALU work of this one lets the matrix core run while the VALU works.
+  // sub-chunk j is fetched into stage j % 3 at step j - 3, written to LDS buffer j % 2 at step j - 1 (before that
+  // step's barrier) and multiplied at step j
   store_stage(st0, s_k[0]);
-  store_stage(st1, s_k[1]);
   __syncthreads();
   load_stage(a, ch, 3, s_row, st0);
-  load_stage(a, ch, 4, s_row, st1);
-  floatx4 acc_a[kRB][4], acc_b[kRB][4];
-  mfma_sub(qf, s_k[0], acc_a);
-#define SE_STEP(FAST, SUB, CUR, NXT, NEXT_BUF, STORE_BUF, STAGE)                                                \
+#define SE_STEP(FAST, SUB, NEXT_STAGE)                                                                         \
   if ((SUB) < ch.nsub) {                                                                                       \
-    if ((SUB) + 1 < ch.nsub) mfma_sub(qf, s_k[NEXT_BUF], NXT);                                                 \
-    if constexpr (PASS == 1) stats_valu_step<FAST>(a, qf, (SUB), s_pos, CUR, st);                              \
-    else colsum_valu_step<FAST>(a, qf, (SUB), s_pos, CUR, ml, s_col);                                          \
+    floatx4 sacc[RB][4];                                                                                       \
+    mfma_sub(qf, s_k[(SUB) & 1], sacc);                                                                        \
+    if constexpr (PASS == 1) stats_valu_step<FAST>(a, qf, (SUB), s_pos, sacc, st);                            \
+    else colsum_valu_step<FAST, RB, NW>(a, qf, (SUB), s_pos, sacc, ml, s_col);                                 \
   }                                                                                                            \
-  store_stage(STAGE, s_k[STORE_BUF]);                                                                          \
+  store_stage(NEXT_STAGE, s_k[((SUB) + 1) & 1]);                                                               \
   __syncthreads();                                                                                             \
-  load_stage(a, ch, (SUB) + 5, s_row, STAGE);
-  // step s: MFMA buffer (s + 1) % 3, store buffer / stage (s + 2) % 3; accumulators alternate
-#define SE_SIX(FAST)                                                                                            \
-  for (int sub = 0; sub < ch.nsub; sub += 6) {                                                                 \
-    SE_STEP(FAST, sub, acc_a, acc_b, 1, 2, st2)                                                                \
-    SE_STEP(FAST, sub + 1, acc_b, acc_a, 2, 0, st0)                                                            \
-    SE_STEP(FAST, sub + 2, acc_a, acc_b, 0, 1, st1)                                                            \
-    SE_STEP(FAST, sub + 3, acc_b, acc_a, 1, 2, st2)                                                            \
-    SE_STEP(FAST, sub + 4, acc_a, acc_b, 2, 0, st0)                                                            \
-    SE_STEP(FAST, sub + 5, acc_b, acc_a, 0, 1, st1)                                                            \
-  }
+  load_stage(a, ch, (SUB) + 4, s_row, NEXT_STAGE);
   if (ch.fast) {
-    SE_SIX(true)
+    for (int sub = 0; sub < ch.nsub; sub += 3) {
+      SE_STEP(true, sub, st1)
+      SE_STEP(true, sub + 1, st2)
+      SE_STEP(true, sub + 2, st0)
+    }
   } else {
-    SE_SIX(false)
+    for (int sub = 0; sub < ch.nsub; sub += 3) {
+      SE_STEP(false, sub, st1)
+      SE_STEP(false, sub + 1, st2)
+      SE_STEP(false, sub + 2, st0)
+    }
   }
-#undef SE_SIX
 #undef SE_STEP
 
   if constexpr (PASS == 1) {
@@ -402,29 +425,34 @@ __global__ __launch_bounds__(kMThreads) void window_mfma(ScoreArgs a) {
     float *out = a.stats + ((((int64_t)unit * a.nrg + rg) * a.nkc + kc) * kRowsPerWG) * 2;
     const float c = a.scale_log2;
 #pragma unroll
-    for (int rb = 0; rb < kRB; ++rb)
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const float mr = row16_max(st.m[rb][v]);
         const float lr = row16_sum(st.l[rb][v] * __builtin_amdgcn_exp2f((st.m[rb][v] - mr) * c));
         if ((lane & 15) == 0) {
-          const int r = wave * kMRowsPerWave + rb * 16 + (lane >> 4) * 4 + v;
+          const int r = wave * RPW + rb * 16 + (lane >> 4) * 4 + v;
           out[r * 2] = mr * c;
           out[r * 2 + 1] = lr;
         }
       }
   } else {
     __syncthreads();
-    for (int j = threadIdx.x; j < c1 - c0; j += kMThreads) {
+    for (int j = threadIdx.x; j < c1 - c0; j += NT) {
       float sum = 0.f;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) sum += s_col[w][j];
+      for (int w = 0; w < NW; ++w) sum += s_col[w][j];
       const int idx = c0 + j - k0;
       if (a.nrg == 1) a.scores[(int64_t)unit * a.score_stride + idx] = sum;
       else a.colpart[((int64_t)unit * a.nrg + rg) * a.key_span + idx] = sum;
     }
   }
 }
+
+#ifndef SE_SCORE_RPW
+#define SE_SCORE_RPW 32
+#endif
+constexpr int kScoreRPW = SE_SCORE_RPW;
 
 // ---- VALU path (fp32 inputs, or any d that fits) ---------------------------------------------------------------
 template <int DTYPE, int D>
@@ -606,9 +634,10 @@ extern "C" int32_t se_window_score(const se_cache_t *c, const void *q_win, const
   const dim3 grid(pl.nkc, pl.nrg, units);
   hipStream_t st = (hipStream_t)stream;
   if (mfma) {
-    hipLaunchKernelGGL(se::window_mfma<1>, grid, dim3(se::kMThreads), 0, st, a);
+    constexpr int nt = se::Shape<se::kScoreRPW>::NT;
+    hipLaunchKernelGGL((se::window_mfma<1, se::kScoreRPW>), grid, dim3(nt), 0, st, a);
     hipLaunchKernelGGL(se::stats_merge, dim3(pl.nrg, units), dim3(se::kRowsPerWG), 0, st, a);
-    hipLaunchKernelGGL(se::window_mfma<2>, grid, dim3(se::kMThreads), 0, st, a);
+    hipLaunchKernelGGL((se::window_mfma<2, se::kScoreRPW>), grid, dim3(nt), 0, st, a);
   } else {
     hipLaunchKernelGGL((se::stats_valu<SE_DTYPE_F32, 64>), grid, dim3(se::kThreads), 0, st, a);
     hipLaunchKernelGGL((se::colsum_valu<SE_DTYPE_F32, 64>), grid, dim3(se::kThreads), 0, st, a);

@@ -1,0 +1,200 @@
+"""Parity at the workloads' full sizes, in the launch configuration the benchmark uses.
+
+The GPU runs every sequence; the oracle recomputes a sample of sequences (its cost is the limit), and properties
+that hold at any size are checked on all of them: score rows sum to the number of query rows, the retained sets
+match the oracle's modulo near-ties, the compacted cache is the gather of the original by the GPU's own retained
+indices, and the free list conserves blocks.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_decode_attention_se_amd as se
+import workloads as W
+from gpu_util import (DEV, assert_scores_close, assert_sets_match_modulo_ties, i32, lists_from, resident_rows,
+                      status_word, storage_tensor, to_device)
+from oracle import pipelines as P
+from sparse_decode_attention_se_amd import workflows as WF
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+
+def banner(name):
+    print(f"\n[case] {name}", flush=True)
+
+
+def subcache(c: W.CacheState, seqs):
+    """The sequences `seqs` of a cache as a cache of their own (blocks renumbered in order; spare pool empty)."""
+    seqs = list(seqs)
+    nbs = [int(np.count_nonzero(c.block_table[b] >= 0)) for b in seqs]
+    total = sum(nbs)
+    out = W.empty_cache(len(seqs), c.n_kv, c.d, c.page, c.max_blocks, total + len(seqs) * 2, c.dtype,
+                        slot_cap=c.slot_stack.shape[2], with_meta=c.page_meta is not None,
+                        with_cum=c.cum_score is not None)
+    nxt = 0
+    for i, b in enumerate(seqs):
+        for lb in range(nbs[i]):
+            out.k_pool[nxt] = c.k_pool[c.block_table[b, lb]]
+            out.v_pool[nxt] = c.v_pool[c.block_table[b, lb]]
+            out.block_table[i, lb] = nxt
+            nxt += 1
+        for f in ("pos_map", "ctx_len", "n_slots", "slot_stack", "slot_top"):
+            getattr(out, f)[i] = getattr(c, f)[b]
+        if c.cum_score is not None:
+            out.cum_score[i] = c.cum_score[b]
+    spare = np.arange(out.num_blocks - 1, nxt - 1, -1, dtype=np.int32)
+    out.free_blocks[:spare.size] = spare
+    out.free_top[0] = spare.size
+    return out
+
+
+def test_snapkv_llama8b_full_size():
+    banner("SnapKV Llama-8B shape, 8 x 32768 (oracle on sequences 0 and 7)")
+    cfg = W.C1
+    inp = W.gen_snapkv(cfg, seed=0, threads=16)
+    dc = to_device(inp["cache"], cfg.hq)
+    status = status_word()
+    ev = WF.SnapKVEvent(dc, wq=cfg.wq, protect=cfg.protect, keep=cfg.keep, scale=inp["scale"], status=status)
+    ev.score(storage_tensor(inp["q_win"], "bf16"), i32(inp["q_pos"]))
+    scores = ev.scores.cpu().numpy()
+    ev.select()
+    keep = lists_from(ev.idx, ev.count)
+    ev.compact()
+    ev.decode(storage_tensor(inp["q_dec"], "bf16"))
+    out = ev.out.cpu().numpy()
+    assert se.se_status_read(status) == 0
+    r = cfg.hq // cfg.hkv
+    np.testing.assert_allclose(scores[:, :, :cfg.N].sum(axis=2), r * cfg.wq, rtol=1e-4)
+    dev = dc.to_numpy()
+    # every unit: the compacted cache is the gather of the original by the GPU's retained indices
+    orig = inp["cache"]
+    for b in range(cfg.B):
+        for g in range(cfg.hkv):
+            idx = keep[b][g]
+            assert len(idx) == cfg.keep + cfg.protect and np.all(np.diff(idx) > 0)
+            assert idx[-cfg.protect:].tolist() == list(range(cfg.N - cfg.protect, cfg.N))
+            new = resident_rows(dev, cfg.page, "k_pool", b, g, len(idx))
+            old = resident_rows({"k_pool": orig.k_pool, "block_table": orig.block_table}, cfg.page, "k_pool", b, g,
+                                cfg.N)[idx]
+            np.testing.assert_array_equal(new, old)
+            np.testing.assert_array_equal(dev["pos_map"][b, g, :len(idx)], idx)
+    used = dev["block_table"][dev["block_table"] >= 0].tolist()
+    free = dev["free_blocks"][:dev["free_top"][0]].tolist()
+    assert sorted(used + free) == list(range(orig.num_blocks))
+    # sampled sequences against the oracle
+    for b in (0, 7):
+        sub = dict(inp, cfg=W.scaled(cfg, B=1), cache=subcache(orig, [b]), q_win=inp["q_win"][b:b + 1],
+                   q_pos=inp["q_pos"][b:b + 1], q_dec=inp["q_dec"][b:b + 1])
+        ref = P.snapkv_event(sub)
+        assert_scores_close(scores[b:b + 1, :, :cfg.N], ref["scores"][:, :, :cfg.N], mass=np.full((1, cfg.hkv),
+                                                                                                   r * cfg.wq))
+        for g in range(cfg.hkv):
+            nsw = assert_sets_match_modulo_ties(keep[b][g], ref["keep"][0][g], ref["scores"][0, g],
+                                                floor=1e-6 * r * cfg.wq)
+            if nsw == 0:
+                np.testing.assert_allclose(out[b, g * r:(g + 1) * r], ref["out"][0, g * r:(g + 1) * r], atol=2e-3,
+                                           rtol=0)
+
+
+def test_quest_128k_full_size():
+    banner("Quest, 2 x 131072")
+    cfg = W.C3
+    inp = W.gen_quest(cfg, seed=0, threads=16)
+    ref = P.quest_step(inp)
+    dc = to_device(inp["cache"], cfg.hq)
+    status = status_word()
+    qs = WF.QuestStep(dc, top_pages=cfg.top_pages, scale=inp["scale"], status=status)
+    qs.build()
+    out = qs.run(storage_tensor(inp["q_dec"], "bf16")).cpu().numpy()
+    assert se.se_status_read(status) == 0
+    meta = dc.page_meta.view(torch.int16).cpu().numpy().view(np.uint16)
+    np.testing.assert_array_equal(meta, ref["meta"])
+    ps = qs.page_scores.cpu().numpy()
+    np.testing.assert_allclose(ps, ref["page_scores"], rtol=1e-3, atol=1e-3)
+    got = lists_from(qs.pages, qs.count)
+    r = cfg.hq // cfg.hkv
+    for b in range(cfg.B):
+        for g in range(cfg.hkv):
+            assert len(got[b][g]) == cfg.top_pages + 2 and got[b][g][0] == 0 and got[b][g][-1] == cfg.N // 16 - 1
+            nsw = assert_sets_match_modulo_ties(got[b][g], ref["pages"][b][g], ref["page_scores"][b, g])
+            if nsw == 0:
+                np.testing.assert_allclose(out[b, g * r:(g + 1) * r], ref["out"][b, g * r:(g + 1) * r], atol=2e-3,
+                                           rtol=0)
+
+
+def test_h2o_full_size_first_steps():
+    banner("H2O, 64 x 8192, 12 steps (oracle on sequence 0)")
+    cfg = W.scaled(W.C4, steps=12)
+    inp = W.gen_h2o(cfg, seed=0, threads=16)
+    dc = to_device(inp["cache"], cfg.hq)
+    status = status_word()
+    step = WF.H2OStep(dc, scale=inp["scale"], budget=cfg.budget, recent=cfg.recent, status=status)
+    sub_inp = dict(inp, cfg=W.scaled(cfg, B=1), cache=subcache(inp["cache"], [0]), k_new=inp["k_new"][:, :1],
+                   v_new=inp["v_new"][:, :1], q_steps=inp["q_steps"][:, :1])
+    st = sub_inp["cache"]
+    r = cfg.hq // cfg.hkv
+    diverged = np.zeros(cfg.hkv, bool)
+    for s in range(cfg.steps):
+        st, info = P.h2o_step(sub_inp, st, s)
+        pos = np.full((cfg.B,), cfg.N + s, np.int32)
+        o = step.run(storage_tensor(inp["k_new"][s], "bf16"), storage_tensor(inp["v_new"][s], "bf16"), i32(pos),
+                     storage_tensor(inp["q_steps"][s], "bf16")).cpu().numpy()
+        ev = lists_from(step.evict, step.evict_count)
+        assert all(len(ev[b][g]) == 1 for b in range(cfg.B) for g in range(cfg.hkv))
+        for g in range(cfg.hkv):
+            if diverged[g]:
+                continue
+            np.testing.assert_allclose(o[0, g * r:(g + 1) * r], info["out"][0, g * r:(g + 1) * r], atol=2e-3, rtol=0)
+            if assert_sets_match_modulo_ties(ev[0][g], info["evict"][0][g], info["cum"][0, g],
+                                             floor=1e-6 * r * (s + 1)):
+                diverged[g] = True
+    assert se.se_status_read(status) == 0
+    dev = dc.to_numpy()
+    assert np.all(dev["ctx_len"] == cfg.budget) and np.all(dev["n_slots"] == cfg.N + 1)
+    assert diverged.mean() <= 0.5
+
+
+def test_kara_full_size_event():
+    banner("Kara, 128 x 16384: one event + 4 decode steps (oracle on sequences 0 and 127)")
+    cfg = W.scaled(W.C2, period=4)
+    inp = W.gen_kara(cfg, seed=0, threads=16)
+    dc = to_device(inp["cache"], cfg.hq)
+    status = status_word()
+    ev = WF.KaraEvent(dc, window=cfg.window, protect=cfg.protect, n_cand=cfg.n_cand, budget=cfg.budget,
+                      max_gap=cfg.max_gap, scale=inp["scale"], status=status)
+    q_win = P.kara_window_queries(inp, inp["cache"])
+    ev.run(storage_tensor(q_win, "bf16"))
+    scores = ev.scores.cpu().numpy()
+    cand = lists_from(ev.cand, ev.cand_count)
+    keep = lists_from(ev.keep, ev.keep_count)
+    step = WF.DecodeStep(dc, scale=inp["scale"], status=status)
+    outs = []
+    for s in range(cfg.period):
+        pos = np.full((cfg.B,), cfg.N + s, np.int32)
+        q = np.ascontiguousarray(inp["q_all"][:, :, cfg.N + s - inp["q_first_pos"]])
+        outs.append(step.run(storage_tensor(inp["k_new"][s], "bf16"), storage_tensor(inp["v_new"][s], "bf16"), i32(pos),
+                             storage_tensor(q, "bf16")).cpu().numpy())
+    assert se.se_status_read(status) == 0
+    r = cfg.hq // cfg.hkv
+    np.testing.assert_allclose(scores.sum(axis=2), r * cfg.window, rtol=1e-4)
+    for b in range(cfg.B):
+        for g in range(cfg.hkv):
+            assert cfg.n_cand + cfg.protect <= len(keep[b][g]) <= cfg.budget + cfg.protect
+    for b in (0, cfg.B - 1):
+        sub = dict(inp, cfg=W.scaled(cfg, B=1), cache=subcache(inp["cache"], [b]), q_all=inp["q_all"][b:b + 1],
+                   k_new=inp["k_new"][:, b:b + 1], v_new=inp["v_new"][:, b:b + 1])
+        ref = P.kara_event(sub, sub["cache"])
+        assert_scores_close(scores[b:b + 1], ref["scores"], mass=np.full((1, cfg.hkv), r * cfg.window))
+        st = ref["cache"]
+        exact = []
+        for g in range(cfg.hkv):
+            nsw = assert_sets_match_modulo_ties(cand[b][g], ref["cand"][0][g], ref["scores"][0, g],
+                                                base=cfg.N - cfg.window, floor=1e-6 * r * cfg.window)
+            exact.append(nsw == 0 and keep[b][g].tolist() == ref["keep"][0][g].tolist())
+        for s in range(cfg.period):
+            st, o_ref = P.kara_decode_step(sub, st, s)
+            for g in range(cfg.hkv):
+                if exact[g]:
+                    np.testing.assert_allclose(outs[s][b, g * r:(g + 1) * r], o_ref[0, g * r:(g + 1) * r], atol=2e-3,
+                                               rtol=0)
