@@ -49,6 +49,124 @@ def device_cache(se, cfg, c, dev):
                                                                   if getattr(c, f, None) is not None})
 
 
+# kernels each call launches (for matching profiler rows to calls) and the sources they are built from
+CALL_KERNELS = {
+    "se_window_score": ["window_mfma", "stats_merge", "colsum_reduce", "stats_valu", "colsum_valu"],
+    "se_topk_select": ["topk_kernel"],
+    "se_token2chunk": ["t2c_kernel"],
+    "se_compact_evict": ["gather_move", "gather_finalize", "evict_slots_kernel"],
+    "se_cache_append": ["append_kernel"],
+    "se_page_bounds": ["pages_score", "pages_build"],
+    "se_sparse_decode_attn": ["decode_partial", "decode_merge", "decode_cum"],
+}
+CALL_SOURCES = {
+    "se_window_score": "score.hip", "se_topk_select": "topk.hip", "se_token2chunk": "t2c.hip",
+    "se_compact_evict": "compact.hip", "se_cache_append": "compact.hip", "se_page_bounds": "pages.hip",
+    "se_sparse_decode_attn": "decode.hip",
+}
+CSRC = os.path.join(ROOT, "sparse_decode_attention_se_amd", "csrc")
+
+
+def source_digest(call):
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in (CALL_SOURCES[call], "common.hpp"):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def call_of(kernel_name):
+    for call, ks in CALL_KERNELS.items():
+        if any(k in kernel_name for k in ks):
+            return call
+    return None
+
+
+def measured_traffic(workload, call):
+    """HBM bytes per call from the committed counter summary of this workload, or None when that summary is
+    missing or the call's sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        f = line.split()
+        if len(f) >= 4 and f[0] == "traffic" and f[1] == call:
+            kv = dict(x.split("=", 1) for x in f[2:] if "=" in x)
+            if kv.get("sources") != source_digest(call):
+                return None
+            return int(float(kv["bytes"]))
+    return None
+
+
+def read_csv(path):
+    import csv
+
+    with open(path, newline="") as fh:
+        return list(csv.DictReader(fh))
+
+
+def summarize_profile(directories, calls_per_run, copy_bytes, fetch_factor, write_factor):
+    """Text summary of rocprofv3 CSV output directories: per-kernel duration statistics (kernel trace), per-kernel
+    counter averages and per-call counter sums (counter collection). With both FETCH_SIZE and WRITE_SIZE present,
+    prints one ``traffic`` line per call: HBM bytes per call, each counter divided by the factor a plain copy of
+    known size reads for it, tagged with a digest of the call's sources. Kernels dispatched fewer times than
+    there were calls (set-up work outside the step) are left out of the per-call sums."""
+    import glob
+
+    out = []
+    per_call = {}
+    for directory in directories:
+        for path in sorted(glob.glob(os.path.join(directory, "**", "*_kernel_stats.csv"), recursive=True)):
+            out.append(f"kernel statistics ({os.path.basename(path)}):")
+            out.append(f"{'calls':>6} {'avg us':>10} {'min us':>10} {'max us':>10}  kernel")
+            for r in read_csv(path):
+                out.append(f"{int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} "
+                           f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f}  {r['Name'][:110]}")
+        for path in sorted(glob.glob(os.path.join(directory, "**", "*_counter_collection.csv"), recursive=True)):
+            per_kernel = {}
+            for r in read_csv(path):
+                pk = per_kernel.setdefault((r["Kernel_Name"], r["Counter_Name"]), [0.0, 0])
+                pk[0] += float(r["Counter_Value"])
+                pk[1] += 1
+            out.append(f"counters ({os.path.basename(path)}), per dispatch:")
+            for (name, ctr), (tot, n) in sorted(per_kernel.items()):
+                c = call_of(name) or ("copy" if copy_bytes and "neg_kernel" in name else None)
+                if c is None:
+                    continue
+                out.append(f"  {ctr:12s} {tot / n:14.1f} KiB avg over {n:3d} dispatches  {name[:100]}")
+                if c == "copy":
+                    out.append(f"calibration {ctr} factor={tot * 1024 / (n * copy_bytes):.4f} "
+                               f"(counter bytes / bytes each copy launch reads or writes)")
+                elif n >= calls_per_run:
+                    per_call[(c, ctr)] = per_call.get((c, ctr), 0.0) + tot / calls_per_run
+    for (c, ctr), kib in sorted(per_call.items()):
+        out.append(f"per-call {c} {ctr}_KiB={kib:.1f}")
+    for c in sorted({c for c, _ in per_call}):
+        if (c, "FETCH_SIZE") in per_call and (c, "WRITE_SIZE") in per_call:
+            fetch = per_call[(c, "FETCH_SIZE")] * 1024 / fetch_factor
+            write = per_call[(c, "WRITE_SIZE")] * 1024 / write_factor
+            out.append(f"traffic {c} bytes={fetch + write:.0f} read={fetch:.0f} written={write:.0f} "
+                       f"sources={source_digest(c)}")
+    return "\n".join(out)
+
+
+def calibrate_copy(mib, reps):
+    """A plain streaming copy of known size (torch's elementwise negation: reads and writes mib MiB per launch), for
+    counter calibration."""
+    import torch
+
+    n = mib * 2**20 // 4
+    x = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        torch.neg(x, out=y)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_launch": n * 4, "launches": reps}), flush=True)
+
+
 # ---------------------------------------------------------------------------------------------------------------
 # workloads: each returns (cfg, steps[list of list of (call name, fn)], tokens per step, algorithmic bytes per call,
 # dominant call, inputs for the CPU baseline)
@@ -233,7 +351,18 @@ def main():
     ap.add_argument("--workload", default="c1", choices=sorted(SETUPS))
     ap.add_argument("--cpu-seqs", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, metavar="MIB", help="run only a plain copy of MIB MiB, --steps times")
+    ap.add_argument("--summarize-profile", metavar="DIR", nargs="+",
+                    help="print a summary of rocprofv3 CSV output directories")
+    ap.add_argument("--fetch-factor", type=float, default=1.0, help="FETCH_SIZE bytes per byte a plain copy reads")
+    ap.add_argument("--write-factor", type=float, default=1.0, help="WRITE_SIZE bytes per byte a plain copy writes")
+    ap.add_argument("--calls-per-run", type=int, default=1, help="calls of each entry point in the profiled run")
+    ap.add_argument("--copy-bytes", type=int, default=0, help="bytes per launch of the calibration copy")
     args = ap.parse_args()
+    if args.summarize_profile:
+        print(summarize_profile(args.summarize_profile, args.calls_per_run, args.copy_bytes, args.fetch_factor,
+                                args.write_factor))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the hot path is per (sequence, KV head) and shards with no exchange; "
               "multi-GPU runs are not part of this build", file=sys.stderr)
@@ -242,6 +371,10 @@ def main():
     if copies > 64:
         print("steps + warmup must be <= 64 (one pristine cache copy is kept per step)", file=sys.stderr)
         sys.exit(2)
+
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy, args.steps)
+        return
 
     import torch
 
@@ -279,8 +412,12 @@ def main():
     log("per call ms: " + ", ".join(f"{k} {v:.4f}" for k, v in per_call_ms.items()))
     ms_per_step = elapsed * 1e3 / args.steps
 
-    def roof(name):
+    def roof(name, bound=None):
         t = per_call_ms[name] * 1e-3
+        if (bound or ("mfma" if "flops" in alg[name] else "hbm")) == "mfma":
+            a = alg[name]["flops"] / t / 1e12
+            return {"bound": "mfma", "achieved": round(a, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(a / MFMA_BF16_PEAK_TFLOPS, 4)}
         a = alg[name]["bytes"] / t / 1e9
         return {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(a / HBM_PEAK_GBS, 4)}
@@ -288,12 +425,13 @@ def main():
     dominant = max(per_call_ms, key=per_call_ms.get)
     roofline = roof(dominant)
     roofline["kernel"] = dominant
-    roofline["traffic"] = None
-    breakdown = {n: dict(ms=round(per_call_ms[n], 4), **{k: v for k, v in roof(n).items() if k != "bound"})
-                 for n in calls}
+    roofline["launches"] = CALL_KERNELS[dominant]
+    roofline["traffic"] = measured_traffic(cfg.name, dominant)
+    breakdown = {}
     for n in calls:
+        breakdown[n] = dict(ms=round(per_call_ms[n], 4), **{k: v for k, v in roof(n, "hbm").items() if k != "bound"})
         if "flops" in alg[n]:
-            breakdown[n]["mfma_tflops_one_pass"] = round(alg[n]["flops"] / (per_call_ms[n] * 1e-3) / 1e12, 1)
+            breakdown[n]["mfma_tflops"] = roof(n, "mfma")["achieved"]
     result = {
         "metric": "KV tokens scored+compacted/s",
         "value": round(tokens / (ms_per_step * 1e-3), 1),
