@@ -107,9 +107,10 @@ int32_t se_window_score(const se_cache_t *c, const void *q_win, const int32_t *q
  * (SnapKV selection; Quest build_decode_selection) and "What it is" (H2O eviction by continuous scores).
  * Output per (b, g): idx[(b*n_kv+g)*out_stride + i], i < count[b*n_kv+g], ascending item ids.
  *  LARGEST / SLOT: items are slots. Candidates are the resident slots of [base, n_slots - protect), with base = 0
- *    (scores indexed by slot) or, if window > 0, base = n_slots - window (scores indexed by slot - base). The
- *    min(k, #candidates) best by (score desc, position asc) are returned together with the resident slots of
- *    the protected tail [n_slots - protect, n_slots).
+ *    (scores indexed by slot) or, if window > 0, base = n_slots - window (scores indexed by slot - base; a
+ *    window longer than n_slots raises SE_DEV_INDEX and gives count 0). The min(k, #candidates) best by
+ *    (score desc, position asc) are returned together with the resident slots of the protected tail
+ *    [n_slots - protect, n_slots).
  *  LARGEST / PAGE: items are logical pages [0, ceil(n_slots/page)), scores indexed by page. With forced_ends
  *    the first and last page are always returned and are not candidates. Order (score desc, page asc).
  *  SMALLEST / SLOT: if ctx_len > budget, returns min(k, ctx_len - budget) slots with the lowest score among the

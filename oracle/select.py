@@ -47,6 +47,8 @@ def topk_largest(scores, cache, k: int, *, window: int = 0, protect: int = 0, un
             n, key, resident = _items(cache, b, g, unit, cache.page)
             if unit == "slot":
                 base = n - window if window > 0 else 0
+                if base < 0:
+                    raise ValueError("window longer than the cache")
                 cand = [i for i in range(base, n - protect) if resident[i]]
                 kept = [i for i in range(max(n - protect, 0), n) if resident[i]]
             else:

@@ -47,16 +47,20 @@ SE_DEV float row16_max(float x) {
   x = fmaxf(x, dpp_f<kRowRor1>(x));
   return x;
 }
-// sum over lanes with the same (lane % 16): the four rows of the wave
+// sum over lanes with the same (lane % 16): the four rows of the wave. v_permlane16_swap with both operands x
+// returns (x of the even row of each row pair, x of the odd row) in every lane of the pair; v_permlane32_swap does
+// the same for the two halves of the wave. Both stay on the VALU (no LDS crossbar).
 SE_DEV float cross_row_sum(float x) {
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
+  auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 SE_DEV float cross_row_max(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
+  auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
 }
 SE_DEV float wave_sum(float x) { return cross_row_sum(row16_sum(x)); }
 SE_DEV float wave_max(float x) { return cross_row_max(row16_max(x)); }

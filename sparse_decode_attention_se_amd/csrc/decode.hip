@@ -92,6 +92,11 @@ struct ViewMap {
   }
 };
 
+// Running maxima move only when a logit exceeds them by more than kLazy (log2 units): until then the weights are
+// exp2 of at most kLazy, which fp32 sums hold without loss, and the rescale of l and acc is skipped.
+constexpr float kLazy = 8.f;
+constexpr int kMaxChunkRows = 1024;
+
 template <int DTYPE, int R>
 __global__ __launch_bounds__(kThreads) void decode_partial(DecodeArgs a) {
   using V = Vec<DTYPE>;
@@ -102,16 +107,57 @@ __global__ __launch_bounds__(kThreads) void decode_partial(DecodeArgs a) {
   const int b = unit / a.n_kv, g = unit % a.n_kv;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lrow = lane >> 4, cl = lane & 15;
-  ViewMap vm(a, unit);
-  if (chunk == 0 && threadIdx.x == 0) {
-    if (!a.sel && vm.n > a.rows_bound) raise(a.status, SE_DEV_CAPACITY);
-    if (a.sel && a.sel_count[unit] * a.page > a.rows_bound) raise(a.status, SE_DEV_CAPACITY);
-  }
+  __shared__ int s_row[kMaxChunkRows];
 
   // the group's query heads, this lane's 16-byte slice of each
   u32x4 q[R];
 #pragma unroll
   for (int h = 0; h < R; ++h) q[h] = ld16(a.q + (((int64_t)b * a.n_kv + g) * R + h) * RB + cl * 16);
+
+  // Resolve the chunk's view rows to pool rows (-1: outside the view or not resident) into LDS. Loads are
+  // issued speculatively (only their addresses are range-checked), so the chain is two rounds deep.
+  const int cap = a.max_blocks * a.page;
+  int n = a.n_slots[unit];
+  n = n < 0 ? 0 : (n > cap ? cap : n);
+  const int32_t *list = a.sel ? a.sel + (int64_t)unit * a.sel_stride : nullptr;
+  int rows;
+  if (list) {
+    const int cnt = a.sel_count[unit], bound = a.rows_bound / a.page;
+    if (chunk == 0 && threadIdx.x == 0 && cnt > bound) raise(a.status, SE_DEV_CAPACITY);
+    rows = (cnt < 0 ? 0 : (cnt > bound ? bound : cnt)) * a.page;
+  } else {
+    if (chunk == 0 && threadIdx.x == 0 && n > a.rows_bound) raise(a.status, SE_DEV_CAPACITY);
+    rows = n < a.rows_bound ? n : a.rows_bound;
+  }
+  const int row0 = chunk * a.chunk_rows;
+  const int n_pages = (n + a.page - 1) / a.page;
+  const int32_t *bt = a.bt + (int64_t)b * a.max_blocks;
+  const int32_t *pos = a.pos + (int64_t)unit * cap;
+  bool bad = false;
+  for (int i = threadIdx.x; i < a.chunk_rows; i += kThreads) {
+    const int r = row0 + i;
+    int v = -1;
+    if (r < a.rows_bound) {
+      const int pi = r / a.page, off = r - pi * a.page;
+      const int p = list ? list[pi] : pi;
+      const int prev = list && pi > 0 ? list[pi - 1] : -1;
+      const bool p_safe = p >= 0 && p < a.max_blocks;
+      const int s = (p_safe ? p : 0) * a.page + off;
+      const int blk = bt[p_safe ? p : 0];
+      const int ps = pos[s];
+      if (r < rows) {
+        const bool p_ok = p_safe && p < n_pages && prev < p;
+        if (!p_ok) {
+          bad = true;
+        } else if (s < n && ps >= 0) {
+          if (blk_ok(blk, a.num_blocks)) v = (blk * a.n_kv + g) * a.page + off;
+          else bad = true;
+        }
+      }
+    }
+    s_row[i] = v;
+  }
+  if (bad) raise(a.status, SE_DEV_INDEX);
 
   float m[R], l[R], acc[R][EPL];
 #pragma unroll
@@ -121,53 +167,42 @@ __global__ __launch_bounds__(kThreads) void decode_partial(DecodeArgs a) {
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
   }
+  __syncthreads();
 
+  // each wave streams a contiguous quarter of the chunk, 16 rows (4 lane-rows x 4) per step, double-buffered
   const int per_wave = a.chunk_rows / 4;
-  const int r_begin = chunk * a.chunk_rows + wave * per_wave;
-  const int r_end = min(r_begin + per_wave, vm.rows);
-  const int32_t *bt = a.bt + (int64_t)b * a.max_blocks;
-  const int32_t *pos = a.pos + (int64_t)unit * a.max_blocks * a.page;
-  bool bad = false;
+  const int w0 = wave * per_wave;
+  int lim = rows - row0 - w0;
+  lim = lim < 0 ? 0 : (lim > per_wave ? per_wave : lim);
+  const int nit = (lim + 15) / 16;
 
-  for (int r0 = r_begin; r0 < r_end; r0 += 4 * kUnroll) {
-    u32x4 kv[kUnroll], vv[kUnroll];
-    int rows[kUnroll];
-    bool valid[kUnroll];
+  auto load = [&](int it, u32x4 (&kb)[kUnroll], u32x4 (&vb)[kUnroll], int (&rv)[kUnroll]) {
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      int r = r0 + u * 4 + lrow;
-      rows[u] = r;
-      int s = r < r_end ? vm.slot(r) : -1;
-      bad |= (s == -2);
-      valid[u] = s >= 0 && pos[s] >= 0;
-      int blk = valid[u] ? bt[s / a.page] : -1;
-      if (valid[u] && (blk < 0 || blk >= a.num_blocks)) {
-        valid[u] = false;
-        bad = true;
-      }
-      if (valid[u]) {
-        int64_t off = (((int64_t)blk * a.n_kv + g) * a.page + (s % a.page)) * RB + cl * 16;
-        kv[u] = ld16(a.k + off);
-        vv[u] = ld16(a.v + off);
-      } else {
-        kv[u] = u32x4{0, 0, 0, 0};
-        vv[u] = u32x4{0, 0, 0, 0};
-      }
+      const int i = it * 16 + u * 4 + lrow;
+      const int v = i < lim ? s_row[w0 + i] : -1;
+      const int64_t off = (int64_t)(v >= 0 ? v : 0) * RB + cl * 16;
+      kb[u] = ld16(a.k + off);
+      vb[u] = ld16(a.v + off);
+      rv[u] = v;
     }
+  };
+  auto step = [&](int it, const u32x4 (&kb)[kUnroll], const u32x4 (&vb)[kUnroll], const int (&rv)[kUnroll]) {
     float sc[kUnroll][R];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
 #pragma unroll
       for (int h = 0; h < R; ++h) {
-        float d = row16_sum(V::dot(q[h], kv[u], 0.f));
-        sc[u][h] = valid[u] ? d * a.scale_log2 : -INFINITY;
+        const float d = row16_sum(V::dot(q[h], kb[u], 0.f));
+        sc[u][h] = rv[u] >= 0 ? d * a.scale_log2 : -INFINITY;
       }
     }
     if (a.logits) {
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
-        if (cl == 0 && rows[u] < r_end) {
-          float *dst = a.logits + ((int64_t)unit * a.rows_bound + rows[u]) * R;
+        const int i = it * 16 + u * 4 + lrow;
+        if (cl == 0 && i < lim) {
+          float *dst = a.logits + ((int64_t)unit * a.rows_bound + row0 + w0 + i) * R;
 #pragma unroll
           for (int h = 0; h < R; ++h) dst[h] = sc[u][h];
         }
@@ -175,29 +210,43 @@ __global__ __launch_bounds__(kThreads) void decode_partial(DecodeArgs a) {
     }
 #pragma unroll
     for (int h = 0; h < R; ++h) {
-      float mn = m[h];
+      float mx = sc[0][h];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) mn = fmaxf(mn, sc[u][h]);
-      float f = __builtin_amdgcn_exp2f(m[h] - mn);
-      m[h] = mn;
-      l[h] *= f;
+      for (int u = 1; u < kUnroll; ++u) mx = fmaxf(mx, sc[u][h]);
+      if (mx > m[h] + kLazy) {
+        const float f = __builtin_amdgcn_exp2f(m[h] - mx);
+        m[h] = mx;
+        l[h] *= f;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[h][e] *= f;
+        for (int e = 0; e < EPL; ++e) acc[h][e] *= f;
+      }
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
+      const bool ok = rv[u] >= 0;  // rows outside the view read row 0 of the pool: drop its values
+      const u32x4 w = {ok ? vb[u].x : 0u, ok ? vb[u].y : 0u, ok ? vb[u].z : 0u, ok ? vb[u].w : 0u};
       float x[EPL];
-      V::widen(vv[u], x);
+      V::widen(w, x);
 #pragma unroll
       for (int h = 0; h < R; ++h) {
-        float p = __builtin_amdgcn_exp2f(sc[u][h] - m[h]);
+        const float p = __builtin_amdgcn_exp2f(sc[u][h] - m[h]);
         l[h] += p;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(p, x[e], acc[h][e]);
       }
     }
+  };
+
+  u32x4 ka[kUnroll], va[kUnroll], kb2[kUnroll], vb2[kUnroll];
+  int ra[kUnroll], rb2[kUnroll];
+  if (nit > 0) load(0, ka, va, ra);
+  for (int it = 0; it < nit; it += 2) {
+    if (it + 1 < nit) load(it + 1, kb2, vb2, rb2);
+    step(it, ka, va, ra);
+    if (it + 1 >= nit) break;
+    if (it + 2 < nit) load(it + 2, ka, va, ra);
+    step(it + 1, kb2, vb2, rb2);
   }
-  if (bad) raise(a.status, SE_DEV_INDEX);
 
   // merge the four lane-rows of the wave
 #pragma unroll
@@ -334,9 +383,9 @@ Plan make_plan(const se_cache_t *c, const se_decode_params_t *p, int has_sel) {
     pl.rows_bound = p->max_slots > 0 && p->max_slots < cap ? p->max_slots : cap;
   }
   pl.units = c->B * c->n_kv;
-  int ch = 512;
-  while (ch > 64 && (long long)pl.units * ((pl.rows_bound + ch - 1) / ch) < 2048) ch /= 2;
-  while ((pl.rows_bound + ch - 1) / ch > kMaxChunks) ch *= 2;
+  // the largest chunk (<= kMaxChunkRows) that still gives >= 8192 workgroups, else the smallest (64 rows)
+  int ch = kMaxChunkRows;
+  while (ch > 64 && (long long)pl.units * ((pl.rows_bound + ch - 1) / ch) < 8192) ch /= 2;
   pl.chunk_rows = ch;
   pl.nchunk = (pl.rows_bound + ch - 1) / ch;
   if (pl.nchunk < 1) pl.nchunk = 1;
@@ -391,6 +440,8 @@ extern "C" int32_t se_sparse_decode_attn(se_cache_t *c, const void *q, const int
   const bool ok_shape = (c->dtype == SE_DTYPE_BF16 && c->d == 128) || (c->dtype == SE_DTYPE_F32 && c->d == 64);
   if (!ok_shape) return SE_ERR_DTYPE;
   se::Plan pl = se::make_plan(c, p, has_sel);
+  if (pl.nchunk > se::kMaxChunks) return SE_ERR_UNSUPPORTED;  // views beyond 4M slots per (sequence, head)
+  if ((long long)c->num_blocks * c->n_kv * c->page >= (1ll << 31)) return SE_ERR_UNSUPPORTED;
   if (ws_bytes < pl.part_bytes + pl.logit_bytes || !ws) return SE_ERR_WORKSPACE;
   se::DecodeArgs a;
   a.k = (const char *)c->k_pool;

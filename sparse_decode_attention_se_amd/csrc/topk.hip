@@ -86,7 +86,17 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
   const int32_t *pos = a.pos + (int64_t)unit * a.max_slots;
   const float *sc = a.scores + (int64_t)unit * a.score_stride;
   const bool page_unit = a.unit_kind == SE_UNIT_PAGE;
-  const int n_items = page_unit ? (n + a.page - 1) / a.page : n;
+  // with a window, the items are the window's slots [base, n); otherwise all slots (or pages) from 0
+  const bool win = !page_unit && a.window > 0;
+  const int base = win ? n - a.window : 0;
+  if (base < 0) {  // a window longer than the cache
+    if (t == 0) {
+      raise(a.status, SE_DEV_INDEX);
+      a.count[unit] = 0;
+    }
+    return;
+  }
+  const int n_items = page_unit ? (n + a.page - 1) / a.page : n - base;
   if (n_items > PER * kThreads) {
     if (t == 0) {
       raise(a.status, SE_DEV_CAPACITY);
@@ -118,7 +128,6 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
   it.cand_mask = 0;
   it.keep_mask = 0;
   int ncand_local = 0;
-  const int base = (!page_unit && a.window > 0) ? n - a.window : 0;
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
     const int i = t * PER + j;
@@ -132,19 +141,19 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
       cand = !end;
       it.tie[j] = (uint32_t)i;
     } else {
-      const int p = pos[i];
+      const int p = pos[base + i];
       if (p < 0) continue;
       if (a.mode == SE_TOPK_SMALLEST) {
         cand = p <= limit;
         it.tie[j] = 0x7fffffffu - (uint32_t)p;
       } else {
-        keep = i >= n - a.protect;
-        cand = !keep && i >= base;
+        keep = base + i >= n - a.protect;
+        cand = !keep;
         it.tie[j] = (uint32_t)p;
       }
     }
     if (cand) {
-      const float s = sc[i - base];
+      const float s = sc[i];
       it.key[j] = a.mode == SE_TOPK_SMALLEST ? ~orderable(s) : orderable(s);
       it.cand_mask |= 1u << j;
       ++ncand_local;
@@ -237,7 +246,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
   }
 #pragma unroll
   for (int j = 0; j < PER; ++j)
-    if ((out_mask >> j) & 1u) out[o++] = t * PER + j;
+    if ((out_mask >> j) & 1u) out[o++] = base + t * PER + j;
   if (t == 0) a.count[unit] = total;
 }
 
@@ -259,7 +268,9 @@ extern "C" int32_t se_topk_select(const se_cache_t *c, const float *scores, cons
   if (p->mode == SE_TOPK_SMALLEST && p->unit != SE_UNIT_SLOT) return SE_ERR_PARAM;
   if (p->window > 0 && p->protect > p->window) return SE_ERR_PARAM;
   const int max_slots = c->max_blocks * c->page;
-  const int n_items = p->unit == SE_UNIT_PAGE ? c->max_blocks : max_slots;
+  const int n_items = p->unit == SE_UNIT_PAGE ? c->max_blocks
+                      : (p->mode == SE_TOPK_LARGEST && p->window > 0 && p->window < max_slots) ? p->window
+                                                                                                : max_slots;
   long long need = p->k;
   if (p->mode == SE_TOPK_LARGEST) need += p->unit == SE_UNIT_PAGE ? (p->forced_ends ? 2 : 0) : p->protect;
   if (p->out_stride < need && p->out_stride < n_items) return SE_ERR_SHAPE;
