@@ -18,9 +18,9 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;
-constexpr int kRowsPerWG = 256;
-constexpr int kRowsPerWave = 64;
+// query rows per workgroup of the fp32 VALU path (one thread per row); the MFMA path picks 128 or 256 per call
+constexpr int kValuRows = 128;
+constexpr int kMaxRowsPerWG = 256;
 
 struct ScoreArgs {
   const char *k;
@@ -34,6 +34,7 @@ struct ScoreArgs {
   int32_t *status;
   int32_t mode, n_kv, R, wq, page, max_blocks, num_blocks, window, protect, score_stride;
   int32_t nrg, nkc, kc, key_span;
+  int32_t rpg;  // query rows per row group (workgroup)
   float scale_log2;
 };
 
@@ -65,15 +66,15 @@ SE_DEV const char *q_row(const ScoreArgs &a, int b, int g, int rho, int row_byte
 
 // merge the per-chunk statistics of this workgroup's 256 rows into log2(sum) + max (or +inf for empty rows)
 SE_DEV float merge_row(const ScoreArgs &a, int unit, int rg, int r) {
-  const float *st = a.stats + (((int64_t)unit * a.nrg + rg) * a.nkc * kRowsPerWG + r) * 2;
+  const float *st = a.stats + (((int64_t)unit * a.nrg + rg) * a.nkc * a.rpg + r) * 2;
   float mm = -1e30f, ll = 0.f;
   int c = 0;
   for (; c + 8 <= a.nkc; c += 8) {  // eight independent loads in flight
     float m8[8], l8[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      m8[i] = st[(int64_t)(c + i) * kRowsPerWG * 2];
-      l8[i] = st[(int64_t)(c + i) * kRowsPerWG * 2 + 1];
+      m8[i] = st[(int64_t)(c + i) * a.rpg * 2];
+      l8[i] = st[(int64_t)(c + i) * a.rpg * 2 + 1];
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -83,7 +84,7 @@ SE_DEV float merge_row(const ScoreArgs &a, int unit, int rg, int r) {
     }
   }
   for (; c < a.nkc; ++c) {
-    const float m1 = st[(int64_t)c * kRowsPerWG * 2], l1 = st[(int64_t)c * kRowsPerWG * 2 + 1];
+    const float m1 = st[(int64_t)c * a.rpg * 2], l1 = st[(int64_t)c * a.rpg * 2 + 1];
     const float mn = fmaxf(mm, m1);
     ll = ll * __builtin_amdgcn_exp2f(mm - mn) + l1 * __builtin_amdgcn_exp2f(m1 - mn);
     mm = mn;
@@ -96,9 +97,9 @@ SE_DEV void merge_stats(const ScoreArgs &a, int unit, int rg, float *s_mlog) {
 }
 
 // one thread per query row: the merged statistics used by the column-sum pass
-__global__ __launch_bounds__(kRowsPerWG) void stats_merge(ScoreArgs a) {
+__global__ __launch_bounds__(kMaxRowsPerWG) void stats_merge(ScoreArgs a) {
   const int unit = blockIdx.y, rg = blockIdx.x;
-  a.mlog[((int64_t)unit * a.nrg + rg) * kRowsPerWG + threadIdx.x] = merge_row(a, unit, rg, threadIdx.x);
+  a.mlog[((int64_t)unit * a.nrg + rg) * a.rpg + threadIdx.x] = merge_row(a, unit, rg, threadIdx.x);
 }
 
 // ---- MFMA path (bf16, d = 128) -------------------------------------------------------------------------------
@@ -108,17 +109,21 @@ __global__ __launch_bounds__(kRowsPerWG) void stats_merge(ScoreArgs a) {
 // and K fragments of the next 64 keys are loaded while the current 64 are multiplied. Logits stay unscaled;
 // the scale (times log2 e) is folded into the exp2 argument.
 constexpr int kSub = 64;
-constexpr int kMaxChunk = 2048;  // keys per workgroup
 
-// Workgroup shape: NW waves x RPW query rows (NW * RPW = 256). RPW = 64 halves the LDS reads per key (every wave
-// reads the whole K sub-chunk) and keeps a workgroup under 256 VGPRs and ~56 KiB LDS, so two workgroups share a
-// CU and their barrier phases drift apart, overlapping one's LDS/memory phase with the other's VALU phase.
-template <int RPW>
+// Workgroup shape: NW waves x RPW query rows, and at most MAXC keys per workgroup (the LDS tables are sized for
+// them). With NW = 4 (128 rows, 1024 keys, ~80 KiB LDS) two workgroups share a CU, so the two waves of each SIMD
+// belong to different workgroups whose barriers are independent and one's MFMA/LDS phases overlap the other's
+// VALU phase; that shape is used when a unit has more than 256 query rows. Otherwise NW = 8 covers all of a
+// unit's rows (up to 256) in one workgroup, so K is read once and no cross-group column sum is needed.
+template <int RPW, int NW_>
 struct Shape {
-  static constexpr int RB = RPW / 16;           // 16-row MFMA blocks per wave
-  static constexpr int NW = kRowsPerWG / RPW;   // waves per workgroup
-  static constexpr int NT = NW * 64;            // threads
-  static constexpr int SPT = kSub * 16 / NT;    // 16-byte pieces of a sub-chunk fetched per thread
+  static constexpr int RB = RPW / 16;            // 16-row MFMA blocks per wave
+  static constexpr int NW = NW_;                 // waves per workgroup
+  static constexpr int NT = NW * 64;             // threads
+  static constexpr int ROWS = NW * RPW;          // query rows per workgroup
+  static constexpr int MAXC = NW >= 8 ? 2048 : 1024;
+  static constexpr int BPW = 16 / NW;            // 1 KiB blocks of a sub-chunk each wave fetches
+  static constexpr int WPS = RPW == 16 ? 4 : 2;  // waves per SIMD the register budget is cut for
 };
 
 template <int RB>
@@ -149,7 +154,7 @@ struct Chunk {
 };
 
 // stage the chunk's key positions and pool row indices in LDS; keys that cannot be read get position -1
-template <int NT>
+template <int NT, int MAXC>
 SE_DEV Chunk stage_chunk(const ScoreArgs &a, int b, int g, int c0, int c1, int rg, int *s_blk, int *s_pos,
                          int *s_row, int *s_mm) {
   Chunk ch;
@@ -167,7 +172,7 @@ SE_DEV Chunk stage_chunk(const ScoreArgs &a, int b, int g, int c0, int c1, int r
   __syncthreads();
   const int32_t *pos = a.pos + ((int64_t)b * a.n_kv + g) * a.max_blocks * a.page;
   int mn = 0x7fffffff, mx = -1;
-  constexpr int kPer = kMaxChunk / NT;
+  constexpr int kPer = MAXC / NT;
   int pv[kPer];
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {  // all position loads in flight at once
@@ -192,8 +197,8 @@ SE_DEV Chunk stage_chunk(const ScoreArgs &a, int b, int g, int c0, int c1, int r
   }
   atomicMin(&s_mm[0], mn);
   atomicMax(&s_mm[1], mx);
-  for (int r = threadIdx.x; r < kRowsPerWG; r += NT) {
-    const int lim = row_limit(a, b, rg * kRowsPerWG + r);
+  for (int r = threadIdx.x; r < a.rpg; r += NT) {
+    const int lim = row_limit(a, b, rg * a.rpg + r);
     if (lim >= 0) atomicMin(&s_mm[2], lim);
   }
   __syncthreads();
@@ -201,42 +206,47 @@ SE_DEV Chunk stage_chunk(const ScoreArgs &a, int b, int g, int c0, int c1, int r
   return ch;
 }
 
-// K staging: 64-key sub-chunks (16 KiB) pass through registers into a double-buffered LDS tile, three
-// sub-chunks ahead of the one being multiplied. Thread t fetches SPT consecutive 16-byte pieces of one key. In LDS
-// the 4 keys of each 1 KiB block are stored as 64 16-byte positions, piece c of key r at position r * 16 + (c ^
-// swz), swz = 4 * (block % 4) + r: the 16 lanes of a B-fragment read (16 keys, one piece each) hit 16 distinct
-// 16-byte bank groups.
+// K staging: 64-key sub-chunks (16 KiB) go from global memory straight into a ring of kRing LDS buffers with LDS
+// DMA (global_load_lds_dwordx4: lane i of a wave writes 16 bytes at M0 + 16 i, no registers involved). In LDS the 4
+// keys of each 1 KiB block are stored as 64 16-byte positions, piece c of key r at position r * 16 + (c ^ swz),
+// swz = 4 * (block % 4) + r: the 16 lanes of a B-fragment read (16 keys, one piece each) hit 16 distinct 16-byte
+// bank groups. So lane i of the DMA that fills a block fetches key r = i / 16, piece (i % 16) ^ swz.
 constexpr int kSubBytes = kSub * 256;
+constexpr int kRing = 4;
 
 SE_DEV int swz(int r, int blk) { return ((blk & 3) << 2) | r; }
 
-template <int SPT>
-struct Stage {
-  u32x4 v[SPT];
-};
-
-template <int SPT>
-SE_DEV void load_stage(const ScoreArgs &a, const Chunk &ch, int sub, const int *s_row, Stage<SPT> &st) {
-  // branch-free so that the compiler's wait counts stay exact: keys that are never read (free, past the chunk or
-  // past the last sub-chunk) fetch row 0 of the pool instead and are masked by position later
-  constexpr int TPK = 16 / SPT;  // threads per key
-  const int kt = threadIdx.x / TPK, q = threadIdx.x % TPK;
-  const int row = sub < ch.nsub ? s_row[sub * kSub + kt] : 0;
-  const char *src = a.k + (int64_t)row * 256 + q * SPT * 16;
-#pragma unroll
-  for (int i = 0; i < SPT; ++i) st.v[i] = ld16(src + i * 16);
+// The DMA is issued as inline assembly so that the compiler's wait-count bookkeeping does not track it (it would
+// otherwise wait for every DMA in flight before any LDS read); the kernel waits for its DMAs itself in publish().
+// The compiler's own waits stay correct: they can only over-count. One wait state separates the M0 write from
+// the DMA that reads it.
+SE_DEV void lds_dma16(const char *g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(g) : "memory", "m0");
 }
 
-template <int SPT>
-SE_DEV void store_stage(const Stage<SPT> &st, char *slot) {
-  constexpr int TPK = 16 / SPT;
-  const int kt = threadIdx.x / TPK, q = threadIdx.x % TPK;
-  const int blk = kt >> 2, r = kt & 3;
+// fetch sub-chunk `sub` of the chunk into ring slot sub % kRing (nothing past the last sub-chunk)
+template <int NW>
+SE_DEV void issue_sub(const ScoreArgs &a, const Chunk &ch, int sub, const int *s_row, uint32_t ring) {
+  if (sub >= ch.nsub) return;  // uniform
+  constexpr int BPW = 16 / NW;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane >> 4;
+  const uint32_t slot = ring + (uint32_t)(sub % kRing) * kSubBytes;
 #pragma unroll
-  for (int i = 0; i < SPT; ++i) {
-    const int c = q * SPT + i;
-    *reinterpret_cast<u32x4 *>(slot + blk * 1024 + (r * 16 + (c ^ swz(r, blk))) * 16) = st.v[i];
+  for (int i = 0; i < BPW; ++i) {
+    const int blk = wave * BPW + i;
+    const int c = (lane & 15) ^ swz(r, blk);
+    const int row = s_row[sub * kSub + blk * 4 + r];
+    lds_dma16(a.k + (int64_t)row * 256 + c * 16, __builtin_amdgcn_readfirstlane(slot + blk * 1024));
   }
+}
+
+// Wait until at most N of this wave's DMAs are still in flight and its LDS accesses are done, then meet the other
+// waves: afterwards every wave's older DMAs have landed. The memory clobber keeps the compiler from moving LDS
+// accesses across.
+template <int N>
+SE_DEV void publish() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
 // B fragment of key tile tt, k-step ks from a staged sub-chunk
@@ -272,176 +282,242 @@ SE_DEV void mfma_sub(const QFrags<RB> &qf, const char *slot, floatx4 (&s)[RB][4]
 // pass 1 state: running max (unscaled logits) and sum of exp2((s - max) * c) per S row of the lane
 template <int RB>
 struct Stats {
-  float m[RB][4], l[RB][4];
+  float l[RB][4];    // sum of exp2((s - m) * c) over the row's keys so far
+  float thr[RB][4];  // m + kLazy / c: a logit above it moves the reference m
+  float nmc[RB][4];  // -m * c (m itself is not kept)
 };
 
-// Pass 1 VALU: the running max is only moved (and the sum rescaled) when a logit exceeds it by more than
-// kLazy / c in log2 units; until then terms are exp2 of values up to kLazy, which fp32 holds exactly enough.
+// Pass 1 VALU: the running max m of a row is only moved (and its sum rescaled) when a logit exceeds it by more than
+// kLazy / c in log2 units; until then terms are exp2 of at most kLazy, which fp32 sums hold exactly enough. The
+// common step is branch-free, so the compiler interleaves it with the next sub-chunk's MFMAs: every row's terms
+// are taken against its stored reference, and rows whose max moved keep their old sum (a select). stats_fix then
+// redoes those rows in a wave-uniform branch that is rarely taken once the first keys have been seen.
 constexpr float kLazy = 8.f;
 
-template <bool FAST, int RB>
-SE_DEV void stats_valu_step(const ScoreArgs &a, const QFrags<RB> &qf, int sub, const int *s_pos,
-                            const floatx4 (&s)[RB][4], Stats<RB> &st) {
-  const int lane = threadIdx.x & 63;
-  const float c = a.scale_log2;
-  int kp[4];
-  if (!FAST)
+// max of four values that are finite or -inf: two v_max3_f32, without the NaN-quieting copies that fmaxf of
+// MFMA results would add
+SE_DEV float max4(float a, float b, float c, float d) {
+  float t, r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(t) : "v"(a), "v"(b), "v"(c));
+  asm("v_max3_f32 %0, %1, %2, %2" : "=v"(r) : "v"(t), "v"(d));
+  return r;
+}
+
+template <int RB>
+SE_DEV void stats_init(const ScoreArgs &a, Stats<RB> &st) {
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) kp[tt] = s_pos[sub * kSub + tt * 16 + (lane & 15)];
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      st.l[rb][v] = 0.f;
+      st.thr[rb][v] = -1e30f;
+      st.nmc[rb][v] = 1e30f;  // m * c = -1e30: the first visible key moves it
+    }
+}
+
+// masks the sub-chunk's logits in place (keys a row may not see become -inf) unless FAST
+template <bool FAST, int RB>
+SE_DEV void mask_logits(const QFrags<RB> &qf, int sub, const int *s_pos, floatx4 (&s)[RB][4]) {
+  if (FAST) return;
+  const int lane = threadIdx.x & 63;
+  int kp[4];
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) kp[tt] = s_pos[sub * kSub + tt * 16 + (lane & 15)];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        s[rb][tt][v] = (kp[tt] >= 0 && kp[tt] <= qf.lim[rb][v]) ? s[rb][tt][v] : -INFINITY;
+}
+
+// returns (per lane) whether any of the lane's rows moved
+template <int RB>
+SE_DEV bool stats_step(const ScoreArgs &a, const floatx4 (&s)[RB][4], Stats<RB> &st) {
+  const float c = a.scale_log2;
+  bool moved = false;
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      float x[4];
+      const float xm = max4(s[rb][0][v], s[rb][1][v], s[rb][2][v], s[rb][3][v]);
+      const bool mv = xm > st.thr[rb][v];
+      moved |= mv;
+      float acc = 0.f;
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        x[tt] = s[rb][tt][v];
-        if (!FAST) x[tt] = (kp[tt] >= 0 && kp[tt] <= qf.lim[rb][v]) ? x[tt] : -INFINITY;
-      }
-      const float xm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-#ifdef SE_NO_LAZY
-      if (xm > st.m[rb][v]) {
-#else
-      if (__builtin_expect((xm - st.m[rb][v]) * c > kLazy, 0)) {  // rare: move the reference and rescale
-#endif
-        st.l[rb][v] *= __builtin_amdgcn_exp2f((st.m[rb][v] - xm) * c);
-        st.m[rb][v] = xm;
-      }
-      const float nmc = -st.m[rb][v] * c;
-      float acc = st.l[rb][v];
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) acc += __builtin_amdgcn_exp2f(fmaf(x[tt], c, nmc));
-      st.l[rb][v] = acc;
+      for (int tt = 0; tt < 4; ++tt) acc += __builtin_amdgcn_exp2f(fmaf(s[rb][tt][v], c, st.nmc[rb][v]));
+      // an empty use: the sum is computed here for every row, branch-free, in the block of the MFMAs it
+      // interleaves with (otherwise the compiler computes it only under !mv, in a divergent branch per row)
+      asm volatile("" ::"v"(acc));
+      st.l[rb][v] = mv ? st.l[rb][v] : st.l[rb][v] + acc;
     }
   }
+  return moved;
 }
 
-template <bool FAST, int RB, int NW>
-SE_DEV void colsum_valu_step(const ScoreArgs &a, const QFrags<RB> &qf, int sub, const int *s_pos,
-                             const floatx4 (&s)[RB][4], const float (&ml)[RB][4], float (*s_col)[kMaxChunk]) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+template <int RB>
+SE_DEV void stats_fix(const ScoreArgs &a, const floatx4 (&s)[RB][4], Stats<RB> &st) {
   const float c = a.scale_log2;
-  int kp[4];
-  if (!FAST)
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) kp[tt] = s_pos[sub * kSub + tt * 16 + (lane & 15)];
-  float col[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
+    for (int v = 0; v < 4; ++v) {
+      const float xm = max4(s[rb][0][v], s[rb][1][v], s[rb][2][v], s[rb][3][v]);
+      if (xm > st.thr[rb][v]) {
+        const float nmc = -xm * c;
+        float acc = st.l[rb][v] * __builtin_amdgcn_exp2f(nmc - st.nmc[rb][v]);
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        float p = __builtin_amdgcn_exp2f(fmaf(s[rb][tt][v], c, -ml[rb][v]));
-        if (!FAST) p = (kp[tt] >= 0 && kp[tt] <= qf.lim[rb][v]) ? p : 0.f;
-        col[tt] += p;
+        for (int tt = 0; tt < 4; ++tt) acc += __builtin_amdgcn_exp2f(fmaf(s[rb][tt][v], c, nmc));
+        st.l[rb][v] = acc;
+        st.thr[rb][v] = xm + kLazy / c;
+        st.nmc[rb][v] = nmc;
       }
     }
   }
+}
+
+template <int RB, int NW>
+SE_DEV void colsum_step(const ScoreArgs &a, const floatx4 (&s)[RB][4], const float (&ml)[RB][4],
+                        float (*s_cs)[kSub]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const float c = a.scale_log2;
+  float col[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int tt = 0; tt < 4; ++tt) {
-    const float cs = cross_row_sum(col[tt]);
-    if (lane < 16) s_col[wave][sub * kSub + tt * 16 + lane] = cs;
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) col[tt] += __builtin_amdgcn_exp2f(fmaf(s[rb][tt][v], c, -ml[rb][v]));
+  // after the cross-row sum the four rows of the wave hold the same column sums: all lanes store, same values
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) s_cs[wave][tt * 16 + (lane & 15)] = cross_row_sum(col[tt]);
+}
+
+// Scheduling groups for one step: per k-step, the 4 B-fragment LDS reads, then its RB*4 MFMAs each followed by NV
+// VALU instructions (of the previous sub-chunk's softmax work).
+template <int RB, int NV>
+SE_DEV void interleave() {
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // DS read
+#pragma unroll
+    for (int i = 0; i < RB * 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);  // VALU
+    }
   }
 }
 
-template <int PASS, int RPW>
-__global__ __launch_bounds__(Shape<RPW>::NT) void window_mfma(ScoreArgs a) {
-  using S = Shape<RPW>;
-  constexpr int RB = S::RB, NW = S::NW, NT = S::NT, SPT = S::SPT;
+template <int PASS, int RPW, int NW_>
+__global__ __launch_bounds__((Shape<RPW, NW_>::NT), (Shape<RPW, NW_>::WPS)) void window_mfma(ScoreArgs a) {
+  using S = Shape<RPW, NW_>;
+  constexpr int RB = S::RB, NW = S::NW, NT = S::NT, BPW = S::BPW, kMaxChunk = S::MAXC;
+  constexpr int kAhead = (kRing - 2) * BPW;  // this wave's DMAs younger than the sub-chunk a step publishes
   const int unit = blockIdx.z, rg = blockIdx.y, kc = blockIdx.x;
   const int b = unit / a.n_kv, g = unit % a.n_kv;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  __shared__ __attribute__((aligned(1024))) char s_k[2][kSubBytes];
+  __shared__ __attribute__((aligned(1024))) char s_k[kRing][kSubBytes];
   __shared__ int s_blk[kMaxChunk / 16 + 2];
   __shared__ int s_pos[kMaxChunk];
   __shared__ int s_row[kMaxChunk];
   __shared__ int s_mm[3];
-  __shared__ float s_col[PASS == 2 ? NW : 1][PASS == 2 ? kMaxChunk : 1];
+  __shared__ float s_cs[PASS == 2 ? 2 : 1][NW][kSub];     // pass 2: each wave's column sums of one step
+  __shared__ float s_col[PASS == 2 ? kMaxChunk : 1];      // pass 2: the chunk's column sums
   int k0, k1, n;
   key_range(a, unit, k0, k1, n);
   const int c0 = k0 + kc * a.kc, c1 = min(c0 + a.kc, k1);
   if (PASS == 2 && c0 >= c1) return;  // uniform: nothing to score in this chunk
-  const Chunk ch = stage_chunk<NT>(a, b, g, c0, max(c0, c1), rg, s_blk, s_pos, s_row, s_mm);
-  // sub-chunks 0..2 in flight before anything else
-  Stage<SPT> st0, st1, st2;
-  load_stage(a, ch, 0, s_row, st0);
-  load_stage(a, ch, 1, s_row, st1);
-  load_stage(a, ch, 2, s_row, st2);
-  const int rho_wave = rg * kRowsPerWG + wave * RPW;
+  const Chunk ch = stage_chunk<NT, kMaxChunk>(a, b, g, c0, max(c0, c1), rg, s_blk, s_pos, s_row, s_mm);
+  const int rho_wave = rg * a.rpg + wave * RPW;
   QFrags<RB> qf;
   load_q(a, b, g, rho_wave, qf);
-
   Stats<RB> st;
   float ml[RB][4];
   if (PASS == 1) {
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        st.m[rb][v] = -1e30f;
-        st.l[rb][v] = 0.f;
-      }
+    stats_init(a, st);
   } else {
-    const float *mlog = a.mlog + ((int64_t)unit * a.nrg + rg) * kRowsPerWG;
+    const float *mlog = a.mlog + ((int64_t)unit * a.nrg + rg) * a.rpg;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int v = 0; v < 4; ++v)
         ml[rb][v] = qf.lim[rb][v] >= 0 ? mlog[wave * RPW + rb * 16 + (lane >> 4) * 4 + v] : INFINITY;
   }
-  // sub-chunk j is fetched into stage j % 3 at step j - 3, written to LDS buffer j % 2 at step j - 1 (before that
-  // step's barrier) and multiplied at step j
-  store_stage(st0, s_k[0]);
-  __syncthreads();
-  load_stage(a, ch, 3, s_row, st0);
-#define SE_STEP(FAST, SUB, NEXT_STAGE)                                                                         \
-  if ((SUB) < ch.nsub) {                                                                                       \
-    floatx4 sacc[RB][4];                                                                                       \
-    mfma_sub(qf, s_k[(SUB) & 1], sacc);                                                                        \
-    if constexpr (PASS == 1) stats_valu_step<FAST>(a, qf, (SUB), s_pos, sacc, st);                            \
-    else colsum_valu_step<FAST, RB, NW>(a, qf, (SUB), s_pos, sacc, ml, s_col);                                 \
-  }                                                                                                            \
-  store_stage(NEXT_STAGE, s_k[((SUB) + 1) & 1]);                                                               \
-  __syncthreads();                                                                                             \
-  load_stage(a, ch, (SUB) + 4, s_row, NEXT_STAGE);
-  if (ch.fast) {
-    for (int sub = 0; sub < ch.nsub; sub += 3) {
-      SE_STEP(true, sub, st1)
-      SE_STEP(true, sub + 1, st2)
-      SE_STEP(true, sub + 2, st0)
-    }
-  } else {
-    for (int sub = 0; sub < ch.nsub; sub += 3) {
-      SE_STEP(false, sub, st1)
-      SE_STEP(false, sub + 1, st2)
-      SE_STEP(false, sub + 2, st0)
-    }
+  // the query fragments and row statistics arrive before any DMA is issued (the compiler sees this wait)
+  __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0)
+
+  // Sub-chunk j is fetched into ring slot j % 4 at step j - 4 (the first four before the loop), published by the
+  // barrier of step j - 2, multiplied at step j - 1 into accumulator set (j + 1) % 2, and its softmax work done at
+  // step j. Within a step the MFMAs of sub-chunk j + 1 and the VALU work of sub-chunk j are independent, and the
+  // scheduling groups interleave them so the matrix core and the vector ALU of a wave run concurrently. MFMAs
+  // past the last sub-chunk read a stale slot; their result is never used.
+  const uint32_t ring = (uint32_t)(uintptr_t)&s_k[0][0];
+#pragma unroll
+  for (int j = 0; j < kRing; ++j) issue_sub<NW>(a, ch, j, s_row, ring);
+  publish<kAhead>();  // sub-chunks 0 and 1
+  floatx4 acc0[RB][4], acc1[RB][4];
+  mfma_sub(qf, s_k[0], acc0);
+#define SE_STEP(FAST, SUB, CUR, NEXT)                                                                          \
+  {                                                                                                            \
+    mask_logits<FAST>(qf, (SUB), s_pos, CUR);                                                                  \
+    mfma_sub(qf, s_k[((SUB) + 1) % kRing], NEXT);                                                              \
+    if constexpr (PASS == 1) {                                                                                 \
+      const bool moved = stats_step(a, CUR, st);                                                               \
+      interleave<RB, 4>();                                                                                     \
+      if (__ballot(moved)) stats_fix(a, CUR, st);                                                              \
+    } else {                                                                                                   \
+      colsum_step<RB, NW>(a, CUR, ml, s_cs[(SUB) & 1]);                                                        \
+      interleave<RB, 3>();                                                                                     \
+    }                                                                                                          \
+    issue_sub<NW>(a, ch, (SUB) + kRing, s_row, ring);                                                          \
+    publish<kAhead>();                                                                                         \
+    if constexpr (PASS == 2) {                                                                                 \
+      if (threadIdx.x < kSub) {                                                                                \
+        float sum = 0.f;                                                                                       \
+        _Pragma("unroll") for (int w = 0; w < NW; ++w) sum += s_cs[(SUB) & 1][w][threadIdx.x];                 \
+        s_col[(SUB) * kSub + threadIdx.x] = sum;                                                               \
+      }                                                                                                        \
+    }                                                                                                          \
   }
+#define SE_LOOP(FAST)                                                                                          \
+  {                                                                                                            \
+    int sub = 0;                                                                                               \
+    for (; sub + 2 <= ch.nsub; sub += 2) {                                                                     \
+      SE_STEP(FAST, sub, acc0, acc1)                                                                           \
+      SE_STEP(FAST, sub + 1, acc1, acc0)                                                                       \
+    }                                                                                                          \
+    if (sub < ch.nsub) SE_STEP(FAST, sub, acc0, acc1)                                                          \
+  }
+  if (ch.fast) {
+    SE_LOOP(true)
+  } else {
+    SE_LOOP(false)
+  }
+#undef SE_LOOP
 #undef SE_STEP
+  __builtin_amdgcn_s_waitcnt(0x3f70);  // no DMA outlives the loop
 
   if constexpr (PASS == 1) {
     // combine the 16 lanes (keys) of each row; write the chunk's (max, sum) per row in the log2 domain
-    float *out = a.stats + ((((int64_t)unit * a.nrg + rg) * a.nkc + kc) * kRowsPerWG) * 2;
-    const float c = a.scale_log2;
+    float *out = a.stats + ((((int64_t)unit * a.nrg + rg) * a.nkc + kc) * a.rpg) * 2;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const float mr = row16_max(st.m[rb][v]);
-        const float lr = row16_sum(st.l[rb][v] * __builtin_amdgcn_exp2f((st.m[rb][v] - mr) * c));
+        const float mc = -st.nmc[rb][v];  // this lane's m * c
+        const float mr = row16_max(mc);
+        const float lr = row16_sum(st.l[rb][v] * __builtin_amdgcn_exp2f(mc - mr));
         if ((lane & 15) == 0) {
           const int r = wave * RPW + rb * 16 + (lane >> 4) * 4 + v;
-          out[r * 2] = mr * c;
+          out[r * 2] = mr;
           out[r * 2 + 1] = lr;
         }
       }
   } else {
     __syncthreads();
     for (int j = threadIdx.x; j < c1 - c0; j += NT) {
-      float sum = 0.f;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) sum += s_col[w][j];
+      const float sum = s_col[j];
       const int idx = c0 + j - k0;
       if (a.nrg == 1) a.scores[(int64_t)unit * a.score_stride + idx] = sum;
       else a.colpart[((int64_t)unit * a.nrg + rg) * a.key_span + idx] = sum;
@@ -482,13 +558,13 @@ SE_DEV const char *key_row(const ScoreArgs &a, int b, int g, int key, int row_by
 }
 
 template <int DTYPE, int D>
-__global__ __launch_bounds__(kThreads) void stats_valu(ScoreArgs a) {
+__global__ __launch_bounds__(kValuRows) void stats_valu(ScoreArgs a) {
   constexpr int RBY = D * (DTYPE == SE_DTYPE_F32 ? 4 : 2);
   const int unit = blockIdx.z, rg = blockIdx.y, kc = blockIdx.x;
   const int b = unit / a.n_kv, g = unit % a.n_kv;
   int k0, k1, n;
   key_range(a, unit, k0, k1, n);
-  const int rho = rg * kRowsPerWG + threadIdx.x;
+  const int rho = rg * kValuRows + threadIdx.x;
   const int lim = row_limit(a, b, rho);
   const char *qr = lim >= 0 ? q_row(a, b, g, rho, RBY) : nullptr;
   float m = -1e30f, l = 0.f;
@@ -502,33 +578,33 @@ __global__ __launch_bounds__(kThreads) void stats_valu(ScoreArgs a) {
     l = l * __builtin_amdgcn_exp2f(m - mn) + __builtin_amdgcn_exp2f(x - mn);
     m = mn;
   }
-  float *out = a.stats + ((((int64_t)unit * a.nrg + rg) * a.nkc + kc) * kRowsPerWG + threadIdx.x) * 2;
+  float *out = a.stats + ((((int64_t)unit * a.nrg + rg) * a.nkc + kc) * kValuRows + threadIdx.x) * 2;
   out[0] = m;
   out[1] = l;
 }
 
 template <int DTYPE, int D>
-__global__ __launch_bounds__(kThreads) void colsum_valu(ScoreArgs a) {
+__global__ __launch_bounds__(kValuRows) void colsum_valu(ScoreArgs a) {
   constexpr int RBY = D * (DTYPE == SE_DTYPE_F32 ? 4 : 2);
   const int unit = blockIdx.z, rg = blockIdx.y, kc = blockIdx.x;
   const int b = unit / a.n_kv, g = unit % a.n_kv;
-  __shared__ float s_mlog[kRowsPerWG];
-  __shared__ int s_lim[kRowsPerWG];
+  __shared__ float s_mlog[kValuRows];
+  __shared__ int s_lim[kValuRows];
   int k0, k1, n;
   key_range(a, unit, k0, k1, n);
   const int c0 = k0 + kc * a.kc, c1 = min(c0 + a.kc, k1);
   if (c0 >= c1) return;
   merge_stats(a, unit, rg, s_mlog);
-  s_lim[threadIdx.x] = row_limit(a, b, rg * kRowsPerWG + threadIdx.x);
+  s_lim[threadIdx.x] = row_limit(a, b, rg * kValuRows + threadIdx.x);
   __syncthreads();
-  const int rows = min(kRowsPerWG, a.R * a.wq - rg * kRowsPerWG);
-  for (int key = c0 + threadIdx.x; key < c1; key += kThreads) {
+  const int rows = min(kValuRows, a.R * a.wq - rg * kValuRows);
+  for (int key = c0 + threadIdx.x; key < c1; key += kValuRows) {
     int p;
     const char *kr = key_row(a, b, g, key, RBY, p);
     float sum = 0.f;
     for (int r = 0; r < rows && kr; ++r) {
       if (p > s_lim[r]) continue;
-      const char *qr = q_row(a, b, g, rg * kRowsPerWG + r, RBY);
+      const char *qr = q_row(a, b, g, rg * kValuRows + r, RBY);
       sum += __builtin_amdgcn_exp2f(row_dot<DTYPE, D>(qr, kr) * a.scale_log2 - s_mlog[r]);
     }
     int idx = key - k0;
@@ -550,7 +626,7 @@ __global__ void colsum_reduce(ScoreArgs a) {
 }
 
 struct Plan {
-  int nrg, nkc, kc, key_span;
+  int nrg, nkc, kc, key_span, rpg, nw;  // nw: waves per MFMA workgroup (0: the fp32 VALU path)
   size_t stats_bytes, col_bytes, mlog_bytes;
 };
 
@@ -558,18 +634,36 @@ Plan make_plan(const se_cache_t *c, const se_window_params_t *p) {
   Plan pl;
   const int R = c->n_q / c->n_kv;
   const int rows = R * p->n_query;
-  pl.nrg = (rows + kRowsPerWG - 1) / kRowsPerWG;
+  const bool mfma = c->dtype == SE_DTYPE_BF16 && c->d == 128;
+  int maxc;
+  if (!mfma) {
+    pl.nw = 0, pl.rpg = kValuRows, maxc = 1024;
+  } else if (rows <= 256) {
+    pl.nw = 8, pl.rpg = Shape<kScoreRPW, 8>::ROWS, maxc = Shape<kScoreRPW, 8>::MAXC;
+  } else {
+    pl.nw = 4, pl.rpg = Shape<kScoreRPW, 4>::ROWS, maxc = Shape<kScoreRPW, 4>::MAXC;
+  }
+  pl.nrg = (rows + pl.rpg - 1) / pl.rpg;
   const int max_slots = c->max_blocks * c->page;
   pl.key_span = p->mode == SE_SCORE_CAUSAL ? max_slots : p->window - p->protect;
   const int span64 = (pl.key_span + 63) / 64 * 64;
-  pl.kc = span64 < kMaxChunk ? span64 : kMaxChunk;
+  pl.kc = span64 < maxc ? span64 : maxc;
   if (pl.kc < 64) pl.kc = 64;
   pl.nkc = (pl.key_span + pl.kc - 1) / pl.kc;
   const size_t units = (size_t)c->B * c->n_kv;
-  pl.stats_bytes = se_host::align_up(units * pl.nrg * pl.nkc * kRowsPerWG * 2 * sizeof(float));
+  pl.stats_bytes = se_host::align_up(units * pl.nrg * pl.nkc * pl.rpg * 2 * sizeof(float));
   pl.col_bytes = pl.nrg > 1 ? se_host::align_up(units * pl.nrg * pl.key_span * sizeof(float)) : 0;
-  pl.mlog_bytes = se_host::align_up(units * pl.nrg * kRowsPerWG * sizeof(float));
+  pl.mlog_bytes = se_host::align_up(units * pl.nrg * pl.rpg * sizeof(float));
   return pl;
+}
+
+template <int NW>
+void launch_mfma(const Plan &pl, const ScoreArgs &a, int units, hipStream_t st) {
+  using S = Shape<kScoreRPW, NW>;
+  const dim3 grid(pl.nkc, pl.nrg, units);
+  hipLaunchKernelGGL((window_mfma<1, kScoreRPW, NW>), grid, dim3(S::NT), 0, st, a);
+  hipLaunchKernelGGL(stats_merge, dim3(pl.nrg, units), dim3(pl.rpg), 0, st, a);
+  hipLaunchKernelGGL((window_mfma<2, kScoreRPW, NW>), grid, dim3(S::NT), 0, st, a);
 }
 
 }  // namespace
@@ -629,18 +723,18 @@ extern "C" int32_t se_window_score(const se_cache_t *c, const void *q_win, const
   a.nkc = pl.nkc;
   a.kc = pl.kc;
   a.key_span = pl.key_span;
+  a.rpg = pl.rpg;
   a.scale_log2 = p->scale * 1.4426950408889634f;
   const int units = c->B * c->n_kv;
   const dim3 grid(pl.nkc, pl.nrg, units);
   hipStream_t st = (hipStream_t)stream;
-  if (mfma) {
-    constexpr int nt = se::Shape<se::kScoreRPW>::NT;
-    hipLaunchKernelGGL((se::window_mfma<1, se::kScoreRPW>), grid, dim3(nt), 0, st, a);
-    hipLaunchKernelGGL(se::stats_merge, dim3(pl.nrg, units), dim3(se::kRowsPerWG), 0, st, a);
-    hipLaunchKernelGGL((se::window_mfma<2, se::kScoreRPW>), grid, dim3(nt), 0, st, a);
+  if (pl.nw == 8) {
+    se::launch_mfma<8>(pl, a, units, st);
+  } else if (pl.nw == 4) {
+    se::launch_mfma<4>(pl, a, units, st);
   } else {
-    hipLaunchKernelGGL((se::stats_valu<SE_DTYPE_F32, 64>), grid, dim3(se::kThreads), 0, st, a);
-    hipLaunchKernelGGL((se::colsum_valu<SE_DTYPE_F32, 64>), grid, dim3(se::kThreads), 0, st, a);
+    hipLaunchKernelGGL((se::stats_valu<SE_DTYPE_F32, 64>), grid, dim3(se::kValuRows), 0, st, a);
+    hipLaunchKernelGGL((se::colsum_valu<SE_DTYPE_F32, 64>), grid, dim3(se::kValuRows), 0, st, a);
   }
   if (pl.nrg > 1) {
     const int bx = (pl.key_span + 255) / 256;
