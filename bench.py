@@ -54,7 +54,7 @@ CALL_KERNELS = {
     "se_window_score": ["window_mfma", "stats_merge", "colsum_reduce", "stats_valu", "colsum_valu"],
     "se_topk_select": ["topk_kernel"],
     "se_token2chunk": ["t2c_kernel"],
-    "se_compact_evict": ["gather_move", "gather_finalize", "evict_slots_kernel"],
+    "se_compact_evict": ["gather_move", "gather_extents", "gather_push", "evict_slots_kernel"],
     "se_cache_append": ["append_kernel"],
     "se_page_bounds": ["pages_score", "pages_build"],
     "se_sparse_decode_attn": ["decode_partial", "decode_merge", "decode_cum"],

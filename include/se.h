@@ -162,6 +162,8 @@ int32_t se_token2chunk(const se_cache_t *c, const int32_t *idx, const int32_t *c
  *    logical block, and their table entries become -1. In place; bit-exact.
  *  EVICT_SLOTS: per (b, g) each listed resident slot is freed: position -1, cumulative score 0, pushed on the
  *    slot stack, ctx_len - 1. No data moves.
+ * GATHER needs a workspace of se_compact_evict_workspace_size bytes ((2 B + 1) int32, rounded up); EVICT_SLOTS
+ * needs none.
  */
 enum { SE_COMPACT_GATHER = 0, SE_COMPACT_EVICT_SLOTS = 1 };
 typedef struct {

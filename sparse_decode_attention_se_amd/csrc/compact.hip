@@ -79,51 +79,71 @@ SE_DEV bool is_hazard_dest(const int32_t *s, const UnitPlan &u, int j) {
   return lo < u.h && s[lo] == want;
 }
 
-// copy `nrows` rows (row r: source slot src[r] -> dest slot dst[r], -1 = skip) of one unit; every read of the
-// tile completes before its first write. nrows * row_bytes / 16 <= kMovePer * kMoveThreads.
-SE_DEV void move_rows(const GatherArgs &a, int b, int g, int unit, const int *src, const int *dst, int nrows) {
+// Per-row move descriptors of a tile, prepared in LDS: byte offsets of the source and destination rows (-1: skip),
+// the destination slot and the source row's position and cumulative score.
+struct Tile {
+  int64_t soff[kMoveRowsMax], doff[kMoveRowsMax];
+  int dslot[kMoveRowsMax], pval[kMoveRowsMax];
+  float cval[kMoveRowsMax];
+};
+
+// row r of the tile moves source slot ss to destination slot ds (ss < 0: nothing). The block table, position and
+// cumulative-score loads depend only on the slots, so they are all in flight together.
+SE_DEV void prepare_row(const GatherArgs &a, int b, int g, int unit, int r, int ss, int ds, Tile &t) {
+  int64_t so = -1, dof = -1;
+  int pv = -1;
+  float cv = 0.f;
+  if (ss >= 0) {
+    const int32_t *bt = a.bt + (int64_t)b * a.max_blocks;
+    const int64_t base = (int64_t)unit * a.max_blocks * a.page;
+    const int sb = bt[ss / a.page], db = bt[ds / a.page];
+    pv = a.pos[base + ss];
+    if (a.cum) cv = a.cum[base + ss];
+    if (blk_ok(sb, a.num_blocks) && blk_ok(db, a.num_blocks)) {
+      so = (((int64_t)sb * a.n_kv + g) * a.page + ss % a.page) * a.row_bytes;
+      dof = (((int64_t)db * a.n_kv + g) * a.page + ds % a.page) * a.row_bytes;
+    }
+  }
+  t.soff[r] = so;
+  t.doff[r] = dof;
+  t.dslot[r] = ds;
+  t.pval[r] = pv;
+  t.cval[r] = cv;
+}
+
+// move the prepared rows of a tile; with ORDERED every read of the tile completes before its first write.
+// nrows * row_bytes / 16 <= kMovePer * kMoveThreads.
+template <bool ORDERED>
+SE_DEV void move_tile(const GatherArgs &a, int unit, const Tile &t, int nrows) {
   const int cpr = a.row_bytes / 16;
   const int total = nrows * cpr;
-  const int32_t *bt = a.bt + (int64_t)b * a.max_blocks;
-  int32_t *pos = a.pos + (int64_t)unit * a.max_blocks * a.page;
-  float *cum = a.cum ? a.cum + (int64_t)unit * a.max_blocks * a.page : nullptr;
-  constexpr int kPer = kMovePer;
-  u32x4 kbuf[kPer], vbuf[kPer];
-  int32_t pbuf[kPer];
-  float cbuf[kPer];
-  int64_t doff[kPer];
+  u32x4 kbuf[kMovePer], vbuf[kMovePer];
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int t = threadIdx.x + i * kMoveThreads;
-    doff[i] = -1;
-    if (t >= total) continue;
-    const int r = t / cpr, ch = t % cpr, ss = src[r], ds = dst[r];
-    if (ss < 0) continue;
-    const int sb = bt[ss / a.page], db = bt[ds / a.page];
-    if (!blk_ok(sb, a.num_blocks) || !blk_ok(db, a.num_blocks)) continue;
-    const int64_t soff = (((int64_t)sb * a.n_kv + g) * a.page + ss % a.page) * a.row_bytes + ch * 16;
-    doff[i] = (((int64_t)db * a.n_kv + g) * a.page + ds % a.page) * a.row_bytes + ch * 16;
-    kbuf[i] = ld16(a.k + soff);
-    vbuf[i] = ld16(a.v + soff);
+  for (int i = 0; i < kMovePer; ++i) {
+    const int x = threadIdx.x + i * kMoveThreads;
+    if (x >= total) continue;
+    const int64_t so = t.soff[x / cpr];
+    if (so < 0) continue;
+    kbuf[i] = ld16(a.k + so + (x % cpr) * 16);
+    vbuf[i] = ld16(a.v + so + (x % cpr) * 16);
+  }
+  if (ORDERED) __syncthreads();
+  const int64_t base = (int64_t)unit * a.max_blocks * a.page;
+#pragma unroll
+  for (int i = 0; i < kMovePer; ++i) {
+    const int x = threadIdx.x + i * kMoveThreads;
+    if (x >= total) continue;
+    const int r = x / cpr, ch = x % cpr;
+    const int64_t so = t.soff[r], dof = t.doff[r];
+    if (so < 0) continue;
+    st16(a.k + dof + ch * 16, kbuf[i]);
+    st16(a.v + dof + ch * 16, vbuf[i]);
     if (ch == 0) {
-      pbuf[i] = pos[ss];
-      if (cum) cbuf[i] = cum[ss];
+      a.pos[base + t.dslot[r]] = t.pval[r];
+      if (a.cum) a.cum[base + t.dslot[r]] = t.cval[r];
     }
   }
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    if (doff[i] < 0) continue;
-    const int t = threadIdx.x + i * kMoveThreads;
-    const int r = t / cpr, ch = t % cpr;
-    st16(a.k + doff[i], kbuf[i]);
-    st16(a.v + doff[i], vbuf[i]);
-    if (ch == 0) {
-      pos[dst[r]] = pbuf[i];
-      if (cum) cum[dst[r]] = cbuf[i];
-    }
-  }
-  __syncthreads();
+  if (ORDERED) __syncthreads();
 }
 
 template <int kMoveRows>
@@ -132,7 +152,7 @@ __global__ __launch_bounds__(kMoveThreads) void gather_move(GatherArgs a) {
   const int b = unit / a.n_kv, g = unit % a.n_kv;
   __shared__ UnitPlan s_plan;
   __shared__ int s_idx[kIdxLds];
-  __shared__ int s_src[kMoveRowsMax], s_dst[kMoveRowsMax];
+  __shared__ Tile s_tile;
   __shared__ uint32_t s_bits[kMaxBitmapWords];
   __shared__ int s_list[kWindowWords * 32];
   __shared__ int s_scan[kWindowWords];
@@ -158,18 +178,22 @@ __global__ __launch_bounds__(kMoveThreads) void gather_move(GatherArgs a) {
     const int j0 = (blockIdx.x - 1) * kMoveRows;
     if (j0 >= u.cnt) return;
     if (threadIdx.x < kMoveRows) {
-      int j = j0 + threadIdx.x, src = -1;
+      const int j = j0 + threadIdx.x;
+      int src = -1;
       if (j < u.cnt && j >= u.h) {
-        int sj = s[j];
-        bool valid = sj >= lim && sj < u.n && (j == 0 || s[j - 1] < sj) && pos[sj] >= 0;
+        const int sj = s[j];
+        const bool valid = sj >= lim && sj < u.n && (j == 0 || s[j - 1] < sj);
         if (!valid) raise(a.status, SE_DEV_INDEX);
         else if (!is_hazard_dest(s, u, j)) src = sj;
       }
-      s_src[threadIdx.x] = src;
-      s_dst[threadIdx.x] = u.w0 + j;
+      prepare_row(a, b, g, unit, threadIdx.x, src, u.w0 + j, s_tile);
+      if (src >= 0 && s_tile.pval[threadIdx.x] < 0) {  // not resident
+        raise(a.status, SE_DEV_INDEX);
+        s_tile.soff[threadIdx.x] = -1;
+      }
     }
     __syncthreads();
-    move_rows(a, b, g, unit, s_src, s_dst, kMoveRows);
+    move_tile<false>(a, unit, s_tile, kMoveRows);
     return;
   }
 
@@ -215,14 +239,13 @@ __global__ __launch_bounds__(kMoveThreads) void gather_move(GatherArgs a) {
         int src = -1, j = 0;
         if (t0 + threadIdx.x < nlist) {
           j = s_list[t0 + threadIdx.x];
-          int sj = s[j];
+          const int sj = s[j];
           if (sj >= u.w0 && sj < u.n) src = sj;
         }
-        s_src[threadIdx.x] = src;
-        s_dst[threadIdx.x] = u.w0 + j;
+        prepare_row(a, b, g, unit, threadIdx.x, src, u.w0 + j, s_tile);
       }
       __syncthreads();
-      move_rows(a, b, g, unit, s_src, s_dst, kMoveRows);
+      move_tile<true>(a, unit, s_tile, kMoveRows);
     }
   }
 }
@@ -230,56 +253,55 @@ __global__ __launch_bounds__(kMoveThreads) void gather_move(GatherArgs a) {
 struct FinalArgs {
   int32_t *bt, *n_slots, *ctx, *free_blocks, *free_top, *slot_stack, *slot_top;
   const int32_t *count;
+  int32_t *ws;  // [0, B): blocks each sequence frees; [B, 2B): its new extent; [2B]: the free-stack top on entry
   int32_t *status;
   int32_t B, n_kv, page, max_blocks, num_blocks, slot_cap, window;
 };
 
-constexpr int kFinalThreads = 1024;
-constexpr int kMaxSeq = 4096;
+constexpr int kFinalThreads = 256;
 
-// single workgroup: per-(b,g) counters and slot stacks, then the blocks past each sequence's new extent go to
-// the free stack in order of sequence, then logical block
-__global__ __launch_bounds__(kFinalThreads) void gather_finalize(FinalArgs a) {
-  __shared__ int s_new_ext[kMaxSeq];
-  __shared__ int s_old_ext[kMaxSeq];
-  __shared__ int s_excl[kMaxSeq + 1];
-  __shared__ int s_scan[kFinalThreads];
-  const int units = a.B * a.n_kv;
+SE_DEV bool unit_ok(const FinalArgs &a, int n, int cnt, int &w0) {
   const int cap = a.max_blocks * a.page;
-  const int top0 = *a.free_top;
-  if (top0 < 0 || top0 > a.num_blocks) {
-    if (threadIdx.x == 0) raise(a.status, SE_DEV_CAPACITY);
-    return;
-  }
-  for (int b = threadIdx.x; b < a.B; b += kFinalThreads) {
-    int mx = 0;
-    for (int g = 0; g < a.n_kv; ++g) {
-      int unit = b * a.n_kv + g;
-      int n = a.n_slots[unit], cnt = a.count[unit];
-      int w0 = a.window > 0 ? n - a.window : 0;
-      bool ok = n >= 0 && n <= cap && w0 >= 0 && cnt >= 0 && cnt <= n - w0;
-      mx = max(mx, ok ? w0 + cnt : min(max(n, 0), cap));
-    }
-    s_new_ext[b] = (mx + a.page - 1) / a.page;
-    s_old_ext[b] = a.max_blocks;
+  w0 = a.window > 0 ? n - a.window : 0;
+  return n >= 0 && n <= cap && w0 >= 0 && cnt >= 0 && cnt <= n - w0;
+}
+
+// one workgroup per sequence: its new extent (max over heads of the kept prefix), its allocated extent (first
+// unallocated table entry at or after it: allocated entries form a prefix), then the per-head counters and slot
+// stacks. Writes how many blocks the sequence frees.
+__global__ __launch_bounds__(kFinalThreads) void gather_extents(FinalArgs a) {
+  __shared__ int s_new, s_old;
+  const int b = blockIdx.x;
+  const int cap = a.max_blocks * a.page;
+  if (threadIdx.x == 0) {
+    s_new = 0;
+    s_old = a.max_blocks;
   }
   __syncthreads();
-  // end of each allocated prefix: first unallocated entry at or after the new extent
-  for (int i = threadIdx.x; i < a.B * a.max_blocks; i += kFinalThreads) {
-    const int b = i / a.max_blocks, j = i % a.max_blocks;
-    if (j >= s_new_ext[b] && a.bt[i] < 0) atomicMin(&s_old_ext[b], j);
+  for (int g = threadIdx.x; g < a.n_kv; g += kFinalThreads) {
+    const int unit = b * a.n_kv + g;
+    const int n = a.n_slots[unit], cnt = a.count[unit];
+    int w0;
+    const int ext = unit_ok(a, n, cnt, w0) ? w0 + cnt : min(max(n, 0), cap);
+    atomicMax(&s_new, (ext + a.page - 1) / a.page);
   }
-  for (int unit = threadIdx.x; unit < units; unit += kFinalThreads) {
-    int n = a.n_slots[unit], cnt = a.count[unit];
-    int w0 = a.window > 0 ? n - a.window : 0;
-    bool ok = n >= 0 && n <= cap && w0 >= 0 && cnt >= 0 && cnt <= n - w0;
-    if (!ok) continue;
+  __syncthreads();
+  const int new_ext = s_new;
+  const int32_t *bt = a.bt + (int64_t)b * a.max_blocks;
+  for (int j = new_ext + threadIdx.x; j < a.max_blocks; j += kFinalThreads)
+    if (bt[j] < 0) atomicMin(&s_old, j);
+  for (int g = threadIdx.x; g < a.n_kv; g += kFinalThreads) {
+    const int unit = b * a.n_kv + g;
+    const int n = a.n_slots[unit], cnt = a.count[unit];
+    int w0;
+    if (!unit_ok(a, n, cnt, w0)) continue;
     int holes = 0;
     if (a.slot_cap > 0 && a.slot_stack) {
-      int top = min(max(a.slot_top[unit], 0), a.slot_cap), kept = 0;
+      const int top = min(max(a.slot_top[unit], 0), a.slot_cap);
+      int kept = 0;
       int32_t *st = a.slot_stack + (int64_t)unit * a.slot_cap;
       for (int i = 0; i < top; ++i) {
-        int sl = st[i];
+        const int sl = st[i];
         if (sl >= w0) ++holes; else st[kept++] = sl;
       }
       a.slot_top[unit] = kept;
@@ -288,42 +310,53 @@ __global__ __launch_bounds__(kFinalThreads) void gather_finalize(FinalArgs a) {
     a.n_slots[unit] = w0 + cnt;
   }
   __syncthreads();
-  // exclusive scan of the freed counts over sequences
-  int carry = 0;
-  for (int base = 0; base < a.B; base += kFinalThreads) {
-    const int b = base + threadIdx.x;
-    const int v = b < a.B ? max(s_old_ext[b] - s_new_ext[b], 0) : 0;
-    s_scan[threadIdx.x] = v;
-    __syncthreads();
-    for (int off = 1; off < kFinalThreads; off <<= 1) {
-      int x = threadIdx.x >= off ? s_scan[threadIdx.x - off] : 0;
-      __syncthreads();
-      s_scan[threadIdx.x] += x;
-      __syncthreads();
-    }
-    if (b < a.B) s_excl[b] = carry + s_scan[threadIdx.x] - v;
-    carry += s_scan[kFinalThreads - 1];
-    __syncthreads();
+  if (threadIdx.x == 0) {
+    a.ws[b] = max(s_old - new_ext, 0);
+    a.ws[a.B + b] = new_ext;
+    if (b == 0) a.ws[2 * a.B] = *a.free_top;
   }
-  if (threadIdx.x == 0) s_excl[a.B] = carry;
-  __syncthreads();
-  if (top0 + carry > a.num_blocks) {
-    if (threadIdx.x == 0) raise(a.status, SE_DEV_CAPACITY);
+}
+
+// one workgroup per sequence: push its freed blocks (ascending logical block) after those of the sequences before
+// it; the offset is the sum of their counts. Nothing is pushed if the stack cannot take every freed block.
+__global__ __launch_bounds__(kFinalThreads) void gather_push(FinalArgs a) {
+  __shared__ int s_red[2][kFinalThreads / 64];
+  const int b = blockIdx.x;
+  const int top0 = a.ws[2 * a.B];
+  if (top0 < 0 || top0 > a.num_blocks) {
+    if (b == 0 && threadIdx.x == 0) raise(a.status, SE_DEV_CAPACITY);
     return;
   }
-  // push: freed block f belongs to the sequence b with s_excl[b] <= f < s_excl[b + 1]
-  for (int f = threadIdx.x; f < carry; f += kFinalThreads) {
-    int lo = 0, hi = a.B - 1;
-    while (lo < hi) {
-      int mid = (lo + hi + 1) >> 1;
-      if (s_excl[mid] <= f) lo = mid; else hi = mid - 1;
-    }
-    const int b = lo, j = s_new_ext[b] + (f - s_excl[b]);
-    int32_t *e = a.bt + (int64_t)b * a.max_blocks + j;
-    a.free_blocks[top0 + f] = *e;
-    *e = -1;
+  int before = 0, total = 0;
+  for (int i = threadIdx.x; i < a.B; i += kFinalThreads) {
+    const int v = a.ws[i];
+    total += v;
+    if (i < b) before += v;
   }
-  if (threadIdx.x == 0) *a.free_top = top0 + carry;
+  before = wave_sum_i(before);
+  total = wave_sum_i(total);
+  if ((threadIdx.x & 63) == 0) {
+    s_red[0][threadIdx.x >> 6] = before;
+    s_red[1][threadIdx.x >> 6] = total;
+  }
+  __syncthreads();
+  before = total = 0;
+#pragma unroll
+  for (int w = 0; w < kFinalThreads / 64; ++w) {
+    before += s_red[0][w];
+    total += s_red[1][w];
+  }
+  if (top0 + total > a.num_blocks) {
+    if (b == 0 && threadIdx.x == 0) raise(a.status, SE_DEV_CAPACITY);
+    return;
+  }
+  const int mine = a.ws[b], new_ext = a.ws[a.B + b];
+  int32_t *bt = a.bt + (int64_t)b * a.max_blocks;
+  for (int i = threadIdx.x; i < mine; i += kFinalThreads) {
+    a.free_blocks[top0 + before + i] = bt[new_ext + i];
+    bt[new_ext + i] = -1;
+  }
+  if (b == 0 && threadIdx.x == 0) *a.free_top = top0 + total;
 }
 
 // ---- slot eviction ------------------------------------------------------------------------------------------------
@@ -486,13 +519,14 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
 }  // namespace
 }  // namespace se
 
-extern "C" size_t se_compact_evict_workspace_size(const se_cache_t *, const se_compact_params_t *) { return 0; }
+extern "C" size_t se_compact_evict_workspace_size(const se_cache_t *c, const se_compact_params_t *p) {
+  if (se_host::check_cache(c) != SE_OK || !p || p->mode != SE_COMPACT_GATHER) return 0;
+  return se_host::align_up((size_t)(2 * c->B + 1) * sizeof(int32_t));
+}
 
 extern "C" int32_t se_compact_evict(se_cache_t *c, const int32_t *idx, const int32_t *count,
                                     const se_compact_params_t *p, int32_t *status, void *ws, size_t ws_bytes,
                                     se_stream_t stream) {
-  (void)ws;
-  (void)ws_bytes;
   int32_t rc = se_host::check_cache(c);
   if (rc != SE_OK) return rc;
   if (!idx || !count || !p) return SE_ERR_NULL;
@@ -504,7 +538,7 @@ extern "C" int32_t se_compact_evict(se_cache_t *c, const int32_t *idx, const int
   if (p->mode == SE_COMPACT_GATHER) {
     if (!c->free_blocks || !c->free_top) return SE_ERR_NULL;
     if (p->idx_stride > 32 * se::kMaxBitmapWords) return SE_ERR_UNSUPPORTED;
-    if (c->B > se::kMaxSeq) return SE_ERR_UNSUPPORTED;
+    if (!ws || ws_bytes < se_compact_evict_workspace_size(c, p)) return SE_ERR_WORKSPACE;
     se::GatherArgs a;
     a.k = (char *)c->k_pool;
     a.v = (char *)c->v_pool;
@@ -546,7 +580,9 @@ extern "C" int32_t se_compact_evict(se_cache_t *c, const int32_t *idx, const int
     f.num_blocks = c->num_blocks;
     f.slot_cap = (c->slot_stack && c->slot_top) ? c->slot_cap : 0;
     f.window = p->window;
-    hipLaunchKernelGGL(se::gather_finalize, dim3(1), dim3(se::kFinalThreads), 0, st, f);
+    f.ws = (int32_t *)ws;
+    hipLaunchKernelGGL(se::gather_extents, dim3(c->B), dim3(se::kFinalThreads), 0, st, f);
+    hipLaunchKernelGGL(se::gather_push, dim3(c->B), dim3(se::kFinalThreads), 0, st, f);
     return se_host::launch_status();
   }
   if (p->mode == SE_COMPACT_EVICT_SLOTS) {

@@ -249,6 +249,16 @@ SE_DEV void publish() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
+// publish sub-chunk `need` when the DMA groups of sub-chunks [0, issued) have been issued, one group of BPW per
+// sub-chunk: the groups younger than `need` that exist may stay in flight (up to kRing - 2 of them)
+template <int BPW>
+SE_DEV void publish_upto(int need, int issued) {
+  const int younger = issued - 1 - need;  // uniform
+  if (younger >= kRing - 2) publish<(kRing - 2) * BPW>();
+  else if (younger == 1) publish<BPW>();
+  else publish<0>();
+}
+
 // B fragment of key tile tt, k-step ks from a staged sub-chunk
 SE_DEV bf16x8 read_frag(const char *slot, int tt, int ks) {
   const int lane = threadIdx.x & 63;
@@ -413,7 +423,6 @@ template <int PASS, int RPW, int NW_>
 __global__ __launch_bounds__((Shape<RPW, NW_>::NT), (Shape<RPW, NW_>::WPS)) void window_mfma(ScoreArgs a) {
   using S = Shape<RPW, NW_>;
   constexpr int RB = S::RB, NW = S::NW, NT = S::NT, BPW = S::BPW, kMaxChunk = S::MAXC;
-  constexpr int kAhead = (kRing - 2) * BPW;  // this wave's DMAs younger than the sub-chunk a step publishes
   const int unit = blockIdx.z, rg = blockIdx.y, kc = blockIdx.x;
   const int b = unit / a.n_kv, g = unit % a.n_kv;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -455,7 +464,7 @@ __global__ __launch_bounds__((Shape<RPW, NW_>::NT), (Shape<RPW, NW_>::WPS)) void
   const uint32_t ring = (uint32_t)(uintptr_t)&s_k[0][0];
 #pragma unroll
   for (int j = 0; j < kRing; ++j) issue_sub<NW>(a, ch, j, s_row, ring);
-  publish<kAhead>();  // sub-chunks 0 and 1
+  publish_upto<BPW>(1, min(ch.nsub, kRing));  // sub-chunks 0 and 1
   floatx4 acc0[RB][4], acc1[RB][4];
   mfma_sub(qf, s_k[0], acc0);
 #define SE_STEP(FAST, SUB, CUR, NEXT)                                                                          \
@@ -471,7 +480,7 @@ __global__ __launch_bounds__((Shape<RPW, NW_>::NT), (Shape<RPW, NW_>::WPS)) void
       interleave<RB, 3>();                                                                                     \
     }                                                                                                          \
     issue_sub<NW>(a, ch, (SUB) + kRing, s_row, ring);                                                          \
-    publish<kAhead>();                                                                                         \
+    publish_upto<BPW>((SUB) + 2, min(ch.nsub, (SUB) + kRing + 1));                                             \
     if constexpr (PASS == 2) {                                                                                 \
       if (threadIdx.x < kSub) {                                                                                \
         float sum = 0.f;                                                                                       \

@@ -65,6 +65,8 @@ def test_host_validation_without_device():
     cp = _lib.se_compact_params_t(7, 0, 8)  # unknown mode
     c.free_blocks = c.free_top = 16
     assert lib.se_compact_evict(C.byref(c), 16, 16, C.byref(cp), None, None, 0, None) == _lib.SE_ERR_PARAM
+    cp = _lib.se_compact_params_t(0, 0, 8)  # GATHER needs its small workspace
+    assert lib.se_compact_evict(C.byref(c), 16, 16, C.byref(cp), None, None, 0, None) == _lib.SE_ERR_WORKSPACE
 
 
 def test_workspace_sizes_are_host_only():
@@ -76,3 +78,7 @@ def test_workspace_sizes_are_host_only():
     assert lib.se_sparse_decode_attn_workspace_size(C.byref(c), C.byref(p), 0) > 0
     wp = _lib.se_window_params_t(0.1, 0, 64, 0, 0, 32768)
     assert lib.se_window_score_workspace_size(C.byref(c), C.byref(wp)) > 0
+    cp = _lib.se_compact_params_t(0, 0, 2048)
+    assert lib.se_compact_evict_workspace_size(C.byref(c), C.byref(cp)) >= (2 * 8 + 1) * 4
+    cp = _lib.se_compact_params_t(1, 0, 1)
+    assert lib.se_compact_evict_workspace_size(C.byref(c), C.byref(cp)) == 0
