@@ -58,6 +58,7 @@ struct DecodeArgs {
   const char *q;
   const int32_t *sel, *sel_count;
   float *out, *part, *logits, *cum;
+  float *mil;  // with accumulate: per (unit, head) the merged max and 1/sum, written by decode_merge
   int32_t *status;
   int32_t n_kv, page, max_blocks, num_blocks, sel_stride, rows_bound, chunk_rows, nchunk;
   float scale_log2;
@@ -96,6 +97,10 @@ struct ViewMap {
 // exp2 of at most kLazy, which fp32 sums hold without loss, and the rescale of l and acc is skipped.
 constexpr float kLazy = 8.f;
 constexpr int kMaxChunkRows = 1024;
+#ifndef SE_DECODE_MIN_WGS
+#define SE_DECODE_MIN_WGS 8192
+#endif
+constexpr int kMinWGs = SE_DECODE_MIN_WGS;
 
 template <int DTYPE, int R>
 __global__ __launch_bounds__(kThreads) void decode_partial(DecodeArgs a) {
@@ -322,14 +327,21 @@ __global__ __launch_bounds__(128) void decode_merge(DecodeArgs a) {
   const int b = unit / a.n_kv, g = unit % a.n_kv;
   const float *part = a.part + (int64_t)unit * a.nchunk * R * (D + 2);
   __shared__ float s_w[kMaxChunks];
-  __shared__ float s_l;
+  __shared__ float s_l, s_m;
   if (threadIdx.x < 64) {
     float mm, ll;
     merge_ml(part, a.nchunk, R, D, h, mm, ll, s_w);
-    if (threadIdx.x == 0) s_l = ll;
+    if (threadIdx.x == 0) {
+      s_l = ll;
+      s_m = mm;
+    }
   }
   __syncthreads();
   const float inv = s_l > 0.f ? 1.f / s_l : 0.f;
+  if (a.mil && threadIdx.x == 0) {  // for decode_cum
+    a.mil[((int64_t)unit * R + h) * 2] = s_m;
+    a.mil[((int64_t)unit * R + h) * 2 + 1] = inv;
+  }
   for (int e = threadIdx.x; e < D; e += 128) {
     float o = 0.f;
 #pragma unroll 4
@@ -338,34 +350,30 @@ __global__ __launch_bounds__(128) void decode_merge(DecodeArgs a) {
   }
 }
 
-// cumulative scores: cum[slot] += sum over the group's heads of that head's softmax weight on the slot
+// cumulative scores: cum[slot] += sum over the group's heads of that head's softmax weight on the slot, from the
+// stored logits and the merged (max, 1/sum) of each head
 template <int DTYPE, int R>
 __global__ __launch_bounds__(kThreads) void decode_cum(DecodeArgs a) {
-  constexpr int D = 16 * Vec<DTYPE>::EPL;
   const int unit = blockIdx.y;
-  const float *part = a.part + (int64_t)unit * a.nchunk * R * (D + 2);
-  __shared__ float s_m[R], s_il[R];
-  if (threadIdx.x < 64) {
-    for (int h = 0; h < R; ++h) {
-      float mm, ll;
-      merge_ml(part, a.nchunk, R, D, h, mm, ll, nullptr);
-      if (threadIdx.x == 0) {
-        s_m[h] = mm;
-        s_il[h] = ll > 0.f ? 1.f / ll : 0.f;
-      }
-    }
+  float mm[R], il[R];
+#pragma unroll
+  for (int h = 0; h < R; ++h) {
+    mm[h] = a.mil[((int64_t)unit * R + h) * 2];
+    il[h] = a.mil[((int64_t)unit * R + h) * 2 + 1];
   }
-  __syncthreads();
   ViewMap vm(a, unit);
   const int r = blockIdx.x * kThreads + threadIdx.x;
   if (r >= vm.rows) return;
   const int s = vm.slot(r);
   if (s < 0) return;
   const float *lg = a.logits + ((int64_t)unit * a.rows_bound + r) * R;
-  if (lg[0] == -INFINITY) return;  // free slot: not in the view
+  float x[R];
+#pragma unroll
+  for (int h = 0; h < R; ++h) x[h] = lg[h];
+  if (x[0] == -INFINITY) return;  // free slot: not in the view
   float sum = 0.f;
 #pragma unroll
-  for (int h = 0; h < R; ++h) sum += __builtin_amdgcn_exp2f(lg[h] - s_m[h]) * s_il[h];
+  for (int h = 0; h < R; ++h) sum += __builtin_amdgcn_exp2f(x[h] - mm[h]) * il[h];
   a.cum[(int64_t)unit * a.max_blocks * a.page + s] += sum;
 }
 
@@ -383,15 +391,17 @@ Plan make_plan(const se_cache_t *c, const se_decode_params_t *p, int has_sel) {
     pl.rows_bound = p->max_slots > 0 && p->max_slots < cap ? p->max_slots : cap;
   }
   pl.units = c->B * c->n_kv;
-  // the largest chunk (<= kMaxChunkRows) that still gives >= 8192 workgroups, else the smallest (64 rows)
+  // the largest chunk (<= kMaxChunkRows) that still gives >= kMinWGs workgroups, else the smallest (64 rows)
   int ch = kMaxChunkRows;
-  while (ch > 64 && (long long)pl.units * ((pl.rows_bound + ch - 1) / ch) < 8192) ch /= 2;
+  while (ch > 64 && (long long)pl.units * ((pl.rows_bound + ch - 1) / ch) < kMinWGs) ch /= 2;
   pl.chunk_rows = ch;
   pl.nchunk = (pl.rows_bound + ch - 1) / ch;
   if (pl.nchunk < 1) pl.nchunk = 1;
   int R = c->n_q / c->n_kv;
   pl.part_bytes = se_host::align_up((size_t)pl.units * pl.nchunk * R * (c->d + 2) * sizeof(float));
-  pl.logit_bytes = p->accumulate ? se_host::align_up((size_t)pl.units * pl.rows_bound * R * sizeof(float)) : 0;
+  pl.logit_bytes = p->accumulate ? se_host::align_up((size_t)pl.units * pl.rows_bound * R * sizeof(float)) +
+                                       se_host::align_up((size_t)pl.units * R * 2 * sizeof(float))
+                                 : 0;
   return pl;
 }
 
@@ -456,6 +466,9 @@ extern "C" int32_t se_sparse_decode_attn(se_cache_t *c, const void *q, const int
   a.part = (float *)ws;
   a.logits = p->accumulate ? (float *)((char *)ws + pl.part_bytes) : nullptr;
   a.cum = p->accumulate ? c->cum_score : nullptr;
+  a.mil = p->accumulate ? (float *)((char *)ws + pl.part_bytes +
+                                    se_host::align_up((size_t)pl.units * pl.rows_bound * (c->n_q / c->n_kv) * sizeof(float)))
+                        : nullptr;
   a.status = status;
   a.n_kv = c->n_kv;
   a.page = c->page;
