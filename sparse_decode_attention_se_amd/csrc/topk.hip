@@ -3,10 +3,11 @@
 // page selection; "What it is": H2O eviction by continuous attention scores).
 //
 // One workgroup per unit. Scores become order-preserving 32-bit keys (for the smallest mode the complement),
-// and an MSB-first radix select over 8-bit digits finds the K-th key T with LDS histograms. Items with key T
-// are then resolved by a second radix select over their tie key (position, or page id; the complement of the
-// position for the smallest mode), so the result is exactly "K best by (score, tie key)". A workgroup-wide
-// scan over items in order writes the ascending output. Given identical fp32 scores the result is exact.
+// and an MSB-first radix select over 8-bit digits of key - min (from the highest differing bit) finds the K-th
+// key T with LDS histograms. Items with key T are then resolved by a second radix select over their tie key
+// (position, or page id; the complement of the position for the smallest mode), so the result is exactly "K
+// best by (score, tie key)". Per-wave ballots and one scan over them write the ascending output. Given
+// identical fp32 scores the result is exact.
 #include "common.hpp"
 
 namespace se {
@@ -27,60 +28,114 @@ struct TopkArgs {
   int32_t n_kv, page, max_slots;
 };
 
-// candidate item state of one thread: PER contiguous items
-template <int PER>
-struct Items {
-  uint32_t key[PER];
-  uint32_t tie[PER];
-  uint32_t cand_mask;  // bit j: item is a candidate
-  uint32_t keep_mask;  // bit j: item is always kept
-};
+// One workgroup per unit; item i lives in thread i % kThreads, register j = i / kThreads (coalesced loads).
+constexpr int kWaves = kThreads / 64;
 
-// find, among items with (v & mask) == prefix and the given candidate mask, the digit at `shift` such that
-// `want` items lie at or above it; returns the updated prefix and decrements want by the count above.
-template <int PER>
-SE_DEV void radix_pass(const uint32_t (&v)[PER], uint32_t sel, uint32_t &prefix, uint32_t &mask, int shift,
-                       int &want, uint32_t *s_hist, int *s_res) {
-  for (int i = threadIdx.x; i < 256; i += kThreads) s_hist[i] = 0;
-  __syncthreads();
+// block-wide reductions (every thread gets the result); s_red holds kWaves values
+SE_DEV uint32_t block_min_u(uint32_t x, uint32_t *s_red) {
 #pragma unroll
-  for (int j = 0; j < PER; ++j)
-    if (((sel >> j) & 1u) && (v[j] & mask) == prefix) atomicAdd(&s_hist[(v[j] >> shift) & 255u], 1u);
+  for (int o = 32; o >= 1; o >>= 1) x = min(x, (uint32_t)__shfl_xor((int)x, o));
   __syncthreads();
-  // inclusive scan from the top digit: c(t) = #items with digit >= 255 - t
-  if (threadIdx.x < 256) s_hist[256 + threadIdx.x] = s_hist[255 - threadIdx.x];
+  if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = x;
   __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {
-    uint32_t x = 0;
-    if (threadIdx.x < 256 && threadIdx.x >= off) x = s_hist[256 + threadIdx.x - off];
-    __syncthreads();
-    if (threadIdx.x < 256) s_hist[256 + threadIdx.x] += x;
-    __syncthreads();
-  }
-  if (threadIdx.x < 256) {
-    uint32_t c = s_hist[256 + threadIdx.x];
-    uint32_t cprev = threadIdx.x ? s_hist[256 + threadIdx.x - 1] : 0u;
-    if (cprev < (uint32_t)want && (uint32_t)want <= c) {
-      s_res[0] = 255 - threadIdx.x;
-      s_res[1] = (int)cprev;
-    }
-  }
+  x = s_red[0];
+  for (int w = 1; w < kWaves; ++w) x = min(x, s_red[w]);
+  return x;
+}
+SE_DEV uint32_t block_max_u(uint32_t x, uint32_t *s_red) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = max(x, (uint32_t)__shfl_xor((int)x, o));
   __syncthreads();
-  const int digit = s_res[0];
-  want -= s_res[1];
-  prefix |= (uint32_t)digit << shift;
-  mask |= 255u << shift;
+  if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = x;
   __syncthreads();
+  x = s_red[0];
+  for (int w = 1; w < kWaves; ++w) x = max(x, s_red[w]);
+  return x;
+}
+SE_DEV int block_sum_i(int x, uint32_t *s_red) {
+  x = wave_sum_i(x);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = (uint32_t)x;
+  __syncthreads();
+  x = 0;
+  for (int w = 0; w < kWaves; ++w) x += (int)s_red[w];
+  return x;
 }
 
+// Among the items of `mask` (bit j: register j), the `want`-th largest value T of v (1 <= want <= #items). On
+// return `want` is the number of items equal to T still to be taken (those above T are all taken). Radix select
+// over 8-bit digits of v - min, starting at the highest bit in which the items differ, so the first histogram
+// already spreads over many bins.
 template <int PER>
+SE_DEV uint32_t radix_kth(const uint32_t (&v)[PER], uint32_t mask, int &want, uint32_t *s_hist, uint32_t *s_red,
+                          int *s_res) {
+  uint32_t lo = 0xffffffffu, hi = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j)
+    if ((mask >> j) & 1u) {
+      lo = min(lo, v[j]);
+      hi = max(hi, v[j]);
+    }
+  lo = block_min_u(lo, s_red);
+  hi = block_max_u(hi, s_red);
+  if (lo >= hi) return hi;  // all equal
+  int top = 32 - __clz(hi - lo);
+  uint32_t prefix = 0;  // digits of (T - lo) above bit `top` found so far
+  const int lane = threadIdx.x & 63;
+  while (top > 0) {
+    const int w = top < 8 ? top : 8, sh = top - w;
+    const uint32_t dmask = (1u << w) - 1u;
+    for (int i = threadIdx.x; i < 256; i += kThreads) s_hist[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      if (!((mask >> j) & 1u)) continue;
+      const uint32_t x = v[j] - lo;
+      if ((top >= 32 ? 0u : x >> top) == prefix) atomicAdd(&s_hist[(x >> sh) & dmask], 1u);
+    }
+    __syncthreads();
+    if (threadIdx.x < 64) {
+      // lane l holds bins 4l..4l+3; counts strictly above each bin, from the top digit down
+      uint32_t c[4], t = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        c[q] = s_hist[4 * lane + q];
+        t += c[q];
+      }
+      uint32_t incl = t;  // sum over lanes >= l
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = (uint32_t)__shfl_down((int)incl, o);
+        if (lane + o < 64) incl += y;
+      }
+      uint32_t above = incl - t;
+#pragma unroll
+      for (int q = 3; q >= 0; --q) {
+        if (above < (uint32_t)want && (uint32_t)want <= above + c[q]) {
+          s_res[0] = 4 * lane + q;
+          s_res[1] = (int)above;
+        }
+        above += c[q];
+      }
+    }
+    __syncthreads();
+    const uint32_t d = (uint32_t)s_res[0];
+    want -= s_res[1];
+    prefix = (prefix << w) | d;
+    top = sh;
+    __syncthreads();
+  }
+  return lo + prefix;
+}
+
+template <int PER, bool ONE>  // ONE: k == 1, selected by one arg-max instead of radix passes
 __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
-  __shared__ uint32_t s_hist[512];
+  __shared__ uint32_t s_hist[256];
+  __shared__ uint32_t s_red[kWaves];
   __shared__ int s_res[2];
-  __shared__ int s_scan[kThreads];
-  __shared__ int s_red[kThreads / 64];
+  __shared__ int s_cnt[PER * kWaves];
   const int unit = blockIdx.x;
-  const int t = threadIdx.x;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   int n = a.n_slots[unit];
   n = n < 0 ? 0 : (n > a.max_slots ? a.max_slots : n);
   const int32_t *pos = a.pos + (int64_t)unit * a.max_slots;
@@ -105,138 +160,166 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
     return;
   }
 
-  // the smallest mode needs the largest resident position first
-  int limit = 0;
-  if (a.mode == SE_TOPK_SMALLEST) {
-    int mx = -1;
-    for (int j = 0; j < PER; ++j) {
-      int i = t * PER + j;
-      if (i < n_items) mx = max(mx, pos[i]);
-    }
+  // Positions (slot units) and scores, every load issued up front and unconditionally (clamped to index 0 where
+  // the item does not exist or has no score) so that all are in flight together; selects drop what is not needed.
+  const int n_scored = win ? a.window - a.protect : n_items;  // scores exist for items [0, n_scored)
+  int pv[PER];
+  float sv[PER];
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) mx = max(mx, __shfl_xor(mx, o));
-    if ((t & 63) == 0) s_red[t >> 6] = mx;
-    __syncthreads();
-    mx = -1;
-    for (int w = 0; w < kThreads / 64; ++w) mx = max(mx, s_red[w]);
-    limit = mx - a.recent;
-    __syncthreads();
+  for (int j = 0; j < PER; ++j) {
+    const int i = j * kThreads + t;
+    pv[j] = pos[base + (i < n_items ? i : 0)];
+    sv[j] = sc[i < n_scored && i < n_items ? i : 0];
   }
+  int mx = -1;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int i = j * kThreads + t;
+    if (page_unit || i >= n_items) pv[j] = -1;
+    mx = max(mx, pv[j]);
+  }
+  int limit = 0;
+  if (a.mode == SE_TOPK_SMALLEST) limit = (int)block_max_u((uint32_t)(mx + 1), s_red) - 1 - a.recent;
 
-  // gather keys
-  Items<PER> it;
-  it.cand_mask = 0;
-  it.keep_mask = 0;
+  // keys of the candidates (tie keys, which order equal scores, are recomputed in the rare tie path below)
+  uint32_t key[PER], cand = 0, keep = 0;
   int ncand_local = 0;
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
-    const int i = t * PER + j;
-    it.key[j] = 0;
-    it.tie[j] = 0;
+    const int i = j * kThreads + t;
+    key[j] = 0;
     if (i >= n_items) continue;
-    bool cand = false, keep = false;
+    bool c = false, k = false;
     if (page_unit) {
-      bool end = a.forced_ends && (i == 0 || i == n_items - 1);
-      keep = end;
-      cand = !end;
-      it.tie[j] = (uint32_t)i;
+      const bool end = a.forced_ends && (i == 0 || i == n_items - 1);
+      k = end;
+      c = !end;
     } else {
-      const int p = pos[base + i];
+      const int p = pv[j];
       if (p < 0) continue;
       if (a.mode == SE_TOPK_SMALLEST) {
-        cand = p <= limit;
-        it.tie[j] = 0x7fffffffu - (uint32_t)p;
+        c = p <= limit;
       } else {
-        keep = base + i >= n - a.protect;
-        cand = !keep;
-        it.tie[j] = (uint32_t)p;
+        k = base + i >= n - a.protect;
+        c = !k;
       }
     }
-    if (cand) {
-      const float s = sc[i];
-      it.key[j] = a.mode == SE_TOPK_SMALLEST ? ~orderable(s) : orderable(s);
-      it.cand_mask |= 1u << j;
+    if (c) {
+      const float x = sv[j];
+      key[j] = a.mode == SE_TOPK_SMALLEST ? ~orderable(x) : orderable(x);
+      cand |= 1u << j;
       ++ncand_local;
     }
-    if (keep) it.keep_mask |= 1u << j;
+    if (k) keep |= 1u << j;
   }
-  // total candidates
-  int ncand = ncand_local;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) ncand += __shfl_xor(ncand, o);
-  if ((t & 63) == 0) s_red[t >> 6] = ncand;
-  __syncthreads();
-  ncand = 0;
-  for (int w = 0; w < kThreads / 64; ++w) ncand += s_red[w];
-  __syncthreads();
+  const int ncand = block_sum_i(ncand_local, s_red);
 
   int want = a.k;
   if (a.mode == SE_TOPK_SMALLEST) {
-    int over = a.ctx[unit] - a.budget;
+    const int over = a.ctx[unit] - a.budget;
     want = min(want, over < 0 ? 0 : over);
   }
   want = min(want, ncand);
 
-  uint32_t sel_mask = 0;
+  uint32_t sel = 0;
   if (want == ncand) {
-    sel_mask = it.cand_mask;
+    sel = cand;
+  } else if (ONE) {
+    // one item (H2O evicts one per step): the largest key, then the smallest tie key among the items holding it
+    uint32_t bk = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+      if ((cand >> j) & 1u) bk = max(bk, key[j]);
+    bk = block_max_u(bk, s_red);
+    auto tie_of = [&](int j) {
+      const int i = j * kThreads + t;
+      return page_unit ? (uint32_t)i : (a.mode == SE_TOPK_SMALLEST ? 0x7fffffffu - (uint32_t)pv[j] : (uint32_t)pv[j]);
+    };
+    uint32_t bt = 0xffffffffu;
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+      if (((cand >> j) & 1u) && key[j] == bk) bt = min(bt, tie_of(j));
+    bt = block_min_u(bt, s_red);
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+      if (((cand >> j) & 1u) && key[j] == bk && tie_of(j) == bt) sel |= 1u << j;
   } else if (want > 0) {
-    uint32_t prefix = 0, mask = 0;
     int w = want;
-#pragma unroll 1
-    for (int shift = 24; shift >= 0; shift -= 8) radix_pass<PER>(it.key, it.cand_mask, prefix, mask, shift, w, s_hist, s_res);
-    const uint32_t T = prefix;  // the want-th largest key; w items with key == T still to take
-    uint32_t eq_mask = 0;
+    const uint32_t T = radix_kth<PER>(key, cand, w, s_hist, s_red, s_res);
+    uint32_t eq = 0;
     int n_eq_local = 0;
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
-      if (!((it.cand_mask >> j) & 1u)) continue;
-      if (it.key[j] > T) sel_mask |= 1u << j;
-      else if (it.key[j] == T) {
-        eq_mask |= 1u << j;
+      if (!((cand >> j) & 1u)) continue;
+      if (key[j] > T) sel |= 1u << j;
+      else if (key[j] == T) {
+        eq |= 1u << j;
         ++n_eq_local;
       }
     }
-    int n_eq = n_eq_local;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) n_eq += __shfl_xor(n_eq, o);
-    if ((t & 63) == 0) s_red[t >> 6] = n_eq;
-    __syncthreads();
-    n_eq = 0;
-    for (int ww = 0; ww < kThreads / 64; ++ww) n_eq += s_red[ww];
-    __syncthreads();
+    const int n_eq = block_sum_i(n_eq_local, s_red);
     if (n_eq == w) {
-      sel_mask |= eq_mask;
+      sel |= eq;
     } else {
-      // the w smallest tie keys among the tied items: radix select the largest complements
+      // the w smallest tie keys among the tied items: the w largest complements (tie keys are distinct). The tie
+      // key is the page id, the position (largest mode) or 0x7fffffff - position (smallest mode: the higher
+      // position goes first).
       uint32_t inv[PER];
 #pragma unroll
-      for (int j = 0; j < PER; ++j) inv[j] = ~it.tie[j];
-      uint32_t p2 = 0, m2 = 0;
-      int w2 = w;
-#pragma unroll 1
-      for (int shift = 24; shift >= 0; shift -= 8) radix_pass<PER>(inv, eq_mask, p2, m2, shift, w2, s_hist, s_res);
-      // tie keys are distinct among resident items, so exactly one item holds the threshold and w2 == 1
+      for (int j = 0; j < PER; ++j) {
+        const int i = j * kThreads + t;
+        uint32_t tie = 0;
+        if ((eq >> j) & 1u) {
+          if (page_unit) tie = (uint32_t)i;
+          else {
+            const int p = pos[base + i];
+            tie = a.mode == SE_TOPK_SMALLEST ? 0x7fffffffu - (uint32_t)p : (uint32_t)p;
+          }
+        }
+        inv[j] = ~tie;
+      }
+      const uint32_t T2 = radix_kth<PER>(inv, eq, w, s_hist, s_red, s_res);
 #pragma unroll
       for (int j = 0; j < PER; ++j)
-        if (((eq_mask >> j) & 1u) && inv[j] >= p2) sel_mask |= 1u << j;
+        if (((eq >> j) & 1u) && inv[j] >= T2) sel |= 1u << j;
     }
   }
 
-  // ascending output: scan of per-thread counts over contiguous item ranges
-  const uint32_t out_mask = sel_mask | it.keep_mask;
-  const int mine = __popc(out_mask);
-  s_scan[t] = mine;
-  __syncthreads();
-  for (int off = 1; off < kThreads; off <<= 1) {
-    int x = t >= off ? s_scan[t - off] : 0;
-    __syncthreads();
-    s_scan[t] += x;
-    __syncthreads();
+  // ascending output: items are ordered by (register j, wave, lane); per (j, wave) counts from ballots, one
+  // exclusive scan over them, then each selected item's rank inside its wave
+  const uint32_t out = sel | keep;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const uint64_t b = __ballot((out >> j) & 1u);
+    if (lane == 0) s_cnt[j * kWaves + wave] = __popcll(b);
   }
-  int o = s_scan[t] - mine;
-  const int total = s_scan[kThreads - 1];
-  int32_t *out = a.idx + (int64_t)unit * a.out_stride;
+  __syncthreads();
+  if (t < 64) {
+    constexpr int E = (PER * kWaves + 63) / 64;  // entries per lane
+    int v[E], sum = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int x = lane * E + e;
+      v[e] = x < PER * kWaves ? s_cnt[x] : 0;
+      sum += v[e];
+    }
+    int incl = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    int run = incl - sum;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int x = lane * E + e;
+      if (x < PER * kWaves) s_cnt[x] = run;
+      run += v[e];
+    }
+    if (lane == 63) s_res[0] = incl;
+  }
+  __syncthreads();
+  const int total = s_res[0];
   if (total > a.out_stride) {
     if (t == 0) {
       raise(a.status, SE_DEV_CAPACITY);
@@ -244,9 +327,13 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
     }
     return;
   }
+  int32_t *dst = a.idx + (int64_t)unit * a.out_stride;
+  const uint64_t lt = (1ull << lane) - 1ull;
 #pragma unroll
-  for (int j = 0; j < PER; ++j)
-    if ((out_mask >> j) & 1u) out[o++] = base + t * PER + j;
+  for (int j = 0; j < PER; ++j) {
+    const uint64_t b = __ballot((out >> j) & 1u);
+    if ((out >> j) & 1u) dst[s_cnt[j * kWaves + wave] + __popcll(b & lt)] = base + j * kThreads + t;
+  }
   if (t == 0) a.count[unit] = total;
 }
 
@@ -301,11 +388,18 @@ extern "C" int32_t se_topk_select(const se_cache_t *c, const float *scores, cons
   const int units = c->B * c->n_kv;
   hipStream_t st = (hipStream_t)stream;
   const int per = (n_items + se::kThreads - 1) / se::kThreads;
-  if (per <= 1) hipLaunchKernelGGL(se::topk_kernel<1>, dim3(units), dim3(se::kThreads), 0, st, a);
-  else if (per <= 4) hipLaunchKernelGGL(se::topk_kernel<4>, dim3(units), dim3(se::kThreads), 0, st, a);
-  else if (per <= 8) hipLaunchKernelGGL(se::topk_kernel<8>, dim3(units), dim3(se::kThreads), 0, st, a);
-  else if (per <= 16) hipLaunchKernelGGL(se::topk_kernel<16>, dim3(units), dim3(se::kThreads), 0, st, a);
-  else if (per <= 32) hipLaunchKernelGGL(se::topk_kernel<32>, dim3(units), dim3(se::kThreads), 0, st, a);
+  const dim3 grid(units), block(se::kThreads);
+#define SE_TOPK_LAUNCH(P)                                                                                      \
+  do {                                                                                                         \
+    if (p->k == 1) hipLaunchKernelGGL((se::topk_kernel<P, true>), grid, block, 0, st, a);                     \
+    else hipLaunchKernelGGL((se::topk_kernel<P, false>), grid, block, 0, st, a);                               \
+  } while (0)
+  if (per <= 1) SE_TOPK_LAUNCH(1);
+  else if (per <= 4) SE_TOPK_LAUNCH(4);
+  else if (per <= 8) SE_TOPK_LAUNCH(8);
+  else if (per <= 16) SE_TOPK_LAUNCH(16);
+  else if (per <= 32) SE_TOPK_LAUNCH(32);
   else return SE_ERR_UNSUPPORTED;
+#undef SE_TOPK_LAUNCH
   return se_host::launch_status();
 }

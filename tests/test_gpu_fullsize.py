@@ -198,3 +198,36 @@ def test_kara_full_size_event():
                 if exact[g]:
                     np.testing.assert_allclose(outs[s][b, g * r:(g + 1) * r], o_ref[0, g * r:(g + 1) * r], atol=2e-3,
                                                rtol=0)
+
+
+def test_window_scores_repeat_bitwise_at_full_size():
+    """Every kernel of the path is deterministic, so repeated runs must agree bit for bit; a missing wait or barrier
+    shows up here as a difference between runs (the full-size shapes exercise every chunk-end case)."""
+    banner("window scores repeated 4x: Llama-8B SnapKV 8 x 32768 and Kara 128 x 16384")
+    cfg = W.C1
+    inp = W.gen_snapkv(cfg, seed=1, threads=16)
+    dc = to_device(inp["cache"], cfg.hq)
+    ev = WF.SnapKVEvent(dc, wq=cfg.wq, protect=cfg.protect, keep=cfg.keep, scale=inp["scale"])
+    q_win, q_pos = storage_tensor(inp["q_win"], "bf16"), i32(inp["q_pos"])
+    runs = []
+    for _ in range(4):
+        ev.score(q_win, q_pos)
+        runs.append(ev.scores.clone())
+    for r in runs[1:]:
+        assert torch.equal(r, runs[0])
+    del dc, ev, runs
+    cfg = W.scaled(W.C2, period=1, events=1)
+    inp = W.gen_kara(cfg, seed=1, threads=16)
+    dc = to_device(inp["cache"], cfg.hq)
+    ke = WF.KaraEvent(dc, window=cfg.window, protect=cfg.protect, n_cand=cfg.n_cand, budget=cfg.budget,
+                      max_gap=cfg.max_gap, scale=inp["scale"])
+    qk = storage_tensor(np.ascontiguousarray(inp["q_all"][:, :, :cfg.window]), "bf16")
+    runs = []
+    for _ in range(4):
+        se.se_window_score(dc, qk, None, ke.scores, scale=ke.scale, mode=se.SE_SCORE_BIDIR, n_query=cfg.window,
+                           window=cfg.window, protect=cfg.protect)
+        runs.append(ke.scores.clone())
+    r = cfg.hq // cfg.hkv
+    np.testing.assert_allclose(runs[0].sum(dim=2).cpu().numpy(), r * cfg.window, rtol=1e-4)
+    for x in runs[1:]:
+        assert torch.equal(x, runs[0])

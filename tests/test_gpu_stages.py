@@ -208,6 +208,34 @@ def test_topk_window_and_pages_and_smallest_exact():
         assert [x.tolist() for r in lists_from(idx, cnt) for x in r] == [x.tolist() for r in ref for x in r]
 
 
+@pytest.mark.parametrize("levels", [0, 3])
+def test_topk_single_item_exact(levels):
+    """k = 1 takes its own arg-max path: largest slots, pages with forced ends and smallest, with heavy ties."""
+    banner(f"topk k=1 levels={levels}")
+    c = punch_holes(_topk_cache(N=2000), 0.002, 11)
+    dc = to_device(c, 12)
+    cnt = torch.zeros((2, 3), dtype=torch.int32, device=DEV)
+    scores = W.gen_scores(12, (2, 3, c.pos_map.shape[2]), levels=levels)
+    for protect in (0, 64):
+        ref = oracle.topk_largest(scores, c, 1, protect=protect)
+        idx = torch.zeros((2, 3, 65), dtype=torch.int32, device=DEV)
+        se.se_topk_select(dc, torch.from_numpy(scores).to(DEV), idx, cnt, mode=se.SE_TOPK_LARGEST,
+                          unit=se.SE_UNIT_SLOT, k=1, protect=protect)
+        assert [x.tolist() for r in lists_from(idx, cnt) for x in r] == [x.tolist() for r in ref for x in r]
+    pscores = W.gen_scores(13, (2, 3, c.max_blocks), levels=levels)
+    ref = oracle.topk_largest(pscores, c, 1, unit="page", forced_ends=True)
+    idx = torch.zeros((2, 3, 3), dtype=torch.int32, device=DEV)
+    se.se_topk_select(dc, torch.from_numpy(pscores).to(DEV), idx, cnt, mode=se.SE_TOPK_LARGEST, unit=se.SE_UNIT_PAGE,
+                      k=1, forced_ends=1)
+    assert [x.tolist() for r in lists_from(idx, cnt) for x in r] == [x.tolist() for r in ref for x in r]
+    for budget in (1990, 1000):
+        ref = oracle.topk_smallest(scores, c, 1, budget=budget, recent=256)
+        idx = torch.zeros((2, 3, 1), dtype=torch.int32, device=DEV)
+        se.se_topk_select(dc, torch.from_numpy(scores).to(DEV), idx, cnt, mode=se.SE_TOPK_SMALLEST,
+                          unit=se.SE_UNIT_SLOT, k=1, budget=budget, recent=256)
+        assert [x.tolist() for r in lists_from(idx, cnt) for x in r] == [x.tolist() for r in ref for x in r]
+
+
 # ------------------------------------------------------------------ Token2Chunk -----------------------------------
 def test_token2chunk_exact():
     banner("token2chunk")
