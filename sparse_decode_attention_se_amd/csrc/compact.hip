@@ -444,20 +444,27 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
   }
   __syncthreads();
   // per sequence: the logical block its heads lack, if any (allocated entries form a prefix, so a single
-  // token per head can only enter one new block)
+  // token per head can only enter one new block; heads that lack different blocks are an index error). One
+  // thread per head; the sequence's answer is gathered with LDS min/max.
+  __shared__ int s_lbmin[kAppendMaxSeq];
   for (int b = threadIdx.x; b < a.B; b += kAppendThreads) {
-    int need = -1;
-    for (int g = 0; g < a.n_kv; ++g) {
-      int lb = s_slot[b * a.n_kv + g] / a.page;
-      int cur = a.bt[(int64_t)b * a.max_blocks + lb];
-      if (cur >= a.num_blocks) atomicOr(&s_fail, 1);
-      if (cur < 0) {
-        if (need >= 0 && need != lb) atomicOr(&s_fail, 2);
-        need = lb;
-      }
-    }
-    s_lb[b] = need;
+    s_lb[b] = -1;
+    s_lbmin[b] = 0x7fffffff;
   }
+  __syncthreads();
+  for (int unit = threadIdx.x; unit < units; unit += kAppendThreads) {
+    const int b = unit / a.n_kv;
+    const int lb = s_slot[unit] / a.page;
+    const int cur = a.bt[(int64_t)b * a.max_blocks + lb];
+    if (cur >= a.num_blocks) atomicOr(&s_fail, 1);
+    if (cur < 0) {
+      atomicMax(&s_lb[b], lb);
+      atomicMin(&s_lbmin[b], lb);
+    }
+  }
+  __syncthreads();
+  for (int b = threadIdx.x; b < a.B; b += kAppendThreads)
+    if (s_lb[b] >= 0 && s_lbmin[b] != s_lb[b]) atomicOr(&s_fail, 2);
   __syncthreads();
   // exclusive scan of the pops over sequences, in sequence order
   int carry = 0;
@@ -505,14 +512,29 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
     s_blk[unit] = a.bt[(int64_t)b * a.max_blocks + slot / a.page];
   }
   __syncthreads();
-  const int cpr = a.row_bytes / 16;
-  for (int t = threadIdx.x; t < units * cpr; t += kAppendThreads) {
-    int unit = t / cpr, ch = t % cpr;
-    int g = unit % a.n_kv, slot = s_slot[unit];
-    int64_t off = (((int64_t)s_blk[unit] * a.n_kv + g) * a.page + slot % a.page) * a.row_bytes + ch * 16;
-    int64_t src = (int64_t)unit * a.row_bytes + ch * 16;
-    st16(a.k + off, ld16(a.k_new + src));
-    st16(a.v + off, ld16(a.v_new + src));
+  // copy the new rows: each thread loads kCopyBatch 16-byte pieces of K and of V before storing any of them
+  constexpr int kCopyBatch = 8;
+  const int cpr = a.row_bytes / 16, total = units * cpr;
+  for (int t0 = threadIdx.x; t0 < total; t0 += kAppendThreads * kCopyBatch) {
+    u32x4 kb[kCopyBatch], vb[kCopyBatch];
+#pragma unroll
+    for (int u = 0; u < kCopyBatch; ++u) {
+      const int t = t0 + u * kAppendThreads;
+      if (t >= total) continue;
+      const int64_t src = (int64_t)(t / cpr) * a.row_bytes + (t % cpr) * 16;
+      kb[u] = ld16(a.k_new + src);
+      vb[u] = ld16(a.v_new + src);
+    }
+#pragma unroll
+    for (int u = 0; u < kCopyBatch; ++u) {
+      const int t = t0 + u * kAppendThreads;
+      if (t >= total) continue;
+      const int unit = t / cpr, ch = t % cpr;
+      const int g = unit % a.n_kv, slot = s_slot[unit];
+      const int64_t off = (((int64_t)s_blk[unit] * a.n_kv + g) * a.page + slot % a.page) * a.row_bytes + ch * 16;
+      st16(a.k + off, kb[u]);
+      st16(a.v + off, vb[u]);
+    }
   }
 }
 
