@@ -68,12 +68,17 @@ CSRC = os.path.join(ROOT, "sparse_decode_attention_se_amd", "csrc")
 
 
 def source_digest(call):
+    """Digest of a call's kernel sources with comments and blank space removed, so that only code changes count."""
     import hashlib
+    import re
 
     h = hashlib.sha256()
     for f in (CALL_SOURCES[call], "common.hpp"):
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(CSRC, f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

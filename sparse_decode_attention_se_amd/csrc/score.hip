@@ -8,8 +8,8 @@
 // softmax needs each row's global max and sum before any weight can be added to a key, so the work is two passes
 // over QK^T: pass 1 streams K in chunks and keeps an online (max, sum) per row; pass 2 merges those, recomputes
 // QK^T and adds exp2(s - max - log2 sum) into per-key column sums. For bf16 (d = 128) QK^T runs on MFMA
-// (v_mfma_f32_16x16x32_bf16, fp32 accumulate); fp32 inputs use a plain VALU path. A workgroup covers 256 query
-// rows (4 waves x 64) and one key chunk; with more than 256 rows, a third kernel sums the row groups' column sums.
+// (v_mfma_f32_16x16x32_bf16, fp32 accumulate); fp32 inputs use a plain VALU path. A workgroup covers 128 or 256
+// query rows (4 or 8 waves x 32) and one key chunk; with several row groups, a third kernel sums their column sums.
 #include "common.hpp"
 
 namespace se {
@@ -105,9 +105,9 @@ __global__ __launch_bounds__(kMaxRowsPerWG) void stats_merge(ScoreArgs a) {
 // ---- MFMA path (bf16, d = 128) -------------------------------------------------------------------------------
 // S = Q K^T per 16x16 tile: A = 16 query rows x 32 dims, B = 32 dims x 16 keys; lane l holds A row l%16 and B
 // column l%16 with dims 8*(l/16)..+8 of each 32-dim step, and receives S rows 4*(l/16)..+4 of column l%16.
-// A workgroup owns one key chunk (<= 1024 keys): the chunk's block ids and positions are staged in LDS once,
-// and K fragments of the next 64 keys are loaded while the current 64 are multiplied. Logits stay unscaled;
-// the scale (times log2 e) is folded into the exp2 argument.
+// A workgroup owns one key chunk (<= 2048 keys): the chunk's row addresses and positions are staged in LDS once,
+// and K moves through an LDS ring 64 keys at a time, the next sub-chunks in flight while the current one is
+// multiplied. Logits stay unscaled; the scale (times log2 e) is folded into the exp2 argument.
 constexpr int kSub = 64;
 
 // Workgroup shape: NW waves x RPW query rows, and at most MAXC keys per workgroup (the LDS tables are sized for
