@@ -87,6 +87,7 @@ typedef struct se_cache {
  *     unused. Each query row is a softmax over the resident region slots (no mask);
  *     scores[(b*n_kv+g)*score_stride + (s - w0)] for s in the region.
  * Arithmetic: products of stored values exact, fp32 accumulation, fp32 output.
+ * Errors: SE_ERR_UNSUPPORTED when num_blocks * n_kv * page >= 2^31 (pool rows are addressed with 32-bit ids).
  */
 enum { SE_SCORE_CAUSAL = 0, SE_SCORE_BIDIR = 1 };
 typedef struct {

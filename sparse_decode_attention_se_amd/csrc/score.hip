@@ -534,6 +534,310 @@ __global__ __launch_bounds__((Shape<RPW, NW_>::NT), (Shape<RPW, NW_>::WPS)) void
   }
 }
 
+// ---- streaming MFMA path (bf16, d = 128, at most 256 query rows) ------------------------------------------------
+// S^T = K Q^T per 16x16 tile: A = 16 keys x 32 dims, held in registers, B = 32 dims x 16 query rows, read from LDS.
+// Lane l receives query row l%16 and keys 4*(l/16)..+4 of the tile. The 128 dims are contracted in a permuted
+// order (k-step t, lane group h = l/16 take dims 32h + 8t..+8), so that a lane reads 64 contiguous bytes of its
+// key row; Q is read with the same permutation. Each wave streams its own 64-key steps of the chunk straight from
+// global memory (the next step's loads in flight while the current one is computed): K never passes through LDS
+// and no barrier separates the steps, so the waves of a SIMD drift apart and one wave's MFMAs run while another
+// does its softmax work.
+constexpr int kStreamRows = 256;
+constexpr int kStreamQB = kStreamRows / 16;  // 16-row query blocks
+
+// one 64-key step of a wave: the K fragments of its four 16-key tiles and, per tile, the position of the key this
+// lane loads (tile row l%16; -1: outside the chunk or not resident)
+struct KStep {
+  bf16x8 f[4][4];  // [key tile][k-step]
+  int pos[4];
+};
+
+// the block-table entries and positions of a step's keys (loaded a step before the keys themselves)
+struct KAddr {
+  int blk[4], pos[4], page[4];
+};
+
+// every load is issued unconditionally (indices clamped into the chunk), so none waits behind a branch
+SE_DEV void kaddr_load(const ScoreArgs &a, int b, int g, int c0, int c1, int step, KAddr &ad) {
+  const int lane = threadIdx.x & 63;
+  const int32_t *bt = a.bt + (int64_t)b * a.max_blocks;
+  const int32_t *pos = a.pos + ((int64_t)b * a.n_kv + g) * a.max_blocks * a.page;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    const int key = min(c0 + step * kSub + kb * 16 + (lane & 15), c1 - 1);
+    ad.page[kb] = key / a.page;
+    ad.blk[kb] = bt[ad.page[kb]];
+    ad.pos[kb] = pos[key];
+  }
+}
+
+SE_DEV void kstep_fetch(const ScoreArgs &a, int g, int c0, int c1, int step, const KAddr &ad, KStep &ks) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    const int key = c0 + step * kSub + kb * 16 + (lane & 15);
+    const bool ok = (key < c1) & (ad.pos[kb] >= 0) & ((unsigned)ad.blk[kb] < (unsigned)a.num_blocks);
+    const int keep = -(int)ok;  // all ones or zero: arithmetic instead of a select the compiler may branch on
+    const int row = ((ad.blk[kb] * a.n_kv + g) * a.page + (key - ad.page[kb] * a.page)) & keep;
+    ks.pos[kb] = (ad.pos[kb] & keep) | ~keep;
+    const char *src = a.k + (int64_t)row * 256 + (lane >> 4) * 64;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) ks.f[kb][t] = __builtin_bit_cast(bf16x8, ld16(src + t * 16));
+  }
+}
+
+// B fragment (query block qb, k-step t) from the swizzled Q rows in LDS: piece p of row r sits at
+// r * 256 + ((p ^ (r % 16)) * 16), so the 16 rows a read touches fall in distinct bank groups
+SE_DEV bf16x8 q_frag(const char *s_q, int qb, int t) {
+  const int lane = threadIdx.x & 63;
+  const int r = qb * 16 + (lane & 15);
+  const int piece = (lane >> 4) * 4 + t;
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(s_q + r * 256 + ((piece ^ (lane & 15)) << 4)));
+}
+
+SE_DEV void stile(const KStep &ks, const char *s_q, int qb, floatx4 (&acc)[4]) {
+  bf16x8 qf[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) qf[t] = q_frag(s_q, qb, t);
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) acc[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) acc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ks.f[kb][t], qf[t], acc[kb], 0, 0, 0);
+}
+
+// max of 16 values that are VALU results (never MFMA results: the asm is outside the compiler's hazard checks,
+// and an MFMA result needs wait states before a VALU instruction may read it)
+SE_DEV float max16(const float (&x)[16]) {
+  return fmaxf(fmaxf(max4(x[0], x[1], x[2], x[3]), max4(x[4], x[5], x[6], x[7])),
+               fmaxf(max4(x[8], x[9], x[10], x[11]), max4(x[12], x[13], x[14], x[15])));
+}
+
+// keys of the lane's outputs that its query row may not see become -inf (the row's limit and the keys' positions
+// come from LDS: s_kp holds the positions of the wave's 64 keys of this step)
+SE_DEV void stream_mask(const int *s_kp, int lim, floatx4 (&acc)[4]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int p = s_kp[kb * 16 + (lane >> 4) * 4 + v];
+      acc[kb][v] = (p >= 0 && p <= lim) ? acc[kb][v] : -INFINITY;
+    }
+}
+
+// sums of 16 values over the 16 lanes of a row, scattered: lane j of the row receives the total of value j.
+// Four exchange rounds (partners j^15, j^7, j^2, j^1 within the row); each halves the values a lane carries.
+template <int CTRL>
+SE_DEV float dpp_any(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+template <int N, int CTRL>
+SE_DEV void rs_round(float (&v)[16], bool hi) {
+#pragma unroll
+  for (int i = 0; i < N / 2; ++i) {
+    const float keep = hi ? v[N / 2 + i] : v[i];
+    const float send = hi ? v[i] : v[N / 2 + i];
+    v[i] = keep + dpp_any<CTRL>(send);
+  }
+}
+SE_DEV float row16_reduce_scatter(float (&v)[16]) {
+  const int j = threadIdx.x & 15;
+  rs_round<16, 0x140>(v, j & 8);  // row_mirror: j <-> 15 - j
+  rs_round<8, 0x141>(v, j & 4);   // row_half_mirror: j <-> 7 - j
+  rs_round<4, 0x4e>(v, j & 2);    // quad_perm [2,3,0,1]
+  rs_round<2, 0xb1>(v, j & 1);    // quad_perm [1,0,3,2]
+  return v[0];
+}
+
+template <int PASS, int NW>
+__global__ __launch_bounds__(NW * 64, 2) void window_stream(ScoreArgs a) {
+  constexpr int NT = NW * 64;
+  const int unit = blockIdx.z, rg = blockIdx.y, chunk = blockIdx.x;
+  const int b = unit / a.n_kv, g = unit % a.n_kv;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ __attribute__((aligned(16))) char s_q[kStreamRows * 256];
+  __shared__ int s_lim[kStreamRows];
+  __shared__ int s_kp[NW][kSub];
+  __shared__ int s_limmin;
+  int k0, k1, n;
+  key_range(a, unit, k0, k1, n);
+  const int c0 = k0 + chunk * a.kc, c1 = min(c0 + a.kc, k1);
+  if (PASS == 2 && c0 >= c1) return;  // uniform: nothing to score in this chunk
+  const int nsub = c1 > c0 ? (c1 - c0 + kSub - 1) / kSub : 0;
+  const int rows = min(kStreamRows, a.R * a.wq - rg * kStreamRows);
+
+  // the wave's first step, and the addresses of its second, are in flight while the query rows are staged
+  KStep ka, kb2;
+  KAddr ad;
+  int s = __builtin_amdgcn_readfirstlane(wave);
+  if (s < nsub) {
+    kaddr_load(a, b, g, c0, c1, s, ad);
+    kstep_fetch(a, g, c0, c1, s, ad, ka);
+    kaddr_load(a, b, g, c0, c1, min(s + NW, nsub - 1), ad);
+  }
+
+  if (threadIdx.x == 0) s_limmin = 0x7fffffff;
+  const char *qbase = a.q + (((int64_t)b * a.n_kv + g) * a.R * a.wq + (int64_t)rg * kStreamRows) * 256;
+  constexpr int kPieces = kStreamRows * 16 / NT;
+  u32x4 qv[kPieces];
+#pragma unroll
+  for (int j = 0; j < kPieces; ++j) {  // rows past the last are read from row 0 and stored as zeros
+    const int i = threadIdx.x + j * NT;
+    qv[j] = ld16(qbase + (int64_t)((i >> 4) < rows ? i : (i & 15)) * 16);
+  }
+#pragma unroll
+  for (int j = 0; j < kPieces; ++j) {
+    const int i = threadIdx.x + j * NT, r = i >> 4, p = i & 15;
+    const bool in = r < rows;
+    const u32x4 v = {in ? qv[j].x : 0u, in ? qv[j].y : 0u, in ? qv[j].z : 0u, in ? qv[j].w : 0u};
+    *reinterpret_cast<u32x4 *>(s_q + r * 256 + ((p ^ (r & 15)) << 4)) = v;
+  }
+  __syncthreads();  // s_limmin initialised
+  for (int r = threadIdx.x; r < kStreamRows; r += NT) {
+    const int lim = row_limit(a, b, rg * kStreamRows + r);
+    s_lim[r] = lim;
+    if (lim >= 0) atomicMin(&s_limmin, lim);
+  }
+  __syncthreads();
+  const int limmin = s_limmin;
+  const int nqb = (rows + 15) / 16;
+  const float c = a.scale_log2;
+
+  // pass 1: per query block, the lane's running sum of exp2(s c - m c) over its keys, and -m c. The reference m
+  // starts at the first visible logit and afterwards only moves up, when a logit exceeds it by more than kLazy / c
+  // (the terms stay below 2^kLazy meanwhile, which fp32 sums hold exactly enough).
+  float st_l[kStreamQB], st_nmc[kStreamQB];
+  // pass 2: per query block, the merged statistic of the lane's row (+inf: no such row)
+  float ml[kStreamQB];
+  if (PASS == 1) {
+#pragma unroll
+    for (int qb = 0; qb < kStreamQB; ++qb) st_l[qb] = 0.f, st_nmc[qb] = 0.f;
+  } else {
+    const float *mlog = a.mlog + ((int64_t)unit * a.nrg + rg) * a.rpg;
+#pragma unroll
+    for (int qb = 0; qb < kStreamQB; ++qb) {
+      const int r = qb * 16 + (lane & 15);
+      const float v = mlog[r];  // a.rpg = kStreamRows entries exist for every row group
+      ml[qb] = r < rows ? v : INFINITY;
+    }
+  }
+
+  auto step = [&](const KStep &ks, int sidx) {
+    int pmin = min(min(ks.pos[0], ks.pos[1]), min(ks.pos[2], ks.pos[3]));
+    int pmax = max(max(ks.pos[0], ks.pos[1]), max(ks.pos[2], ks.pos[3]));
+    const bool fast = __builtin_amdgcn_ballot_w64(!(pmin >= 0 && pmax <= limmin)) == 0;
+    if (!fast) {
+      if (lane < 16) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) s_kp[wave][kb * 16 + lane] = ks.pos[kb];
+      }
+      // LDS accesses of a wave complete in order; this keeps the compiler from moving the reads above the writes
+      asm volatile("" ::: "memory");
+    }
+    float col[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) col[i] = 0.f;
+#pragma unroll
+    for (int qb = 0; qb < kStreamQB; ++qb) {
+      if (qb < nqb) {  // uniform
+        floatx4 acc[4];
+        stile(ks, s_q, qb, acc);
+        if (!fast) stream_mask(s_kp[wave], s_lim[qb * 16 + (lane & 15)], acc);
+        if constexpr (PASS == 1) {
+          float t[16];  // s c - m c against the current reference
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) t[kb * 4 + v] = fmaf(acc[kb][v], c, st_nmc[qb]);
+          const float tm = max16(t);
+          const bool first = st_l[qb] == 0.f;  // nothing visible yet: the reference is not set
+          const bool mv = (tm > kLazy) | (first & (tm > -INFINITY));
+          if (__builtin_amdgcn_ballot_w64(mv)) {
+            if (mv) {  // the reference moves to the lane's largest logit of this block
+              st_l[qb] = first ? 0.f : st_l[qb] * __builtin_amdgcn_exp2f(-tm);
+              st_nmc[qb] -= tm;
+#pragma unroll
+              for (int i = 0; i < 16; ++i) t[i] -= tm;
+            }
+          }
+          float sum = 0.f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sum += __builtin_amdgcn_exp2f(t[i]);
+          st_l[qb] += sum;
+        } else {
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) col[kb * 4 + v] += __builtin_amdgcn_exp2f(fmaf(acc[kb][v], c, -ml[qb]));
+        }
+      }
+    }
+    if constexpr (PASS == 2) {
+      const float tot = row16_reduce_scatter(col);
+      const int j = lane & 15;
+      const int key = sidx * kSub + (j >> 2) * 16 + (lane >> 4) * 4 + (j & 3);
+      if (c0 + key < c1) {
+        const int idx = c0 + key - k0;
+        if (a.nrg == 1) a.scores[(int64_t)unit * a.score_stride + idx] = tot;
+        else a.colpart[((int64_t)unit * a.nrg + rg) * a.key_span + idx] = tot;
+      }
+    }
+  };
+
+  // Two register sets: while a step is computed, the next one's keys load into the other set and the addresses
+  // of the one after are loaded (the wait for those addresses, a step later, also covers the keys in flight).
+  // The loads are unconditional: past the wave's last step they fetch that step again, unused, so that no path
+  // through the loop skips a wait (the compiler's wait counts would otherwise hold the MFMAs for the prefetch).
+  const int last = nsub - 1;
+  while (s < nsub) {
+    kstep_fetch(a, g, c0, c1, min(s + NW, last), ad, kb2);
+    kaddr_load(a, b, g, c0, c1, min(s + 2 * NW, last), ad);
+    step(ka, s);
+    s += NW;
+    if (s >= nsub) break;
+    kstep_fetch(a, g, c0, c1, min(s + NW, last), ad, ka);
+    kaddr_load(a, b, g, c0, c1, min(s + 2 * NW, last), ad);
+    step(kb2, s);
+    s += NW;
+  }
+
+  if constexpr (PASS == 1) {
+    // combine the four lanes of each row, then the waves, and write the chunk's (max, sum) per row (log2 domain)
+    __syncthreads();  // every wave is done with s_q: it holds the per-wave row statistics from here on
+    float2 *s_st = reinterpret_cast<float2 *>(s_q);  // [NW][kStreamRows]
+#pragma unroll
+    for (int qb = 0; qb < kStreamQB; ++qb) {
+      const float mc = st_l[qb] > 0.f ? -st_nmc[qb] : -1e30f;  // this lane's m c (none: no visible key)
+      const float mr = cross_row_max(mc);
+      const float lr = cross_row_sum(st_l[qb] * __builtin_amdgcn_exp2f(mc - mr));
+      if (lane < 16) s_st[wave * kStreamRows + qb * 16 + lane] = make_float2(mr, lr);
+    }
+    __syncthreads();
+    float *out = a.stats + ((((int64_t)unit * a.nrg + rg) * a.nkc + chunk) * a.rpg) * 2;
+    for (int r = threadIdx.x; r < kStreamRows; r += NT) {
+      float mm = -1e30f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) mm = fmaxf(mm, s_st[w * kStreamRows + r].x);
+      float ll = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) ll += s_st[w * kStreamRows + r].y * __builtin_amdgcn_exp2f(s_st[w * kStreamRows + r].x - mm);
+      out[r * 2] = mm;
+      out[r * 2 + 1] = ll;
+    }
+  }
+}
+
+#ifndef SE_STREAM_NW
+#define SE_STREAM_NW 4
+#endif
+#ifndef SE_STREAM_WGS
+#define SE_STREAM_WGS 512
+#endif
+constexpr int kStreamNW = SE_STREAM_NW;
+constexpr int kStreamWGs = SE_STREAM_WGS;  // workgroups a launch aims for (two per CU at NW = 4)
+
 #ifndef SE_SCORE_RPW
 #define SE_SCORE_RPW 32
 #endif
@@ -635,7 +939,7 @@ __global__ void colsum_reduce(ScoreArgs a) {
 }
 
 struct Plan {
-  int nrg, nkc, kc, key_span, rpg, nw;  // nw: waves per MFMA workgroup (0: the fp32 VALU path)
+  int nrg, nkc, kc, key_span, rpg, nw;  // nw: waves per MFMA workgroup (0: fp32 VALU path, -1: streaming)
   size_t stats_bytes, col_bytes, mlog_bytes;
 };
 
@@ -647,8 +951,8 @@ Plan make_plan(const se_cache_t *c, const se_window_params_t *p) {
   int maxc;
   if (!mfma) {
     pl.nw = 0, pl.rpg = kValuRows, maxc = 1024;
-  } else if (rows <= 256) {
-    pl.nw = 8, pl.rpg = Shape<kScoreRPW, 8>::ROWS, maxc = Shape<kScoreRPW, 8>::MAXC;
+  } else if (rows <= kStreamRows) {
+    pl.nw = -1, pl.rpg = kStreamRows, maxc = 0;
   } else {
     pl.nw = 4, pl.rpg = Shape<kScoreRPW, 4>::ROWS, maxc = Shape<kScoreRPW, 4>::MAXC;
   }
@@ -656,8 +960,18 @@ Plan make_plan(const se_cache_t *c, const se_window_params_t *p) {
   const int max_slots = c->max_blocks * c->page;
   pl.key_span = p->mode == SE_SCORE_CAUSAL ? max_slots : p->window - p->protect;
   const int span64 = (pl.key_span + 63) / 64 * 64;
-  pl.kc = span64 < maxc ? span64 : maxc;
-  if (pl.kc < 64) pl.kc = 64;
+  if (pl.nw < 0) {
+    // chunks of whole rounds of 64-key steps (one per wave) that give about kStreamWGs workgroups
+    const long long groups = (long long)c->B * c->n_kv * pl.nrg;
+    const long long per = (kStreamWGs + groups - 1) / groups;
+    const int round = kSub * kStreamNW;
+    long long kc = (pl.key_span + per - 1) / per;
+    kc = (kc + round - 1) / round * round;
+    pl.kc = (int)(kc < round ? round : (kc > 16384 ? 16384 : kc));
+  } else {
+    pl.kc = span64 < maxc ? span64 : maxc;
+    if (pl.kc < 64) pl.kc = 64;
+  }
   pl.nkc = (pl.key_span + pl.kc - 1) / pl.kc;
   const size_t units = (size_t)c->B * c->n_kv;
   pl.stats_bytes = se_host::align_up(units * pl.nrg * pl.nkc * pl.rpg * 2 * sizeof(float));
@@ -704,6 +1018,7 @@ extern "C" int32_t se_window_score(const se_cache_t *c, const void *q_win, const
   const bool mfma = c->dtype == SE_DTYPE_BF16 && c->d == 128;
   const bool valu = c->dtype == SE_DTYPE_F32 && c->d == 64;
   if (!mfma && !valu) return SE_ERR_DTYPE;
+  if ((long long)c->num_blocks * c->n_kv * c->page >= (1ll << 31)) return SE_ERR_UNSUPPORTED;  // 32-bit row ids
   se::Plan pl = se::make_plan(c, p);
   if (!ws || ws_bytes < pl.stats_bytes + pl.col_bytes + pl.mlog_bytes) return SE_ERR_WORKSPACE;
   se::ScoreArgs a;
@@ -737,8 +1052,10 @@ extern "C" int32_t se_window_score(const se_cache_t *c, const void *q_win, const
   const int units = c->B * c->n_kv;
   const dim3 grid(pl.nkc, pl.nrg, units);
   hipStream_t st = (hipStream_t)stream;
-  if (pl.nw == 8) {
-    se::launch_mfma<8>(pl, a, units, st);
+  if (pl.nw < 0) {
+    hipLaunchKernelGGL((se::window_stream<1, se::kStreamNW>), grid, dim3(se::kStreamNW * 64), 0, st, a);
+    hipLaunchKernelGGL(se::stats_merge, dim3(pl.nrg, units), dim3(pl.rpg), 0, st, a);
+    hipLaunchKernelGGL((se::window_stream<2, se::kStreamNW>), grid, dim3(se::kStreamNW * 64), 0, st, a);
   } else if (pl.nw == 4) {
     se::launch_mfma<4>(pl, a, units, st);
   } else {
