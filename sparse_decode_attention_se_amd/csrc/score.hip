@@ -536,9 +536,8 @@ __global__ __launch_bounds__((Shape<RPW, NW_>::NT), (Shape<RPW, NW_>::WPS)) void
 
 // ---- streaming MFMA path (bf16, d = 128, at most 256 query rows) ------------------------------------------------
 // S^T = K Q^T per 16x16 tile: A = 16 keys x 32 dims, held in registers, B = 32 dims x 16 query rows, read from LDS.
-// Lane l receives query row l%16 and keys 4*(l/16)..+4 of the tile. The 128 dims are contracted in a permuted
-// order (k-step t, lane group h = l/16 take dims 32h + 8t..+8), so that a lane reads 64 contiguous bytes of its
-// key row; Q is read with the same permutation. Each wave streams its own 64-key steps of the chunk straight from
+// Lane l receives query row l%16 and keys 4*(l/16)..+4 of the tile. K-step t covers dims 32t..32t+32 (lane group
+// h = l/16 holds dims 32t + 8h..+8), so each key load instruction reads 64 contiguous bytes of 16 rows. Each wave streams its own 64-key steps of the chunk straight from
 // global memory (the next step's loads in flight while the current one is computed): K never passes through LDS
 // and no barrier separates the steps, so the waves of a SIMD drift apart and one wave's MFMAs run while another
 // does its softmax work.
@@ -580,9 +579,9 @@ SE_DEV void kstep_fetch(const ScoreArgs &a, int g, int c0, int c1, int step, con
     const int keep = -(int)ok;  // all ones or zero: arithmetic instead of a select the compiler may branch on
     const int row = ((ad.blk[kb] * a.n_kv + g) * a.page + (key - ad.page[kb] * a.page)) & keep;
     ks.pos[kb] = (ad.pos[kb] & keep) | ~keep;
-    const char *src = a.k + (int64_t)row * 256 + (lane >> 4) * 64;
+    const char *src = a.k + (int64_t)row * 256 + (lane >> 4) * 16;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) ks.f[kb][t] = __builtin_bit_cast(bf16x8, ld16(src + t * 16));
+    for (int t = 0; t < 4; ++t) ks.f[kb][t] = __builtin_bit_cast(bf16x8, ld16(src + t * 64));
   }
 }
 
@@ -591,7 +590,7 @@ SE_DEV void kstep_fetch(const ScoreArgs &a, int g, int c0, int c1, int step, con
 SE_DEV bf16x8 q_frag(const char *s_q, int qb, int t) {
   const int lane = threadIdx.x & 63;
   const int r = qb * 16 + (lane & 15);
-  const int piece = (lane >> 4) * 4 + t;
+  const int piece = t * 4 + (lane >> 4);
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(s_q + r * 256 + ((piece ^ (lane & 15)) << 4)));
 }
 
