@@ -8,8 +8,11 @@
 // softmax needs each row's global max and sum before any weight can be added to a key, so the work is two passes
 // over QK^T: pass 1 streams K in chunks and keeps an online (max, sum) per row; pass 2 merges those, recomputes
 // QK^T and adds exp2(s - max - log2 sum) into per-key column sums. For bf16 (d = 128) QK^T runs on MFMA
-// (v_mfma_f32_16x16x32_bf16, fp32 accumulate); fp32 inputs use a plain VALU path. A workgroup covers 128 or 256
-// query rows (4 or 8 waves x 32) and one key chunk; with several row groups, a third kernel sums their column sums.
+// (v_mfma_f32_16x16x32_bf16, fp32 accumulate); fp32 inputs use a plain VALU path. A workgroup covers up to 256
+// query rows and one key chunk; with several row groups, a last kernel sums their column sums. When one chunk holds
+// a unit's whole key range and every wave has at most two steps, a single kernel does both passes.
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace se {
@@ -102,210 +105,16 @@ __global__ __launch_bounds__(kMaxRowsPerWG) void stats_merge(ScoreArgs a) {
   a.mlog[((int64_t)unit * a.nrg + rg) * a.rpg + threadIdx.x] = merge_row(a, unit, rg, threadIdx.x);
 }
 
-// ---- MFMA path (bf16, d = 128) -------------------------------------------------------------------------------
-// S = Q K^T per 16x16 tile: A = 16 query rows x 32 dims, B = 32 dims x 16 keys; lane l holds A row l%16 and B
-// column l%16 with dims 8*(l/16)..+8 of each 32-dim step, and receives S rows 4*(l/16)..+4 of column l%16.
-// A workgroup owns one key chunk (<= 2048 keys): the chunk's row addresses and positions are staged in LDS once,
-// and K moves through an LDS ring 64 keys at a time, the next sub-chunks in flight while the current one is
-// multiplied. Logits stay unscaled; the scale (times log2 e) is folded into the exp2 argument.
-constexpr int kSub = 64;
+constexpr int kSub = 64;  // keys per step of a wave
 
-// Workgroup shape: NW waves x RPW query rows, and at most MAXC keys per workgroup (the LDS tables are sized for
-// them). With NW = 4 (128 rows, 1024 keys, ~80 KiB LDS) two workgroups share a CU, so the two waves of each SIMD
-// belong to different workgroups whose barriers are independent and one's MFMA/LDS phases overlap the other's
-// VALU phase; that shape is used when a unit has more than 256 query rows. Otherwise NW = 8 covers all of a
-// unit's rows (up to 256) in one workgroup, so K is read once and no cross-group column sum is needed.
-template <int RPW, int NW_>
-struct Shape {
-  static constexpr int RB = RPW / 16;            // 16-row MFMA blocks per wave
-  static constexpr int NW = NW_;                 // waves per workgroup
-  static constexpr int NT = NW * 64;             // threads
-  static constexpr int ROWS = NW * RPW;          // query rows per workgroup
-  static constexpr int MAXC = NW >= 8 ? 2048 : 1024;
-  static constexpr int BPW = 16 / NW;            // 1 KiB blocks of a sub-chunk each wave fetches
-  static constexpr int WPS = RPW == 16 ? 4 : 2;  // waves per SIMD the register budget is cut for
-};
-
-template <int RB>
-struct QFrags {
-  bf16x8 f[RB][4];  // [row block][k-step]
-  int lim[RB][4];   // [row block][v]: position limit of S row 4*(l/16)+v of the block (-1: no such row)
-};
-
-template <int RB>
-SE_DEV void load_q(const ScoreArgs &a, int b, int g, int rho_wave, QFrags<RB> &qf) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    int rho = rho_wave + rb * 16 + (lane & 15);
-    bool ok = rho < a.R * a.wq;
-    const char *row = ok ? q_row(a, b, g, rho, 256) + (lane >> 4) * 16 : nullptr;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      qf.f[rb][ks] = __builtin_bit_cast(bf16x8, ok ? ld16(row + ks * 64) : u32x4{0, 0, 0, 0});
-#pragma unroll
-    for (int v = 0; v < 4; ++v) qf.lim[rb][v] = row_limit(a, b, rho_wave + rb * 16 + (lane >> 4) * 4 + v);
-  }
-}
-
-struct Chunk {
-  int c0, c1, pbase, nsub;
-  bool fast;  // every key of the chunk exists, is resident and visible to every row of the workgroup
-};
-
-// stage the chunk's key positions and pool row indices in LDS; keys that cannot be read get position -1
-template <int NT, int MAXC>
-SE_DEV Chunk stage_chunk(const ScoreArgs &a, int b, int g, int c0, int c1, int rg, int *s_blk, int *s_pos,
-                         int *s_row, int *s_mm) {
-  Chunk ch;
-  ch.c0 = c0;
-  ch.c1 = c1;
-  ch.pbase = c0 / a.page;
-  ch.nsub = (c1 - c0 + kSub - 1) / kSub;
-  const int npg = c1 > c0 ? (c1 - 1) / a.page - ch.pbase + 1 : 0;
-  if (threadIdx.x == 0) {
-    s_mm[0] = 0x7fffffff;  // min position
-    s_mm[1] = -1;          // max position
-    s_mm[2] = 0x7fffffff;  // min row limit of the workgroup's rows
-  }
-  for (int i = threadIdx.x; i < npg; i += NT) s_blk[i] = a.bt[(int64_t)b * a.max_blocks + ch.pbase + i];
-  __syncthreads();
-  const int32_t *pos = a.pos + ((int64_t)b * a.n_kv + g) * a.max_blocks * a.page;
-  int mn = 0x7fffffff, mx = -1;
-  constexpr int kPer = MAXC / NT;
-  int pv[kPer];
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {  // all position loads in flight at once
-    const int key = c0 + threadIdx.x + j * NT;
-    pv[j] = key < c1 ? pos[key] : -1;
-  }
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int i = threadIdx.x + j * NT;
-    if (i >= ch.nsub * kSub) break;
-    const int key = c0 + i;
-    int p = pv[j], row = 0;
-    if (key < c1) {
-      const int blk = s_blk[key / a.page - ch.pbase];
-      if (p >= 0 && !blk_ok(blk, a.num_blocks)) p = -1;
-      if (p >= 0) row = (blk * a.n_kv + g) * a.page + key % a.page;
-      mn = min(mn, p);
-      mx = max(mx, p);
-    }
-    s_pos[i] = p;
-    s_row[i] = row;
-  }
-  atomicMin(&s_mm[0], mn);
-  atomicMax(&s_mm[1], mx);
-  for (int r = threadIdx.x; r < a.rpg; r += NT) {
-    const int lim = row_limit(a, b, rg * a.rpg + r);
-    if (lim >= 0) atomicMin(&s_mm[2], lim);
-  }
-  __syncthreads();
-  ch.fast = (c1 - c0 == ch.nsub * kSub) && s_mm[0] >= 0 && s_mm[1] <= s_mm[2];
-  return ch;
-}
-
-// K staging: 64-key sub-chunks (16 KiB) go from global memory straight into a ring of kRing LDS buffers with LDS
-// DMA (global_load_lds_dwordx4: lane i of a wave writes 16 bytes at M0 + 16 i, no registers involved). In LDS the 4
-// keys of each 1 KiB block are stored as 64 16-byte positions, piece c of key r at position r * 16 + (c ^ swz),
-// swz = 4 * (block % 4) + r: the 16 lanes of a B-fragment read (16 keys, one piece each) hit 16 distinct 16-byte
-// bank groups. So lane i of the DMA that fills a block fetches key r = i / 16, piece (i % 16) ^ swz.
-constexpr int kSubBytes = kSub * 256;
-constexpr int kRing = 4;
-
-SE_DEV int swz(int r, int blk) { return ((blk & 3) << 2) | r; }
-
-// The DMA is issued as inline assembly so that the compiler's wait-count bookkeeping does not track it (it would
-// otherwise wait for every DMA in flight before any LDS read); the kernel waits for its DMAs itself in publish().
-// The compiler's own waits stay correct: they can only over-count. One wait state separates the M0 write from
-// the DMA that reads it.
-SE_DEV void lds_dma16(const char *g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(g) : "memory", "m0");
-}
-
-// fetch sub-chunk `sub` of the chunk into ring slot sub % kRing (nothing past the last sub-chunk)
-template <int NW>
-SE_DEV void issue_sub(const ScoreArgs &a, const Chunk &ch, int sub, const int *s_row, uint32_t ring) {
-  if (sub >= ch.nsub) return;  // uniform
-  constexpr int BPW = 16 / NW;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int r = lane >> 4;
-  const uint32_t slot = ring + (uint32_t)(sub % kRing) * kSubBytes;
-#pragma unroll
-  for (int i = 0; i < BPW; ++i) {
-    const int blk = wave * BPW + i;
-    const int c = (lane & 15) ^ swz(r, blk);
-    const int row = s_row[sub * kSub + blk * 4 + r];
-    lds_dma16(a.k + (int64_t)row * 256 + c * 16, __builtin_amdgcn_readfirstlane(slot + blk * 1024));
-  }
-}
-
-// Wait until at most N of this wave's DMAs are still in flight and its LDS accesses are done, then meet the other
-// waves: afterwards every wave's older DMAs have landed. The memory clobber keeps the compiler from moving LDS
-// accesses across.
-template <int N>
-SE_DEV void publish() {
-  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
-}
-
-// publish sub-chunk `need` when the DMA groups of sub-chunks [0, issued) have been issued, one group of BPW per
-// sub-chunk: the groups younger than `need` that exist may stay in flight (up to kRing - 2 of them)
-template <int BPW>
-SE_DEV void publish_upto(int need, int issued) {
-  const int younger = issued - 1 - need;  // uniform
-  if (younger >= kRing - 2) publish<(kRing - 2) * BPW>();
-  else if (younger == 1) publish<BPW>();
-  else publish<0>();
-}
-
-// B fragment of key tile tt, k-step ks from a staged sub-chunk
-SE_DEV bf16x8 read_frag(const char *slot, int tt, int ks) {
-  const int lane = threadIdx.x & 63;
-  const int key = tt * 16 + (lane & 15);
-  const int blk = key >> 2, r = key & 3;
-  const int piece = ks * 4 + (lane >> 4);
-  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(slot + blk * 1024 + (r * 16 + (piece ^ swz(r, blk))) * 16));
-}
-
-// S tiles of the wave's row blocks x the sub-chunk's 4 key tiles; k-step outermost so each step issues RB*4
-// independent MFMAs
-template <int RB>
-SE_DEV void mfma_sub(const QFrags<RB> &qf, const char *slot, floatx4 (&s)[RB][4]) {
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) s[rb][tt] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    bf16x8 k[4];
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) k[tt] = read_frag(slot, tt, ks);
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt)
-        s[rb][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf.f[rb][ks], k[tt], s[rb][tt], 0, 0, 0);
-  }
-}
-
-// pass 1 state: running max (unscaled logits) and sum of exp2((s - max) * c) per S row of the lane
-template <int RB>
-struct Stats {
-  float l[RB][4];    // sum of exp2((s - m) * c) over the row's keys so far
-  float thr[RB][4];  // m + kLazy / c: a logit above it moves the reference m
-  float nmc[RB][4];  // -m * c (m itself is not kept)
-};
-
-// Pass 1 VALU: the running max m of a row is only moved (and its sum rescaled) when a logit exceeds it by more than
-// kLazy / c in log2 units; until then terms are exp2 of at most kLazy, which fp32 sums hold exactly enough. The
-// common step is branch-free, so the compiler interleaves it with the next sub-chunk's MFMAs: every row's terms
-// are taken against its stored reference, and rows whose max moved keep their old sum (a select). stats_fix then
-// redoes those rows in a wave-uniform branch that is rarely taken once the first keys have been seen.
+// The lazy running max of pass 1: a row's reference m only moves (and its sum is rescaled) when a logit exceeds it
+// by more than kLazy / c in log2 units; until then the terms are exp2 of at most kLazy, which fp32 sums hold
+// exactly enough.
 constexpr float kLazy = 8.f;
 
-// max of four values that are finite or -inf: two v_max3_f32, without the NaN-quieting copies that fmaxf of
-// MFMA results would add
+// max of four values that are finite or -inf: two v_max3_f32, without the NaN-quieting copies fmaxf would add.
+// Only for VALU results: inline asm is outside the compiler's hazard checks, and an MFMA result needs wait states
+// before a VALU instruction may read it.
 SE_DEV float max4(float a, float b, float c, float d) {
   float t, r;
   asm("v_max3_f32 %0, %1, %2, %3" : "=v"(t) : "v"(a), "v"(b), "v"(c));
@@ -313,234 +122,13 @@ SE_DEV float max4(float a, float b, float c, float d) {
   return r;
 }
 
-template <int RB>
-SE_DEV void stats_init(const ScoreArgs &a, Stats<RB> &st) {
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      st.l[rb][v] = 0.f;
-      st.thr[rb][v] = -1e30f;
-      st.nmc[rb][v] = 1e30f;  // m * c = -1e30: the first visible key moves it
-    }
-}
-
-// masks the sub-chunk's logits in place (keys a row may not see become -inf) unless FAST
-template <bool FAST, int RB>
-SE_DEV void mask_logits(const QFrags<RB> &qf, int sub, const int *s_pos, floatx4 (&s)[RB][4]) {
-  if (FAST) return;
-  const int lane = threadIdx.x & 63;
-  int kp[4];
-#pragma unroll
-  for (int tt = 0; tt < 4; ++tt) kp[tt] = s_pos[sub * kSub + tt * 16 + (lane & 15)];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-      for (int v = 0; v < 4; ++v)
-        s[rb][tt][v] = (kp[tt] >= 0 && kp[tt] <= qf.lim[rb][v]) ? s[rb][tt][v] : -INFINITY;
-}
-
-// returns (per lane) whether any of the lane's rows moved
-template <int RB>
-SE_DEV bool stats_step(const ScoreArgs &a, const floatx4 (&s)[RB][4], Stats<RB> &st) {
-  const float c = a.scale_log2;
-  bool moved = false;
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const float xm = max4(s[rb][0][v], s[rb][1][v], s[rb][2][v], s[rb][3][v]);
-      const bool mv = xm > st.thr[rb][v];
-      moved |= mv;
-      float acc = 0.f;
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) acc += __builtin_amdgcn_exp2f(fmaf(s[rb][tt][v], c, st.nmc[rb][v]));
-      // an empty use: the sum is computed here for every row, branch-free, in the block of the MFMAs it
-      // interleaves with (otherwise the compiler computes it only under !mv, in a divergent branch per row)
-      asm volatile("" ::"v"(acc));
-      st.l[rb][v] = mv ? st.l[rb][v] : st.l[rb][v] + acc;
-    }
-  }
-  return moved;
-}
-
-template <int RB>
-SE_DEV void stats_fix(const ScoreArgs &a, const floatx4 (&s)[RB][4], Stats<RB> &st) {
-  const float c = a.scale_log2;
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const float xm = max4(s[rb][0][v], s[rb][1][v], s[rb][2][v], s[rb][3][v]);
-      if (xm > st.thr[rb][v]) {
-        const float nmc = -xm * c;
-        float acc = st.l[rb][v] * __builtin_amdgcn_exp2f(nmc - st.nmc[rb][v]);
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) acc += __builtin_amdgcn_exp2f(fmaf(s[rb][tt][v], c, nmc));
-        st.l[rb][v] = acc;
-        st.thr[rb][v] = xm + kLazy / c;
-        st.nmc[rb][v] = nmc;
-      }
-    }
-  }
-}
-
-template <int RB, int NW>
-SE_DEV void colsum_step(const ScoreArgs &a, const floatx4 (&s)[RB][4], const float (&ml)[RB][4],
-                        float (*s_cs)[kSub]) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const float c = a.scale_log2;
-  float col[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) col[tt] += __builtin_amdgcn_exp2f(fmaf(s[rb][tt][v], c, -ml[rb][v]));
-  // after the cross-row sum the four rows of the wave hold the same column sums: all lanes store, same values
-#pragma unroll
-  for (int tt = 0; tt < 4; ++tt) s_cs[wave][tt * 16 + (lane & 15)] = cross_row_sum(col[tt]);
-}
-
-// Scheduling groups for one step: per k-step, the 4 B-fragment LDS reads, then its RB*4 MFMAs each followed by NV
-// VALU instructions (of the previous sub-chunk's softmax work).
-template <int RB, int NV>
-SE_DEV void interleave() {
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // DS read
-#pragma unroll
-    for (int i = 0; i < RB * 4; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);  // VALU
-    }
-  }
-}
-
-template <int PASS, int RPW, int NW_>
-__global__ __launch_bounds__((Shape<RPW, NW_>::NT), (Shape<RPW, NW_>::WPS)) void window_mfma(ScoreArgs a) {
-  using S = Shape<RPW, NW_>;
-  constexpr int RB = S::RB, NW = S::NW, NT = S::NT, BPW = S::BPW, kMaxChunk = S::MAXC;
-  const int unit = blockIdx.z, rg = blockIdx.y, kc = blockIdx.x;
-  const int b = unit / a.n_kv, g = unit % a.n_kv;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  __shared__ __attribute__((aligned(1024))) char s_k[kRing][kSubBytes];
-  __shared__ int s_blk[kMaxChunk / 16 + 2];
-  __shared__ int s_pos[kMaxChunk];
-  __shared__ int s_row[kMaxChunk];
-  __shared__ int s_mm[3];
-  __shared__ float s_cs[PASS == 2 ? 2 : 1][NW][kSub];     // pass 2: each wave's column sums of one step
-  __shared__ float s_col[PASS == 2 ? kMaxChunk : 1];      // pass 2: the chunk's column sums
-  int k0, k1, n;
-  key_range(a, unit, k0, k1, n);
-  const int c0 = k0 + kc * a.kc, c1 = min(c0 + a.kc, k1);
-  if (PASS == 2 && c0 >= c1) return;  // uniform: nothing to score in this chunk
-  const Chunk ch = stage_chunk<NT, kMaxChunk>(a, b, g, c0, max(c0, c1), rg, s_blk, s_pos, s_row, s_mm);
-  const int rho_wave = rg * a.rpg + wave * RPW;
-  QFrags<RB> qf;
-  load_q(a, b, g, rho_wave, qf);
-  Stats<RB> st;
-  float ml[RB][4];
-  if (PASS == 1) {
-    stats_init(a, st);
-  } else {
-    const float *mlog = a.mlog + ((int64_t)unit * a.nrg + rg) * a.rpg;
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int v = 0; v < 4; ++v)
-        ml[rb][v] = qf.lim[rb][v] >= 0 ? mlog[wave * RPW + rb * 16 + (lane >> 4) * 4 + v] : INFINITY;
-  }
-  // the query fragments and row statistics arrive before any DMA is issued (the compiler sees this wait)
-  __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0)
-
-  // Sub-chunk j is fetched into ring slot j % 4 at step j - 4 (the first four before the loop), published by the
-  // barrier of step j - 2, multiplied at step j - 1 into accumulator set (j + 1) % 2, and its softmax work done at
-  // step j. Within a step the MFMAs of sub-chunk j + 1 and the VALU work of sub-chunk j are independent, and the
-  // scheduling groups interleave them so the matrix core and the vector ALU of a wave run concurrently. MFMAs
-  // past the last sub-chunk read a stale slot; their result is never used.
-  const uint32_t ring = (uint32_t)(uintptr_t)&s_k[0][0];
-#pragma unroll
-  for (int j = 0; j < kRing; ++j) issue_sub<NW>(a, ch, j, s_row, ring);
-  publish_upto<BPW>(1, min(ch.nsub, kRing));  // sub-chunks 0 and 1
-  floatx4 acc0[RB][4], acc1[RB][4];
-  mfma_sub(qf, s_k[0], acc0);
-#define SE_STEP(FAST, SUB, CUR, NEXT)                                                                          \
-  {                                                                                                            \
-    mask_logits<FAST>(qf, (SUB), s_pos, CUR);                                                                  \
-    mfma_sub(qf, s_k[((SUB) + 1) % kRing], NEXT);                                                              \
-    if constexpr (PASS == 1) {                                                                                 \
-      const bool moved = stats_step(a, CUR, st);                                                               \
-      interleave<RB, 4>();                                                                                     \
-      if (__ballot(moved)) stats_fix(a, CUR, st);                                                              \
-    } else {                                                                                                   \
-      colsum_step<RB, NW>(a, CUR, ml, s_cs[(SUB) & 1]);                                                        \
-      interleave<RB, 3>();                                                                                     \
-    }                                                                                                          \
-    issue_sub<NW>(a, ch, (SUB) + kRing, s_row, ring);                                                          \
-    publish_upto<BPW>((SUB) + 2, min(ch.nsub, (SUB) + kRing + 1));                                             \
-    if constexpr (PASS == 2) {                                                                                 \
-      if (threadIdx.x < kSub) {                                                                                \
-        float sum = 0.f;                                                                                       \
-        _Pragma("unroll") for (int w = 0; w < NW; ++w) sum += s_cs[(SUB) & 1][w][threadIdx.x];                 \
-        s_col[(SUB) * kSub + threadIdx.x] = sum;                                                               \
-      }                                                                                                        \
-    }                                                                                                          \
-  }
-#define SE_LOOP(FAST)                                                                                          \
-  {                                                                                                            \
-    int sub = 0;                                                                                               \
-    for (; sub + 2 <= ch.nsub; sub += 2) {                                                                     \
-      SE_STEP(FAST, sub, acc0, acc1)                                                                           \
-      SE_STEP(FAST, sub + 1, acc1, acc0)                                                                       \
-    }                                                                                                          \
-    if (sub < ch.nsub) SE_STEP(FAST, sub, acc0, acc1)                                                          \
-  }
-  if (ch.fast) {
-    SE_LOOP(true)
-  } else {
-    SE_LOOP(false)
-  }
-#undef SE_LOOP
-#undef SE_STEP
-  __builtin_amdgcn_s_waitcnt(0x3f70);  // no DMA outlives the loop
-
-  if constexpr (PASS == 1) {
-    // combine the 16 lanes (keys) of each row; write the chunk's (max, sum) per row in the log2 domain
-    float *out = a.stats + ((((int64_t)unit * a.nrg + rg) * a.nkc + kc) * a.rpg) * 2;
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const float mc = -st.nmc[rb][v];  // this lane's m * c
-        const float mr = row16_max(mc);
-        const float lr = row16_sum(st.l[rb][v] * __builtin_amdgcn_exp2f(mc - mr));
-        if ((lane & 15) == 0) {
-          const int r = wave * RPW + rb * 16 + (lane >> 4) * 4 + v;
-          out[r * 2] = mr;
-          out[r * 2 + 1] = lr;
-        }
-      }
-  } else {
-    __syncthreads();
-    for (int j = threadIdx.x; j < c1 - c0; j += NT) {
-      const float sum = s_col[j];
-      const int idx = c0 + j - k0;
-      if (a.nrg == 1) a.scores[(int64_t)unit * a.score_stride + idx] = sum;
-      else a.colpart[((int64_t)unit * a.nrg + rg) * a.key_span + idx] = sum;
-    }
-  }
-}
-
-// ---- streaming MFMA path (bf16, d = 128, at most 256 query rows) ------------------------------------------------
+// ---- MFMA path (bf16, d = 128) -------------------------------------------------------------------------------
 // S^T = K Q^T per 16x16 tile: A = 16 keys x 32 dims, held in registers, B = 32 dims x 16 query rows, read from LDS.
 // Lane l receives query row l%16 and keys 4*(l/16)..+4 of the tile. K-step t covers dims 32t..32t+32 (lane group
-// h = l/16 holds dims 32t + 8h..+8), so each key load instruction reads 64 contiguous bytes of 16 rows. Each wave streams its own 64-key steps of the chunk straight from
-// global memory (the next step's loads in flight while the current one is computed): K never passes through LDS
-// and no barrier separates the steps, so the waves of a SIMD drift apart and one wave's MFMAs run while another
-// does its softmax work.
+// h = l/16 holds dims 32t + 8h..+8), so each key load instruction reads 64 contiguous bytes of 16 rows.
+// Each wave streams its own 64-key steps of the chunk straight from global memory (the next step's loads in flight
+// while the current one is computed): K never passes through LDS and no barrier separates the steps, so the waves
+// of a SIMD drift apart and one wave's MFMAs run while another does its softmax work.
 constexpr int kStreamRows = 256;
 constexpr int kStreamQB = kStreamRows / 16;  // 16-row query blocks
 
@@ -650,6 +238,9 @@ SE_DEV float row16_reduce_scatter(float (&v)[16]) {
   return v[0];
 }
 
+// PASS 1: row statistics of the chunk; PASS 2: column sums with the merged statistics. PASS 3 (a unit's whole key
+// range in one chunk of at most two steps per wave): both, in one workgroup, with the keys kept in registers and
+// the row statistics merged in LDS.
 template <int PASS, int NW>
 __global__ __launch_bounds__(NW * 64, 2) void window_stream(ScoreArgs a) {
   constexpr int NT = NW * 64;
@@ -660,10 +251,12 @@ __global__ __launch_bounds__(NW * 64, 2) void window_stream(ScoreArgs a) {
   __shared__ int s_lim[kStreamRows];
   __shared__ int s_kp[NW][kSub];
   __shared__ int s_limmin;
+  __shared__ float2 s_st3[PASS == 3 ? NW * kStreamRows : 1];  // fused: per-wave row statistics
+  __shared__ float s_ml3[PASS == 3 ? kStreamRows : 1];        // fused: merged statistic per row
   int k0, k1, n;
   key_range(a, unit, k0, k1, n);
   const int c0 = k0 + chunk * a.kc, c1 = min(c0 + a.kc, k1);
-  if (PASS == 2 && c0 >= c1) return;  // uniform: nothing to score in this chunk
+  if (PASS != 1 && c0 >= c1) return;  // uniform: nothing to score in this chunk
   const int nsub = c1 > c0 ? (c1 - c0 + kSub - 1) / kSub : 0;
   const int rows = min(kStreamRows, a.R * a.wq - rg * kStreamRows);
 
@@ -675,6 +268,7 @@ __global__ __launch_bounds__(NW * 64, 2) void window_stream(ScoreArgs a) {
     kaddr_load(a, b, g, c0, c1, s, ad);
     kstep_fetch(a, g, c0, c1, s, ad, ka);
     kaddr_load(a, b, g, c0, c1, min(s + NW, nsub - 1), ad);
+    if (PASS == 3) kstep_fetch(a, g, c0, c1, min(s + NW, nsub - 1), ad, kb2);
   }
 
   if (threadIdx.x == 0) s_limmin = 0x7fffffff;
@@ -710,7 +304,7 @@ __global__ __launch_bounds__(NW * 64, 2) void window_stream(ScoreArgs a) {
   float st_l[kStreamQB], st_nmc[kStreamQB];
   // pass 2: per query block, the merged statistic of the lane's row (+inf: no such row)
   float ml[kStreamQB];
-  if (PASS == 1) {
+  if (PASS != 2) {
 #pragma unroll
     for (int qb = 0; qb < kStreamQB; ++qb) st_l[qb] = 0.f, st_nmc[qb] = 0.f;
   } else {
@@ -723,7 +317,8 @@ __global__ __launch_bounds__(NW * 64, 2) void window_stream(ScoreArgs a) {
     }
   }
 
-  auto step = [&](const KStep &ks, int sidx) {
+  auto step = [&](const KStep &ks, int sidx, auto pass_tag) {
+    constexpr int P = decltype(pass_tag)::value;
     int pmin = min(min(ks.pos[0], ks.pos[1]), min(ks.pos[2], ks.pos[3]));
     int pmax = max(max(ks.pos[0], ks.pos[1]), max(ks.pos[2], ks.pos[3]));
     const bool fast = __builtin_amdgcn_ballot_w64(!(pmin >= 0 && pmax <= limmin)) == 0;
@@ -744,7 +339,7 @@ __global__ __launch_bounds__(NW * 64, 2) void window_stream(ScoreArgs a) {
         floatx4 acc[4];
         stile(ks, s_q, qb, acc);
         if (!fast) stream_mask(s_kp[wave], s_lim[qb * 16 + (lane & 15)], acc);
-        if constexpr (PASS == 1) {
+        if constexpr (P == 1) {
           float t[16];  // s c - m c against the current reference
 #pragma unroll
           for (int kb = 0; kb < 4; ++kb)
@@ -773,7 +368,7 @@ __global__ __launch_bounds__(NW * 64, 2) void window_stream(ScoreArgs a) {
         }
       }
     }
-    if constexpr (PASS == 2) {
+    if constexpr (P == 2) {
       const float tot = row16_reduce_scatter(col);
       const int j = lane & 15;
       const int key = sidx * kSub + (j >> 2) * 16 + (lane >> 4) * 4 + (j & 3);
@@ -789,16 +384,47 @@ __global__ __launch_bounds__(NW * 64, 2) void window_stream(ScoreArgs a) {
   // of the one after are loaded (the wait for those addresses, a step later, also covers the keys in flight).
   // The loads are unconditional: past the wave's last step they fetch that step again, unused, so that no path
   // through the loop skips a wait (the compiler's wait counts would otherwise hold the MFMAs for the prefetch).
+  using P1 = std::integral_constant<int, 1>;
+  using P2 = std::integral_constant<int, 2>;
+  if constexpr (PASS == 3) {
+    // both passes over the wave's (at most two) steps, which stay in registers
+    if (s < nsub) step(ka, s, P1{});
+    if (s + NW < nsub) step(kb2, s + NW, P1{});
+#pragma unroll
+    for (int qb = 0; qb < kStreamQB; ++qb) {
+      const float mc = st_l[qb] > 0.f ? -st_nmc[qb] : -1e30f;  // this lane's m c (none: no visible key)
+      const float mr = cross_row_max(mc);
+      const float lr = cross_row_sum(st_l[qb] * __builtin_amdgcn_exp2f(mc - mr));
+      if (lane < 16) s_st3[wave * kStreamRows + qb * 16 + lane] = make_float2(mr, lr);
+    }
+    __syncthreads();
+    for (int r = threadIdx.x; r < kStreamRows; r += NT) {
+      float mm = -1e30f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) mm = fmaxf(mm, s_st3[w * kStreamRows + r].x);
+      float ll = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) ll += s_st3[w * kStreamRows + r].y * __builtin_amdgcn_exp2f(s_st3[w * kStreamRows + r].x - mm);
+      // the row's normaliser max + log2(sum); +inf for rows that do not exist or see no key (they score nothing)
+      s_ml3[r] = (r < rows && ll > 0.f) ? mm + __log2f(ll) : INFINITY;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int qb = 0; qb < kStreamQB; ++qb) ml[qb] = s_ml3[qb * 16 + (lane & 15)];
+    if (s < nsub) step(ka, s, P2{});
+    if (s + NW < nsub) step(kb2, s + NW, P2{});
+    return;
+  }
   const int last = nsub - 1;
   while (s < nsub) {
     kstep_fetch(a, g, c0, c1, min(s + NW, last), ad, kb2);
     kaddr_load(a, b, g, c0, c1, min(s + 2 * NW, last), ad);
-    step(ka, s);
+    step(ka, s, std::integral_constant<int, PASS>{});
     s += NW;
     if (s >= nsub) break;
     kstep_fetch(a, g, c0, c1, min(s + NW, last), ad, ka);
     kaddr_load(a, b, g, c0, c1, min(s + 2 * NW, last), ad);
-    step(kb2, s);
+    step(kb2, s, std::integral_constant<int, PASS>{});
     s += NW;
   }
 
@@ -836,11 +462,6 @@ __global__ __launch_bounds__(NW * 64, 2) void window_stream(ScoreArgs a) {
 #endif
 constexpr int kStreamNW = SE_STREAM_NW;
 constexpr int kStreamWGs = SE_STREAM_WGS;  // workgroups a launch aims for (two per CU at NW = 4)
-
-#ifndef SE_SCORE_RPW
-#define SE_SCORE_RPW 32
-#endif
-constexpr int kScoreRPW = SE_SCORE_RPW;
 
 // ---- VALU path (fp32 inputs, or any d that fits) ---------------------------------------------------------------
 template <int DTYPE, int D>
@@ -950,10 +571,8 @@ Plan make_plan(const se_cache_t *c, const se_window_params_t *p) {
   int maxc;
   if (!mfma) {
     pl.nw = 0, pl.rpg = kValuRows, maxc = 1024;
-  } else if (rows <= kStreamRows) {
-    pl.nw = -1, pl.rpg = kStreamRows, maxc = 0;
   } else {
-    pl.nw = 4, pl.rpg = Shape<kScoreRPW, 4>::ROWS, maxc = Shape<kScoreRPW, 4>::MAXC;
+    pl.nw = -1, pl.rpg = kStreamRows, maxc = 0;
   }
   pl.nrg = (rows + pl.rpg - 1) / pl.rpg;
   const int max_slots = c->max_blocks * c->page;
@@ -979,14 +598,6 @@ Plan make_plan(const se_cache_t *c, const se_window_params_t *p) {
   return pl;
 }
 
-template <int NW>
-void launch_mfma(const Plan &pl, const ScoreArgs &a, int units, hipStream_t st) {
-  using S = Shape<kScoreRPW, NW>;
-  const dim3 grid(pl.nkc, pl.nrg, units);
-  hipLaunchKernelGGL((window_mfma<1, kScoreRPW, NW>), grid, dim3(S::NT), 0, st, a);
-  hipLaunchKernelGGL(stats_merge, dim3(pl.nrg, units), dim3(pl.rpg), 0, st, a);
-  hipLaunchKernelGGL((window_mfma<2, kScoreRPW, NW>), grid, dim3(S::NT), 0, st, a);
-}
 
 }  // namespace
 }  // namespace se
@@ -1051,12 +662,12 @@ extern "C" int32_t se_window_score(const se_cache_t *c, const void *q_win, const
   const int units = c->B * c->n_kv;
   const dim3 grid(pl.nkc, pl.nrg, units);
   hipStream_t st = (hipStream_t)stream;
-  if (pl.nw < 0) {
+  if (pl.nw < 0 && pl.nkc == 1 && (pl.key_span + se::kSub - 1) / se::kSub <= 2 * se::kStreamNW) {
+    hipLaunchKernelGGL((se::window_stream<3, se::kStreamNW>), grid, dim3(se::kStreamNW * 64), 0, st, a);
+  } else if (pl.nw < 0) {
     hipLaunchKernelGGL((se::window_stream<1, se::kStreamNW>), grid, dim3(se::kStreamNW * 64), 0, st, a);
     hipLaunchKernelGGL(se::stats_merge, dim3(pl.nrg, units), dim3(pl.rpg), 0, st, a);
     hipLaunchKernelGGL((se::window_stream<2, se::kStreamNW>), grid, dim3(se::kStreamNW * 64), 0, st, a);
-  } else if (pl.nw == 4) {
-    se::launch_mfma<4>(pl, a, units, st);
   } else {
     hipLaunchKernelGGL((se::stats_valu<SE_DTYPE_F32, 64>), grid, dim3(se::kValuRows), 0, st, a);
     hipLaunchKernelGGL((se::colsum_valu<SE_DTYPE_F32, 64>), grid, dim3(se::kValuRows), 0, st, a);
