@@ -36,6 +36,7 @@ struct ScoreArgs {
   float *mlog;     // [units][nrg][256] merged row statistics: max + log2(sum), +inf for empty rows
   int32_t *status;
   int32_t mode, n_kv, R, wq, page, max_blocks, num_blocks, window, protect, score_stride;
+  int32_t page_shift;  // log2(page) when page is a power of two, else -1
   int32_t nrg, nkc, kc, key_span;
   int32_t rpg;  // query rows per row group (workgroup)
   float scale_log2;
@@ -145,6 +146,13 @@ struct KAddr {
 };
 
 // every load is issued unconditionally (indices clamped into the chunk), so none waits behind a branch
+// the page of a slot: a shift when the page size is a power of two (no integer division in the hot loop)
+template <bool POW2>
+SE_DEV int page_of(const ScoreArgs &a, int slot) {
+  return POW2 ? slot >> a.page_shift : slot / a.page;
+}
+
+template <bool POW2>
 SE_DEV void kaddr_load(const ScoreArgs &a, int b, int g, int c0, int c1, int step, KAddr &ad) {
   const int lane = threadIdx.x & 63;
   const int32_t *bt = a.bt + (int64_t)b * a.max_blocks;
@@ -152,12 +160,13 @@ SE_DEV void kaddr_load(const ScoreArgs &a, int b, int g, int c0, int c1, int ste
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
     const int key = min(c0 + step * kSub + kb * 16 + (lane & 15), c1 - 1);
-    ad.page[kb] = key / a.page;
+    ad.page[kb] = page_of<POW2>(a, key);
     ad.blk[kb] = bt[ad.page[kb]];
     ad.pos[kb] = pos[key];
   }
 }
 
+template <bool POW2>
 SE_DEV void kstep_fetch(const ScoreArgs &a, int g, int c0, int c1, int step, const KAddr &ad, KStep &ks) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
@@ -165,7 +174,8 @@ SE_DEV void kstep_fetch(const ScoreArgs &a, int g, int c0, int c1, int step, con
     const int key = c0 + step * kSub + kb * 16 + (lane & 15);
     const bool ok = (key < c1) & (ad.pos[kb] >= 0) & ((unsigned)ad.blk[kb] < (unsigned)a.num_blocks);
     const int keep = -(int)ok;  // all ones or zero: arithmetic instead of a select the compiler may branch on
-    const int row = ((ad.blk[kb] * a.n_kv + g) * a.page + (key - ad.page[kb] * a.page)) & keep;
+    const int off = POW2 ? (key & (a.page - 1)) : key - ad.page[kb] * a.page;
+    const int row = ((ad.blk[kb] * a.n_kv + g) * a.page + off) & keep;
     ks.pos[kb] = (ad.pos[kb] & keep) | ~keep;
     const char *src = a.k + (int64_t)row * 256 + (lane >> 4) * 16;
 #pragma unroll
@@ -241,7 +251,7 @@ SE_DEV float row16_reduce_scatter(float (&v)[16]) {
 // PASS 1: row statistics of the chunk; PASS 2: column sums with the merged statistics. PASS 3 (a unit's whole key
 // range in one chunk of at most two steps per wave): both, in one workgroup, with the keys kept in registers and
 // the row statistics merged in LDS.
-template <int PASS, int NW>
+template <int PASS, int NW, bool POW2>
 __global__ __launch_bounds__(NW * 64, 2) void window_stream(ScoreArgs a) {
   constexpr int NT = NW * 64;
   const int unit = blockIdx.z, rg = blockIdx.y, chunk = blockIdx.x;
@@ -265,10 +275,10 @@ __global__ __launch_bounds__(NW * 64, 2) void window_stream(ScoreArgs a) {
   KAddr ad;
   int s = __builtin_amdgcn_readfirstlane(wave);
   if (s < nsub) {
-    kaddr_load(a, b, g, c0, c1, s, ad);
-    kstep_fetch(a, g, c0, c1, s, ad, ka);
-    kaddr_load(a, b, g, c0, c1, min(s + NW, nsub - 1), ad);
-    if (PASS == 3) kstep_fetch(a, g, c0, c1, min(s + NW, nsub - 1), ad, kb2);
+    kaddr_load<POW2>(a, b, g, c0, c1, s, ad);
+    kstep_fetch<POW2>(a, g, c0, c1, s, ad, ka);
+    kaddr_load<POW2>(a, b, g, c0, c1, min(s + NW, nsub - 1), ad);
+    if (PASS == 3) kstep_fetch<POW2>(a, g, c0, c1, min(s + NW, nsub - 1), ad, kb2);
   }
 
   if (threadIdx.x == 0) s_limmin = 0x7fffffff;
@@ -417,13 +427,13 @@ __global__ __launch_bounds__(NW * 64, 2) void window_stream(ScoreArgs a) {
   }
   const int last = nsub - 1;
   while (s < nsub) {
-    kstep_fetch(a, g, c0, c1, min(s + NW, last), ad, kb2);
-    kaddr_load(a, b, g, c0, c1, min(s + 2 * NW, last), ad);
+    kstep_fetch<POW2>(a, g, c0, c1, min(s + NW, last), ad, kb2);
+    kaddr_load<POW2>(a, b, g, c0, c1, min(s + 2 * NW, last), ad);
     step(ka, s, std::integral_constant<int, PASS>{});
     s += NW;
     if (s >= nsub) break;
-    kstep_fetch(a, g, c0, c1, min(s + NW, last), ad, ka);
-    kaddr_load(a, b, g, c0, c1, min(s + 2 * NW, last), ad);
+    kstep_fetch<POW2>(a, g, c0, c1, min(s + NW, last), ad, ka);
+    kaddr_load<POW2>(a, b, g, c0, c1, min(s + 2 * NW, last), ad);
     step(kb2, s, std::integral_constant<int, PASS>{});
     s += NW;
   }
@@ -558,6 +568,12 @@ __global__ void colsum_reduce(ScoreArgs a) {
   }
 }
 
+template <int PASS>
+void launch_stream(const ScoreArgs &a, dim3 grid, hipStream_t st) {
+  if (a.page_shift >= 0) hipLaunchKernelGGL((window_stream<PASS, kStreamNW, true>), grid, dim3(kStreamNW * 64), 0, st, a);
+  else hipLaunchKernelGGL((window_stream<PASS, kStreamNW, false>), grid, dim3(kStreamNW * 64), 0, st, a);
+}
+
 struct Plan {
   int nrg, nkc, kc, key_span, rpg, nw;  // nw: waves per MFMA workgroup (0: fp32 VALU path, -1: streaming)
   size_t stats_bytes, col_bytes, mlog_bytes;
@@ -579,11 +595,12 @@ Plan make_plan(const se_cache_t *c, const se_window_params_t *p) {
   pl.key_span = p->mode == SE_SCORE_CAUSAL ? max_slots : p->window - p->protect;
   const int span64 = (pl.key_span + 63) / 64 * 64;
   if (pl.nw < 0) {
-    // chunks of whole rounds of 64-key steps (one per wave) that give about kStreamWGs workgroups
+    // chunks of whole rounds of 64-key steps (one per wave) that give about kStreamWGs workgroups; a key range of
+    // at most two steps per wave stays one chunk (the single-kernel path)
     const long long groups = (long long)c->B * c->n_kv * pl.nrg;
     const long long per = (kStreamWGs + groups - 1) / groups;
     const int round = kSub * kStreamNW;
-    long long kc = (pl.key_span + per - 1) / per;
+    long long kc = pl.key_span <= 2 * round ? pl.key_span : (pl.key_span + per - 1) / per;
     kc = (kc + round - 1) / round * round;
     pl.kc = (int)(kc < round ? round : (kc > 16384 ? 16384 : kc));
   } else {
@@ -648,6 +665,7 @@ extern "C" int32_t se_window_score(const se_cache_t *c, const void *q_win, const
   a.R = c->n_q / c->n_kv;
   a.wq = p->n_query;
   a.page = c->page;
+  a.page_shift = (c->page & (c->page - 1)) == 0 ? __builtin_ctz((unsigned)c->page) : -1;
   a.max_blocks = c->max_blocks;
   a.num_blocks = c->num_blocks;
   a.window = p->window;
@@ -663,11 +681,11 @@ extern "C" int32_t se_window_score(const se_cache_t *c, const void *q_win, const
   const dim3 grid(pl.nkc, pl.nrg, units);
   hipStream_t st = (hipStream_t)stream;
   if (pl.nw < 0 && pl.nkc == 1 && (pl.key_span + se::kSub - 1) / se::kSub <= 2 * se::kStreamNW) {
-    hipLaunchKernelGGL((se::window_stream<3, se::kStreamNW>), grid, dim3(se::kStreamNW * 64), 0, st, a);
+    se::launch_stream<3>(a, grid, st);
   } else if (pl.nw < 0) {
-    hipLaunchKernelGGL((se::window_stream<1, se::kStreamNW>), grid, dim3(se::kStreamNW * 64), 0, st, a);
+    se::launch_stream<1>(a, grid, st);
     hipLaunchKernelGGL(se::stats_merge, dim3(pl.nrg, units), dim3(pl.rpg), 0, st, a);
-    hipLaunchKernelGGL((se::window_stream<2, se::kStreamNW>), grid, dim3(se::kStreamNW * 64), 0, st, a);
+    se::launch_stream<2>(a, grid, st);
   } else {
     hipLaunchKernelGGL((se::stats_valu<SE_DTYPE_F32, 64>), grid, dim3(se::kValuRows), 0, st, a);
     hipLaunchKernelGGL((se::colsum_valu<SE_DTYPE_F32, 64>), grid, dim3(se::kValuRows), 0, st, a);

@@ -20,9 +20,10 @@ def banner(name):
     print(f"\n[case] {name}", flush=True)
 
 
-def snap_inputs(B=2, hq=8, hkv=2, d=128, N=1500, wq=64, protect=64, keep=200, dtype="bf16", seed=0, spikes=0.04):
+def snap_inputs(B=2, hq=8, hkv=2, d=128, N=1500, wq=64, protect=64, keep=200, dtype="bf16", seed=0, spikes=0.04,
+                page=16):
     cfg = W.SnapKV("t", B=B, hq=hq, hkv=hkv, d=d, N=N, wq=wq, protect=protect, keep=keep, dtype=dtype,
-                   spike_frac=spikes)
+                   spike_frac=spikes, page=page)
     return W.gen_snapkv(cfg, seed=seed, threads=4)
 
 
@@ -103,10 +104,12 @@ def test_decode_accumulates_cumulative_scores():
 
 
 # ------------------------------------------------------------------ window scores -------------------------------
-@pytest.mark.parametrize("N", [1500, 700])
-def test_window_score_causal_bf16(N):
-    banner(f"window causal bf16 N={N}")
-    inp = snap_inputs(N=N)
+@pytest.mark.parametrize("N,page", [(1500, 16), (700, 16), (1500, 12), (300, 12)])
+def test_window_score_causal_bf16(N, page):
+    """Two-kernel path (1500 and 700 slots) and single-kernel path (a unit's keys in one chunk: 300 slots); page
+    12 takes the addressing without power-of-two shifts."""
+    banner(f"window causal bf16 N={N} page={page}")
+    inp = snap_inputs(N=N, page=page)
     st = punch_holes(inp["cache"], 0.002, 4)
     ref = oracle.window_score_causal(st, inp["q_win"], inp["q_pos"], inp["scale"])
     dc = to_device(st, 8)
