@@ -172,6 +172,31 @@ def calibrate_copy(mib, reps):
     print(json.dumps({"copy_bytes_per_launch": n * 4, "launches": reps}), flush=True)
 
 
+def copy_ceiling(reps):
+    """What a plain streaming kernel reaches at the byte counts of the smaller calls: torch's elementwise negation
+    moving 2 x S bytes (S read, S written) per launch, timed with events over reps back-to-back launches."""
+    import torch
+
+    for mib in (8, 16, 32, 64, 128, 256, 1024):
+        n = mib * 2**20 // 4
+        x = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        y = torch.empty_like(x)
+        for _ in range(3):
+            torch.neg(x, out=y)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            torch.neg(x, out=y)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        moved = 2 * n * 4
+        print(json.dumps({"copy_mib": mib, "bytes_moved": moved, "us": round(us, 2),
+                          "gb_s": round(moved / us / 1e3, 1), "frac_of_8tb": round(moved / us / 8e6, 3)}), flush=True)
+        del x, y
+
+
 # ---------------------------------------------------------------------------------------------------------------
 # workloads: each returns (cfg, steps[list of list of (call name, fn)], tokens per step, algorithmic bytes per call,
 # dominant call, inputs for the CPU baseline)
@@ -357,6 +382,8 @@ def main():
     ap.add_argument("--cpu-seqs", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, metavar="MIB", help="run only a plain copy of MIB MiB, --steps times")
+    ap.add_argument("--copy-ceiling", action="store_true",
+                    help="time plain copies of 8 MiB to 1 GiB (--steps launches each) and exit")
     ap.add_argument("--summarize-profile", metavar="DIR", nargs="+",
                     help="print a summary of rocprofv3 CSV output directories")
     ap.add_argument("--fetch-factor", type=float, default=1.0, help="FETCH_SIZE bytes per byte a plain copy reads")
@@ -379,6 +406,9 @@ def main():
 
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy, args.steps)
+        return
+    if args.copy_ceiling:
+        copy_ceiling(args.steps)
         return
 
     import torch
