@@ -98,7 +98,7 @@ struct ViewMap {
 constexpr float kLazy = 8.f;
 constexpr int kMaxChunkRows = 1024;
 #ifndef SE_DECODE_MIN_WGS
-#define SE_DECODE_MIN_WGS 8192
+#define SE_DECODE_MIN_WGS 512
 #endif
 constexpr int kMinWGs = SE_DECODE_MIN_WGS;
 

@@ -274,10 +274,13 @@ __global__ __launch_bounds__(NW * 64, 2) void window_stream(ScoreArgs a) {
   KStep ka, kb2;
   KAddr ad;
   int s = __builtin_amdgcn_readfirstlane(wave);
+  // Pass 2 walks the chunk's steps last to first: the keys pass 1 read last are the likeliest still to be in the
+  // last-level cache. ph maps a wave's step order to the step it scores.
+  auto ph = [&](int x) { return PASS == 2 ? nsub - 1 - x : x; };
   if (s < nsub) {
-    kaddr_load<POW2>(a, b, g, c0, c1, s, ad);
-    kstep_fetch<POW2>(a, g, c0, c1, s, ad, ka);
-    kaddr_load<POW2>(a, b, g, c0, c1, min(s + NW, nsub - 1), ad);
+    kaddr_load<POW2>(a, b, g, c0, c1, ph(s), ad);
+    kstep_fetch<POW2>(a, g, c0, c1, ph(s), ad, ka);
+    kaddr_load<POW2>(a, b, g, c0, c1, ph(min(s + NW, nsub - 1)), ad);
     if (PASS == 3) kstep_fetch<POW2>(a, g, c0, c1, min(s + NW, nsub - 1), ad, kb2);
   }
 
@@ -427,14 +430,14 @@ __global__ __launch_bounds__(NW * 64, 2) void window_stream(ScoreArgs a) {
   }
   const int last = nsub - 1;
   while (s < nsub) {
-    kstep_fetch<POW2>(a, g, c0, c1, min(s + NW, last), ad, kb2);
-    kaddr_load<POW2>(a, b, g, c0, c1, min(s + 2 * NW, last), ad);
-    step(ka, s, std::integral_constant<int, PASS>{});
+    kstep_fetch<POW2>(a, g, c0, c1, ph(min(s + NW, last)), ad, kb2);
+    kaddr_load<POW2>(a, b, g, c0, c1, ph(min(s + 2 * NW, last)), ad);
+    step(ka, ph(s), std::integral_constant<int, PASS>{});
     s += NW;
     if (s >= nsub) break;
-    kstep_fetch<POW2>(a, g, c0, c1, min(s + NW, last), ad, ka);
-    kaddr_load<POW2>(a, b, g, c0, c1, min(s + 2 * NW, last), ad);
-    step(kb2, s, std::integral_constant<int, PASS>{});
+    kstep_fetch<POW2>(a, g, c0, c1, ph(min(s + NW, last)), ad, ka);
+    kaddr_load<POW2>(a, b, g, c0, c1, ph(min(s + 2 * NW, last)), ad);
+    step(kb2, ph(s), std::integral_constant<int, PASS>{});
     s += NW;
   }
 
