@@ -192,16 +192,21 @@ SE_DEV bf16x8 q_frag(const char *s_q, int qb, int t) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(s_q + r * 256 + ((piece ^ (lane & 15)) << 4)));
 }
 
+// PRIO: the MFMAs are issued at raised wave priority, so that the other wave of the SIMD, in its softmax work, takes
+// the issue slots between them (pass 1, which holds its row statistics in registers, has no room for the change)
+template <bool PRIO = false>
 SE_DEV void stile(const KStep &ks, const char *s_q, int qb, floatx4 (&acc)[4]) {
   bf16x8 qf[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) qf[t] = q_frag(s_q, qb, t);
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) acc[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+  if (PRIO) __builtin_amdgcn_s_setprio(2);
 #pragma unroll
   for (int t = 0; t < 4; ++t)
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) acc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ks.f[kb][t], qf[t], acc[kb], 0, 0, 0);
+  if (PRIO) __builtin_amdgcn_s_setprio(0);
 }
 
 // max of 16 values that are VALU results (never MFMA results: the asm is outside the compiler's hazard checks,
@@ -350,7 +355,7 @@ __global__ __launch_bounds__(NW * 64, 2) void window_stream(ScoreArgs a) {
     for (int qb = 0; qb < kStreamQB; ++qb) {
       if (qb < nqb) {  // uniform
         floatx4 acc[4];
-        stile(ks, s_q, qb, acc);
+        stile<P == 2>(ks, s_q, qb, acc);
         if (!fast) stream_mask(s_kp[wave], s_lim[qb * 16 + (lane & 15)], acc);
         if constexpr (P == 1) {
           float t[16];  // s c - m c against the current reference
