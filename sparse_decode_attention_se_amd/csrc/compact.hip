@@ -10,8 +10,9 @@
 // h = #{j : s_j < w0 + cnt}; those outputs form a prefix, and so do the identity outputs (s_j = w0 + j,
 // nothing to move), [0, i0). The only conflicting pairs are (reader k in [i0, h), writer s_k - w0). Workgroup
 // 0 of each unit moves exactly that set S in ascending tiles (all reads of a tile before its writes); every
-// other output reads a slot >= w0 + cnt, which nobody writes, and writes a slot no reader needs, so the
-// remaining workgroups move them with no ordering at all. Bit-exact, deterministic, one pass over the data.
+// other output reads a slot >= w0 + cnt, which nobody writes, and writes a slot no reader needs, so the other
+// workgroups move them with no ordering at all (a unit with a single tile: workgroup 0, after S). Bit-exact,
+// deterministic, one pass over the data.
 #include "common.hpp"
 
 namespace se {
@@ -32,6 +33,7 @@ struct GatherArgs {
   const int32_t *n_slots, *idx, *count;
   int32_t *status;
   int32_t n_kv, page, max_blocks, num_blocks, row_bytes, window, idx_stride;
+  int32_t fold;  // 1: a unit's outputs fit one tile, which workgroup 0 moves after the hazard set
 };
 
 struct UnitPlan {
@@ -173,10 +175,11 @@ __global__ __launch_bounds__(kMoveThreads) void gather_move(GatherArgs a) {
   const int32_t *pos = a.pos + (int64_t)unit * a.max_blocks * a.page;
   const int lim = u.w0 + u.cnt;
 
-  if (blockIdx.x > 0) {
-    // free-running movers: outputs j >= h whose destination no hazardous reader needs
-    const int j0 = (blockIdx.x - 1) * kMoveRows;
-    if (j0 >= u.cnt) return;
+  // free-running movers: outputs j >= h of tile j0 whose destination no hazardous reader needs. They touch no row
+  // the hazard set does, so they move in any order with it: workgroup x >= 1 moves tile x - 1, or, when a unit has
+  // a single tile, workgroup 0 moves it after the hazard set.
+  auto free_tile = [&](int j0) {
+    if (j0 >= u.cnt) return;  // uniform
     if (threadIdx.x < kMoveRows) {
       const int j = j0 + threadIdx.x;
       int src = -1;
@@ -194,6 +197,9 @@ __global__ __launch_bounds__(kMoveThreads) void gather_move(GatherArgs a) {
     }
     __syncthreads();
     move_tile<false>(a, unit, s_tile, kMoveRows);
+  };
+  if (blockIdx.x > 0) {
+    free_tile((blockIdx.x - 1) * kMoveRows);
     return;
   }
 
@@ -248,6 +254,7 @@ __global__ __launch_bounds__(kMoveThreads) void gather_move(GatherArgs a) {
       move_tile<true>(a, unit, s_tile, kMoveRows);
     }
   }
+  if (a.fold) free_tile(0);  // move_tile<true> ended with a barrier: s_tile is free
 }
 
 struct FinalArgs {
@@ -578,13 +585,13 @@ extern "C" int32_t se_compact_evict(se_cache_t *c, const int32_t *idx, const int
     a.row_bytes = row_bytes;
     a.window = p->window;
     a.idx_stride = p->idx_stride;
-    if (row_bytes <= 256) {
-      const int tiles = 1 + (p->idx_stride + 255) / 256;
-      hipLaunchKernelGGL(se::gather_move<256>, dim3(tiles, units), dim3(se::kMoveThreads), 0, st, a);
-    } else {
-      const int tiles = 1 + (p->idx_stride + 127) / 128;
-      hipLaunchKernelGGL(se::gather_move<128>, dim3(tiles, units), dim3(se::kMoveThreads), 0, st, a);
-    }
+    // workgroup 0 moves the hazard set, workgroup x >= 1 tile x - 1; a unit with one tile takes one workgroup
+    const int tile_rows = row_bytes <= 256 ? 256 : 128;
+    const int nt = (p->idx_stride + tile_rows - 1) / tile_rows;
+    a.fold = nt <= 1;
+    const dim3 grid(a.fold ? 1 : nt + 1, units);
+    if (row_bytes <= 256) hipLaunchKernelGGL(se::gather_move<256>, grid, dim3(se::kMoveThreads), 0, st, a);
+    else hipLaunchKernelGGL(se::gather_move<128>, grid, dim3(se::kMoveThreads), 0, st, a);
     se::FinalArgs f;
     f.bt = c->block_table;
     f.n_slots = c->n_slots;
