@@ -51,7 +51,7 @@ def device_cache(se, cfg, c, dev):
 
 # kernels each call launches (for matching profiler rows to calls) and the sources they are built from
 CALL_KERNELS = {
-    "se_window_score": ["window_stream", "stats_merge", "colsum_reduce", "stats_valu", "colsum_valu"],
+    "se_window_score": ["window_stream", "colsum_reduce", "stats_valu", "colsum_valu"],
     "se_topk_select": ["topk_kernel"],
     "se_token2chunk": ["t2c_kernel"],
     "se_compact_evict": ["gather_move", "gather_extents", "gather_push", "evict_slots_kernel"],

@@ -23,7 +23,6 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 // query rows per workgroup of the fp32 VALU path (one thread per row); the MFMA path picks 128 or 256 per call
 constexpr int kValuRows = 128;
-constexpr int kMaxRowsPerWG = 256;
 
 struct ScoreArgs {
   const char *k;
@@ -33,7 +32,6 @@ struct ScoreArgs {
   float *scores;
   float *stats;    // [units][nrg][nkc][256][2] (max, sum) in the log2 domain
   float *colpart;  // [units][nrg][key_span] when nrg > 1
-  float *mlog;     // [units][nrg][256] merged row statistics: max + log2(sum), +inf for empty rows
   int32_t *status;
   int32_t mode, n_kv, R, wq, page, max_blocks, num_blocks, window, protect, score_stride;
   int32_t page_shift;  // log2(page) when page is a power of two, else -1
@@ -100,11 +98,6 @@ SE_DEV void merge_stats(const ScoreArgs &a, int unit, int rg, float *s_mlog) {
   s_mlog[threadIdx.x] = merge_row(a, unit, rg, threadIdx.x);
 }
 
-// one thread per query row: the merged statistics used by the column-sum pass
-__global__ __launch_bounds__(kMaxRowsPerWG) void stats_merge(ScoreArgs a) {
-  const int unit = blockIdx.y, rg = blockIdx.x;
-  a.mlog[((int64_t)unit * a.nrg + rg) * a.rpg + threadIdx.x] = merge_row(a, unit, rg, threadIdx.x);
-}
 
 constexpr int kSub = 64;  // keys per step of a wave
 
@@ -268,6 +261,7 @@ __global__ __launch_bounds__(NW * 64, 2) void window_stream(ScoreArgs a) {
   __shared__ int s_limmin;
   __shared__ float2 s_st3[PASS == 3 ? NW * kStreamRows : 1];  // fused: per-wave row statistics
   __shared__ float s_ml3[PASS == 3 ? kStreamRows : 1];        // fused: merged statistic per row
+  __shared__ float s_ml2[PASS == 2 ? kStreamRows : 1];        // pass 2: the chunks' statistics merged per row
   int k0, k1, n;
   key_range(a, unit, k0, k1, n);
   const int c0 = k0 + chunk * a.kc, c1 = min(c0 + a.kc, k1);
@@ -310,6 +304,7 @@ __global__ __launch_bounds__(NW * 64, 2) void window_stream(ScoreArgs a) {
     const int lim = row_limit(a, b, rg * kStreamRows + r);
     s_lim[r] = lim;
     if (lim >= 0) atomicMin(&s_limmin, lim);
+    if (PASS == 2) s_ml2[r] = merge_row(a, unit, rg, r);  // max + log2(sum) of every chunk's statistics
   }
   __syncthreads();
   const int limmin = s_limmin;
@@ -326,12 +321,10 @@ __global__ __launch_bounds__(NW * 64, 2) void window_stream(ScoreArgs a) {
 #pragma unroll
     for (int qb = 0; qb < kStreamQB; ++qb) st_l[qb] = 0.f, st_nmc[qb] = 0.f;
   } else {
-    const float *mlog = a.mlog + ((int64_t)unit * a.nrg + rg) * a.rpg;
 #pragma unroll
     for (int qb = 0; qb < kStreamQB; ++qb) {
       const int r = qb * 16 + (lane & 15);
-      const float v = mlog[r];  // a.rpg = kStreamRows entries exist for every row group
-      ml[qb] = r < rows ? v : INFINITY;
+      ml[qb] = r < rows ? s_ml2[r] : INFINITY;
     }
   }
 
@@ -584,7 +577,7 @@ void launch_stream(const ScoreArgs &a, dim3 grid, hipStream_t st) {
 
 struct Plan {
   int nrg, nkc, kc, key_span, rpg, nw;  // nw: waves per MFMA workgroup (0: fp32 VALU path, -1: streaming)
-  size_t stats_bytes, col_bytes, mlog_bytes;
+  size_t stats_bytes, col_bytes;
 };
 
 Plan make_plan(const se_cache_t *c, const se_window_params_t *p) {
@@ -619,7 +612,6 @@ Plan make_plan(const se_cache_t *c, const se_window_params_t *p) {
   const size_t units = (size_t)c->B * c->n_kv;
   pl.stats_bytes = se_host::align_up(units * pl.nrg * pl.nkc * pl.rpg * 2 * sizeof(float));
   pl.col_bytes = pl.nrg > 1 ? se_host::align_up(units * pl.nrg * pl.key_span * sizeof(float)) : 0;
-  pl.mlog_bytes = se_host::align_up(units * pl.nrg * pl.rpg * sizeof(float));
   return pl;
 }
 
@@ -630,7 +622,7 @@ Plan make_plan(const se_cache_t *c, const se_window_params_t *p) {
 extern "C" size_t se_window_score_workspace_size(const se_cache_t *c, const se_window_params_t *p) {
   if (se_host::check_cache(c) != SE_OK || !p) return 0;
   se::Plan pl = se::make_plan(c, p);
-  return pl.stats_bytes + pl.col_bytes + pl.mlog_bytes;
+  return pl.stats_bytes + pl.col_bytes;
 }
 
 extern "C" int32_t se_window_score(const se_cache_t *c, const void *q_win, const int32_t *q_pos,
@@ -655,7 +647,7 @@ extern "C" int32_t se_window_score(const se_cache_t *c, const void *q_win, const
   if (!mfma && !valu) return SE_ERR_DTYPE;
   if ((long long)c->num_blocks * c->n_kv * c->page >= (1ll << 31)) return SE_ERR_UNSUPPORTED;  // 32-bit row ids
   se::Plan pl = se::make_plan(c, p);
-  if (!ws || ws_bytes < pl.stats_bytes + pl.col_bytes + pl.mlog_bytes) return SE_ERR_WORKSPACE;
+  if (!ws || ws_bytes < pl.stats_bytes + pl.col_bytes) return SE_ERR_WORKSPACE;
   se::ScoreArgs a;
   a.k = (const char *)c->k_pool;
   a.bt = c->block_table;
@@ -666,7 +658,6 @@ extern "C" int32_t se_window_score(const se_cache_t *c, const void *q_win, const
   a.scores = scores;
   a.stats = (float *)ws;
   a.colpart = pl.col_bytes ? (float *)((char *)ws + pl.stats_bytes) : nullptr;
-  a.mlog = (float *)((char *)ws + pl.stats_bytes + pl.col_bytes);
   a.status = status;
   a.mode = p->mode;
   a.n_kv = c->n_kv;
@@ -692,7 +683,6 @@ extern "C" int32_t se_window_score(const se_cache_t *c, const void *q_win, const
     se::launch_stream<3>(a, grid, st);
   } else if (pl.nw < 0) {
     se::launch_stream<1>(a, grid, st);
-    hipLaunchKernelGGL(se::stats_merge, dim3(pl.nrg, units), dim3(pl.rpg), 0, st, a);
     se::launch_stream<2>(a, grid, st);
   } else {
     hipLaunchKernelGGL((se::stats_valu<SE_DTYPE_F32, 64>), grid, dim3(se::kValuRows), 0, st, a);
