@@ -153,6 +153,44 @@ def test_window_score_bidir():
     np.testing.assert_allclose(got.sum(axis=2), 2048.0, rtol=1e-5)
 
 
+@pytest.mark.parametrize("wq,N", [(128, 900), (20, 1300)])
+def test_window_score_causal_row_groups(wq, N):
+    """512 query rows per unit (two row groups, whose partial column sums a last kernel adds up) and 80 rows (a row
+    count that is not a multiple of 16)."""
+    banner(f"window causal bf16 wq={wq} N={N}")
+    inp = snap_inputs(N=N, wq=wq)
+    st = punch_holes(inp["cache"], 0.002, 5)
+    ref = oracle.window_score_causal(st, inp["q_win"], inp["q_pos"], inp["scale"])
+    dc = to_device(st, 8)
+    S = st.pos_map.shape[2]
+    scores = torch.zeros((2, 2, S), dtype=torch.float32, device=DEV)
+    se.se_window_score(dc, storage_tensor(inp["q_win"], "bf16"), i32(inp["q_pos"]), scores, scale=inp["scale"],
+                       mode=se.SE_SCORE_CAUSAL, n_query=wq)
+    got = scores.cpu().numpy()
+    assert_scores_close(got[:, :, :N], ref[:, :, :N], mass=np.full((2, 2), 4.0 * wq))
+    np.testing.assert_allclose(got.sum(axis=2), 4.0 * wq, rtol=1e-5)
+
+
+def test_window_score_bidir_long_window():
+    """A 1024-token window (960 region keys): the two-kernel path in bidirectional mode."""
+    banner("window bidir, window 1024")
+    cfg = W.Kara("t", B=2, hq=8, hkv=2, d=128, N=1500, window=1024, protect=64, cand_frac=0.2, budget_frac=0.2,
+                 max_gap=8, period=4, events=1, rho=0.9)
+    inp = W.gen_kara(cfg, seed=4, threads=4)
+    st = inp["cache"]
+    from oracle.pipelines import kara_window_queries
+
+    qw = kara_window_queries(inp, st)
+    ref = oracle.window_score_bidir(st, qw, inp["scale"], 1024, 64)
+    dc = to_device(st, 8)
+    scores = torch.zeros((2, 2, 960), dtype=torch.float32, device=DEV)
+    se.se_window_score(dc, storage_tensor(qw, "bf16"), None, scores, scale=inp["scale"], mode=se.SE_SCORE_BIDIR,
+                       n_query=1024, window=1024, protect=64)
+    got = scores.cpu().numpy()
+    assert_scores_close(got, ref, mass=np.full((2, 2), 4 * 1024.0))
+    np.testing.assert_allclose(got.sum(axis=2), 4096.0, rtol=1e-5)
+
+
 # ------------------------------------------------------------------ top-K -----------------------------------------
 def _topk_cache(B=2, G=3, N=3000, page=16):
     c = W.empty_cache(B, G, 128, page, -(-N // page), B * -(-N // page), "bf16")
