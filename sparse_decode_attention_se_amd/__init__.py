@@ -188,7 +188,7 @@ def se_page_bounds(cache, op, q=None, page_scores=None, *, status=None, stream=N
 
 
 def se_sparse_decode_attn(cache, q, out, *, scale, sel_pages=None, sel_count=None, max_sel=0, max_slots=0,
-                          accumulate=False, status=None, stream=None):
+                          accumulate=False, status=None, stream=None, ws=None):
     lib = _lib.load()
     st, sp = _stream(stream)
     c = cache.desc()
@@ -196,7 +196,10 @@ def se_sparse_decode_attn(cache, q, out, *, scale, sel_pages=None, sel_count=Non
     p = _lib.se_decode_params_t(scale, sel_pages.shape[-1] if has_sel else 0,
                                 (max_sel or sel_pages.shape[-1]) if has_sel else 0, max_slots, int(accumulate))
     nb = lib.se_sparse_decode_attn_workspace_size(C.byref(c), C.byref(p), int(has_sel))
-    ws = _workspace(nb, cache.device, stream)
+    if ws is None:
+        ws = _workspace(nb, cache.device, stream)
+    elif ws.numel() * ws.element_size() < nb:
+        raise ValueError(f"se_sparse_decode_attn: workspace of {ws.numel() * ws.element_size()} bytes, needs {nb}")
     _check("se_sparse_decode_attn", lib.se_sparse_decode_attn(C.byref(c), _ptr(q), _ptr(sel_pages), _ptr(sel_count),
                                                               C.byref(p), _ptr(out), _ptr(status), _ptr(ws), nb,
                                                               sp))

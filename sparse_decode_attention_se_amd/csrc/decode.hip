@@ -8,7 +8,8 @@
 // per-row dot products reduce inside a 16-lane DPP row. Each lane-row keeps an online softmax (max, sum,
 // weighted V) for the R query heads of the group; lane-rows and waves merge at the end and the workgroup
 // writes one (m, l, acc[d]) partial per head. A second kernel merges the chunks and, when asked, turns the
-// stored logits into probabilities and adds them to cum_score.
+// stored logits into probabilities and adds them to cum_score. Accumulating decode over all slots of views that
+// fit in LDS takes a one-launch path instead (decode_unit).
 #include "common.hpp"
 
 namespace se {
@@ -377,8 +378,272 @@ __global__ __launch_bounds__(kThreads) void decode_cum(DecodeArgs a) {
   a.cum[(int64_t)unit * a.max_blocks * a.page + s] += sum;
 }
 
+// Accumulating decode with the unit's logits kept in LDS: one workgroup of kUnitThreads per unit streams the
+// whole view (each wave a contiguous run of 16-row steps), so the merged (max, sum) of every head is known inside
+// the workgroup and the cumulative scores are updated from LDS: no partials, no logits in HBM, one launch. Used
+// when the view is not page-selected and rows_bound * R logits fit kUnitLdsFloats. With one workgroup per CU,
+// each wave keeps twice the split kernel's rows in flight.
+constexpr int kUnitThreads = 512;
+constexpr int kUnitWaves = kUnitThreads / 64;
+constexpr int kUnitLdsFloats = 38912;  // 152 KiB
+constexpr int kUnitMaxRows = 9984;     // and at most this many rows: 20 cumulative scores per thread
+constexpr int U = 4;   // wave-loads per lane-row and step: 16 rows (8 KiB of K and V) per wave
+constexpr int UG = 4;  // rows per lane-row whose scores are live at once
+constexpr int NB = 4;  // K/V buffers: three steps in flight while one is computed
+
+template <int DTYPE, int R>
+__global__ __launch_bounds__(kUnitThreads) void decode_unit(DecodeArgs a) {
+  using V = Vec<DTYPE>;
+  constexpr int EPL = V::EPL;
+  constexpr int D = 16 * EPL;
+  constexpr int RB = 256;
+  constexpr int kMaxRows = kUnitLdsFloats / R < kUnitMaxRows ? kUnitLdsFloats / R : kUnitMaxRows;
+  constexpr int kCum = (kMaxRows + kUnitThreads - 1) / kUnitThreads;
+  constexpr int SR = 4 * U;  // rows per step: 4 lane-rows x U
+  constexpr int SUB = NB * SR;  // rows per sub-chunk (NB steps), resolved one per lane
+  const int unit = blockIdx.x;
+  const int b = unit / a.n_kv, g = unit % a.n_kv;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lrow = lane >> 4, cl = lane & 15;
+  __shared__ float s_lg[kUnitLdsFloats];
+  __shared__ float s_ml[kUnitWaves][R][2];
+  __shared__ float s_acc[R][D];
+
+  u32x4 q[R];
+#pragma unroll
+  for (int h = 0; h < R; ++h) q[h] = ld16(a.q + (((int64_t)b * a.n_kv + g) * R + h) * RB + cl * 16);
+
+  const int cap = a.max_blocks * a.page;
+  int n = a.n_slots[unit];
+  n = n < 0 ? 0 : (n > cap ? cap : n);
+  if (threadIdx.x == 0 && n > a.rows_bound) raise(a.status, SE_DEV_CAPACITY);
+  const int rows = n < a.rows_bound ? n : a.rows_bound;
+  const int nit_all = (rows + SR - 1) / SR;
+  const int it0 = wave * nit_all / kUnitWaves, it1 = (wave + 1) * nit_all / kUnitWaves;
+  const int nst = it1 - it0;  // this wave's steps: rows [wr0, wr1)
+  const int wr0 = it0 * SR, wr1 = it1 * SR < rows ? it1 * SR : rows;
+  const int32_t *bt = a.bt + (int64_t)b * a.max_blocks;
+  const int32_t *pos = a.pos + (int64_t)unit * cap;
+  float *cum = a.cum + (int64_t)unit * cap;
+
+  // Rows are resolved SUB at a time, lane i holding row wr0 + SUB k + i of sub-chunk k (pool row, or -1 when not
+  // resident); a step takes its rows from that register with ds_bpermute. The block-table and position loads of
+  // sub-chunk k + 2 go out while sub-chunk k streams (clamped addresses, no branch).
+  bool bad = false;
+  auto res_issue = [&](int k, int &blk, int &ps) {
+    const int r = wr0 + SUB * k + lane;
+    const int rr = lane < SUB && r < wr1 ? r : 0;
+    blk = bt[rr / a.page];
+    ps = pos[rr];
+  };
+  auto res_make = [&](int k, int blk, int ps) {
+    const int r = wr0 + SUB * k + lane;
+    int v = -1;
+    if (lane < SUB && r < wr1 && ps >= 0) {
+      if (blk_ok(blk, a.num_blocks)) v = (blk * a.n_kv + g) * a.page + r % a.page;
+      else bad = true;
+    }
+    return v;
+  };
+  auto rows_from = [&](int vs, int half, int (&rv)[U]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) rv[u] = __builtin_amdgcn_ds_bpermute((half * SR + u * 4 + lrow) * 4, vs);
+  };
+  auto load = [&](const int (&rv)[U], u32x4 (&kb)[U], u32x4 (&vb)[U]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t off = (int64_t)(rv[u] >= 0 ? rv[u] : 0) * RB + cl * 16;
+      kb[u] = ld16(a.k + off);
+      vb[u] = ld16(a.v + off);
+    }
+  };
+
+  float m[R], l[R], acc[R][EPL];
+#pragma unroll
+  for (int h = 0; h < R; ++h) {
+    m[h] = -1e30f;
+    l[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
+  }
+  // one step in groups of UG rows per lane-row (fewer live scores)
+  auto step = [&](int rbase, const u32x4 (&kb)[U], const u32x4 (&vb)[U], const int (&rv)[U]) {
+#pragma unroll
+    for (int hf = 0; hf < U / UG; ++hf) {
+      float sc[UG][R];
+#pragma unroll
+      for (int uu = 0; uu < UG; ++uu) {
+        const int u = hf * UG + uu;
+#pragma unroll
+        for (int h = 0; h < R; ++h) {
+          const float d = row16_sum(V::dot(q[h], kb[u], 0.f));
+          sc[uu][h] = rv[u] >= 0 ? d * a.scale_log2 : -INFINITY;
+        }
+        const int r = rbase + u * 4 + lrow;
+        if (cl == 0 && r < rows) {
+#pragma unroll
+          for (int h = 0; h < R; ++h) s_lg[r * R + h] = sc[uu][h];
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < R; ++h) {
+        float mx = sc[0][h];
+#pragma unroll
+        for (int uu = 1; uu < UG; ++uu) mx = fmaxf(mx, sc[uu][h]);
+        if (mx > m[h] + kLazy) {
+          const float f = __builtin_amdgcn_exp2f(m[h] - mx);
+          m[h] = mx;
+          l[h] *= f;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[h][e] *= f;
+        }
+      }
+#pragma unroll
+      for (int uu = 0; uu < UG; ++uu) {
+        const int u = hf * UG + uu;
+        const bool ok = rv[u] >= 0;
+        const u32x4 w = {ok ? vb[u].x : 0u, ok ? vb[u].y : 0u, ok ? vb[u].z : 0u, ok ? vb[u].w : 0u};
+        float x[EPL];
+        V::widen(w, x);
+#pragma unroll
+        for (int h = 0; h < R; ++h) {
+          const float p = __builtin_amdgcn_exp2f(sc[uu][h] - m[h]);
+          l[h] += p;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(p, x[e], acc[h][e]);
+        }
+      }
+    }
+  };
+
+  // steps 4k .. 4k+3 form sub-chunk k and use buffers 0 .. 3; the K/V loads of the next three steps are in
+  // flight while a step is computed
+  static_assert(NB == 4, "the loop below is written for four buffers");
+  int r0[U], r1[U], r2[U], r3[U], vcur = -1, rbk = 0, rpk = 0, rbn = 0, rpn = 0;
+  u32x4 k0[U], v0[U], k1[U], v1[U], k2[U], v2[U], k3[U], v3[U];
+  if (nst > 0) {
+    res_issue(0, rbk, rpk);
+    res_issue(1, rbn, rpn);
+    vcur = res_make(0, rbk, rpk);
+    rows_from(vcur, 0, r0);
+    load(r0, k0, v0);
+    if (nst > 1) {
+      rows_from(vcur, 1, r1);
+      load(r1, k1, v1);
+    }
+    if (nst > 2) {
+      rows_from(vcur, 2, r2);
+      load(r2, k2, v2);
+    }
+  }
+  for (int k = 0; NB * k < nst; ++k) {
+    const int j = NB * k;
+    res_issue(k + 2, rbk, rpk);
+    if (j + 3 < nst) {
+      rows_from(vcur, 3, r3);
+      load(r3, k3, v3);
+    }
+    step(wr0 + j * SR, k0, v0, r0);
+    if (j + 1 >= nst) break;
+    const int vnext = res_make(k + 1, rbn, rpn);
+    if (j + 4 < nst) {
+      rows_from(vnext, 0, r0);
+      load(r0, k0, v0);
+    }
+    step(wr0 + (j + 1) * SR, k1, v1, r1);
+    if (j + 2 >= nst) break;
+    if (j + 5 < nst) {
+      rows_from(vnext, 1, r1);
+      load(r1, k1, v1);
+    }
+    step(wr0 + (j + 2) * SR, k2, v2, r2);
+    if (j + 3 >= nst) break;
+    if (j + 6 < nst) {
+      rows_from(vnext, 2, r2);
+      load(r2, k2, v2);
+    }
+    step(wr0 + (j + 3) * SR, k3, v3, r3);
+    vcur = vnext;
+    rbn = rbk;
+    rpn = rpk;
+  }
+  if (bad) raise(a.status, SE_DEV_INDEX);
+
+  // this thread's cumulative scores, loaded while the waves merge
+  float cv[kCum];
+#pragma unroll
+  for (int k = 0; k < kCum; ++k) {
+    const int r = k * kUnitThreads + threadIdx.x;
+    cv[k] = cum[r < rows ? r : 0];
+  }
+
+  // merge the four lane-rows of each wave, then the waves: max and sum first, then acc one wave at a time
+#pragma unroll
+  for (int off = 16; off <= 32; off <<= 1) {
+#pragma unroll
+    for (int h = 0; h < R; ++h) {
+      float mo = __shfl_xor(m[h], off), lo = __shfl_xor(l[h], off);
+      float mn = fmaxf(m[h], mo);
+      float fa = __builtin_amdgcn_exp2f(m[h] - mn), fb = __builtin_amdgcn_exp2f(mo - mn);
+      l[h] = l[h] * fa + lo * fb;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[h][e] = acc[h][e] * fa + __shfl_xor(acc[h][e], off) * fb;
+      m[h] = mn;
+    }
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int h = 0; h < R; ++h) {
+      s_ml[wave][h][0] = m[h];
+      s_ml[wave][h][1] = l[h];
+    }
+  }
+  __syncthreads();
+  float M[R], iL[R];
+#pragma unroll
+  for (int h = 0; h < R; ++h) {
+    float mm = s_ml[0][h][0];
+#pragma unroll
+    for (int w = 1; w < kUnitWaves; ++w) mm = fmaxf(mm, s_ml[w][h][0]);
+    float ll = 0.f;
+#pragma unroll
+    for (int w = 0; w < kUnitWaves; ++w) ll += s_ml[w][h][1] * __builtin_amdgcn_exp2f(s_ml[w][h][0] - mm);
+    M[h] = mm;
+    iL[h] = ll > 0.f ? 1.f / ll : 0.f;
+  }
+  for (int w = 0; w < kUnitWaves; ++w) {
+    if (wave == w && lane < 16) {
+#pragma unroll
+      for (int h = 0; h < R; ++h) {
+        const float f = __builtin_amdgcn_exp2f(m[h] - M[h]);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          float &dst = s_acc[h][cl * EPL + e];
+          dst = (w == 0 ? 0.f : dst) + acc[h][e] * f;
+        }
+      }
+    }
+    __syncthreads();
+  }
+  float *out = a.out + (((int64_t)b * a.n_kv + g) * R) * D;
+  for (int i = threadIdx.x; i < R * D; i += kUnitThreads) out[i] = s_acc[i / D][i % D] * iL[i / D];
+
+  // cum[slot] += the group's summed weight on the slot; free slots (logit -inf) keep their value
+#pragma unroll
+  for (int k = 0; k < kCum; ++k) {
+    const int r = k * kUnitThreads + threadIdx.x;
+    if (r >= rows) break;
+    if (s_lg[r * R] == -INFINITY) continue;
+    float sum = 0.f;
+#pragma unroll
+    for (int h = 0; h < R; ++h) sum += __builtin_amdgcn_exp2f(s_lg[r * R + h] - M[h]) * iL[h];
+    cum[r] = cv[k] + sum;
+  }
+}
+
 struct Plan {
   int rows_bound, chunk_rows, nchunk, units;
+  bool unit_path;  // decode_unit: accumulate over all slots, logits fit in LDS
   size_t part_bytes, logit_bytes;
 };
 
@@ -402,11 +667,18 @@ Plan make_plan(const se_cache_t *c, const se_decode_params_t *p, int has_sel) {
   pl.logit_bytes = p->accumulate ? se_host::align_up((size_t)pl.units * pl.rows_bound * R * sizeof(float)) +
                                        se_host::align_up((size_t)pl.units * R * 2 * sizeof(float))
                                  : 0;
+  pl.unit_path = p->accumulate && !has_sel && (long long)pl.rows_bound * R <= kUnitLdsFloats &&
+                 pl.rows_bound <= kUnitMaxRows;
+  if (pl.unit_path) pl.part_bytes = pl.logit_bytes = 0;
   return pl;
 }
 
 template <int DTYPE, int R>
-void launch(const DecodeArgs &a, int units, int nchunk, hipStream_t st) {
+void launch(const DecodeArgs &a, int units, int nchunk, bool unit_path, hipStream_t st) {
+  if (unit_path) {
+    hipLaunchKernelGGL((decode_unit<DTYPE, R>), dim3(units), dim3(kUnitThreads), 0, st, a);
+    return;
+  }
   hipLaunchKernelGGL((decode_partial<DTYPE, R>), dim3(nchunk, units), dim3(kThreads), 0, st, a);
   hipLaunchKernelGGL((decode_merge<DTYPE, R>), dim3(units * R), dim3(128), 0, st, a);
   if (a.cum)
@@ -415,12 +687,12 @@ void launch(const DecodeArgs &a, int units, int nchunk, hipStream_t st) {
 }
 
 template <int DTYPE>
-int32_t dispatch_r(int R, const DecodeArgs &a, int units, int nchunk, hipStream_t st) {
+int32_t dispatch_r(int R, const DecodeArgs &a, int units, int nchunk, bool unit_path, hipStream_t st) {
   switch (R) {
-    case 1: launch<DTYPE, 1>(a, units, nchunk, st); break;
-    case 2: launch<DTYPE, 2>(a, units, nchunk, st); break;
-    case 4: launch<DTYPE, 4>(a, units, nchunk, st); break;
-    case 8: launch<DTYPE, 8>(a, units, nchunk, st); break;
+    case 1: launch<DTYPE, 1>(a, units, nchunk, unit_path, st); break;
+    case 2: launch<DTYPE, 2>(a, units, nchunk, unit_path, st); break;
+    case 4: launch<DTYPE, 4>(a, units, nchunk, unit_path, st); break;
+    case 8: launch<DTYPE, 8>(a, units, nchunk, unit_path, st); break;
     default: return SE_ERR_UNSUPPORTED;
   }
   return se_host::launch_status();
@@ -452,7 +724,8 @@ extern "C" int32_t se_sparse_decode_attn(se_cache_t *c, const void *q, const int
   se::Plan pl = se::make_plan(c, p, has_sel);
   if (pl.nchunk > se::kMaxChunks) return SE_ERR_UNSUPPORTED;  // views beyond 4M slots per (sequence, head)
   if ((long long)c->num_blocks * c->n_kv * c->page >= (1ll << 31)) return SE_ERR_UNSUPPORTED;
-  if (ws_bytes < pl.part_bytes + pl.logit_bytes || !ws) return SE_ERR_WORKSPACE;
+  if (pl.part_bytes + pl.logit_bytes > 0 && (ws_bytes < pl.part_bytes + pl.logit_bytes || !ws))
+    return SE_ERR_WORKSPACE;
   se::DecodeArgs a;
   a.k = (const char *)c->k_pool;
   a.v = (const char *)c->v_pool;
@@ -481,6 +754,6 @@ extern "C" int32_t se_sparse_decode_attn(se_cache_t *c, const void *q, const int
   a.scale_log2 = p->scale * 1.4426950408889634f;
   const int R = c->n_q / c->n_kv;
   hipStream_t st = (hipStream_t)stream;
-  if (c->dtype == SE_DTYPE_BF16) return se::dispatch_r<SE_DTYPE_BF16>(R, a, pl.units, pl.nchunk, st);
-  return se::dispatch_r<SE_DTYPE_F32>(R, a, pl.units, pl.nchunk, st);
+  if (c->dtype == SE_DTYPE_BF16) return se::dispatch_r<SE_DTYPE_BF16>(R, a, pl.units, pl.nchunk, pl.unit_path, st);
+  return se::dispatch_r<SE_DTYPE_F32>(R, a, pl.units, pl.nchunk, pl.unit_path, st);
 }

@@ -37,10 +37,11 @@ def punch_holes(state, frac, seed, slot_cap=8):
 
 
 # ------------------------------------------------------------------ decode --------------------------------------
-@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64)])
-def test_decode_all_slots(dtype, d):
-    banner(f"decode all slots {dtype}")
-    inp = snap_inputs(d=d, dtype=dtype, N=777)
+@pytest.mark.parametrize("dtype,d,N", [("bf16", 128, 777), ("f32", 64, 777), ("bf16", 128, 40), ("f32", 64, 40)])
+def test_decode_all_slots(dtype, d, N):
+    # N = 40: the whole view is one chunk, whose workgroup writes the output without partials
+    banner(f"decode all slots {dtype} N={N}")
+    inp = snap_inputs(d=d, dtype=dtype, N=N, wq=8, protect=8, keep=16)
     st = punch_holes(inp["cache"], 0.01, 1)
     ref, _ = oracle.decode_attn(st, inp["q_dec"], inp["scale"])
     dc = to_device(st, 8)
@@ -82,25 +83,55 @@ def test_decode_max_slots_bound_and_pages():
     assert se.se_status_read(status) & se.SE_DEV_CAPACITY
 
 
-def test_decode_accumulates_cumulative_scores():
-    banner("decode cum")
-    cfg = W.H2O("t", B=3, hq=8, hkv=2, d=128, N=900, budget=900, recent=32, steps=2, zipf=1.1)
+@pytest.mark.parametrize("B,N", [(3, 900), (3, 40), (1, 12000)])
+def test_decode_accumulates_cumulative_scores(B, N):
+    banner(f"decode cum B={B} N={N}")
+    cfg = W.H2O("t", B=B, hq=8, hkv=2, d=128, N=N, budget=N, recent=min(32, N // 2), steps=2, zipf=1.1)
     inp = W.gen_h2o(cfg, seed=5, threads=4)
     st = punch_holes(inp["cache"], 0.005, 2)
     st.cum_score[:] = np.random.default_rng(0).random(st.cum_score.shape).astype(np.float32)
     ref_out, ref_cum = oracle.decode_attn(st, inp["q_steps"][0], inp["scale"], accumulate=True)
     dc = to_device(st, 8)
-    out = torch.empty((3, 8, 128), dtype=torch.float32, device=DEV)
+    out = torch.empty((B, 8, 128), dtype=torch.float32, device=DEV)
     se.se_sparse_decode_attn(dc, storage_tensor(inp["q_steps"][0], "bf16"), out, scale=inp["scale"],
                              accumulate=True)
     np.testing.assert_allclose(out.cpu().numpy(), ref_out, atol=2e-3, rtol=0)
     cum = dc.cum_score.cpu().numpy()
-    for b in range(3):
+    for b in range(B):
         for g in range(2):
             n = int(st.n_slots[b, g])
             res = st.pos_map[b, g, :n] >= 0
             np.testing.assert_allclose(cum[b, g, :n][res], ref_cum[b, g, :n][res], rtol=1e-5, atol=1e-7)
             np.testing.assert_array_equal(cum[b, g, :n][~res], st.cum_score[b, g, :n][~res])
+
+
+def test_decode_workspace_needs_no_clearing():
+    """The merge's arrival counters live in the workspace: garbage there, reuse across calls of other shapes and
+    repeated calls all give the same outputs."""
+    banner("decode workspace reuse")
+    inp = snap_inputs(N=1000)
+    st = inp["cache"]
+    dc = to_device(st, 8)
+    q = storage_tensor(inp["q_dec"], "bf16")
+    ref, _ = oracle.decode_attn(st, inp["q_dec"], inp["scale"])
+    ws = torch.full((1 << 22,), 0xFF, dtype=torch.uint8, device=DEV)
+    outs = []
+    for _ in range(3):
+        out = torch.empty((2, 8, 128), dtype=torch.float32, device=DEV)
+        se.se_sparse_decode_attn(dc, q, out, scale=inp["scale"], ws=ws)
+        outs.append(out.cpu().numpy())
+    np.testing.assert_allclose(outs[0], ref, atol=2e-3, rtol=0)
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+    # a page-selected call of another size on the same workspace, then the dense one again
+    n_pages = -(-1000 // 16)
+    pages = [[np.arange(0, n_pages, 3, dtype=np.int32)] * 2] * 2
+    sel, cnt = W.pack_lists(pages, n_pages)
+    out = torch.empty((2, 8, 128), dtype=torch.float32, device=DEV)
+    se.se_sparse_decode_attn(dc, q, out, scale=inp["scale"], sel_pages=i32(sel), sel_count=i32(cnt), ws=ws)
+    ref_sel, _ = oracle.decode_attn(st, inp["q_dec"], inp["scale"], pages=pages)
+    np.testing.assert_allclose(out.cpu().numpy(), ref_sel, atol=2e-3, rtol=0)
+    se.se_sparse_decode_attn(dc, q, out, scale=inp["scale"], ws=ws)
+    assert np.array_equal(out.cpu().numpy(), outs[0])
 
 
 # ------------------------------------------------------------------ window scores -------------------------------
