@@ -74,8 +74,12 @@ def test_workspace_sizes_are_host_only():
     c = _lib.se_cache_t()
     c.k_pool = c.v_pool = c.block_table = c.pos_map = c.ctx_len = c.n_slots = 16
     c.B, c.n_kv, c.n_q, c.d, c.page, c.num_blocks, c.max_blocks, c.dtype = 8, 8, 32, 128, 16, 16384, 2048, 1
-    p = _lib.se_decode_params_t(0.1, 0, 0, 2048, 1)
+    p = _lib.se_decode_params_t(0.1, 0, 0, 2048, 0)  # split-K partials
     assert lib.se_sparse_decode_attn_workspace_size(C.byref(c), C.byref(p), 0) > 0
+    p = _lib.se_decode_params_t(0.1, 0, 0, 2048, 1)  # accumulating, logits fit in LDS: no workspace
+    assert lib.se_sparse_decode_attn_workspace_size(C.byref(c), C.byref(p), 0) == 0
+    p = _lib.se_decode_params_t(0.1, 0, 0, 0, 1)  # accumulating over 32768 slots: partials and logits
+    assert lib.se_sparse_decode_attn_workspace_size(C.byref(c), C.byref(p), 0) > 8 * 8 * 32768 * 4 * 4
     wp = _lib.se_window_params_t(0.1, 0, 64, 0, 0, 32768)
     assert lib.se_window_score_workspace_size(C.byref(c), C.byref(wp)) > 0
     cp = _lib.se_compact_params_t(0, 0, 2048)
