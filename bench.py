@@ -57,7 +57,7 @@ CALL_KERNELS = {
     "se_compact_evict": ["gather_move", "gather_extents", "gather_push", "evict_slots_kernel"],
     "se_cache_append": ["append_kernel"],
     "se_page_bounds": ["pages_score", "pages_build"],
-    "se_sparse_decode_attn": ["decode_partial", "decode_merge", "decode_cum"],
+    "se_sparse_decode_attn": ["decode_partial", "decode_merge", "decode_cum", "decode_unit"],
 }
 CALL_SOURCES = {
     "se_window_score": "score.hip", "se_topk_select": "topk.hip", "se_token2chunk": "t2c.hip",

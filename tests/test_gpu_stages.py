@@ -52,6 +52,20 @@ def test_decode_all_slots(dtype, d, N):
     np.testing.assert_allclose(out.cpu().numpy(), ref, atol=2e-3, rtol=0)
 
 
+def test_decode_many_units_256_row_chunks():
+    # 64 units of 2100 slots: 256-row chunks (all four steps of a wave in flight), ragged last chunk
+    banner("decode 64 units x 2100 slots")
+    inp = snap_inputs(B=8, hq=32, hkv=8, N=2100, wq=8, protect=8, keep=16, seed=4)
+    st = punch_holes(inp["cache"], 0.01, 5)
+    ref, _ = oracle.decode_attn(st, inp["q_dec"], inp["scale"])
+    dc = to_device(st, 32)
+    out = torch.empty((8, 32, 128), dtype=torch.float32, device=DEV)
+    status = status_word()
+    se.se_sparse_decode_attn(dc, storage_tensor(inp["q_dec"], "bf16"), out, scale=inp["scale"], status=status)
+    assert se.se_status_read(status) == 0
+    np.testing.assert_allclose(out.cpu().numpy(), ref, atol=2e-3, rtol=0)
+
+
 def test_decode_max_slots_bound_and_pages():
     banner("decode page lists")
     inp = snap_inputs(N=1000)
