@@ -28,11 +28,12 @@ unpinned".
 """
 from .cache_ops import cache_append, compact_gather, evict_slots
 from .decode import decode_attn
-from .pages import page_bounds_build, page_bounds_score
+from .pages import page_bounds_build, page_bounds_refresh, page_bounds_score
 from .score import window_score_bidir, window_score_causal
 from .select import token2chunk, topk_largest, topk_smallest
 
 __all__ = [
     "window_score_causal", "window_score_bidir", "topk_largest", "topk_smallest", "token2chunk",
-    "compact_gather", "evict_slots", "cache_append", "page_bounds_build", "page_bounds_score", "decode_attn",
+    "compact_gather", "evict_slots", "cache_append", "page_bounds_build", "page_bounds_refresh", "page_bounds_score",
+    "decode_attn",
 ]

@@ -65,3 +65,32 @@ def page_bounds_score(cache, meta, q: np.ndarray):
             best[empty] = -np.inf
             out[b, g, :n_pages] = best
     return out
+
+
+def page_bounds_refresh(cache, meta, mode: str, page_lo=None, max_pages=None):
+    """Quest metadata maintenance (SparseEngine page, "How it works": method metadata is kept beside the KV and
+    follows the cache manager's writes and evictions): the metadata of the chosen pages becomes what
+    ``page_bounds_build`` gives for the cache as it is now; every other page keeps its value from ``meta``.
+
+    mode "last": page ceil(n_slots / page) - 1 of each (b, g), the page a high-water append writes (none when
+    n_slots = 0). mode "from": pages [page_lo[b][g], ceil(n_slots / page)) (page_lo None = 0), at most
+    ``max_pages`` of them.
+    """
+    full = page_bounds_build(cache)
+    out = meta.copy()
+    B, n_kv = cache.n_slots.shape
+    for b in range(B):
+        for g in range(n_kv):
+            n_pages = -(-int(cache.n_slots[b, g]) // cache.page)
+            if mode == "last":
+                lo, hi = n_pages - 1, n_pages
+            elif mode == "from":
+                lo, hi = (0 if page_lo is None else int(page_lo[b][g])), n_pages
+                if max_pages is not None:
+                    hi = min(hi, lo + max_pages)
+            else:
+                raise ValueError(mode)
+            lo = max(lo, 0)
+            if lo < hi:
+                out[b, g, lo:hi] = full[b, g, lo:hi]
+    return out

@@ -312,6 +312,47 @@ def test_page_bound_is_an_upper_bound_and_tight_for_equal_keys():
     assert abs(u2[0, 0, 1] - exact) < 1e-9
 
 
+@pytest.mark.parametrize("N", [32, 37])
+def test_refresh_last_page_after_append_equals_rebuild(N):
+    # N = 32: the append opens a new page (a spare block is popped); N = 37: it lands in the partly filled last page
+    cfg = W.H2O("tiny", B=2, hq=4, hkv=2, d=8, N=N, budget=N, recent=4, steps=2, zipf=1.1, dtype="f32")
+    inp = W.gen_h2o(cfg, seed=2, threads=1)
+    c0 = inp["cache"]
+    meta0 = oracle.page_bounds_build(c0)
+    c1, slots = oracle.cache_append(c0, inp["k_new"][0], inp["v_new"][0], np.full((2,), N, np.int32))
+    assert (slots == N).all()
+    got = oracle.page_bounds_refresh(c1, meta0, "last")
+    want = oracle.page_bounds_build(c1)
+    np.testing.assert_array_equal(got, want)
+    assert not np.array_equal(meta0, want)  # the append did change the metadata
+    # an empty range changes nothing
+    n_pages = -(-(N + 1) // 16)
+    same = oracle.page_bounds_refresh(c1, meta0, "from", page_lo=np.full((2, 2), n_pages))
+    np.testing.assert_array_equal(same, meta0)
+
+
+@pytest.mark.parametrize("window", [0, 27])
+def test_refresh_from_page_after_compaction_equals_rebuild(window):
+    # window 27 of 61 slots (page 4): w0 = 34 is not page-aligned, so page 8 holds both untouched and moved slots
+    inp = tiny_snapkv(B=2, hq=4, hkv=2, d=8, N=61, dtype="f32")
+    c = inp["cache"]
+    page = c.page
+    meta = oracle.page_bounds_build(c)
+    rs = np.random.default_rng(4)
+    w0 = 61 - window if window else 0
+    keep = [[np.sort(rs.choice(np.arange(w0, 61), size=12, replace=False)).astype(np.int32) for g in range(2)]
+            for b in range(2)]
+    c2 = oracle.compact_gather(c, keep, window=window)
+    lo = np.full((2, 2), w0 // page)
+    got = oracle.page_bounds_refresh(c2, meta, "from", page_lo=lo)
+    want = oracle.page_bounds_build(c2)
+    for b in range(2):
+        for g in range(2):
+            n_pages = -(-int(c2.n_slots[b, g]) // page)
+            np.testing.assert_array_equal(got[b, g, :n_pages], want[b, g, :n_pages])
+            np.testing.assert_array_equal(got[b, g, n_pages:], meta[b, g, n_pages:])
+
+
 # ------------------------------------------------------------------ decode -------------------------------------------
 def test_decode_matches_library_attention():
     inp = tiny_snapkv(B=2, hq=4, hkv=2, d=8, N=40)
