@@ -197,6 +197,22 @@ enum { SE_PAGES_BUILD = 0, SE_PAGES_SCORE = 1 };
 int32_t se_page_bounds(se_cache_t *c, int32_t op, const void *q, float *page_scores, int32_t score_stride,
                        int32_t *status, void *ws, size_t ws_bytes, se_stream_t stream);
 
+/* ---- Quest metadata maintenance -------------------------------------------------------------------------------
+ * The metadata Quest keeps beside the KV (SparseEngine page, "How it works") must follow the cache: an append
+ * changes the page it writes, a compaction rewrites the kept prefix. This call writes, for the chosen logical
+ * pages of every unit u = b*n_kv + g, exactly what BUILD writes for them (min / max over the page's resident
+ * keys, +inf / -inf without any), from the cache as it is now. Other pages are not touched. Needs page_meta.
+ *  LAST_PAGE: page ceil(n_slots/page) - 1 of each unit (the page a high-water append wrote; none if n_slots = 0).
+ *    page_lo and max_pages are ignored.
+ *  FROM_PAGE: pages [page_lo[u], ceil(n_slots/page)) (page_lo: device [B][n_kv]; NULL = page 0 for every unit),
+ *    at most max_pages (>= 1) of them per unit: a longer range raises SE_DEV_CAPACITY and only its first
+ *    max_pages pages are written; page_lo[u] outside [0, max_blocks] raises SE_DEV_INDEX and skips the unit.
+ * A slot reused from the slot stack (H2O) can lie in any page: refresh from that page, or BUILD. No workspace.
+ */
+enum { SE_REFRESH_LAST_PAGE = 0, SE_REFRESH_FROM_PAGE = 1 };
+int32_t se_page_bounds_refresh(se_cache_t *c, int32_t mode, const int32_t *page_lo, int32_t max_pages,
+                               int32_t *status, void *ws, size_t ws_bytes, se_stream_t stream);
+
 /* ---- decode attention over the view ---------------------------------------------------------------------------
  * o = Attention(q, View), View = BuildView(C, I) (SparseEngine page, "How it works"). For each query head h of
  * KV head g: out[b][h][e] = sum over slots s in View(b, g) of softmax_s(scale * q[b][h] . k_s) v_s[e], fp32

@@ -11,15 +11,15 @@ import torch
 
 from . import _lib
 from ._lib import (SE_COMPACT_EVICT_SLOTS, SE_COMPACT_GATHER, SE_DEV_CAPACITY, SE_DEV_INDEX, SE_DTYPE_BF16,
-                   SE_DTYPE_F32, SE_PAGES_BUILD, SE_PAGES_SCORE, SE_SCORE_BIDIR, SE_SCORE_CAUSAL, SE_TOPK_LARGEST,
-                   SE_TOPK_SMALLEST, SE_UNIT_PAGE, SE_UNIT_SLOT)
+                   SE_DTYPE_F32, SE_PAGES_BUILD, SE_PAGES_SCORE, SE_REFRESH_FROM_PAGE, SE_REFRESH_LAST_PAGE,
+                   SE_SCORE_BIDIR, SE_SCORE_CAUSAL, SE_TOPK_LARGEST, SE_TOPK_SMALLEST, SE_UNIT_PAGE, SE_UNIT_SLOT)
 
 __all__ = [
     "DeviceCache", "SEError", "se_window_score", "se_topk_select", "se_token2chunk", "se_compact_evict",
-    "se_cache_append", "se_page_bounds", "se_sparse_decode_attn", "se_status_read", "se_version",
-    "SE_SCORE_CAUSAL", "SE_SCORE_BIDIR", "SE_TOPK_LARGEST", "SE_TOPK_SMALLEST", "SE_UNIT_SLOT", "SE_UNIT_PAGE",
-    "SE_COMPACT_GATHER", "SE_COMPACT_EVICT_SLOTS", "SE_PAGES_BUILD", "SE_PAGES_SCORE", "SE_DEV_INDEX",
-    "SE_DEV_CAPACITY",
+    "se_cache_append", "se_page_bounds", "se_page_bounds_refresh", "se_sparse_decode_attn", "se_status_read",
+    "se_version", "SE_SCORE_CAUSAL", "SE_SCORE_BIDIR", "SE_TOPK_LARGEST", "SE_TOPK_SMALLEST", "SE_UNIT_SLOT",
+    "SE_UNIT_PAGE", "SE_COMPACT_GATHER", "SE_COMPACT_EVICT_SLOTS", "SE_PAGES_BUILD", "SE_PAGES_SCORE",
+    "SE_REFRESH_LAST_PAGE", "SE_REFRESH_FROM_PAGE", "SE_DEV_INDEX", "SE_DEV_CAPACITY",
 ]
 
 
@@ -185,6 +185,18 @@ def se_page_bounds(cache, op, q=None, page_scores=None, *, status=None, stream=N
     stride = 0 if page_scores is None else page_scores.shape[-1]
     _check("se_page_bounds", lib.se_page_bounds(C.byref(c), op, _ptr(q), _ptr(page_scores), stride, _ptr(status),
                                                 None, 0, sp))
+
+
+def se_page_bounds_refresh(cache, mode, page_lo=None, max_pages=0, *, status=None, stream=None):
+    """Quest metadata maintenance: BUILD's values for the last page of each unit (SE_REFRESH_LAST_PAGE) or for
+    pages [page_lo[u], ceil(n_slots/page)), at most max_pages per unit (SE_REFRESH_FROM_PAGE; page_lo None =
+    page 0; max_pages 0 = the block table's width)."""
+    lib = _lib.load()
+    st, sp = _stream(stream)
+    c = cache.desc()
+    mp = int(max_pages) if max_pages else int(cache.block_table.shape[1])
+    _check("se_page_bounds_refresh", lib.se_page_bounds_refresh(C.byref(c), int(mode), _ptr(page_lo), mp,
+                                                                _ptr(status), None, 0, sp))
 
 
 def se_sparse_decode_attn(cache, q, out, *, scale, sel_pages=None, sel_count=None, max_sel=0, max_slots=0,

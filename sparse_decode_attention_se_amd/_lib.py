@@ -15,6 +15,7 @@ SE_TOPK_LARGEST, SE_TOPK_SMALLEST = 0, 1
 SE_UNIT_SLOT, SE_UNIT_PAGE = 0, 1
 SE_COMPACT_GATHER, SE_COMPACT_EVICT_SLOTS = 0, 1
 SE_PAGES_BUILD, SE_PAGES_SCORE = 0, 1
+SE_REFRESH_LAST_PAGE, SE_REFRESH_FROM_PAGE = 0, 1
 
 P = C.c_void_p
 I32 = C.c_int32
@@ -65,6 +66,7 @@ EXPORTS = {
     "se_compact_evict": (I32, [C.POINTER(se_cache_t), P, P, C.POINTER(se_compact_params_t), P, P, C.c_size_t, P]),
     "se_cache_append": (I32, [C.POINTER(se_cache_t), P, P, P, P, P, C.c_size_t, P]),
     "se_page_bounds": (I32, [C.POINTER(se_cache_t), I32, P, P, I32, P, P, C.c_size_t, P]),
+    "se_page_bounds_refresh": (I32, [C.POINTER(se_cache_t), I32, P, I32, P, P, C.c_size_t, P]),
     "se_sparse_decode_attn_workspace_size": (C.c_size_t, [C.POINTER(se_cache_t), C.POINTER(se_decode_params_t),
                                                           I32]),
     "se_sparse_decode_attn": (I32, [C.POINTER(se_cache_t), P, P, P, C.POINTER(se_decode_params_t), P, P, P,

@@ -2,7 +2,8 @@
 // query-dependent page selection at build_decode_selection; the metadata is kept beside the KV).
 //   BUILD  page_meta[b][g][p] = (elementwise min, elementwise max) of the resident keys of page p
 //   SCORE  U[b][g][p] = max over the group's query heads of sum_e max(q_e * min_e, q_e * max_e)
-// Both are HBM streams: a page's key tile for one head is 16 rows x 256 B contiguous, read by 16 lanes.
+//   REFRESH (se_page_bounds_refresh) BUILD's values for the pages an append or a compaction changed
+// All are HBM streams: a page's key tile for one head is 16 rows x 256 B contiguous, read by 16 lanes.
 #include "common.hpp"
 
 namespace se {
@@ -19,6 +20,8 @@ struct PagesArgs {
   float *scores;
   int32_t *status;
   int32_t n_kv, page, max_blocks, num_blocks, score_stride, R;
+  const int32_t *page_lo;     // refresh: first page per unit (NULL = 0)
+  int32_t refresh_last, max_pages;
 };
 
 template <int DTYPE>
@@ -45,16 +48,11 @@ SE_DEV u32x4 pack(const float *x) {
   return w;
 }
 
+// page p of unit (b, g) with n slots: (min, max) over its resident keys into page_meta (+inf / -inf without any),
+// by the 16 lanes of one row, lane cl holding bytes [16 cl, 16 cl + 16) of the key
 template <int DTYPE>
-__global__ __launch_bounds__(kThreads) void pages_build(PagesArgs a) {
+SE_DEV void build_page(const PagesArgs &a, int unit, int b, int g, int p, int cl, int n) {
   constexpr int EPL = DTYPE == SE_DTYPE_BF16 ? 8 : 4;
-  const int unit = blockIdx.y;
-  const int b = unit / a.n_kv, g = unit % a.n_kv;
-  const int p = blockIdx.x * kPagesPerWG + (threadIdx.x >> 4);
-  const int cl = threadIdx.x & 15;
-  if (p >= a.max_blocks) return;
-  int n = a.n_slots[unit];
-  n = min(max(n, 0), a.max_blocks * a.page);
   float lo[EPL], hi[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) {
@@ -82,6 +80,47 @@ __global__ __launch_bounds__(kThreads) void pages_build(PagesArgs a) {
   char *m = a.meta + ((int64_t)unit * a.max_blocks + p) * 2 * 256 + cl * 16;
   st16(m, pack<DTYPE>(lo));
   st16(m + 256, pack<DTYPE>(hi));
+}
+
+template <int DTYPE>
+__global__ __launch_bounds__(kThreads) void pages_build(PagesArgs a) {
+  const int unit = blockIdx.y;
+  const int b = unit / a.n_kv, g = unit % a.n_kv;
+  const int p = blockIdx.x * kPagesPerWG + (threadIdx.x >> 4);
+  if (p >= a.max_blocks) return;
+  int n = a.n_slots[unit];
+  n = min(max(n, 0), a.max_blocks * a.page);
+  build_page<DTYPE>(a, unit, b, g, p, threadIdx.x & 15, n);
+}
+
+// the unit's pages [lo, ceil(n_slots / page)), lo = page_lo[unit] (0 without page_lo), or only its last page;
+// at most max_pages of them
+template <int DTYPE>
+__global__ __launch_bounds__(kThreads) void pages_refresh(PagesArgs a) {
+  const int unit = blockIdx.y;
+  const int b = unit / a.n_kv, g = unit % a.n_kv;
+  int n = a.n_slots[unit];
+  n = min(max(n, 0), a.max_blocks * a.page);
+  const int n_pages = (n + a.page - 1) / a.page;
+  int lo, hi;
+  if (a.refresh_last) {
+    lo = n_pages - 1;
+    hi = n_pages;
+  } else {
+    lo = a.page_lo ? a.page_lo[unit] : 0;
+    hi = n_pages;
+    if (lo < 0 || lo > a.max_blocks) {
+      if (blockIdx.x == 0 && threadIdx.x == 0) raise(a.status, SE_DEV_INDEX);
+      return;
+    }
+    if (hi - lo > a.max_pages) {
+      if (blockIdx.x == 0 && threadIdx.x == 0) raise(a.status, SE_DEV_CAPACITY);
+      hi = lo + a.max_pages;
+    }
+  }
+  const int p = lo + blockIdx.x * kPagesPerWG + (threadIdx.x >> 4);
+  if (p < 0 || p >= hi) return;
+  build_page<DTYPE>(a, unit, b, g, p, threadIdx.x & 15, n);
 }
 
 template <int DTYPE, int R>
@@ -146,6 +185,9 @@ extern "C" int32_t se_page_bounds(se_cache_t *c, int32_t op, const void *q, floa
   a.num_blocks = c->num_blocks;
   a.score_stride = score_stride;
   a.R = c->n_q / c->n_kv;
+  a.page_lo = nullptr;
+  a.refresh_last = 0;
+  a.max_pages = 0;
   const dim3 grid((c->max_blocks + se::kPagesPerWG - 1) / se::kPagesPerWG, c->B * c->n_kv);
   hipStream_t st = (hipStream_t)stream;
   if (op == SE_PAGES_BUILD) {
@@ -171,5 +213,42 @@ extern "C" int32_t se_page_bounds(se_cache_t *c, int32_t op, const void *q, floa
     default: return SE_ERR_UNSUPPORTED;
   }
 #undef SE_PAGES_R
+  return se_host::launch_status();
+}
+
+extern "C" int32_t se_page_bounds_refresh(se_cache_t *c, int32_t mode, const int32_t *page_lo, int32_t max_pages,
+                                          int32_t *status, void *ws, size_t ws_bytes, se_stream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  int32_t rc = se_host::check_cache(c);
+  if (rc != SE_OK) return rc;
+  if (!c->page_meta) return SE_ERR_NULL;
+  const bool ok_shape = (c->dtype == SE_DTYPE_BF16 && c->d == 128) || (c->dtype == SE_DTYPE_F32 && c->d == 64);
+  if (!ok_shape) return SE_ERR_DTYPE;
+  if (mode != SE_REFRESH_LAST_PAGE && mode != SE_REFRESH_FROM_PAGE) return SE_ERR_PARAM;
+  if (mode == SE_REFRESH_FROM_PAGE && max_pages < 1) return SE_ERR_PARAM;
+  se::PagesArgs a;
+  a.k = (const char *)c->k_pool;
+  a.bt = c->block_table;
+  a.pos = c->pos_map;
+  a.n_slots = c->n_slots;
+  a.meta = (char *)c->page_meta;
+  a.q = nullptr;
+  a.scores = nullptr;
+  a.status = status;
+  a.n_kv = c->n_kv;
+  a.page = c->page;
+  a.max_blocks = c->max_blocks;
+  a.num_blocks = c->num_blocks;
+  a.score_stride = 0;
+  a.R = c->n_q / c->n_kv;
+  a.page_lo = mode == SE_REFRESH_FROM_PAGE ? page_lo : nullptr;
+  a.refresh_last = mode == SE_REFRESH_LAST_PAGE;
+  const int pages = a.refresh_last ? 1 : (max_pages < c->max_blocks ? max_pages : c->max_blocks);
+  a.max_pages = pages;
+  const dim3 grid((pages + se::kPagesPerWG - 1) / se::kPagesPerWG, c->B * c->n_kv);
+  hipStream_t st = (hipStream_t)stream;
+  if (c->dtype == SE_DTYPE_BF16) hipLaunchKernelGGL(se::pages_refresh<SE_DTYPE_BF16>, grid, dim3(se::kThreads), 0, st, a);
+  else hipLaunchKernelGGL(se::pages_refresh<SE_DTYPE_F32>, grid, dim3(se::kThreads), 0, st, a);
   return se_host::launch_status();
 }

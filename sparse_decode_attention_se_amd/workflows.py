@@ -8,10 +8,10 @@ the current stream, and nothing here synchronises.
 """
 import torch
 
-from . import (SE_COMPACT_EVICT_SLOTS, SE_COMPACT_GATHER, SE_PAGES_BUILD, SE_PAGES_SCORE, SE_SCORE_BIDIR,
-               SE_SCORE_CAUSAL, SE_TOPK_LARGEST, SE_TOPK_SMALLEST, SE_UNIT_PAGE, SE_UNIT_SLOT, se_cache_append,
-               se_compact_evict, se_page_bounds, se_sparse_decode_attn, se_token2chunk, se_topk_select,
-               se_window_score)
+from . import (SE_COMPACT_EVICT_SLOTS, SE_COMPACT_GATHER, SE_PAGES_BUILD, SE_PAGES_SCORE, SE_REFRESH_FROM_PAGE,
+               SE_REFRESH_LAST_PAGE, SE_SCORE_BIDIR, SE_SCORE_CAUSAL, SE_TOPK_LARGEST, SE_TOPK_SMALLEST, SE_UNIT_PAGE,
+               SE_UNIT_SLOT, se_cache_append, se_compact_evict, se_page_bounds, se_page_bounds_refresh,
+               se_sparse_decode_attn, se_token2chunk, se_topk_select, se_window_score)
 
 
 def _dims(cache):
@@ -130,6 +130,14 @@ class QuestStep:
 
     def build(self):
         se_page_bounds(self.cache, SE_PAGES_BUILD, status=self.status)
+
+    def refresh_last_page(self):
+        """After a high-water append: the metadata of the page it wrote."""
+        se_page_bounds_refresh(self.cache, SE_REFRESH_LAST_PAGE, status=self.status)
+
+    def refresh_from(self, page_lo=None, max_pages=0):
+        """After a compaction: the metadata of pages [page_lo, end) of every unit (page_lo None = 0)."""
+        se_page_bounds_refresh(self.cache, SE_REFRESH_FROM_PAGE, page_lo, max_pages, status=self.status)
 
     def run(self, q):
         se_page_bounds(self.cache, SE_PAGES_SCORE, q, self.page_scores, status=self.status)

@@ -10,8 +10,9 @@ import torch
 import oracle
 import sparse_decode_attention_se_amd as se
 import workloads as W
-from gpu_util import (DEV, assert_scores_close, compare_cache, i32, lists_from, status_word, storage_tensor,
-                      to_device)
+from gpu_util import (DEV, assert_scores_close, assert_sets_match_modulo_ties, compare_cache, i32, lists_from,
+                      status_word, storage_tensor, to_device)
+from sparse_decode_attention_se_amd import workflows as WF
 
 pytestmark = pytest.mark.gpu
 
@@ -460,3 +461,87 @@ def test_page_bounds_build_exact_and_score():
     r = u[:, :, :n_pages]
     assert np.all(np.isfinite(r))
     np.testing.assert_allclose(g, r, rtol=1e-3, atol=1e-3)
+
+
+# ------------------------------------------------------------------ page metadata refresh -------------------------
+def meta_bits(dc):
+    return dc.page_meta.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("N", [32, 37, 1000])
+def test_page_bounds_refresh_last_page_after_append(N):
+    # N = 32: the append opens a page (a block is popped); 37 and 1000: it lands in the partly filled last page
+    banner(f"refresh last page after append N={N}")
+    cfg = W.H2O("t", B=3, hq=8, hkv=2, d=128, N=N, budget=N, recent=4, steps=1, zipf=1.1)
+    inp = W.gen_h2o(cfg, seed=7, threads=2)
+    st = inp["cache"]
+    st.page_meta = oracle.page_bounds_build(st)
+    pos = np.full((3,), N, np.int32)
+    ref, _ = oracle.cache_append(st, inp["k_new"][0], inp["v_new"][0], pos)
+    want = oracle.page_bounds_build(ref)
+    assert not np.array_equal(want, st.page_meta)
+    dc = to_device(st, 8)
+    status = status_word()
+    se.se_cache_append(dc, storage_tensor(inp["k_new"][0], "bf16"), storage_tensor(inp["v_new"][0], "bf16"), i32(pos),
+                       status=status)
+    se.se_page_bounds_refresh(dc, se.SE_REFRESH_LAST_PAGE, status=status)
+    assert se.se_status_read(status) == 0
+    np.testing.assert_array_equal(meta_bits(dc), want)
+
+
+@pytest.mark.parametrize("window", [0, 300])
+def test_page_bounds_refresh_after_compaction_and_quest_over_evicted_cache(window):
+    """Physical eviction, then logical selection on the evicted cache: the metadata of the compacted pages is
+    refreshed, page scores and the page choice follow the oracle, and decode over every page equals dense decode
+    over the retained slots."""
+    banner(f"refresh after compaction, Quest over the evicted cache, window={window}")
+    from types import SimpleNamespace
+    from oracle import pipelines as P
+
+    inp = snap_inputs(B=2, N=1337, seed=9)
+    st = inp["cache"]
+    st.page_meta = oracle.page_bounds_build(st)
+    n = 1337
+    w0 = n - window if window else 0  # w0 = 1037 is not page-aligned
+    rs = np.random.default_rng(9)
+    keep = [[np.sort(rs.choice(np.arange(w0, n), size=100 + 37 * (b + g), replace=False)).astype(np.int32)
+             for g in range(2)] for b in range(2)]
+    ref = oracle.compact_gather(st, keep, window=window)
+    dc = to_device(st, 8)
+    idx, cnt = W.pack_lists(keep, 200)
+    status = status_word()
+    se.se_compact_evict(dc, i32(idx), i32(cnt), mode=se.SE_COMPACT_GATHER, window=window, status=status)
+    lo = np.full((2, 2), w0 // 16, np.int32)
+    se.se_page_bounds_refresh(dc, se.SE_REFRESH_FROM_PAGE, i32(lo), status=status)
+    assert se.se_status_read(status) == 0
+    got, want = meta_bits(dc), oracle.page_bounds_build(ref)
+    for b in range(2):
+        for g in range(2):
+            n_pages = -(-int(ref.n_slots[b, g]) // 16)
+            np.testing.assert_array_equal(got[b, g, :n_pages], want[b, g, :n_pages])
+            np.testing.assert_array_equal(got[b, g, n_pages:], st.page_meta[b, g, n_pages:])
+
+    # Quest page selection and decode over the evicted cache
+    top = 3
+    qref = P.quest_step(dict(cfg=SimpleNamespace(top_pages=top), q_dec=inp["q_dec"], scale=inp["scale"]), ref)
+    qs = WF.QuestStep(dc, top_pages=top, scale=inp["scale"], status=status)
+    out = qs.run(storage_tensor(inp["q_dec"], "bf16")).cpu().numpy()
+    assert se.se_status_read(status) == 0
+    ps = qs.page_scores.cpu().numpy()
+    sel = lists_from(qs.pages, qs.count)
+    for b in range(2):
+        for g in range(2):
+            n_pages = -(-int(ref.n_slots[b, g]) // 16)
+            np.testing.assert_allclose(ps[b, g, :n_pages], qref["page_scores"][b, g, :n_pages], rtol=1e-3, atol=1e-3)
+            if not assert_sets_match_modulo_ties(sel[b][g], qref["pages"][b][g], qref["page_scores"][b, g]):
+                np.testing.assert_allclose(out[b, 4 * g:4 * g + 4], qref["out"][b, 4 * g:4 * g + 4], atol=2e-3, rtol=0)
+    # every page selected: dense decode over the retained slots
+    n_pages_max = int(-(-ref.n_slots.max() // 16))
+    allp = [[np.arange(-(-int(ref.n_slots[b, g]) // 16), dtype=np.int32) for g in range(2)] for b in range(2)]
+    sel_all, cnt_all = W.pack_lists(allp, n_pages_max)
+    out_all = torch.empty((2, 8, 128), dtype=torch.float32, device=DEV)
+    se.se_sparse_decode_attn(dc, storage_tensor(inp["q_dec"], "bf16"), out_all, scale=inp["scale"],
+                             sel_pages=i32(sel_all), sel_count=i32(cnt_all), status=status)
+    dense, _ = oracle.decode_attn(ref, inp["q_dec"], inp["scale"])
+    assert se.se_status_read(status) == 0
+    np.testing.assert_allclose(out_all.cpu().numpy(), dense, atol=2e-3, rtol=0)
