@@ -57,11 +57,13 @@ CALL_KERNELS = {
     "se_compact_evict": ["gather_move", "gather_extents", "gather_push", "evict_slots_kernel"],
     "se_cache_append": ["append_kernel"],
     "se_page_bounds": ["pages_score", "pages_build"],
+    "se_page_bounds_refresh": ["pages_refresh"],
     "se_sparse_decode_attn": ["decode_partial", "decode_merge", "decode_cum", "decode_unit"],
 }
 CALL_SOURCES = {
     "se_window_score": "score.hip", "se_topk_select": "topk.hip", "se_token2chunk": "t2c.hip",
     "se_compact_evict": "compact.hip", "se_cache_append": "compact.hip", "se_page_bounds": "pages.hip",
+    "se_page_bounds_refresh": "pages.hip",
     "se_sparse_decode_attn": "decode.hip",
 }
 CSRC = os.path.join(ROOT, "sparse_decode_attention_se_amd", "csrc")
@@ -307,6 +309,45 @@ def setup_c3(se, WF, W, copies, dev):
     return cfg, steps, B * N, alg, None
 
 
+def setup_c5(se, WF, W, copies, dev):
+    """C3's Quest decode step with its cache maintenance: append the decode token, refresh the metadata of the page
+    it wrote, then page scores, page choice and decode. Every step runs on its own pristine copy, as in C3."""
+    import torch
+
+    cfg = W.C5
+    inp = W.gen_quest(cfg, seed=0, threads=16)
+    base = device_cache(se, cfg, inp["cache"], dev)
+    q = to_dev_bf16(inp["q_dec"], dev)
+    k_new, v_new = to_dev_bf16(inp["k_new"][0], dev), to_dev_bf16(inp["v_new"][0], dev)
+    pos = torch.full((cfg.B,), cfg.N, dtype=torch.int32, device=dev)
+    WF.QuestStep(base, top_pages=cfg.top_pages, scale=inp["scale"]).build()
+    caches = [base] + [base.clone() for _ in range(copies - 1)]
+    steps = []
+    for c in caches:
+        qs = WF.QuestStep(c, top_pages=cfg.top_pages, scale=inp["scale"])
+        steps.append([
+            ("se_cache_append", lambda c=c: se.se_cache_append(c, k_new, v_new, pos)),
+            ("se_page_bounds_refresh", lambda qs=qs: qs.refresh_last_page()),
+            ("se_page_bounds", lambda qs=qs: se.se_page_bounds(qs.cache, se.SE_PAGES_SCORE, q, qs.page_scores)),
+            ("se_topk_select", lambda qs=qs: se.se_topk_select(
+                qs.cache, qs.page_scores, qs.pages, qs.count, mode=se.SE_TOPK_LARGEST, unit=se.SE_UNIT_PAGE,
+                k=cfg.top_pages, forced_ends=1)),
+            ("se_sparse_decode_attn", lambda qs=qs: se.se_sparse_decode_attn(
+                qs.cache, q, qs.out, scale=qs.scale, sel_pages=qs.pages, sel_count=qs.count)),
+        ])
+    B, G, N, row = cfg.B, cfg.hkv, cfg.N + 1, cfg.d * 2
+    P_ = -(-N // cfg.page)
+    sel = cfg.top_pages + 2
+    alg = {
+        "se_cache_append": {"bytes": B * G * 2 * row * 2 + B * G * 4 * 4},
+        "se_page_bounds_refresh": {"bytes": B * G * (cfg.page * row + 2 * row)},
+        "se_page_bounds": {"bytes": B * G * P_ * 2 * row + B * G * P_ * 4 + B * cfg.hq * row},
+        "se_topk_select": {"bytes": B * G * P_ * 4 + B * G * sel * 4},
+        "se_sparse_decode_attn": {"bytes": B * G * sel * cfg.page * (2 * row + 4) + B * cfg.hq * cfg.d * (2 + 4)},
+    }
+    return cfg, steps, B * N, alg, None
+
+
 def setup_c4(se, WF, W, copies, dev):
     cfg = W.scaled(W.C4, steps=copies)
     inp = W.gen_h2o(cfg, seed=0, threads=16)
@@ -341,7 +382,7 @@ def setup_c4(se, WF, W, copies, dev):
     return cfg, steps, B * n, alg, None
 
 
-SETUPS = {"c1": setup_c1, "c2": setup_c2, "c3": setup_c3, "c4": setup_c4}
+SETUPS = {"c1": setup_c1, "c2": setup_c2, "c3": setup_c3, "c4": setup_c4, "c5": setup_c5}
 
 
 def cpu_baseline(inp, n_seq):

@@ -185,3 +185,39 @@ def test_pipeline_h2o_small():
     if not diverged.any():
         compare_cache(dc.to_numpy(), st, cum_exact=False)
     assert diverged.mean() < 0.5
+
+
+def test_pipeline_quest_with_append_small():
+    """Quest decode steps that first append a token: the refreshed metadata equals a rebuild of the appended cache
+    after every step, and page choice and decode follow the oracle."""
+    banner("pipeline Quest with appends, 2 seqs x 8192, 3 steps")
+    cfg = W.scaled(W.C5, N=8192, top_pages=48, steps=3)
+    inp = W.gen_quest(cfg, seed=1, threads=8)
+    st = inp["cache"]
+    dc = to_device(st, cfg.hq)
+    status = status_word()
+    qs = WF.QuestStep(dc, top_pages=cfg.top_pages, scale=inp["scale"], status=status)
+    qs.build()
+    q = storage_tensor(inp["q_dec"], "bf16")
+    r = cfg.hq // cfg.hkv
+    for s in range(cfg.steps):
+        pos = np.full((cfg.B,), cfg.N + s, np.int32)
+        st, _ = oracle.cache_append(st, inp["k_new"][s], inp["v_new"][s], pos)
+        se.se_cache_append(dc, storage_tensor(inp["k_new"][s], "bf16"), storage_tensor(inp["v_new"][s], "bf16"),
+                           i32(pos), status=status)
+        qs.refresh_last_page()
+        out = qs.run(q).cpu().numpy()
+        assert se.se_status_read(status) == 0
+        ref = P.quest_step(inp, st)
+        meta = dc.page_meta.view(torch.int16).cpu().numpy().view(np.uint16)
+        np.testing.assert_array_equal(meta, ref["meta"])
+        n_pages = -(-(cfg.N + s + 1) // 16)
+        ps = qs.page_scores.cpu().numpy()
+        np.testing.assert_allclose(ps[:, :, :n_pages], ref["page_scores"][:, :, :n_pages], rtol=1e-3, atol=1e-3)
+        got = lists_from(qs.pages, qs.count)
+        for b in range(cfg.B):
+            for g in range(cfg.hkv):
+                assert n_pages - 1 in got[b][g]  # the page holding the new token is always read
+                if not assert_sets_match_modulo_ties(got[b][g], ref["pages"][b][g], ref["page_scores"][b, g]):
+                    np.testing.assert_allclose(out[b, g * r:(g + 1) * r], ref["out"][b, g * r:(g + 1) * r],
+                                               atol=2e-3, rtol=0)

@@ -157,6 +157,7 @@ class Quest:
     shift: float
     dtype: str = "bf16"
     page: int = 16
+    steps: int = 0  # decode tokens appended after the prompt (room for them in the cache, and their K/V)
 
 
 @dataclass(frozen=True)
@@ -187,8 +188,11 @@ C2 = Kara("c2_kara_qwen3_4b", B=128, hq=32, hkv=8, d=128, N=16384, window=512, p
           budget_frac=0.2, max_gap=8, period=128, events=1, rho=0.9)
 C3 = Quest("c3_quest_128k", B=2, hq=32, hkv=8, d=128, N=131072, top_pages=256, shift_frac=0.01, shift=2.0)
 C4 = H2O("c4_h2o", B=64, hq=32, hkv=8, d=128, N=8192, budget=8192, recent=256, steps=1024, zipf=1.1)
+# Quest decode with its metadata kept current: C3's cache and query, each step first appending a decode token
+C5 = Quest("c5_quest_128k_append", B=2, hq=32, hkv=8, d=128, N=131072, top_pages=256, shift_frac=0.01, shift=2.0,
+           steps=16)
 
-FULL = {c.name: c for c in (C0, C1, C2, C3, C4)}
+FULL = {c.name: c for c in (C0, C1, C2, C3, C4, C5)}
 
 
 def scaled(cfg, **kw):
@@ -395,9 +399,11 @@ def gen_kara(cfg: Kara, seed: int = 0, threads: int = 8) -> dict:
 
 def gen_quest(cfg: Quest, seed: int = 0, threads: int = 8) -> dict:
     """Inputs of the Quest-style workload: a full cache with a fraction of pages shifted along the group's query
-    direction, page metadata storage, and one decode query per sequence."""
+    direction, page metadata storage, and one decode query per sequence. With ``cfg.steps`` > 0 the cache has
+    room for that many appended tokens, whose keys and values (``k_new``, ``v_new`` [steps][B][n_kv][d], i.i.d.
+    N(0,1)) are drawn from streams of their own, so the prompt's draws do not change."""
     B, hq, hkv, d, N, page = cfg.B, cfg.hq, cfg.hkv, cfg.d, cfg.N, cfg.page
-    max_blocks = -(-N // page)
+    max_blocks = -(-(N + cfg.steps) // page)
     cache = empty_cache(B, hkv, d, page, max_blocks, B * max_blocks, cfg.dtype, with_meta=True)
     nb = layout_initial(cache, N)
     r = hq // hkv
@@ -419,7 +425,13 @@ def gen_quest(cfg: Quest, seed: int = 0, threads: int = 8) -> dict:
         write_sequence(cache.v_pool, nb, b, to_storage(v, cfg.dtype), page)
 
     _pmap(fill, range(B), threads)
-    return dict(cfg=cfg, cache=cache, q_dec=q_dec, scale=1.0 / math.sqrt(d))
+    out = dict(cfg=cfg, cache=cache, q_dec=q_dec, scale=1.0 / math.sqrt(d))
+    if cfg.steps:
+        out["k_new"] = np.stack([to_storage(_normal(seed, TAG_KNEW, b, (cfg.steps, hkv, d)), cfg.dtype)
+                                 for b in range(B)], axis=1)
+        out["v_new"] = np.stack([to_storage(_normal(seed, TAG_VNEW, b, (cfg.steps, hkv, d)), cfg.dtype)
+                                 for b in range(B)], axis=1)
+    return out
 
 
 def gen_h2o(cfg: H2O, seed: int = 0, threads: int = 8) -> dict:
