@@ -29,8 +29,15 @@ def _items(cache, b, g, unit, page):
 
 
 def topk_largest(scores, cache, k: int, *, window: int = 0, protect: int = 0, unit: str = "slot",
-                 forced_ends: bool = False):
+                 forced_ends: bool = False, prune_range=None, block_refs=None, emit: str = "kept"):
     """Per (b, g): the k best candidates plus the always-kept items, as an ascending item list.
+
+    Range-restricted pruning (SparseEngine page, "How it works", sparse prefix-cache pruning: the application
+    names a position range [L, R), a scoring policy keeps part of it, the mask applies to idle blocks only, and
+    the resident set becomes R' = (R minus T) plus I). With ``prune_range = (L, R)`` (slot unit) a slot is a
+    candidate only if its position lies in [L, R) and, when ``block_refs`` (per physical block, > 0 = busy) is
+    given, its block is idle; every other resident slot is always kept. ``emit = "dropped"`` returns the
+    candidates that were not chosen (the slots to free) instead of the kept list.
 
     scores: [B][n_kv][S] (float32 or float64). Slot unit: items are slots ``[0, n_slots)``; with ``window`` > 0
     the candidate region starts at ``base = n_slots - window`` and scores are indexed by ``slot - base``,
@@ -51,6 +58,16 @@ def topk_largest(scores, cache, k: int, *, window: int = 0, protect: int = 0, un
                     raise ValueError("window longer than the cache")
                 cand = [i for i in range(base, n - protect) if resident[i]]
                 kept = [i for i in range(max(n - protect, 0), n) if resident[i]]
+                if prune_range is not None:
+                    lo, hi = prune_range
+
+                    def prunable(i):
+                        if not lo <= key[i] < hi:
+                            return False
+                        return block_refs is None or block_refs[cache.block_table[b, i // cache.page]] == 0
+
+                    kept = sorted(kept + [i for i in cand if not prunable(i)])
+                    cand = [i for i in cand if prunable(i)]
             else:
                 base = 0
                 if forced_ends and n >= 2:
@@ -61,7 +78,10 @@ def topk_largest(scores, cache, k: int, *, window: int = 0, protect: int = 0, un
                     cand, kept = list(range(n)), []
             ranked = sorted(cand, key=lambda i: (-scores[b, g, i - base], key[i]))
             chosen = ranked[:min(k, len(ranked))]
-            row.append(np.array(sorted(chosen + kept), np.int32))
+            if emit == "dropped":
+                row.append(np.array(sorted(ranked[len(chosen):]), np.int32))
+            else:
+                row.append(np.array(sorted(chosen + kept), np.int32))
         out.append(row)
     return out
 

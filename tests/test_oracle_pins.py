@@ -286,6 +286,64 @@ def test_evict_then_append_reuses_slot_and_keeps_counts():
     assert slots.tolist() == [[4]] and c.pos_map[0, 0, 4] == 10 and c.n_slots[0, 0] == 10
 
 
+# ------------------------------------------------------------------ range-restricted pruning ----------------------
+def _prune_case(seed=3, N=90, busy_frac=0.3):
+    inp = tiny_snapkv(B=2, hq=4, hkv=2, d=8, N=N, dtype="f32", seed=seed)
+    c = inp["cache"]
+    c.slot_stack = np.zeros((2, 2, N), np.int32)  # room for every eviction
+    rs = np.random.default_rng(seed)
+    c.pos_map[0, 1, [5, 40, 41]] = -1  # a few holes
+    refs = (rs.random(c.num_blocks) < busy_frac).astype(np.int32)
+    scores = rs.random((2, 2, N)).round(2)  # coarse values: many ties
+    return c, refs, scores
+
+
+def _brute_kept_positions(c, refs, scores, b, g, k, lo, hi):
+    """R' = (R minus T) plus I, straight from the definition on one (b, g)."""
+    n = int(c.n_slots[b, g])
+    res = [s for s in range(n) if c.pos_map[b, g, s] >= 0]
+    T = [s for s in res if lo <= c.pos_map[b, g, s] < hi and refs[c.block_table[b, s // c.page]] == 0]
+    order = np.lexsort((np.array([c.pos_map[b, g, s] for s in T]), -np.array([scores[b, g, s] for s in T])))
+    I = [T[i] for i in order[:k]]
+    return sorted(int(c.pos_map[b, g, s]) for s in set(res) - set(T) | set(I))
+
+
+@pytest.mark.parametrize("k", [0, 7, 1000])
+def test_range_pruning_keeps_outside_busy_and_top_k(k):
+    c, refs, scores = _prune_case()
+    lo, hi = 20, 70
+    kept = oracle.topk_largest(scores, c, k, prune_range=(lo, hi), block_refs=refs)
+    dropped = oracle.topk_largest(scores, c, k, prune_range=(lo, hi), block_refs=refs, emit="dropped")
+    after = oracle.evict_slots(c, dropped)
+    for b in range(2):
+        for g in range(2):
+            n = int(c.n_slots[b, g])
+            res = {s for s in range(n) if c.pos_map[b, g, s] >= 0}
+            assert set(kept[b][g]) | set(dropped[b][g]) == res and not set(kept[b][g]) & set(dropped[b][g])
+            want = _brute_kept_positions(c, refs, scores, b, g, k, lo, hi)
+            now = sorted(int(x) for x in after.pos_map[b, g, :n] if x >= 0)
+            assert now == want
+            assert [int(c.pos_map[b, g, s]) for s in kept[b][g]] == want
+            # busy blocks and positions outside the range lose nothing
+            for s in res:
+                p = c.pos_map[b, g, s]
+                if not lo <= p < hi or refs[c.block_table[b, s // c.page]] > 0:
+                    assert s in set(kept[b][g])
+            if k == 0:
+                assert all(lo <= c.pos_map[b, g, s] < hi for s in dropped[b][g])
+            if k == 1000:
+                assert len(dropped[b][g]) == 0
+
+
+def test_range_pruning_without_refs_or_with_full_range_is_plain_top_k():
+    c, refs, scores = _prune_case(busy_frac=0.0)
+    plain = oracle.topk_largest(scores, c, 11)
+    ranged = oracle.topk_largest(scores, c, 11, prune_range=(0, 1 << 30), block_refs=np.zeros_like(refs))
+    for b in range(2):
+        for g in range(2):
+            assert plain[b][g].tolist() == ranged[b][g].tolist()
+
+
 # ------------------------------------------------------------------ page bounds -----------------------------------
 def test_page_bound_is_an_upper_bound_and_tight_for_equal_keys():
     cfg = W.Quest("tiny", B=2, hq=4, hkv=2, d=16, N=100, top_pages=2, shift_frac=0.1, shift=2.0)
