@@ -117,6 +117,14 @@ int32_t se_window_score(const se_cache_t *c, const void *q_win, const int32_t *q
  *  SMALLEST / SLOT: if ctx_len > budget, returns min(k, ctx_len - budget) slots with the lowest score among the
  *    resident slots whose position is <= (max resident position - recent); order (score asc, position desc).
  *    Otherwise count = 0.
+ *  Range-restricted pruning (LARGEST / SLOT; SparseEngine page, "How it works", sparse prefix-cache pruning:
+ *    the application names a 0-based position range [L, R), a scoring policy keeps part of it, the mask applies
+ *    to idle blocks only and the resident set becomes R' = (R minus T) plus I): with range_hi > range_lo a
+ *    resident slot is a candidate only if range_lo <= position < range_hi and, when block_refs is given (device
+ *    [num_blocks], > 0 = the block has active references or transfers), its physical block is idle. Every other
+ *    resident slot of the region is kept. emit_dropped != 0 returns the candidates that were not chosen, ascending
+ *    (the list SE_COMPACT_EVICT_SLOTS frees) instead of the kept list. Needs out_stride >= the item count.
+ *    block_refs needs a range; range and emit_dropped need LARGEST / SLOT (else SE_ERR_PARAM).
  * Scores must not be NaN.
  */
 enum { SE_TOPK_LARGEST = 0, SE_TOPK_SMALLEST = 1 };
@@ -127,6 +135,8 @@ typedef struct {
   int32_t forced_ends;     /* LARGEST / PAGE */
   int32_t budget, recent;  /* SMALLEST */
   int32_t score_stride, out_stride;
+  int32_t range_lo, range_hi, emit_dropped; /* range-restricted pruning (0, 0, 0: off) */
+  const int32_t *block_refs;                /* NULL: every block idle */
 } se_topk_params_t;
 
 size_t se_topk_select_workspace_size(const se_cache_t *c, const se_topk_params_t *p);
@@ -162,7 +172,9 @@ int32_t se_token2chunk(const se_cache_t *c, const int32_t *idx, const int32_t *c
  *    (same physical ids); the rest of its allocated blocks are pushed on free_blocks in order of sequence, then
  *    logical block, and their table entries become -1. In place; bit-exact.
  *  EVICT_SLOTS: per (b, g) each listed resident slot is freed: position -1, cumulative score 0, pushed on the
- *    slot stack, ctx_len - 1. No data moves.
+ *    slot stack (in list order), ctx_len - 1. No data moves. The list must be ascending and distinct (as
+ *    se_topk_select returns it); an entry that is out of order, out of range or not resident raises SE_DEV_INDEX
+ *    and is skipped; entries beyond the slot stack's capacity are not evicted and raise SE_DEV_CAPACITY.
  * GATHER needs a workspace of se_compact_evict_workspace_size bytes ((2 B + 1) int32, rounded up); EVICT_SLOTS
  * needs none.
  */

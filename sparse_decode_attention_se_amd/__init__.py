@@ -136,13 +136,16 @@ def se_window_score(cache, q_win, q_pos, scores, *, scale, mode, n_query, window
 
 
 def se_topk_select(cache, scores, idx, count, *, mode, unit, k, window=0, protect=0, forced_ends=0, budget=0,
-                   recent=0, score_stride=None, out_stride=None, status=None, stream=None):
+                   recent=0, score_stride=None, out_stride=None, prune_range=None, block_refs=None,
+                   emit_dropped=False, status=None, stream=None):
     lib = _lib.load()
     st, sp = _stream(stream)
     c = cache.desc()
+    lo, hi = prune_range if prune_range is not None else (0, 0)
     p = _lib.se_topk_params_t(mode, unit, k, window, protect, forced_ends, budget, recent,
                               score_stride if score_stride is not None else scores.shape[-1],
-                              out_stride if out_stride is not None else idx.shape[-1])
+                              out_stride if out_stride is not None else idx.shape[-1], int(lo), int(hi),
+                              int(emit_dropped), _ptr(block_refs))
     nb = lib.se_topk_select_workspace_size(C.byref(c), C.byref(p))
     ws = _workspace(nb, cache.device, stream)
     _check("se_topk_select", lib.se_topk_select(C.byref(c), _ptr(scores), C.byref(p), _ptr(idx), _ptr(count),

@@ -38,7 +38,8 @@ class se_window_params_t(C.Structure):
 
 class se_topk_params_t(C.Structure):
     _fields_ = [("mode", I32), ("unit", I32), ("k", I32), ("window", I32), ("protect", I32), ("forced_ends", I32),
-                ("budget", I32), ("recent", I32), ("score_stride", I32), ("out_stride", I32)]
+                ("budget", I32), ("recent", I32), ("score_stride", I32), ("out_stride", I32), ("range_lo", I32),
+                ("range_hi", I32), ("emit_dropped", I32), ("block_refs", C.c_void_p)]
 
 
 class se_t2c_params_t(C.Structure):

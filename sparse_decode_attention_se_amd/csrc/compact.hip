@@ -375,38 +375,66 @@ struct EvictArgs {
   int32_t units, max_slots, slot_cap, idx_stride;
 };
 
-__global__ void evict_slots_kernel(EvictArgs a) {
-  int unit = blockIdx.x * blockDim.x + threadIdx.x;
-  if (unit >= a.units) return;
-  int cnt = a.count[unit], n = a.n_slots[unit];
+// One workgroup per unit; its list (ascending, distinct) in chunks of kEvictThreads entries. Valid entries are
+// pushed on the slot stack in list order (rank by a block scan); entries past the stack's capacity are not evicted
+// and raise SE_DEV_CAPACITY, invalid ones (not resident, out of range, out of order) raise SE_DEV_INDEX.
+constexpr int kEvictThreads = 256;
+__global__ __launch_bounds__(kEvictThreads) void evict_slots_kernel(EvictArgs a) {
+  __shared__ int s_wave[kEvictThreads / 64];
+  const int unit = blockIdx.x;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int cnt = a.count[unit], n = a.n_slots[unit], top = a.slot_top[unit];
   if (cnt < 0 || cnt > a.idx_stride) {
-    raise(a.status, SE_DEV_INDEX);
+    if (t == 0) raise(a.status, SE_DEV_INDEX);
+    return;
+  }
+  if (top < 0 || top > a.slot_cap) {
+    if (t == 0) raise(a.status, SE_DEV_CAPACITY);
     return;
   }
   int32_t *pos = a.pos + (int64_t)unit * a.max_slots;
   int32_t *st = a.slot_stack + (int64_t)unit * a.slot_cap;
   const int32_t *list = a.idx + (int64_t)unit * a.idx_stride;
-  int top = a.slot_top[unit];
-  if (top < 0 || top > a.slot_cap) {
-    raise(a.status, SE_DEV_CAPACITY);
-    return;
-  }
-  for (int i = 0; i < cnt; ++i) {
-    int s = list[i];
-    if (s < 0 || s >= n || s >= a.max_slots || pos[s] < 0) {
-      raise(a.status, SE_DEV_INDEX);
-      continue;
+  int pushed = 0;  // valid entries of the chunks before this one
+  for (int c0 = 0; c0 < cnt; c0 += kEvictThreads) {
+    const int i = c0 + t;
+    bool valid = false;
+    int s = -1;
+    if (i < cnt) {
+      s = list[i];
+      const int prev = i > 0 ? list[i - 1] : -1;
+      valid = s >= 0 && s < n && s < a.max_slots && prev < s && pos[s] >= 0;
+      if (!valid) raise(a.status, SE_DEV_INDEX);
     }
-    if (top >= a.slot_cap) {
-      raise(a.status, SE_DEV_CAPACITY);
-      break;
+    // exclusive rank of this entry among the chunk's valid ones
+    const uint64_t bal = __ballot(valid);
+    const int in_wave = __popcll(bal & ((1ull << lane) - 1ull));
+    if (lane == 0) s_wave[wave] = __popcll(bal);
+    __syncthreads();
+    int before = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < kEvictThreads / 64; ++w) {
+      before += w < wave ? s_wave[w] : 0;
+      total += s_wave[w];
     }
-    pos[s] = -1;
-    if (a.cum) a.cum[(int64_t)unit * a.max_slots + s] = 0.f;
-    st[top++] = s;
-    a.ctx[unit] -= 1;
+    __syncthreads();  // s_wave is rewritten by the next chunk
+    const int at = top + pushed + before + in_wave;
+    if (valid) {
+      if (at < a.slot_cap) {
+        pos[s] = -1;
+        if (a.cum) a.cum[(int64_t)unit * a.max_slots + s] = 0.f;
+        st[at] = s;
+      } else {
+        raise(a.status, SE_DEV_CAPACITY);
+      }
+    }
+    pushed += total;
   }
-  a.slot_top[unit] = top;
+  if (t == 0) {
+    const int done = min(pushed, a.slot_cap - top);
+    a.slot_top[unit] = top + done;
+    a.ctx[unit] -= done;
+  }
 }
 
 // ---- append -------------------------------------------------------------------------------------------------------
@@ -630,7 +658,7 @@ extern "C" int32_t se_compact_evict(se_cache_t *c, const int32_t *idx, const int
     a.max_slots = c->max_blocks * c->page;
     a.slot_cap = c->slot_cap;
     a.idx_stride = p->idx_stride;
-    hipLaunchKernelGGL(se::evict_slots_kernel, dim3((units + 255) / 256), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(se::evict_slots_kernel, dim3(units), dim3(se::kEvictThreads), 0, st, a);
     return se_host::launch_status();
   }
   return SE_ERR_PARAM;

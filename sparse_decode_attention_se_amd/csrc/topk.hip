@@ -8,6 +8,11 @@
 // (position, or page id; the complement of the position for the smallest mode), so the result is exactly "K
 // best by (score, tie key)". Per-wave ballots and one scan over them write the ascending output. Given
 // identical fp32 scores the result is exact.
+//
+// Range-restricted pruning (SparseEngine page, "How it works": the application names a position range, a scoring
+// policy keeps part of it, and the mask applies to idle blocks only): with a range, only resident slots whose
+// position lies in it and whose block has no references are candidates; the others are kept. The output can be
+// the dropped candidates instead, the list slot eviction frees.
 #include "common.hpp"
 
 namespace se {
@@ -23,9 +28,11 @@ SE_DEV uint32_t orderable(float f) {
 struct TopkArgs {
   const float *scores;
   const int32_t *pos, *n_slots, *ctx;
+  const int32_t *bt, *refs;  // block table and per-block reference counts (refs may be NULL: all idle)
   int32_t *idx, *count, *status;
   int32_t mode, unit_kind, k, window, protect, forced_ends, budget, recent, score_stride, out_stride;
-  int32_t n_kv, page, max_slots;
+  int32_t range_lo, range_hi, emit_dropped;  // range active when range_hi > range_lo
+  int32_t n_kv, page, max_slots, max_blocks, num_blocks;
 };
 
 // One workgroup per unit; item i lives in thread i % kThreads, register j = i / kThreads (coalesced loads).
@@ -181,6 +188,24 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
   int limit = 0;
   if (a.mode == SE_TOPK_SMALLEST) limit = (int)block_max_u((uint32_t)(mx + 1), s_red) - 1 - a.recent;
 
+  // range-restricted pruning: which items sit in a block with references (block-table loads, then counts)
+  const bool rng = !page_unit && a.range_hi > a.range_lo;
+  uint32_t busy = 0;
+  if (rng && a.refs) {
+    const int32_t *btb = a.bt + (int64_t)(unit / a.n_kv) * a.max_blocks;
+    int blk[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int i = j * kThreads + t;
+      blk[j] = btb[(base + (i < n_items ? i : 0)) / a.page];
+    }
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const bool ok = blk_ok(blk[j], a.num_blocks);
+      if (ok && a.refs[blk[j]] > 0) busy |= 1u << j;
+    }
+  }
+
   // keys of the candidates (tie keys, which order equal scores, are recomputed in the rare tie path below)
   uint32_t key[PER], cand = 0, keep = 0;
   int ncand_local = 0;
@@ -201,6 +226,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
         c = p <= limit;
       } else {
         k = base + i >= n - a.protect;
+        if (!k && rng && (p < a.range_lo || p >= a.range_hi || ((busy >> j) & 1u))) k = true;
         c = !k;
       }
     }
@@ -287,7 +313,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
 
   // ascending output: items are ordered by (register j, wave, lane); per (j, wave) counts from ballots, one
   // exclusive scan over them, then each selected item's rank inside its wave
-  const uint32_t out = sel | keep;
+  const uint32_t out = a.emit_dropped ? (cand & ~sel) : (sel | keep);
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
     const uint64_t b = __ballot((out >> j) & 1u);
@@ -354,6 +380,10 @@ extern "C" int32_t se_topk_select(const se_cache_t *c, const float *scores, cons
   if (p->unit != SE_UNIT_SLOT && p->unit != SE_UNIT_PAGE) return SE_ERR_PARAM;
   if (p->mode == SE_TOPK_SMALLEST && p->unit != SE_UNIT_SLOT) return SE_ERR_PARAM;
   if (p->window > 0 && p->protect > p->window) return SE_ERR_PARAM;
+  const bool rng = p->range_hi > p->range_lo;
+  if ((rng || p->emit_dropped || p->block_refs) && (p->mode != SE_TOPK_LARGEST || p->unit != SE_UNIT_SLOT))
+    return SE_ERR_PARAM;
+  if (p->block_refs && !rng) return SE_ERR_PARAM;
   const int max_slots = c->max_blocks * c->page;
   const int n_items = p->unit == SE_UNIT_PAGE ? c->max_blocks
                       : (p->mode == SE_TOPK_LARGEST && p->window > 0 && p->window < max_slots) ? p->window
@@ -361,6 +391,7 @@ extern "C" int32_t se_topk_select(const se_cache_t *c, const float *scores, cons
   long long need = p->k;
   if (p->mode == SE_TOPK_LARGEST) need += p->unit == SE_UNIT_PAGE ? (p->forced_ends ? 2 : 0) : p->protect;
   if (p->out_stride < need && p->out_stride < n_items) return SE_ERR_SHAPE;
+  if ((rng || p->emit_dropped) && p->out_stride < n_items) return SE_ERR_SHAPE;  // kept or dropped: up to every slot
   if (p->unit == SE_UNIT_SLOT && p->window == 0 && p->score_stride < max_slots) return SE_ERR_SHAPE;
   if (p->unit == SE_UNIT_SLOT && p->window > 0 && p->score_stride < p->window - p->protect) return SE_ERR_SHAPE;
   if (p->unit == SE_UNIT_PAGE && p->score_stride < c->max_blocks) return SE_ERR_SHAPE;
@@ -369,6 +400,13 @@ extern "C" int32_t se_topk_select(const se_cache_t *c, const float *scores, cons
   a.pos = c->pos_map;
   a.n_slots = c->n_slots;
   a.ctx = c->ctx_len;
+  a.bt = c->block_table;
+  a.refs = p->block_refs;
+  a.range_lo = p->range_lo;
+  a.range_hi = p->range_hi;
+  a.emit_dropped = p->emit_dropped;
+  a.max_blocks = c->max_blocks;
+  a.num_blocks = c->num_blocks;
   a.idx = idx;
   a.count = count;
   a.status = status;

@@ -54,6 +54,37 @@ class SnapKVEvent:
         return self.out
 
 
+class PruneRange:
+    """Sparse prefix-cache pruning over an application's position range [L, R) (SparseEngine page, "How it
+    works"): causal window scores of the last queries -> the best `keep` slots of the range among idle blocks,
+    every other resident slot kept -> the dropped slots freed onto the slot stacks (no data moves, so blocks with
+    references are never written)."""
+
+    def __init__(self, cache, *, wq, scale, status=None):
+        B, G, S, d = _dims(cache)
+        dev = cache.device
+        self.cache, self.wq, self.scale, self.status = cache, wq, scale, status
+        self.scores = torch.zeros((B, G, S), dtype=torch.float32, device=dev)
+        self.drop = torch.zeros((B, G, S), dtype=torch.int32, device=dev)
+        self.count = torch.zeros((B, G), dtype=torch.int32, device=dev)
+
+    def score(self, q_win, q_pos):
+        se_window_score(self.cache, q_win, q_pos, self.scores, scale=self.scale, mode=SE_SCORE_CAUSAL,
+                        n_query=self.wq, status=self.status)
+
+    def select(self, lo, hi, keep, block_refs=None):
+        se_topk_select(self.cache, self.scores, self.drop, self.count, mode=SE_TOPK_LARGEST, unit=SE_UNIT_SLOT,
+                       k=keep, prune_range=(lo, hi), block_refs=block_refs, emit_dropped=True, status=self.status)
+
+    def evict(self):
+        se_compact_evict(self.cache, self.drop, self.count, mode=SE_COMPACT_EVICT_SLOTS, status=self.status)
+
+    def run(self, q_win, q_pos, lo, hi, keep, block_refs=None):
+        self.score(q_win, q_pos)
+        self.select(lo, hi, keep, block_refs)
+        self.evict()
+
+
 class KaraEvent:
     """Bidirectional scores of the trailing window -> top-K candidates -> Token2Chunk -> trailing compaction."""
 

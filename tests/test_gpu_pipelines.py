@@ -221,3 +221,41 @@ def test_pipeline_quest_with_append_small():
                 if not assert_sets_match_modulo_ties(got[b][g], ref["pages"][b][g], ref["page_scores"][b, g]):
                     np.testing.assert_allclose(out[b, g * r:(g + 1) * r], ref["out"][b, g * r:(g + 1) * r],
                                                atol=2e-3, rtol=0)
+
+
+def test_pipeline_prune_range_then_decode():
+    """Range pruning at the Llama-8B head shape on 2 x 4096 tokens: the GPU's window scores drive both the GPU and
+    the oracle selection (the scores themselves are compared to the oracle's), the pruned cache equals the
+    oracle's bit for bit, and a decode step over it matches."""
+    banner("pipeline range pruning, 2 seqs x 4096")
+    cfg = W.SnapKV("prune", B=2, hq=32, hkv=8, d=128, N=4096, wq=64, protect=0, keep=0, dtype="bf16",
+                   spike_frac=0.04, spike_std=3.0)
+    inp = W.gen_snapkv(cfg, seed=5, threads=8)
+    st = inp["cache"]
+    stack = np.full((2, 8, 4096), -1, np.int32)
+    stack[:, :, :st.slot_stack.shape[2]] = st.slot_stack
+    st.slot_stack = stack
+    rs = np.random.default_rng(5)
+    refs = (rs.random(st.num_blocks) < 0.2).astype(np.int32)
+    lo, hi, keep = 512, 3584, 600
+    dc = to_device(st, cfg.hq)
+    status = status_word()
+    pr = WF.PruneRange(dc, wq=cfg.wq, scale=inp["scale"], status=status)
+    pr.score(storage_tensor(inp["q_win"], "bf16"), i32(inp["q_pos"]))
+    gpu_scores = pr.scores.cpu().numpy()
+    ora_scores = oracle.window_score_causal(st, inp["q_win"], inp["q_pos"], inp["scale"])
+    mass = np.full((2, 8), float(cfg.hq // cfg.hkv * cfg.wq))
+    for b in range(2):
+        assert_scores_close(gpu_scores[b, :, :4096], ora_scores[b, :, :4096], mass[b])
+    pr.select(lo, hi, keep, i32(refs))
+    pr.evict()
+    assert se.se_status_read(status) == 0
+    dropped = oracle.topk_largest(gpu_scores, st, keep, prune_range=(lo, hi), block_refs=refs, emit="dropped")
+    assert [len(x) for row in lists_from(pr.drop, pr.count) for x in row] == [len(x) for row in dropped for x in row]
+    ref = oracle.evict_slots(st, dropped)
+    compare_cache(dc.to_numpy(), ref)
+    out = torch.empty((2, cfg.hq, 128), dtype=torch.float32, device=DEV)
+    se.se_sparse_decode_attn(dc, storage_tensor(inp["q_dec"], "bf16"), out, scale=inp["scale"], status=status)
+    want, _ = oracle.decode_attn(ref, inp["q_dec"], inp["scale"])
+    assert se.se_status_read(status) == 0
+    np.testing.assert_allclose(out.cpu().numpy(), want, atol=2e-3, rtol=0)

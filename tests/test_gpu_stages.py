@@ -545,3 +545,63 @@ def test_page_bounds_refresh_after_compaction_and_quest_over_evicted_cache(windo
     dense, _ = oracle.decode_attn(ref, inp["q_dec"], inp["scale"])
     assert se.se_status_read(status) == 0
     np.testing.assert_allclose(out_all.cpu().numpy(), dense, atol=2e-3, rtol=0)
+
+
+# ------------------------------------------------------------------ range-restricted pruning ----------------------
+@pytest.mark.parametrize("k", [0, 60, 5000])
+def test_topk_range_pruning_and_parallel_slot_eviction_exact(k):
+    """Kept and dropped lists for a position range with busy blocks equal the oracle's on the same fp32 scores
+    (coarse values: many ties), and evicting the dropped slots gives the oracle's cache state bit for bit."""
+    banner(f"range pruning k={k}")
+    inp = snap_inputs(B=2, N=1500, seed=11)
+    st = punch_holes(inp["cache"], 0.004, 6)
+    stack = np.full((2, 2, 1500), -1, np.int32)  # room for every eviction
+    stack[:, :, :st.slot_stack.shape[2]] = st.slot_stack
+    st.slot_stack = stack
+    rs = np.random.default_rng(12)
+    refs = (rs.random(st.num_blocks) < 0.25).astype(np.int32)
+    scores = (rs.random((2, 2, st.pos_map.shape[2])) * 50).round().astype(np.float32)
+    lo, hi = 200, 1300
+    kept = oracle.topk_largest(scores, st, k, prune_range=(lo, hi), block_refs=refs)
+    dropped = oracle.topk_largest(scores, st, k, prune_range=(lo, hi), block_refs=refs, emit="dropped")
+    dc = to_device(st, 8)
+    status = status_word()
+    sc = torch.from_numpy(scores).to(DEV)
+    stride = st.pos_map.shape[2]
+    idx = torch.full((2, 2, stride), -7, dtype=torch.int32, device=DEV)
+    cnt = torch.zeros((2, 2), dtype=torch.int32, device=DEV)
+    refs_d = i32(refs)
+    se.se_topk_select(dc, sc, idx, cnt, mode=se.SE_TOPK_LARGEST, unit=se.SE_UNIT_SLOT, k=k, prune_range=(lo, hi),
+                      block_refs=refs_d, status=status)
+    got = lists_from(idx, cnt)
+    for b in range(2):
+        for g in range(2):
+            assert got[b][g].tolist() == kept[b][g].tolist()
+    se.se_topk_select(dc, sc, idx, cnt, mode=se.SE_TOPK_LARGEST, unit=se.SE_UNIT_SLOT, k=k, prune_range=(lo, hi),
+                      block_refs=refs_d, emit_dropped=True, status=status)
+    got = lists_from(idx, cnt)
+    for b in range(2):
+        for g in range(2):
+            assert got[b][g].tolist() == dropped[b][g].tolist()
+    se.se_compact_evict(dc, idx, cnt, mode=se.SE_COMPACT_EVICT_SLOTS, status=status)
+    assert se.se_status_read(status) == 0
+    compare_cache(dc.to_numpy(), oracle.evict_slots(st, dropped))
+
+
+def test_slot_eviction_reports_bad_entries_and_capacity():
+    banner("slot eviction errors")
+    inp = snap_inputs(B=1, N=300)
+    st = punch_holes(inp["cache"], 0.01, 2)  # fills part of the slot stacks
+    dc = to_device(st, 8)
+    status = status_word()
+    idx, cnt = W.pack_lists([[np.array([7, 5, 9], np.int32), np.array([2], np.int32)]], 4)  # out of order
+    se.se_compact_evict(dc, i32(idx), i32(cnt), mode=se.SE_COMPACT_EVICT_SLOTS, status=status)
+    assert se.se_status_read(status) & se.SE_DEV_INDEX
+    free = [s for s in range(300) if st.pos_map[0, 0, s] >= 0 and s not in (7, 9)][:20]
+    idx, cnt = W.pack_lists([[np.array(free, np.int32), np.array([], np.int32)]], 20)
+    se.se_compact_evict(dc, i32(idx), i32(cnt), mode=se.SE_COMPACT_EVICT_SLOTS, status=status)
+    assert se.se_status_read(status) & se.SE_DEV_CAPACITY
+    d = dc.to_numpy()
+    cap = st.slot_stack.shape[2]
+    assert d["slot_top"][0, 0] == cap  # filled to capacity, nothing beyond
+    assert (d["pos_map"][0, 0, :300] < 0).sum() == cap and d["ctx_len"][0, 0] == 300 - cap
