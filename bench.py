@@ -348,6 +348,41 @@ def setup_c5(se, WF, W, copies, dev):
     return cfg, steps, B * N, alg, None
 
 
+def setup_c6(se, WF, W, copies, dev):
+    """Range-restricted pruning on the Llama-8B cache: window scores, the range's best slots among idle blocks (the
+    dropped list), slot eviction, then a decode step over the pruned cache. Every step on its own pristine copy."""
+    import torch
+
+    cfg = W.C6
+    inp = W.gen_prune(cfg, seed=0, threads=16)
+    base = device_cache(se, cfg, inp["cache"], dev)
+    caches = [base] + [base.clone() for _ in range(copies - 1)]
+    q_win, q_dec = to_dev_bf16(inp["q_win"], dev), to_dev_bf16(inp["q_dec"], dev)
+    q_pos = torch.from_numpy(inp["q_pos"]).to(dev)
+    refs = torch.from_numpy(inp["block_refs"]).to(dev)
+    out = torch.empty((cfg.B, cfg.hq, cfg.d), dtype=torch.float32, device=dev)
+    prs = [WF.PruneRange(c, wq=cfg.wq, scale=inp["scale"]) for c in caches]
+    steps = [[("se_window_score", lambda p=p: p.score(q_win, q_pos)),
+              ("se_topk_select", lambda p=p: p.select(cfg.range_lo, cfg.range_hi, cfg.keep, refs)),
+              ("se_compact_evict", p.evict),
+              ("se_sparse_decode_attn", lambda p=p: se.se_sparse_decode_attn(p.cache, q_dec, out, scale=inp["scale"]))]
+             for p in prs]
+    B, G, N, r, row, page = cfg.B, cfg.hkv, cfg.N, cfg.hq // cfg.hkv, cfg.d * 2, cfg.page
+    # slots each unit frees: the idle slots of the range beyond the kept ones (every slot starts resident)
+    c0 = inp["cache"]
+    slots = np.arange(cfg.range_lo, cfg.range_hi)
+    dropped = sum(max(int((inp["block_refs"][c0.block_table[b, slots // page]] == 0).sum()) - cfg.keep, 0)
+                  for b in range(B)) * G
+    alg = {
+        "se_window_score": {"bytes": B * G * N * row + B * cfg.hq * cfg.wq * row + B * G * N * 4,
+                            "flops": 2.0 * B * G * r * cfg.wq * N * cfg.d},
+        "se_topk_select": {"bytes": B * G * N * 4 * 2 + 2 * B * (N // page) * 4 + dropped * 4},
+        "se_compact_evict": {"bytes": dropped * 4 * 3},
+        "se_sparse_decode_attn": {"bytes": (B * G * N - dropped) * row * 2 + B * G * N * 4 + B * cfg.hq * cfg.d * 6},
+    }
+    return cfg, steps, B * N, alg, None
+
+
 def setup_c4(se, WF, W, copies, dev):
     cfg = W.scaled(W.C4, steps=copies)
     inp = W.gen_h2o(cfg, seed=0, threads=16)
@@ -382,7 +417,7 @@ def setup_c4(se, WF, W, copies, dev):
     return cfg, steps, B * n, alg, None
 
 
-SETUPS = {"c1": setup_c1, "c2": setup_c2, "c3": setup_c3, "c4": setup_c4, "c5": setup_c5}
+SETUPS = {"c1": setup_c1, "c2": setup_c2, "c3": setup_c3, "c4": setup_c4, "c5": setup_c5, "c6": setup_c6}
 
 
 def cpu_baseline(inp, n_seq):

@@ -375,10 +375,13 @@ struct EvictArgs {
   int32_t units, max_slots, slot_cap, idx_stride;
 };
 
-// One workgroup per unit; its list (ascending, distinct) in chunks of kEvictThreads entries. Valid entries are
-// pushed on the slot stack in list order (rank by a block scan); entries past the stack's capacity are not evicted
-// and raise SE_DEV_CAPACITY, invalid ones (not resident, out of range, out of order) raise SE_DEV_INDEX.
+// One workgroup per unit; its list (ascending, distinct) in chunks of kEvictThreads x kEvictPer entries, thread t
+// taking kEvictPer consecutive entries of a chunk (their loads in flight together). Valid entries are pushed on
+// the slot stack in list order (rank by a block scan of per-thread counts); entries past the stack's capacity
+// are not evicted and raise SE_DEV_CAPACITY, invalid ones (not resident, out of range, out of order) raise
+// SE_DEV_INDEX.
 constexpr int kEvictThreads = 256;
+constexpr int kEvictPer = 8;
 __global__ __launch_bounds__(kEvictThreads) void evict_slots_kernel(EvictArgs a) {
   __shared__ int s_wave[kEvictThreads / 64];
   const int unit = blockIdx.x;
@@ -396,37 +399,59 @@ __global__ __launch_bounds__(kEvictThreads) void evict_slots_kernel(EvictArgs a)
   int32_t *st = a.slot_stack + (int64_t)unit * a.slot_cap;
   const int32_t *list = a.idx + (int64_t)unit * a.idx_stride;
   int pushed = 0;  // valid entries of the chunks before this one
-  for (int c0 = 0; c0 < cnt; c0 += kEvictThreads) {
-    const int i = c0 + t;
-    bool valid = false;
-    int s = -1;
-    if (i < cnt) {
-      s = list[i];
-      const int prev = i > 0 ? list[i - 1] : -1;
-      valid = s >= 0 && s < n && s < a.max_slots && prev < s && pos[s] >= 0;
-      if (!valid) raise(a.status, SE_DEV_INDEX);
+  for (int c0 = 0; c0 < cnt; c0 += kEvictThreads * kEvictPer) {
+    const int i0 = c0 + t * kEvictPer;
+    int s[kEvictPer], ps[kEvictPer];
+    const int prev = i0 > 0 && i0 < cnt ? list[i0 - 1] : -1;
+#pragma unroll
+    for (int e = 0; e < kEvictPer; ++e) s[e] = i0 + e < cnt ? list[i0 + e] : -1;
+#pragma unroll
+    for (int e = 0; e < kEvictPer; ++e) {
+      const bool in = s[e] >= 0 && s[e] < n && s[e] < a.max_slots;
+      ps[e] = pos[in ? s[e] : 0];
     }
-    // exclusive rank of this entry among the chunk's valid ones
-    const uint64_t bal = __ballot(valid);
-    const int in_wave = __popcll(bal & ((1ull << lane) - 1ull));
-    if (lane == 0) s_wave[wave] = __popcll(bal);
+    uint32_t valid = 0;
+    int mine = 0;
+#pragma unroll
+    for (int e = 0; e < kEvictPer; ++e) {
+      if (i0 + e >= cnt) continue;
+      const int before_e = e == 0 ? prev : s[e - 1];
+      const bool ok = s[e] >= 0 && s[e] < n && s[e] < a.max_slots && before_e < s[e] && ps[e] >= 0;
+      if (ok) {
+        valid |= 1u << e;
+        ++mine;
+      } else {
+        raise(a.status, SE_DEV_INDEX);
+      }
+    }
+    // exclusive rank of this thread's first valid entry among the chunk's valid ones
+    int incl = mine;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    if (lane == 63) s_wave[wave] = incl;
     __syncthreads();
-    int before = 0, total = 0;
+    int before = incl - mine, total = 0;
 #pragma unroll
     for (int w = 0; w < kEvictThreads / 64; ++w) {
       before += w < wave ? s_wave[w] : 0;
       total += s_wave[w];
     }
     __syncthreads();  // s_wave is rewritten by the next chunk
-    const int at = top + pushed + before + in_wave;
-    if (valid) {
+    int at = top + pushed + before;
+#pragma unroll
+    for (int e = 0; e < kEvictPer; ++e) {
+      if (!((valid >> e) & 1u)) continue;
       if (at < a.slot_cap) {
-        pos[s] = -1;
-        if (a.cum) a.cum[(int64_t)unit * a.max_slots + s] = 0.f;
-        st[at] = s;
+        pos[s[e]] = -1;
+        if (a.cum) a.cum[(int64_t)unit * a.max_slots + s[e]] = 0.f;
+        st[at] = s[e];
       } else {
         raise(a.status, SE_DEV_CAPACITY);
       }
+      ++at;
     }
     pushed += total;
   }

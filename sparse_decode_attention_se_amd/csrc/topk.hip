@@ -141,6 +141,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
   __shared__ uint32_t s_red[kWaves];
   __shared__ int s_res[2];
   __shared__ int s_cnt[PER * kWaves];
+  __shared__ uint32_t s_busy[(PER * kThreads + 31) / 32];  // range pruning: logical pages in busy blocks
   const int unit = blockIdx.x;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   int n = a.n_slots[unit];
@@ -188,22 +189,20 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
   int limit = 0;
   if (a.mode == SE_TOPK_SMALLEST) limit = (int)block_max_u((uint32_t)(mx + 1), s_red) - 1 - a.recent;
 
-  // range-restricted pruning: which items sit in a block with references (block-table loads, then counts)
+  // range-restricted pruning: a bit per logical page of the sequence whose block has references, in LDS (threads
+  // load block-table entries and counts cooperatively); an item looks up its page's bit
   const bool rng = !page_unit && a.range_hi > a.range_lo;
-  uint32_t busy = 0;
-  if (rng && a.refs) {
+  const bool gate = rng && a.refs;
+  if (gate) {
+    const int n_lp = (n + a.page - 1) / a.page;
+    for (int i = t; i < (PER * kThreads + 31) / 32; i += kThreads) s_busy[i] = 0u;
+    __syncthreads();
     const int32_t *btb = a.bt + (int64_t)(unit / a.n_kv) * a.max_blocks;
-    int blk[PER];
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int i = j * kThreads + t;
-      blk[j] = btb[(base + (i < n_items ? i : 0)) / a.page];
+    for (int lp = t; lp < n_lp && lp < PER * kThreads; lp += kThreads) {
+      const int blk = btb[lp];
+      if (blk_ok(blk, a.num_blocks) && a.refs[blk] > 0) atomicOr(&s_busy[lp >> 5], 1u << (lp & 31));
     }
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const bool ok = blk_ok(blk[j], a.num_blocks);
-      if (ok && a.refs[blk[j]] > 0) busy |= 1u << j;
-    }
+    __syncthreads();
   }
 
   // keys of the candidates (tie keys, which order equal scores, are recomputed in the rare tie path below)
@@ -226,7 +225,10 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
         c = p <= limit;
       } else {
         k = base + i >= n - a.protect;
-        if (!k && rng && (p < a.range_lo || p >= a.range_hi || ((busy >> j) & 1u))) k = true;
+        if (!k && rng) {
+          const int lp = (base + i) / a.page;
+          if (p < a.range_lo || p >= a.range_hi || (gate && ((s_busy[lp >> 5] >> (lp & 31)) & 1u))) k = true;
+        }
         c = !k;
       }
     }

@@ -60,6 +60,7 @@ def storage_np_dtype(dtype: str):
 
 # stream tags: one per tensor kind
 TAG_QWIN, TAG_K, TAG_V, TAG_QDEC, TAG_SPIKE, TAG_SHIFT, TAG_ZIPF, TAG_KNEW, TAG_VNEW, TAG_SCORES, TAG_IDX = range(11)
+TAG_BUSY = 11
 
 
 def rng_for(seed: int, tag: int, b: int = 0) -> np.random.Generator:
@@ -142,6 +143,30 @@ class Kara:
 
 
 @dataclass(frozen=True)
+class Prune:
+    """Sparse prefix-cache pruning over an application's position range [range_lo, range_hi): the last ``wq``
+    queries score every causally visible key (SnapKV-style policy), ``keep`` slots of the range are retained among
+    the slots of idle blocks, the rest of the range's idle slots are freed. ``busy_frac`` of the physical blocks
+    carry references (seeded) and are never pruned."""
+
+    name: str
+    B: int
+    hq: int
+    hkv: int
+    d: int
+    N: int
+    wq: int
+    range_lo: int
+    range_hi: int
+    keep: int
+    busy_frac: float
+    dtype: str = "bf16"
+    page: int = 16
+    spike_frac: float = 0.04
+    spike_std: float = 3.0
+
+
+@dataclass(frozen=True)
 class Quest:
     """Query-dependent page selection decode: per-page key min/max bounds, top pages per KV head plus the first
     and last page, then decode attention over the selected pages."""
@@ -191,8 +216,11 @@ C4 = H2O("c4_h2o", B=64, hq=32, hkv=8, d=128, N=8192, budget=8192, recent=256, s
 # Quest decode with its metadata kept current: C3's cache and query, each step first appending a decode token
 C5 = Quest("c5_quest_128k_append", B=2, hq=32, hkv=8, d=128, N=131072, top_pages=256, shift_frac=0.01, shift=2.0,
            steps=16)
+# Range-restricted pruning on C1's cache: 20% of the positions [1024, 31744) kept, 5% of the blocks busy
+C6 = Prune("c6_prune_llama8b", B=8, hq=32, hkv=8, d=128, N=32768, wq=64, range_lo=1024, range_hi=31744, keep=6144,
+           busy_frac=0.05)
 
-FULL = {c.name: c for c in (C0, C1, C2, C3, C4, C5)}
+FULL = {c.name: c for c in (C0, C1, C2, C3, C4, C5, C6)}
 
 
 def scaled(cfg, **kw):
@@ -395,6 +423,20 @@ def gen_kara(cfg: Kara, seed: int = 0, threads: int = 8) -> dict:
     _pmap(fill, range(B), threads)
     return dict(cfg=cfg, cache=cache, q_all=q_all, q_first_pos=q0, k_new=k_new, v_new=v_new,
                 scale=1.0 / math.sqrt(d))
+
+
+def gen_prune(cfg: Prune, seed: int = 0, threads: int = 8) -> dict:
+    """Inputs of range-restricted pruning: the SnapKV-style cache and queries of the same shape (same draws), slot
+    stacks with room for every slot, and per-block reference counts (1 on a seeded ``busy_frac`` of blocks)."""
+    snap = SnapKV(cfg.name, B=cfg.B, hq=cfg.hq, hkv=cfg.hkv, d=cfg.d, N=cfg.N, wq=cfg.wq, protect=0, keep=0,
+                  dtype=cfg.dtype, page=cfg.page, spike_frac=cfg.spike_frac, spike_std=cfg.spike_std)
+    inp = gen_snapkv(snap, seed=seed, threads=threads)
+    c = inp["cache"]
+    stack = np.full((cfg.B, cfg.hkv, c.pos_map.shape[2]), -1, np.int32)
+    stack[:, :, :c.slot_stack.shape[2]] = c.slot_stack
+    c.slot_stack = stack
+    refs = (rng_for(seed, TAG_BUSY, 0).random(c.num_blocks) < cfg.busy_frac).astype(np.int32)
+    return dict(inp, cfg=cfg, block_refs=refs)
 
 
 def gen_quest(cfg: Quest, seed: int = 0, threads: int = 8) -> dict:
