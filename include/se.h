@@ -117,7 +117,7 @@ int32_t se_window_score(const se_cache_t *c, const void *q_win, const int32_t *q
  *  SMALLEST / SLOT: if ctx_len > budget, returns min(k, ctx_len - budget) slots with the lowest score among the
  *    resident slots whose position is <= (max resident position - recent); order (score asc, position desc).
  *    Otherwise count = 0.
- *  Range-restricted pruning (LARGEST / SLOT; SparseEngine page, "How it works", sparse prefix-cache pruning:
+ *  Range-restricted pruning (LARGEST / SLOT; SparseEngine page, "How it differs", sparse prefix-cache pruning:
  *    the application names a 0-based position range [L, R), a scoring policy keeps part of it, the mask applies
  *    to idle blocks only and the resident set becomes R' = (R minus T) plus I): with range_hi > range_lo a
  *    resident slot is a candidate only if range_lo <= position < range_hi and, when block_refs is given (device

@@ -32,7 +32,7 @@ def topk_largest(scores, cache, k: int, *, window: int = 0, protect: int = 0, un
                  forced_ends: bool = False, prune_range=None, block_refs=None, emit: str = "kept"):
     """Per (b, g): the k best candidates plus the always-kept items, as an ascending item list.
 
-    Range-restricted pruning (SparseEngine page, "How it works", sparse prefix-cache pruning: the application
+    Range-restricted pruning (SparseEngine page, "How it differs", sparse prefix-cache pruning: the application
     names a position range [L, R), a scoring policy keeps part of it, the mask applies to idle blocks only, and
     the resident set becomes R' = (R minus T) plus I). With ``prune_range = (L, R)`` (slot unit) a slot is a
     candidate only if its position lies in [L, R) and, when ``block_refs`` (per physical block, > 0 = busy) is

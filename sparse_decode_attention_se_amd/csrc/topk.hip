@@ -9,7 +9,7 @@
 // best by (score, tie key)". Per-wave ballots and one scan over them write the ascending output. Given
 // identical fp32 scores the result is exact.
 //
-// Range-restricted pruning (SparseEngine page, "How it works": the application names a position range, a scoring
+// Range-restricted pruning (SparseEngine page, "How it differs": the application names a position range, a scoring
 // policy keeps part of it, and the mask applies to idle blocks only): with a range, only resident slots whose
 // position lies in it and whose block has no references are candidates; the others are kept. The output can be
 // the dropped candidates instead, the list slot eviction frees.

@@ -56,7 +56,7 @@ class SnapKVEvent:
 
 class PruneRange:
     """Sparse prefix-cache pruning over an application's position range [L, R) (SparseEngine page, "How it
-    works"): causal window scores of the last queries -> the best `keep` slots of the range among idle blocks,
+    differs"): causal window scores of the last queries -> the best `keep` slots of the range among idle blocks,
     every other resident slot kept -> the dropped slots freed onto the slot stacks (no data moves, so blocks with
     references are never written)."""
 
