@@ -420,8 +420,9 @@ def setup_c4(se, WF, W, copies, dev):
 SETUPS = {"c1": setup_c1, "c2": setup_c2, "c3": setup_c3, "c4": setup_c4, "c5": setup_c5, "c6": setup_c6}
 
 
-def cpu_baseline(inp, n_seq):
-    """The oracle (as it stands) on the first n_seq sequences of the SnapKV workload, timed on the host cores."""
+def cpu_baseline(inp, n_seq, min_seconds):
+    """The oracle (as it stands) on the first n_seq sequences of the SnapKV workload, timed on the host cores: the
+    whole event on that sample, repeated until at least min_seconds have passed."""
     import oracle.pipelines as P
     import workloads as W
 
@@ -442,11 +443,17 @@ def cpu_baseline(inp, n_seq):
         dtype=c.dtype, page=c.page)
     sub_inp = dict(inp, cfg=W.scaled(cfg, B=n_seq), cache=sub, q_win=inp["q_win"][:n_seq], q_pos=inp["q_pos"][:n_seq],
                    q_dec=inp["q_dec"][:n_seq])
+    reps = 0
     t0 = time.perf_counter()
-    P.snapkv_event(sub_inp)
-    dt = time.perf_counter() - t0
-    return {"value": n_seq * cfg.N / dt, "unit": "KV tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{n_seq} of {cfg.B} sequences of the same workload (one full event each), {dt:.1f} s"}
+    while True:
+        P.snapkv_event(sub_inp)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    return {"value": reps * n_seq * cfg.N / dt, "unit": "KV tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n_seq} of {cfg.B} sequences of the same workload, the whole event (score, select, compact, "
+                      f"decode) {reps} times, {dt:.1f} s"}
 
 
 def main():
@@ -455,7 +462,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="c1", choices=sorted(SETUPS))
-    ap.add_argument("--cpu-seqs", type=int, default=4)
+    ap.add_argument("--cpu-seqs", type=int, default=8)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle time for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, metavar="MIB", help="run only a plain copy of MIB MiB, --steps times")
     ap.add_argument("--copy-ceiling", action="store_true",
@@ -565,7 +573,7 @@ def main():
         del steps
         torch.cuda.empty_cache()
         log("timing the oracle on the host")
-        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seqs)
+        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seqs, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 
