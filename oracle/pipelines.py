@@ -90,3 +90,22 @@ def h2o_step(inp, cache, step: int):
     evict = topk_smallest(cum, cache, 1, budget=cfg.budget, recent=cfg.recent)
     cache = evict_slots(cache, evict)
     return cache, dict(out=out, evict=evict, slots=slots, cum=cum)
+
+
+def h2o_prefill_chunk(inp, cache, c: int):
+    """Chunk c of H2O's chunked prefill (SparseEngine page, "What it is": H2O keeps cumulative attention scores and
+    evicts physically; "How it works": eviction at the prefill hook). The extent grows by the chunk, whose keys and
+    values the prefill has written; the chunk's queries add their causal weights to the cumulative scores (float32
+    storage); then the lowest scores outside the most recent positions are evicted down to the budget."""
+    cfg = inp["cfg"]
+    lo, hi = c * cfg.chunk, (c + 1) * cfg.chunk
+    cache = cache.copy()
+    if c > 0:
+        cache.n_slots[:] += cfg.chunk
+        cache.ctx_len[:] += cfg.chunk
+    q_pos = np.broadcast_to(np.arange(lo, hi, dtype=np.int32), (cfg.B, cfg.chunk))
+    s = window_score_causal(cache, inp["q_all"][:, :, lo:hi], q_pos, inp["scale"])
+    cache.cum_score = (cache.cum_score.astype(np.float64) + s).astype(np.float32)
+    evict = topk_smallest(cache.cum_score, cache, cfg.chunk, budget=cfg.budget, recent=cfg.recent)
+    cache = evict_slots(cache, evict)
+    return cache, dict(scores=s, evict=evict, cum=cache.cum_score)

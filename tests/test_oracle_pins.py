@@ -344,6 +344,40 @@ def test_range_pruning_without_refs_or_with_full_range_is_plain_top_k():
             assert plain[b][g].tolist() == ranged[b][g].tolist()
 
 
+# ------------------------------------------------------------------ H2O chunked prefill -----------------------------
+def test_h2o_prefill_chunks_match_brute_force():
+    """Three prefill chunks on a tiny cache against a loop written from the rule: every chunk query's softmax over
+    the resident keys it may see is added to the keys' cumulative scores, then while ctx > budget the lowest score
+    among positions <= newest - recent is evicted (ties to the higher position)."""
+    cfg = W.H2OPrefill("tiny", B=1, hq=4, hkv=2, d=8, N=24, chunk=8, budget=10, recent=3, dtype="f32", page=4)
+    inp = W.gen_h2o_prefill(cfg, seed=4, threads=1)
+    st = inp["cache"]
+    K = W.gather_contiguous(st, "k").astype(np.float64)  # [B][hkv][N][d] by position (slot = position here)
+    q = inp["q_all"].astype(np.float64)
+    cum = np.zeros((2, 24))
+    alive = np.ones((2, 24), bool)
+    for c in range(3):
+        st, info = P.h2o_prefill_chunk(inp, st, c)
+        hi = 8 * (c + 1)
+        for g in range(2):
+            for h in (2 * g, 2 * g + 1):
+                for t in range(8 * c, hi):
+                    vis = [j for j in range(t + 1) if alive[g, j]]
+                    x = np.array([q[0, h, t] @ K[0, g, j] for j in vis]) * inp["scale"]
+                    p = np.exp(x - x.max())
+                    cum[g, vis] += p / p.sum()
+            while alive[g, :hi].sum() > cfg.budget:
+                newest = max(j for j in range(hi) if alive[g, j])
+                elig = [j for j in range(hi) if alive[g, j] and j <= newest - cfg.recent]
+                worst = min(elig, key=lambda j: (np.float32(cum[g, j]), -j))
+                alive[g, worst] = False
+                cum[g, worst] = 0.0
+            got = st.pos_map[0, g, :hi] >= 0
+            assert got.tolist() == alive[g, :hi].tolist(), (c, g)
+            np.testing.assert_allclose(st.cum_score[0, g, :hi][got], cum[g, :hi][got], rtol=1e-6)
+        assert st.ctx_len[0].tolist() == [min(hi, cfg.budget)] * 2
+
+
 # ------------------------------------------------------------------ page bounds -----------------------------------
 def test_page_bound_is_an_upper_bound_and_tight_for_equal_keys():
     cfg = W.Quest("tiny", B=2, hq=4, hkv=2, d=16, N=100, top_pages=2, shift_frac=0.1, shift=2.0)

@@ -61,6 +61,7 @@ def storage_np_dtype(dtype: str):
 # stream tags: one per tensor kind
 TAG_QWIN, TAG_K, TAG_V, TAG_QDEC, TAG_SPIKE, TAG_SHIFT, TAG_ZIPF, TAG_KNEW, TAG_VNEW, TAG_SCORES, TAG_IDX = range(11)
 TAG_BUSY = 11
+TAG_QALL = 12
 
 
 def rng_for(seed: int, tag: int, b: int = 0) -> np.random.Generator:
@@ -167,6 +168,28 @@ class Prune:
 
 
 @dataclass(frozen=True)
+class H2OPrefill:
+    """H2O eviction during chunked prefill: when a chunk of ``chunk`` prompt tokens has been written, the causal
+    attention weights of the chunk's queries are added to the cumulative score of every key they see, and while
+    the context exceeds ``budget`` the lowest-score tokens outside the most recent ``recent`` positions are
+    evicted (their slots freed)."""
+
+    name: str
+    B: int
+    hq: int
+    hkv: int
+    d: int
+    N: int
+    chunk: int
+    budget: int
+    recent: int
+    dtype: str = "bf16"
+    page: int = 16
+    spike_frac: float = 0.04
+    spike_std: float = 3.0
+
+
+@dataclass(frozen=True)
 class Quest:
     """Query-dependent page selection decode: per-page key min/max bounds, top pages per KV head plus the first
     and last page, then decode attention over the selected pages."""
@@ -220,7 +243,10 @@ C5 = Quest("c5_quest_128k_append", B=2, hq=32, hkv=8, d=128, N=131072, top_pages
 C6 = Prune("c6_prune_llama8b", B=8, hq=32, hkv=8, d=128, N=32768, wq=64, range_lo=1024, range_hi=31744, keep=6144,
            busy_frac=0.05)
 
-FULL = {c.name: c for c in (C0, C1, C2, C3, C4, C5, C6)}
+# H2O's chunked-prefill eviction on the Llama-8B head shape: 8 x 8192 prompt tokens in chunks of 512, budget 2048
+C7 = H2OPrefill("c7_h2o_prefill_llama8b", B=8, hq=32, hkv=8, d=128, N=8192, chunk=512, budget=2048, recent=256)
+
+FULL = {c.name: c for c in (C0, C1, C2, C3, C4, C5, C6, C7)}
 
 
 def scaled(cfg, **kw):
@@ -437,6 +463,27 @@ def gen_prune(cfg: Prune, seed: int = 0, threads: int = 8) -> dict:
     c.slot_stack = stack
     refs = (rng_for(seed, TAG_BUSY, 0).random(c.num_blocks) < cfg.busy_frac).astype(np.int32)
     return dict(inp, cfg=cfg, block_refs=refs)
+
+
+def gen_h2o_prefill(cfg: H2OPrefill, seed: int = 0, threads: int = 8) -> dict:
+    """Inputs of H2O's chunked-prefill eviction: the prompt's keys and values laid out in the cache as the prefill
+    writes them (the SnapKV-style draws of the same shape), the query of every prompt token ``q_all``
+    [B][hq][N][d] (a stream of its own), cumulative scores at 0 and slot stacks with room for every slot. The
+    cache's extent is the first chunk; each later chunk's tokens are already in place past it."""
+    snap = SnapKV(cfg.name, B=cfg.B, hq=cfg.hq, hkv=cfg.hkv, d=cfg.d, N=cfg.N, wq=1, protect=0, keep=0,
+                  dtype=cfg.dtype, page=cfg.page, spike_frac=cfg.spike_frac, spike_std=cfg.spike_std)
+    inp = gen_snapkv(snap, seed=seed, threads=threads)
+    c = inp["cache"]
+    S = c.pos_map.shape[2]
+    stack = np.full((cfg.B, cfg.hkv, S), -1, np.int32)
+    stack[:, :, :c.slot_stack.shape[2]] = c.slot_stack
+    c.slot_stack = stack
+    c.cum_score = np.zeros((cfg.B, cfg.hkv, S), np.float32)
+    c.n_slots[:] = cfg.chunk
+    c.ctx_len[:] = cfg.chunk
+    q_all = np.stack(_pmap(lambda b: to_storage(_normal(seed, TAG_QALL, b, (cfg.hq, cfg.N, cfg.d)), cfg.dtype),
+                           range(cfg.B), threads))
+    return dict(cfg=cfg, cache=c, q_all=q_all, q_dec=inp["q_dec"], scale=inp["scale"])
 
 
 def gen_quest(cfg: Quest, seed: int = 0, threads: int = 8) -> dict:
