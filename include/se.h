@@ -86,6 +86,9 @@ typedef struct se_cache {
  *     window - protect slots. q_win [B][n_q][window][d] holds the queries of the window's tokens; q_pos is
  *     unused. Each query row is a softmax over the resident region slots (no mask);
  *     scores[(b*n_kv+g)*score_stride + (s - w0)] for s in the region.
+ * accumulate != 0: every score is added to the value the output already holds instead of replacing it, so with
+ *   scores = cum_score (score_stride = max_blocks * page) the causal scores of a prefill chunk's queries are added to
+ *   H2O's cumulative scores (SparseEngine page, "What it is": H2O keeps cumulative attention scores).
  * Arithmetic: products of stored values exact, fp32 accumulation, fp32 output.
  * Errors: SE_ERR_UNSUPPORTED when num_blocks * n_kv * page >= 2^31 (pool rows are addressed with 32-bit ids).
  */
@@ -97,6 +100,7 @@ typedef struct {
   int32_t window;       /* BIDIR only */
   int32_t protect;      /* BIDIR only: trailing window slots outside the key region */
   int32_t score_stride; /* floats between consecutive (b, g) rows of scores */
+  int32_t accumulate;   /* 0: scores = the window's scores; else scores += them */
 } se_window_params_t;
 
 size_t se_window_score_workspace_size(const se_cache_t *c, const se_window_params_t *p);

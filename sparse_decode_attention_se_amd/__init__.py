@@ -123,12 +123,12 @@ class DeviceCache:
 
 # ---------------------------------------------------------------------------------------------------------------
 def se_window_score(cache, q_win, q_pos, scores, *, scale, mode, n_query, window=0, protect=0, score_stride=None,
-                    status=None, stream=None):
+                    accumulate=False, status=None, stream=None):
     lib = _lib.load()
     st, sp = _stream(stream)
     c = cache.desc()
     p = _lib.se_window_params_t(scale, mode, n_query, window, protect,
-                                score_stride if score_stride is not None else scores.shape[-1])
+                                score_stride if score_stride is not None else scores.shape[-1], int(accumulate))
     nb = lib.se_window_score_workspace_size(C.byref(c), C.byref(p))
     ws = _workspace(nb, cache.device, stream)
     _check("se_window_score", lib.se_window_score(C.byref(c), _ptr(q_win), _ptr(q_pos), C.byref(p), _ptr(scores),

@@ -33,7 +33,7 @@ class se_cache_t(C.Structure):
 
 class se_window_params_t(C.Structure):
     _fields_ = [("scale", C.c_float), ("mode", I32), ("n_query", I32), ("window", I32), ("protect", I32),
-                ("score_stride", I32)]
+                ("score_stride", I32), ("accumulate", I32)]
 
 
 class se_topk_params_t(C.Structure):

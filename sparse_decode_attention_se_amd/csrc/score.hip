@@ -37,8 +37,12 @@ struct ScoreArgs {
   int32_t page_shift;  // log2(page) when page is a power of two, else -1
   int32_t nrg, nkc, kc, key_span;
   int32_t rpg;  // query rows per row group (workgroup)
+  int32_t accumulate;  // add the scores to what the output holds (H2O cumulative scores)
   float scale_log2;
 };
+
+// the one write of a key's score (added to the output's value when accumulating)
+SE_DEV void put_score(const ScoreArgs &a, int64_t at, float v) { a.scores[at] = a.accumulate ? a.scores[at] + v : v; }
 
 // key range of a unit: [k0, k1) slots; scores index = slot - k0
 SE_DEV void key_range(const ScoreArgs &a, int unit, int &k0, int &k1, int &n) {
@@ -385,7 +389,7 @@ __global__ __launch_bounds__(NW * 64, 2) void window_stream(ScoreArgs a) {
       const int key = sidx * kSub + (j >> 2) * 16 + (lane >> 4) * 4 + (j & 3);
       if (c0 + key < c1) {
         const int idx = c0 + key - k0;
-        if (a.nrg == 1) a.scores[(int64_t)unit * a.score_stride + idx] = tot;
+        if (a.nrg == 1) put_score(a, (int64_t)unit * a.score_stride + idx, tot);
         else a.colpart[((int64_t)unit * a.nrg + rg) * a.key_span + idx] = tot;
       }
     }
@@ -552,7 +556,7 @@ __global__ __launch_bounds__(kValuRows) void colsum_valu(ScoreArgs a) {
       sum += __builtin_amdgcn_exp2f(row_dot<DTYPE, D>(qr, kr) * a.scale_log2 - s_mlog[r]);
     }
     int idx = key - k0;
-    if (a.nrg == 1) a.scores[(int64_t)unit * a.score_stride + idx] = sum;
+    if (a.nrg == 1) put_score(a, (int64_t)unit * a.score_stride + idx, sum);
     else a.colpart[((int64_t)unit * a.nrg + rg) * a.key_span + idx] = sum;
   }
 }
@@ -565,7 +569,7 @@ __global__ void colsum_reduce(ScoreArgs a) {
   for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < k1 - k0; j += gridDim.x * blockDim.x) {
     float s = 0.f;
     for (int r = 0; r < a.nrg; ++r) s += a.colpart[((int64_t)unit * a.nrg + r) * a.key_span + j];
-    a.scores[(int64_t)unit * a.score_stride + j] = s;
+    put_score(a, (int64_t)unit * a.score_stride + j, s);
   }
 }
 
@@ -676,6 +680,7 @@ extern "C" int32_t se_window_score(const se_cache_t *c, const void *q_win, const
   a.key_span = pl.key_span;
   a.rpg = pl.rpg;
   a.scale_log2 = p->scale * 1.4426950408889634f;
+  a.accumulate = p->accumulate != 0;
   const int units = c->B * c->n_kv;
   const dim3 grid(pl.nkc, pl.nrg, units);
   hipStream_t st = (hipStream_t)stream;

@@ -85,6 +85,36 @@ class PruneRange:
         self.evict()
 
 
+class H2OPrefillChunk:
+    """H2O at the end of a prefill chunk (SparseEngine page, "What it is" and "How it works"): the chunk's queries
+    add their causal attention weights to the cumulative scores -> the lowest scores outside the most recent
+    positions are chosen while the context exceeds the budget -> their slots are freed. The chunk's keys and
+    values are written by the prefill before this runs."""
+
+    def __init__(self, cache, *, chunk, budget, recent, scale, status=None):
+        B, G, S, d = _dims(cache)
+        self.cache, self.chunk, self.budget, self.recent, self.scale, self.status = (
+            cache, chunk, budget, recent, scale, status)
+        self.evict = torch.zeros((B, G, chunk), dtype=torch.int32, device=cache.device)
+        self.count = torch.zeros((B, G), dtype=torch.int32, device=cache.device)
+
+    def score(self, q_chunk, q_pos):
+        se_window_score(self.cache, q_chunk, q_pos, self.cache.cum_score, scale=self.scale, mode=SE_SCORE_CAUSAL,
+                        n_query=self.chunk, accumulate=True, status=self.status)
+
+    def select(self):
+        se_topk_select(self.cache, self.cache.cum_score, self.evict, self.count, mode=SE_TOPK_SMALLEST,
+                       unit=SE_UNIT_SLOT, k=self.chunk, budget=self.budget, recent=self.recent, status=self.status)
+
+    def evict_slots(self):
+        se_compact_evict(self.cache, self.evict, self.count, mode=SE_COMPACT_EVICT_SLOTS, status=self.status)
+
+    def run(self, q_chunk, q_pos):
+        self.score(q_chunk, q_pos)
+        self.select()
+        self.evict_slots()
+
+
 class KaraEvent:
     """Bidirectional scores of the trailing window -> top-K candidates -> Token2Chunk -> trailing compaction."""
 

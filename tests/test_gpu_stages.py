@@ -605,3 +605,27 @@ def test_slot_eviction_reports_bad_entries_and_capacity():
     cap = st.slot_stack.shape[2]
     assert d["slot_top"][0, 0] == cap  # filled to capacity, nothing beyond
     assert (d["pos_map"][0, 0, :300] < 0).sum() == cap and d["ctx_len"][0, 0] == 300 - cap
+
+
+# ------------------------------------------------------------------ accumulating window scores --------------------
+@pytest.mark.parametrize("dtype,d,wq,N", [("bf16", 128, 64, 1300), ("bf16", 128, 128, 900), ("f32", 64, 32, 700)])
+def test_window_score_accumulates_into_existing_scores(dtype, d, wq, N):
+    # wq = 128 at group size 4: 512 query rows, so rows are split over workgroups and summed by the reduction
+    banner(f"accumulating window scores {dtype} wq={wq} N={N}")
+    inp = snap_inputs(d=d, dtype=dtype, N=N, wq=wq, protect=8, keep=16)
+    st = punch_holes(inp["cache"], 0.01, 3)
+    ora = oracle.window_score_causal(st, inp["q_win"], inp["q_pos"], inp["scale"])
+    dc = to_device(st, 8)
+    S = st.pos_map.shape[2]
+    init = np.random.default_rng(7).random((2, 2, S)).astype(np.float32)
+    scores = torch.from_numpy(init.copy()).to(DEV)
+    status = status_word()
+    se.se_window_score(dc, storage_tensor(inp["q_win"], dtype), i32(inp["q_pos"]), scores, scale=inp["scale"],
+                       mode=se.SE_SCORE_CAUSAL, n_query=wq, accumulate=True, status=status)
+    assert se.se_status_read(status) == 0
+    got = scores.cpu().numpy().astype(np.float64) - init
+    mass = np.full((2, 2), 4.0 * wq)
+    for b in range(2):
+        tol = 1e-3 * np.abs(ora[b, :, :N]) + 1e-6 * mass[b][:, None] + 2e-7  # + the fp32 add to init < 1
+        assert np.all(np.abs(got[b, :, :N] - ora[b, :, :N]) <= tol)
+    np.testing.assert_array_equal(scores.cpu().numpy()[:, :, N:], init[:, :, N:])  # past n_slots: untouched
