@@ -1,6 +1,6 @@
 """Benchmark of the sparse-KV hot path on one MI355X. Prints one JSON line.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c1|c2|c3|c4] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c1|...|c7] [--no-cpu-baseline]
 
 A step is one pass of the workload's hot path over its batch, with every input resident in HBM before timing:
 
@@ -14,9 +14,15 @@ A step is one pass of the workload's hot path over its batch, with every input r
      decode attention over the 258 selected pages (page metadata built once, outside the step).
   c4 H2O continuous eviction on 64 sequences at the 8192-token budget: append, decode with cumulative scores,
      bottom-1 eviction outside the 256 most recent positions (the step loop of the workload itself).
+  c5 c3's Quest decode with its cache maintenance: append the decode token, refresh the metadata of its page,
+     then page bounds, page choice and decode.
+  c6 range-restricted pruning on c1's cache: window scores, the best 20% of positions [1024, 31744) among idle
+     blocks (5% of blocks busy), the rest of the range freed, one decode step over the pruned cache.
+  c7 H2O's chunked-prefill eviction on 8 x 8192 prompt tokens: per chunk of 512, the chunk's causal scores added
+     to the cumulative scores, bottom-K down to the 2048 budget, slots freed (one step = the whole prefill).
 
 Steps that change the cache destructively, or whose working set would stay in the 256 MB Infinity Cache between
-steps, run each on a pristine copy of the cache (c1, c2, c3). Per-call times come from HIP events on the stream
+steps, run each on a pristine copy of the cache (c1, c2, c3, c5, c6, c7). Per-call times come from HIP events on the stream
 the calls are launched on.
 """
 import argparse
@@ -529,8 +535,8 @@ def main():
                                 args.write_factor))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the hot path is per (sequence, KV head) and shards with no exchange; "
-              "multi-GPU runs are not part of this build", file=sys.stderr)
+        print("bench.py measures one GPU only: every step works within one (sequence, KV head) and shards across GPUs "
+              "by sequence or KV head with no exchange, so one GPU's throughput is the figure", file=sys.stderr)
         sys.exit(2)
     copies = args.steps + args.warmup
     if copies > 64:

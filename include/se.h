@@ -46,7 +46,7 @@ enum {
   SE_ERR_DTYPE = 3,       /* unsupported element type or head dimension */
   SE_ERR_PARAM = 4,       /* a parameter outside its domain */
   SE_ERR_WORKSPACE = 5,   /* workspace missing or too small */
-  SE_ERR_UNSUPPORTED = 6, /* a combination this build does not implement */
+  SE_ERR_UNSUPPORTED = 6, /* a combination the library does not implement */
   SE_ERR_HIP = 7,         /* a HIP runtime call failed */
   /* device status bits, OR-ed into *status */
   SE_DEV_INDEX = 1 << 8,    /* an index list entry out of range, unsorted, duplicated or not resident */
