@@ -148,3 +148,50 @@ def cache_append(cache, k_new: np.ndarray, v_new: np.ndarray, pos: np.ndarray):
             out.pos_map[b, g, s] = pos[b]
             out.ctx_len[b, g] += 1
     return out, slots
+
+
+def cache_append_chunk(cache, k_new: np.ndarray, v_new: np.ndarray, pos0: np.ndarray):
+    """Write T tokens per (b, g) at its high-water slots [n_slots, n_slots + T) (SparseEngine page, "How it
+    works": the cache manager allocates and writes; a prefill chunk arrives as a block of tokens): k_new, v_new
+    [B][n_kv][T][d] stored values, positions pos0[b] + t. The slot stacks are left alone. The logical blocks the
+    new slots need are taken from the free stack in order of sequence, then logical block.
+
+    All or nothing: if a slot range or the free stack cannot take the whole call, nothing changes and
+    CapacityError is raised.
+    """
+    out = cache.copy()
+    B, n_kv = cache.n_slots.shape
+    T = k_new.shape[2]
+    page = cache.page
+    max_slots = cache.pos_map.shape[2]
+    need = []
+    for b in range(B):
+        blocks = set()
+        for g in range(n_kv):
+            n = int(cache.n_slots[b, g])
+            if n + T > max_slots:
+                raise CapacityError("sequence is at its maximum number of slots")
+            blocks |= {s // page for s in range(n, n + T)}
+        need.append(sorted(lb for lb in blocks if cache.block_table[b, lb] < 0))
+    if sum(len(m) for m in need) > int(cache.free_top[0]):
+        raise CapacityError("free stack exhausted")
+    top = int(cache.free_top[0])
+    for b in range(B):
+        for lb in need[b]:
+            top -= 1
+            out.block_table[b, lb] = cache.free_blocks[top]
+    out.free_top[0] = top
+    for b in range(B):
+        for g in range(n_kv):
+            n = int(cache.n_slots[b, g])
+            for t in range(T):
+                s = n + t
+                blk = out.block_table[b, s // page]
+                out.k_pool[blk, g, s % page] = k_new[b, g, t]
+                out.v_pool[blk, g, s % page] = v_new[b, g, t]
+                out.pos_map[b, g, s] = pos0[b] + t
+                if out.cum_score is not None:
+                    out.cum_score[b, g, s] = 0.0
+            out.n_slots[b, g] = n + T
+            out.ctx_len[b, g] += T
+    return out

@@ -378,6 +378,49 @@ def test_h2o_prefill_chunks_match_brute_force():
         assert st.ctx_len[0].tolist() == [min(hi, cfg.budget)] * 2
 
 
+def _h2o_tiny(N, T, seed=6):
+    cfg = W.H2O("tiny", B=2, hq=4, hkv=2, d=4, N=N, budget=N + T, recent=2, steps=T, zipf=1.1, dtype="f32", page=4)
+    return W.gen_h2o(cfg, seed=seed, threads=1)
+
+
+@pytest.mark.parametrize("N,T", [(8, 9), (10, 3), (11, 1)])
+def test_chunk_append_equals_single_appends_by_position(N, T):
+    """A chunk of T tokens gives, position by position, the cache T single-token appends give (no free slots to
+    reuse): same K/V per position, maps, counts; the blocks taken are the same set."""
+    inp = _h2o_tiny(N, T)
+    c = inp["cache"]
+    kc = np.ascontiguousarray(inp["k_new"].transpose(1, 2, 0, 3))  # [B][n_kv][T][d]
+    vc = np.ascontiguousarray(inp["v_new"].transpose(1, 2, 0, 3))
+    one = c
+    for t in range(T):
+        one, _ = oracle.cache_append(one, inp["k_new"][t], inp["v_new"][t], np.full((2,), N + t, np.int32))
+    chunk = oracle.cache_append_chunk(c, kc, vc, np.full((2,), N, np.int32))
+    for f in ("n_slots", "ctx_len", "pos_map", "free_top"):
+        np.testing.assert_array_equal(getattr(chunk, f), getattr(one, f))
+    np.testing.assert_array_equal(W.gather_contiguous(chunk, "k"), W.gather_contiguous(one, "k"))
+    np.testing.assert_array_equal(W.gather_contiguous(chunk, "v"), W.gather_contiguous(one, "v"))
+    used = lambda x: sorted(int(v) for v in x.block_table.ravel() if v >= 0)
+    assert used(chunk) == used(one)
+    top = int(chunk.free_top[0])
+    assert sorted(used(chunk) + [int(x) for x in chunk.free_blocks[:top]]) == list(range(c.num_blocks))
+
+
+def test_chunk_append_pops_in_sequence_then_block_order_and_is_all_or_nothing():
+    inp = _h2o_tiny(8, 9)  # each sequence needs logical blocks 2, 3 and 4
+    c = inp["cache"]
+    kc = np.ascontiguousarray(inp["k_new"].transpose(1, 2, 0, 3))
+    vc = np.ascontiguousarray(inp["v_new"].transpose(1, 2, 0, 3))
+    top = int(c.free_top[0])
+    out = oracle.cache_append_chunk(c, kc, vc, np.full((2,), 8, np.int32))
+    popped = [int(c.free_blocks[top - 1 - i]) for i in range(6)]
+    assert [int(out.block_table[b, lb]) for b in range(2) for lb in (2, 3, 4)] == popped
+    short = c.copy()
+    short.free_top[0] = 5  # one block short
+    with pytest.raises(oracle.cache_ops.CapacityError):
+        oracle.cache_append_chunk(short, kc, vc, np.full((2,), 8, np.int32))
+    np.testing.assert_array_equal(short.n_slots, c.n_slots)
+
+
 # ------------------------------------------------------------------ page bounds -----------------------------------
 def test_page_bound_is_an_upper_bound_and_tight_for_equal_keys():
     cfg = W.Quest("tiny", B=2, hq=4, hkv=2, d=16, N=100, top_pages=2, shift_frac=0.1, shift=2.0)
