@@ -62,13 +62,14 @@ CALL_KERNELS = {
     "se_token2chunk": ["t2c_kernel"],
     "se_compact_evict": ["gather_move", "gather_extents", "gather_push", "evict_slots_kernel"],
     "se_cache_append": ["append_kernel"],
+    "se_cache_append_chunk": ["chunk_plan", "chunk_write"],
     "se_page_bounds": ["pages_score", "pages_build"],
     "se_page_bounds_refresh": ["pages_refresh"],
     "se_sparse_decode_attn": ["decode_partial", "decode_merge", "decode_cum", "decode_unit"],
 }
 CALL_SOURCES = {
     "se_window_score": "score.hip", "se_topk_select": "topk.hip", "se_token2chunk": "t2c.hip",
-    "se_compact_evict": "compact.hip", "se_cache_append": "compact.hip", "se_page_bounds": "pages.hip",
+    "se_compact_evict": "compact.hip", "se_cache_append": "compact.hip", "se_cache_append_chunk": "compact.hip", "se_page_bounds": "pages.hip",
     "se_page_bounds_refresh": "pages.hip",
     "se_sparse_decode_attn": "decode.hip",
 }
@@ -390,10 +391,9 @@ def setup_c6(se, WF, W, copies, dev):
 
 
 def setup_c7(se, WF, W, copies, dev):
-    """H2O's chunked-prefill eviction on 8 x 8192 prompt tokens: per chunk of 512, the chunk's causal window scores
-    added to the cumulative scores, the bottom slots outside the recent 256 chosen down to the 2048 budget, and
-    their slots freed. One step is the whole prefill (16 chunks) on its own pristine copy. Between chunks the
-    harness advances the extent over the chunk the prefill has written (two small torch additions)."""
+    """H2O's chunked-prefill eviction on 8 x 8192 prompt tokens: per chunk of 512, the chunk appended, its causal
+    window scores added to the cumulative scores, the bottom slots outside the recent 256 chosen down to the 2048
+    budget, and their slots freed. One step is the whole prefill (16 chunks) on its own pristine copy."""
     import torch
 
     cfg = W.C7
@@ -405,10 +405,11 @@ def setup_c7(se, WF, W, copies, dev):
             for c in range(n_chunks)]
     q_pos = [torch.arange(c * cfg.chunk, (c + 1) * cfg.chunk, dtype=torch.int32, device=dev).repeat(cfg.B, 1)
              for c in range(n_chunks)]
-
-    def advance(cache):
-        cache.n_slots += cfg.chunk
-        cache.ctx_len += cfg.chunk
+    k_ch = [to_dev_bf16(np.ascontiguousarray(inp["k_all"][:, :, c * cfg.chunk:(c + 1) * cfg.chunk]), dev)
+            for c in range(n_chunks)]
+    v_ch = [to_dev_bf16(np.ascontiguousarray(inp["v_all"][:, :, c * cfg.chunk:(c + 1) * cfg.chunk]), dev)
+            for c in range(n_chunks)]
+    pos0 = [torch.full((cfg.B,), c * cfg.chunk, dtype=torch.int32, device=dev) for c in range(n_chunks)]
 
     steps = []
     for c in caches:
@@ -416,7 +417,7 @@ def setup_c7(se, WF, W, copies, dev):
         step = []
         for k in range(n_chunks):
             if k > 0:
-                step.append(("prefill extent (harness)", lambda c=c: advance(c)))
+                step.append(("se_cache_append_chunk", lambda pf=pf, k=k: pf.append(k_ch[k], v_ch[k], pos0[k])))
             step += [("se_window_score", lambda pf=pf, k=k: pf.score(q_ch[k], q_pos[k])),
                      ("se_topk_select", pf.select), ("se_compact_evict", pf.evict_slots)]
         steps.append(step)
@@ -427,7 +428,7 @@ def setup_c7(se, WF, W, copies, dev):
     slots = [(k + 1) * cfg.chunk for k in range(n_chunks)]
     evicted = [max(keys[k] - cfg.budget, 0) for k in range(n_chunks)]
     alg = {
-        "prefill extent (harness)": {"bytes": (n_chunks - 1) * B * G * 4 * 4},
+        "se_cache_append_chunk": {"bytes": (n_chunks - 1) * B * G * cfg.chunk * (2 * row * 2 + 4)},
         "se_window_score": {"bytes": sum(B * G * (kk * row + s_ * 8) + B * cfg.hq * cfg.chunk * row
                                          for kk, s_ in zip(keys, slots)),
                             "flops": sum(2.0 * B * G * r * cfg.chunk * kk * d for kk in keys)},

@@ -15,7 +15,7 @@ Each driver calls the oracle steps in the order the method takes them:
 """
 import numpy as np
 
-from .cache_ops import cache_append, compact_gather, evict_slots
+from .cache_ops import cache_append, cache_append_chunk, compact_gather, evict_slots
 from .decode import decode_attn
 from .pages import page_bounds_build, page_bounds_score
 from .score import window_score_bidir, window_score_causal
@@ -94,15 +94,17 @@ def h2o_step(inp, cache, step: int):
 
 def h2o_prefill_chunk(inp, cache, c: int):
     """Chunk c of H2O's chunked prefill (SparseEngine page, "What it is": H2O keeps cumulative attention scores and
-    evicts physically; "How it works": eviction at the prefill hook). The extent grows by the chunk, whose keys and
-    values the prefill has written; the chunk's queries add their causal weights to the cumulative scores (float32
-    storage); then the lowest scores outside the most recent positions are evicted down to the budget."""
+    evicts physically; "How it works": eviction at the prefill hook). The chunk's keys and values are appended
+    (the first chunk is already in the cache); the chunk's queries add their causal weights to the cumulative
+    scores (float32 storage); then the lowest scores outside the most recent positions are evicted down to the
+    budget."""
     cfg = inp["cfg"]
     lo, hi = c * cfg.chunk, (c + 1) * cfg.chunk
-    cache = cache.copy()
     if c > 0:
-        cache.n_slots[:] += cfg.chunk
-        cache.ctx_len[:] += cfg.chunk
+        cache = cache_append_chunk(cache, inp["k_all"][:, :, lo:hi], inp["v_all"][:, :, lo:hi],
+                                   np.full((cfg.B,), lo, np.int32))
+    else:
+        cache = cache.copy()
     q_pos = np.broadcast_to(np.arange(lo, hi, dtype=np.int32), (cfg.B, cfg.chunk))
     s = window_score_causal(cache, inp["q_all"][:, :, lo:hi], q_pos, inp["scale"])
     cache.cum_score = (cache.cum_score.astype(np.float64) + s).astype(np.float32)

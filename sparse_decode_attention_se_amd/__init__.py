@@ -16,7 +16,7 @@ from ._lib import (SE_COMPACT_EVICT_SLOTS, SE_COMPACT_GATHER, SE_DEV_CAPACITY, S
 
 __all__ = [
     "DeviceCache", "SEError", "se_window_score", "se_topk_select", "se_token2chunk", "se_compact_evict",
-    "se_cache_append", "se_page_bounds", "se_page_bounds_refresh", "se_sparse_decode_attn", "se_status_read",
+    "se_cache_append", "se_cache_append_chunk", "se_page_bounds", "se_page_bounds_refresh", "se_sparse_decode_attn", "se_status_read",
     "se_version", "SE_SCORE_CAUSAL", "SE_SCORE_BIDIR", "SE_TOPK_LARGEST", "SE_TOPK_SMALLEST", "SE_UNIT_SLOT",
     "SE_UNIT_PAGE", "SE_COMPACT_GATHER", "SE_COMPACT_EVICT_SLOTS", "SE_PAGES_BUILD", "SE_PAGES_SCORE",
     "SE_REFRESH_LAST_PAGE", "SE_REFRESH_FROM_PAGE", "SE_DEV_INDEX", "SE_DEV_CAPACITY",
@@ -179,6 +179,18 @@ def se_cache_append(cache, k_new, v_new, pos, *, status=None, stream=None):
     c = cache.desc()
     _check("se_cache_append", lib.se_cache_append(C.byref(c), _ptr(k_new), _ptr(v_new), _ptr(pos), _ptr(status),
                                                   None, 0, sp))
+
+
+def se_cache_append_chunk(cache, k_new, v_new, pos0, *, status=None, stream=None):
+    """Append T tokens per (sequence, KV head) at the high-water slots; k_new, v_new [B][n_kv][T][d], pos0 [B]."""
+    lib = _lib.load()
+    st, sp = _stream(stream)
+    c = cache.desc()
+    T = int(k_new.shape[2])
+    nb = lib.se_cache_append_chunk_workspace_size(C.byref(c), T)
+    ws = _workspace(nb, cache.device, stream)
+    _check("se_cache_append_chunk", lib.se_cache_append_chunk(C.byref(c), _ptr(k_new), _ptr(v_new), _ptr(pos0), T,
+                                                              _ptr(status), _ptr(ws), nb, sp))
 
 
 def se_page_bounds(cache, op, q=None, page_scores=None, *, status=None, stream=None):

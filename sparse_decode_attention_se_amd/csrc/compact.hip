@@ -4,6 +4,7 @@
 //   se_compact_evict  GATHER       in-place keep-prefix compaction + block freeing
 //                     EVICT_SLOTS  slot eviction onto the per-head slot stack
 //   se_cache_append   one decode token per (sequence, KV head)
+//   se_cache_append_chunk  T tokens per (sequence, KV head) at the high-water slots (a prefill chunk)
 //
 // In-place gather hazard. Output j of a (sequence, head) unit copies slot s_j to slot w0 + j, with s ascending
 // and s_j >= w0 + j. Writing slot w0 + j destroys a source only if some output k < j reads s_k = w0 + j. Let
@@ -598,6 +599,133 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
   }
 }
 
+// ---- chunk append: T tokens per unit at the high-water slots -------------------------------------------------------
+struct ChunkArgs {
+  char *k, *v;
+  int32_t *bt, *pos, *ctx, *n_slots, *free_blocks, *free_top;
+  float *cum;
+  const char *k_new, *v_new;
+  const int32_t *pos0;
+  int32_t *flag;  // workspace: 1 when chunk_plan committed the call
+  int32_t *status;
+  int32_t B, n_kv, page, max_blocks, num_blocks, row_bytes, T;
+};
+
+// One workgroup: per sequence the logical blocks its heads' new slots [n, n + T) need beyond the allocated prefix;
+// pops for them in (sequence, logical block) order; then, only if everything fits, the commit: block table,
+// free-stack top, n_slots and ctx_len. chunk_write copies the rows afterwards.
+__global__ __launch_bounds__(kAppendThreads) void chunk_plan(ChunkArgs a) {
+  __shared__ int s_first[kAppendMaxSeq], s_last[kAppendMaxSeq], s_alloc[kAppendMaxSeq], s_need[kAppendMaxSeq];
+  __shared__ int s_before[kAppendMaxSeq];
+  __shared__ int s_scan[kAppendThreads];
+  __shared__ int s_fail;
+  const int units = a.B * a.n_kv;
+  const int cap = a.max_blocks * a.page;
+  if (threadIdx.x == 0) {
+    s_fail = 0;
+    *a.flag = 0;
+  }
+  for (int b = threadIdx.x; b < a.B; b += kAppendThreads) {
+    s_first[b] = -1;
+    s_last[b] = -1;
+    s_alloc[b] = 0x7fffffff;
+  }
+  __syncthreads();
+  // blocks below the largest n / page of a sequence's heads hold resident slots, so they are allocated; its new
+  // slots reach block (largest n + T - 1) / page
+  for (int unit = threadIdx.x; unit < units; unit += kAppendThreads) {
+    const int n = a.n_slots[unit], b = unit / a.n_kv;
+    if (n < 0 || n + a.T > cap) {
+      atomicOr(&s_fail, 1);
+      continue;
+    }
+    atomicMax(&s_first[b], n / a.page);
+    atomicMax(&s_last[b], (n + a.T - 1) / a.page);
+  }
+  __syncthreads();
+  // the first unallocated table entry in each sequence's window [first, last] (allocated entries form a
+  // prefix), over all (sequence, entry) pairs at once; a window spans at most `span` entries
+  const int span = (a.T + a.page - 1) / a.page + 1;
+  for (int x = threadIdx.x; x < a.B * span; x += kAppendThreads) {
+    const int b = x / span, j = s_first[b] + x % span;
+    if (s_first[b] < 0 || j > s_last[b]) continue;
+    const int cur = a.bt[(int64_t)b * a.max_blocks + j];
+    if (cur >= a.num_blocks) atomicOr(&s_fail, 2);
+    if (cur < 0) atomicMin(&s_alloc[b], j);
+  }
+  __syncthreads();
+  for (int b = threadIdx.x; b < a.B; b += kAppendThreads) {
+    const int l = s_last[b], al = s_alloc[b];
+    s_need[b] = (l >= 0 && al <= l) ? l - al + 1 : 0;
+  }
+  __syncthreads();
+  const int top0 = *a.free_top;
+  if (top0 < 0 || top0 > a.num_blocks) {
+    if (threadIdx.x == 0) raise(a.status, SE_DEV_CAPACITY);
+    return;
+  }
+  // exclusive scan of the needs over sequences: sequence b pops free_blocks[top0 - 1 - (s_before[b] + i)]
+  int carry = 0;
+  for (int base = 0; base < a.B; base += kAppendThreads) {
+    const int b = base + threadIdx.x;
+    const int v = b < a.B ? s_need[b] : 0;
+    s_scan[threadIdx.x] = v;
+    __syncthreads();
+    for (int off = 1; off < kAppendThreads; off <<= 1) {
+      const int x = threadIdx.x >= off ? s_scan[threadIdx.x - off] : 0;
+      __syncthreads();
+      s_scan[threadIdx.x] += x;
+      __syncthreads();
+    }
+    if (b < a.B) s_before[b] = carry + s_scan[threadIdx.x] - v;
+    carry += s_scan[kAppendThreads - 1];
+    __syncthreads();  // s_scan is rewritten by the next chunk of sequences
+  }
+  if (threadIdx.x == 0 && carry > top0) s_fail |= 1;
+  __syncthreads();
+  if (s_fail) {
+    if (threadIdx.x == 0) raise(a.status, (s_fail & 2) ? SE_DEV_INDEX : SE_DEV_CAPACITY);
+    return;  // all or nothing: nothing was written
+  }
+  for (int b = threadIdx.x; b < a.B; b += kAppendThreads)
+    for (int i = 0; i < s_need[b]; ++i)
+      a.bt[(int64_t)b * a.max_blocks + s_alloc[b] + i] = a.free_blocks[top0 - 1 - (s_before[b] + i)];
+  for (int unit = threadIdx.x; unit < units; unit += kAppendThreads) {
+    a.n_slots[unit] += a.T;
+    a.ctx[unit] += a.T;
+  }
+  if (threadIdx.x == 0) {
+    *a.free_top = top0 - carry;
+    *a.flag = 1;
+  }
+}
+
+// grid (row tiles, units): copy the chunk's K/V rows of a unit into its new slots n_slots - T + t, set positions
+// pos0[b] + t and clear cumulative scores; nothing when chunk_plan did not commit
+constexpr int kChunkThreads = 256;
+__global__ __launch_bounds__(kChunkThreads) void chunk_write(ChunkArgs a) {
+  if (*a.flag != 1) return;
+  const int unit = blockIdx.y, b = unit / a.n_kv, g = unit % a.n_kv;
+  const int cap = a.max_blocks * a.page;
+  const int cpr = a.row_bytes / 16;
+  const int rows = kChunkThreads / cpr;  // rows per workgroup
+  const int base = a.n_slots[unit] - a.T;
+  const int32_t *bt = a.bt + (int64_t)b * a.max_blocks;
+  const int t = blockIdx.x * rows + threadIdx.x / cpr, ch = threadIdx.x % cpr;
+  if (t >= a.T) return;
+  const int slot = base + t;
+  const int blk = bt[slot / a.page];
+  const int64_t src = ((int64_t)unit * a.T + t) * a.row_bytes + ch * 16;
+  const int64_t dst = (((int64_t)blk * a.n_kv + g) * a.page + slot % a.page) * a.row_bytes + ch * 16;
+  const u32x4 kr = ld16(a.k_new + src), vr = ld16(a.v_new + src);
+  st16(a.k + dst, kr);
+  st16(a.v + dst, vr);
+  if (ch == 0) {
+    a.pos[(int64_t)unit * cap + slot] = a.pos0[b] + t;
+    if (a.cum) a.cum[(int64_t)unit * cap + slot] = 0.f;
+  }
+}
+
 }  // namespace
 }  // namespace se
 
@@ -724,5 +852,51 @@ extern "C" int32_t se_cache_append(se_cache_t *c, const void *k_new, const void 
   a.slot_cap = c->slot_cap;
   a.row_bytes = row_bytes;
   hipLaunchKernelGGL(se::append_kernel, dim3(1), dim3(se::kAppendThreads), 0, (hipStream_t)stream, a);
+  return se_host::launch_status();
+}
+
+extern "C" size_t se_cache_append_chunk_workspace_size(const se_cache_t *c, int32_t T) {
+  (void)T;
+  if (se_host::check_cache(c) != SE_OK) return 0;
+  return se_host::align_up(sizeof(int32_t));
+}
+
+extern "C" int32_t se_cache_append_chunk(se_cache_t *c, const void *k_new, const void *v_new, const int32_t *pos0,
+                                         int32_t T, int32_t *status, void *ws, size_t ws_bytes,
+                                         se_stream_t stream) {
+  int32_t rc = se_host::check_cache(c);
+  if (rc != SE_OK) return rc;
+  if (!k_new || !v_new || !pos0 || !c->free_blocks || !c->free_top) return SE_ERR_NULL;
+  if (T < 1 || (long long)T > (long long)c->max_blocks * c->page) return SE_ERR_PARAM;
+  if (c->B > se::kAppendMaxSeq) return SE_ERR_UNSUPPORTED;
+  const int row_bytes = c->d * se::elem_bytes(c->dtype);
+  if (row_bytes % 16 != 0 || row_bytes > 512) return SE_ERR_DTYPE;
+  if (!ws || ws_bytes < se_cache_append_chunk_workspace_size(c, T)) return SE_ERR_WORKSPACE;
+  se::ChunkArgs a;
+  a.k = (char *)c->k_pool;
+  a.v = (char *)c->v_pool;
+  a.bt = c->block_table;
+  a.pos = c->pos_map;
+  a.ctx = c->ctx_len;
+  a.n_slots = c->n_slots;
+  a.free_blocks = c->free_blocks;
+  a.free_top = c->free_top;
+  a.cum = c->cum_score;
+  a.k_new = (const char *)k_new;
+  a.v_new = (const char *)v_new;
+  a.pos0 = pos0;
+  a.flag = (int32_t *)ws;
+  a.status = status;
+  a.B = c->B;
+  a.n_kv = c->n_kv;
+  a.page = c->page;
+  a.max_blocks = c->max_blocks;
+  a.num_blocks = c->num_blocks;
+  a.row_bytes = row_bytes;
+  a.T = T;
+  hipStream_t st = (hipStream_t)stream;
+  hipLaunchKernelGGL(se::chunk_plan, dim3(1), dim3(se::kAppendThreads), 0, st, a);
+  const int rows = se::kChunkThreads / (row_bytes / 16);
+  hipLaunchKernelGGL(se::chunk_write, dim3((T + rows - 1) / rows, c->B * c->n_kv), dim3(se::kChunkThreads), 0, st, a);
   return se_host::launch_status();
 }

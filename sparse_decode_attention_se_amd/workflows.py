@@ -10,7 +10,7 @@ import torch
 
 from . import (SE_COMPACT_EVICT_SLOTS, SE_COMPACT_GATHER, SE_PAGES_BUILD, SE_PAGES_SCORE, SE_REFRESH_FROM_PAGE,
                SE_REFRESH_LAST_PAGE, SE_SCORE_BIDIR, SE_SCORE_CAUSAL, SE_TOPK_LARGEST, SE_TOPK_SMALLEST, SE_UNIT_PAGE,
-               SE_UNIT_SLOT, se_cache_append, se_compact_evict, se_page_bounds, se_page_bounds_refresh,
+               SE_UNIT_SLOT, se_cache_append, se_cache_append_chunk, se_compact_evict, se_page_bounds, se_page_bounds_refresh,
                se_sparse_decode_attn, se_token2chunk, se_topk_select, se_window_score)
 
 
@@ -86,10 +86,10 @@ class PruneRange:
 
 
 class H2OPrefillChunk:
-    """H2O at the end of a prefill chunk (SparseEngine page, "What it is" and "How it works"): the chunk's queries
-    add their causal attention weights to the cumulative scores -> the lowest scores outside the most recent
-    positions are chosen while the context exceeds the budget -> their slots are freed. The chunk's keys and
-    values are written by the prefill before this runs."""
+    """H2O at the end of a prefill chunk (SparseEngine page, "What it is" and "How it works"): the chunk's keys and
+    values are appended -> its queries add their causal attention weights to the cumulative scores -> the lowest
+    scores outside the most recent positions are chosen while the context exceeds the budget -> their slots are
+    freed."""
 
     def __init__(self, cache, *, chunk, budget, recent, scale, status=None):
         B, G, S, d = _dims(cache)
@@ -97,6 +97,9 @@ class H2OPrefillChunk:
             cache, chunk, budget, recent, scale, status)
         self.evict = torch.zeros((B, G, chunk), dtype=torch.int32, device=cache.device)
         self.count = torch.zeros((B, G), dtype=torch.int32, device=cache.device)
+
+    def append(self, k_chunk, v_chunk, pos0):
+        se_cache_append_chunk(self.cache, k_chunk, v_chunk, pos0, status=self.status)
 
     def score(self, q_chunk, q_pos):
         se_window_score(self.cache, q_chunk, q_pos, self.cache.cum_score, scale=self.scale, mode=SE_SCORE_CAUSAL,
@@ -109,7 +112,9 @@ class H2OPrefillChunk:
     def evict_slots(self):
         se_compact_evict(self.cache, self.evict, self.count, mode=SE_COMPACT_EVICT_SLOTS, status=self.status)
 
-    def run(self, q_chunk, q_pos):
+    def run(self, q_chunk, q_pos, k_chunk=None, v_chunk=None, pos0=None):
+        if k_chunk is not None:  # the first chunk of a prompt may already be in the cache
+            self.append(k_chunk, v_chunk, pos0)
         self.score(q_chunk, q_pos)
         self.select()
         self.evict_slots()

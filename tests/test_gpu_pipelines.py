@@ -262,9 +262,9 @@ def test_pipeline_prune_range_then_decode():
 
 
 def test_pipeline_h2o_prefill_chunks():
-    """H2O's chunked-prefill eviction, 2 seqs x 1536 tokens in chunks of 512 with a budget of 700: cumulative scores
-    and evicted sets follow the oracle chunk by chunk (sets modulo near ties; a unit that diverges is not compared
-    further), and the context ends at the budget."""
+    """H2O's chunked-prefill eviction, 2 seqs x 1536 tokens in chunks of 512 with a budget of 700: each chunk is
+    appended, cumulative scores and evicted sets follow the oracle chunk by chunk (sets modulo near ties; a unit
+    that diverges is not compared further), and the context ends at the budget."""
     banner("pipeline H2O prefill, 2 seqs x 1536, 3 chunks")
     cfg = W.scaled(W.C7, B=2, N=1536, budget=700, recent=64)
     inp = W.gen_h2o_prefill(cfg, seed=3, threads=4)
@@ -276,12 +276,14 @@ def test_pipeline_h2o_prefill_chunks():
     r = cfg.hq // cfg.hkv
     diverged = np.zeros((cfg.B, cfg.hkv), bool)
     for c in range(cfg.N // cfg.chunk):
-        if c > 0:  # the prefill has written the chunk's K/V past the extent: advance it (harness plumbing)
-            dc.n_slots += cfg.chunk
-            dc.ctx_len += cfg.chunk
         lo, hi = c * cfg.chunk, (c + 1) * cfg.chunk
         q_pos = np.broadcast_to(np.arange(lo, hi, dtype=np.int32), (cfg.B, cfg.chunk)).copy()
-        pf.run(storage_tensor(np.ascontiguousarray(inp["q_all"][:, :, lo:hi]), "bf16"), i32(q_pos))
+        kv = {}
+        if c > 0:
+            kv = dict(k_chunk=storage_tensor(np.ascontiguousarray(inp["k_all"][:, :, lo:hi]), "bf16"),
+                      v_chunk=storage_tensor(np.ascontiguousarray(inp["v_all"][:, :, lo:hi]), "bf16"),
+                      pos0=i32(np.full((cfg.B,), lo, np.int32)))
+        pf.run(storage_tensor(np.ascontiguousarray(inp["q_all"][:, :, lo:hi]), "bf16"), i32(q_pos), **kv)
         st, info = P.h2o_prefill_chunk(inp, st, c)
         assert se.se_status_read(status) == 0
         cum = dc.cum_score.cpu().numpy()
@@ -299,4 +301,5 @@ def test_pipeline_h2o_prefill_chunks():
                     diverged[b, g] = True
     d = dc.to_numpy()
     assert np.all(d["ctx_len"] == cfg.budget) and np.all(d["n_slots"] == cfg.N)
+    assert d["free_top"][0] == st.free_top[0] and np.array_equal(d["block_table"], st.block_table)
     assert diverged.mean() <= 0.5

@@ -629,3 +629,38 @@ def test_window_score_accumulates_into_existing_scores(dtype, d, wq, N):
         tol = 1e-3 * np.abs(ora[b, :, :N]) + 1e-6 * mass[b][:, None] + 2e-7  # + the fp32 add to init < 1
         assert np.all(np.abs(got[b, :, :N] - ora[b, :, :N]) <= tol)
     np.testing.assert_array_equal(scores.cpu().numpy()[:, :, N:], init[:, :, N:])  # past n_slots: untouched
+
+
+# ------------------------------------------------------------------ chunk append ----------------------------------
+@pytest.mark.parametrize("N,T,dtype,d", [(47, 512, "bf16", 128), (64, 37, "bf16", 128), (100, 1, "bf16", 128),
+                                         (30, 70, "f32", 64)])
+def test_chunk_append_bit_exact(N, T, dtype, d):
+    banner(f"chunk append N={N} T={T} {dtype}")
+    cfg = W.H2O("t", B=3, hq=8, hkv=2, d=d, N=N, budget=N + T, recent=4, steps=T, zipf=1.1, dtype=dtype)
+    inp = W.gen_h2o(cfg, seed=8, threads=2)
+    st = punch_holes(inp["cache"], 0.02, 4)  # freed slots stay on the stacks: a chunk goes to the high-water mark
+    kc = np.ascontiguousarray(inp["k_new"].transpose(1, 2, 0, 3))
+    vc = np.ascontiguousarray(inp["v_new"].transpose(1, 2, 0, 3))
+    pos0 = np.full((3,), N, np.int32)
+    ref = oracle.cache_append_chunk(st, kc, vc, pos0)
+    dc = to_device(st, 8)
+    status = status_word()
+    se.se_cache_append_chunk(dc, storage_tensor(kc, dtype), storage_tensor(vc, dtype), i32(pos0), status=status)
+    assert se.se_status_read(status) == 0
+    compare_cache(dc.to_numpy(), ref)
+
+
+def test_chunk_append_is_all_or_nothing():
+    banner("chunk append capacity")
+    cfg = W.H2O("t", B=2, hq=8, hkv=2, d=128, N=40, budget=100, recent=4, steps=60, zipf=1.1)
+    inp = W.gen_h2o(cfg, seed=9, threads=2)
+    st = inp["cache"]
+    st.free_top[0] = 1  # each sequence needs more than one new block
+    before = st.copy()
+    kc = np.ascontiguousarray(inp["k_new"].transpose(1, 2, 0, 3))
+    dc = to_device(st, 8)
+    status = status_word()
+    se.se_cache_append_chunk(dc, storage_tensor(kc, "bf16"), storage_tensor(kc, "bf16"),
+                             i32(np.full((2,), 40, np.int32)), status=status)
+    assert se.se_status_read(status) & se.SE_DEV_CAPACITY
+    compare_cache(dc.to_numpy(), before)

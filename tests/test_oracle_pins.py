@@ -352,7 +352,7 @@ def test_h2o_prefill_chunks_match_brute_force():
     cfg = W.H2OPrefill("tiny", B=1, hq=4, hkv=2, d=8, N=24, chunk=8, budget=10, recent=3, dtype="f32", page=4)
     inp = W.gen_h2o_prefill(cfg, seed=4, threads=1)
     st = inp["cache"]
-    K = W.gather_contiguous(st, "k").astype(np.float64)  # [B][hkv][N][d] by position (slot = position here)
+    K = inp["k_all"].astype(np.float64)  # [B][hkv][N][d] by position
     q = inp["q_all"].astype(np.float64)
     cum = np.zeros((2, 24))
     alive = np.ones((2, 24), bool)

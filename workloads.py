@@ -466,24 +466,27 @@ def gen_prune(cfg: Prune, seed: int = 0, threads: int = 8) -> dict:
 
 
 def gen_h2o_prefill(cfg: H2OPrefill, seed: int = 0, threads: int = 8) -> dict:
-    """Inputs of H2O's chunked-prefill eviction: the prompt's keys and values laid out in the cache as the prefill
-    writes them (the SnapKV-style draws of the same shape), the query of every prompt token ``q_all``
-    [B][hq][N][d] (a stream of its own), cumulative scores at 0 and slot stacks with room for every slot. The
-    cache's extent is the first chunk; each later chunk's tokens are already in place past it."""
+    """Inputs of H2O's chunked-prefill eviction: the keys and values of every prompt token ``k_all``, ``v_all``
+    [B][n_kv][N][d] (the SnapKV-style draws of the same shape), the query of every prompt token ``q_all``
+    [B][hq][N][d] (a stream of its own), and a cache holding the first chunk, with the other blocks on the free
+    stack, cumulative scores at 0 and slot stacks with room for every slot. Later chunks are appended."""
     snap = SnapKV(cfg.name, B=cfg.B, hq=cfg.hq, hkv=cfg.hkv, d=cfg.d, N=cfg.N, wq=1, protect=0, keep=0,
                   dtype=cfg.dtype, page=cfg.page, spike_frac=cfg.spike_frac, spike_std=cfg.spike_std)
     inp = gen_snapkv(snap, seed=seed, threads=threads)
-    c = inp["cache"]
-    S = c.pos_map.shape[2]
-    stack = np.full((cfg.B, cfg.hkv, S), -1, np.int32)
-    stack[:, :, :c.slot_stack.shape[2]] = c.slot_stack
-    c.slot_stack = stack
-    c.cum_score = np.zeros((cfg.B, cfg.hkv, S), np.float32)
-    c.n_slots[:] = cfg.chunk
-    c.ctx_len[:] = cfg.chunk
+    full = inp["cache"]
+    k_all = np.ascontiguousarray(gather_contiguous(full, "k")[:, :, :cfg.N])
+    v_all = np.ascontiguousarray(gather_contiguous(full, "v")[:, :, :cfg.N])
+    max_blocks = -(-cfg.N // cfg.page)
+    S = max_blocks * cfg.page
+    c = empty_cache(cfg.B, cfg.hkv, cfg.d, cfg.page, max_blocks, cfg.B * max_blocks, cfg.dtype, slot_cap=S,
+                    with_cum=True)
+    nb = layout_initial(c, cfg.chunk)
+    for b in range(cfg.B):
+        write_sequence(c.k_pool, nb, b, k_all[b, :, :cfg.chunk], cfg.page)
+        write_sequence(c.v_pool, nb, b, v_all[b, :, :cfg.chunk], cfg.page)
     q_all = np.stack(_pmap(lambda b: to_storage(_normal(seed, TAG_QALL, b, (cfg.hq, cfg.N, cfg.d)), cfg.dtype),
                            range(cfg.B), threads))
-    return dict(cfg=cfg, cache=c, q_all=q_all, q_dec=inp["q_dec"], scale=inp["scale"])
+    return dict(cfg=cfg, cache=c, k_all=k_all, v_all=v_all, q_all=q_all, q_dec=inp["q_dec"], scale=inp["scale"])
 
 
 def gen_quest(cfg: Quest, seed: int = 0, threads: int = 8) -> dict:
