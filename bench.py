@@ -392,8 +392,8 @@ def setup_c6(se, WF, W, copies, dev):
 
 def setup_c7(se, WF, W, copies, dev):
     """H2O's chunked-prefill eviction on 8 x 8192 prompt tokens: per chunk of 512, the chunk appended, its causal
-    window scores added to the cumulative scores, the bottom slots outside the recent 256 chosen down to the 2048
-    budget, and their slots freed. One step is the whole prefill (16 chunks) on its own pristine copy."""
+    window scores added to the cumulative scores, the recent 256 plus the best 1792 others kept (the 2048 budget)
+    and the cache compacted in place. One step is the whole prefill (16 chunks) on its own pristine copy."""
     import torch
 
     cfg = W.C7
@@ -419,21 +419,21 @@ def setup_c7(se, WF, W, copies, dev):
             if k > 0:
                 step.append(("se_cache_append_chunk", lambda pf=pf, k=k: pf.append(k_ch[k], v_ch[k], pos0[k])))
             step += [("se_window_score", lambda pf=pf, k=k: pf.score(q_ch[k], q_pos[k])),
-                     ("se_topk_select", pf.select), ("se_compact_evict", pf.evict_slots)]
+                     ("se_topk_select", pf.select), ("se_compact_evict", pf.compact)]
         steps.append(step)
     B, G, r, row, d = cfg.B, cfg.hkv, cfg.hq // cfg.hkv, cfg.d * 2, cfg.d
-    # per chunk k: the resident keys its queries see (the budget's survivors, then the chunk), the slots scanned
-    # (every slot up to the extent) and the slots evicted
+    # per chunk k: the keys its queries see (the budget's survivors, then the chunk; the cache is dense), and the
+    # rows compaction keeps
     keys = [min(k * cfg.chunk, cfg.budget) + cfg.chunk for k in range(n_chunks)]
-    slots = [(k + 1) * cfg.chunk for k in range(n_chunks)]
-    evicted = [max(keys[k] - cfg.budget, 0) for k in range(n_chunks)]
+    slots = keys
+    kept = [min(kk, cfg.budget) for kk in keys]
     alg = {
         "se_cache_append_chunk": {"bytes": (n_chunks - 1) * B * G * cfg.chunk * (2 * row * 2 + 4)},
         "se_window_score": {"bytes": sum(B * G * (kk * row + s_ * 8) + B * cfg.hq * cfg.chunk * row
                                          for kk, s_ in zip(keys, slots)),
                             "flops": sum(2.0 * B * G * r * cfg.chunk * kk * d for kk in keys)},
-        "se_topk_select": {"bytes": sum(B * G * (s_ * 8 + e * 4) for s_, e in zip(slots, evicted))},
-        "se_compact_evict": {"bytes": sum(B * G * e * 12 for e in evicted)},
+        "se_topk_select": {"bytes": sum(B * G * (s_ * 8 + kp * 4) for s_, kp in zip(slots, kept))},
+        "se_compact_evict": {"bytes": sum(B * G * kp * (2 * row * 2 + 8) for kp in kept)},
     }
     return cfg, steps, B * cfg.N, alg, None
 

@@ -96,8 +96,9 @@ def h2o_prefill_chunk(inp, cache, c: int):
     """Chunk c of H2O's chunked prefill (SparseEngine page, "What it is": H2O keeps cumulative attention scores and
     evicts physically; "How it works": eviction at the prefill hook). The chunk's keys and values are appended
     (the first chunk is already in the cache); the chunk's queries add their causal weights to the cumulative
-    scores (float32 storage); then the lowest scores outside the most recent positions are evicted down to the
-    budget."""
+    scores (float32 storage); then, while the context exceeds the budget, the lowest scores outside the most recent
+    positions are evicted. The cache stays dense (compacted after every chunk), so its last ``recent`` slots are
+    the most recent positions and H2O's choice is: keep those, plus the best ``budget - recent`` of the rest."""
     cfg = inp["cfg"]
     lo, hi = c * cfg.chunk, (c + 1) * cfg.chunk
     if c > 0:
@@ -108,6 +109,7 @@ def h2o_prefill_chunk(inp, cache, c: int):
     q_pos = np.broadcast_to(np.arange(lo, hi, dtype=np.int32), (cfg.B, cfg.chunk))
     s = window_score_causal(cache, inp["q_all"][:, :, lo:hi], q_pos, inp["scale"])
     cache.cum_score = (cache.cum_score.astype(np.float64) + s).astype(np.float32)
-    evict = topk_smallest(cache.cum_score, cache, cfg.chunk, budget=cfg.budget, recent=cfg.recent)
-    cache = evict_slots(cache, evict)
-    return cache, dict(scores=s, evict=evict, cum=cache.cum_score)
+    keep = topk_largest(cache.cum_score, cache, cfg.budget - cfg.recent, protect=cfg.recent)
+    cum = cache.cum_score.copy()
+    cache = compact_gather(cache, keep)
+    return cache, dict(scores=s, keep=keep, cum=cum)

@@ -87,15 +87,16 @@ class PruneRange:
 
 class H2OPrefillChunk:
     """H2O at the end of a prefill chunk (SparseEngine page, "What it is" and "How it works"): the chunk's keys and
-    values are appended -> its queries add their causal attention weights to the cumulative scores -> the lowest
-    scores outside the most recent positions are chosen while the context exceeds the budget -> their slots are
-    freed."""
+    values are appended -> its queries add their causal attention weights to the cumulative scores -> while the
+    context exceeds the budget, the lowest scores outside the most recent positions go. The cache is compacted
+    after every chunk, so its last `recent` slots are the most recent positions and the choice is: keep them plus
+    the best `budget - recent` of the rest (in-place gather), leaving the next chunk a dense cache to score."""
 
     def __init__(self, cache, *, chunk, budget, recent, scale, status=None):
         B, G, S, d = _dims(cache)
         self.cache, self.chunk, self.budget, self.recent, self.scale, self.status = (
             cache, chunk, budget, recent, scale, status)
-        self.evict = torch.zeros((B, G, chunk), dtype=torch.int32, device=cache.device)
+        self.keep = torch.zeros((B, G, budget), dtype=torch.int32, device=cache.device)
         self.count = torch.zeros((B, G), dtype=torch.int32, device=cache.device)
 
     def append(self, k_chunk, v_chunk, pos0):
@@ -106,18 +107,18 @@ class H2OPrefillChunk:
                         n_query=self.chunk, accumulate=True, status=self.status)
 
     def select(self):
-        se_topk_select(self.cache, self.cache.cum_score, self.evict, self.count, mode=SE_TOPK_SMALLEST,
-                       unit=SE_UNIT_SLOT, k=self.chunk, budget=self.budget, recent=self.recent, status=self.status)
+        se_topk_select(self.cache, self.cache.cum_score, self.keep, self.count, mode=SE_TOPK_LARGEST,
+                       unit=SE_UNIT_SLOT, k=self.budget - self.recent, protect=self.recent, status=self.status)
 
-    def evict_slots(self):
-        se_compact_evict(self.cache, self.evict, self.count, mode=SE_COMPACT_EVICT_SLOTS, status=self.status)
+    def compact(self):
+        se_compact_evict(self.cache, self.keep, self.count, mode=SE_COMPACT_GATHER, status=self.status)
 
     def run(self, q_chunk, q_pos, k_chunk=None, v_chunk=None, pos0=None):
         if k_chunk is not None:  # the first chunk of a prompt may already be in the cache
             self.append(k_chunk, v_chunk, pos0)
         self.score(q_chunk, q_pos)
         self.select()
-        self.evict_slots()
+        self.compact()
 
 
 class KaraEvent:

@@ -348,7 +348,8 @@ def test_range_pruning_without_refs_or_with_full_range_is_plain_top_k():
 def test_h2o_prefill_chunks_match_brute_force():
     """Three prefill chunks on a tiny cache against a loop written from the rule: every chunk query's softmax over
     the resident keys it may see is added to the keys' cumulative scores, then while ctx > budget the lowest score
-    among positions <= newest - recent is evicted (ties to the higher position)."""
+    among positions <= newest - recent is evicted (ties to the higher position). Compared by position: the
+    resident set and the cumulative scores."""
     cfg = W.H2OPrefill("tiny", B=1, hq=4, hkv=2, d=8, N=24, chunk=8, budget=10, recent=3, dtype="f32", page=4)
     inp = W.gen_h2o_prefill(cfg, seed=4, threads=1)
     st = inp["cache"]
@@ -372,9 +373,10 @@ def test_h2o_prefill_chunks_match_brute_force():
                 worst = min(elig, key=lambda j: (np.float32(cum[g, j]), -j))
                 alive[g, worst] = False
                 cum[g, worst] = 0.0
-            got = st.pos_map[0, g, :hi] >= 0
-            assert got.tolist() == alive[g, :hi].tolist(), (c, g)
-            np.testing.assert_allclose(st.cum_score[0, g, :hi][got], cum[g, :hi][got], rtol=1e-6)
+            n = int(st.n_slots[0, g])
+            pos = st.pos_map[0, g, :n]
+            assert sorted(pos.tolist()) == [j for j in range(hi) if alive[g, j]], (c, g)
+            np.testing.assert_allclose(st.cum_score[0, g, :n], cum[g, pos], rtol=1e-6)
         assert st.ctx_len[0].tolist() == [min(hi, cfg.budget)] * 2
 
 
