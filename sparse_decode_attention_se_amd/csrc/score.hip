@@ -44,6 +44,22 @@ struct ScoreArgs {
 // the one write of a key's score (added to the output's value when accumulating)
 SE_DEV void put_score(const ScoreArgs &a, int64_t at, float v) { a.scores[at] = a.accumulate ? a.scores[at] + v : v; }
 
+// Workgroups go to the 8 XCDs round-robin by linear id, and each XCD has its own L2. The (chunk, row group, unit)
+// item of a workgroup is remapped so that every XCD takes a contiguous range of items: the row groups of a unit,
+// which stream the same keys, run on one XCD close together in time and share its L2.
+SE_DEV void xcd_item(int &chunk, int &rg, int &unit) {
+  constexpr int kXcd = 8;
+  const int nx = gridDim.x, ny = gridDim.y;
+  const int total = nx * ny * gridDim.z;
+  const int lin = blockIdx.x + nx * (blockIdx.y + ny * blockIdx.z);
+  const int per = total / kXcd, rem = total % kXcd;
+  const int x = lin % kXcd, i = lin / kXcd;
+  const int item = (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + i;
+  chunk = item % nx;
+  rg = (item / nx) % ny;
+  unit = item / (nx * ny);
+}
+
 // key range of a unit: [k0, k1) slots; scores index = slot - k0
 SE_DEV void key_range(const ScoreArgs &a, int unit, int &k0, int &k1, int &n) {
   n = a.n_slots[unit];
@@ -256,7 +272,8 @@ SE_DEV float row16_reduce_scatter(float (&v)[16]) {
 template <int PASS, int NW, bool POW2>
 __global__ __launch_bounds__(NW * 64, 2) void window_stream(ScoreArgs a) {
   constexpr int NT = NW * 64;
-  const int unit = blockIdx.z, rg = blockIdx.y, chunk = blockIdx.x;
+  int chunk, rg, unit;
+  xcd_item(chunk, rg, unit);
   const int b = unit / a.n_kv, g = unit % a.n_kv;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   __shared__ __attribute__((aligned(16))) char s_q[kStreamRows * 256];
