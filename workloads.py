@@ -172,7 +172,7 @@ class H2OPrefill:
     """H2O eviction during chunked prefill: when a chunk of ``chunk`` prompt tokens has been written, the causal
     attention weights of the chunk's queries are added to the cumulative score of every key they see, and while
     the context exceeds ``budget`` the lowest-score tokens outside the most recent ``recent`` positions are
-    evicted (their slots freed)."""
+    evicted (the cache is compacted and the freed blocks returned)."""
 
     name: str
     B: int
