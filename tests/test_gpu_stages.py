@@ -664,3 +664,26 @@ def test_chunk_append_is_all_or_nothing():
                              i32(np.full((2,), 40, np.int32)), status=status)
     assert se.se_status_read(status) & se.SE_DEV_CAPACITY
     compare_cache(dc.to_numpy(), before)
+
+
+def test_chunk_append_after_compaction_with_unequal_heads():
+    # after a whole-cache gather the heads of a sequence hold different slot counts: the chunk's blocks follow the
+    # longest head, the shorter heads' new slots fall in allocated blocks
+    banner("chunk append after compaction, unequal heads")
+    cfg = W.H2O("t", B=2, hq=8, hkv=2, d=128, N=300, budget=600, recent=4, steps=100, zipf=1.1)
+    inp = W.gen_h2o(cfg, seed=10, threads=2)
+    st = inp["cache"]
+    counts = np.array([[40, 290], [150, 7]], np.int32)
+    keep = W.gen_keep_sets(3, st.n_slots, counts, pattern="random")
+    ref = oracle.compact_gather(st, keep)
+    dc = to_device(st, 8)
+    idx, cnt = W.pack_lists(keep, 300)
+    status = status_word()
+    se.se_compact_evict(dc, i32(idx), i32(cnt), mode=se.SE_COMPACT_GATHER, status=status)
+    kc = np.ascontiguousarray(inp["k_new"].transpose(1, 2, 0, 3))
+    vc = np.ascontiguousarray(inp["v_new"].transpose(1, 2, 0, 3))
+    pos0 = np.full((2,), 300, np.int32)
+    ref = oracle.cache_append_chunk(ref, kc, vc, pos0)
+    se.se_cache_append_chunk(dc, storage_tensor(kc, "bf16"), storage_tensor(vc, "bf16"), i32(pos0), status=status)
+    assert se.se_status_read(status) == 0
+    compare_cache(dc.to_numpy(), ref)
