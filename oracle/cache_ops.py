@@ -107,7 +107,8 @@ def evict_slots(cache, evict):
 
 
 def cache_append(cache, k_new: np.ndarray, v_new: np.ndarray, pos: np.ndarray):
-    """Write one token per (b, g): k_new, v_new [B][n_kv][d] stored values, pos [B] its position.
+    """Write one token per (b, g): k_new, v_new [B][n_kv][d] stored values, pos [B] its position; its cumulative
+    score (H2O, SparseEngine page "What it is") starts at 0.
 
     All or nothing: if the free stack cannot supply every block the call needs, nothing changes and
     CapacityError is raised.
@@ -147,6 +148,8 @@ def cache_append(cache, k_new: np.ndarray, v_new: np.ndarray, pos: np.ndarray):
             out.v_pool[blk, g, s % page] = v_new[b, g]
             out.pos_map[b, g, s] = pos[b]
             out.ctx_len[b, g] += 1
+            if out.cum_score is not None:  # a token just written has received no attention yet
+                out.cum_score[b, g, s] = 0.0
     return out, slots
 
 
