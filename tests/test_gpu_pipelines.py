@@ -305,3 +305,76 @@ def test_pipeline_h2o_prefill_chunks():
     d = dc.to_numpy()
     assert np.all(d["ctx_len"] == cfg.budget) and np.all(d["n_slots"] == cfg.budget)
     assert diverged.mean() <= 0.5
+
+
+def test_mixed_cache_operations_stay_bit_exact():
+    """A seeded sequence of single and chunk appends, slot evictions and whole-cache compactions, each followed by a
+    page-metadata refresh, on the GPU and the oracle in lockstep: maps, stacks, free list, K/V, cumulative scores
+    and page metadata match bit for bit after every operation, and an accumulating decode at the end matches."""
+    banner("mixed cache operations, 2 seqs, 14 operations")
+    cfg = W.H2O("t", B=2, hq=8, hkv=2, d=128, N=150, budget=1000, recent=4, steps=200, zipf=1.1)
+    inp = W.gen_h2o(cfg, seed=21, threads=2)
+    st = inp["cache"]
+    stack = np.full((2, 2, 64), -1, np.int32)
+    stack[:, :, :st.slot_stack.shape[2]] = st.slot_stack
+    st.slot_stack = stack
+    rs = np.random.default_rng(22)
+    st.cum_score[:] = rs.random(st.cum_score.shape).astype(np.float32)
+    st.page_meta = oracle.page_bounds_build(st)
+    dc = to_device(st, 8)
+    status = status_word()
+    tok, pos_next = 0, 150
+    ops = ["append", "chunk", "evict", "compact"] * 3 + ["append", "evict"]
+    rs.shuffle(ops)
+    for step, op in enumerate(ops):
+        if op == "append":
+            pos = np.full((2,), pos_next, np.int32)
+            st, _ = oracle.cache_append(st, inp["k_new"][tok], inp["v_new"][tok], pos)
+            se.se_cache_append(dc, storage_tensor(inp["k_new"][tok], "bf16"),
+                               storage_tensor(inp["v_new"][tok], "bf16"), i32(pos), status=status)
+            tok, pos_next = tok + 1, pos_next + 1
+        elif op == "chunk":
+            T = int(rs.integers(1, 40))
+            kc = np.ascontiguousarray(inp["k_new"][tok:tok + T].transpose(1, 2, 0, 3))
+            vc = np.ascontiguousarray(inp["v_new"][tok:tok + T].transpose(1, 2, 0, 3))
+            pos0 = np.full((2,), pos_next, np.int32)
+            st = oracle.cache_append_chunk(st, kc, vc, pos0)
+            se.se_cache_append_chunk(dc, storage_tensor(kc, "bf16"), storage_tensor(vc, "bf16"), i32(pos0),
+                                     status=status)
+            tok, pos_next = tok + T, pos_next + T
+        elif op == "evict":
+            ev = [[np.sort(rs.choice(np.where(st.pos_map[b, g, :st.n_slots[b, g]] >= 0)[0], size=1 + (b + g) % 3,
+                                     replace=False)).astype(np.int32) for g in range(2)] for b in range(2)]
+            st = oracle.evict_slots(st, ev)
+            idx, cnt = W.pack_lists(ev, 3)
+            se.se_compact_evict(dc, i32(idx), i32(cnt), mode=se.SE_COMPACT_EVICT_SLOTS, status=status)
+        else:
+            keep = []
+            for b in range(2):
+                row = []
+                for g in range(2):
+                    res = np.where(st.pos_map[b, g, :st.n_slots[b, g]] >= 0)[0]
+                    row.append(np.sort(rs.choice(res, size=int(0.7 * res.size), replace=False)).astype(np.int32))
+                keep.append(row)
+            st = oracle.compact_gather(st, keep)
+            idx, cnt = W.pack_lists(keep, int(st.pos_map.shape[2]))
+            se.se_compact_evict(dc, i32(idx), i32(cnt), mode=se.SE_COMPACT_GATHER, status=status)
+        # an append may reuse a freed slot in any page, a compaction rewrites the prefix: refresh every used page
+        st.page_meta = oracle.page_bounds_refresh(st, st.page_meta, "from")
+        se.se_page_bounds_refresh(dc, se.SE_REFRESH_FROM_PAGE, status=status)
+        assert se.se_status_read(status) == 0, (step, op)
+        d = dc.to_numpy()
+        compare_cache(d, st)
+        meta = dc.page_meta.view(torch.int16).cpu().numpy().view(np.uint16)
+        for b in range(2):
+            for g in range(2):
+                n_pages = -(-int(st.n_slots[b, g]) // 16)
+                np.testing.assert_array_equal(meta[b, g, :n_pages], st.page_meta[b, g, :n_pages], err_msg=op)
+    out = torch.empty((2, 8, 128), dtype=torch.float32, device=DEV)
+    q = inp["q_steps"][0]
+    se.se_sparse_decode_attn(dc, storage_tensor(q, "bf16"), out, scale=inp["scale"], accumulate=True, status=status)
+    ref_out, ref_cum = oracle.decode_attn(st, q, inp["scale"], accumulate=True)
+    assert se.se_status_read(status) == 0
+    np.testing.assert_allclose(out.cpu().numpy(), ref_out, atol=2e-3, rtol=0)
+    st.cum_score = ref_cum.astype(np.float32)
+    compare_cache(dc.to_numpy(), st, cum_exact=False)
