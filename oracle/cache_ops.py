@@ -153,23 +153,25 @@ def cache_append(cache, k_new: np.ndarray, v_new: np.ndarray, pos: np.ndarray):
     return out, slots
 
 
-def cache_append_chunk(cache, k_new: np.ndarray, v_new: np.ndarray, pos0: np.ndarray):
-    """Write T tokens per (b, g) at its high-water slots [n_slots, n_slots + T) (SparseEngine page, "How it
+def cache_append_chunk(cache, k_new: np.ndarray, v_new: np.ndarray, pos0: np.ndarray, counts=None):
+    """Write T_b tokens per (b, g) at its high-water slots [n_slots, n_slots + T_b) (SparseEngine page, "How it
     works": the cache manager allocates and writes; a prefill chunk arrives as a block of tokens): k_new, v_new
-    [B][n_kv][T][d] stored values, positions pos0[b] + t. The slot stacks are left alone. The logical blocks the
-    new slots need are taken from the free stack in order of sequence, then logical block.
+    [B][n_kv][T][d] stored values (rows t < T_b), positions pos0[b] + t, with T_b = counts[b] (all T without
+    counts). The slot stacks are left alone. The logical blocks the new slots need are taken from the free stack in
+    order of sequence, then logical block.
 
     All or nothing: if a slot range or the free stack cannot take the whole call, nothing changes and
     CapacityError is raised.
     """
     out = cache.copy()
     B, n_kv = cache.n_slots.shape
-    T = k_new.shape[2]
     page = cache.page
     max_slots = cache.pos_map.shape[2]
+    Tb = [int(k_new.shape[2]) if counts is None else int(counts[b]) for b in range(B)]
     need = []
     for b in range(B):
         blocks = set()
+        T = Tb[b]
         for g in range(n_kv):
             n = int(cache.n_slots[b, g])
             if n + T > max_slots:
@@ -185,6 +187,7 @@ def cache_append_chunk(cache, k_new: np.ndarray, v_new: np.ndarray, pos0: np.nda
             out.block_table[b, lb] = cache.free_blocks[top]
     out.free_top[0] = top
     for b in range(B):
+        T = Tb[b]
         for g in range(n_kv):
             n = int(cache.n_slots[b, g])
             for t in range(T):

@@ -407,6 +407,22 @@ def test_chunk_append_equals_single_appends_by_position(N, T):
     assert sorted(used(chunk) + [int(x) for x in chunk.free_blocks[:top]]) == list(range(c.num_blocks))
 
 
+def test_chunk_append_with_counts_equals_per_sequence_appends():
+    """Counts per sequence (one of them 0) give each sequence what a chunk of its own count would."""
+    inp = _h2o_tiny(10, 7)
+    c = inp["cache"]
+    kc = np.ascontiguousarray(inp["k_new"].transpose(1, 2, 0, 3))
+    vc = np.ascontiguousarray(inp["v_new"].transpose(1, 2, 0, 3))
+    both = oracle.cache_append_chunk(c, kc, vc, np.full((2,), 10, np.int32), counts=np.array([5, 0]))
+    assert both.n_slots.tolist() == [[15, 15], [10, 10]]
+    alone = oracle.cache_append_chunk(c, kc[:, :, :5], vc[:, :, :5], np.full((2,), 10, np.int32),
+                                      counts=np.array([5, 0]))
+    np.testing.assert_array_equal(W.gather_contiguous(both, "k"), W.gather_contiguous(alone, "k"))
+    full5 = oracle.cache_append_chunk(c, kc[:, :, :5], vc[:, :, :5], np.full((2,), 10, np.int32))
+    np.testing.assert_array_equal(W.gather_contiguous(both, "k")[0], W.gather_contiguous(full5, "k")[0])
+    np.testing.assert_array_equal(both.pos_map[1], c.pos_map[1])
+
+
 def test_chunk_append_pops_in_sequence_then_block_order_and_is_all_or_nothing():
     inp = _h2o_tiny(8, 9)  # each sequence needs logical blocks 2, 3 and 4
     c = inp["cache"]
