@@ -203,18 +203,20 @@ int32_t se_cache_append(se_cache_t *c, const void *k_new, const void *v_new, con
                         void *ws, size_t ws_bytes, se_stream_t stream);
 
 /* ---- append a chunk of tokens per (sequence, KV head) -------------------------------------------------------
- * CacheManager allocate/write for a prefill chunk (SparseEngine page, "How it works"). Per (b, g) the T tokens
- * take the slots [n_slots, n_slots + T) (the high-water mark; freed slots on the slot stack are left for single-
- * token appends): k_new, v_new [B][n_kv][T][d] of dtype are written there, pos_map = pos0[b] + t (pos0: device
- * [B]), cumulative scores (if present) 0, n_slots and ctx_len + T. Logical blocks the new slots need beyond a
+ * CacheManager allocate/write for a prefill chunk (SparseEngine page, "How it works"). Sequence b appends
+ * T_b = counts[b] tokens (counts: device [B], each in [0, T]; NULL = T for every sequence). Per (b, g) they take
+ * the slots [n_slots, n_slots + T_b) (the high-water mark; freed slots on the slot stack are left for single-
+ * token appends): k_new, v_new [B][n_kv][T][d] of dtype (rows t < T_b are read) are written there,
+ * pos_map = pos0[b] + t (pos0: device [B]), cumulative scores (if present) 0, n_slots and ctx_len + T_b. Logical blocks the new slots need beyond a
  * sequence's allocated prefix are popped from free_blocks in order of sequence, then logical block. All or
- * nothing: if the free stack or a unit's slot range cannot take the whole call, nothing changes and
- * SE_DEV_CAPACITY is raised (SE_DEV_INDEX for a block table entry out of range). B <= 2048. Workspace:
+ * nothing: if the free stack or a unit's slot range cannot take the whole call (or a count is outside [0, T]),
+ * nothing changes and SE_DEV_CAPACITY is raised (SE_DEV_INDEX for a block table entry out of range). B <= 2048.
+ * Workspace:
  * se_cache_append_chunk_workspace_size bytes (one int32).
  */
 size_t se_cache_append_chunk_workspace_size(const se_cache_t *c, int32_t T);
 int32_t se_cache_append_chunk(se_cache_t *c, const void *k_new, const void *v_new, const int32_t *pos0, int32_t T,
-                              int32_t *status, void *ws, size_t ws_bytes, se_stream_t stream);
+                              const int32_t *counts, int32_t *status, void *ws, size_t ws_bytes, se_stream_t stream);
 
 /* ---- Quest page bounds ---------------------------------------------------------------------------------------
  * SparseEngine page, "What it is"/"How it works": Quest's query-dependent page selection. Needs page_meta.

@@ -181,8 +181,9 @@ def se_cache_append(cache, k_new, v_new, pos, *, status=None, stream=None):
                                                   None, 0, sp))
 
 
-def se_cache_append_chunk(cache, k_new, v_new, pos0, *, status=None, stream=None):
-    """Append T tokens per (sequence, KV head) at the high-water slots; k_new, v_new [B][n_kv][T][d], pos0 [B]."""
+def se_cache_append_chunk(cache, k_new, v_new, pos0, *, counts=None, status=None, stream=None):
+    """Append T tokens per (sequence, KV head) at the high-water slots (counts[b] <= T for sequence b when given);
+    k_new, v_new [B][n_kv][T][d], pos0 [B]."""
     lib = _lib.load()
     st, sp = _stream(stream)
     c = cache.desc()
@@ -190,7 +191,7 @@ def se_cache_append_chunk(cache, k_new, v_new, pos0, *, status=None, stream=None
     nb = lib.se_cache_append_chunk_workspace_size(C.byref(c), T)
     ws = _workspace(nb, cache.device, stream)
     _check("se_cache_append_chunk", lib.se_cache_append_chunk(C.byref(c), _ptr(k_new), _ptr(v_new), _ptr(pos0), T,
-                                                              _ptr(status), _ptr(ws), nb, sp))
+                                                              _ptr(counts), _ptr(status), _ptr(ws), nb, sp))
 
 
 def se_page_bounds(cache, op, q=None, page_scores=None, *, status=None, stream=None):

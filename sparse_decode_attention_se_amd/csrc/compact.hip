@@ -606,10 +606,18 @@ struct ChunkArgs {
   float *cum;
   const char *k_new, *v_new;
   const int32_t *pos0;
+  const int32_t *counts;  // tokens of each sequence (<= T), or NULL: T for every sequence
   int32_t *flag;  // workspace: 1 when chunk_plan committed the call
   int32_t *status;
   int32_t B, n_kv, page, max_blocks, num_blocks, row_bytes, T;
 };
+
+// tokens appended to sequence b (-1: a count outside [0, T], which fails the call)
+SE_DEV int chunk_count(const ChunkArgs &a, int b) {
+  if (!a.counts) return a.T;
+  const int c = a.counts[b];
+  return c >= 0 && c <= a.T ? c : -1;
+}
 
 // One workgroup: per sequence the logical blocks its heads' new slots [n, n + T) need beyond the allocated prefix;
 // pops for them in (sequence, logical block) order; then, only if everything fits, the commit: block table,
@@ -635,12 +643,14 @@ __global__ __launch_bounds__(kAppendThreads) void chunk_plan(ChunkArgs a) {
   // slots reach block (largest n + T - 1) / page
   for (int unit = threadIdx.x; unit < units; unit += kAppendThreads) {
     const int n = a.n_slots[unit], b = unit / a.n_kv;
-    if (n < 0 || n + a.T > cap) {
+    const int tb = chunk_count(a, b);
+    if (tb < 0 || n < 0 || n + tb > cap) {
       atomicOr(&s_fail, 1);
       continue;
     }
+    if (tb == 0) continue;
     atomicMax(&s_first[b], n / a.page);
-    atomicMax(&s_last[b], (n + a.T - 1) / a.page);
+    atomicMax(&s_last[b], (n + tb - 1) / a.page);
   }
   __syncthreads();
   // the first unallocated table entry in each sequence's window [first, last] (allocated entries form a
@@ -691,8 +701,9 @@ __global__ __launch_bounds__(kAppendThreads) void chunk_plan(ChunkArgs a) {
     for (int i = 0; i < s_need[b]; ++i)
       a.bt[(int64_t)b * a.max_blocks + s_alloc[b] + i] = a.free_blocks[top0 - 1 - (s_before[b] + i)];
   for (int unit = threadIdx.x; unit < units; unit += kAppendThreads) {
-    a.n_slots[unit] += a.T;
-    a.ctx[unit] += a.T;
+    const int tb = chunk_count(a, unit / a.n_kv);
+    a.n_slots[unit] += tb;
+    a.ctx[unit] += tb;
   }
   if (threadIdx.x == 0) {
     *a.free_top = top0 - carry;
@@ -709,10 +720,11 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_write(ChunkArgs a) {
   const int cap = a.max_blocks * a.page;
   const int cpr = a.row_bytes / 16;
   const int rows = kChunkThreads / cpr;  // rows per workgroup
-  const int base = a.n_slots[unit] - a.T;
+  const int tb = chunk_count(a, b);
+  const int base = a.n_slots[unit] - tb;
   const int32_t *bt = a.bt + (int64_t)b * a.max_blocks;
   const int t = blockIdx.x * rows + threadIdx.x / cpr, ch = threadIdx.x % cpr;
-  if (t >= a.T) return;
+  if (t >= tb) return;
   const int slot = base + t;
   const int blk = bt[slot / a.page];
   const int64_t src = ((int64_t)unit * a.T + t) * a.row_bytes + ch * 16;
@@ -862,8 +874,8 @@ extern "C" size_t se_cache_append_chunk_workspace_size(const se_cache_t *c, int3
 }
 
 extern "C" int32_t se_cache_append_chunk(se_cache_t *c, const void *k_new, const void *v_new, const int32_t *pos0,
-                                         int32_t T, int32_t *status, void *ws, size_t ws_bytes,
-                                         se_stream_t stream) {
+                                         int32_t T, const int32_t *counts, int32_t *status, void *ws,
+                                         size_t ws_bytes, se_stream_t stream) {
   int32_t rc = se_host::check_cache(c);
   if (rc != SE_OK) return rc;
   if (!k_new || !v_new || !pos0 || !c->free_blocks || !c->free_top) return SE_ERR_NULL;
@@ -885,6 +897,7 @@ extern "C" int32_t se_cache_append_chunk(se_cache_t *c, const void *k_new, const
   a.k_new = (const char *)k_new;
   a.v_new = (const char *)v_new;
   a.pos0 = pos0;
+  a.counts = counts;
   a.flag = (int32_t *)ws;
   a.status = status;
   a.B = c->B;

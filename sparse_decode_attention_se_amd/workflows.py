@@ -6,6 +6,8 @@ accumulation and eviction every decode step; and where the KARA page ("Method" p
 compression of trailing blocks. Output buffers are allocated once per driver; every step is a libse call on
 the current stream, and nothing here synchronises.
 """
+from collections import OrderedDict
+
 import torch
 
 from . import (SE_COMPACT_EVICT_SLOTS, SE_COMPACT_GATHER, SE_PAGES_BUILD, SE_PAGES_SCORE, SE_REFRESH_FROM_PAGE,
@@ -213,3 +215,56 @@ class QuestStep:
         se_sparse_decode_attn(self.cache, q, self.out, scale=self.scale, sel_pages=self.pages, sel_count=self.count,
                               status=self.status)
         return self.out
+
+
+class ChainCacheIndex:
+    """Cross-request reuse of an evicted cache (SparseEngine page, "How it differs": Chain Cache lets eviction
+    methods reuse their compressed state across turns; ChainCacheIndex links a session to its retained KV, its
+    method metadata and its logical token prefix; a request resumes from the retained state and prefills only the
+    unprocessed suffix; idle chains are reclaimed in least-recently-used order).
+
+    Host-side bookkeeping over a DeviceCache whose B sequence slots are the places sessions live. A finished
+    session stays parked in its slot (retained KV, positions, cumulative scores and page metadata untouched)
+    under its chain id and logical prefix. acquire() finds the parked chain whose prefix is the longest prefix of
+    a request's tokens and hands back its slot; otherwise a free slot; otherwise it reclaims the least recently
+    used chain: a whole-cache gather that keeps every resident slot of the other sequences and nothing of the
+    victim's returns the victim's blocks to the free stack. The caller appends the suffix (se_cache_append_chunk)
+    and runs the method on the slot, then parks it again."""
+
+    def __init__(self, cache, status=None):
+        self.cache, self.status = cache, status
+        self.free = list(range(cache.block_table.shape[0]))
+        self.chains = OrderedDict()  # chain id -> (slot, logical prefix), least recently used first
+
+    def park(self, chain_id, slot, prefix):
+        self.chains[chain_id] = (slot, tuple(prefix))
+        self.chains.move_to_end(chain_id)
+        if slot in self.free:
+            self.free.remove(slot)
+
+    def acquire(self, tokens):
+        """(slot, number of tokens already in it, chain id or None) for a request with these logical tokens."""
+        tokens = tuple(tokens)
+        best = None
+        for cid, (slot, prefix) in self.chains.items():
+            if len(prefix) <= len(tokens) and tokens[:len(prefix)] == prefix:
+                if best is None or len(prefix) > len(self.chains[best][1]):
+                    best = cid
+        if best is not None:
+            slot, prefix = self.chains.pop(best)
+            return slot, len(prefix), best
+        if self.free:
+            return self.free.pop(0), 0, None
+        victim, (slot, _) = self.chains.popitem(last=False)
+        self.reclaim(slot)
+        return slot, 0, None
+
+    def reclaim(self, slot):
+        """Free every block of one sequence slot (its resident set becomes empty); the others are untouched."""
+        c = self.cache
+        B, G, S = c.pos_map.shape
+        keep = torch.arange(S, dtype=torch.int32, device=c.device).repeat(B, G, 1)
+        count = c.n_slots.clone()
+        count[slot] = 0
+        # the other sequences keep all their slots below n_slots, which must then all be resident
+        se_compact_evict(c, keep, count, mode=SE_COMPACT_GATHER, status=self.status)

@@ -378,3 +378,63 @@ def test_mixed_cache_operations_stay_bit_exact():
     np.testing.assert_allclose(out.cpu().numpy(), ref_out, atol=2e-3, rtol=0)
     st.cum_score = ref_cum.astype(np.float32)
     compare_cache(dc.to_numpy(), st, cum_exact=False)
+
+
+def test_chain_cache_resume_suffix_and_lru_reclaim():
+    """Two sessions end their prompts with SnapKV's eviction and are parked. A request that extends session A
+    resumes in A's slot and appends only its suffix; its decode matches attention over the retained prefix plus the
+    suffix. A new request with no matching chain and no free slot reclaims the least recently used chain (B), whose
+    blocks return to the free stack, and its prompt goes into that slot. The cache matches the oracle bit for bit
+    after every step."""
+    banner("chain cache: resume with a suffix, LRU reclaim")
+    cfg = W.SnapKV("chain", B=2, hq=8, hkv=2, d=128, N=600, wq=32, protect=16, keep=100, dtype="bf16",
+                   spike_frac=0.04)
+    inp = W.gen_snapkv(cfg, seed=13, threads=4)
+    st = inp["cache"]
+    dc = to_device(st, cfg.hq)
+    status = status_word()
+    ev = WF.SnapKVEvent(dc, wq=cfg.wq, protect=cfg.protect, keep=cfg.keep, scale=inp["scale"], status=status)
+    ev.score(storage_tensor(inp["q_win"], "bf16"), i32(inp["q_pos"]))
+    ev.select()
+    ev.compact()
+    st = oracle.compact_gather(st, lists_from(ev.idx, ev.count))  # the GPU's choice, replayed on the oracle
+    compare_cache(dc.to_numpy(), st)
+    chains = WF.ChainCacheIndex(dc, status=status)
+    prompt = {"A": [("A", i) for i in range(600)], "B": [("B", i) for i in range(600)]}
+    chains.park("A", 0, prompt["A"])
+    chains.park("B", 1, prompt["B"])
+    rs = np.random.default_rng(14)
+
+    def chunk(T):
+        return W.to_storage(rs.standard_normal((2, 2, T, 128)), "bf16")
+
+    # A's session continues: 48 new tokens, appended to slot 0 alone
+    request = prompt["A"] + [("A", 600 + i) for i in range(48)]
+    assert chains.acquire(request) == (0, 600, "A")
+    ks, vs = chunk(48), chunk(48)
+    counts, pos0 = np.array([48, 0], np.int32), np.array([600, 0], np.int32)
+    st = oracle.cache_append_chunk(st, ks, vs, pos0, counts=counts)
+    se.se_cache_append_chunk(dc, storage_tensor(ks, "bf16"), storage_tensor(vs, "bf16"), i32(pos0),
+                             counts=i32(counts), status=status)
+    out = torch.empty((2, cfg.hq, 128), dtype=torch.float32, device=DEV)
+    se.se_sparse_decode_attn(dc, storage_tensor(inp["q_dec"], "bf16"), out, scale=inp["scale"], status=status)
+    want, _ = oracle.decode_attn(st, inp["q_dec"], inp["scale"])
+    assert se.se_status_read(status) == 0
+    compare_cache(dc.to_numpy(), st)
+    np.testing.assert_allclose(out.cpu().numpy(), want, atol=2e-3, rtol=0)
+    chains.park("A", 0, request)
+    # an unrelated request: B, least recently used, is reclaimed and slot 1 takes the new prompt
+    top0 = int(st.free_top[0])
+    assert chains.acquire([("C", i) for i in range(100)]) == (1, 0, None)
+    keep = [[np.arange(int(st.n_slots[0, g]), dtype=np.int32) for g in range(2)], [np.zeros(0, np.int32)] * 2]
+    st = oracle.compact_gather(st, keep)
+    assert st.n_slots[1].tolist() == [0, 0] and int(st.free_top[0]) > top0
+    compare_cache(dc.to_numpy(), st)
+    kc, vc = chunk(100), chunk(100)
+    counts, pos0 = np.array([0, 100], np.int32), np.array([0, 0], np.int32)
+    st = oracle.cache_append_chunk(st, kc, vc, pos0, counts=counts)
+    se.se_cache_append_chunk(dc, storage_tensor(kc, "bf16"), storage_tensor(vc, "bf16"), i32(pos0),
+                             counts=i32(counts), status=status)
+    assert se.se_status_read(status) == 0
+    compare_cache(dc.to_numpy(), st)
+    assert chains.acquire(request + [("A", 648)]) == (0, 648, "A")  # A is still parked
