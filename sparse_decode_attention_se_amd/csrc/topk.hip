@@ -189,18 +189,21 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
   int limit = 0;
   if (a.mode == SE_TOPK_SMALLEST) limit = (int)block_max_u((uint32_t)(mx + 1), s_red) - 1 - a.recent;
 
-  // range-restricted pruning: a bit per logical page of the sequence whose block has references, in LDS (threads
-  // load block-table entries and counts cooperatively); an item looks up its page's bit
+  // range-restricted pruning: a bit per logical page of the items (pages from the one holding slot `base`) whose
+  // block has references, in LDS (threads load block-table entries and counts cooperatively); an item looks up
+  // its page's bit. The items span at most PER * kThreads pages, the bitmap's size.
   const bool rng = !page_unit && a.range_hi > a.range_lo;
   const bool gate = rng && a.refs;
+  const int p_lo = base / a.page;
   if (gate) {
     const int n_lp = (n + a.page - 1) / a.page;
     for (int i = t; i < (PER * kThreads + 31) / 32; i += kThreads) s_busy[i] = 0u;
     __syncthreads();
     const int32_t *btb = a.bt + (int64_t)(unit / a.n_kv) * a.max_blocks;
-    for (int lp = t; lp < n_lp && lp < PER * kThreads; lp += kThreads) {
+    for (int lp = p_lo + t; lp < n_lp && lp - p_lo < PER * kThreads; lp += kThreads) {
       const int blk = btb[lp];
-      if (blk_ok(blk, a.num_blocks) && a.refs[blk] > 0) atomicOr(&s_busy[lp >> 5], 1u << (lp & 31));
+      const int q = lp - p_lo;
+      if (blk_ok(blk, a.num_blocks) && a.refs[blk] > 0) atomicOr(&s_busy[q >> 5], 1u << (q & 31));
     }
     __syncthreads();
   }
@@ -226,7 +229,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
       } else {
         k = base + i >= n - a.protect;
         if (!k && rng) {
-          const int lp = (base + i) / a.page;
+          const int lp = (base + i) / a.page - p_lo;
           if (p < a.range_lo || p >= a.range_hi || (gate && ((s_busy[lp >> 5] >> (lp & 31)) & 1u))) k = true;
         }
         c = !k;

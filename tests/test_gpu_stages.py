@@ -588,6 +588,31 @@ def test_topk_range_pruning_and_parallel_slot_eviction_exact(k):
     compare_cache(dc.to_numpy(), oracle.evict_slots(st, dropped))
 
 
+def test_topk_range_pruning_inside_a_window_exact():
+    # items are the last 600 slots (scores indexed from the window's first slot): busy pages are looked up
+    # relative to the window's first page
+    banner("range pruning inside a window")
+    inp = snap_inputs(B=2, N=5000, seed=15)
+    st = inp["cache"]
+    rs = np.random.default_rng(16)
+    refs = (rs.random(st.num_blocks) < 0.3).astype(np.int32)
+    W_ = 600
+    scores = (rs.random((2, 2, W_)) * 20).round().astype(np.float32)
+    lo, hi, k = 4500, 4950, 90
+    want = oracle.topk_largest(scores, st, k, window=W_, prune_range=(lo, hi), block_refs=refs)
+    dc = to_device(st, 8)
+    status = status_word()
+    idx = torch.full((2, 2, W_), -7, dtype=torch.int32, device=DEV)
+    cnt = torch.zeros((2, 2), dtype=torch.int32, device=DEV)
+    se.se_topk_select(dc, torch.from_numpy(scores).to(DEV), idx, cnt, mode=se.SE_TOPK_LARGEST, unit=se.SE_UNIT_SLOT,
+                      k=k, window=W_, prune_range=(lo, hi), block_refs=i32(refs), status=status)
+    assert se.se_status_read(status) == 0
+    got = lists_from(idx, cnt)
+    for b in range(2):
+        for g in range(2):
+            assert got[b][g].tolist() == want[b][g].tolist()
+
+
 def test_slot_eviction_reports_bad_entries_and_capacity():
     banner("slot eviction errors")
     inp = snap_inputs(B=1, N=300)
