@@ -26,7 +26,8 @@ vector operations only as the textbook primitives (dot products, exp, sort).
 Parity pins: see ``tests/test_oracle_pins.py`` and ``tests/test_golden.py``. No function here is "parity
 unpinned".
 """
-from .cache_ops import cache_append, cache_append_chunk, compact_gather, evict_slots
+from .cache_ops import (cache_append, cache_append_chunk, compact_gather, evict_slots, put_sequence_range,
+                        sequence_range)
 from .decode import decode_attn
 from .pages import page_bounds_build, page_bounds_refresh, page_bounds_score
 from .score import window_score_bidir, window_score_causal
@@ -36,5 +37,5 @@ __all__ = [
     "window_score_causal", "window_score_bidir", "topk_largest", "topk_smallest", "token2chunk",
     "compact_gather", "evict_slots", "cache_append", "cache_append_chunk", "page_bounds_build", "page_bounds_refresh",
     "page_bounds_score",
-    "decode_attn",
+    "decode_attn", "sequence_range", "put_sequence_range",
 ]

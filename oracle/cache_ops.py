@@ -201,3 +201,32 @@ def cache_append_chunk(cache, k_new: np.ndarray, v_new: np.ndarray, pos0: np.nda
             out.n_slots[b, g] = n + T
             out.ctx_len[b, g] += T
     return out
+
+
+_PER_SEQUENCE = ("block_table", "pos_map", "ctx_len", "n_slots", "slot_stack", "slot_top", "page_meta", "cum_score")
+
+
+def sequence_range(cache, b0: int, b1: int):
+    """The sequences [b0, b1) as a cache of their own (KARA page, "Method" part 3: KvLLM compresses selected
+    sequences). Per-sequence arrays are those sequences' rows; the block pool and the free-block stack are the
+    whole cache's, since blocks are shared by every sequence."""
+    sub = cache.copy()
+    for f in _PER_SEQUENCE:
+        x = getattr(cache, f)
+        if x is not None:
+            setattr(sub, f, x[b0:b1].copy())
+    return sub
+
+
+def put_sequence_range(cache, sub, b0: int):
+    """A copy of ``cache`` with the sequences [b0, b0 + sub.B) and the shared block pool and free-block stack
+    taken from ``sub`` (a cache made by sequence_range and changed since)."""
+    out = cache.copy()
+    b1 = b0 + sub.B
+    for f in _PER_SEQUENCE:
+        x = getattr(out, f)
+        if x is not None:
+            x[b0:b1] = getattr(sub, f)
+    for f in ("k_pool", "v_pool", "free_blocks", "free_top"):
+        getattr(out, f)[...] = getattr(sub, f)
+    return out

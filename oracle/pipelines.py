@@ -12,10 +12,14 @@ Each driver calls the oracle steps in the order the method takes them:
   pages plus the first and last -> decode over the selected pages.
 * H2O (SparseEngine page, "What it is"): per step append -> decode with cumulative-score accumulation ->
   when over budget, evict the lowest score outside the recent positions.
+* The compression policy loop (KARA page, "Method" part 3, and "Problem" point 1): decode steps over the whole
+  batch; after a step, Kara's event on the sequences the policy names (KvLLM's periodic schedule, or the
+  threshold trigger it replaces), one event per run of consecutive sequences.
 """
 import numpy as np
 
-from .cache_ops import cache_append, cache_append_chunk, compact_gather, evict_slots
+from .cache_ops import (cache_append, cache_append_chunk, compact_gather, evict_slots, put_sequence_range,
+                        sequence_range)
 from .decode import decode_attn
 from .pages import page_bounds_build, page_bounds_score
 from .score import window_score_bidir, window_score_causal
@@ -113,3 +117,73 @@ def h2o_prefill_chunk(inp, cache, c: int):
     cum = cache.cum_score.copy()
     cache = compact_gather(cache, keep)
     return cache, dict(scores=s, keep=keep, cum=cum)
+
+
+def kara_event_range(cache, q_win, b0: int, b1: int, *, scale, window, protect, n_cand, budget, max_gap,
+                     keep=None):
+    """Kara's compression event on the sequences [b0, b1) alone; every other sequence is left as it is (KARA
+    page, "Method" part 3: the trailing blocks of selected sequences are compressed). q_win [b1-b0][hq][window][d]
+    are the window's queries. ``keep`` (per sequence of the range, per KV head) replaces the Token2Chunk result
+    when given: an equally valid choice made elsewhere where near-tied scores allow several."""
+    sub = sequence_range(cache, b0, b1)
+    scores = window_score_bidir(sub, q_win, scale, window, protect)
+    cand = topk_largest(scores, sub, n_cand, window=window, protect=protect)
+    chosen = token2chunk(cand, scores.astype(np.float32), sub, max_gap=max_gap, budget=budget, window=window,
+                         protect=protect)
+    sub = compact_gather(sub, chosen if keep is None else keep, window=window)
+    return dict(scores=scores, cand=cand, keep=chosen, cache=put_sequence_range(cache, sub, b0))
+
+
+def policy_due(policy: str, t: int, B: int, period: int):
+    """Sequences compressed after decode step t (0-based).
+
+    periodic (KvLLM, KARA page "Method" part 3): every sequence, after every ``period``-th step.
+    threshold (KARA page, "Problem" point 1): sequence b joins with (b * period) // B tokens already in its
+    uncompressed tail and is compressed when the tail reaches ``period`` tokens; the staggered tails make a few
+    sequences reach the threshold at almost every step.
+    """
+    if policy == "periodic":
+        return list(range(B)) if (t + 1) % period == 0 else []
+    if policy == "threshold":
+        return [b for b in range(B) if (t + 1 + (b * period) // B) % period == 0]
+    raise ValueError(policy)
+
+
+def runs_of(seqs):
+    """Maximal runs [b0, b1) of consecutive sequence ids, ascending."""
+    out = []
+    for b in sorted(seqs):
+        if out and out[-1][1] == b:
+            out[-1][1] = b + 1
+        else:
+            out.append([b, b + 1])
+    return [tuple(r) for r in out]
+
+
+def kara_recent_window_queries(inp, b0: int, b1: int, t: int):
+    """Queries of the ``window`` most recent tokens of sequences [b0, b1) once decode step t has appended its
+    token (positions N + t + 1 - window .. N + t; t = -1 before the first step), [b1-b0][hq][window][d] (harness
+    plumbing: a slice of the stored queries)."""
+    cfg = inp["cfg"]
+    s = cfg.N + t + 1 - cfg.window - inp["q_first_pos"]
+    if s < 0:
+        raise ValueError("window reaches before the first stored query")
+    return np.ascontiguousarray(inp["q_all"][b0:b1, :, s:s + cfg.window])
+
+
+def kara_policy_loop(inp, cache, policy: str, steps: int):
+    """``steps`` decode steps of the whole batch (append, then attend); after each, Kara's event on every run of
+    consecutive sequences the policy names, scored with the queries of each sequence's most recent tokens.
+    Returns the final cache, the decode outputs per step and the events as (step, b0, b1)."""
+    cfg = inp["cfg"]
+    outs, events = [], []
+    for t in range(steps):
+        cache, o = kara_decode_step(inp, cache, t)
+        outs.append(o)
+        for b0, b1 in runs_of(policy_due(policy, t, cfg.B, cfg.period)):
+            ev = kara_event_range(cache, kara_recent_window_queries(inp, b0, b1, t), b0, b1, scale=inp["scale"],
+                                  window=cfg.window, protect=cfg.protect, n_cand=cfg.n_cand, budget=cfg.budget,
+                                  max_gap=cfg.max_gap)
+            cache = ev["cache"]
+            events.append((t, b0, b1))
+    return cache, outs, events

@@ -595,3 +595,136 @@ def test_h2o_loop_invariants_brute_force():
             del K[g][victim], V[g][victim], cum[g][victim]
             res = set(int(x) for x in c.pos_map[0, g] if x >= 0)
             assert res == set(K[g]) and len(res) == 48 and c.ctx_len[0, g] == 48
+
+
+# ------------------------------------------------------------------ compression policy loop --------------------
+def tiny_kara_loop(B=5, period=8, events=2, cand_frac=0.2, budget_frac=0.2, seed=3):
+    cfg = W.scaled(W.C2, B=B, hq=4, hkv=2, d=16, N=300, window=64, protect=8, period=period, events=events,
+                   cand_frac=cand_frac, budget_frac=budget_frac, dtype="f32", page=4)
+    return W.gen_kara(cfg, seed=seed, threads=1)
+
+
+def event_kw(inp):
+    cfg = inp["cfg"]
+    return dict(scale=inp["scale"], window=cfg.window, protect=cfg.protect, n_cand=cfg.n_cand, budget=cfg.budget,
+                max_gap=cfg.max_gap)
+
+
+def assert_same_state(a, b, seqs):
+    """Per-sequence state and the resident K/V rows of the given sequences are identical."""
+    Ka, Kb = W.gather_contiguous(a, "k"), W.gather_contiguous(b, "k")
+    Va, Vb = W.gather_contiguous(a, "v"), W.gather_contiguous(b, "v")
+    for s in seqs:
+        np.testing.assert_array_equal(a.pos_map[s], b.pos_map[s])
+        np.testing.assert_array_equal(a.n_slots[s], b.n_slots[s])
+        np.testing.assert_array_equal(a.ctx_len[s], b.ctx_len[s])
+        res = a.pos_map[s] >= 0
+        np.testing.assert_array_equal(Ka[s][res], Kb[s][res])
+        np.testing.assert_array_equal(Va[s][res], Vb[s][res])
+
+
+def test_event_on_a_sequence_range_acts_on_those_sequences_alone():
+    inp = tiny_kara_loop()
+    cfg, c = inp["cfg"], inp["cache"]
+    q = P.kara_recent_window_queries(inp, 0, cfg.B, -1)
+    full = P.kara_event_range(c, q, 0, cfg.B, **event_kw(inp))
+    # the whole batch as one range is the event over the batch (before any step the most recent tokens are the
+    # window's slots, whose queries the plain event looks up by position)
+    plain = P.kara_event(inp, c)
+    assert_same_state(full["cache"], plain["cache"], range(cfg.B))
+    assert full["cache"].free_top[0] == plain["cache"].free_top[0] > c.free_top[0]
+    part = P.kara_event_range(c, q[1:3], 1, 3, **event_kw(inp))
+    out = part["cache"]
+    # sequences 1 and 2 end as the batch-wide event leaves them, the others as they were
+    assert_same_state(out, full["cache"], [1, 2])
+    assert_same_state(out, c, [0, 3, 4])
+    np.testing.assert_array_equal(out.block_table[[0, 3, 4]], c.block_table[[0, 3, 4]])
+    # the freed blocks are those the batch-wide event freed from sequences 1 and 2, in the same order
+    top0 = int(c.free_top[0])
+    owned = set(c.block_table[1:3].ravel().tolist()) - {-1}
+    pushed_full = full["cache"].free_blocks[top0:full["cache"].free_top[0]].tolist()
+    pushed = out.free_blocks[top0:out.free_top[0]].tolist()
+    assert pushed == [x for x in pushed_full if x in owned] and len(pushed) > 0
+    used = out.block_table[out.block_table >= 0].tolist()
+    assert sorted(used + out.free_blocks[:out.free_top[0]].tolist()) == list(range(out.num_blocks))
+
+
+@pytest.mark.parametrize("B,period", [(6, 8), (128, 128), (20, 4), (3, 16)])
+def test_policy_schedules(B, period):
+    T = 3 * period
+    for policy in ("periodic", "threshold"):
+        fired = {b: [] for b in range(B)}
+        per_step = []
+        for t in range(T):
+            due = P.policy_due(policy, t, B, period)
+            assert due == sorted(set(due))
+            per_step.append(len(due))
+            for b in due:
+                fired[b].append(t)
+        for b in range(B):
+            # one compression per `period` decode steps under either policy
+            assert len(fired[b]) == 3 and np.all(np.diff(fired[b]) == period)
+            if policy == "periodic":
+                assert fired[b][0] == period - 1
+            else:
+                assert fired[b][0] == period - 1 - (b * period) // B
+        if policy == "threshold":
+            # the staggered tails spread the events: no step holds more than ceil(B / period)
+            assert max(per_step) == -(-B // period)
+        else:
+            assert max(per_step) == B and per_step.count(B) == 3
+    assert P.runs_of([0, 1, 2, 4, 5, 9]) == [(0, 3), (4, 6), (9, 10)]
+    assert P.runs_of([]) == []
+
+
+@pytest.mark.parametrize("policy", ["periodic", "threshold"])
+def test_policy_loop_with_full_budget_is_plain_decode(policy):
+    # budget and candidates covering the whole window keep every slot: each event is the identity, so the loop
+    # equals plain decode steps (append, then attend)
+    inp = tiny_kara_loop(cand_frac=1.0, budget_frac=1.0)
+    cfg = inp["cfg"]
+    assert cfg.n_cand == cfg.window - cfg.protect and cfg.budget == cfg.window
+    cache, outs, events = P.kara_policy_loop(inp, inp["cache"], policy, cfg.steps)
+    want = [(t, b0, b1) for t in range(cfg.steps) for b0, b1 in P.runs_of(P.policy_due(policy, t, cfg.B, cfg.period))]
+    assert events == want and len(events) > 0
+    st = inp["cache"]
+    for t in range(cfg.steps):
+        st, o = P.kara_decode_step(inp, st, t)
+        np.testing.assert_array_equal(outs[t], o)
+    assert_same_state(cache, st, range(cfg.B))
+    assert cache.free_top[0] == st.free_top[0]
+
+
+@pytest.mark.parametrize("policy", ["periodic", "threshold"])
+def test_policy_loop_invariants(policy):
+    inp = tiny_kara_loop()
+    cfg = inp["cfg"]
+    cache, outs, events = P.kara_policy_loop(inp, inp["cache"], policy, cfg.steps)
+    assert len(events) > 0
+    T = cfg.N + cfg.steps
+    for b in range(cfg.B):
+        for g in range(cfg.hkv):
+            n = int(cache.n_slots[b, g])
+            pos = cache.pos_map[b, g, :n]
+            # dense, in position order, every position at most once, the newest token kept; each event's window
+            # reaches back at most one region past what earlier events removed, so the prefix before that stays
+            assert np.all(pos >= 0) and np.all(np.diff(pos) > 0) and pos[-1] == T - 1
+            assert int(cache.ctx_len[b, g]) == n < T
+            n_ev = sum(1 for _, b0, b1 in events if b0 <= b < b1)
+            keep0 = cfg.N - cfg.window - n_ev * (cfg.window - cfg.protect)
+            assert n_ev == cfg.events and keep0 > 0
+            np.testing.assert_array_equal(pos[:keep0], np.arange(keep0))
+    used = cache.block_table[cache.block_table >= 0].tolist()
+    assert sorted(used + cache.free_blocks[:cache.free_top[0]].tolist()) == list(range(cache.num_blocks))
+
+
+def test_recent_window_queries_are_those_of_the_latest_positions():
+    inp = tiny_kara_loop()
+    cfg = inp["cfg"]
+    for t in (-1, 0, 5, cfg.steps - 1):
+        q = P.kara_recent_window_queries(inp, 1, 4, t)
+        last = cfg.N + t  # position of the token step t appended (t = -1: the prompt's last)
+        for j, p in enumerate(range(last - cfg.window + 1, last + 1)):
+            np.testing.assert_array_equal(q[:, :, j], inp["q_all"][1:4, :, p - inp["q_first_pos"]])
+    with pytest.raises(ValueError):
+        P.kara_recent_window_queries(inp, 0, 1, -2)
