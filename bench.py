@@ -1,6 +1,6 @@
 """Benchmark of the sparse-KV hot path on one MI355X. Prints one JSON line.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c1|...|c7] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c1|...|c8] [--no-cpu-baseline]
 
 A step is one pass of the workload's hot path over its batch, with every input resident in HBM before timing:
 
@@ -20,6 +20,11 @@ A step is one pass of the workload's hot path over its batch, with every input r
      blocks (5% of blocks busy), the rest of the range freed, one decode step over the pruned cache.
   c7 H2O's chunked-prefill eviction on 8 x 8192 prompt tokens: per chunk of 512, the chunk's causal scores added
      to the cumulative scores, bottom-K down to the 2048 budget, slots freed (one step = the whole prefill).
+  c8 compression policy loop on c2's batch: 128 decode steps (append + attention over the whole batch), with
+     Kara's event on the sequences each policy names: KvLLM's periodic policy (all 128 sequences after step 128)
+     against a threshold trigger (each sequence when its staggered uncompressed tail reaches 128 tokens, one
+     event per step). A step is one decode step; the line reports decode tokens/s under the periodic policy and
+     both policies' compression share. --steps and --warmup do not apply (one period, after an untimed pass).
 
 Steps that change the cache destructively, or whose working set would stay in the 256 MB Infinity Cache between
 steps, run each on a pristine copy of the cache (c1, c2, c3, c5, c6, c7). Per-call times come from HIP events on the stream
@@ -476,6 +481,117 @@ SETUPS = {"c1": setup_c1, "c2": setup_c2, "c3": setup_c3, "c4": setup_c4, "c5": 
           "c7": setup_c7}
 
 
+def run_policy_loop(se, WF, W, dev):
+    """c8: one period of decode steps under each compression policy. Returns the JSON line."""
+    import torch
+
+    cfg = W.C8
+    t0 = time.time()
+    inp = W.gen_kara(cfg, seed=0, threads=16)
+    base = device_cache(se, cfg, inp["cache"], dev)
+    S, B, G, row = cfg.steps, cfg.B, cfg.hkv, cfg.d * 2
+    q0 = inp["q_first_pos"]
+    k_new = [to_dev_bf16(inp["k_new"][t], dev) for t in range(S)]
+    v_new = [to_dev_bf16(inp["v_new"][t], dev) for t in range(S)]
+    q_dec = [to_dev_bf16(np.ascontiguousarray(inp["q_all"][:, :, cfg.N + t - q0]), dev) for t in range(S)]
+    pos = [torch.full((B,), cfg.N + t, dtype=torch.int32, device=dev) for t in range(S)]
+    # each event's window queries are those of its sequences' `window` most recent tokens: a slice of the stored
+    # queries, staged per scheduled run before timing (the schedules do not depend on the data)
+    q_run = {}
+    kw = dict(period=cfg.period, window=cfg.window, protect=cfg.protect, n_cand=cfg.n_cand, budget=cfg.budget,
+              max_gap=cfg.max_gap, scale=inp["scale"])
+    for policy in WF.CompressionLoop.POLICIES:
+        probe = WF.CompressionLoop(base, policy=policy, **kw)
+        for t in range(S):
+            s = cfg.N + t + 1 - cfg.window - q0
+            for b0, b1 in probe.due(t):
+                if (b0, b1, t) not in q_run:
+                    q_run[(b0, b1, t)] = to_dev_bf16(
+                        np.ascontiguousarray(inp["q_all"][b0:b1, :, s:s + cfg.window]), dev)
+
+    def window_queries(b0, b1, t):
+        return q_run[(b0, b1, t)]
+
+    del inp
+    torch.cuda.synchronize()
+    log(f"{cfg.name}: inputs ready in {time.time() - t0:.1f} s, {torch.cuda.memory_allocated() / 2**30:.1f} GiB "
+        f"resident")
+
+    results = {}
+    for policy in WF.CompressionLoop.POLICIES:
+        # untimed pass: warms up and records each step's view size (the kernels are deterministic, so the timed
+        # pass on a fresh copy sees the same sizes)
+        loop = WF.CompressionLoop(base.clone(), policy=policy, **kw)
+        view_rows = []
+        for t in range(S):
+            loop.decode(k_new[t], v_new[t], pos[t], q_dec[t])
+            view_rows.append(int(loop.cache.n_slots.sum()))
+            for b0, b1 in loop.due(t):
+                loop.compress(b0, b1, window_queries(b0, b1, t))
+        del loop
+        loop = WF.CompressionLoop(base.clone(), policy=policy, **kw)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(S)]
+        compress_steps = []
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        for t in range(S):
+            e = ev[t]
+            se.se_cache_append(loop.cache, k_new[t], v_new[t], pos[t])
+            e[0].record()
+            se.se_sparse_decode_attn(loop.cache, q_dec[t], loop.out, scale=loop.scale)
+            e[1].record()
+            runs = loop.due(t)
+            if runs:
+                compress_steps.append(t)
+                for b0, b1 in runs:
+                    loop.compress(b0, b1, window_queries(b0, b1, t))
+                e[2].record()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t_start
+        dec_ms = [ev[t][0].elapsed_time(ev[t][1]) for t in range(S)]
+        comp_ms = sum(ev[t][1].elapsed_time(ev[t][2]) for t in compress_steps)
+        n_events = sum(len(loop.due(t)) for t in range(S))
+        dec_bytes = float(np.mean(view_rows)) * (2 * row + 4) + B * cfg.hq * cfg.d * (2 + 4)
+        results[policy] = {
+            "ms_per_step": round(elapsed * 1e3 / S, 4),
+            "tokens_per_s": round(B * S / elapsed, 1),
+            "events": n_events,
+            "decode_ms": round(float(np.mean(dec_ms)), 4),
+            "decode_gb_s": round(dec_bytes / (float(np.mean(dec_ms)) * 1e-3) / 1e9, 1),
+            "compress_ms_total": round(comp_ms, 3),
+            "compress_share": round(comp_ms / (elapsed * 1e3), 4),
+        }
+        log(f"{policy}: {results[policy]}")
+        del loop
+        torch.cuda.empty_cache()
+
+    per = results["periodic"]
+    a = per["decode_gb_s"]
+    return {
+        "metric": "decode tokens/s",
+        "value": per["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": S,
+        "warmup": S,
+        "ms_per_step": per["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "batch": B, "seq_len": cfg.N, "q_heads": cfg.hq, "kv_heads": cfg.hkv,
+                   "head_dim": cfg.d, "page": cfg.page, "window": cfg.window, "period": cfg.period,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": a, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(a / HBM_PEAK_GBS, 4), "kernel": "se_sparse_decode_attn",
+                     "launches": CALL_KERNELS["se_sparse_decode_attn"],
+                     "traffic": measured_traffic(cfg.name, "se_sparse_decode_attn")},
+        "policies": results,
+        "threshold_vs_periodic": round(results["threshold"]["tokens_per_s"] / per["tokens_per_s"], 4),
+    }
+
+
 def cpu_baseline(inp, n_seq, min_seconds):
     """The oracle (as it stands) on the first n_seq sequences of the SnapKV workload, timed on the host cores: the
     whole event on that sample, repeated until at least min_seconds have passed."""
@@ -517,7 +633,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="c1", choices=sorted(SETUPS))
+    ap.add_argument("--workload", default="c1", choices=sorted(SETUPS) + ["c8"])
     ap.add_argument("--cpu-seqs", type=int, default=8)
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle time for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -558,6 +674,9 @@ def main():
     from sparse_decode_attention_se_amd import workflows as WF
 
     dev = "cuda:0"
+    if args.workload == "c8":
+        print(json.dumps(run_policy_loop(se, WF, W, dev)), flush=True)
+        return
     t0 = time.time()
     cfg, steps, tokens, alg, inp = SETUPS[args.workload](se, WF, W, copies, dev)
     torch.cuda.synchronize()

@@ -102,6 +102,18 @@ class DeviceCache:
         return DeviceCache(self.n_q, **{f: (None if getattr(self, f) is None else getattr(self, f).clone())
                                         for f in self.FIELDS})
 
+    SHARED = ("k_pool", "v_pool", "free_blocks", "free_top")
+
+    def seq_view(self, b0, b1):
+        """Sequences [b0, b1) as a cache of their own, without copying: the per-sequence tensors are views of
+        those rows and the block pool and free-block stack are this cache's (blocks are shared by every
+        sequence). A call on the view reads and changes those sequences alone, plus the shared pool and stack."""
+        B = self.block_table.shape[0]
+        if not 0 <= b0 < b1 <= B:
+            raise ValueError(f"sequence range [{b0}, {b1}) outside [0, {B})")
+        return DeviceCache(self.n_q, **{f: (getattr(self, f) if f in self.SHARED or getattr(self, f) is None
+                                            else getattr(self, f)[b0:b1]) for f in self.FIELDS})
+
     @property
     def device(self):
         return self.k_pool.device

@@ -151,6 +151,84 @@ class KaraEvent:
                          status=self.status)
 
 
+class CompressionLoop:
+    """A decode loop whose compression follows a policy (KARA page, "Method" part 3: KvLLM compresses the
+    trailing blocks of selected sequences every fixed number of decode steps; "Problem" point 1: threshold-
+    triggered policies compress a sequence when its cache reaches a threshold, and fire more and more often as
+    concurrency grows).
+
+    Each step appends every sequence's token and attends over its resident slots, the whole batch at once. Then
+    the sequences the policy names are compressed by Kara's event (bidirectional window scores, top-K candidates,
+    Token2Chunk, trailing-window compaction) on a view of each run of consecutive sequences, so the other
+    sequences are not touched.
+      periodic:  every sequence after every ``period``-th step (one batched event);
+      threshold: sequence b joins with an uncompressed tail of (b * period) // B tokens and is compressed when
+                 the tail reaches ``period`` tokens, so events of a few sequences fall at almost every step.
+    The caller supplies each event's window queries (those of the sequences' ``window`` most recent tokens).
+    """
+
+    POLICIES = ("periodic", "threshold")
+
+    def __init__(self, cache, *, policy, period, window, protect, n_cand, budget, max_gap, scale, status=None):
+        if policy not in self.POLICIES:
+            raise ValueError(f"policy must be one of {self.POLICIES}")
+        B, G, S, d = _dims(cache)
+        dev = cache.device
+        self.cache, self.policy, self.period = cache, policy, int(period)
+        self.window, self.protect, self.n_cand, self.budget, self.max_gap = window, protect, n_cand, budget, max_gap
+        self.scale, self.status, self.B = scale, status, B
+        R = window - protect
+        self.scores = torch.zeros((B, G, R), dtype=torch.float32, device=dev)
+        self.cand = torch.zeros((B, G, n_cand + protect), dtype=torch.int32, device=dev)
+        self.cand_count = torch.zeros((B, G), dtype=torch.int32, device=dev)
+        self.keep = torch.zeros((B, G, max(budget, n_cand) + protect), dtype=torch.int32, device=dev)
+        self.keep_count = torch.zeros((B, G), dtype=torch.int32, device=dev)
+        self.out = torch.zeros((B, cache.n_q, d), dtype=torch.float32, device=dev)
+
+    def due(self, t):
+        """Runs [b0, b1) of consecutive sequences to compress after decode step t (0-based)."""
+        P, B = self.period, self.B
+        if self.policy == "periodic":
+            seqs = range(B) if (t + 1) % P == 0 else ()
+        else:
+            seqs = [b for b in range(B) if (t + 1 + (b * P) // B) % P == 0]
+        runs = []
+        for b in seqs:
+            if runs and runs[-1][1] == b:
+                runs[-1][1] = b + 1
+            else:
+                runs.append([b, b + 1])
+        return [tuple(r) for r in runs]
+
+    def decode(self, k_new, v_new, pos, q):
+        se_cache_append(self.cache, k_new, v_new, pos, status=self.status)
+        se_sparse_decode_attn(self.cache, q, self.out, scale=self.scale, status=self.status)
+        return self.out
+
+    def compress(self, b0, b1, q_win):
+        """Kara's event on sequences [b0, b1); q_win [b1-b0][n_q][window][d]."""
+        view = self.cache.seq_view(b0, b1)
+        sc, cand, cc = self.scores[b0:b1], self.cand[b0:b1], self.cand_count[b0:b1]
+        keep, kc = self.keep[b0:b1], self.keep_count[b0:b1]
+        w, pr = self.window, self.protect
+        se_window_score(view, q_win, None, sc, scale=self.scale, mode=SE_SCORE_BIDIR, n_query=w, window=w,
+                        protect=pr, status=self.status)
+        se_topk_select(view, sc, cand, cc, mode=SE_TOPK_LARGEST, unit=SE_UNIT_SLOT, k=self.n_cand, window=w,
+                       protect=pr, status=self.status)
+        se_token2chunk(view, cand, cc, sc, keep, kc, max_gap=self.max_gap, budget=self.budget, window=w, protect=pr,
+                       status=self.status)
+        se_compact_evict(view, keep, kc, mode=SE_COMPACT_GATHER, window=w, status=self.status)
+
+    def step(self, t, k_new, v_new, pos, q, window_queries):
+        """Decode step t, then the events it triggers; window_queries(b0, b1) gives an event's queries.
+        Returns the step's attention output and the runs compressed."""
+        out = self.decode(k_new, v_new, pos, q)
+        runs = self.due(t)
+        for b0, b1 in runs:
+            self.compress(b0, b1, window_queries(b0, b1))
+        return out, runs
+
+
 class DecodeStep:
     """Append this step's token, then attend over every resident slot (optionally accumulating H2O scores)."""
 

@@ -86,3 +86,40 @@ def test_workspace_sizes_are_host_only():
     assert lib.se_compact_evict_workspace_size(C.byref(c), C.byref(cp)) >= (2 * 8 + 1) * 4
     cp = _lib.se_compact_params_t(1, 0, 1)
     assert lib.se_compact_evict_workspace_size(C.byref(c), C.byref(cp)) == 0
+
+
+def test_compression_loop_schedule_and_sequence_views_on_host():
+    # host logic only: the workflow's schedule against the oracle's, and a sequence view's tensors are the rows
+    # of the whole cache's (no copy), with the pool and free stack shared
+    import workloads as W
+    from oracle import pipelines as P
+    import sparse_decode_attention_se_amd as se
+    from sparse_decode_attention_se_amd import workflows as WF
+
+    cfg = W.scaled(W.C2, B=12, hq=4, hkv=2, d=16, N=200, window=32, protect=4, period=8, dtype="f32", page=4)
+    inp = W.gen_kara(cfg, seed=1, threads=1)
+    dc = se.DeviceCache.from_arrays(cfg.hq, cfg.dtype, "cpu", **{f: getattr(inp["cache"], f)
+                                                                 for f in se.DeviceCache.FIELDS
+                                                                 if getattr(inp["cache"], f) is not None})
+    for policy in ("periodic", "threshold"):
+        loop = WF.CompressionLoop(dc, policy=policy, period=cfg.period, window=cfg.window, protect=cfg.protect,
+                                  n_cand=cfg.n_cand, budget=cfg.budget, max_gap=cfg.max_gap, scale=inp["scale"])
+        for t in range(3 * cfg.period):
+            assert loop.due(t) == P.runs_of(P.policy_due(policy, t, cfg.B, cfg.period))
+    with pytest.raises(ValueError):
+        WF.CompressionLoop(dc, policy="sometimes", period=8, window=32, protect=4, n_cand=5, budget=6, max_gap=2,
+                           scale=1.0)
+    v = dc.seq_view(3, 7)
+    for f in se.DeviceCache.FIELDS:
+        x, y = getattr(dc, f), getattr(v, f)
+        if x is None:
+            assert y is None
+        elif f in se.DeviceCache.SHARED:
+            assert y is x
+        else:
+            assert y.shape[0] == 4 and y.data_ptr() == x[3].data_ptr() and y.is_contiguous()
+    c = v.desc()
+    assert c.B == 4 and c.block_table == dc.block_table[3].data_ptr() and c.k_pool == dc.k_pool.data_ptr()
+    for bad in ((0, 0), (-1, 2), (5, 13)):
+        with pytest.raises(ValueError):
+            dc.seq_view(*bad)

@@ -438,3 +438,53 @@ def test_chain_cache_resume_suffix_and_lru_reclaim():
     assert se.se_status_read(status) == 0
     compare_cache(dc.to_numpy(), st)
     assert chains.acquire(request + [("A", 648)]) == (0, 648, "A")  # A is still parked
+
+
+@pytest.mark.parametrize("policy", ["periodic", "threshold"])
+def test_compression_policy_loop(policy):
+    # 12 sequences, period 8: the threshold policy's tails start at 0, 0, 1, 2, 2, 3, 4, 4, 5, 6, 6, 7 tokens, so
+    # its events cover one or two consecutive sequences at every step; the periodic policy's cover all twelve
+    banner(f"compression policy loop ({policy}), 12 seqs x 700, window 128, period 8, 24 steps")
+    cfg = W.scaled(W.C2, B=12, N=700, window=128, protect=16, period=8, events=3)
+    inp = W.gen_kara(cfg, seed=5, threads=8)
+    dc = to_device(inp["cache"], cfg.hq)
+    status = status_word()
+    kw = dict(window=cfg.window, protect=cfg.protect, n_cand=cfg.n_cand, budget=cfg.budget, max_gap=cfg.max_gap,
+              scale=inp["scale"])
+    loop = WF.CompressionLoop(dc, policy=policy, period=cfg.period, status=status, **kw)
+    r = cfg.hq // cfg.hkv
+    st = inp["cache"]
+    n_runs = resynced = 0
+    for t in range(cfg.steps):
+        st, o_ref = P.kara_decode_step(inp, st, t)
+        pos = np.full((cfg.B,), cfg.N + t, np.int32)
+        q = np.ascontiguousarray(inp["q_all"][:, :, cfg.N + t - inp["q_first_pos"]])
+        o, runs = loop.step(t, storage_tensor(inp["k_new"][t], "bf16"), storage_tensor(inp["v_new"][t], "bf16"),
+                            i32(pos), storage_tensor(q, "bf16"),
+                            lambda b0, b1: storage_tensor(P.kara_recent_window_queries(inp, b0, b1, t), "bf16"))
+        np.testing.assert_allclose(o.cpu().numpy(), o_ref, atol=2e-3, rtol=0)
+        assert runs == P.runs_of(P.policy_due(policy, t, cfg.B, cfg.period))
+        for b0, b1 in runs:
+            qw = P.kara_recent_window_queries(inp, b0, b1, t)
+            ref = P.kara_event_range(st, qw, b0, b1, **kw)
+            assert_scores_close(loop.scores[b0:b1].cpu().numpy(), ref["scores"],
+                                mass=np.full((b1 - b0, cfg.hkv), r * cfg.window))
+            cand = lists_from(loop.cand[b0:b1], loop.cand_count[b0:b1])
+            keep = lists_from(loop.keep[b0:b1], loop.keep_count[b0:b1])
+            same = True
+            for i in range(b1 - b0):
+                for g in range(cfg.hkv):
+                    base = int(st.n_slots[b0 + i, g]) - cfg.window
+                    assert_sets_match_modulo_ties(cand[i][g], ref["cand"][i][g], ref["scores"][i, g], base=base,
+                                                  floor=1e-6 * r * cfg.window)
+                    same &= keep[i][g].tolist() == ref["keep"][i][g].tolist()
+            if not same:
+                # a near-tie swap among the candidates: continue the oracle from the device's equally valid choice
+                ref = P.kara_event_range(st, qw, b0, b1, keep=keep, **kw)
+                resynced += 1
+            st = ref["cache"]
+            n_runs += 1
+        assert se.se_status_read(status) == 0
+        compare_cache(dc.to_numpy(), st)
+    want_runs = sum(len(P.runs_of(P.policy_due(policy, t, cfg.B, cfg.period))) for t in range(cfg.steps))
+    assert n_runs == want_runs > 0 and resynced <= 1

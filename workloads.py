@@ -246,7 +246,12 @@ C6 = Prune("c6_prune_llama8b", B=8, hq=32, hkv=8, d=128, N=32768, wq=64, range_l
 # H2O's chunked-prefill eviction on the Llama-8B head shape: 8 x 8192 prompt tokens in chunks of 512, budget 2048
 C7 = H2OPrefill("c7_h2o_prefill_llama8b", B=8, hq=32, hkv=8, d=128, N=8192, chunk=512, budget=2048, recent=256)
 
-FULL = {c.name: c for c in (C0, C1, C2, C3, C4, C5, C6, C7)}
+# KvLLM's periodic compression against a threshold trigger on C2's batch: one period of 128 decode steps, every
+# sequence compressed once (all together, or each when its staggered tail reaches 128 tokens)
+C8 = Kara("c8_kvllm_policy_qwen3_4b", B=128, hq=32, hkv=8, d=128, N=16384, window=512, protect=64, cand_frac=0.2,
+          budget_frac=0.2, max_gap=8, period=128, events=1, rho=0.9)
+
+FULL = {c.name: c for c in (C0, C1, C2, C3, C4, C5, C6, C7, C8)}
 
 
 def scaled(cfg, **kw):
