@@ -305,9 +305,9 @@ class ChainCacheIndex:
     session stays parked in its slot (retained KV, positions, cumulative scores and page metadata untouched)
     under its chain id and logical prefix. acquire() finds the parked chain whose prefix is the longest prefix of
     a request's tokens and hands back its slot; otherwise a free slot; otherwise it reclaims the least recently
-    used chain: a whole-cache gather that keeps every resident slot of the other sequences and nothing of the
-    victim's returns the victim's blocks to the free stack. The caller appends the suffix (se_cache_append_chunk)
-    and runs the method on the slot, then parks it again."""
+    used chain: a gather that keeps nothing, on a view of the victim's sequence alone, returns its blocks to the
+    free stack. The caller appends the suffix (se_cache_append_chunk) and runs the method on the slot, then parks
+    it again."""
 
     def __init__(self, cache, status=None):
         self.cache, self.status = cache, status
@@ -338,11 +338,11 @@ class ChainCacheIndex:
         return slot, 0, None
 
     def reclaim(self, slot):
-        """Free every block of one sequence slot (its resident set becomes empty); the others are untouched."""
-        c = self.cache
-        B, G, S = c.pos_map.shape
-        keep = torch.arange(S, dtype=torch.int32, device=c.device).repeat(B, G, 1)
-        count = c.n_slots.clone()
-        count[slot] = 0
-        # the other sequences keep all their slots below n_slots, which must then all be resident
-        se_compact_evict(c, keep, count, mode=SE_COMPACT_GATHER, status=self.status)
+        """Free every block of one sequence slot (its resident set becomes empty): a gather that keeps nothing,
+        on a view of that sequence alone, so the other sequences are neither read nor written."""
+        view = self.cache.seq_view(slot, slot + 1)
+        G = view.pos_map.shape[1]
+        dev = view.device
+        keep = torch.zeros((1, G, 1), dtype=torch.int32, device=dev)
+        count = torch.zeros((1, G), dtype=torch.int32, device=dev)
+        se_compact_evict(view, keep, count, mode=SE_COMPACT_GATHER, status=self.status)

@@ -426,9 +426,12 @@ def test_chain_cache_resume_suffix_and_lru_reclaim():
     # an unrelated request: B, least recently used, is reclaimed and slot 1 takes the new prompt
     top0 = int(st.free_top[0])
     assert chains.acquire([("C", i) for i in range(100)]) == (1, 0, None)
-    keep = [[np.arange(int(st.n_slots[0, g]), dtype=np.int32) for g in range(2)], [np.zeros(0, np.int32)] * 2]
-    st = oracle.compact_gather(st, keep)
+    # the reclaim is a gather that keeps nothing, on the victim's sequence alone
+    victim = oracle.compact_gather(oracle.sequence_range(st, 1, 2), [[np.zeros(0, np.int32)] * 2])
+    st_other = st
+    st = oracle.put_sequence_range(st, victim, 1)
     assert st.n_slots[1].tolist() == [0, 0] and int(st.free_top[0]) > top0
+    np.testing.assert_array_equal(st.pos_map[0], st_other.pos_map[0])
     compare_cache(dc.to_numpy(), st)
     kc, vc = chunk(100), chunk(100)
     counts, pos0 = np.array([0, 100], np.int32), np.array([0, 0], np.int32)
