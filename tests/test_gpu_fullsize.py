@@ -24,12 +24,13 @@ def banner(name):
     print(f"\n[case] {name}", flush=True)
 
 
-def subcache(c: W.CacheState, seqs):
-    """The sequences `seqs` of a cache as a cache of their own (blocks renumbered in order; spare pool empty)."""
+def subcache(c: W.CacheState, seqs, spare=2):
+    """The sequences `seqs` of a cache as a cache of their own (blocks renumbered in order; `spare` free blocks per
+    sequence)."""
     seqs = list(seqs)
     nbs = [int(np.count_nonzero(c.block_table[b] >= 0)) for b in seqs]
     total = sum(nbs)
-    out = W.empty_cache(len(seqs), c.n_kv, c.d, c.page, c.max_blocks, total + len(seqs) * 2, c.dtype,
+    out = W.empty_cache(len(seqs), c.n_kv, c.d, c.page, c.max_blocks, total + len(seqs) * spare, c.dtype,
                         slot_cap=c.slot_stack.shape[2], with_meta=c.page_meta is not None,
                         with_cum=c.cum_score is not None)
     nxt = 0
@@ -198,6 +199,69 @@ def test_kara_full_size_event():
                 if exact[g]:
                     np.testing.assert_allclose(outs[s][b, g * r:(g + 1) * r], o_ref[0, g * r:(g + 1) * r], atol=2e-3,
                                                rtol=0)
+
+
+@pytest.mark.parametrize("policy,seqs", [("threshold", (127, 64)), ("periodic", (0,))])
+def test_policy_loop_full_size(policy, seqs):
+    banner(f"compression policy loop ({policy}), 128 x 16384, one period of 128 steps (oracle on sequences {seqs})")
+    cfg = W.C8
+    inp = W.gen_kara(cfg, seed=0, threads=16)
+    dc = to_device(inp["cache"], cfg.hq)
+    status = status_word()
+    kw = dict(window=cfg.window, protect=cfg.protect, n_cand=cfg.n_cand, budget=cfg.budget, max_gap=cfg.max_gap,
+              scale=inp["scale"])
+    loop = WF.CompressionLoop(dc, policy=policy, period=cfg.period, status=status, **kw)
+    q0 = inp["q_first_pos"]
+    check = set(range(0, cfg.steps, 8)) | {cfg.steps - 1}
+    fired, outs = {}, {}
+    for t in range(cfg.steps):
+        pos = np.full((cfg.B,), cfg.N + t, np.int32)
+        q = np.ascontiguousarray(inp["q_all"][:, :, cfg.N + t - q0])
+        o, runs = loop.step(t, storage_tensor(inp["k_new"][t], "bf16"), storage_tensor(inp["v_new"][t], "bf16"),
+                            i32(pos), storage_tensor(q, "bf16"),
+                            lambda b0, b1: storage_tensor(P.kara_recent_window_queries(inp, b0, b1, t), "bf16"))
+        for b0, b1 in runs:
+            for b in seqs:
+                if b0 <= b < b1:
+                    fired[b] = t
+        if t in check:
+            outs[t] = o[list(seqs)].cpu().numpy()
+    assert se.se_status_read(status) == 0
+    dev = dc.to_numpy()
+    cand = lists_from(loop.cand, loop.cand_count)
+    keep = lists_from(loop.keep, loop.keep_count)
+    scores = loop.scores.cpu().numpy()
+    r = cfg.hq // cfg.hkv
+    for i, b in enumerate(seqs):
+        # each sampled sequence is compressed once, when the schedule says
+        assert fired[b] == [t for t in range(cfg.steps) if b in P.policy_due(policy, t, cfg.B, cfg.period)][0]
+        sub = dict(inp, cfg=W.scaled(cfg, B=1), q_all=inp["q_all"][b:b + 1], k_new=inp["k_new"][:, b:b + 1],
+                   v_new=inp["v_new"][:, b:b + 1])
+        st = subcache(inp["cache"], [b], spare=16)
+        for t in range(cfg.steps):
+            st, _ = oracle.cache_append(st, sub["k_new"][t], sub["v_new"][t], np.full((1,), cfg.N + t, np.int32))
+            if t in check:
+                o_ref, _ = oracle.decode_attn(st, np.ascontiguousarray(sub["q_all"][:, :, cfg.N + t - q0]), inp["scale"])
+                np.testing.assert_allclose(outs[t][i], o_ref[0], atol=2e-3, rtol=0)
+            if t == fired[b]:
+                qw = P.kara_recent_window_queries(sub, 0, 1, t)
+                ref = P.kara_event_range(st, qw, 0, 1, **kw)
+                assert_scores_close(scores[b:b + 1], ref["scores"], mass=np.full((1, cfg.hkv), r * cfg.window))
+                for g in range(cfg.hkv):
+                    assert_sets_match_modulo_ties(cand[b][g], ref["cand"][0][g], ref["scores"][0, g],
+                                                  base=int(st.n_slots[0, g]) - cfg.window, floor=1e-6 * r * cfg.window)
+                if any(keep[b][g].tolist() != ref["keep"][0][g].tolist() for g in range(cfg.hkv)):
+                    # a near-tie swap: continue the oracle from the device's equally valid choice
+                    ref = P.kara_event_range(st, qw, 0, 1, keep=[keep[b]], **kw)
+                st = ref["cache"]
+        ora = {"k_pool": st.k_pool, "v_pool": st.v_pool, "block_table": st.block_table}
+        for g in range(cfg.hkv):
+            n = int(st.n_slots[0, g])
+            assert int(dev["n_slots"][b, g]) == n and int(dev["ctx_len"][b, g]) == int(st.ctx_len[0, g])
+            np.testing.assert_array_equal(dev["pos_map"][b, g, :n], st.pos_map[0, g, :n])
+            for which in ("k_pool", "v_pool"):
+                np.testing.assert_array_equal(resident_rows(dev, cfg.page, which, b, g, n),
+                                              resident_rows(ora, cfg.page, which, 0, g, n))
 
 
 def test_window_scores_repeat_bitwise_at_full_size():
