@@ -17,7 +17,7 @@ from ._lib import (SE_COMPACT_EVICT_SLOTS, SE_COMPACT_GATHER, SE_DEV_CAPACITY, S
 __all__ = [
     "DeviceCache", "SEError", "se_window_score", "se_topk_select", "se_token2chunk", "se_compact_evict",
     "se_cache_append", "se_cache_append_chunk", "se_page_bounds", "se_page_bounds_refresh", "se_sparse_decode_attn", "se_status_read",
-    "se_version", "SE_SCORE_CAUSAL", "SE_SCORE_BIDIR", "SE_TOPK_LARGEST", "SE_TOPK_SMALLEST", "SE_UNIT_SLOT",
+    "se_version", "set_operand_checks", "SE_SCORE_CAUSAL", "SE_SCORE_BIDIR", "SE_TOPK_LARGEST", "SE_TOPK_SMALLEST", "SE_UNIT_SLOT",
     "SE_UNIT_PAGE", "SE_COMPACT_GATHER", "SE_COMPACT_EVICT_SLOTS", "SE_PAGES_BUILD", "SE_PAGES_SCORE",
     "SE_REFRESH_LAST_PAGE", "SE_REFRESH_FROM_PAGE", "SE_DEV_INDEX", "SE_DEV_CAPACITY",
 ]
@@ -32,6 +32,47 @@ class SEError(RuntimeError):
 
 def _ptr(t):
     return None if t is None else C.c_void_p(t.data_ptr())
+
+
+_CHECKS = [True]
+
+
+def set_operand_checks(on):
+    """Turn the binding's host-side operand checks on or off; returns the previous setting. They are on by
+    default; a hot loop whose operands were checked once (same tensors, same shapes) may turn them off to save
+    their Python cost per call."""
+    prev = _CHECKS[0]
+    _CHECKS[0] = bool(on)
+    return prev
+
+
+def _need(call, name, t, n, dtype, device, optional=False):
+    """Host-side check of an operand before its pointer crosses the C ABI: a contiguous tensor of `dtype` on the
+    cache's device holding at least `n` elements (the kernels index it that far)."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{call}: {name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{call}: {name} must be a torch tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{call}: {name} has dtype {t.dtype}, needs {dtype}")
+    if t.device != device:
+        raise ValueError(f"{call}: {name} is on {t.device}, the cache on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{call}: {name} must be contiguous")
+    if t.numel() < n:
+        raise ValueError(f"{call}: {name} holds {t.numel()} elements, needs at least {n}")
+
+
+def _dims(cache):
+    """(B, n_kv, n_q, d, page, max_blocks, num_blocks, pool dtype, device)."""
+    num_blocks, n_kv, page, d = cache.k_pool.shape
+    B, max_blocks = cache.block_table.shape
+    return B, n_kv, cache.n_q, d, page, max_blocks, num_blocks, cache.k_pool.dtype, cache.k_pool.device
+
+
+I32, F32 = torch.int32, torch.float32
 
 
 def _stream(stream):
@@ -136,11 +177,18 @@ class DeviceCache:
 # ---------------------------------------------------------------------------------------------------------------
 def se_window_score(cache, q_win, q_pos, scores, *, scale, mode, n_query, window=0, protect=0, score_stride=None,
                     accumulate=False, status=None, stream=None):
+    stride = score_stride if score_stride is not None else scores.shape[-1]
+    if _CHECKS[0]:
+        B, G, Hq, d, page, mb, nblk, pdt, dev = _dims(cache)
+        call = "se_window_score"
+        _need(call, "q_win", q_win, B * Hq * n_query * d, pdt, dev)
+        _need(call, "q_pos", q_pos, B * n_query, I32, dev, optional=mode != SE_SCORE_CAUSAL)
+        _need(call, "scores", scores, B * G * stride, F32, dev)
+        _need(call, "status", status, 1, I32, dev, optional=True)
     lib = _lib.load()
     st, sp = _stream(stream)
     c = cache.desc()
-    p = _lib.se_window_params_t(scale, mode, n_query, window, protect,
-                                score_stride if score_stride is not None else scores.shape[-1], int(accumulate))
+    p = _lib.se_window_params_t(scale, mode, n_query, window, protect, stride, int(accumulate))
     nb = lib.se_window_score_workspace_size(C.byref(c), C.byref(p))
     ws = _workspace(nb, cache.device, stream)
     _check("se_window_score", lib.se_window_score(C.byref(c), _ptr(q_win), _ptr(q_pos), C.byref(p), _ptr(scores),
@@ -150,14 +198,22 @@ def se_window_score(cache, q_win, q_pos, scores, *, scale, mode, n_query, window
 def se_topk_select(cache, scores, idx, count, *, mode, unit, k, window=0, protect=0, forced_ends=0, budget=0,
                    recent=0, score_stride=None, out_stride=None, prune_range=None, block_refs=None,
                    emit_dropped=False, status=None, stream=None):
+    sstride = score_stride if score_stride is not None else scores.shape[-1]
+    ostride = out_stride if out_stride is not None else idx.shape[-1]
+    if _CHECKS[0]:
+        B, G, Hq, d, page, mb, nblk, pdt, dev = _dims(cache)
+        call = "se_topk_select"
+        _need(call, "scores", scores, B * G * sstride, F32, dev)
+        _need(call, "idx", idx, B * G * ostride, I32, dev)
+        _need(call, "count", count, B * G, I32, dev)
+        _need(call, "block_refs", block_refs, nblk, I32, dev, optional=True)
+        _need(call, "status", status, 1, I32, dev, optional=True)
     lib = _lib.load()
     st, sp = _stream(stream)
     c = cache.desc()
     lo, hi = prune_range if prune_range is not None else (0, 0)
-    p = _lib.se_topk_params_t(mode, unit, k, window, protect, forced_ends, budget, recent,
-                              score_stride if score_stride is not None else scores.shape[-1],
-                              out_stride if out_stride is not None else idx.shape[-1], int(lo), int(hi),
-                              int(emit_dropped), _ptr(block_refs))
+    p = _lib.se_topk_params_t(mode, unit, k, window, protect, forced_ends, budget, recent, sstride, ostride, int(lo),
+                              int(hi), int(emit_dropped), _ptr(block_refs))
     nb = lib.se_topk_select_workspace_size(C.byref(c), C.byref(p))
     ws = _workspace(nb, cache.device, stream)
     _check("se_topk_select", lib.se_topk_select(C.byref(c), _ptr(scores), C.byref(p), _ptr(idx), _ptr(count),
@@ -166,6 +222,15 @@ def se_topk_select(cache, scores, idx, count, *, mode, unit, k, window=0, protec
 
 def se_token2chunk(cache, idx, count, scores, idx_out, count_out, *, max_gap, budget, window, protect,
                    status=None, stream=None):
+    if _CHECKS[0]:
+        B, G, Hq, d, page, mb, nblk, pdt, dev = _dims(cache)
+        call = "se_token2chunk"
+        _need(call, "idx", idx, B * G * idx.shape[-1], I32, dev)
+        _need(call, "count", count, B * G, I32, dev)
+        _need(call, "scores", scores, B * G * scores.shape[-1], F32, dev)
+        _need(call, "idx_out", idx_out, B * G * idx_out.shape[-1], I32, dev)
+        _need(call, "count_out", count_out, B * G, I32, dev)
+        _need(call, "status", status, 1, I32, dev, optional=True)
     lib = _lib.load()
     st, sp = _stream(stream)
     c = cache.desc()
@@ -175,6 +240,12 @@ def se_token2chunk(cache, idx, count, scores, idx_out, count_out, *, max_gap, bu
 
 
 def se_compact_evict(cache, idx, count, *, mode, window=0, status=None, stream=None):
+    if _CHECKS[0]:
+        B, G, Hq, d, page, mb, nblk, pdt, dev = _dims(cache)
+        call = "se_compact_evict"
+        _need(call, "idx", idx, B * G * idx.shape[-1], I32, dev)
+        _need(call, "count", count, B * G, I32, dev)
+        _need(call, "status", status, 1, I32, dev, optional=True)
     lib = _lib.load()
     st, sp = _stream(stream)
     c = cache.desc()
@@ -186,6 +257,13 @@ def se_compact_evict(cache, idx, count, *, mode, window=0, status=None, stream=N
 
 
 def se_cache_append(cache, k_new, v_new, pos, *, status=None, stream=None):
+    if _CHECKS[0]:
+        B, G, Hq, d, page, mb, nblk, pdt, dev = _dims(cache)
+        call = "se_cache_append"
+        _need(call, "k_new", k_new, B * G * d, pdt, dev)
+        _need(call, "v_new", v_new, B * G * d, pdt, dev)
+        _need(call, "pos", pos, B, I32, dev)
+        _need(call, "status", status, 1, I32, dev, optional=True)
     lib = _lib.load()
     st, sp = _stream(stream)
     c = cache.desc()
@@ -196,10 +274,18 @@ def se_cache_append(cache, k_new, v_new, pos, *, status=None, stream=None):
 def se_cache_append_chunk(cache, k_new, v_new, pos0, *, counts=None, status=None, stream=None):
     """Append T tokens per (sequence, KV head) at the high-water slots (counts[b] <= T for sequence b when given);
     k_new, v_new [B][n_kv][T][d], pos0 [B]."""
+    T = int(k_new.shape[2])
+    if _CHECKS[0]:
+        B, G, Hq, d, page, mb, nblk, pdt, dev = _dims(cache)
+        call = "se_cache_append_chunk"
+        _need(call, "k_new", k_new, B * G * T * d, pdt, dev)
+        _need(call, "v_new", v_new, B * G * T * d, pdt, dev)
+        _need(call, "pos0", pos0, B, I32, dev)
+        _need(call, "counts", counts, B, I32, dev, optional=True)
+        _need(call, "status", status, 1, I32, dev, optional=True)
     lib = _lib.load()
     st, sp = _stream(stream)
     c = cache.desc()
-    T = int(k_new.shape[2])
     nb = lib.se_cache_append_chunk_workspace_size(C.byref(c), T)
     ws = _workspace(nb, cache.device, stream)
     _check("se_cache_append_chunk", lib.se_cache_append_chunk(C.byref(c), _ptr(k_new), _ptr(v_new), _ptr(pos0), T,
@@ -207,10 +293,16 @@ def se_cache_append_chunk(cache, k_new, v_new, pos0, *, counts=None, status=None
 
 
 def se_page_bounds(cache, op, q=None, page_scores=None, *, status=None, stream=None):
+    stride = 0 if page_scores is None else page_scores.shape[-1]
+    if _CHECKS[0]:
+        B, G, Hq, d, page, mb, nblk, pdt, dev = _dims(cache)
+        call = "se_page_bounds"
+        _need(call, "q", q, B * Hq * d, pdt, dev, optional=op != SE_PAGES_SCORE)
+        _need(call, "page_scores", page_scores, B * G * stride, F32, dev, optional=op != SE_PAGES_SCORE)
+        _need(call, "status", status, 1, I32, dev, optional=True)
     lib = _lib.load()
     st, sp = _stream(stream)
     c = cache.desc()
-    stride = 0 if page_scores is None else page_scores.shape[-1]
     _check("se_page_bounds", lib.se_page_bounds(C.byref(c), op, _ptr(q), _ptr(page_scores), stride, _ptr(status),
                                                 None, 0, sp))
 
@@ -219,6 +311,10 @@ def se_page_bounds_refresh(cache, mode, page_lo=None, max_pages=0, *, status=Non
     """Quest metadata maintenance: BUILD's values for the last page of each unit (SE_REFRESH_LAST_PAGE) or for
     pages [page_lo[u], ceil(n_slots/page)), at most max_pages per unit (SE_REFRESH_FROM_PAGE; page_lo None =
     page 0; max_pages 0 = the block table's width)."""
+    if _CHECKS[0]:
+        B, G, Hq, d, page, mb, nblk, pdt, dev = _dims(cache)
+        _need("se_page_bounds_refresh", "page_lo", page_lo, B * G, I32, dev, optional=True)
+        _need("se_page_bounds_refresh", "status", status, 1, I32, dev, optional=True)
     lib = _lib.load()
     st, sp = _stream(stream)
     c = cache.desc()
@@ -229,10 +325,19 @@ def se_page_bounds_refresh(cache, mode, page_lo=None, max_pages=0, *, status=Non
 
 def se_sparse_decode_attn(cache, q, out, *, scale, sel_pages=None, sel_count=None, max_sel=0, max_slots=0,
                           accumulate=False, status=None, stream=None, ws=None):
+    has_sel = sel_pages is not None
+    if _CHECKS[0]:
+        B, G, Hq, d, page, mb, nblk, pdt, dev = _dims(cache)
+        call = "se_sparse_decode_attn"
+        _need(call, "q", q, B * Hq * d, pdt, dev)
+        _need(call, "out", out, B * Hq * d, F32, dev)
+        _need(call, "sel_pages", sel_pages, B * G * (sel_pages.shape[-1] if has_sel else 0), I32, dev,
+              optional=True)
+        _need(call, "sel_count", sel_count, B * G, I32, dev, optional=not has_sel)
+        _need(call, "status", status, 1, I32, dev, optional=True)
     lib = _lib.load()
     st, sp = _stream(stream)
     c = cache.desc()
-    has_sel = sel_pages is not None
     p = _lib.se_decode_params_t(scale, sel_pages.shape[-1] if has_sel else 0,
                                 (max_sel or sel_pages.shape[-1]) if has_sel else 0, max_slots, int(accumulate))
     nb = lib.se_sparse_decode_attn_workspace_size(C.byref(c), C.byref(p), int(has_sel))

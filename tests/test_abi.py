@@ -123,3 +123,37 @@ def test_compression_loop_schedule_and_sequence_views_on_host():
     for bad in ((0, 0), (-1, 2), (5, 13)):
         with pytest.raises(ValueError):
             dc.seq_view(*bad)
+
+
+def test_binding_rejects_bad_operands_before_the_library():
+    # the kernels index operands by the cache's sizes: a short, mistyped or strided tensor is refused on the host
+    import torch
+
+    import sparse_decode_attention_se_amd as se
+    import workloads as W
+
+    cfg = W.scaled(W.C2, B=3, hq=4, hkv=2, d=16, N=64, window=32, protect=4, period=4, dtype="f32", page=4)
+    inp = W.gen_kara(cfg, seed=1, threads=1)
+    dc = se.DeviceCache.from_arrays(cfg.hq, cfg.dtype, "cpu", **{f: getattr(inp["cache"], f)
+                                                                 for f in se.DeviceCache.FIELDS
+                                                                 if getattr(inp["cache"], f) is not None})
+    k = torch.zeros((3, 2, 16), dtype=torch.float32)
+    pos = torch.zeros(3, dtype=torch.int32)
+    with pytest.raises(ValueError, match="k_new holds"):
+        se.se_cache_append(dc, k[:2], k, pos)
+    with pytest.raises(TypeError, match="dtype"):
+        se.se_cache_append(dc, k, k, pos.long())
+    with pytest.raises(ValueError, match="contiguous"):
+        se.se_cache_append(dc, k.transpose(0, 1), k, pos)
+    with pytest.raises(ValueError, match="required"):
+        se.se_cache_append(dc, k, None, pos)
+    q = torch.zeros((3, 4, 16), dtype=torch.float32)
+    with pytest.raises(ValueError, match="out holds"):
+        se.se_sparse_decode_attn(dc, q, torch.zeros((3, 4, 8)), scale=0.25)
+    scores = torch.zeros((3, 2, 28), dtype=torch.float32)
+    with pytest.raises(ValueError, match="q_win holds"):
+        se.se_window_score(dc, torch.zeros((3, 4, 31, 16)), None, scores, scale=0.25, mode=se.SE_SCORE_BIDIR,
+                           n_query=32, window=32, protect=4)
+    with pytest.raises(ValueError, match="count holds"):
+        se.se_topk_select(dc, scores, torch.zeros((3, 2, 28), dtype=torch.int32), torch.zeros((3, 1), dtype=torch.int32),
+                          mode=se.SE_TOPK_LARGEST, unit=se.SE_UNIT_SLOT, k=4, window=32, protect=4)
