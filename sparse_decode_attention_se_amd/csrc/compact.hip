@@ -489,14 +489,17 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
   const int units = a.B * a.n_kv;
   const int cap = a.max_blocks * a.page;
   if (threadIdx.x == 0) s_fail = 0;
+  // loads that depend on nothing go out first: the free-stack top and each unit's high-water mark
+  const int top0 = *a.free_top;
   __syncthreads();
   for (int unit = threadIdx.x; unit < units; unit += kAppendThreads) {
     int top = a.slot_cap > 0 ? a.slot_top[unit] : 0;
+    const int hw = a.n_slots[unit];
     if (top < 0 || top > a.slot_cap) {
       atomicOr(&s_fail, 1);
       top = 0;
     }
-    int slot = top > 0 ? a.slot_stack[(int64_t)unit * a.slot_cap + top - 1] : a.n_slots[unit];
+    int slot = top > 0 ? a.slot_stack[(int64_t)unit * a.slot_cap + top - 1] : hw;
     if (slot < 0 || slot >= cap) {
       atomicOr(&s_fail, 1);
       slot = 0;
@@ -529,7 +532,6 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
   __syncthreads();
   // exclusive scan of the pops over sequences, in sequence order
   int carry = 0;
-  const int top0 = *a.free_top;
   if (top0 < 0 || top0 > a.num_blocks) {
     if (threadIdx.x == 0) raise(a.status, SE_DEV_CAPACITY);
     return;
