@@ -491,3 +491,30 @@ def test_compression_policy_loop(policy):
         compare_cache(dc.to_numpy(), st)
     want_runs = sum(len(P.runs_of(P.policy_due(policy, t, cfg.B, cfg.period))) for t in range(cfg.steps))
     assert n_runs == want_runs > 0 and resynced <= 1
+
+
+def test_events_on_disjoint_sequence_views_share_the_free_stack():
+    # two runs compressed one after the other in the same step: each frees blocks onto the one shared stack, and
+    # the sequences between and after them are not touched
+    banner("Kara events on sequence views [0, 2) and [5, 7) of 8 sequences")
+    cfg = W.scaled(W.C2, B=8, N=640, window=128, protect=16, period=8, events=1)
+    inp = W.gen_kara(cfg, seed=9, threads=8)
+    dc = to_device(inp["cache"], cfg.hq)
+    status = status_word()
+    kw = dict(window=cfg.window, protect=cfg.protect, n_cand=cfg.n_cand, budget=cfg.budget, max_gap=cfg.max_gap,
+              scale=inp["scale"])
+    loop = WF.CompressionLoop(dc, policy="threshold", period=cfg.period, status=status, **kw)
+    st = inp["cache"]
+    for b0, b1 in ((0, 2), (5, 7)):
+        qw = P.kara_recent_window_queries(inp, b0, b1, -1)
+        loop.compress(b0, b1, storage_tensor(qw, "bf16"))
+        keep = lists_from(loop.keep[b0:b1], loop.keep_count[b0:b1])
+        ref = P.kara_event_range(st, qw, b0, b1, **kw)
+        if any(keep[i][g].tolist() != ref["keep"][i][g].tolist() for i in range(b1 - b0) for g in range(cfg.hkv)):
+            ref = P.kara_event_range(st, qw, b0, b1, keep=keep, **kw)  # a near-tie swap: the device's choice
+        st = ref["cache"]
+        assert se.se_status_read(status) == 0
+        compare_cache(dc.to_numpy(), st)
+    assert int(st.free_top[0]) > int(inp["cache"].free_top[0])
+    np.testing.assert_array_equal(st.pos_map[2:5], inp["cache"].pos_map[2:5])
+    np.testing.assert_array_equal(st.pos_map[7], inp["cache"].pos_map[7])
