@@ -52,15 +52,18 @@ def kara_window_queries(inp, cache):
     return q
 
 
-def kara_event(inp, cache):
+def kara_event(inp, cache, keep=None):
+    """Kara's event on the whole batch. ``keep`` (per (b, g)) replaces the Token2Chunk result when given: an
+    equally valid choice made elsewhere where near-tied scores allow several (teacher forcing)."""
     cfg = inp["cfg"]
     q_win = kara_window_queries(inp, cache)
     scores = window_score_bidir(cache, q_win, inp["scale"], cfg.window, cfg.protect)
     cand = topk_largest(scores, cache, cfg.n_cand, window=cfg.window, protect=cfg.protect)
     scores32 = scores.astype(np.float32)
-    keep = token2chunk(cand, scores32, cache, max_gap=cfg.max_gap, budget=cfg.budget, window=cfg.window,
-                       protect=cfg.protect)
-    compacted = compact_gather(cache, keep, window=cfg.window)
+    chosen = token2chunk(cand, scores32, cache, max_gap=cfg.max_gap, budget=cfg.budget, window=cfg.window,
+                         protect=cfg.protect)
+    compacted = compact_gather(cache, chosen if keep is None else keep, window=cfg.window)
+    keep = chosen
     return dict(q_win=q_win, scores=scores, cand=cand, keep=keep, cache=compacted)
 
 
@@ -85,24 +88,30 @@ def quest_step(inp, cache=None):
     return dict(meta=meta, page_scores=pscores, pages=pages, out=out, cache=with_meta)
 
 
-def h2o_step(inp, cache, step: int):
+def h2o_step(inp, cache, step: int, evict=None):
+    """One H2O decode step: append, attend with cumulative scores, evict the lowest score outside the recent
+    positions. ``evict`` (per (b, g)) replaces the oracle's choice when given: an equally valid choice made
+    elsewhere where near-tied cumulative scores allow several (teacher forcing); the returned ``evict`` is
+    always the oracle's own."""
     cfg = inp["cfg"]
     pos = np.full((cfg.B,), cfg.N + step, np.int32)
     cache, slots = cache_append(cache, inp["k_new"][step], inp["v_new"][step], pos)
     out, cum = decode_attn(cache, inp["q_steps"][step], inp["scale"], accumulate=True)
     cache.cum_score = cum
-    evict = topk_smallest(cum, cache, 1, budget=cfg.budget, recent=cfg.recent)
-    cache = evict_slots(cache, evict)
+    chosen = topk_smallest(cum, cache, 1, budget=cfg.budget, recent=cfg.recent)
+    cache = evict_slots(cache, chosen if evict is None else evict)
+    evict = chosen
     return cache, dict(out=out, evict=evict, slots=slots, cum=cum)
 
 
-def h2o_prefill_chunk(inp, cache, c: int):
+def h2o_prefill_chunk(inp, cache, c: int, keep=None):
     """Chunk c of H2O's chunked prefill (SparseEngine page, "What it is": H2O keeps cumulative attention scores and
     evicts physically; "How it works": eviction at the prefill hook). The chunk's keys and values are appended
     (the first chunk is already in the cache); the chunk's queries add their causal weights to the cumulative
     scores (float32 storage); then, while the context exceeds the budget, the lowest scores outside the most recent
     positions are evicted. The cache stays dense (compacted after every chunk), so its last ``recent`` slots are
-    the most recent positions and H2O's choice is: keep those, plus the best ``budget - recent`` of the rest."""
+    the most recent positions and H2O's choice is: keep those, plus the best ``budget - recent`` of the rest.
+    ``keep`` replaces that choice when given (teacher forcing, as in ``h2o_step``)."""
     cfg = inp["cfg"]
     lo, hi = c * cfg.chunk, (c + 1) * cfg.chunk
     if c > 0:
@@ -113,9 +122,10 @@ def h2o_prefill_chunk(inp, cache, c: int):
     q_pos = np.broadcast_to(np.arange(lo, hi, dtype=np.int32), (cfg.B, cfg.chunk))
     s = window_score_causal(cache, inp["q_all"][:, :, lo:hi], q_pos, inp["scale"])
     cache.cum_score = (cache.cum_score.astype(np.float64) + s).astype(np.float32)
-    keep = topk_largest(cache.cum_score, cache, cfg.budget - cfg.recent, protect=cfg.recent)
+    chosen = topk_largest(cache.cum_score, cache, cfg.budget - cfg.recent, protect=cfg.recent)
     cum = cache.cum_score.copy()
-    cache = compact_gather(cache, keep)
+    cache = compact_gather(cache, chosen if keep is None else keep)
+    keep = chosen
     return cache, dict(scores=s, keep=keep, cum=cum)
 
 

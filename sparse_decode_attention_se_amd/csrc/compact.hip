@@ -247,9 +247,17 @@ __global__ __launch_bounds__(kMoveThreads) void gather_move(GatherArgs a) {
         if (t0 + threadIdx.x < nlist) {
           j = s_list[t0 + threadIdx.x];
           const int sj = s[j];
-          if (sj >= u.w0 && sj < u.n) src = sj;
+          // outputs below h were validated above; an output j >= h listed here (its destination is a hazardous
+          // reader's source) gets the free movers' checks: ascending, past the kept prefix, inside the unit
+          const bool valid = j < u.h || (sj >= lim && sj < u.n && (j == 0 || s[j - 1] < sj));
+          if (!valid) raise(a.status, SE_DEV_INDEX);
+          else if (sj >= u.w0 && sj < u.n) src = sj;
         }
         prepare_row(a, b, g, unit, threadIdx.x, src, u.w0 + j, s_tile);
+        if (src >= 0 && s_tile.pval[threadIdx.x] < 0) {  // not resident: flagged, not moved
+          raise(a.status, SE_DEV_INDEX);
+          s_tile.soff[threadIdx.x] = -1;
+        }
       }
       __syncthreads();
       move_tile<true>(a, unit, s_tile, kMoveRows);

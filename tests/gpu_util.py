@@ -2,8 +2,11 @@
 import numpy as np
 import torch
 
+import oracle
 import sparse_decode_attention_se_amd as se
 import workloads as W
+from oracle import pipelines as P
+from sparse_decode_attention_se_amd import workflows as WF
 
 DEV = "cuda:0"
 
@@ -36,9 +39,11 @@ def lists_from(idx: torch.Tensor, count: torch.Tensor):
 
 
 def assert_scores_close(gpu: np.ndarray, ora: np.ndarray, mass: np.ndarray, rtol=1e-3, floor=1e-6):
-    """|gpu - ora| <= rtol |ora| + floor * row mass (entries below floor * mass count as ties at zero)."""
-    tol = rtol * np.abs(ora) + floor * mass[..., None]
-    bad = np.abs(gpu.astype(np.float64) - ora) > tol
+    """|gpu - ora| <= rtol |ora| for every score. A pair where both values are below floor * row mass counts as a
+    tie at zero (float32 exponentials underflow and flush where float64 ones do not); no other slack."""
+    g = gpu.astype(np.float64)
+    tie = (np.abs(g) <= floor * mass[..., None]) & (np.abs(ora) <= floor * mass[..., None])
+    bad = (np.abs(g - ora) > rtol * np.abs(ora)) & ~tie
     if bad.any():
         i = np.argwhere(bad)[0]
         raise AssertionError(f"{bad.sum()} scores differ, first at {tuple(i)}: gpu {gpu[tuple(i)]} oracle "
@@ -58,6 +63,16 @@ def assert_sets_match_modulo_ties(gpu_list, ora_list, ora_scores_row, base=0, rt
     return len(G - O)
 
 
+def assert_token2chunk_of(keep_lists, cand_lists, scores32, cache, *, max_gap, budget, window, protect):
+    """Where several results are correct: the device's kept lists must be exactly the oracle's Token2Chunk of the
+    device's own candidates and float32 scores (the fill is a deterministic function of those two)."""
+    want = oracle.token2chunk(cand_lists, scores32, cache, max_gap=max_gap, budget=budget, window=window,
+                              protect=protect)
+    for b, row in enumerate(want):
+        for g, w in enumerate(row):
+            assert np.asarray(keep_lists[b][g]).tolist() == w.tolist(), (b, g)
+
+
 def resident_rows(arrays: dict, page: int, which: str, b: int, g: int, n: int):
     """[n][d] rows of slots 0..n-1 of (b, g) read through the block table (bit patterns)."""
     pool = arrays[which]
@@ -66,8 +81,10 @@ def resident_rows(arrays: dict, page: int, which: str, b: int, g: int, n: int):
     return pool[bt[s // page], g, s % page]
 
 
-def compare_cache(dev: dict, ora: W.CacheState, data=True, cum_exact=True):
-    """Bit-exact comparison of everything the cache defines (slots below n_slots; stack entries below top)."""
+def compare_cache(dev: dict, ora: W.CacheState, data=True, cum_exact=True, cum_mass=None):
+    """Bit-exact comparison of everything the cache defines (slots below n_slots; stack entries below top). With
+    cum_exact False the cumulative scores are compared as scores: 1e-3 relative, values below 1e-6 of the per-unit
+    mass ``cum_mass`` [B][n_kv] on both sides counting as ties at zero."""
     np.testing.assert_array_equal(dev["n_slots"], ora.n_slots)
     np.testing.assert_array_equal(dev["ctx_len"], ora.ctx_len)
     np.testing.assert_array_equal(dev["block_table"], ora.block_table)
@@ -93,5 +110,49 @@ def compare_cache(dev: dict, ora: W.CacheState, data=True, cum_exact=True):
                 if cum_exact:
                     np.testing.assert_array_equal(dev["cum_score"][b, g, :n], ora.cum_score[b, g, :n])
                 else:
-                    np.testing.assert_allclose(dev["cum_score"][b, g, :n], ora.cum_score[b, g, :n], rtol=1e-3,
-                                               atol=1e-6 * 4)
+                    assert cum_mass is not None, "inexact cumulative scores need the unit's mass"
+                    assert_scores_close(dev["cum_score"][b, g, :n][None], ora.cum_score[b, g, :n][None].astype(
+                        np.float64), mass=np.array([cum_mass[b, g]], np.float64))
+
+
+def run_h2o_teacher_forced(inp, dc, st, steps, seqs=None, status=None, check_every=1):
+    """H2O decode steps on the device (every sequence of dc) and on the oracle (the sequences ``seqs`` of the
+    device's batch, held in ``st`` as a cache of their own; all when None), in lock-step. At every step and every
+    sampled head: the decode output within 2e-3, and the device's evicted slot equal to the oracle's or a near tie
+    of it by the oracle's cumulative scores, after which the oracle continues from the device's eviction (teacher
+    forcing). Every ``check_every`` steps the sampled sequences' maps, stacks and cumulative scores are compared."""
+    cfg = inp["cfg"]
+    B_dev = int(dc.pos_map.shape[0])
+    seqs = list(range(B_dev)) if seqs is None else list(seqs)
+    r = cfg.hq // cfg.hkv
+    step = WF.H2OStep(dc, scale=inp["scale"], budget=cfg.budget, recent=cfg.recent, status=status)
+    swaps = 0
+    for s in range(steps):
+        pos = np.full((B_dev,), cfg.N + s, np.int32)
+        o = step.run(storage_tensor(inp["k_new"][s], "bf16"), storage_tensor(inp["v_new"][s], "bf16"), i32(pos),
+                     storage_tensor(inp["q_steps"][s], "bf16")).cpu().numpy()
+        ev_all = lists_from(step.evict, step.evict_count)
+        ev = [ev_all[b] for b in seqs]
+        sub = dict(inp, cfg=W.scaled(cfg, B=len(seqs)), k_new=inp["k_new"][:, seqs], v_new=inp["v_new"][:, seqs],
+                   q_steps=inp["q_steps"][:, seqs])
+        st, info = P.h2o_step(sub, st, s, evict=ev)
+        mass = r * (s + 1)
+        for i, b in enumerate(seqs):
+            np.testing.assert_allclose(o[b], info["out"][i], atol=2e-3, rtol=0)
+            for g in range(cfg.hkv):
+                swaps += assert_sets_match_modulo_ties(ev[i][g], info["evict"][i][g], info["cum"][i, g],
+                                                       floor=1e-6 * mass)
+        if (s + 1) % check_every == 0 or s == steps - 1:
+            d = {f: getattr(dc, f).cpu().numpy() for f in ("n_slots", "ctx_len", "pos_map", "slot_top", "slot_stack",
+                                                          "cum_score")}
+            for i, b in enumerate(seqs):
+                for g in range(cfg.hkv):
+                    n = int(st.n_slots[i, g])
+                    assert int(d["n_slots"][b, g]) == n and int(d["ctx_len"][b, g]) == int(st.ctx_len[i, g])
+                    np.testing.assert_array_equal(d["pos_map"][b, g, :n], st.pos_map[i, g, :n])
+                    t = int(st.slot_top[i, g])
+                    assert int(d["slot_top"][b, g]) == t
+                    np.testing.assert_array_equal(d["slot_stack"][b, g, :t], st.slot_stack[i, g, :t])
+                    assert_scores_close(d["cum_score"][b, g, :n][None], st.cum_score[i, g, :n][None].astype(
+                        np.float64), mass=np.array([float(mass)]))
+    return st, swaps

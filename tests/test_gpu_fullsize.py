@@ -12,8 +12,8 @@ import torch
 import oracle
 import sparse_decode_attention_se_amd as se
 import workloads as W
-from gpu_util import (DEV, assert_scores_close, assert_sets_match_modulo_ties, i32, lists_from, resident_rows,
-                      status_word, storage_tensor, to_device)
+from gpu_util import (DEV, assert_scores_close, assert_sets_match_modulo_ties, assert_token2chunk_of, i32, lists_from,
+                      resident_rows, run_h2o_teacher_forced, status_word, storage_tensor, to_device)
 from oracle import pipelines as P
 from sparse_decode_attention_se_amd import workflows as WF
 
@@ -90,12 +90,14 @@ def test_snapkv_llama8b_full_size():
         ref = P.snapkv_event(sub)
         assert_scores_close(scores[b:b + 1, :, :cfg.N], ref["scores"][:, :, :cfg.N], mass=np.full((1, cfg.hkv),
                                                                                                    r * cfg.wq))
+        swapped = 0
         for g in range(cfg.hkv):
-            nsw = assert_sets_match_modulo_ties(keep[b][g], ref["keep"][0][g], ref["scores"][0, g],
-                                                floor=1e-6 * r * cfg.wq)
-            if nsw == 0:
-                np.testing.assert_allclose(out[b, g * r:(g + 1) * r], ref["out"][0, g * r:(g + 1) * r], atol=2e-3,
-                                           rtol=0)
+            swapped += assert_sets_match_modulo_ties(keep[b][g], ref["keep"][0][g], ref["scores"][0, g],
+                                                     floor=1e-6 * r * cfg.wq)
+        want = ref["out"]
+        if swapped:  # near-tie swaps: the oracle decodes over the device's equally valid choice
+            want, _ = oracle.decode_attn(oracle.compact_gather(sub["cache"], [keep[b]]), sub["q_dec"], inp["scale"])
+        np.testing.assert_allclose(out[b], want[0], atol=2e-3, rtol=0)
 
 
 def test_quest_128k_full_size():
@@ -112,48 +114,37 @@ def test_quest_128k_full_size():
     meta = dc.page_meta.view(torch.int16).cpu().numpy().view(np.uint16)
     np.testing.assert_array_equal(meta, ref["meta"])
     ps = qs.page_scores.cpu().numpy()
-    np.testing.assert_allclose(ps, ref["page_scores"], rtol=1e-3, atol=1e-3)
+    np.testing.assert_allclose(ps, ref["page_scores"], rtol=1e-3, atol=0)
     got = lists_from(qs.pages, qs.count)
-    r = cfg.hq // cfg.hkv
+    swapped = 0
     for b in range(cfg.B):
         for g in range(cfg.hkv):
             assert len(got[b][g]) == cfg.top_pages + 2 and got[b][g][0] == 0 and got[b][g][-1] == cfg.N // 16 - 1
-            nsw = assert_sets_match_modulo_ties(got[b][g], ref["pages"][b][g], ref["page_scores"][b, g])
-            if nsw == 0:
-                np.testing.assert_allclose(out[b, g * r:(g + 1) * r], ref["out"][b, g * r:(g + 1) * r], atol=2e-3,
-                                           rtol=0)
+            swapped += assert_sets_match_modulo_ties(got[b][g], ref["pages"][b][g], ref["page_scores"][b, g])
+    want = ref["out"]
+    if swapped:  # near-tie swaps: the oracle decodes over the device's equally valid page choice
+        want, _ = oracle.decode_attn(ref["cache"], inp["q_dec"], inp["scale"], pages=got)
+    np.testing.assert_allclose(out, want, atol=2e-3, rtol=0)
 
 
-def test_h2o_full_size_first_steps():
-    banner("H2O, 64 x 8192, 12 steps (oracle on sequence 0)")
-    cfg = W.scaled(W.C4, steps=12)
+def test_h2o_full_size_teacher_forced():
+    """H2O at its full shape (64 sequences from 8192 tokens, budget 8192, recent 256) for 128 steps on the device;
+    the oracle follows sequences 0 and 63 step by step on every head: outputs, evictions (teacher-forced at near
+    ties), maps, slot stacks and cumulative scores."""
+    banner("H2O, 64 x 8192, 128 steps (oracle on sequences 0 and 63, every head, every step)")
+    cfg = W.scaled(W.C4, steps=128)
     inp = W.gen_h2o(cfg, seed=0, threads=16)
     dc = to_device(inp["cache"], cfg.hq)
     status = status_word()
-    step = WF.H2OStep(dc, scale=inp["scale"], budget=cfg.budget, recent=cfg.recent, status=status)
-    sub_inp = dict(inp, cfg=W.scaled(cfg, B=1), cache=subcache(inp["cache"], [0]), k_new=inp["k_new"][:, :1],
-                   v_new=inp["v_new"][:, :1], q_steps=inp["q_steps"][:, :1])
-    st = sub_inp["cache"]
-    r = cfg.hq // cfg.hkv
-    diverged = np.zeros(cfg.hkv, bool)
-    for s in range(cfg.steps):
-        st, info = P.h2o_step(sub_inp, st, s)
-        pos = np.full((cfg.B,), cfg.N + s, np.int32)
-        o = step.run(storage_tensor(inp["k_new"][s], "bf16"), storage_tensor(inp["v_new"][s], "bf16"), i32(pos),
-                     storage_tensor(inp["q_steps"][s], "bf16")).cpu().numpy()
-        ev = lists_from(step.evict, step.evict_count)
-        assert all(len(ev[b][g]) == 1 for b in range(cfg.B) for g in range(cfg.hkv))
-        for g in range(cfg.hkv):
-            if diverged[g]:
-                continue
-            np.testing.assert_allclose(o[0, g * r:(g + 1) * r], info["out"][0, g * r:(g + 1) * r], atol=2e-3, rtol=0)
-            if assert_sets_match_modulo_ties(ev[0][g], info["evict"][0][g], info["cum"][0, g],
-                                             floor=1e-6 * r * (s + 1)):
-                diverged[g] = True
+    seqs = (0, cfg.B - 1)
+    st, swaps = run_h2o_teacher_forced(inp, dc, subcache(inp["cache"], seqs), cfg.steps, seqs=seqs, status=status,
+                                       check_every=16)
     assert se.se_status_read(status) == 0
-    dev = dc.to_numpy()
-    assert np.all(dev["ctx_len"] == cfg.budget) and np.all(dev["n_slots"] == cfg.N + 1)
-    assert diverged.mean() <= 0.5
+    ctx = dc.ctx_len.cpu().numpy()
+    n_slots = dc.n_slots.cpu().numpy()
+    # one token in, one out every step once over budget: the context stays at the budget, the slots at budget + 1
+    assert np.all(ctx == cfg.budget) and np.all(n_slots == cfg.N + 1)
+    print(f"near-tie evictions adopted from the device: {swaps}", flush=True)
 
 
 def test_kara_full_size_event():
@@ -187,18 +178,17 @@ def test_kara_full_size_event():
                    k_new=inp["k_new"][:, b:b + 1], v_new=inp["v_new"][:, b:b + 1])
         ref = P.kara_event(sub, sub["cache"])
         assert_scores_close(scores[b:b + 1], ref["scores"], mass=np.full((1, cfg.hkv), r * cfg.window))
-        st = ref["cache"]
-        exact = []
         for g in range(cfg.hkv):
-            nsw = assert_sets_match_modulo_ties(cand[b][g], ref["cand"][0][g], ref["scores"][0, g],
-                                                base=cfg.N - cfg.window, floor=1e-6 * r * cfg.window)
-            exact.append(nsw == 0 and keep[b][g].tolist() == ref["keep"][0][g].tolist())
+            assert_sets_match_modulo_ties(cand[b][g], ref["cand"][0][g], ref["scores"][0, g],
+                                          base=cfg.N - cfg.window, floor=1e-6 * r * cfg.window)
+        assert_token2chunk_of([keep[b]], [cand[b]], scores[b:b + 1], sub["cache"], max_gap=cfg.max_gap,
+                              budget=cfg.budget, window=cfg.window, protect=cfg.protect)
+        if any(keep[b][g].tolist() != ref["keep"][0][g].tolist() for g in range(cfg.hkv)):
+            ref = P.kara_event(sub, sub["cache"], keep=[keep[b]])  # a near-tie swap: the device's choice
+        st = ref["cache"]
         for s in range(cfg.period):
             st, o_ref = P.kara_decode_step(sub, st, s)
-            for g in range(cfg.hkv):
-                if exact[g]:
-                    np.testing.assert_allclose(outs[s][b, g * r:(g + 1) * r], o_ref[0, g * r:(g + 1) * r], atol=2e-3,
-                                               rtol=0)
+            np.testing.assert_allclose(outs[s][b], o_ref[0], atol=2e-3, rtol=0)
 
 
 @pytest.mark.parametrize("policy,seqs", [("threshold", (127, 64)), ("periodic", (0,))])
@@ -250,6 +240,8 @@ def test_policy_loop_full_size(policy, seqs):
                 for g in range(cfg.hkv):
                     assert_sets_match_modulo_ties(cand[b][g], ref["cand"][0][g], ref["scores"][0, g],
                                                   base=int(st.n_slots[0, g]) - cfg.window, floor=1e-6 * r * cfg.window)
+                assert_token2chunk_of([keep[b]], [cand[b]], scores[b:b + 1], st, max_gap=cfg.max_gap,
+                                      budget=cfg.budget, window=cfg.window, protect=cfg.protect)
                 if any(keep[b][g].tolist() != ref["keep"][0][g].tolist() for g in range(cfg.hkv)):
                     # a near-tie swap: continue the oracle from the device's equally valid choice
                     ref = P.kara_event_range(st, qw, 0, 1, keep=[keep[b]], **kw)

@@ -597,6 +597,44 @@ def test_h2o_loop_invariants_brute_force():
             assert res == set(K[g]) and len(res) == 48 and c.ctx_len[0, g] == 48
 
 
+def test_append_into_a_slot_with_a_stale_score_starts_it_at_zero():
+    """H2O's cumulative score of a token is the attention it has received since it was written (SparseEngine page,
+    "What it is": continuous scores during generation). A freed slot may still carry an old score (a caller that
+    freed it without clearing, or stale values past the high-water mark). After one H2O step appends into such a
+    slot, the new token's score must be exactly this step's group weight on it, formed here by an explicit softmax,
+    and every older token's score its old value plus its weight; a new chunk's high-water slots start at zero."""
+    cfg = W.H2O("tiny", B=1, hq=4, hkv=2, d=8, N=20, budget=100, recent=2, steps=1, zipf=1.1, page=4)
+    inp = W.gen_h2o(cfg, seed=4, threads=1)
+    c = inp["cache"]
+    c.cum_score[:] = 3.0  # every slot, resident or not, holds a score of 3
+    for g in range(2):  # free slot 5 the way a careless caller might: its score stays behind
+        c.pos_map[0, g, 5] = -1
+        c.slot_stack[0, g, c.slot_top[0, g]] = 5
+        c.slot_top[0, g] += 1
+        c.ctx_len[0, g] -= 1
+    out, info = P.h2o_step(inp, c, 0)
+    assert info["slots"].tolist() == [[5, 5]]
+    for g in range(2):
+        res = [s for s in range(20) if s == 5 or c.pos_map[0, g, s] >= 0]
+        K = {s: W.bf16_bits_to_f32(inp["k_new"][0, 0, g] if s == 5 else
+                                   c.k_pool[c.block_table[0, s // 4], g, s % 4]).astype(np.float64) for s in res}
+        mass = dict.fromkeys(res, 0.0)
+        for h in (2 * g, 2 * g + 1):
+            q = W.bf16_bits_to_f32(inp["q_steps"][0, 0, h]).astype(np.float64)
+            z = {s: inp["scale"] * float(K[s] @ q) for s in res}
+            den = sum(math.exp(v) for v in z.values())
+            for s in res:
+                mass[s] += math.exp(z[s]) / den
+        assert out.cum_score[0, g, 5] == np.float32(mass[5])
+        for s in res:
+            if s != 5:
+                assert out.cum_score[0, g, s] == np.float32(3.0 + mass[s])
+    # a chunk at the high-water mark: slots 20.. held stale scores of 3 and start at 0
+    kc = np.zeros((1, 2, 3, 8), c.k_pool.dtype)
+    after = oracle.cache_append_chunk(c, kc, kc, np.array([20], np.int32))
+    assert np.all(after.cum_score[0, :, 20:23] == 0) and np.all(after.cum_score[0, :, :5] == 3.0)
+
+
 # ------------------------------------------------------------------ compression policy loop --------------------
 def tiny_kara_loop(B=5, period=8, events=2, cand_frac=0.2, budget_frac=0.2, seed=3):
     cfg = W.scaled(W.C2, B=B, hq=4, hkv=2, d=16, N=300, window=64, protect=8, period=period, events=events,
