@@ -4,12 +4,13 @@
 
 A step is one pass of the workload's hot path over its batch, with every input resident in HBM before timing:
 
-  c1 (default, the headline) SnapKV-style prefill-end eviction on 8 Llama-3.1-8B-shaped sequences x 32768 tokens
-     (32 q / 8 KV heads, d 128, bf16, page 16): causal window scores of the last 64 queries, top-1984 + 64
-     protected keys per KV head, in-place compaction with block freeing, one decode step over the retained KV.
-  c2 Kara periodic compression on 128 Qwen3-4B-shaped sequences x 16384 tokens: bidirectional scores of the
-     trailing 512-token window, top-20% candidates, Token2Chunk, trailing-block compaction, then one decode step
-     (append + attention over the whole cache).
+  c2 (default, the headline: the largest workload) Kara periodic compression on 128 Qwen3-4B-shaped sequences x
+     16384 tokens (32 q / 8 KV heads, d 128, bf16, page 16; an 8.6 GB cache): bidirectional scores of the trailing
+     512-token window, top-20% candidates, Token2Chunk, trailing-block compaction, then one decode step (append +
+     attention over the whole cache).
+  c1 SnapKV-style prefill-end eviction on 8 Llama-3.1-8B-shaped sequences x 32768 tokens: causal window scores of
+     the last 64 queries, top-1984 + 64 protected keys per KV head, in-place compaction with block freeing, one
+     decode step over the retained KV.
   c3 Quest decode on 2 sequences x 131072 tokens: page bounds against the query, top-256 pages + first/last,
      decode attention over the 258 selected pages (page metadata built once, outside the step).
   c4 H2O continuous eviction on 64 sequences at the 8192-token budget: append, decode with cumulative scores,
@@ -26,9 +27,13 @@ A step is one pass of the workload's hot path over its batch, with every input r
      event per step). A step is one decode step; the line reports decode tokens/s under the periodic policy and
      both policies' compression share. --steps and --warmup do not apply (one period, after an untimed pass).
 
-Steps that change the cache destructively, or whose working set would stay in the 256 MB Infinity Cache between
-steps, run each on a pristine copy of the cache (c1, c2, c3, c5, c6, c7). Per-call times come from HIP events on the stream
-the calls are launched on.
+Every workload but c4 changes its cache or would leave its working set in the 256 MB last-level cache between
+steps, so before each of its steps the cache is copied back from one pristine clone and 1 GiB is written to flush
+the last-level cache, outside the timed region; each step's wall time is taken between two device
+synchronisations. c4's steps run back to back on one evolving cache. Per-call times come from HIP events on the
+stream the calls are launched on. Every call reports index and capacity errors into one status word, checked
+after the warm-up and after the timed steps. For c1 and c2 the oracle is timed on the host first, on all cores
+(one worker process per core) and on one core.
 """
 import argparse
 import json
@@ -212,23 +217,46 @@ def copy_ceiling(reps):
 
 
 # ---------------------------------------------------------------------------------------------------------------
-# workloads: each returns (cfg, steps[list of list of (call name, fn)], tokens per step, algorithmic bytes per call,
-# dominant call, inputs for the CPU baseline)
+# workloads: each builds a Workload on the device
 # ---------------------------------------------------------------------------------------------------------------
 
 
-def setup_c1(se, WF, W, copies, dev):
-    cfg = W.C1
-    inp = W.gen_snapkv(cfg, seed=0, threads=16)
-    base = device_cache(se, cfg, inp["cache"], dev)
-    caches = [base] + [base.clone() for _ in range(copies - 1)]
+class Workload:
+    """A benchmark workload on the device.
+
+    step(i) -> [(entry point, fn)]: the calls of step i, in order. restore: None for a workload whose steps run
+    back to back on one evolving cache (H2O); otherwise a function that puts the cache back into its pristine state
+    before a step (a device copy from one pristine clone), outside the timed region. tokens: KV tokens per step (the
+    metric's unit); alg: algorithmic bytes (and flops for scoring) per call of each entry point."""
+
+    def __init__(self, cfg, tokens, alg, step, restore=None):
+        self.cfg, self.tokens, self.alg, self.step, self.restore = cfg, tokens, alg, step, restore
+
+
+def restorer(se, work):
+    """A pristine clone of the cache and a function that copies it back into ``work`` (every field)."""
+    pristine = work.clone()
+
+    def restore():
+        for f in se.DeviceCache.FIELDS:
+            x = getattr(work, f)
+            if x is not None:
+                x.copy_(getattr(pristine, f))
+
+    return restore
+
+
+def setup_c1(se, WF, W, dev, status, steps):
     import torch
 
+    cfg = W.C1
+    inp = W.gen_snapkv(cfg, seed=0, threads=16)
+    c = device_cache(se, cfg, inp["cache"], dev)
     q_win, q_dec = to_dev_bf16(inp["q_win"], dev), to_dev_bf16(inp["q_dec"], dev)
     q_pos = torch.from_numpy(inp["q_pos"]).to(dev)
-    evs = [WF.SnapKVEvent(c, wq=cfg.wq, protect=cfg.protect, keep=cfg.keep, scale=inp["scale"]) for c in caches]
-    steps = [[("se_window_score", lambda e=e: e.score(q_win, q_pos)), ("se_topk_select", e.select),
-              ("se_compact_evict", e.compact), ("se_sparse_decode_attn", lambda e=e: e.decode(q_dec))] for e in evs]
+    e = WF.SnapKVEvent(c, wq=cfg.wq, protect=cfg.protect, keep=cfg.keep, scale=inp["scale"], status=status)
+    calls = [("se_window_score", lambda: e.score(q_win, q_pos)), ("se_topk_select", e.select),
+             ("se_compact_evict", e.compact), ("se_sparse_decode_attn", lambda: e.decode(q_dec))]
     B, G, N, r, row = cfg.B, cfg.hkv, cfg.N, cfg.hq // cfg.hkv, cfg.d * 2
     keep = cfg.keep + cfg.protect
     alg = {
@@ -238,43 +266,43 @@ def setup_c1(se, WF, W, copies, dev):
         "se_compact_evict": {"bytes": 2 * (B * G * keep * row * 2) + 2 * B * G * keep * 4},
         "se_sparse_decode_attn": {"bytes": B * G * keep * row * 2 + B * cfg.hq * cfg.d * (2 + 4)},
     }
-    return cfg, steps, B * N, alg, inp
+    return Workload(cfg, B * N, alg, lambda i: calls, restorer(se, c))
 
 
-def setup_c2(se, WF, W, copies, dev):
-    cfg = W.scaled(W.C2, period=1, events=1)
-    inp = W.gen_kara(cfg, seed=0, threads=16)
-    base = device_cache(se, cfg, inp["cache"], dev)
-    caches = [base] + [base.clone() for _ in range(copies - 1)]
+def setup_c2(se, WF, W, dev, status, steps):
+    """Kara's event on the whole batch (bidirectional window scores, top-K candidates, Token2Chunk, trailing-window
+    compaction), then one decode step (append, attention over every resident slot)."""
     import torch
 
+    cfg = W.scaled(W.C2, period=1, events=1)
+    inp = W.gen_kara(cfg, seed=0, threads=16)
+    c = device_cache(se, cfg, inp["cache"], dev)
     # the fresh cache's trailing window holds positions N - window .. N - 1, the first queries the workload keeps
     assert inp["q_first_pos"] == cfg.N - cfg.window
     q_win = to_dev_bf16(np.ascontiguousarray(inp["q_all"][:, :, :cfg.window]), dev)
     k_new, v_new = to_dev_bf16(inp["k_new"][0], dev), to_dev_bf16(inp["v_new"][0], dev)
     q = to_dev_bf16(np.ascontiguousarray(inp["q_all"][:, :, cfg.N - inp["q_first_pos"]]), dev)
     pos = torch.full((cfg.B,), cfg.N, dtype=torch.int32, device=dev)
-    steps = []
-    for c in caches:
-        ev = WF.KaraEvent(c, window=cfg.window, protect=cfg.protect, n_cand=cfg.n_cand, budget=cfg.budget,
-                          max_gap=cfg.max_gap, scale=inp["scale"])
-        dec = WF.DecodeStep(c, scale=inp["scale"])
-        steps.append([
-            ("se_window_score", lambda ev=ev: se.se_window_score(
-                ev.cache, q_win, None, ev.scores, scale=ev.scale, mode=se.SE_SCORE_BIDIR, n_query=cfg.window,
-                window=cfg.window, protect=cfg.protect)),
-            ("se_topk_select", lambda ev=ev: se.se_topk_select(
-                ev.cache, ev.scores, ev.cand, ev.cand_count, mode=se.SE_TOPK_LARGEST, unit=se.SE_UNIT_SLOT,
-                k=cfg.n_cand, window=cfg.window, protect=cfg.protect)),
-            ("se_token2chunk", lambda ev=ev: se.se_token2chunk(
-                ev.cache, ev.cand, ev.cand_count, ev.scores, ev.keep, ev.keep_count, max_gap=cfg.max_gap,
-                budget=cfg.budget, window=cfg.window, protect=cfg.protect)),
-            ("se_compact_evict", lambda ev=ev: se.se_compact_evict(
-                ev.cache, ev.keep, ev.keep_count, mode=se.SE_COMPACT_GATHER, window=cfg.window)),
-            ("se_cache_append", lambda dec=dec: se.se_cache_append(dec.cache, k_new, v_new, pos)),
-            ("se_sparse_decode_attn", lambda dec=dec: se.se_sparse_decode_attn(dec.cache, q, dec.out,
-                                                                               scale=dec.scale)),
-        ])
+    del inp
+    ev = WF.KaraEvent(c, window=cfg.window, protect=cfg.protect, n_cand=cfg.n_cand, budget=cfg.budget,
+                      max_gap=cfg.max_gap, scale=1.0 / np.sqrt(cfg.d), status=status)
+    dec = WF.DecodeStep(c, scale=ev.scale, status=status)
+    calls = [
+        ("se_window_score", lambda: se.se_window_score(
+            c, q_win, None, ev.scores, scale=ev.scale, mode=se.SE_SCORE_BIDIR, n_query=cfg.window,
+            window=cfg.window, protect=cfg.protect, status=status)),
+        ("se_topk_select", lambda: se.se_topk_select(
+            c, ev.scores, ev.cand, ev.cand_count, mode=se.SE_TOPK_LARGEST, unit=se.SE_UNIT_SLOT,
+            k=cfg.n_cand, window=cfg.window, protect=cfg.protect, status=status)),
+        ("se_token2chunk", lambda: se.se_token2chunk(
+            c, ev.cand, ev.cand_count, ev.scores, ev.keep, ev.keep_count, max_gap=cfg.max_gap,
+            budget=cfg.budget, window=cfg.window, protect=cfg.protect, status=status)),
+        ("se_compact_evict", lambda: se.se_compact_evict(
+            c, ev.keep, ev.keep_count, mode=se.SE_COMPACT_GATHER, window=cfg.window, status=status)),
+        ("se_cache_append", lambda: se.se_cache_append(c, k_new, v_new, pos, status=status)),
+        ("se_sparse_decode_attn", lambda: se.se_sparse_decode_attn(c, q, dec.out, scale=dec.scale,
+                                                                   status=status)),
+    ]
     B, G, N, r, row, W_ = cfg.B, cfg.hkv, cfg.N, cfg.hq // cfg.hkv, cfg.d * 2, cfg.window
     R = W_ - cfg.protect
     kept = cfg.budget + cfg.protect  # upper bound of the retained window
@@ -288,28 +316,24 @@ def setup_c2(se, WF, W, copies, dev):
         "se_cache_append": {"bytes": 2 * B * G * row * 2},
         "se_sparse_decode_attn": {"bytes": B * G * after * (2 * row + 4) + B * cfg.hq * cfg.d * (2 + 4)},
     }
-    return cfg, steps, B * W_, alg, None
+    return Workload(cfg, B * W_, alg, lambda i: calls, restorer(se, c))
 
 
-def setup_c3(se, WF, W, copies, dev):
+def setup_c3(se, WF, W, dev, status, steps):
     cfg = W.C3
     inp = W.gen_quest(cfg, seed=0, threads=16)
-    base = device_cache(se, cfg, inp["cache"], dev)
+    c = device_cache(se, cfg, inp["cache"], dev)
     q = to_dev_bf16(inp["q_dec"], dev)
-    QS = WF.QuestStep(base, top_pages=cfg.top_pages, scale=inp["scale"])
-    QS.build()  # page metadata: built once for the cache, then carried by every copy
-    caches = [base] + [base.clone() for _ in range(copies - 1)]
-    steps = []
-    for c in caches:
-        qs = WF.QuestStep(c, top_pages=cfg.top_pages, scale=inp["scale"])
-        steps.append([
-            ("se_page_bounds", lambda qs=qs: se.se_page_bounds(qs.cache, se.SE_PAGES_SCORE, q, qs.page_scores)),
-            ("se_topk_select", lambda qs=qs: se.se_topk_select(
-                qs.cache, qs.page_scores, qs.pages, qs.count, mode=se.SE_TOPK_LARGEST, unit=se.SE_UNIT_PAGE,
-                k=cfg.top_pages, forced_ends=1)),
-            ("se_sparse_decode_attn", lambda qs=qs: se.se_sparse_decode_attn(
-                qs.cache, q, qs.out, scale=qs.scale, sel_pages=qs.pages, sel_count=qs.count)),
-        ])
+    qs = WF.QuestStep(c, top_pages=cfg.top_pages, scale=inp["scale"], status=status)
+    qs.build()  # page metadata: built once for the cache, outside the step
+    calls = [
+        ("se_page_bounds", lambda: se.se_page_bounds(c, se.SE_PAGES_SCORE, q, qs.page_scores, status=status)),
+        ("se_topk_select", lambda: se.se_topk_select(
+            c, qs.page_scores, qs.pages, qs.count, mode=se.SE_TOPK_LARGEST, unit=se.SE_UNIT_PAGE,
+            k=cfg.top_pages, forced_ends=1, status=status)),
+        ("se_sparse_decode_attn", lambda: se.se_sparse_decode_attn(
+            c, q, qs.out, scale=qs.scale, sel_pages=qs.pages, sel_count=qs.count, status=status)),
+    ]
     B, G, N, row = cfg.B, cfg.hkv, cfg.N, cfg.d * 2
     P_ = N // cfg.page
     sel = cfg.top_pages + 2
@@ -318,35 +342,32 @@ def setup_c3(se, WF, W, copies, dev):
         "se_topk_select": {"bytes": B * G * P_ * 4 + B * G * sel * 4},
         "se_sparse_decode_attn": {"bytes": B * G * sel * cfg.page * (2 * row + 4) + B * cfg.hq * cfg.d * (2 + 4)},
     }
-    return cfg, steps, B * N, alg, None
+    return Workload(cfg, B * N, alg, lambda i: calls, restorer(se, c))
 
 
-def setup_c5(se, WF, W, copies, dev):
+def setup_c5(se, WF, W, dev, status, steps):
     """C3's Quest decode step with its cache maintenance: append the decode token, refresh the metadata of the page
-    it wrote, then page scores, page choice and decode. Every step runs on its own pristine copy, as in C3."""
+    it wrote, then page scores, page choice and decode."""
     import torch
 
     cfg = W.C5
     inp = W.gen_quest(cfg, seed=0, threads=16)
-    base = device_cache(se, cfg, inp["cache"], dev)
+    c = device_cache(se, cfg, inp["cache"], dev)
     q = to_dev_bf16(inp["q_dec"], dev)
     k_new, v_new = to_dev_bf16(inp["k_new"][0], dev), to_dev_bf16(inp["v_new"][0], dev)
     pos = torch.full((cfg.B,), cfg.N, dtype=torch.int32, device=dev)
-    WF.QuestStep(base, top_pages=cfg.top_pages, scale=inp["scale"]).build()
-    caches = [base] + [base.clone() for _ in range(copies - 1)]
-    steps = []
-    for c in caches:
-        qs = WF.QuestStep(c, top_pages=cfg.top_pages, scale=inp["scale"])
-        steps.append([
-            ("se_cache_append", lambda c=c: se.se_cache_append(c, k_new, v_new, pos)),
-            ("se_page_bounds_refresh", lambda qs=qs: qs.refresh_last_page()),
-            ("se_page_bounds", lambda qs=qs: se.se_page_bounds(qs.cache, se.SE_PAGES_SCORE, q, qs.page_scores)),
-            ("se_topk_select", lambda qs=qs: se.se_topk_select(
-                qs.cache, qs.page_scores, qs.pages, qs.count, mode=se.SE_TOPK_LARGEST, unit=se.SE_UNIT_PAGE,
-                k=cfg.top_pages, forced_ends=1)),
-            ("se_sparse_decode_attn", lambda qs=qs: se.se_sparse_decode_attn(
-                qs.cache, q, qs.out, scale=qs.scale, sel_pages=qs.pages, sel_count=qs.count)),
-        ])
+    qs = WF.QuestStep(c, top_pages=cfg.top_pages, scale=inp["scale"], status=status)
+    qs.build()
+    calls = [
+        ("se_cache_append", lambda: se.se_cache_append(c, k_new, v_new, pos, status=status)),
+        ("se_page_bounds_refresh", qs.refresh_last_page),
+        ("se_page_bounds", lambda: se.se_page_bounds(c, se.SE_PAGES_SCORE, q, qs.page_scores, status=status)),
+        ("se_topk_select", lambda: se.se_topk_select(
+            c, qs.page_scores, qs.pages, qs.count, mode=se.SE_TOPK_LARGEST, unit=se.SE_UNIT_PAGE,
+            k=cfg.top_pages, forced_ends=1, status=status)),
+        ("se_sparse_decode_attn", lambda: se.se_sparse_decode_attn(
+            c, q, qs.out, scale=qs.scale, sel_pages=qs.pages, sel_count=qs.count, status=status)),
+    ]
     B, G, N, row = cfg.B, cfg.hkv, cfg.N + 1, cfg.d * 2
     P_ = -(-N // cfg.page)
     sel = cfg.top_pages + 2
@@ -357,28 +378,27 @@ def setup_c5(se, WF, W, copies, dev):
         "se_topk_select": {"bytes": B * G * P_ * 4 + B * G * sel * 4},
         "se_sparse_decode_attn": {"bytes": B * G * sel * cfg.page * (2 * row + 4) + B * cfg.hq * cfg.d * (2 + 4)},
     }
-    return cfg, steps, B * N, alg, None
+    return Workload(cfg, B * N, alg, lambda i: calls, restorer(se, c))
 
 
-def setup_c6(se, WF, W, copies, dev):
+def setup_c6(se, WF, W, dev, status, steps):
     """Range-restricted pruning on the Llama-8B cache: window scores, the range's best slots among idle blocks (the
-    dropped list), slot eviction, then a decode step over the pruned cache. Every step on its own pristine copy."""
+    dropped list), slot eviction, then a decode step over the pruned cache."""
     import torch
 
     cfg = W.C6
     inp = W.gen_prune(cfg, seed=0, threads=16)
-    base = device_cache(se, cfg, inp["cache"], dev)
-    caches = [base] + [base.clone() for _ in range(copies - 1)]
+    c = device_cache(se, cfg, inp["cache"], dev)
     q_win, q_dec = to_dev_bf16(inp["q_win"], dev), to_dev_bf16(inp["q_dec"], dev)
     q_pos = torch.from_numpy(inp["q_pos"]).to(dev)
     refs = torch.from_numpy(inp["block_refs"]).to(dev)
     out = torch.empty((cfg.B, cfg.hq, cfg.d), dtype=torch.float32, device=dev)
-    prs = [WF.PruneRange(c, wq=cfg.wq, scale=inp["scale"]) for c in caches]
-    steps = [[("se_window_score", lambda p=p: p.score(q_win, q_pos)),
-              ("se_topk_select", lambda p=p: p.select(cfg.range_lo, cfg.range_hi, cfg.keep, refs)),
-              ("se_compact_evict", p.evict),
-              ("se_sparse_decode_attn", lambda p=p: se.se_sparse_decode_attn(p.cache, q_dec, out, scale=inp["scale"]))]
-             for p in prs]
+    p = WF.PruneRange(c, wq=cfg.wq, scale=inp["scale"], status=status)
+    calls = [("se_window_score", lambda: p.score(q_win, q_pos)),
+             ("se_topk_select", lambda: p.select(cfg.range_lo, cfg.range_hi, cfg.keep, refs)),
+             ("se_compact_evict", p.evict),
+             ("se_sparse_decode_attn", lambda: se.se_sparse_decode_attn(c, q_dec, out, scale=inp["scale"],
+                                                                        status=status))]
     B, G, N, r, row, page = cfg.B, cfg.hkv, cfg.N, cfg.hq // cfg.hkv, cfg.d * 2, cfg.page
     # slots each unit frees: the idle slots of the range beyond the kept ones (every slot starts resident)
     c0 = inp["cache"]
@@ -392,80 +412,74 @@ def setup_c6(se, WF, W, copies, dev):
         "se_compact_evict": {"bytes": dropped * 4 * 3},
         "se_sparse_decode_attn": {"bytes": (B * G * N - dropped) * row * 2 + B * G * N * 4 + B * cfg.hq * cfg.d * 6},
     }
-    return cfg, steps, B * N, alg, None
+    return Workload(cfg, B * N, alg, lambda i: calls, restorer(se, c))
 
 
-def setup_c7(se, WF, W, copies, dev):
+def setup_c7(se, WF, W, dev, status, steps):
     """H2O's chunked-prefill eviction on 8 x 8192 prompt tokens: per chunk of 512, the chunk appended, its causal
     window scores added to the cumulative scores, the recent 256 plus the best 1792 others kept (the 2048 budget)
-    and the cache compacted in place. One step is the whole prefill (16 chunks) on its own pristine copy."""
+    and the cache compacted in place. One step is the whole prefill (16 chunks)."""
     import torch
 
     cfg = W.C7
     inp = W.gen_h2o_prefill(cfg, seed=0, threads=16)
-    base = device_cache(se, cfg, inp["cache"], dev)
-    caches = [base] + [base.clone() for _ in range(copies - 1)]
+    c = device_cache(se, cfg, inp["cache"], dev)
     n_chunks = cfg.N // cfg.chunk
-    q_ch = [to_dev_bf16(np.ascontiguousarray(inp["q_all"][:, :, c * cfg.chunk:(c + 1) * cfg.chunk]), dev)
-            for c in range(n_chunks)]
-    q_pos = [torch.arange(c * cfg.chunk, (c + 1) * cfg.chunk, dtype=torch.int32, device=dev).repeat(cfg.B, 1)
-             for c in range(n_chunks)]
-    k_ch = [to_dev_bf16(np.ascontiguousarray(inp["k_all"][:, :, c * cfg.chunk:(c + 1) * cfg.chunk]), dev)
-            for c in range(n_chunks)]
-    v_ch = [to_dev_bf16(np.ascontiguousarray(inp["v_all"][:, :, c * cfg.chunk:(c + 1) * cfg.chunk]), dev)
-            for c in range(n_chunks)]
-    pos0 = [torch.full((cfg.B,), c * cfg.chunk, dtype=torch.int32, device=dev) for c in range(n_chunks)]
-
-    steps = []
-    for c in caches:
-        pf = WF.H2OPrefillChunk(c, chunk=cfg.chunk, budget=cfg.budget, recent=cfg.recent, scale=inp["scale"])
-        step = []
-        for k in range(n_chunks):
-            if k > 0:
-                step.append(("se_cache_append_chunk", lambda pf=pf, k=k: pf.append(k_ch[k], v_ch[k], pos0[k])))
-            step += [("se_window_score", lambda pf=pf, k=k: pf.score(q_ch[k], q_pos[k])),
-                     ("se_topk_select", pf.select), ("se_compact_evict", pf.compact)]
-        steps.append(step)
+    sl = [slice(k * cfg.chunk, (k + 1) * cfg.chunk) for k in range(n_chunks)]
+    q_ch = [to_dev_bf16(np.ascontiguousarray(inp["q_all"][:, :, x]), dev) for x in sl]
+    k_ch = [to_dev_bf16(np.ascontiguousarray(inp["k_all"][:, :, x]), dev) for x in sl]
+    v_ch = [to_dev_bf16(np.ascontiguousarray(inp["v_all"][:, :, x]), dev) for x in sl]
+    q_pos = [torch.arange(x.start, x.stop, dtype=torch.int32, device=dev).repeat(cfg.B, 1) for x in sl]
+    pos0 = [torch.full((cfg.B,), x.start, dtype=torch.int32, device=dev) for x in sl]
+    pf = WF.H2OPrefillChunk(c, chunk=cfg.chunk, budget=cfg.budget, recent=cfg.recent, scale=inp["scale"],
+                            status=status)
+    calls = []
+    for k in range(n_chunks):
+        if k > 0:
+            calls.append(("se_cache_append_chunk", lambda k=k: pf.append(k_ch[k], v_ch[k], pos0[k])))
+        calls += [("se_window_score", lambda k=k: pf.score(q_ch[k], q_pos[k])),
+                  ("se_topk_select", pf.select), ("se_compact_evict", pf.compact)]
     B, G, r, row, d = cfg.B, cfg.hkv, cfg.hq // cfg.hkv, cfg.d * 2, cfg.d
     # per chunk k: the keys its queries see (the budget's survivors, then the chunk; the cache is dense), and the
     # rows compaction keeps
     keys = [min(k * cfg.chunk, cfg.budget) + cfg.chunk for k in range(n_chunks)]
-    slots = keys
     kept = [min(kk, cfg.budget) for kk in keys]
     alg = {
         "se_cache_append_chunk": {"bytes": (n_chunks - 1) * B * G * cfg.chunk * (2 * row * 2 + 4)},
-        "se_window_score": {"bytes": sum(B * G * (kk * row + s_ * 8) + B * cfg.hq * cfg.chunk * row
-                                         for kk, s_ in zip(keys, slots)),
+        "se_window_score": {"bytes": sum(B * G * (kk * row + kk * 8) + B * cfg.hq * cfg.chunk * row for kk in keys),
                             "flops": sum(2.0 * B * G * r * cfg.chunk * kk * d for kk in keys)},
-        "se_topk_select": {"bytes": sum(B * G * (s_ * 8 + kp * 4) for s_, kp in zip(slots, kept))},
+        "se_topk_select": {"bytes": sum(B * G * (kk * 8 + kp * 4) for kk, kp in zip(keys, kept))},
         "se_compact_evict": {"bytes": sum(B * G * kp * (2 * row * 2 + 8) for kp in kept)},
     }
-    return cfg, steps, B * cfg.N, alg, None
+    return Workload(cfg, B * cfg.N, alg, lambda i: calls, restorer(se, c))
 
 
-def setup_c4(se, WF, W, copies, dev):
-    cfg = W.scaled(W.C4, steps=copies)
-    inp = W.gen_h2o(cfg, seed=0, threads=16)
-    c = device_cache(se, cfg, inp["cache"], dev)
+def setup_c4(se, WF, W, dev, status, steps):
+    """H2O's decode loop: each step appends its token, attends with cumulative scores, evicts the lowest score
+    outside the recent positions. The steps run back to back on one cache, each with its own token and query."""
     import torch
 
-    h2o = WF.H2OStep(c, scale=inp["scale"], budget=cfg.budget, recent=cfg.recent)
-    k_new = [to_dev_bf16(inp["k_new"][s], dev) for s in range(copies)]
-    v_new = [to_dev_bf16(inp["v_new"][s], dev) for s in range(copies)]
-    q = [to_dev_bf16(inp["q_steps"][s], dev) for s in range(copies)]
-    pos = [torch.full((cfg.B,), cfg.N + s, dtype=torch.int32, device=dev) for s in range(copies)]
-    steps = []
-    for s in range(copies):
-        steps.append([
-            ("se_cache_append", lambda s=s: se.se_cache_append(c, k_new[s], v_new[s], pos[s])),
-            ("se_sparse_decode_attn", lambda s=s: se.se_sparse_decode_attn(c, q[s], h2o.out, scale=h2o.scale,
-                                                                           accumulate=True)),
+    cfg = W.scaled(W.C4, steps=steps)
+    inp = W.gen_h2o(cfg, seed=0, threads=16)
+    c = device_cache(se, cfg, inp["cache"], dev)
+    h2o = WF.H2OStep(c, scale=inp["scale"], budget=cfg.budget, recent=cfg.recent, status=status)
+    k_new = [to_dev_bf16(inp["k_new"][s], dev) for s in range(steps)]
+    v_new = [to_dev_bf16(inp["v_new"][s], dev) for s in range(steps)]
+    q = [to_dev_bf16(inp["q_steps"][s], dev) for s in range(steps)]
+    pos = [torch.full((cfg.B,), cfg.N + s, dtype=torch.int32, device=dev) for s in range(steps)]
+
+    def step(s):
+        return [
+            ("se_cache_append", lambda: se.se_cache_append(c, k_new[s], v_new[s], pos[s], status=status)),
+            ("se_sparse_decode_attn", lambda: se.se_sparse_decode_attn(c, q[s], h2o.out, scale=h2o.scale,
+                                                                       accumulate=True, status=status)),
             ("se_topk_select", lambda: se.se_topk_select(c, c.cum_score, h2o.evict, h2o.evict_count,
                                                          mode=se.SE_TOPK_SMALLEST, unit=se.SE_UNIT_SLOT, k=1,
-                                                         budget=cfg.budget, recent=cfg.recent)),
+                                                         budget=cfg.budget, recent=cfg.recent, status=status)),
             ("se_compact_evict", lambda: se.se_compact_evict(c, h2o.evict, h2o.evict_count,
-                                                             mode=se.SE_COMPACT_EVICT_SLOTS)),
-        ])
+                                                             mode=se.SE_COMPACT_EVICT_SLOTS, status=status)),
+        ]
+
     B, G, row = cfg.B, cfg.hkv, cfg.d * 2
     n = cfg.budget + 1
     alg = {
@@ -474,14 +488,14 @@ def setup_c4(se, WF, W, copies, dev):
         "se_topk_select": {"bytes": B * G * n * 8},
         "se_compact_evict": {"bytes": B * G * 16},
     }
-    return cfg, steps, B * n, alg, None
+    return Workload(cfg, B * n, alg, step)
 
 
 SETUPS = {"c1": setup_c1, "c2": setup_c2, "c3": setup_c3, "c4": setup_c4, "c5": setup_c5, "c6": setup_c6,
           "c7": setup_c7}
 
 
-def run_policy_loop(se, WF, W, dev):
+def run_policy_loop(se, WF, W, dev, status):
     """c8: one period of decode steps under each compression policy. Returns the JSON line."""
     import torch
 
@@ -499,7 +513,7 @@ def run_policy_loop(se, WF, W, dev):
     # queries, staged per scheduled run before timing (the schedules do not depend on the data)
     q_run = {}
     kw = dict(period=cfg.period, window=cfg.window, protect=cfg.protect, n_cand=cfg.n_cand, budget=cfg.budget,
-              max_gap=cfg.max_gap, scale=inp["scale"])
+              max_gap=cfg.max_gap, scale=inp["scale"], status=status)
     for policy in WF.CompressionLoop.POLICIES:
         probe = WF.CompressionLoop(base, policy=policy, **kw)
         for t in range(S):
@@ -528,6 +542,7 @@ def run_policy_loop(se, WF, W, dev):
             view_rows.append(int(loop.cache.n_slots.sum()))
             for b0, b1 in loop.due(t):
                 loop.compress(b0, b1, window_queries(b0, b1, t))
+        require_clean_status(se, status, f"the untimed {policy} pass")
         del loop
         loop = WF.CompressionLoop(base.clone(), policy=policy, **kw)
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(S)]
@@ -537,9 +552,9 @@ def run_policy_loop(se, WF, W, dev):
         t_start = time.perf_counter()
         for t in range(S):
             e = ev[t]
-            se.se_cache_append(loop.cache, k_new[t], v_new[t], pos[t])
+            se.se_cache_append(loop.cache, k_new[t], v_new[t], pos[t], status=status)
             e[0].record()
-            se.se_sparse_decode_attn(loop.cache, q_dec[t], loop.out, scale=loop.scale)
+            se.se_sparse_decode_attn(loop.cache, q_dec[t], loop.out, scale=loop.scale, status=status)
             e[1].record()
             runs = loop.due(t)
             if runs:
@@ -550,6 +565,7 @@ def run_policy_loop(se, WF, W, dev):
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t_start
         se.set_operand_checks(prev)
+        require_clean_status(se, status, f"the timed {policy} pass")
         dec_ms = [ev[t][0].elapsed_time(ev[t][1]) for t in range(S)]
         comp_ms = sum(ev[t][1].elapsed_time(ev[t][2]) for t in compress_steps)
         n_events = sum(len(loop.due(t)) for t in range(S))
@@ -594,40 +610,115 @@ def run_policy_loop(se, WF, W, dev):
     }
 
 
-def cpu_baseline(inp, n_seq, min_seconds):
-    """The oracle (as it stands) on the first n_seq sequences of the SnapKV workload, timed on the host cores: the
-    whole event on that sample, repeated until at least min_seconds have passed."""
+# ---------------------------------------------------------------------------------------------------------------
+# the oracle on the host cores (a baseline, not the target)
+# ---------------------------------------------------------------------------------------------------------------
+
+
+def _oracle_sample(workload, first, n_seq):
+    """Inputs of sequences [first, first + n_seq) of a workload and a function running its step on the oracle once
+    (returns the KV tokens of the metric that step covers)."""
     import oracle.pipelines as P
     import workloads as W
 
-    try:
-        from threadpoolctl import threadpool_info
+    if workload == "c1":
+        cfg = W.scaled(W.C1, B=n_seq)
+        inp = W.gen_snapkv(cfg, seed=0, threads=1, first=first)
+        return lambda: (P.snapkv_event(inp), n_seq * cfg.N)[1]
+    if workload == "c2":
+        cfg = W.scaled(W.C2, B=n_seq, period=1, events=1)
+        inp = W.gen_kara(cfg, seed=0, threads=1, first=first)
 
-        threads = max([x.get("num_threads", 1) for x in threadpool_info()] + [1])
-    except Exception:
-        threads = os.cpu_count() or 1
-    cfg = inp["cfg"]
-    c = inp["cache"]
-    nb = c.max_blocks
-    sub = W.CacheState(
-        k_pool=c.k_pool[:n_seq * nb], v_pool=c.v_pool[:n_seq * nb], block_table=c.block_table[:n_seq].copy(),
-        pos_map=c.pos_map[:n_seq].copy(), ctx_len=c.ctx_len[:n_seq].copy(), n_slots=c.n_slots[:n_seq].copy(),
-        free_blocks=np.zeros((n_seq * nb,), np.int32), free_top=np.zeros((1,), np.int32),
-        slot_stack=c.slot_stack[:n_seq].copy(), slot_top=c.slot_top[:n_seq].copy(), page_meta=None,
-        dtype=c.dtype, page=c.page)
-    sub_inp = dict(inp, cfg=W.scaled(cfg, B=n_seq), cache=sub, q_win=inp["q_win"][:n_seq], q_pos=inp["q_pos"][:n_seq],
-                   q_dec=inp["q_dec"][:n_seq])
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
-        P.snapkv_event(sub_inp)
-        reps += 1
-        dt = time.perf_counter() - t0
-        if dt >= min_seconds:
-            break
-    return {"value": reps * n_seq * cfg.N / dt, "unit": "KV tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{n_seq} of {cfg.B} sequences of the same workload, the whole event (score, select, compact, "
-                      f"decode) {reps} times, {dt:.1f} s"}
+        def run():
+            ev = P.kara_event(inp, inp["cache"])
+            P.kara_decode_step(inp, ev["cache"], 0)
+            return n_seq * cfg.window
+
+        return run
+    raise ValueError(workload)
+
+
+def _oracle_worker(workload, first, n_seq, min_seconds, barrier, results):
+    from threadpoolctl import threadpool_limits
+
+    with threadpool_limits(1):  # one core per worker: numpy's BLAS would otherwise start a pool of its own
+        run = _oracle_sample(workload, first, n_seq)
+        if barrier is not None:
+            barrier.wait()
+        tokens, reps = 0, 0
+        t0 = time.perf_counter()
+        while True:
+            tokens += run()
+            reps += 1
+            dt = time.perf_counter() - t0
+            if dt >= min_seconds:
+                results.put((tokens, reps, dt))
+                return
+
+
+def _run_workers(ctx, workload, n, n_seq, min_seconds):
+    """n forked worker processes, worker w on sequences [w n_seq, (w + 1) n_seq), timed from a common start."""
+    barrier = ctx.Barrier(n) if n > 1 else None
+    results = ctx.Queue()
+    procs = [ctx.Process(target=_oracle_worker, args=(workload, w * n_seq, n_seq, min_seconds, barrier, results))
+             for w in range(n)]
+    for p in procs:
+        p.start()
+    out = [results.get() for _ in procs]
+    for p in procs:
+        p.join()
+        if p.exitcode != 0:
+            raise RuntimeError(f"oracle worker exited with {p.exitcode}")
+    return out
+
+
+def host_cores():
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return n
+
+
+def cpu_baseline(workload, n_seq, min_seconds, max_workers=16):
+    """The oracle as it stands, timed on the host: once with one worker process per core (up to ``max_workers``,
+    each on its own ``n_seq`` sequences of the workload, started together), once on a single core. Each worker runs
+    the workload's step on its sample until ``min_seconds`` have passed. Runs before the GPU is touched (the
+    workers are forked)."""
+    import multiprocessing as mp
+
+    ctx = mp.get_context("fork")
+    avail = host_cores()
+    n = max(1, min(max_workers, avail))
+    res = _run_workers(ctx, workload, n, n_seq, min_seconds)
+    wall = max(r[2] for r in res)
+    tokens = sum(r[0] for r in res)
+    one = _run_workers(ctx, workload, 1, n_seq, min_seconds)[0]
+    what = {"c1": "the whole event (window scores, top-K, compaction, decode)",
+            "c2": "the whole step (Kara's event: window scores, top-K, Token2Chunk, compaction; then append and "
+                  "decode)"}[workload]
+    return {
+        "value": round(tokens / wall, 1), "unit": "KV tokens/s", "cores": n, "kind": "oracle",
+        "sample": f"{n} worker processes (one per core of {avail} available, BLAS limited to one thread each), "
+                  f"worker w on sequences [{n_seq}w, {n_seq}w + {n_seq}) of the same workload, {what}, repeated "
+                  f"for at least {min_seconds:g} s: {sum(r[1] for r in res)} steps of {n_seq} sequences in "
+                  f"{wall:.1f} s",
+        "single_core": {"value": round(one[0] / one[2], 1), "unit": "KV tokens/s", "cores": 1,
+                        "sample": f"sequences [0, {n_seq}), {one[1]} steps in {one[2]:.1f} s"},
+    }
+
+
+def require_clean_status(se, status, when):
+    """Stop the benchmark if any call flagged a device-side error (index or capacity): the figures would be for
+    work that was skipped."""
+    code = se.se_status_read(status)
+    if code != 0:
+        raise SystemExit(f"device status {code:#x} after {when}: a call reported an index or capacity error")
+
+
+def flush_llc(buf):
+    """Write 1 GiB so that nothing a step reads is left in the 256 MB last-level cache."""
+    buf.fill_(0.0)
 
 
 def main():
@@ -635,8 +726,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="c1", choices=sorted(SETUPS) + ["c8"])
-    ap.add_argument("--cpu-seqs", type=int, default=8)
+    ap.add_argument("--workload", default="c2", choices=sorted(SETUPS) + ["c8"])
+    ap.add_argument("--cpu-seqs", type=int, default=2, help="sequences per oracle worker in the CPU baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle time for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, metavar="MIB", help="run only a plain copy of MIB MiB, --steps times")
@@ -657,10 +748,16 @@ def main():
         print("bench.py measures one GPU only: every step works within one (sequence, KV head) and shards across GPUs "
               "by sequence or KV head with no exchange, so one GPU's throughput is the figure", file=sys.stderr)
         sys.exit(2)
-    copies = args.steps + args.warmup
-    if copies > 64:
-        print("steps + warmup must be <= 64 (one pristine cache copy is kept per step)", file=sys.stderr)
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
         sys.exit(2)
+
+    # the host baseline first: its workers are forked, which must happen before anything touches the GPU
+    cpu = None
+    if args.workload in ("c1", "c2") and not args.no_cpu_baseline:
+        log(f"timing the oracle on the host ({host_cores()} cores available)")
+        cpu = cpu_baseline(args.workload, args.cpu_seqs, args.cpu_seconds)
+        log(f"oracle: {cpu['value']:.0f} tokens/s on {cpu['cores']} cores, {cpu['single_core']['value']:.0f} on one")
 
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy, args.steps)
@@ -676,38 +773,62 @@ def main():
     from sparse_decode_attention_se_amd import workflows as WF
 
     dev = "cuda:0"
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
     if args.workload == "c8":
-        print(json.dumps(run_policy_loop(se, WF, W, dev)), flush=True)
+        print(json.dumps(run_policy_loop(se, WF, W, dev, status)), flush=True)
         return
     t0 = time.time()
-    cfg, steps, tokens, alg, inp = SETUPS[args.workload](se, WF, W, copies, dev)
+    wl = SETUPS[args.workload](se, WF, W, dev, status, args.warmup + args.steps)
+    cfg, alg = wl.cfg, wl.alg
+    flush = torch.empty(2**28, dtype=torch.float32, device=dev) if wl.restore else None
     torch.cuda.synchronize()
     log(f"{cfg.name}: inputs ready in {time.time() - t0:.1f} s, {torch.cuda.memory_allocated() / 2**30:.1f} GiB "
         f"resident")
-    status = torch.zeros(1, dtype=torch.int32, device=dev)
-    calls = [name for name, _ in steps[0]]
+    calls = [name for name, _ in wl.step(0)]
+
+    def prepare():
+        # outside the timed region: the pristine cache back, then the last-level cache flushed
+        if wl.restore:
+            wl.restore()
+            flush_llc(flush)
 
     for i in range(args.warmup):
-        for _, fn in steps[i]:
+        prepare()
+        for _, fn in wl.step(i):
             fn()
     torch.cuda.synchronize()
-    # the warm-up steps ran with the binding's operand checks; the timed steps pass tensors of the same shapes and
-    # kinds (cache copies made the same way, the same inputs)
+    require_clean_status(se, status, "the warm-up steps")
+    # the warm-up steps ran with the binding's operand checks; the timed steps pass the same tensors
     se.set_operand_checks(False)
     marks = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in calls]
              for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for i in range(args.steps):
-        for (name, fn), (e0, e1) in zip(steps[args.warmup + i], marks[i]):
-            e0.record()
-            fn()
-            e1.record()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t_start
+    elapsed = 0.0
+    if wl.restore:
+        # each step on a restored cache with a cold last-level cache; the wall time of each step is taken between
+        # two device synchronisations, and the steps' times are summed
+        for i in range(args.steps):
+            prepare()
+            torch.cuda.synchronize()
+            t_start = time.perf_counter()
+            for (name, fn), (e0, e1) in zip(wl.step(args.warmup + i), marks[i]):
+                e0.record()
+                fn()
+                e1.record()
+            torch.cuda.synchronize()
+            elapsed += time.perf_counter() - t_start
+    else:
+        # the steps back to back on one evolving cache
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        for i in range(args.steps):
+            for (name, fn), (e0, e1) in zip(wl.step(args.warmup + i), marks[i]):
+                e0.record()
+                fn()
+                e1.record()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t_start
     se.set_operand_checks(True)
-    if se.se_status_read(status) != 0:
-        raise SystemExit("device status error")
+    require_clean_status(se, status, "the timed steps")
     # per entry point: its time per step (summed over its calls when a step makes several, as C7's chunks do)
     per_call_ms = {}
     for j, n in enumerate(calls):
@@ -735,9 +856,10 @@ def main():
         breakdown[n] = dict(ms=round(per_call_ms[n], 4), **{k: v for k, v in roof(n, "hbm").items() if k != "bound"})
         if "flops" in alg[n]:
             breakdown[n]["mfma_tflops"] = roof(n, "mfma")["achieved"]
+            breakdown[n]["mfma_frac"] = roof(n, "mfma")["frac"]
     result = {
         "metric": "KV tokens scored+compacted/s",
-        "value": round(tokens / (ms_per_step * 1e-3), 1),
+        "value": round(wl.tokens / (ms_per_step * 1e-3), 1),
         "unit": "KV tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -749,15 +871,14 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": cfg.name, "batch": cfg.B, "seq_len": cfg.N, "q_heads": cfg.hq, "kv_heads": cfg.hkv,
-                   "head_dim": cfg.d, "page": cfg.page, "parallelism": "single GPU"},
+                   "head_dim": cfg.d, "page": cfg.page, "parallelism": "single GPU",
+                   "timing": "each step on a restored cache after a last-level-cache flush" if wl.restore
+                   else "steps back to back on one cache"},
         "roofline": roofline,
         "calls": breakdown,
     }
-    if args.workload == "c1" and not args.no_cpu_baseline:
-        del steps
-        torch.cuda.empty_cache()
-        log("timing the oracle on the host")
-        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seqs, args.cpu_seconds)
+    if cpu is not None:
+        result["cpu_baseline"] = cpu
     print(json.dumps(result), flush=True)
 
 

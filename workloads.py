@@ -377,20 +377,21 @@ def _normal(seed, tag, b, shape):
     return rng_for(seed, tag, b).standard_normal(shape)
 
 
-def gen_snapkv(cfg: SnapKV, seed: int = 0, threads: int = 8, num_blocks: int | None = None) -> dict:
-    """Inputs of a SnapKV-style one-shot eviction: the full cache, the window queries and one decode query."""
+def gen_snapkv(cfg: SnapKV, seed: int = 0, threads: int = 8, num_blocks: int | None = None, first: int = 0) -> dict:
+    """Inputs of a SnapKV-style one-shot eviction: the full cache, the window queries and one decode query. With
+    ``first`` > 0 the B sequences are those numbered ``first .. first + B - 1`` of a larger batch."""
     B, hq, hkv, d, N, page = cfg.B, cfg.hq, cfg.hkv, cfg.d, cfg.N, cfg.page
     max_blocks = -(-N // page)
     num_blocks = num_blocks or B * max_blocks
     cache = empty_cache(B, hkv, d, page, max_blocks, num_blocks, cfg.dtype)
     nb = layout_initial(cache, N)
-    q_win = np.stack(_pmap(lambda b: to_storage(_normal(seed, TAG_QWIN, b, (hq, cfg.wq, d)), cfg.dtype),
+    q_win = np.stack(_pmap(lambda b: to_storage(_normal(seed, TAG_QWIN, first + b, (hq, cfg.wq, d)), cfg.dtype),
                            range(B), threads))
 
     def fill(b):
-        k = _normal(seed, TAG_K, b, (hkv, N, d))
+        k = _normal(seed, TAG_K, first + b, (hkv, N, d))
         if cfg.spike_frac > 0:
-            rs = rng_for(seed, TAG_SPIKE, b)
+            rs = rng_for(seed, TAG_SPIKE, first + b)
             n_spike = int(round(cfg.spike_frac * N))
             for g in range(hkv):
                 where = rs.choice(N, size=n_spike, replace=False)
@@ -399,11 +400,11 @@ def gen_snapkv(cfg: SnapKV, seed: int = 0, threads: int = 8, num_blocks: int | N
                 amp = rs.normal(0.0, cfg.spike_std, size=n_spike)
                 k[g, where, :] += amp[:, None] * u[None, :]
         write_sequence(cache.k_pool, nb, b, to_storage(k, cfg.dtype), page)
-        v = _normal(seed, TAG_V, b, (hkv, N, d))
+        v = _normal(seed, TAG_V, first + b, (hkv, N, d))
         write_sequence(cache.v_pool, nb, b, to_storage(v, cfg.dtype), page)
 
     _pmap(fill, range(B), threads)
-    q_dec = np.stack([to_storage(_normal(seed, TAG_QDEC, b, (hq, d)), cfg.dtype) for b in range(B)])
+    q_dec = np.stack([to_storage(_normal(seed, TAG_QDEC, first + b, (hq, d)), cfg.dtype) for b in range(B)])
     q_pos = np.broadcast_to(np.arange(N - cfg.wq, N, dtype=np.int32), (B, cfg.wq)).copy()
     return dict(cfg=cfg, cache=cache, q_win=q_win, q_pos=q_pos, q_dec=q_dec, scale=1.0 / math.sqrt(d))
 
@@ -418,12 +419,14 @@ def _ar1(rng: np.random.Generator, shape_lead, T, d, rho):
     return lfilter([c], [1.0, -rho], eps, axis=-2)
 
 
-def gen_kara(cfg: Kara, seed: int = 0, threads: int = 8) -> dict:
+def gen_kara(cfg: Kara, seed: int = 0, threads: int = 8, first: int = 0) -> dict:
     """Inputs of the periodic sliding-window compression workload.
 
     The cache starts with N tokens. ``q_all`` holds the queries of positions ``[N - window, N + steps)`` (the
     first event's window and every decode step); ``k_new``/``v_new`` hold the keys and values of the appended
     decode tokens (positions ``N .. N + steps - 1``). All are AR(1) along the token axis, per (head, dim).
+    With ``first`` > 0 the B sequences are those numbered ``first .. first + B - 1`` of a larger batch (the same
+    draws, since every sequence has streams of its own).
     """
     B, hq, hkv, d, N, page = cfg.B, cfg.hq, cfg.hkv, cfg.d, cfg.N, cfg.page
     T = N + cfg.steps
@@ -440,15 +443,15 @@ def gen_kara(cfg: Kara, seed: int = 0, threads: int = 8) -> dict:
     q_all = np.zeros((B, hq, T - q0, d), sd)
 
     def fill(b):
-        k = _ar1(rng_for(seed, TAG_K, b), (hkv,), T, d, cfg.rho)
+        k = _ar1(rng_for(seed, TAG_K, first + b), (hkv,), T, d, cfg.rho)
         ks = to_storage(k, cfg.dtype)
         write_sequence(cache.k_pool, nb, b, np.ascontiguousarray(ks[:, :N]), page)
         k_new[:, b] = ks[:, N:].transpose(1, 0, 2)
-        v = _ar1(rng_for(seed, TAG_V, b), (hkv,), T, d, cfg.rho)
+        v = _ar1(rng_for(seed, TAG_V, first + b), (hkv,), T, d, cfg.rho)
         vs = to_storage(v, cfg.dtype)
         write_sequence(cache.v_pool, nb, b, np.ascontiguousarray(vs[:, :N]), page)
         v_new[:, b] = vs[:, N:].transpose(1, 0, 2)
-        q = _ar1(rng_for(seed, TAG_QWIN, b), (hq,), T - q0, d, cfg.rho)
+        q = _ar1(rng_for(seed, TAG_QWIN, first + b), (hq,), T - q0, d, cfg.rho)
         q_all[b] = to_storage(q, cfg.dtype)
 
     _pmap(fill, range(B), threads)
