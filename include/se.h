@@ -48,6 +48,7 @@ enum {
   SE_ERR_WORKSPACE = 5,   /* workspace missing or too small */
   SE_ERR_UNSUPPORTED = 6, /* a combination the library does not implement */
   SE_ERR_HIP = 7,         /* a HIP runtime call failed */
+  SE_ERR_SCRATCH_LIMIT = 8, /* the call needs more scratch than the allocation-free entry point holds */
   /* device status bits, OR-ed into *status */
   SE_DEV_INDEX = 1 << 8,    /* an index list entry out of range, unsorted, duplicated or not resident */
   SE_DEV_CAPACITY = 1 << 9  /* free block stack, slot stack or slot range exhausted */
@@ -267,6 +268,25 @@ size_t se_sparse_decode_attn_workspace_size(const se_cache_t *c, const se_decode
 int32_t se_sparse_decode_attn(se_cache_t *c, const void *q, const int32_t *sel_pages, const int32_t *sel_count,
                               const se_decode_params_t *p, float *out, int32_t *status, void *ws, size_t ws_bytes,
                               se_stream_t stream);
+
+/* ---- decode attention without allocation -----------------------------------------------------------------------
+ * For callers that cannot allocate device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc. Computes exactly what se_sparse_decode_attn computes (the same kernels, the same
+ * results bit for bit), but its scratch (split partials and, when accumulating, the logits) lives in a static
+ * device array of SE_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on until the process ends,
+ * instead of a caller workspace. The caller still passes every input and output. The array's address is looked
+ * up (hipGetSymbolAddress) at the first call on each device, with that device current; the call allocates
+ * nothing, with HIP or otherwise.
+ * Errors: as se_sparse_decode_attn, plus SE_ERR_SCRATCH_LIMIT (nothing launched) when the call's workspace
+ * (se_sparse_decode_attn_workspace_size) exceeds SE_NOALLOC_SCRATCH_BYTES, and SE_ERR_HIP if the lookup fails.
+ * Every call on a GPU shares that GPU's one array: calls that may overlap on one GPU (different streams, or
+ * different threads without ordering) race and must not be issued; calls in order on one stream are safe. The
+ * array keeps the last call's contents; nothing in it needs an initial value.
+ */
+#define SE_NOALLOC_SCRATCH_BYTES (16u << 20) /* 16 MiB per GPU: e.g. 1024 units x 16 chunks of split partials */
+int32_t se_sparse_decode_attn_noalloc(se_cache_t *c, const void *q, const int32_t *sel_pages,
+                                      const int32_t *sel_count, const se_decode_params_t *p, float *out,
+                                      int32_t *status, se_stream_t stream);
 
 /* ---- utilities ----------------------------------------------------------------------------------------------- */
 /* Synchronise `stream`, copy the device status word to *host_value and (if reset) clear it. */

@@ -11,12 +11,13 @@ import torch
 
 from . import _lib
 from ._lib import (SE_COMPACT_EVICT_SLOTS, SE_COMPACT_GATHER, SE_DEV_CAPACITY, SE_DEV_INDEX, SE_DTYPE_BF16,
-                   SE_DTYPE_F32, SE_PAGES_BUILD, SE_PAGES_SCORE, SE_REFRESH_FROM_PAGE, SE_REFRESH_LAST_PAGE,
+                   SE_DTYPE_F32, SE_ERR_SCRATCH_LIMIT, SE_NOALLOC_SCRATCH_BYTES, SE_PAGES_BUILD, SE_PAGES_SCORE, SE_REFRESH_FROM_PAGE, SE_REFRESH_LAST_PAGE,
                    SE_SCORE_BIDIR, SE_SCORE_CAUSAL, SE_TOPK_LARGEST, SE_TOPK_SMALLEST, SE_UNIT_PAGE, SE_UNIT_SLOT)
 
 __all__ = [
     "DeviceCache", "SEError", "se_window_score", "se_topk_select", "se_token2chunk", "se_compact_evict",
-    "se_cache_append", "se_cache_append_chunk", "se_page_bounds", "se_page_bounds_refresh", "se_sparse_decode_attn", "se_status_read",
+    "se_cache_append", "se_cache_append_chunk", "se_page_bounds", "se_page_bounds_refresh", "se_sparse_decode_attn",
+    "se_sparse_decode_attn_noalloc", "se_status_read",
     "se_version", "set_operand_checks", "SE_SCORE_CAUSAL", "SE_SCORE_BIDIR", "SE_TOPK_LARGEST", "SE_TOPK_SMALLEST", "SE_UNIT_SLOT",
     "SE_UNIT_PAGE", "SE_COMPACT_GATHER", "SE_COMPACT_EVICT_SLOTS", "SE_PAGES_BUILD", "SE_PAGES_SCORE",
     "SE_REFRESH_LAST_PAGE", "SE_REFRESH_FROM_PAGE", "SE_DEV_INDEX", "SE_DEV_CAPACITY",
@@ -348,6 +349,29 @@ def se_sparse_decode_attn(cache, q, out, *, scale, sel_pages=None, sel_count=Non
     _check("se_sparse_decode_attn", lib.se_sparse_decode_attn(C.byref(c), _ptr(q), _ptr(sel_pages), _ptr(sel_count),
                                                               C.byref(p), _ptr(out), _ptr(status), _ptr(ws), nb,
                                                               sp))
+
+
+def se_sparse_decode_attn_noalloc(cache, q, out, *, scale, sel_pages=None, sel_count=None, max_sel=0, max_slots=0,
+                                  accumulate=False, status=None, stream=None):
+    """se_sparse_decode_attn without a workspace: the library's static per-GPU scratch array serves instead, so
+    nothing is allocated (the C entry point rejects calls needing more than SE_NOALLOC_SCRATCH_BYTES)."""
+    has_sel = sel_pages is not None
+    if _CHECKS[0]:
+        B, G, Hq, d, page, mb, nblk, pdt, dev = _dims(cache)
+        call = "se_sparse_decode_attn_noalloc"
+        _need(call, "q", q, B * Hq * d, pdt, dev)
+        _need(call, "out", out, B * Hq * d, F32, dev)
+        _need(call, "sel_pages", sel_pages, B * G * (sel_pages.shape[-1] if has_sel else 0), I32, dev,
+              optional=True)
+        _need(call, "sel_count", sel_count, B * G, I32, dev, optional=not has_sel)
+        _need(call, "status", status, 1, I32, dev, optional=True)
+    lib = _lib.load()
+    st, sp = _stream(stream)
+    c = cache.desc()
+    p = _lib.se_decode_params_t(scale, sel_pages.shape[-1] if has_sel else 0,
+                                (max_sel or sel_pages.shape[-1]) if has_sel else 0, max_slots, int(accumulate))
+    _check("se_sparse_decode_attn_noalloc", lib.se_sparse_decode_attn_noalloc(
+        C.byref(c), _ptr(q), _ptr(sel_pages), _ptr(sel_count), C.byref(p), _ptr(out), _ptr(status), sp))
 
 
 def se_status_read(status, reset=True, stream=None):

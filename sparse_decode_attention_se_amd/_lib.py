@@ -6,7 +6,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libse.so")
 
 # status codes (include/se.h)
-SE_OK, SE_ERR_NULL, SE_ERR_SHAPE, SE_ERR_DTYPE, SE_ERR_PARAM, SE_ERR_WORKSPACE, SE_ERR_UNSUPPORTED, SE_ERR_HIP = range(8)
+(SE_OK, SE_ERR_NULL, SE_ERR_SHAPE, SE_ERR_DTYPE, SE_ERR_PARAM, SE_ERR_WORKSPACE, SE_ERR_UNSUPPORTED, SE_ERR_HIP,
+ SE_ERR_SCRATCH_LIMIT) = range(9)
+SE_NOALLOC_SCRATCH_BYTES = 16 << 20
 SE_DEV_INDEX = 1 << 8
 SE_DEV_CAPACITY = 1 << 9
 SE_DTYPE_F32, SE_DTYPE_BF16 = 0, 1
@@ -74,6 +76,8 @@ EXPORTS = {
                                                           I32]),
     "se_sparse_decode_attn": (I32, [C.POINTER(se_cache_t), P, P, P, C.POINTER(se_decode_params_t), P, P, P,
                                     C.c_size_t, P]),
+    "se_sparse_decode_attn_noalloc": (I32, [C.POINTER(se_cache_t), P, P, P, C.POINTER(se_decode_params_t), P, P,
+                                            P]),
     "se_status_read": (I32, [P, C.POINTER(I32), I32, P]),
     "se_error_string": (C.c_char_p, [I32]),
     "se_version": (C.c_char_p, []),

@@ -24,6 +24,7 @@ extern "C" const char *se_error_string(int32_t code) {
     case SE_ERR_WORKSPACE: return "workspace missing or too small";
     case SE_ERR_UNSUPPORTED: return "combination not implemented";
     case SE_ERR_HIP: return "HIP runtime error";
+    case SE_ERR_SCRATCH_LIMIT: return "needs more scratch than the allocation-free entry point holds";
     default: break;
   }
   if (code & SE_DEV_INDEX) return "device: index list entry out of range, unsorted, duplicated or not resident";

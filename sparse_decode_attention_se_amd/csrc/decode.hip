@@ -10,6 +10,9 @@
 // writes one (m, l, acc[d]) partial per head. A second kernel merges the chunks and, when asked, turns the
 // stored logits into probabilities and adds them to cum_score. Accumulating decode over all slots of views that
 // fit in LDS takes a one-launch path instead (decode_unit).
+#include <atomic>
+#include <mutex>
+
 #include "common.hpp"
 
 namespace se {
@@ -708,9 +711,11 @@ extern "C" size_t se_sparse_decode_attn_workspace_size(const se_cache_t *c, cons
   return pl.part_bytes + pl.logit_bytes;
 }
 
-extern "C" int32_t se_sparse_decode_attn(se_cache_t *c, const void *q, const int32_t *sel_pages,
-                                         const int32_t *sel_count, const se_decode_params_t *p, float *out,
-                                         int32_t *status, void *ws, size_t ws_bytes, se_stream_t stream) {
+namespace {
+
+int32_t decode_call(se_cache_t *c, const void *q, const int32_t *sel_pages, const int32_t *sel_count,
+                    const se_decode_params_t *p, float *out, int32_t *status, void *ws, size_t ws_bytes,
+                    se_stream_t stream) {
   int32_t rc = se_host::check_cache(c);
   if (rc != SE_OK) return rc;
   if (!q || !out || !p) return SE_ERR_NULL;
@@ -756,4 +761,58 @@ extern "C" int32_t se_sparse_decode_attn(se_cache_t *c, const void *q, const int
   hipStream_t st = (hipStream_t)stream;
   if (c->dtype == SE_DTYPE_BF16) return se::dispatch_r<SE_DTYPE_BF16>(R, a, pl.units, pl.nchunk, pl.unit_path, st);
   return se::dispatch_r<SE_DTYPE_F32>(R, a, pl.units, pl.nchunk, pl.unit_path, st);
+}
+
+}  // namespace
+
+extern "C" int32_t se_sparse_decode_attn(se_cache_t *c, const void *q, const int32_t *sel_pages,
+                                         const int32_t *sel_count, const se_decode_params_t *p, float *out,
+                                         int32_t *status, void *ws, size_t ws_bytes, se_stream_t stream) {
+  return decode_call(c, q, sel_pages, sel_count, p, out, status, ws, ws_bytes, stream);
+}
+
+// ---- the allocation-free variant ------------------------------------------------------------------------------
+// For callers that cannot allocate (code under graph capture, tight serving loops): the split partials and the
+// logits live in one file-scope device array per GPU, of SE_NOALLOC_SCRATCH_BYTES. Its device address is looked
+// up once per device (the array's name in host code is only a stand-in for the symbol) and kept. Decode's
+// scratch needs no initial value: every partial and logit is written before it is read.
+static __device__ __align__(256) char scratch[SE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// the scratch array's device address on the current device (looked up at the first call there)
+int32_t scratch_address(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return SE_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return SE_ERR_UNSUPPORTED;
+  void *ptr = g_scratch[dev].load(std::memory_order_acquire);
+  if (!ptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    ptr = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!ptr) {
+      if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return SE_ERR_HIP;
+      g_scratch[dev].store(ptr, std::memory_order_release);
+    }
+  }
+  *out = ptr;
+  return SE_OK;
+}
+
+}  // namespace
+
+extern "C" int32_t se_sparse_decode_attn_noalloc(se_cache_t *c, const void *q, const int32_t *sel_pages,
+                                                 const int32_t *sel_count, const se_decode_params_t *p, float *out,
+                                                 int32_t *status, se_stream_t stream) {
+  int32_t rc = se_host::check_cache(c);
+  if (rc != SE_OK) return rc;
+  if (!p) return SE_ERR_NULL;
+  const size_t need = se_sparse_decode_attn_workspace_size(c, p, sel_pages != nullptr);
+  if (need > (size_t)SE_NOALLOC_SCRATCH_BYTES) return SE_ERR_SCRATCH_LIMIT;
+  void *ws = nullptr;
+  if (need > 0 && (rc = scratch_address(&ws)) != SE_OK) return rc;
+  return decode_call(c, q, sel_pages, sel_count, p, out, status, ws, need, stream);
 }
