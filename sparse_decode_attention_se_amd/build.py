@@ -3,7 +3,7 @@
     python -m sparse_decode_attention_se_amd.build
 
 Every source in csrc/ is compiled by hipcc for gfx950 and linked into one shared library. Packed fp32 vector
-instructions are disabled for the device code.
+instructions are disabled for the device code, and MFMA results are kept in VGPRs.
 """
 import glob
 import os
@@ -13,8 +13,10 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB = os.path.join(HERE, "libse.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+# -amdgpu-mfma-vgpr-form: MFMA results go to ordinary VGPRs (the vector code reads them there); operands that only
+# the MFMAs read may still sit in the accumulation registers
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
-         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-shared"]
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-mllvm", "-amdgpu-mfma-vgpr-form", "-shared"]
 
 
 def sources():

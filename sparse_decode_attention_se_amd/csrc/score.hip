@@ -486,6 +486,282 @@ __global__ __launch_bounds__(NW * 64, 2) void window_stream(ScoreArgs a) {
   }
 }
 
+// ---- bidirectional windows: region keys resident in registers, queries streamed -------------------------------
+// A BIDIR unit has at most a few hundred region keys and r * window query rows (C2: 448 keys, 2048 rows), every row
+// a softmax over all the keys. The keys are loaded once per workgroup and split over its four waves: wave w holds
+// the A fragments of key tiles [w KT, (w + 1) KT) in registers (KT x 4 x 16 B per lane). The query rows stream
+// through in 16-row blocks. Per block a wave computes its logits S^T = K Q^T (lane l: query row l % 16, keys
+// 4 (l / 16) + i of each tile), the rows' sums of exp2 over its own keys against a reference maximum, and publishes
+// (reference, sum) per row in LDS; after one barrier every wave knows each row's overall max M and sum L, and adds
+// exp2(s c - m_w c) exp2(m_w c - M) / L of its keys into per-lane column sums. A row's weights are computed once and
+// never leave the registers. At the end the 16 lanes of a key (one per query row of the block layout) are summed.
+//
+// Software pipeline: the MFMAs of block qb + 1 are issued before the softmax work of block qb, so the matrix unit
+// works while the vector unit does. The query blocks reach LDS by DMA (global_load_lds_dwordx4: lane i of a wave
+// writes 16 bytes at M0 + 16 i, no registers involved) into a ring of kQRing slots, kQRing - 2 blocks ahead of
+// their use; each wave fetches a quarter of every block and waits for its own DMAs before the block's barrier.
+constexpr int kBidirNW = 4;
+constexpr int kBidirMaxKT = 8;  // key tiles per wave: regions of up to 4 x 8 x 16 = 512 keys
+constexpr int kQRing = 8;       // LDS slots of 16 query rows (4 KiB each)
+
+// The DMA is inline assembly so that the compiler's wait-count bookkeeping does not track it (it would otherwise
+// wait for every DMA in flight before any LDS read); the kernel waits for its DMAs itself in bidir_publish(). It
+// has no output register. One wait state separates the M0 write from the DMA that reads it.
+SE_DEV void lds_dma16(const char *g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(g) : "memory", "m0");
+}
+
+// Wait until at most N of this wave's DMAs are in flight and its LDS accesses are done, then meet the other waves:
+// afterwards every wave's older DMAs have landed. The memory clobber keeps the compiler from moving LDS accesses
+// across.
+template <int N>
+SE_DEV void bidir_publish() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// Workgroups per CU the register budget allows: two (256 registers per wave) up to six key tiles per wave; one (512,
+// the accumulators in AGPRs) above, where the keys, two logit sets and the column sums need more.
+#ifndef SE_BIDIR_PIPE_KT
+#define SE_BIDIR_PIPE_KT 8  // key tiles per wave from which the software pipeline is used
+#endif
+template <int KT>
+constexpr bool bidir_pipe() { return KT >= SE_BIDIR_PIPE_KT; }
+template <int KT>
+constexpr int bidir_wgs_per_cu() { return bidir_pipe<KT>() ? 1 : 2; }
+
+template <int KT, bool POW2>
+__global__ __launch_bounds__(kBidirNW * 64, bidir_wgs_per_cu<KT>()) void window_bidir(ScoreArgs a) {
+  int chunk, rg, unit;
+  xcd_item(chunk, rg, unit);
+  const int b = unit / a.n_kv, g = unit % a.n_kv;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ __attribute__((aligned(16))) char s_q[kQRing * 4096];  // query blocks, rows swizzled
+  __shared__ float2 s_ml[2][kBidirNW][16];  // per block parity, wave and row: (m c, sum) of the wave's keys
+  int k0, k1, n;
+  key_range(a, unit, k0, k1, n);
+  const int nkeys = k1 - k0;
+  if (nkeys <= 0) return;  // uniform: the window is longer than the cache (nothing to score)
+  const int total = a.R * a.wq;
+  const int row0 = rg * a.rpg;
+  const int rows = min(a.rpg, total - row0);
+  const int nqb = (rows + 15) / 16;
+  const int32_t *bt = a.bt + (int64_t)b * a.max_blocks;
+  const int32_t *pos = a.pos + (int64_t)unit * a.max_blocks * a.page;
+
+  // DMA of query block qb (any qb: rows past the unit's last are read from its last row and never scored) into its
+  // ring slot. Wave w writes rows 4w..4w+3 of the slot; lane i the 16 bytes at position i % 16 of row 4w + i / 16,
+  // which hold piece (i % 16) ^ row of that row (row r's piece p sits at r * 256 + ((p ^ r) * 16), so the 16 rows a
+  // fragment read touches fall in distinct banks).
+  const char *qunit = a.q + ((int64_t)b * a.n_kv + g) * total * 256;
+  const uint32_t ring = (uint32_t)(uintptr_t)s_q;
+  auto dma_block = [&](int qb) __attribute__((always_inline)) {
+    const int r = wave * 4 + (lane >> 4);
+    const int rho = min(row0 + qb * 16 + r, total - 1);
+    const int piece = (lane & 15) ^ r;
+    lds_dma16(qunit + (int64_t)rho * 256 + piece * 16,
+              __builtin_amdgcn_readfirstlane(ring + (uint32_t)(qb % kQRing) * 4096 + wave * 1024));
+  };
+  // B fragments of block qb (k-steps 0..3) from its ring slot: lane l reads row l % 16, piece 4 t + l / 16
+  auto read_frags = [&](int qb, bf16x8 (&qf)[4]) __attribute__((always_inline)) {
+    const char *slot = s_q + (qb % kQRing) * 4096;
+    const int r = lane & 15;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int piece = t * 4 + (lane >> 4);
+      qf[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(slot + r * 256 + ((piece ^ r) << 4)));
+    }
+  };
+#pragma unroll
+  for (int i = 0; i < kQRing; ++i) dma_block(i);  // the first kQRing blocks are in flight during the key loads
+
+  // resident row of region key j (region-relative), or -1
+  auto key_row_of = [&](int j) __attribute__((always_inline)) {
+    const int key = k0 + min(j, nkeys - 1);
+    const int pg = page_of<POW2>(a, key);
+    const int blk = bt[pg], p = pos[key];
+    const int off = POW2 ? (key & (a.page - 1)) : key - pg * a.page;
+    return (j < nkeys && p >= 0 && (unsigned)blk < (unsigned)a.num_blocks) ? (blk * a.n_kv + g) * a.page + off : -1;
+  };
+  bf16x8 kf[KT][4];
+  uint32_t vmask = 0;  // bit 4 kt + i: the key of this lane's output i of tile kt is scored
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt) {
+    const int tile = wave * KT + kt;
+    const int row = key_row_of(tile * 16 + (lane & 15));
+    const char *src = a.k + (int64_t)(row >= 0 ? row : 0) * 256 + (lane >> 4) * 16;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) kf[kt][t] = __builtin_bit_cast(bf16x8, ld16(src + t * 64));
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (key_row_of(tile * 16 + 4 * (lane >> 4) + i) >= 0) vmask |= 1u << (kt * 4 + i);
+  }
+  const bool all_valid = __builtin_amdgcn_ballot_w64(vmask != (KT == 8 ? 0xffffffffu : (1u << (KT * 4)) - 1)) == 0;
+  __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): the keys, their maps and the first blocks have landed
+  if constexpr (KT >= 6) {
+    // the key fragments, which only the MFMAs read, live in the accumulation registers, so the logits and the
+    // vector work keep the ordinary ones
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) asm volatile("" : "+a"(kf[kt][t]));
+  }
+  __syncthreads();
+
+  const float c = a.scale_log2;
+  float col[KT * 4];
+#pragma unroll
+  for (int i = 0; i < KT * 4; ++i) col[i] = 0.f;
+  auto mfmas = [&](const bf16x8 (&qf)[4], floatx4 (&acc)[KT]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) acc[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) acc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kt][t], qf[t], acc[kt], 0, 0, 0);
+    if constexpr (KT >= 6) {
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) asm volatile("" : "+v"(acc[kt]));  // logits in the ordinary registers
+    }
+  };
+
+  // Block qb, whose logits are in `cur` (MFMAs issued one block earlier); `nxt` receives block qb + 1's, from the
+  // fragments in `qf`, which then take block qb + 2's. ALLV: every key of the wave is scored (no masking).
+  // With ALLV the weights are exp2(s c) with no reference subtracted: a row whose sum of weights over the wave's
+  // keys lies in [2^-80, 2^80] has every weight finite and flushes only terms below 2^-126, under 2^-40 of the sum,
+  // so its normalised weights are as exact as against its maximum. A block with a row outside that band has its
+  // logits computed again from its ring slot and weighted against each row's exact maximum. Without ALLV the keys
+  // that are not scored are masked and the exact maximum is the reference. The weights overwrite the logits in
+  // `cur`. Past the last block the MFMAs and fragment reads still run (their slots hold finished DMAs of clamped
+  // rows) and their results are never used, so the loop body has no branch between the MFMA issues and the weights.
+  auto iteration = [&](int qb, floatx4 (&cur)[KT], floatx4 (&nxt)[KT], bf16x8 (&qf)[4], auto allv_tag)
+      __attribute__((always_inline)) {
+    constexpr bool ALLV = decltype(allv_tag)::value;
+    if constexpr (!bidir_pipe<KT>()) __builtin_amdgcn_sched_barrier(0);  // no overlap of iterations: one logit set
+    float mc = 0.f, l;  // mc: the reference m c of the lane's row (0: none)
+    auto exact_max = [&]() __attribute__((always_inline)) {
+      float x = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) x = fmaxf(x, fmaxf(fmaxf(cur[kt][0], cur[kt][1]), fmaxf(cur[kt][2], cur[kt][3])));
+      return cross_row_max(x);
+    };
+    auto weights = [&]() __attribute__((always_inline)) {
+      l = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          cur[kt][i] = __builtin_amdgcn_exp2f(fmaf(cur[kt][i], c, -mc));
+          l += cur[kt][i];
+        }
+      l = cross_row_sum(l);
+    };
+    auto weights_exact = [&]() __attribute__((always_inline)) {
+      const float mx = exact_max();
+      mc = mx == -INFINITY ? 0.f : mx * c;  // no scored key: every weight is 0
+      weights();
+    };
+    if constexpr (bidir_pipe<KT>()) {
+      mfmas(qf, nxt);
+    } else {  // without the pipeline: this block's own logits, its fragments read just before (visible since the
+              // barrier of block qb - 1)
+      read_frags(qb, qf);
+      mfmas(qf, cur);
+    }
+    if constexpr (ALLV) {
+      weights();
+      if constexpr (bidir_pipe<KT>()) {
+        // one MFMA, then three vector instructions, 4 KT times: the matrix unit runs under the softmax work
+#pragma unroll
+        for (int i = 0; i < 4 * KT; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+        }
+      }
+      if (__builtin_amdgcn_ballot_w64(!(l >= 0x1p-80f && l <= 0x1p80f))) {  // uniform, rare
+        read_frags(qb, qf);  // qf is free until the fragments of a later block are read after the barrier
+        mfmas(qf, cur);
+        weights_exact();
+      }
+    } else {
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cur[kt][i] = (vmask >> (kt * 4 + i)) & 1u ? cur[kt][i] : -INFINITY;
+      weights_exact();
+    }
+    if (lane < 16) s_ml[qb & 1][wave][lane] = make_float2(mc, l);
+    // block qb + 2 complete in LDS for every wave (and this block's (m, l) published) after the barrier
+    bidir_publish<kQRing - 3>();
+    dma_block(qb + kQRing);  // into block qb's slot, which every wave has read; past the last block: unused
+    if constexpr (bidir_pipe<KT>()) read_frags(qb + 2, qf);
+    float2 w[kBidirNW];
+#pragma unroll
+    for (int v = 0; v < kBidirNW; ++v) w[v] = s_ml[qb & 1][v][lane & 15];
+    // the row's total L against the common reference M = max of the waves' references (all 0 in the usual case)
+    float M, L;
+    if (__builtin_amdgcn_ballot_w64((__float_as_uint(w[0].x) | __float_as_uint(w[1].x) | __float_as_uint(w[2].x) |
+                                     __float_as_uint(w[3].x)) != 0u) == 0) {
+      M = 0.f;
+      L = (w[0].y + w[1].y) + (w[2].y + w[3].y);
+    } else {
+      M = -1e30f;
+#pragma unroll
+      for (int v = 0; v < kBidirNW; ++v) M = w[v].y > 0.f ? fmaxf(M, w[v].x) : M;
+      L = 0.f;
+#pragma unroll
+      for (int v = 0; v < kBidirNW; ++v) L += w[v].y > 0.f ? w[v].y * __builtin_amdgcn_exp2f(w[v].x - M) : 0.f;
+    }
+    const bool row_ok = qb * 16 + (lane & 15) < rows && L > 0.f && l > 0.f;
+    const float f = row_ok ? __builtin_amdgcn_exp2f(mc - M) * __builtin_amdgcn_rcpf(L) : 0.f;
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) col[kt * 4 + i] = fmaf(cur[kt][i], f, col[kt * 4 + i]);
+  };
+
+  floatx4 accA[KT], accB[KT];
+  bf16x8 qf[4];
+  if constexpr (bidir_pipe<KT>()) {
+    read_frags(0, qf);
+    mfmas(qf, accA);
+    read_frags(1, qf);
+  }
+  // an even number of blocks (a padding block has no rows: its weights are never added), so the loop body holds two
+  // whole iterations and no exit between them
+  const int nqb2 = (nqb + 1) & ~1;
+  auto run = [&](auto allv_tag) __attribute__((always_inline)) {
+    for (int qb = 0; qb < nqb2; qb += 2) {
+      if constexpr (bidir_pipe<KT>()) {
+        iteration(qb, accA, accB, qf, allv_tag);
+        iteration(qb + 1, accB, accA, qf, allv_tag);
+      } else {
+        iteration(qb, accA, accA, qf, allv_tag);
+        iteration(qb + 1, accA, accA, qf, allv_tag);
+      }
+    }
+  };
+  if (all_valid) run(std::true_type{});
+  else run(std::false_type{});
+  __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): no DMA outlives the loop
+
+  // sum over the 16 query-row lanes of each key; lane j of a row ends with the total of value j of each group of 16
+#pragma unroll
+  for (int g0 = 0; g0 < KT * 4; g0 += 16) {
+    float v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = g0 + i < KT * 4 ? col[g0 + i] : 0.f;
+    const float tot = row16_reduce_scatter(v);
+    const int j = lane & 15, m = g0 + j;
+    if (m < KT * 4) {
+      const int key = (wave * KT + m / 4) * 16 + 4 * (lane >> 4) + (m & 3);
+      if (key < nkeys) {
+        if (a.nrg == 1) put_score(a, (int64_t)unit * a.score_stride + key, tot);
+        else a.colpart[((int64_t)unit * a.nrg + rg) * a.key_span + key] = tot;
+      }
+    }
+  }
+}
+
 #ifndef SE_STREAM_NW
 #define SE_STREAM_NW 4
 #endif
@@ -596,16 +872,62 @@ void launch_stream(const ScoreArgs &a, dim3 grid, hipStream_t st) {
   else hipLaunchKernelGGL((window_stream<PASS, kStreamNW, false>), grid, dim3(kStreamNW * 64), 0, st, a);
 }
 
+template <int KT>
+void launch_bidir_kt(const ScoreArgs &a, dim3 grid, hipStream_t st) {
+  if (a.page_shift >= 0) hipLaunchKernelGGL((window_bidir<KT, true>), grid, dim3(kBidirNW * 64), 0, st, a);
+  else hipLaunchKernelGGL((window_bidir<KT, false>), grid, dim3(kBidirNW * 64), 0, st, a);
+}
+
+void launch_bidir(int kt, const ScoreArgs &a, dim3 grid, hipStream_t st) {
+  switch (kt) {
+    case 1: launch_bidir_kt<1>(a, grid, st); break;
+    case 2: launch_bidir_kt<2>(a, grid, st); break;
+    case 3: launch_bidir_kt<3>(a, grid, st); break;
+    case 4: launch_bidir_kt<4>(a, grid, st); break;
+    case 5: launch_bidir_kt<5>(a, grid, st); break;
+    case 6: launch_bidir_kt<6>(a, grid, st); break;
+    case 7: launch_bidir_kt<7>(a, grid, st); break;
+    default: launch_bidir_kt<8>(a, grid, st); break;
+  }
+}
+
+#ifndef SE_BIDIR_WGS
+#define SE_BIDIR_WGS 512
+#endif
+constexpr int kBidirWGs = SE_BIDIR_WGS;  // workgroups a launch aims for (two per CU)
+
 struct Plan {
   int nrg, nkc, kc, key_span, rpg, nw;  // nw: waves per MFMA workgroup (0: fp32 VALU path, -1: streaming)
+  int bidir_kt;                         // > 0: the register-resident bidirectional kernel, key tiles per wave
   size_t stats_bytes, col_bytes;
 };
 
 Plan make_plan(const se_cache_t *c, const se_window_params_t *p) {
   Plan pl;
+  pl.bidir_kt = 0;
   const int R = c->n_q / c->n_kv;
   const int rows = R * p->n_query;
   const bool mfma = c->dtype == SE_DTYPE_BF16 && c->d == 128;
+  const size_t units = (size_t)c->B * c->n_kv;
+  if (mfma && p->mode == SE_SCORE_BIDIR && p->window - p->protect <= kBidirNW * kBidirMaxKT * 16) {
+    // one workgroup per unit, or row groups of whole 16-row blocks when there are too few units to fill the chip
+    pl.key_span = p->window - p->protect;
+    const int tiles = (pl.key_span + 15) / 16;
+    pl.bidir_kt = (tiles + kBidirNW - 1) / kBidirNW;
+    const int blocks = (rows + 15) / 16;
+    long long want = (kBidirWGs + (long long)units - 1) / (long long)units;
+    if (want > blocks) want = blocks;
+    if (want < 1) want = 1;
+    const int per = (int)((blocks + want - 1) / want);
+    pl.rpg = per * 16;
+    pl.nrg = (rows + pl.rpg - 1) / pl.rpg;
+    pl.nw = -2;
+    pl.nkc = 1;
+    pl.kc = pl.key_span;
+    pl.stats_bytes = 0;
+    pl.col_bytes = pl.nrg > 1 ? se_host::align_up(units * pl.nrg * pl.key_span * sizeof(float)) : 0;
+    return pl;
+  }
   int maxc;
   if (!mfma) {
     pl.nw = 0, pl.rpg = kValuRows, maxc = 1024;
@@ -630,7 +952,6 @@ Plan make_plan(const se_cache_t *c, const se_window_params_t *p) {
     if (pl.kc < 64) pl.kc = 64;
   }
   pl.nkc = (pl.key_span + pl.kc - 1) / pl.kc;
-  const size_t units = (size_t)c->B * c->n_kv;
   pl.stats_bytes = se_host::align_up(units * pl.nrg * pl.nkc * pl.rpg * 2 * sizeof(float));
   pl.col_bytes = pl.nrg > 1 ? se_host::align_up(units * pl.nrg * pl.key_span * sizeof(float)) : 0;
   return pl;
@@ -668,7 +989,7 @@ extern "C" int32_t se_window_score(const se_cache_t *c, const void *q_win, const
   if (!mfma && !valu) return SE_ERR_DTYPE;
   if ((long long)c->num_blocks * c->n_kv * c->page >= (1ll << 31)) return SE_ERR_UNSUPPORTED;  // 32-bit row ids
   se::Plan pl = se::make_plan(c, p);
-  if (!ws || ws_bytes < pl.stats_bytes + pl.col_bytes) return SE_ERR_WORKSPACE;
+  if (pl.stats_bytes + pl.col_bytes > 0 && (!ws || ws_bytes < pl.stats_bytes + pl.col_bytes)) return SE_ERR_WORKSPACE;
   se::ScoreArgs a;
   a.k = (const char *)c->k_pool;
   a.bt = c->block_table;
@@ -677,7 +998,7 @@ extern "C" int32_t se_window_score(const se_cache_t *c, const void *q_win, const
   a.q = (const char *)q_win;
   a.q_pos = q_pos;
   a.scores = scores;
-  a.stats = (float *)ws;
+  a.stats = pl.stats_bytes ? (float *)ws : nullptr;
   a.colpart = pl.col_bytes ? (float *)((char *)ws + pl.stats_bytes) : nullptr;
   a.status = status;
   a.mode = p->mode;
@@ -701,7 +1022,9 @@ extern "C" int32_t se_window_score(const se_cache_t *c, const void *q_win, const
   const int units = c->B * c->n_kv;
   const dim3 grid(pl.nkc, pl.nrg, units);
   hipStream_t st = (hipStream_t)stream;
-  if (pl.nw < 0 && pl.nkc == 1 && (pl.key_span + se::kSub - 1) / se::kSub <= 2 * se::kStreamNW) {
+  if (pl.bidir_kt > 0) {
+    se::launch_bidir(pl.bidir_kt, a, grid, st);
+  } else if (pl.nw < 0 && pl.nkc == 1 && (pl.key_span + se::kSub - 1) / se::kSub <= 2 * se::kStreamNW) {
     se::launch_stream<3>(a, grid, st);
   } else if (pl.nw < 0) {
     se::launch_stream<1>(a, grid, st);

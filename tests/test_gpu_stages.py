@@ -199,6 +199,37 @@ def test_window_score_bidir():
     np.testing.assert_allclose(got.sum(axis=2), 2048.0, rtol=1e-5)
 
 
+@pytest.mark.parametrize("window,protect,holes", [(40, 8, 0.0), (512, 0, 0.0), (300, 17, 0.02)])
+def test_window_score_bidir_shapes(window, protect, holes):
+    """Region sizes the register-resident kernel handles differently: 32 keys (one tile per wave; two waves hold
+    none), 512 keys (eight tiles per wave), and 283 keys (a partial last tile) with free slots in the region (the
+    masked path). Two sequences x two KV heads: each unit's query rows are split over several workgroups."""
+    banner(f"window bidir window={window} protect={protect} holes={holes}")
+    cfg = W.Kara("t", B=2, hq=8, hkv=2, d=128, N=window + 200, window=window, protect=protect, cand_frac=0.2,
+                 budget_frac=0.2, max_gap=8, period=4, events=1, rho=0.9)
+    inp = W.gen_kara(cfg, seed=11, threads=4)
+    st = inp["cache"]
+    if holes:
+        st = punch_holes(st, holes, 12)
+    qw = W.to_storage(np.random.default_rng(13).standard_normal((2, 8, window, 128)), "bf16")
+    ref = oracle.window_score_bidir(st, qw, inp["scale"], window, protect)
+    dc = to_device(st, 8)
+    R = window - protect
+    scores = torch.full((2, 2, R), 7.0, dtype=torch.float32, device=DEV)
+    status = status_word()
+    se.se_window_score(dc, storage_tensor(qw, "bf16"), None, scores, scale=inp["scale"], mode=se.SE_SCORE_BIDIR,
+                       n_query=window, window=window, protect=protect, status=status)
+    assert se.se_status_read(status) == 0
+    got = scores.cpu().numpy()
+    assert_scores_close(got, ref, mass=np.full((2, 2), 4.0 * window))
+    # every query row that sees a resident key gives it mass 1 per head
+    for b in range(2):
+        for g in range(2):
+            n = int(st.n_slots[b, g])
+            seen = np.any(st.pos_map[b, g, n - window:n - protect] >= 0)
+            np.testing.assert_allclose(got[b, g].sum(), 4.0 * window * seen, rtol=1e-5)
+
+
 @pytest.mark.parametrize("wq,N", [(128, 900), (20, 1300)])
 def test_window_score_causal_row_groups(wq, N):
     """512 query rows per unit (two row groups, whose partial column sums a last kernel adds up) and 80 rows (a row
