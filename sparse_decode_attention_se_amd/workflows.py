@@ -262,6 +262,42 @@ class H2OStep(DecodeStep):
         return self.out
 
 
+class H2OGraph:
+    """H2O's decode loop captured as one HIP graph: `steps` steps of append, accumulating decode, bottom-1 and slot
+    eviction (SparseEngine page, "What it is": continuous scores during generation), each with its own token, position
+    and query (k_new, v_new, q, pos: sequences of per-step device tensors). One replay runs every step with no host
+    launch between kernels. Capture records the kernels only; the cache is changed by replays, in stream order.
+
+    With `record` (a list of batch indices), each step also copies that step's evicted slots [steps][B][n_kv],
+    eviction counts and the recorded sequences' outputs [steps][len(record)][n_q][d] into device buffers (small
+    elementwise kernels inside the graph), so a replay can be checked afterwards step by step. None of the calls
+    allocates or clears memory inside the graph."""
+
+    def __init__(self, cache, k_new, v_new, pos, q, *, scale, budget, recent, record=None, status=None):
+        steps = len(q)
+        B, G, S, d = _dims(cache)
+        dev = cache.device
+        self.step = H2OStep(cache, scale=scale, budget=budget, recent=recent, status=status)
+        self.steps = steps
+        self.evict = self.evict_count = self.out = None
+        if record is not None:
+            self.evict = torch.zeros((steps, B, G), dtype=torch.int32, device=dev)
+            self.evict_count = torch.zeros((steps, B, G), dtype=torch.int32, device=dev)
+            self.out = torch.zeros((steps, len(record), cache.n_q, d), dtype=torch.float32, device=dev)
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            for s in range(steps):
+                self.step.run(k_new[s], v_new[s], pos[s], q[s])
+                if record is not None:  # elementwise kernels, not copy engines
+                    torch.add(self.step.evict[:, :, 0], 0, out=self.evict[s])
+                    torch.add(self.step.evict_count, 0, out=self.evict_count[s])
+                    for i, b in enumerate(record):
+                        torch.add(self.step.out[b], 0, out=self.out[s, i])
+
+    def replay(self):
+        self.graph.replay()
+
+
 class QuestStep:
     """Page bounds of the cache (built once) -> page scores -> top pages + first/last -> decode over them."""
 

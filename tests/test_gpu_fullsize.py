@@ -287,3 +287,163 @@ def test_window_scores_repeat_bitwise_at_full_size():
     np.testing.assert_allclose(runs[0].sum(dim=2).cpu().numpy(), r * cfg.window, rtol=1e-4)
     for x in runs[1:]:
         assert torch.equal(x, runs[0])
+
+
+def _fields(dc):
+    """Every tensor of a device cache, cloned."""
+    return {f: getattr(dc, f).clone() for f in se.DeviceCache.FIELDS if getattr(dc, f) is not None}
+
+
+def _assert_same(a: dict, b: dict, what):
+    for k in a:
+        assert torch.equal(a[k], b[k]), f"{what}: {k} differs between two identical runs"
+
+
+def test_every_call_repeats_bitwise_at_full_size():
+    """Each call of the path, run twice on identical state at the workloads' full sizes, gives identical bits:
+    window scores, top-K, Token2Chunk, in-place compaction (whole and trailing), append, decode (split and
+    accumulating), page bounds (build and score). A missing wait or barrier, or an order-dependent reduction,
+    shows up as a difference between the runs."""
+    banner("double runs: Llama-8B SnapKV 8 x 32768, Kara 128 x 16384, Quest 2 x 131072, H2O 64 x 8192")
+    # SnapKV: scores, top-K, whole-cache compaction, decode over the compacted cache
+    cfg = W.C1
+    inp = W.gen_snapkv(cfg, seed=2, threads=16)
+    q_win, q_pos, q_dec = storage_tensor(inp["q_win"], "bf16"), i32(inp["q_pos"]), storage_tensor(inp["q_dec"], "bf16")
+    base = to_device(inp["cache"], cfg.hq)
+    runs = []
+    for _ in range(2):
+        dc = base.clone()
+        status = status_word()
+        ev = WF.SnapKVEvent(dc, wq=cfg.wq, protect=cfg.protect, keep=cfg.keep, scale=inp["scale"], status=status)
+        ev.run(q_win, q_pos, q_dec)
+        assert se.se_status_read(status) == 0
+        runs.append(dict(_fields(dc), scores=ev.scores.clone(), idx=ev.idx.clone(), count=ev.count.clone(),
+                         out=ev.out.clone()))
+        del dc, ev
+    _assert_same(runs[0], runs[1], "SnapKV event")
+    del base, runs, inp
+    torch.cuda.empty_cache()
+    # Kara: bidirectional scores, candidates, Token2Chunk, trailing compaction, append, decode
+    cfg = W.scaled(W.C2, period=1, events=1)
+    inp = W.gen_kara(cfg, seed=2, threads=16)
+    q_win = storage_tensor(np.ascontiguousarray(inp["q_all"][:, :, :cfg.window]), "bf16")
+    k_new, v_new = storage_tensor(inp["k_new"][0], "bf16"), storage_tensor(inp["v_new"][0], "bf16")
+    q = storage_tensor(np.ascontiguousarray(inp["q_all"][:, :, cfg.N - inp["q_first_pos"]]), "bf16")
+    pos = i32(np.full((cfg.B,), cfg.N, np.int32))
+    base = to_device(inp["cache"], cfg.hq)
+    del inp
+    runs = []
+    for _ in range(2):
+        dc = base.clone()
+        status = status_word()
+        ev = WF.KaraEvent(dc, window=cfg.window, protect=cfg.protect, n_cand=cfg.n_cand, budget=cfg.budget,
+                          max_gap=cfg.max_gap, scale=cfg.d ** -0.5, status=status)
+        ev.run(q_win)
+        step = WF.DecodeStep(dc, scale=cfg.d ** -0.5, status=status)
+        step.run(k_new, v_new, pos, q)
+        assert se.se_status_read(status) == 0
+        runs.append(dict(_fields(dc), scores=ev.scores.clone(), cand=ev.cand.clone(), keep=ev.keep.clone(),
+                         keep_count=ev.keep_count.clone(), out=step.out.clone()))
+        del dc, ev, step
+    _assert_same(runs[0], runs[1], "Kara event and decode step")
+    del base, runs
+    torch.cuda.empty_cache()
+    # Quest: page bounds build and score, page choice, decode over the pages (the cache itself is not changed)
+    cfg = W.C3
+    inp = W.gen_quest(cfg, seed=2, threads=16)
+    q = storage_tensor(inp["q_dec"], "bf16")
+    base = to_device(inp["cache"], cfg.hq)
+    runs = []
+    for _ in range(2):
+        dc = base.clone()
+        qs = WF.QuestStep(dc, top_pages=cfg.top_pages, scale=inp["scale"])
+        qs.build()
+        qs.run(q)
+        runs.append(dict(meta=dc.page_meta.clone(), ps=qs.page_scores.clone(), pages=qs.pages.clone(),
+                         out=qs.out.clone()))
+        del dc, qs
+    _assert_same(runs[0], runs[1], "Quest step")
+    del base, runs, inp
+    torch.cuda.empty_cache()
+    # H2O: eight steps of append, accumulating decode, bottom-1, slot eviction
+    cfg = W.scaled(W.C4, steps=8)
+    inp = W.gen_h2o(cfg, seed=2, threads=16)
+    base = to_device(inp["cache"], cfg.hq)
+    runs = []
+    for _ in range(2):
+        dc = base.clone()
+        status = status_word()
+        h2o = WF.H2OStep(dc, scale=inp["scale"], budget=cfg.budget, recent=cfg.recent, status=status)
+        outs = []
+        for s in range(cfg.steps):
+            h2o.run(storage_tensor(inp["k_new"][s], "bf16"), storage_tensor(inp["v_new"][s], "bf16"),
+                    i32(np.full((cfg.B,), cfg.N + s, np.int32)), storage_tensor(inp["q_steps"][s], "bf16"))
+            outs.append(h2o.out.clone())
+        assert se.se_status_read(status) == 0
+        runs.append(dict(_fields(dc), out=torch.stack(outs)))
+        del dc, h2o
+    _assert_same(runs[0], runs[1], "H2O steps")
+
+
+def test_h2o_graph_of_1024_steps_replays_like_eager_and_the_oracle():
+    """The H2O workload's whole loop (64 sequences from 8192 tokens, budget 8192, recent 256, 1024 steps) captured
+    as one HIP graph. Each of two replays, on the restored cache with eager work and synchronisations between them,
+    gives bit for bit what the eager loop gives: every step's evicted slots, the recorded sequence's outputs, the
+    final maps, stacks and cumulative scores. The oracle then follows the replay on that sequence (teacher-forced on
+    the replay's recorded evictions) for its first 384 steps: outputs within 2e-3 and every eviction the oracle's
+    choice or a near tie of it."""
+    banner("H2O graph: 64 x 8192, 1024 steps, two replays against eager; oracle on sequence 37, 384 steps")
+    cfg = W.C4
+    seq, checked = 37, 384
+    inp = W.gen_h2o(cfg, seed=5, threads=16)
+    k_new = [storage_tensor(inp["k_new"][s], "bf16") for s in range(cfg.steps)]
+    v_new = [storage_tensor(inp["v_new"][s], "bf16") for s in range(cfg.steps)]
+    q = [storage_tensor(inp["q_steps"][s], "bf16") for s in range(cfg.steps)]
+    pos = [i32(np.full((cfg.B,), cfg.N + s, np.int32)) for s in range(cfg.steps)]
+    pristine = to_device(inp["cache"], cfg.hq)
+    status = status_word()
+    # eager
+    eager = pristine.clone()
+    h2o = WF.H2OStep(eager, scale=inp["scale"], budget=cfg.budget, recent=cfg.recent, status=status)
+    ev_e, cnt_e, out_e = [], [], []
+    for s in range(cfg.steps):
+        h2o.run(k_new[s], v_new[s], pos[s], q[s])
+        ev_e.append(h2o.evict[:, :, 0].clone())
+        cnt_e.append(h2o.evict_count.clone())
+        out_e.append(h2o.out[seq].clone())
+    assert se.se_status_read(status) == 0
+    ev_e, cnt_e, out_e = torch.stack(ev_e), torch.stack(cnt_e), torch.stack(out_e)
+    final_e = _fields(eager)
+    del eager, h2o
+    # graph: captured once, replayed twice on the restored cache
+    work = pristine.clone()
+    graph = WF.H2OGraph(work, k_new, v_new, pos, q, scale=inp["scale"], budget=cfg.budget, recent=cfg.recent,
+                        record=[seq], status=status)
+    for r in range(2):
+        for f, x in _fields(pristine).items():
+            getattr(work, f).copy_(x)
+        graph.evict.fill_(-7)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert se.se_status_read(status) == 0
+        assert torch.equal(graph.evict, ev_e) and torch.equal(graph.evict_count, cnt_e), r
+        assert torch.equal(graph.out[:, 0], out_e), r
+        _assert_same(final_e, _fields(work), f"replay {r}")
+    assert bool((cnt_e == 1).all())  # over budget at every step: one eviction per (sequence, head)
+    # the oracle along the replay on the sampled sequence
+    ev = graph.evict[:, seq].cpu().numpy()
+    outs = graph.out[:, 0].cpu().numpy()
+    sub = dict(inp, cfg=W.scaled(cfg, B=1), k_new=inp["k_new"][:, seq:seq + 1], v_new=inp["v_new"][:, seq:seq + 1],
+               q_steps=inp["q_steps"][:, seq:seq + 1])
+    st = subcache(inp["cache"], [seq])
+    r_ = cfg.hq // cfg.hkv
+    swaps = 0
+    for s in range(checked):
+        forced = [[np.array([ev[s, g]], np.int32) for g in range(cfg.hkv)]]
+        st, info = P.h2o_step(sub, st, s, evict=forced)
+        np.testing.assert_allclose(outs[s], info["out"][0], atol=2e-3, rtol=0)
+        for g in range(cfg.hkv):
+            swaps += assert_sets_match_modulo_ties(forced[0][g], info["evict"][0][g], info["cum"][0, g],
+                                                   floor=1e-6 * r_ * (s + 1))
+    print(f"near-tie evictions adopted from the replay: {swaps}", flush=True)
