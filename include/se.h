@@ -198,8 +198,10 @@ int32_t se_compact_evict(se_cache_t *c, const int32_t *idx, const int32_t *count
  * one block is popped from free_blocks for it (pops in sequence order). k_new, v_new [B][n_kv][d] of dtype are
  * written, pos_map = pos[b] (pos: device [B]), ctx_len + 1, and the cumulative score (if present) set to 0. All or
  * nothing: if the free stack or a sequence's slot range cannot serve the whole call, nothing changes and
- * SE_DEV_CAPACITY is raised.
+ * SE_DEV_CAPACITY is raised. Workspace: se_cache_append_workspace_size bytes (one int32 per (sequence, KV head):
+ * the pool row each new token goes to, handed from the planning kernel to the copying one).
  */
+size_t se_cache_append_workspace_size(const se_cache_t *c);
 int32_t se_cache_append(se_cache_t *c, const void *k_new, const void *v_new, const int32_t *pos, int32_t *status,
                         void *ws, size_t ws_bytes, se_stream_t stream);
 

@@ -268,8 +268,10 @@ def se_cache_append(cache, k_new, v_new, pos, *, status=None, stream=None):
     lib = _lib.load()
     st, sp = _stream(stream)
     c = cache.desc()
+    nb = lib.se_cache_append_workspace_size(C.byref(c))
+    ws = _workspace(nb, cache.device, stream)
     _check("se_cache_append", lib.se_cache_append(C.byref(c), _ptr(k_new), _ptr(v_new), _ptr(pos), _ptr(status),
-                                                  None, 0, sp))
+                                                  _ptr(ws), nb, sp))
 
 
 def se_cache_append_chunk(cache, k_new, v_new, pos0, *, counts=None, status=None, stream=None):

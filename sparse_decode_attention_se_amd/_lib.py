@@ -67,6 +67,7 @@ EXPORTS = {
                              P]),
     "se_compact_evict_workspace_size": (C.c_size_t, [C.POINTER(se_cache_t), C.POINTER(se_compact_params_t)]),
     "se_compact_evict": (I32, [C.POINTER(se_cache_t), P, P, C.POINTER(se_compact_params_t), P, P, C.c_size_t, P]),
+    "se_cache_append_workspace_size": (C.c_size_t, [C.POINTER(se_cache_t)]),
     "se_cache_append": (I32, [C.POINTER(se_cache_t), P, P, P, P, P, C.c_size_t, P]),
     "se_cache_append_chunk_workspace_size": (C.c_size_t, [C.POINTER(se_cache_t), I32]),
     "se_cache_append_chunk": (I32, [C.POINTER(se_cache_t), P, P, P, I32, P, P, P, C.c_size_t, P]),

@@ -478,6 +478,7 @@ struct AppendArgs {
   float *cum;
   const char *k_new, *v_new;
   const int32_t *pos_new;
+  int32_t *dst_row;  // workspace: per unit, the pool row its new token goes to (-1: none)
   int32_t *status;
   int32_t B, n_kv, page, max_blocks, num_blocks, slot_cap, row_bytes;
 };
@@ -486,10 +487,10 @@ constexpr int kAppendThreads = 1024;
 constexpr int kMaxUnits = 4096;
 constexpr int kAppendMaxSeq = 2048;
 
-// single workgroup: decide every slot and block first, then commit only if the whole call fits
-__global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
+// Plan and maps, one workgroup: decide every slot and block first, then commit only if the whole call fits, and
+// hand each unit's destination pool row to append_copy through the workspace (-1: nothing to copy).
+__global__ __launch_bounds__(kAppendThreads) void append_plan(AppendArgs a) {
   __shared__ int s_slot[kMaxUnits];
-  __shared__ int s_blk[kMaxUnits];      // physical block of each unit's slot
   __shared__ int s_lb[kAppendMaxSeq];   // logical block sequence b lacks (-1 = none)
   __shared__ int s_pop[kAppendMaxSeq];  // free-stack index it pops from
   __shared__ int s_scan[kAppendThreads];
@@ -542,6 +543,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
   int carry = 0;
   if (top0 < 0 || top0 > a.num_blocks) {
     if (threadIdx.x == 0) raise(a.status, SE_DEV_CAPACITY);
+    for (int unit = threadIdx.x; unit < units; unit += kAppendThreads) a.dst_row[unit] = -1;
     return;
   }
   for (int base = 0; base < a.B; base += kAppendThreads) {
@@ -566,6 +568,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
   }
   if (s_fail) {
     if (threadIdx.x == 0) raise(a.status, s_fail == 2 ? SE_DEV_INDEX : SE_DEV_CAPACITY);
+    for (int unit = threadIdx.x; unit < units; unit += kAppendThreads) a.dst_row[unit] = -1;
     return;  // all or nothing: nothing was written
   }
   for (int b = threadIdx.x; b < a.B; b += kAppendThreads)
@@ -580,33 +583,24 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
     a.pos[(int64_t)unit * cap + slot] = a.pos_new[b];
     a.ctx[unit] += 1;
     if (a.cum) a.cum[(int64_t)unit * cap + slot] = 0.f;
-    s_blk[unit] = a.bt[(int64_t)b * a.max_blocks + slot / a.page];
+    const int blk = a.bt[(int64_t)b * a.max_blocks + slot / a.page];
+    a.dst_row[unit] = (blk * a.n_kv + unit % a.n_kv) * a.page + slot % a.page;
   }
-  __syncthreads();
-  // copy the new rows: each thread loads kCopyBatch 16-byte pieces of K and of V before storing any of them
-  constexpr int kCopyBatch = 8;
-  const int cpr = a.row_bytes / 16, total = units * cpr;
-  for (int t0 = threadIdx.x; t0 < total; t0 += kAppendThreads * kCopyBatch) {
-    u32x4 kb[kCopyBatch], vb[kCopyBatch];
-#pragma unroll
-    for (int u = 0; u < kCopyBatch; ++u) {
-      const int t = t0 + u * kAppendThreads;
-      if (t >= total) continue;
-      const int64_t src = (int64_t)(t / cpr) * a.row_bytes + (t % cpr) * 16;
-      kb[u] = ld16(a.k_new + src);
-      vb[u] = ld16(a.v_new + src);
-    }
-#pragma unroll
-    for (int u = 0; u < kCopyBatch; ++u) {
-      const int t = t0 + u * kAppendThreads;
-      if (t >= total) continue;
-      const int unit = t / cpr, ch = t % cpr;
-      const int g = unit % a.n_kv, slot = s_slot[unit];
-      const int64_t off = (((int64_t)s_blk[unit] * a.n_kv + g) * a.page + slot % a.page) * a.row_bytes + ch * 16;
-      st16(a.k + off, kb[u]);
-      st16(a.v + off, vb[u]);
-    }
-  }
+}
+
+// Data: one thread per 16 bytes of a new K row and V row, to the pool row the plan chose
+constexpr int kCopyThreads = 256;
+__global__ __launch_bounds__(kCopyThreads) void append_copy(AppendArgs a) {
+  const int cpr = a.row_bytes / 16;
+  const int t = blockIdx.x * kCopyThreads + threadIdx.x;
+  if (t >= a.B * a.n_kv * cpr) return;
+  const int unit = t / cpr, ch = t % cpr;
+  const int row = a.dst_row[unit];
+  if (row < 0) return;
+  const int64_t src = (int64_t)unit * a.row_bytes + ch * 16, dst = (int64_t)row * a.row_bytes + ch * 16;
+  const u32x4 kr = ld16(a.k_new + src), vr = ld16(a.v_new + src);
+  st16(a.k + dst, kr);
+  st16(a.v + dst, vr);
 }
 
 // ---- chunk append: T tokens per unit at the high-water slots -------------------------------------------------------
@@ -839,17 +833,22 @@ extern "C" int32_t se_compact_evict(se_cache_t *c, const int32_t *idx, const int
   return SE_ERR_PARAM;
 }
 
+extern "C" size_t se_cache_append_workspace_size(const se_cache_t *c) {
+  if (se_host::check_cache(c) != SE_OK) return 0;
+  return se_host::align_up((size_t)c->B * c->n_kv * sizeof(int32_t));
+}
+
 extern "C" int32_t se_cache_append(se_cache_t *c, const void *k_new, const void *v_new, const int32_t *pos,
                                    int32_t *status, void *ws, size_t ws_bytes, se_stream_t stream) {
-  (void)ws;
-  (void)ws_bytes;
   int32_t rc = se_host::check_cache(c);
   if (rc != SE_OK) return rc;
   if (!k_new || !v_new || !pos || !c->free_blocks || !c->free_top) return SE_ERR_NULL;
   if (c->slot_cap > 0 && (!c->slot_stack || !c->slot_top)) return SE_ERR_NULL;
   if (c->B * c->n_kv > se::kMaxUnits || c->B > se::kAppendMaxSeq) return SE_ERR_UNSUPPORTED;
+  if ((long long)c->num_blocks * c->n_kv * c->page >= (1ll << 31)) return SE_ERR_UNSUPPORTED;  // 32-bit row ids
   const int row_bytes = c->d * se::elem_bytes(c->dtype);
   if (row_bytes % 16 != 0) return SE_ERR_DTYPE;
+  if (!ws || ws_bytes < se_cache_append_workspace_size(c)) return SE_ERR_WORKSPACE;
   se::AppendArgs a;
   a.k = (char *)c->k_pool;
   a.v = (char *)c->v_pool;
@@ -873,7 +872,12 @@ extern "C" int32_t se_cache_append(se_cache_t *c, const void *k_new, const void 
   a.num_blocks = c->num_blocks;
   a.slot_cap = c->slot_cap;
   a.row_bytes = row_bytes;
-  hipLaunchKernelGGL(se::append_kernel, dim3(1), dim3(se::kAppendThreads), 0, (hipStream_t)stream, a);
+  a.dst_row = (int32_t *)ws;
+  hipStream_t st = (hipStream_t)stream;
+  hipLaunchKernelGGL(se::append_plan, dim3(1), dim3(se::kAppendThreads), 0, st, a);
+  const int pieces = c->B * c->n_kv * (row_bytes / 16);
+  hipLaunchKernelGGL(se::append_copy, dim3((pieces + se::kCopyThreads - 1) / se::kCopyThreads), dim3(se::kCopyThreads),
+                     0, st, a);
   return se_host::launch_status();
 }
 

@@ -101,13 +101,16 @@ struct ViewMap {
 // exp2 of at most kLazy, which fp32 sums hold without loss, and the rescale of l and acc is skipped.
 constexpr float kLazy = 8.f;
 constexpr int kMaxChunkRows = 1024;
+#ifndef SE_DECODE_WG_PER_CU
+#define SE_DECODE_WG_PER_CU 2  // occupancy hint of the split kernel (the compiler settles at three waves per SIMD)
+#endif
 #ifndef SE_DECODE_MIN_WGS
 #define SE_DECODE_MIN_WGS 512
 #endif
 constexpr int kMinWGs = SE_DECODE_MIN_WGS;
 
 template <int DTYPE, int R>
-__global__ __launch_bounds__(kThreads) void decode_partial(DecodeArgs a) {
+__global__ __launch_bounds__(kThreads, SE_DECODE_WG_PER_CU) void decode_partial(DecodeArgs a) {
   using V = Vec<DTYPE>;
   constexpr int EPL = V::EPL;
   constexpr int D = 16 * EPL;

@@ -4,8 +4,9 @@
 // lower a) while the count of candidates plus fills stays within the budget, and the output is the ascending
 // union followed by the protected tail.
 //
-// One workgroup per (sequence, KV head). Ranks come from an all-pairs comparison (the candidate lists are a
-// few hundred long), the greedy pass over the ranked gaps is inherently sequential and runs on one lane, and
+// One workgroup per (sequence, KV head), with LDS sized to the input list. Ranks come from an all-pairs comparison
+// of the gap priorities (one broadcast LDS read per comparison; the lists are a few hundred long), the greedy pass
+// over the ranked gaps is inherently sequential and runs on one lane over the gap sizes stored in rank order, and
 // a workgroup scan writes the expanded list in order.
 #include "common.hpp"
 
@@ -14,6 +15,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kMaxList = 4096;
+constexpr int kMaxGap = 32767;  // gap sizes are kept as 16-bit values
 
 struct T2CArgs {
   const int32_t *idx, *count, *n_slots;
@@ -22,13 +24,23 @@ struct T2CArgs {
   int32_t max_gap, budget, window, protect, score_stride, in_stride, out_stride, max_slots;
 };
 
+// LDS per workgroup for lists of L entries: candidates, gap priorities, gap index by rank (int32 each), gap size by
+// rank (int16) and fill flags (byte)
+inline size_t t2c_lds_bytes(int in_stride) {
+  const size_t L = (size_t)((in_stride + 3) & ~3);
+  return L * (4 + 4 + 4 + 2 + 1);
+}
+
 __global__ __launch_bounds__(kThreads) void t2c_kernel(T2CArgs a) {
-  __shared__ int s_c[kMaxList];
-  __shared__ float s_prio[kMaxList];
-  __shared__ int s_order[kMaxList];
-  __shared__ unsigned char s_fill[kMaxList];
+  extern __shared__ __attribute__((aligned(16))) char s_dyn[];
+  const int L = (a.in_stride + 3) & ~3;
+  int *s_c = reinterpret_cast<int *>(s_dyn);
+  float *s_prio = reinterpret_cast<float *>(s_c + L);  // NaN: the gap does not qualify
+  int *s_gap_of = reinterpret_cast<int *>(s_prio + L);  // gap index of rank r
+  short *s_size_of = reinterpret_cast<short *>(s_gap_of + L);  // its size
+  unsigned char *s_fill = reinterpret_cast<unsigned char *>(s_size_of + L);
   __shared__ int s_scan[kThreads];
-  __shared__ int s_m, s_bad;
+  __shared__ int s_m, s_bad, s_nq;
   const int unit = blockIdx.x, t = threadIdx.x;
   const int n = a.n_slots[unit];
   const int cnt = min(max(a.count[unit], 0), a.in_stride);
@@ -37,6 +49,7 @@ __global__ __launch_bounds__(kThreads) void t2c_kernel(T2CArgs a) {
   const float *sc = a.scores + (int64_t)unit * a.score_stride;
   if (t == 0) {
     s_m = 0;
+    s_nq = 0;
     s_bad = (a.count[unit] < 0 || a.count[unit] > a.in_stride || base < 0 || n > a.max_slots) ? 1 : 0;
   }
   __syncthreads();
@@ -44,7 +57,7 @@ __global__ __launch_bounds__(kThreads) void t2c_kernel(T2CArgs a) {
     int s = in[i];
     if (s < base || s >= n || (i > 0 && in[i - 1] >= s)) atomicOr(&s_bad, 1);
     if (s < thr && (i + 1 == cnt || in[i + 1] >= thr)) s_m = i + 1;  // candidates are the prefix below thr
-    if (i < kMaxList) s_c[i] = s;
+    s_c[i] = s;
   }
   __syncthreads();
   if (s_bad) {
@@ -56,40 +69,39 @@ __global__ __launch_bounds__(kThreads) void t2c_kernel(T2CArgs a) {
   }
   const int m = s_m;
   const int gaps = m > 0 ? m - 1 : 0;
-  // gap priorities (-1 marks a gap that does not qualify)
+  // gap priorities; a gap that does not qualify gets a quiet NaN, which no comparison below counts
+  int nq = 0;
   for (int i = t; i < gaps; i += kThreads) {
-    int x = s_c[i], y = s_c[i + 1], g = y - x - 1;
-    s_prio[i] = (g >= 1 && g <= a.max_gap) ? __fdiv_rn(sc[x - base] + sc[y - base], (float)(y - x)) : -1.f;
+    const int x = s_c[i], y = s_c[i + 1], g = y - x - 1;
+    const bool q = g >= 1 && g <= a.max_gap;
+    s_prio[i] = q ? __fdiv_rn(sc[x - base] + sc[y - base], (float)(y - x)) : __int_as_float(0x7fc00000);
     s_fill[i] = 0;
+    nq += q;
   }
+  if (nq) atomicAdd(&s_nq, nq);
   __syncthreads();
   // rank of each qualifying gap: priority descending, then lower left endpoint
   for (int i = t; i < gaps; i += kThreads) {
-    int x = s_c[i], y = s_c[i + 1], g = y - x - 1;
-    if (!(g >= 1 && g <= a.max_gap)) continue;
-    float pi = s_prio[i];
+    const float pi = s_prio[i];
+    if (pi != pi) continue;  // does not qualify
     int r = 0;
     for (int j = 0; j < gaps; ++j) {
-      int gj = s_c[j + 1] - s_c[j] - 1;
-      if (!(gj >= 1 && gj <= a.max_gap)) continue;
-      float pj = s_prio[j];
-      r += (pj > pi || (pj == pi && j < i)) ? 1 : 0;
+      const float pj = s_prio[j];
+      r += (pj > pi) | ((pj == pi) & (j < i));
     }
-    s_order[r] = i;
+    s_gap_of[r] = i;
+    s_size_of[r] = (short)(s_c[i + 1] - s_c[i] - 1);
   }
   __syncthreads();
-  if (t == 0) {
-    int nq = 0;
-    for (int i = 0; i < gaps; ++i) {
-      int g = s_c[i + 1] - s_c[i] - 1;
-      nq += (g >= 1 && g <= a.max_gap) ? 1 : 0;
-    }
+  if (t == 0) {  // first fit in rank order until the budget is met
     int total = m;
-    for (int r = 0; r < nq && total < a.budget; ++r) {
-      int i = s_order[r];
-      int g = s_c[i + 1] - s_c[i] - 1;
+    const int q = s_nq;
+#pragma unroll 8
+    for (int r = 0; r < q; ++r) {
+      const int g = s_size_of[r];
+      if (total >= a.budget) break;
       if (total + g <= a.budget) {
-        s_fill[i] = 1;
+        s_fill[s_gap_of[r]] = 1;
         total += g;
       }
     }
@@ -140,6 +152,7 @@ extern "C" int32_t se_token2chunk(const se_cache_t *c, const int32_t *idx, const
   if (!idx || !count || !scores || !p || !idx_out || !count_out) return SE_ERR_NULL;
   if (p->max_gap < 0 || p->budget < 0 || p->window <= 0 || p->protect < 0 || p->protect > p->window)
     return SE_ERR_PARAM;
+  if (p->max_gap > se::kMaxGap) return SE_ERR_UNSUPPORTED;
   if (p->in_stride <= 0 || p->in_stride > se::kMaxList) return SE_ERR_UNSUPPORTED;
   if (p->score_stride < p->window - p->protect) return SE_ERR_SHAPE;
   if (p->out_stride < p->in_stride && p->out_stride < p->budget + p->protect) return SE_ERR_SHAPE;
@@ -160,6 +173,7 @@ extern "C" int32_t se_token2chunk(const se_cache_t *c, const int32_t *idx, const
   a.in_stride = p->in_stride;
   a.out_stride = p->out_stride;
   a.max_slots = c->max_blocks * c->page;
-  hipLaunchKernelGGL(se::t2c_kernel, dim3(c->B * c->n_kv), dim3(se::kThreads), 0, (hipStream_t)stream, a);
+  hipLaunchKernelGGL(se::t2c_kernel, dim3(c->B * c->n_kv), dim3(se::kThreads), se::t2c_lds_bytes(p->in_stride),
+                     (hipStream_t)stream, a);
   return se_host::launch_status();
 }
