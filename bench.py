@@ -72,7 +72,7 @@ CALL_KERNELS = {
     "se_window_score": ["window_stream", "colsum_reduce", "stats_valu", "colsum_valu"],
     "se_topk_select": ["topk_kernel"],
     "se_token2chunk": ["t2c_kernel"],
-    "se_compact_evict": ["gather_move", "gather_extents", "gather_push", "evict_slots_kernel"],
+    "se_compact_evict": ["gather_move", "gather_small", "gather_extents", "gather_push", "evict_slots_kernel"],
     "se_cache_append": ["append_plan", "append_copy"],
     "se_cache_append_chunk": ["chunk_plan", "chunk_write"],
     "se_page_bounds": ["pages_score", "pages_build"],

@@ -266,6 +266,84 @@ __global__ __launch_bounds__(kMoveThreads) void gather_move(GatherArgs a) {
   if (a.fold) free_tile(0);  // move_tile<true> ended with a barrier: s_tile is free
 }
 
+// Small lists: when every unit keeps at most kSmallRows slots (Kara's trailing window: 166), a unit's whole move fits
+// one workgroup, which reads every source row before it writes any destination: no order is needed and no hazard
+// analysis. The list is checked first (ascending, inside [w0, n), resident, mapped blocks); a unit with a bad entry
+// raises SE_DEV_INDEX and moves nothing.
+constexpr int kSmallRows = 256;
+constexpr int kSmallThreads = 512;
+constexpr int kSmallPer = kSmallRows * 16 / kSmallThreads;  // 16-byte pieces of K (and of V) per thread, 256-B rows
+
+__global__ __launch_bounds__(kSmallThreads) void gather_small(GatherArgs a) {
+  const int unit = blockIdx.x;
+  const int b = unit / a.n_kv, g = unit % a.n_kv;
+  __shared__ int64_t s_soff[kSmallRows], s_doff[kSmallRows];  // byte offsets of the rows; -1: nothing to move
+  __shared__ int s_pval[kSmallRows];
+  __shared__ float s_cval[kSmallRows];
+  __shared__ int s_bad, s_cnt, s_w0;
+  const int32_t *idx = a.idx + (int64_t)unit * a.idx_stride;
+  if (threadIdx.x == 0) {
+    const int cap = a.max_blocks * a.page;
+    const int n = a.n_slots[unit], cnt = a.count[unit];
+    const int w0 = a.window > 0 ? n - a.window : 0;
+    const bool ok = n >= 0 && n <= cap && w0 >= 0 && cnt >= 0 && cnt <= n - w0 && cnt <= a.idx_stride &&
+                    cnt <= kSmallRows;
+    s_bad = ok ? 0 : 1;
+    s_cnt = ok ? cnt : 0;
+    s_w0 = w0;
+  }
+  __syncthreads();
+  const int cnt = s_cnt, w0 = s_w0, n = a.n_slots[unit];
+  const int64_t base = (int64_t)unit * a.max_blocks * a.page;
+  if (threadIdx.x < cnt) {
+    const int j = threadIdx.x;
+    const int sj = idx[j];
+    const int prev = j > 0 ? idx[j - 1] : w0 - 1;
+    const int dj = w0 + j;
+    const bool in = sj >= dj && sj < n && prev < sj;  // ascending and inside the range: sj >= w0 + j follows
+    const int32_t *bt = a.bt + (int64_t)b * a.max_blocks;
+    const int ss = in ? sj : dj;
+    const int sb = bt[ss / a.page], db = bt[dj / a.page];
+    const int pv = a.pos[base + ss];
+    s_pval[j] = pv;
+    s_cval[j] = a.cum ? a.cum[base + ss] : 0.f;
+    const bool ok = in && pv >= 0 && blk_ok(sb, a.num_blocks) && blk_ok(db, a.num_blocks);
+    if (!ok) atomicOr(&s_bad, 1);
+    s_soff[j] = ok && sj != dj ? (((int64_t)sb * a.n_kv + g) * a.page + sj % a.page) * a.row_bytes : -1;
+    s_doff[j] = (((int64_t)(ok ? db : 0) * a.n_kv + g) * a.page + dj % a.page) * a.row_bytes;
+  }
+  __syncthreads();
+  if (s_bad) {
+    if (threadIdx.x == 0) raise(a.status, SE_DEV_INDEX);
+    return;
+  }
+  const int cpr = a.row_bytes / 16, total = cnt * cpr;
+  u32x4 kb[kSmallPer], vb[kSmallPer];
+#pragma unroll
+  for (int i = 0; i < kSmallPer; ++i) {
+    const int x = threadIdx.x + i * kSmallThreads;
+    if (x >= total) continue;
+    const int64_t so = s_soff[x / cpr];
+    if (so < 0) continue;
+    kb[i] = ld16(a.k + so + (x % cpr) * 16);
+    vb[i] = ld16(a.v + so + (x % cpr) * 16);
+  }
+  __syncthreads();  // every source row of the unit is read before any destination row is written
+#pragma unroll
+  for (int i = 0; i < kSmallPer; ++i) {
+    const int x = threadIdx.x + i * kSmallThreads;
+    if (x >= total) continue;
+    const int r = x / cpr, ch = x % cpr;
+    if (s_soff[r] < 0) continue;
+    st16(a.k + s_doff[r] + ch * 16, kb[i]);
+    st16(a.v + s_doff[r] + ch * 16, vb[i]);
+  }
+  if (threadIdx.x < cnt) {
+    a.pos[base + w0 + threadIdx.x] = s_pval[threadIdx.x];
+    if (a.cum) a.cum[base + w0 + threadIdx.x] = s_cval[threadIdx.x];
+  }
+}
+
 struct FinalArgs {
   int32_t *bt, *n_slots, *ctx, *free_blocks, *free_top, *slot_stack, *slot_top;
   const int32_t *count;
@@ -782,13 +860,18 @@ extern "C" int32_t se_compact_evict(se_cache_t *c, const int32_t *idx, const int
     a.row_bytes = row_bytes;
     a.window = p->window;
     a.idx_stride = p->idx_stride;
-    // workgroup 0 moves the hazard set, workgroup x >= 1 tile x - 1; a unit with one tile takes one workgroup
-    const int tile_rows = row_bytes <= 256 ? 256 : 128;
-    const int nt = (p->idx_stride + tile_rows - 1) / tile_rows;
-    a.fold = nt <= 1;
-    const dim3 grid(a.fold ? 1 : nt + 1, units);
-    if (row_bytes <= 256) hipLaunchKernelGGL(se::gather_move<256>, grid, dim3(se::kMoveThreads), 0, st, a);
-    else hipLaunchKernelGGL(se::gather_move<128>, grid, dim3(se::kMoveThreads), 0, st, a);
+    if (p->idx_stride <= se::kSmallRows && row_bytes <= 256) {
+      // every unit's move fits one workgroup: all reads, then all writes
+      hipLaunchKernelGGL(se::gather_small, dim3(units), dim3(se::kSmallThreads), 0, st, a);
+    } else {
+      // workgroup 0 moves the hazard set, workgroup x >= 1 tile x - 1; a unit with one tile takes one workgroup
+      const int tile_rows = row_bytes <= 256 ? 256 : 128;
+      const int nt = (p->idx_stride + tile_rows - 1) / tile_rows;
+      a.fold = nt <= 1;
+      const dim3 grid(a.fold ? 1 : nt + 1, units);
+      if (row_bytes <= 256) hipLaunchKernelGGL(se::gather_move<256>, grid, dim3(se::kMoveThreads), 0, st, a);
+      else hipLaunchKernelGGL(se::gather_move<128>, grid, dim3(se::kMoveThreads), 0, st, a);
+    }
     se::FinalArgs f;
     f.bt = c->block_table;
     f.n_slots = c->n_slots;

@@ -473,11 +473,13 @@ def test_compact_rejects_bad_indices():
     assert se.se_status_read(status) & se.SE_DEV_INDEX
 
 
-def test_compact_rejects_a_free_slot_moved_through_the_hazard_list():
+@pytest.mark.parametrize("stride", [4, 300])
+def test_compact_rejects_a_free_slot_moved_through_the_hazard_list(stride):
     """Kept list [1, 3, 10, 11] of a unit: outputs 0 and 1 read slots 1 and 3 before those slots are overwritten,
-    so output 3 (destination slot 3) is moved with the ordered hazard tiles. Its source, slot 11, is a hole: the
+    so with a list stride of 300 (the tiled path) output 3 (destination slot 3) is moved with the ordered hazard
+    tiles; with a stride of 4 the whole unit is one read-then-write workgroup. Its source, slot 11, is a hole: the
     oracle rejects the list, and the device must flag an index error instead of copying the free slot."""
-    banner("compact: free slot at a hazard destination")
+    banner(f"compact: free slot at a hazard destination, list stride {stride}")
     inp = snap_inputs(B=1, N=300)
     st = inp["cache"]
     st.pos_map[0, 0, 11] = -1
@@ -486,7 +488,7 @@ def test_compact_rejects_a_free_slot_moved_through_the_hazard_list():
     with pytest.raises(IndexError):
         oracle.compact_gather(st, keep)
     dc = to_device(st, 8)
-    idx, cnt = W.pack_lists(keep, 4)
+    idx, cnt = W.pack_lists(keep, stride)
     status = status_word()
     se.se_compact_evict(dc, i32(idx), i32(cnt), mode=se.SE_COMPACT_GATHER, status=status)
     assert se.se_status_read(status) & se.SE_DEV_INDEX
