@@ -496,19 +496,33 @@ __global__ __launch_bounds__(NW * 64, 2) void window_stream(ScoreArgs a) {
 // exp2(s c - m_w c) exp2(m_w c - M) / L of its keys into per-lane column sums. A row's weights are computed once and
 // never leave the registers. At the end the 16 lanes of a key (one per query row of the block layout) are summed.
 //
-// Software pipeline: the MFMAs of block qb + 1 are issued before the softmax work of block qb, so the matrix unit
-// works while the vector unit does. The query blocks reach LDS by DMA (global_load_lds_dwordx4: lane i of a wave
-// writes 16 bytes at M0 + 16 i, no registers involved) into a ring of kQRing slots, kQRing - 2 blocks ahead of
-// their use; each wave fetches a quarter of every block and waits for its own DMAs before the block's barrier.
+// Up to seven key tiles per wave, blocks go in pairs with one barrier per pair: both blocks' MFMAs are issued back
+// to back, so the matrix unit works on the second while the vector unit does the first block's softmax. With eight
+// tiles the registers hold one pair only at one workgroup per CU; there a software pipeline issues the MFMAs of
+// block qb + 1 before the softmax work of block qb instead. The query blocks reach LDS by DMA
+// (global_load_lds_dwordx4: lane i of a wave writes 16 bytes at M0 + 16 i, no registers involved) into a ring of
+// kQRing slots, several blocks ahead of their use; each wave fetches a quarter of every block and waits for its own
+// DMAs before the barrier. The loop is unrolled over the ring, so every LDS address is an immediate offset.
 constexpr int kBidirNW = 4;
 constexpr int kBidirMaxKT = 8;  // key tiles per wave: regions of up to 4 x 8 x 16 = 512 keys
-constexpr int kQRing = 8;       // LDS slots of 16 query rows (4 KiB each)
+#ifndef SE_BIDIR_QRING
+#define SE_BIDIR_QRING 8
+#endif
+constexpr int kQRing = SE_BIDIR_QRING;  // LDS slots of 16 query rows (4 KiB each)
+// pairs of blocks alternate between two halves of the published statistics, and a pass over the ring must end on
+// the second half; the waits keep four blocks (pairs) or five (pipeline) in flight
+static_assert(kQRing % 4 == 0 && kQRing >= 8, "ring of a multiple of four slots, at least eight");
 
 // The DMA is inline assembly so that the compiler's wait-count bookkeeping does not track it (it would otherwise
 // wait for every DMA in flight before any LDS read); the kernel waits for its DMAs itself in bidir_publish(). It
 // has no output register. One wait state separates the M0 write from the DMA that reads it.
 SE_DEV void lds_dma16(const char *g, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(g) : "memory", "m0");
+}
+// the same from a wave-uniform base address (scalar registers) plus a 32-bit per-lane byte offset
+SE_DEV void lds_dma16_s(const char *base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(off), "s"(base)
+               : "memory", "m0");
 }
 
 // Wait until at most N of this wave's DMAs are in flight and its LDS accesses are done, then meet the other waves:
@@ -519,8 +533,8 @@ SE_DEV void bidir_publish() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-// Workgroups per CU the register budget allows: two (256 registers per wave) up to six key tiles per wave; one (512,
-// the accumulators in AGPRs) above, where the keys, two logit sets and the column sums need more.
+// Workgroups per CU the register budget allows: two (256 registers per wave: at seven tiles 112 hold the keys, 124
+// the two logit sets, the column sums and the rest) up to seven key tiles per wave; one (512) at eight.
 #ifndef SE_BIDIR_PIPE_KT
 #define SE_BIDIR_PIPE_KT 8  // key tiles per wave from which the software pipeline is used
 #endif
@@ -536,7 +550,8 @@ __global__ __launch_bounds__(kBidirNW * 64, bidir_wgs_per_cu<KT>()) void window_
   const int b = unit / a.n_kv, g = unit % a.n_kv;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   __shared__ __attribute__((aligned(16))) char s_q[kQRing * 4096];  // query blocks, rows swizzled
-  __shared__ float2 s_ml[2][kBidirNW][16];  // per block parity, wave and row: (m c, sum) of the wave's keys
+  // per parity of the barrier, block of the pair, wave and row: (m c, sum) of the wave's keys
+  __shared__ float2 s_ml[2][2][kBidirNW][16];
   int k0, k1, n;
   key_range(a, unit, k0, k1, n);
   const int nkeys = k1 - k0;
@@ -553,26 +568,33 @@ __global__ __launch_bounds__(kBidirNW * 64, bidir_wgs_per_cu<KT>()) void window_
   // which hold piece (i % 16) ^ row of that row (row r's piece p sits at r * 256 + ((p ^ r) * 16), so the 16 rows a
   // fragment read touches fall in distinct banks).
   const char *qunit = a.q + ((int64_t)b * a.n_kv + g) * total * 256;
-  const uint32_t ring = (uint32_t)(uintptr_t)s_q;
-  auto dma_block = [&](int qb) __attribute__((always_inline)) {
-    const int r = wave * 4 + (lane >> 4);
-    const int rho = min(row0 + qb * 16 + r, total - 1);
-    const int piece = (lane & 15) ^ r;
-    lds_dma16(qunit + (int64_t)rho * 256 + piece * 16,
-              __builtin_amdgcn_readfirstlane(ring + (uint32_t)(qb % kQRing) * 4096 + wave * 1024));
+  const uint32_t ring = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)s_q + wave * 1024);
+  const int dma_r = wave * 4 + (lane >> 4);               // row of the block this lane fetches
+  const uint32_t dma_piece = ((lane & 15) ^ dma_r) << 4;  // byte offset of its 16 bytes within the row
+  // `slot` is qb % kQRing; callers pass it as a constant so that the LDS address folds into an immediate. The
+  // block's first row (clamped to the unit's last) is a scalar base; rows past the unit's last read that row.
+  auto dma_block = [&](int qb, int slot) __attribute__((always_inline)) {
+    const int first = min(row0 + qb * 16, total - 1);  // wave-uniform
+    const uint32_t off = (uint32_t)min(dma_r, total - 1 - first) * 256 + dma_piece;
+    lds_dma16_s(qunit + (int64_t)first * 256, off, ring + (uint32_t)slot * 4096);
   };
-  // B fragments of block qb (k-steps 0..3) from its ring slot: lane l reads row l % 16, piece 4 t + l / 16
-  auto read_frags = [&](int qb, bf16x8 (&qf)[4]) __attribute__((always_inline)) {
-    const char *slot = s_q + (qb % kQRing) * 4096;
+  // B fragments of a block (k-steps 0..3) from ring slot `slot`: lane l reads row l % 16, piece 4 t + l / 16
+  uint32_t frag_off[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
     const int r = lane & 15;
+    frag_off[t] = r * 256 + (((t * 4 + (lane >> 4)) ^ r) << 4);
+  }
+  auto read_frags = [&](int slot, bf16x8 (&qf)[4]) __attribute__((always_inline)) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const int piece = t * 4 + (lane >> 4);
-      qf[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(slot + r * 256 + ((piece ^ r) << 4)));
+      qf[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(s_q + frag_off[t] + slot * 4096));
+      // software-pipelined: only the MFMAs read the fragments, so they too live in the accumulation registers
+      if constexpr (bidir_pipe<KT>()) asm volatile("" : "+a"(qf[t]));
     }
   };
 #pragma unroll
-  for (int i = 0; i < kQRing; ++i) dma_block(i);  // the first kQRing blocks are in flight during the key loads
+  for (int i = 0; i < kQRing; ++i) dma_block(i, i);  // the first kQRing blocks are in flight during the key loads
 
   // resident row of region key j (region-relative), or -1
   auto key_row_of = [&](int j) __attribute__((always_inline)) {
@@ -624,53 +646,43 @@ __global__ __launch_bounds__(kBidirNW * 64, bidir_wgs_per_cu<KT>()) void window_
     }
   };
 
-  // Block qb, whose logits are in `cur` (MFMAs issued one block earlier); `nxt` receives block qb + 1's, from the
-  // fragments in `qf`, which then take block qb + 2's. ALLV: every key of the wave is scored (no masking).
-  // With ALLV the weights are exp2(s c) with no reference subtracted: a row whose sum of weights over the wave's
-  // keys lies in [2^-80, 2^80] has every weight finite and flushes only terms below 2^-126, under 2^-40 of the sum,
-  // so its normalised weights are as exact as against its maximum. A block with a row outside that band has its
-  // logits computed again from its ring slot and weighted against each row's exact maximum. Without ALLV the keys
-  // that are not scored are masked and the exact maximum is the reference. The weights overwrite the logits in
-  // `cur`. Past the last block the MFMAs and fragment reads still run (their slots hold finished DMAs of clamped
-  // rows) and their results are never used, so the loop body has no branch between the MFMA issues and the weights.
-  auto iteration = [&](int qb, floatx4 (&cur)[KT], floatx4 (&nxt)[KT], bf16x8 (&qf)[4], auto allv_tag)
+  // Softmax work of one block whose logits are in `cur`; returns the lane's row sum l over the wave's keys and sets
+  // mc, the reference m c it is taken against. ALLV: every key of the wave is scored (no masking). With ALLV the
+  // weights are exp2(s c) with no reference subtracted: a row whose sum of weights over the wave's keys lies in
+  // [2^-80, 2^80] has every weight finite and flushes only terms below 2^-126, under 2^-40 of the sum, so its
+  // normalised weights are as exact as against its maximum. A block with a row outside that band has its logits
+  // computed again from its ring slot (into `qf`, which the MFMAs have consumed) and weighted against each row's
+  // exact maximum. Without ALLV the keys that are not scored are masked and the exact maximum is the reference. The
+  // weights overwrite the logits.
+  auto weights = [&](floatx4 (&cur)[KT], float mc) __attribute__((always_inline)) {
+    float l;
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        cur[kt][i] = __builtin_amdgcn_exp2f(fmaf(cur[kt][i], c, -mc));
+        l = kt == 0 && i == 0 ? cur[0][0] : l + cur[kt][i];
+      }
+    return cross_row_sum(l);
+  };
+  auto weights_exact = [&](floatx4 (&cur)[KT], float &mc) __attribute__((always_inline)) {
+    float x = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) x = fmaxf(x, fmaxf(fmaxf(cur[kt][0], cur[kt][1]), fmaxf(cur[kt][2], cur[kt][3])));
+    const float mx = cross_row_max(x);
+    mc = mx == -INFINITY ? 0.f : mx * c;  // no scored key: every weight is 0
+    return weights(cur, mc);
+  };
+  auto softmax = [&](floatx4 (&cur)[KT], bf16x8 (&qf)[4], int slot, float &mc, auto allv_tag)
       __attribute__((always_inline)) {
     constexpr bool ALLV = decltype(allv_tag)::value;
-    if constexpr (!bidir_pipe<KT>()) __builtin_amdgcn_sched_barrier(0);  // no overlap of iterations: one logit set
-    float mc = 0.f, l;  // mc: the reference m c of the lane's row (0: none)
-    auto exact_max = [&]() __attribute__((always_inline)) {
-      float x = -INFINITY;
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt) x = fmaxf(x, fmaxf(fmaxf(cur[kt][0], cur[kt][1]), fmaxf(cur[kt][2], cur[kt][3])));
-      return cross_row_max(x);
-    };
-    auto weights = [&]() __attribute__((always_inline)) {
-      l = 0.f;
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          cur[kt][i] = __builtin_amdgcn_exp2f(fmaf(cur[kt][i], c, -mc));
-          l += cur[kt][i];
-        }
-      l = cross_row_sum(l);
-    };
-    auto weights_exact = [&]() __attribute__((always_inline)) {
-      const float mx = exact_max();
-      mc = mx == -INFINITY ? 0.f : mx * c;  // no scored key: every weight is 0
-      weights();
-    };
-    if constexpr (bidir_pipe<KT>()) {
-      mfmas(qf, nxt);
-    } else {  // without the pipeline: this block's own logits, its fragments read just before (visible since the
-              // barrier of block qb - 1)
-      read_frags(qb, qf);
-      mfmas(qf, cur);
-    }
+    mc = 0.f;
+    float l;
     if constexpr (ALLV) {
-      weights();
+      l = weights(cur, 0.f);
       if constexpr (bidir_pipe<KT>()) {
-        // one MFMA, then three vector instructions, 4 KT times: the matrix unit runs under the softmax work
+        // one MFMA (of the next block), then three vector instructions, 4 KT times: the matrix unit runs under the
+        // softmax work
 #pragma unroll
         for (int i = 0; i < 4 * KT; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -678,65 +690,124 @@ __global__ __launch_bounds__(kBidirNW * 64, bidir_wgs_per_cu<KT>()) void window_
         }
       }
       if (__builtin_amdgcn_ballot_w64(!(l >= 0x1p-80f && l <= 0x1p80f))) {  // uniform, rare
-        read_frags(qb, qf);  // qf is free until the fragments of a later block are read after the barrier
+        read_frags(slot, qf);
         mfmas(qf, cur);
-        weights_exact();
+        l = weights_exact(cur, mc);
       }
     } else {
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) cur[kt][i] = (vmask >> (kt * 4 + i)) & 1u ? cur[kt][i] : -INFINITY;
-      weights_exact();
+      l = weights_exact(cur, mc);
     }
-    if (lane < 16) s_ml[qb & 1][wave][lane] = make_float2(mc, l);
-    // block qb + 2 complete in LDS for every wave (and this block's (m, l) published) after the barrier
-    bidir_publish<kQRing - 3>();
-    dma_block(qb + kQRing);  // into block qb's slot, which every wave has read; past the last block: unused
-    if constexpr (bidir_pipe<KT>()) read_frags(qb + 2, qf);
+    return l;
+  };
+  // The normalising factor of the lane's row in block qb, from every wave's published (m c, l) in `pub`: the row's
+  // total L against the common reference M = max of the waves' references (all 0 in the usual case).
+  auto norm = [&](const float2 (&pub)[kBidirNW][16], int qb, float mc, float l, auto allv_tag)
+      __attribute__((always_inline)) {
+    constexpr bool ALLV = decltype(allv_tag)::value;
     float2 w[kBidirNW];
 #pragma unroll
-    for (int v = 0; v < kBidirNW; ++v) w[v] = s_ml[qb & 1][v][lane & 15];
-    // the row's total L against the common reference M = max of the waves' references (all 0 in the usual case)
-    float M, L;
+    for (int v = 0; v < kBidirNW; ++v) w[v] = pub[v][lane & 15];
+    float f;
     if (__builtin_amdgcn_ballot_w64((__float_as_uint(w[0].x) | __float_as_uint(w[1].x) | __float_as_uint(w[2].x) |
-                                     __float_as_uint(w[3].x)) != 0u) == 0) {
-      M = 0.f;
-      L = (w[0].y + w[1].y) + (w[2].y + w[3].y);
+                                     __float_as_uint(w[3].x)) != 0u) == 0 &&
+        ALLV && qb * 16 + 16 <= rows) {
+      // every reference is 0, so mc = M = 0; with every key scored, l and L are positive (a sum outside
+      // [2^-80, 2^80] took the exact path, after which l >= 1); and the whole block holds rows
+      f = __builtin_amdgcn_rcpf((w[0].y + w[1].y) + (w[2].y + w[3].y));
     } else {
-      M = -1e30f;
+      float M = -1e30f;
 #pragma unroll
       for (int v = 0; v < kBidirNW; ++v) M = w[v].y > 0.f ? fmaxf(M, w[v].x) : M;
-      L = 0.f;
+      float L = 0.f;
 #pragma unroll
       for (int v = 0; v < kBidirNW; ++v) L += w[v].y > 0.f ? w[v].y * __builtin_amdgcn_exp2f(w[v].x - M) : 0.f;
+      const bool row_ok = qb * 16 + (lane & 15) < rows && L > 0.f && l > 0.f;
+      f = row_ok ? __builtin_amdgcn_exp2f(mc - M) * __builtin_amdgcn_rcpf(L) : 0.f;
     }
-    const bool row_ok = qb * 16 + (lane & 15) < rows && L > 0.f && l > 0.f;
-    const float f = row_ok ? __builtin_amdgcn_exp2f(mc - M) * __builtin_amdgcn_rcpf(L) : 0.f;
+    return f;
+  };
+  auto accumulate = [&](const floatx4 (&cur)[KT], float f) __attribute__((always_inline)) {
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) col[kt * 4 + i] = fmaf(cur[kt][i], f, col[kt * 4 + i]);
   };
+  // the weights are added where they are made: left alone, the compiler sinks each block's additions into the next
+  // block's and keeps the weights of every block of the unrolled loop alive at once
+  auto pin_col = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < KT * 4; ++i) asm volatile("" : "+v"(col[i]));
+  };
 
   floatx4 accA[KT], accB[KT];
   bf16x8 qf[4];
+
+  // Without the pipeline, blocks go in pairs, qb (ring slot `slot`, even) and qb + 1, with one barrier: both blocks'
+  // MFMAs are issued back to back (the fragments read just before, visible since the previous barrier), so the
+  // second block's run under the first block's softmax work, and the pair's (m c, l) are published together.
+  // Afterwards blocks qb + 2 and qb + 3 have landed in LDS for every wave, and the pair's slots are refilled.
+  auto pair = [&](int qb, int slot, auto allv_tag) __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);  // no overlap of pairs: two logit sets
+    read_frags(slot, qf);
+    mfmas(qf, accA);
+    read_frags(slot + 1, qf);
+    mfmas(qf, accB);
+    float mcA, mcB;
+    const float lA = softmax(accA, qf, slot, mcA, allv_tag);
+    const float lB = softmax(accB, qf, slot + 1, mcB, allv_tag);
+    const int par = (slot >> 1) & 1;
+    if (lane < 16) {
+      s_ml[par][0][wave][lane] = make_float2(mcA, lA);
+      s_ml[par][1][wave][lane] = make_float2(mcB, lB);
+    }
+    bidir_publish<kQRing - 4>();
+    dma_block(qb + kQRing, slot);  // into the pair's slots, which every wave has read; past the last block: unused
+    dma_block(qb + kQRing + 1, slot + 1);
+    const float fA = norm(s_ml[par][0], qb, mcA, lA, allv_tag);
+    const float fB = norm(s_ml[par][1], qb + 1, mcB, lB, allv_tag);
+    accumulate(accA, fA);
+    accumulate(accB, fB);
+    pin_col();
+  };
+  // With the pipeline, block qb's logits are in `cur` (MFMAs issued one block earlier); `nxt` receives block
+  // qb + 1's, from the fragments in `qf`, which then take block qb + 2's.
+  auto single = [&](int qb, int slot, floatx4 (&cur)[KT], floatx4 (&nxt)[KT], auto allv_tag)
+      __attribute__((always_inline)) {
+    mfmas(qf, nxt);
+    float mc;
+    const float l = softmax(cur, qf, slot, mc, allv_tag);
+    if (lane < 16) s_ml[slot & 1][0][wave][lane] = make_float2(mc, l);
+    bidir_publish<kQRing - 3>();  // block qb + 2 complete in LDS for every wave, this block's (m c, l) published
+    dma_block(qb + kQRing, slot);
+    read_frags((slot + 2) % kQRing, qf);
+    accumulate(cur, norm(s_ml[slot & 1][0], qb, mc, l, allv_tag));
+    pin_col();
+  };
+
   if constexpr (bidir_pipe<KT>()) {
     read_frags(0, qf);
     mfmas(qf, accA);
     read_frags(1, qf);
   }
-  // an even number of blocks (a padding block has no rows: its weights are never added), so the loop body holds two
-  // whole iterations and no exit between them
-  const int nqb2 = (nqb + 1) & ~1;
+  // A multiple of kQRing blocks (a padding block has no rows: its weights are never added), so the loop body holds
+  // one iteration per ring slot, with the slot a constant in each, and no exit between them. Past the last block
+  // the MFMAs and fragment reads still run (their slots hold finished DMAs of clamped rows) and their results are
+  // never used, so the body has no branch between the MFMA issues and the weights.
+  const int nqbr = (nqb + kQRing - 1) / kQRing * kQRing;
   auto run = [&](auto allv_tag) __attribute__((always_inline)) {
-    for (int qb = 0; qb < nqb2; qb += 2) {
-      if constexpr (bidir_pipe<KT>()) {
-        iteration(qb, accA, accB, qf, allv_tag);
-        iteration(qb + 1, accB, accA, qf, allv_tag);
-      } else {
-        iteration(qb, accA, accA, qf, allv_tag);
-        iteration(qb + 1, accA, accA, qf, allv_tag);
+    for (int qb = 0; qb < nqbr; qb += kQRing) {
+#pragma unroll
+      for (int j = 0; j < kQRing; j += 2) {
+        if constexpr (bidir_pipe<KT>()) {
+          single(qb + j, j, accA, accB, allv_tag);
+          single(qb + j + 1, j + 1, accB, accA, allv_tag);
+        } else {
+          pair(qb + j, j, allv_tag);
+        }
       }
     }
   };
