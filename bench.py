@@ -231,8 +231,36 @@ class Workload:
     before a step (a device copy from one pristine clone), outside the timed region. tokens: KV tokens per step (the
     metric's unit); alg: algorithmic bytes (and flops for scoring) per call of each entry point."""
 
-    def __init__(self, cfg, tokens, alg, step, restore=None):
+    def __init__(self, cfg, tokens, alg, step, restore=None, outputs=None):
         self.cfg, self.tokens, self.alg, self.step, self.restore = cfg, tokens, alg, step, restore
+        self.outputs = outputs or {}  # named device tensors a step writes besides the cache (for tests)
+
+
+def capture_step(wl, i):
+    """The calls of step ``i`` captured as one HIP graph on a side stream (run once eagerly there first, as capture
+    requires), on the restored cache; the caller restores it again before each replay."""
+    import torch
+
+    wl.restore()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _, fn in wl.step(i):
+            fn()
+    torch.cuda.current_stream().wait_stream(side)
+    wl.restore()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _, fn in wl.step(i):
+            fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def cache_tensors(se, c):
+    """Every field of a device cache, by name."""
+    return {f"cache.{f}": getattr(c, f) for f in se.DeviceCache.FIELDS if getattr(c, f) is not None}
 
 
 def restorer(se, work):
@@ -248,10 +276,10 @@ def restorer(se, work):
     return restore
 
 
-def setup_c1(se, WF, W, dev, status, steps):
+def setup_c1(se, WF, W, dev, status, steps, cfg=None):
     import torch
 
-    cfg = W.C1
+    cfg = cfg or W.C1
     inp = W.gen_snapkv(cfg, seed=0, threads=16)
     c = device_cache(se, cfg, inp["cache"], dev)
     q_win, q_dec = to_dev_bf16(inp["q_win"], dev), to_dev_bf16(inp["q_dec"], dev)
@@ -268,15 +296,16 @@ def setup_c1(se, WF, W, dev, status, steps):
         "se_compact_evict": {"bytes": 2 * (B * G * keep * row * 2) + 2 * B * G * keep * 4},
         "se_sparse_decode_attn": {"bytes": B * G * keep * row * 2 + B * cfg.hq * cfg.d * (2 + 4)},
     }
-    return Workload(cfg, B * N, alg, lambda i: calls, restorer(se, c))
+    return Workload(cfg, B * N, alg, lambda i: calls, restorer(se, c),
+                    outputs=dict(cache_tensors(se, c), scores=e.scores, idx=e.idx, count=e.count, out=e.out))
 
 
-def setup_c2(se, WF, W, dev, status, steps):
+def setup_c2(se, WF, W, dev, status, steps, cfg=None):
     """Kara's event on the whole batch (bidirectional window scores, top-K candidates, Token2Chunk, trailing-window
     compaction), then one decode step (append, attention over every resident slot)."""
     import torch
 
-    cfg = W.scaled(W.C2, period=1, events=1)
+    cfg = cfg or W.scaled(W.C2, period=1, events=1)
     inp = W.gen_kara(cfg, seed=0, threads=16)
     c = device_cache(se, cfg, inp["cache"], dev)
     # the fresh cache's trailing window holds positions N - window .. N - 1, the first queries the workload keeps
@@ -318,7 +347,9 @@ def setup_c2(se, WF, W, dev, status, steps):
         "se_cache_append": {"bytes": 2 * B * G * row * 2},
         "se_sparse_decode_attn": {"bytes": B * G * after * (2 * row + 4) + B * cfg.hq * cfg.d * (2 + 4)},
     }
-    return Workload(cfg, B * W_, alg, lambda i: calls, restorer(se, c))
+    return Workload(cfg, B * W_, alg, lambda i: calls, restorer(se, c),
+                    outputs=dict(cache_tensors(se, c), scores=ev.scores, cand=ev.cand, keep=ev.keep,
+                                 keep_count=ev.keep_count, out=dec.out))
 
 
 def setup_c3(se, WF, W, dev, status, steps):
@@ -743,6 +774,8 @@ def main():
     ap.add_argument("--cpu-seqs", type=int, default=2, help="sequences per oracle worker in the CPU baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle time for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="time the steps as host-launched calls, not as replays of the step captured in a HIP graph")
     ap.add_argument("--calibrate-copy", type=int, metavar="MIB", help="run only a plain copy of MIB MiB, --steps times")
     ap.add_argument("--copy-ceiling", action="store_true",
                     help="time plain copies of 8 MiB to 1 GiB (--steps launches each) and exit")
@@ -890,6 +923,27 @@ def main():
         "roofline": roofline,
         "calls": breakdown,
     }
+    if wl.restore and getattr(wl, "graph", None) is None and not args.eager:
+        # One step captured as a HIP graph (a serving loop launches it that way) and replayed, each time on the
+        # restored cache after a last-level-cache flush, between two device synchronisations: the line's step time
+        # is the mean replay. The per-call times and the roofline above come from the eager steps.
+        step_graph = capture_step(wl, args.warmup + args.steps)
+        replay_s = 0.0
+        for i in range(args.steps):
+            prepare()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            step_graph.replay()
+            torch.cuda.synchronize()
+            replay_s += time.perf_counter() - t0
+        require_clean_status(se, status, "the graph replays")
+        ms_per_step = replay_s * 1e3 / args.steps
+        result["value"] = round(wl.tokens / (ms_per_step * 1e-3), 1)
+        result["ms_per_step"] = round(ms_per_step, 4)
+        result["config"]["timing"] = ("each step as one captured HIP graph, replayed on a restored cache after a "
+                                      f"last-level-cache flush; host-launched steps took {elapsed * 1e3 / args.steps:.4f}"
+                                      " ms; per-call times from those")
+        log(f"step graph: {ms_per_step:.4f} ms per replay, host-launched {elapsed * 1e3 / args.steps:.4f} ms")
     if getattr(wl, "graph", None) is not None:
         # the workload's whole loop as one captured graph, replayed on the restored cache after a flush: the line's
         # step time is the replay's per decode step
