@@ -69,7 +69,7 @@ def device_cache(se, cfg, c, dev):
 
 # kernels each call launches (for matching profiler rows to calls) and the sources they are built from
 CALL_KERNELS = {
-    "se_window_score": ["window_stream", "colsum_reduce", "stats_valu", "colsum_valu"],
+    "se_window_score": ["window_stream", "window_bidir", "colsum_reduce", "stats_valu", "colsum_valu"],
     "se_topk_select": ["topk_kernel"],
     "se_token2chunk": ["t2c_kernel"],
     "se_compact_evict": ["gather_move", "gather_small", "gather_extents", "gather_push", "evict_slots_kernel"],
@@ -775,7 +775,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle time for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true",
-                    help="time the steps as host-launched calls, not as replays of the step captured in a HIP graph")
+                    help="time host-launched steps only, with no captured HIP graph (for counter runs that count calls)")
     ap.add_argument("--calibrate-copy", type=int, metavar="MIB", help="run only a plain copy of MIB MiB, --steps times")
     ap.add_argument("--copy-ceiling", action="store_true",
                     help="time plain copies of 8 MiB to 1 GiB (--steps launches each) and exit")
@@ -944,7 +944,7 @@ def main():
                                       f"last-level-cache flush; host-launched steps took {elapsed * 1e3 / args.steps:.4f}"
                                       " ms; per-call times from those")
         log(f"step graph: {ms_per_step:.4f} ms per replay, host-launched {elapsed * 1e3 / args.steps:.4f} ms")
-    if getattr(wl, "graph", None) is not None:
+    if getattr(wl, "graph", None) is not None and not args.eager:
         # the workload's whole loop as one captured graph, replayed on the restored cache after a flush: the line's
         # step time is the replay's per decode step
         flush = torch.empty(2**28, dtype=torch.float32, device=dev)
