@@ -236,6 +236,38 @@ class Workload:
         self.outputs = outputs or {}  # named device tensors a step writes besides the cache (for tests)
 
 
+def per_call_marks(wl, args, prepare, calls):
+    """[(start, end) event per call] for each of args.steps restored steps queued behind a device spin."""
+    import torch
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    torch.cuda._sleep(1 << 22)
+    e1.record()
+    torch.cuda.synchronize()
+    cycles_per_ms = (1 << 22) / max(e0.elapsed_time(e1), 1e-3)
+    spin_ms = 4.0
+    marks = []
+    i = 0
+    while i < args.steps:
+        prepare()
+        torch.cuda.synchronize()
+        torch.cuda._sleep(int(spin_ms * cycles_per_ms))
+        m = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in calls]
+        for (name, fn), (a, b) in zip(wl.step(args.warmup + i), m):
+            a.record()
+            fn()
+            b.record()
+        late = m[0][0].query()  # the device reached the first call before the host had queued the step
+        torch.cuda.synchronize()
+        if late and spin_ms < 1000:
+            spin_ms *= 2
+            continue
+        marks.append(m)
+        i += 1
+    return marks
+
+
 def capture_step(wl, i):
     """The calls of step ``i`` captured as one HIP graph on a side stream (run once eagerly there first, as capture
     requires), on the restored cache; the caller restores it again before each replay."""
@@ -873,6 +905,12 @@ def main():
                 e1.record()
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t_start
+    if wl.restore:
+        # Per-call times: the restored steps again, each behind a device spin long enough that the host has queued
+        # the whole step before the first call starts, so that the events around each call see only device time
+        # (with small calls the device would otherwise wait for the host between them). A spin that ended before
+        # the host had queued the step is doubled and the step run again.
+        marks = per_call_marks(wl, args, prepare, calls)
     se.set_operand_checks(True)
     require_clean_status(se, status, "the timed steps")
     # per entry point: its time per step (summed over its calls when a step makes several, as C7's chunks do)
