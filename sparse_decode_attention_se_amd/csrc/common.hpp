@@ -62,6 +62,32 @@ SE_DEV float cross_row_max(float x) {
   auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
 }
+// sums of 16 values over the 16 lanes of a row, scattered: lane j of the row receives the total of value j.
+// Four exchange rounds (partners 15 - j, 7 - j within each half, j ^ 2, j ^ 1); each halves the values a lane
+// carries: 15 DPP additions instead of 16 full row sums.
+template <int N, int CTRL>
+SE_DEV void rs_round(float (&v)[16], bool hi) {
+#pragma unroll
+  for (int i = 0; i < N / 2; ++i) {
+    const float keep = hi ? v[N / 2 + i] : v[i];
+    const float send = hi ? v[i] : v[N / 2 + i];
+    v[i] = keep + dpp_f<CTRL>(send);
+  }
+}
+SE_DEV float row16_reduce_scatter(float (&v)[16]) {
+  const int j = threadIdx.x & 15;
+  rs_round<16, 0x140>(v, j & 8);  // row_mirror: j <-> 15 - j
+  rs_round<8, 0x141>(v, j & 4);   // row_half_mirror: j <-> 7 - j
+  rs_round<4, 0x4e>(v, j & 2);    // quad_perm [2,3,0,1]
+  rs_round<2, 0xb1>(v, j & 1);    // quad_perm [1,0,3,2]
+  return v[0];
+}
+// lane N of each row of 16 lanes, in every lane of the row (DPP row_newbcast)
+template <int N>
+SE_DEV float row16_bcast(float x) {
+  return dpp_f<0x150 + N>(x);
+}
+
 SE_DEV float wave_sum(float x) { return cross_row_sum(row16_sum(x)); }
 SE_DEV float wave_max(float x) { return cross_row_max(row16_max(x)); }
 

@@ -199,7 +199,69 @@ __global__ __launch_bounds__(kThreads, SE_DECODE_WG_PER_CU) void decode_partial(
       rv[u] = v;
     }
   };
+  // With R x kUnroll = 16 logits per lane-row and step, one per lane (the GQA group of four heads): the partial dot
+  // products are reduce-scattered over the row's 16 lanes, so lane cl holds the logit of row u = cl / R of the
+  // step, head h = cl % R, and does that logit's softmax work alone. Each lane keeps the running max ml and the sum
+  // ll of its head (the four lanes of a head move ml together: their maximum is shared); the weights are then
+  // broadcast to the row for the V accumulation.
+  constexpr bool kOne = R * kUnroll == 16;
+  float ml = -1e30f, ll = 0.f;
+  auto step1 = [&](int it, const u32x4 (&kb)[kUnroll], const u32x4 (&vb)[kUnroll], const int (&rv)[kUnroll])
+      __attribute__((always_inline)) {
+    float d[16];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+      for (int h = 0; h < R; ++h) d[(u * R + h) & 15] = V::dot(q[h], kb[u], 0.f);
+    float s = row16_reduce_scatter(d);
+    const int ul = cl / R, hl = cl % R;
+    const int rvl = ul == 0 ? rv[0] : ul == 1 ? rv[1 % kUnroll] : ul == 2 ? rv[2 % kUnroll] : rv[3 % kUnroll];
+    s = rvl >= 0 ? s * a.scale_log2 : -INFINITY;
+    if (a.logits) {
+      const int i = it * 16 + ul * 4 + lrow;
+      if (i < lim) a.logits[((int64_t)unit * a.rows_bound + row0 + w0 + i) * R + hl] = s;
+    }
+    float mx = fmaxf(s, dpp_f<kRowRor4>(s));  // the head's maximum over the step's rows of this lane-row
+    if constexpr (R == 4) mx = fmaxf(mx, dpp_f<kRowRor8>(mx));
+    if (__builtin_amdgcn_ballot_w64(mx > ml + kLazy)) {  // uniform, rare
+      const float mn = mx > ml + kLazy ? mx : ml;
+      const float f = __builtin_amdgcn_exp2f(ml - mn);
+      ml = mn;
+      ll *= f;
+      float fh[R];
+      fh[0] = row16_bcast<0>(f);
+      if constexpr (R > 1) fh[1 % R] = row16_bcast<1 % R>(f);
+      if constexpr (R > 2) fh[2 % R] = row16_bcast<2 % R>(f), fh[3 % R] = row16_bcast<3 % R>(f);
+#pragma unroll
+      for (int h = 0; h < R; ++h)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[h][e] *= fh[h];
+    }
+    const float p = __builtin_amdgcn_exp2f(s - ml);
+    ll += p;
+    float pj[16];
+    pj[0] = row16_bcast<0>(p), pj[1] = row16_bcast<1>(p), pj[2] = row16_bcast<2>(p), pj[3] = row16_bcast<3>(p);
+    pj[4] = row16_bcast<4>(p), pj[5] = row16_bcast<5>(p), pj[6] = row16_bcast<6>(p), pj[7] = row16_bcast<7>(p);
+    pj[8] = row16_bcast<8>(p), pj[9] = row16_bcast<9>(p), pj[10] = row16_bcast<10>(p);
+    pj[11] = row16_bcast<11>(p), pj[12] = row16_bcast<12>(p), pj[13] = row16_bcast<13>(p);
+    pj[14] = row16_bcast<14>(p), pj[15] = row16_bcast<15>(p);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const bool ok = rv[u] >= 0;  // rows outside the view read row 0 of the pool: drop its values
+      const u32x4 w = {ok ? vb[u].x : 0u, ok ? vb[u].y : 0u, ok ? vb[u].z : 0u, ok ? vb[u].w : 0u};
+      float x[EPL];
+      V::widen(w, x);
+#pragma unroll
+      for (int h = 0; h < R; ++h)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(pj[(u * R + h) & 15], x[e], acc[h][e]);
+    }
+  };
   auto step = [&](int it, const u32x4 (&kb)[kUnroll], const u32x4 (&vb)[kUnroll], const int (&rv)[kUnroll]) {
+    if constexpr (kOne) {
+      step1(it, kb, vb, rv);
+      return;
+    }
     float sc[kUnroll][R];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
@@ -260,6 +322,17 @@ __global__ __launch_bounds__(kThreads, SE_DECODE_WG_PER_CU) void decode_partial(
     step(it + 1, kb2, vb2, rb2);
   }
 
+  if constexpr (kOne) {
+    // per head: the max every lane of the head holds, the sum over the head's four lanes, in every lane of the row
+    float lsum = ll + dpp_f<kRowRor4>(ll);
+    if constexpr (R == 4) lsum += dpp_f<kRowRor8>(lsum);
+    m[0] = row16_bcast<0>(ml), l[0] = row16_bcast<0>(lsum);
+    if constexpr (R > 1) m[1 % R] = row16_bcast<1 % R>(ml), l[1 % R] = row16_bcast<1 % R>(lsum);
+    if constexpr (R > 2) {
+      m[2 % R] = row16_bcast<2 % R>(ml), l[2 % R] = row16_bcast<2 % R>(lsum);
+      m[3 % R] = row16_bcast<3 % R>(ml), l[3 % R] = row16_bcast<3 % R>(lsum);
+    }
+  }
   // merge the four lane-rows of the wave
 #pragma unroll
   for (int off = 16; off <= 32; off <<= 1) {
@@ -472,8 +545,65 @@ __global__ __launch_bounds__(kUnitThreads) void decode_unit(DecodeArgs a) {
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
   }
+  // With R x U = 16, one logit per lane as in decode_partial (lane cl: row u = cl / R of the step, head cl % R),
+  // which also writes it to LDS for the cumulative scores.
+  constexpr bool kOne = R * U == 16;
+  float ml = -1e30f, ll = 0.f;
+  auto step1 = [&](int rbase, const u32x4 (&kb)[U], const u32x4 (&vb)[U], const int (&rv)[U])
+      __attribute__((always_inline)) {
+    float d[16];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int h = 0; h < R; ++h) d[(u * R + h) & 15] = V::dot(q[h], kb[u], 0.f);
+    float s = row16_reduce_scatter(d);
+    const int ul = cl / R, hl = cl % R;
+    const int rvl = ul == 0 ? rv[0] : ul == 1 ? rv[1 % U] : ul == 2 ? rv[2 % U] : rv[3 % U];
+    s = rvl >= 0 ? s * a.scale_log2 : -INFINITY;
+    const int r = rbase + ul * 4 + lrow;
+    if (r < rows) s_lg[r * R + hl] = s;
+    float mx = fmaxf(s, dpp_f<kRowRor4>(s));
+    if constexpr (R == 4) mx = fmaxf(mx, dpp_f<kRowRor8>(mx));
+    if (__builtin_amdgcn_ballot_w64(mx > ml + kLazy)) {  // uniform, rare
+      const float mn = mx > ml + kLazy ? mx : ml;
+      const float f = __builtin_amdgcn_exp2f(ml - mn);
+      ml = mn;
+      ll *= f;
+      float fh[R];
+      fh[0] = row16_bcast<0>(f);
+      if constexpr (R > 1) fh[1 % R] = row16_bcast<1 % R>(f);
+      if constexpr (R > 2) fh[2 % R] = row16_bcast<2 % R>(f), fh[3 % R] = row16_bcast<3 % R>(f);
+#pragma unroll
+      for (int h = 0; h < R; ++h)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[h][e] *= fh[h];
+    }
+    const float p = __builtin_amdgcn_exp2f(s - ml);
+    ll += p;
+    float pj[16];
+    pj[0] = row16_bcast<0>(p), pj[1] = row16_bcast<1>(p), pj[2] = row16_bcast<2>(p), pj[3] = row16_bcast<3>(p);
+    pj[4] = row16_bcast<4>(p), pj[5] = row16_bcast<5>(p), pj[6] = row16_bcast<6>(p), pj[7] = row16_bcast<7>(p);
+    pj[8] = row16_bcast<8>(p), pj[9] = row16_bcast<9>(p), pj[10] = row16_bcast<10>(p);
+    pj[11] = row16_bcast<11>(p), pj[12] = row16_bcast<12>(p), pj[13] = row16_bcast<13>(p);
+    pj[14] = row16_bcast<14>(p), pj[15] = row16_bcast<15>(p);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool ok = rv[u] >= 0;
+      const u32x4 w = {ok ? vb[u].x : 0u, ok ? vb[u].y : 0u, ok ? vb[u].z : 0u, ok ? vb[u].w : 0u};
+      float x[EPL];
+      V::widen(w, x);
+#pragma unroll
+      for (int h = 0; h < R; ++h)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(pj[(u * R + h) & 15], x[e], acc[h][e]);
+    }
+  };
   // one step in groups of UG rows per lane-row (fewer live scores)
   auto step = [&](int rbase, const u32x4 (&kb)[U], const u32x4 (&vb)[U], const int (&rv)[U]) {
+    if constexpr (kOne) {
+      step1(rbase, kb, vb, rv);
+      return;
+    }
 #pragma unroll
     for (int hf = 0; hf < U / UG; ++hf) {
       float sc[UG][R];
@@ -575,6 +705,16 @@ __global__ __launch_bounds__(kUnitThreads) void decode_unit(DecodeArgs a) {
   }
   if (bad) raise(a.status, SE_DEV_INDEX);
 
+  if constexpr (kOne) {
+    float lsum = ll + dpp_f<kRowRor4>(ll);
+    if constexpr (R == 4) lsum += dpp_f<kRowRor8>(lsum);
+    m[0] = row16_bcast<0>(ml), l[0] = row16_bcast<0>(lsum);
+    if constexpr (R > 1) m[1 % R] = row16_bcast<1 % R>(ml), l[1 % R] = row16_bcast<1 % R>(lsum);
+    if constexpr (R > 2) {
+      m[2 % R] = row16_bcast<2 % R>(ml), l[2 % R] = row16_bcast<2 % R>(lsum);
+      m[3 % R] = row16_bcast<3 % R>(ml), l[3 % R] = row16_bcast<3 % R>(lsum);
+    }
+  }
   // this thread's cumulative scores, loaded while the waves merge
   float cv[kCum];
 #pragma unroll

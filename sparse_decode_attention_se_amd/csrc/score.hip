@@ -242,30 +242,6 @@ SE_DEV void stream_mask(const int *s_kp, int lim, floatx4 (&acc)[4]) {
     }
 }
 
-// sums of 16 values over the 16 lanes of a row, scattered: lane j of the row receives the total of value j.
-// Four exchange rounds (partners j^15, j^7, j^2, j^1 within the row); each halves the values a lane carries.
-template <int CTRL>
-SE_DEV float dpp_any(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
-}
-template <int N, int CTRL>
-SE_DEV void rs_round(float (&v)[16], bool hi) {
-#pragma unroll
-  for (int i = 0; i < N / 2; ++i) {
-    const float keep = hi ? v[N / 2 + i] : v[i];
-    const float send = hi ? v[i] : v[N / 2 + i];
-    v[i] = keep + dpp_any<CTRL>(send);
-  }
-}
-SE_DEV float row16_reduce_scatter(float (&v)[16]) {
-  const int j = threadIdx.x & 15;
-  rs_round<16, 0x140>(v, j & 8);  // row_mirror: j <-> 15 - j
-  rs_round<8, 0x141>(v, j & 4);   // row_half_mirror: j <-> 7 - j
-  rs_round<4, 0x4e>(v, j & 2);    // quad_perm [2,3,0,1]
-  rs_round<2, 0xb1>(v, j & 1);    // quad_perm [1,0,3,2]
-  return v[0];
-}
-
 // PASS 1: row statistics of the chunk; PASS 2: column sums with the merged statistics. PASS 3 (a unit's whole key
 // range in one chunk of at most two steps per wave): both, in one workgroup, with the keys kept in registers and
 // the row statistics merged in LDS.
