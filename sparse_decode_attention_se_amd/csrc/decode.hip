@@ -19,6 +19,21 @@ namespace se {
 namespace {
 
 constexpr int kThreads = 256;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+// out[h] = x of lane h of the lane's row of 16, h < N
+template <int N>
+SE_DEV void bcast_r(float x, float (&out)[N]) {
+  out[0] = row16_bcast<0>(x);
+  if constexpr (N > 1) out[1 % N] = row16_bcast<1 % N>(x);
+  if constexpr (N > 2) out[2 % N] = row16_bcast<2 % N>(x), out[3 % N] = row16_bcast<3 % N>(x);
+  if constexpr (N > 4) {
+    out[4 % N] = row16_bcast<4 % N>(x), out[5 % N] = row16_bcast<5 % N>(x);
+    out[6 % N] = row16_bcast<6 % N>(x), out[7 % N] = row16_bcast<7 % N>(x);
+  }
+}
 constexpr int kUnroll = 4;  // wave-loads in flight per lane-row
 
 template <int DTYPE>
@@ -125,6 +140,22 @@ __global__ __launch_bounds__(kThreads, SE_DECODE_WG_PER_CU) void decode_partial(
   u32x4 q[R];
 #pragma unroll
   for (int h = 0; h < R; ++h) q[h] = ld16(a.q + (((int64_t)b * a.n_kv + g) * R + h) * RB + cl * 16);
+  // bf16, d = 128: the step's logits come from MFMA. S^T = K Q^T per 16 keys (v_mfma_f32_16x16x32_bf16, four
+  // k-steps): A = 16 keys x 32 dims (lane l: key l % 16, dims 32 t + 8 (l / 16)), B = 32 dims x 16 columns, the
+  // group's R query heads and zeros (lane l: head l % 16). Lane l receives keys 4 (l / 16) + v of head l % 16:
+  // in lane-row lr, lanes 0..R-1 hold the logits of keys 4 lr .. 4 lr + 3, the keys whose V slices that lane-row
+  // accumulates, so the weights reach them by broadcasts inside the row.
+  constexpr bool kMfma = DTYPE == SE_DTYPE_BF16 && EPL == 8;
+  bf16x8 qf[4];
+  if constexpr (kMfma) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      qf[t] = __builtin_bit_cast(
+          bf16x8, cl < R ? ld16(a.q + (((int64_t)b * a.n_kv + g) * R + (cl < R ? cl : 0)) * RB + t * 64 + lrow * 16)
+                         : z);
+    }
+  }
 
   // Resolve the chunk's view rows to pool rows (-1: outside the view or not resident) into LDS. Loads are
   // issued speculatively (only their addresses are range-checked), so the chain is two rounds deep.
@@ -189,6 +220,22 @@ __global__ __launch_bounds__(kThreads, SE_DECODE_WG_PER_CU) void decode_partial(
   const int nit = (lim + 15) / 16;
 
   auto load = [&](int it, u32x4 (&kb)[kUnroll], u32x4 (&vb)[kUnroll], int (&rv)[kUnroll]) {
+    if constexpr (kMfma) {
+      // K in the MFMA layout (key cl of the step, k-step t at byte 64 t); V of keys 4 lrow + u, slice cl
+      const int ik = it * 16 + cl;
+      const int vk = ik < lim ? s_row[w0 + ik] : -1;
+      const char *kr = a.k + (int64_t)(vk >= 0 ? vk : 0) * RB + lrow * 16;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) kb[t] = ld16(kr + t * 64);
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int i = it * 16 + lrow * 4 + u;
+        const int v = i < lim ? s_row[w0 + i] : -1;
+        vb[u] = ld16(a.v + (int64_t)(v >= 0 ? v : 0) * RB + cl * 16);
+        rv[u] = v;
+      }
+      return;
+    }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int i = it * 16 + u * 4 + lrow;
@@ -257,8 +304,61 @@ __global__ __launch_bounds__(kThreads, SE_DECODE_WG_PER_CU) void decode_partial(
         for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(pj[(u * R + h) & 15], x[e], acc[h][e]);
     }
   };
+  // The MFMA step: lane (lr, c) with c < R holds the logits of keys 4 lr + v, head c, and does their softmax work:
+  // the head's maximum over the step's 16 keys (in-lane, then across the four lane-rows), its running max ml
+  // (shared by the head's four lanes) and its lane-row's sum ll.
+  auto stepm = [&](int it, const u32x4 (&kb)[kUnroll], const u32x4 (&vb)[kUnroll], const int (&rv)[kUnroll])
+      __attribute__((always_inline)) {
+    floatx4 lg = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) lg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kb[t]), qf[t],
+                                                                           lg, 0, 0, 0);
+    float sv[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) sv[v] = rv[v] >= 0 ? lg[v] * a.scale_log2 : -INFINITY;
+    if (a.logits && cl < R) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int i = it * 16 + lrow * 4 + v;
+        if (i < lim) a.logits[((int64_t)unit * a.rows_bound + row0 + w0 + i) * R + cl] = sv[v];
+      }
+    }
+    const float mx = cross_row_max(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
+    if (__builtin_amdgcn_ballot_w64(mx > ml + kLazy)) {  // uniform, rare
+      const float mn = mx > ml + kLazy ? mx : ml;
+      const float f = __builtin_amdgcn_exp2f(ml - mn);
+      ml = mn;
+      ll *= f;
+      float fh[R];
+      bcast_r<R>(f, fh);
+#pragma unroll
+      for (int h = 0; h < R; ++h)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[h][e] *= fh[h];
+    }
+    float pv[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) pv[v] = __builtin_amdgcn_exp2f(sv[v] - ml);
+    ll += (pv[0] + pv[1]) + (pv[2] + pv[3]);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      float ph[R];
+      bcast_r<R>(pv[u], ph);
+      const bool ok = rv[u] >= 0;  // rows outside the view read row 0 of the pool: drop its values
+      const u32x4 w = {ok ? vb[u].x : 0u, ok ? vb[u].y : 0u, ok ? vb[u].z : 0u, ok ? vb[u].w : 0u};
+      float x[EPL];
+      V::widen(w, x);
+#pragma unroll
+      for (int h = 0; h < R; ++h)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(ph[h], x[e], acc[h][e]);
+    }
+  };
   auto step = [&](int it, const u32x4 (&kb)[kUnroll], const u32x4 (&vb)[kUnroll], const int (&rv)[kUnroll]) {
-    if constexpr (kOne) {
+    if constexpr (kMfma) {
+      stepm(it, kb, vb, rv);
+      return;
+    } else if constexpr (kOne) {
       step1(it, kb, vb, rv);
       return;
     }
@@ -322,7 +422,11 @@ __global__ __launch_bounds__(kThreads, SE_DECODE_WG_PER_CU) void decode_partial(
     step(it + 1, kb2, vb2, rb2);
   }
 
-  if constexpr (kOne) {
+  if constexpr (kMfma) {
+    // per head and lane-row: the head's max and the row's sum, from lane h of the row, in every lane of the row
+    bcast_r<R>(ml, m);
+    bcast_r<R>(ll, l);
+  } else if constexpr (kOne) {
     // per head: the max every lane of the head holds, the sum over the head's four lanes, in every lane of the row
     float lsum = ll + dpp_f<kRowRor4>(ll);
     if constexpr (R == 4) lsum += dpp_f<kRowRor8>(lsum);
@@ -491,6 +595,18 @@ __global__ __launch_bounds__(kUnitThreads) void decode_unit(DecodeArgs a) {
   u32x4 q[R];
 #pragma unroll
   for (int h = 0; h < R; ++h) q[h] = ld16(a.q + (((int64_t)b * a.n_kv + g) * R + h) * RB + cl * 16);
+  // bf16, d = 128: logits from MFMA in decode_partial's layout (lane-row lr's lanes 0..R-1 hold keys 4 lr + v)
+  constexpr bool kMfma = DTYPE == SE_DTYPE_BF16 && EPL == 8;
+  bf16x8 qf[4];
+  if constexpr (kMfma) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      qf[t] = __builtin_bit_cast(
+          bf16x8, cl < R ? ld16(a.q + (((int64_t)b * a.n_kv + g) * R + (cl < R ? cl : 0)) * RB + t * 64 + lrow * 16)
+                         : z);
+    }
+  }
 
   const int cap = a.max_blocks * a.page;
   int n = a.n_slots[unit];
@@ -524,11 +640,27 @@ __global__ __launch_bounds__(kUnitThreads) void decode_unit(DecodeArgs a) {
     }
     return v;
   };
-  auto rows_from = [&](int vs, int half, int (&rv)[U]) {
+  // rv[u]: the pool row of the step's row u * 4 + lrow (MFMA: of row lrow * 4 + u, the V rows, and rv[U] that of
+  // row cl, the lane's key for the K fragments)
+  auto rows_from = [&](int vs, int half, int (&rv)[U + 1]) {
+    if constexpr (kMfma) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) rv[u] = __builtin_amdgcn_ds_bpermute((half * SR + lrow * 4 + u) * 4, vs);
+      rv[U] = __builtin_amdgcn_ds_bpermute((half * SR + cl) * 4, vs);
+      return;
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) rv[u] = __builtin_amdgcn_ds_bpermute((half * SR + u * 4 + lrow) * 4, vs);
   };
-  auto load = [&](const int (&rv)[U], u32x4 (&kb)[U], u32x4 (&vb)[U]) {
+  auto load = [&](const int (&rv)[U + 1], u32x4 (&kb)[U], u32x4 (&vb)[U]) {
+    if constexpr (kMfma) {
+      const char *kr = a.k + (int64_t)(rv[U] >= 0 ? rv[U] : 0) * RB + lrow * 16;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) kb[t] = ld16(kr + t * 64);
+#pragma unroll
+      for (int u = 0; u < U; ++u) vb[u] = ld16(a.v + (int64_t)(rv[u] >= 0 ? rv[u] : 0) * RB + cl * 16);
+      return;
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t off = (int64_t)(rv[u] >= 0 ? rv[u] : 0) * RB + cl * 16;
@@ -549,7 +681,7 @@ __global__ __launch_bounds__(kUnitThreads) void decode_unit(DecodeArgs a) {
   // which also writes it to LDS for the cumulative scores.
   constexpr bool kOne = R * U == 16;
   float ml = -1e30f, ll = 0.f;
-  auto step1 = [&](int rbase, const u32x4 (&kb)[U], const u32x4 (&vb)[U], const int (&rv)[U])
+  auto step1 = [&](int rbase, const u32x4 (&kb)[U], const u32x4 (&vb)[U], const int (&rv)[U + 1])
       __attribute__((always_inline)) {
     float d[16];
 #pragma unroll
@@ -598,9 +730,59 @@ __global__ __launch_bounds__(kUnitThreads) void decode_unit(DecodeArgs a) {
         for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(pj[(u * R + h) & 15], x[e], acc[h][e]);
     }
   };
+  auto stepm = [&](int rbase, const u32x4 (&kb)[U], const u32x4 (&vb)[U], const int (&rv)[U + 1])
+      __attribute__((always_inline)) {
+    floatx4 lg = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) lg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kb[t]), qf[t],
+                                                                           lg, 0, 0, 0);
+    float sv[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) sv[v] = rv[v] >= 0 ? lg[v] * a.scale_log2 : -INFINITY;
+    if (cl < R) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int r = rbase + lrow * 4 + v;
+        if (r < rows) s_lg[r * R + cl] = sv[v];
+      }
+    }
+    const float mx = cross_row_max(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
+    if (__builtin_amdgcn_ballot_w64(mx > ml + kLazy)) {  // uniform, rare
+      const float mn = mx > ml + kLazy ? mx : ml;
+      const float f = __builtin_amdgcn_exp2f(ml - mn);
+      ml = mn;
+      ll *= f;
+      float fh[R];
+      bcast_r<R>(f, fh);
+#pragma unroll
+      for (int h = 0; h < R; ++h)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[h][e] *= fh[h];
+    }
+    float pv[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) pv[v] = __builtin_amdgcn_exp2f(sv[v] - ml);
+    ll += (pv[0] + pv[1]) + (pv[2] + pv[3]);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float ph[R];
+      bcast_r<R>(pv[u], ph);
+      const bool ok = rv[u] >= 0;
+      const u32x4 w = {ok ? vb[u].x : 0u, ok ? vb[u].y : 0u, ok ? vb[u].z : 0u, ok ? vb[u].w : 0u};
+      float x[EPL];
+      V::widen(w, x);
+#pragma unroll
+      for (int h = 0; h < R; ++h)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(ph[h], x[e], acc[h][e]);
+    }
+  };
   // one step in groups of UG rows per lane-row (fewer live scores)
-  auto step = [&](int rbase, const u32x4 (&kb)[U], const u32x4 (&vb)[U], const int (&rv)[U]) {
-    if constexpr (kOne) {
+  auto step = [&](int rbase, const u32x4 (&kb)[U], const u32x4 (&vb)[U], const int (&rv)[U + 1]) {
+    if constexpr (kMfma) {
+      stepm(rbase, kb, vb, rv);
+      return;
+    } else if constexpr (kOne) {
       step1(rbase, kb, vb, rv);
       return;
     }
@@ -655,7 +837,7 @@ __global__ __launch_bounds__(kUnitThreads) void decode_unit(DecodeArgs a) {
   // steps 4k .. 4k+3 form sub-chunk k and use buffers 0 .. 3; the K/V loads of the next three steps are in
   // flight while a step is computed
   static_assert(NB == 4, "the loop below is written for four buffers");
-  int r0[U], r1[U], r2[U], r3[U], vcur = -1, rbk = 0, rpk = 0, rbn = 0, rpn = 0;
+  int r0[U + 1], r1[U + 1], r2[U + 1], r3[U + 1], vcur = -1, rbk = 0, rpk = 0, rbn = 0, rpn = 0;
   u32x4 k0[U], v0[U], k1[U], v1[U], k2[U], v2[U], k3[U], v3[U];
   if (nst > 0) {
     res_issue(0, rbk, rpk);
@@ -705,7 +887,10 @@ __global__ __launch_bounds__(kUnitThreads) void decode_unit(DecodeArgs a) {
   }
   if (bad) raise(a.status, SE_DEV_INDEX);
 
-  if constexpr (kOne) {
+  if constexpr (kMfma) {
+    bcast_r<R>(ml, m);
+    bcast_r<R>(ll, l);
+  } else if constexpr (kOne) {
     float lsum = ll + dpp_f<kRowRor4>(ll);
     if constexpr (R == 4) lsum += dpp_f<kRowRor8>(lsum);
     m[0] = row16_bcast<0>(ml), l[0] = row16_bcast<0>(lsum);
