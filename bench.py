@@ -807,7 +807,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle time for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true",
-                    help="time host-launched steps only, with no captured HIP graph (for counter runs that count calls)")
+                    help="host-launched steps only: no captured HIP graph and no separate per-call pass (for profiler "
+                         "runs that count calls per step)")
     ap.add_argument("--calibrate-copy", type=int, metavar="MIB", help="run only a plain copy of MIB MiB, --steps times")
     ap.add_argument("--copy-ceiling", action="store_true",
                     help="time plain copies of 8 MiB to 1 GiB (--steps launches each) and exit")
@@ -905,7 +906,7 @@ def main():
                 e1.record()
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t_start
-    if wl.restore:
+    if wl.restore and not args.eager:
         # Per-call times: the restored steps again, each behind a device spin long enough that the host has queued
         # the whole step before the first call starts, so that the events around each call see only device time
         # (with small calls the device would otherwise wait for the host between them). A spin that ended before
