@@ -65,8 +65,8 @@ SE_DEV float cross_row_max(float x) {
 // sums of 16 values over the 16 lanes of a row, scattered: lane j of the row receives the total of value j.
 // Four exchange rounds (partners 15 - j, 7 - j within each half, j ^ 2, j ^ 1); each halves the values a lane
 // carries: 15 DPP additions instead of 16 full row sums.
-template <int N, int CTRL>
-SE_DEV void rs_round(float (&v)[16], bool hi) {
+template <int N, int CTRL, int M>
+SE_DEV void rs_round(float (&v)[M], bool hi) {
 #pragma unroll
   for (int i = 0; i < N / 2; ++i) {
     const float keep = hi ? v[N / 2 + i] : v[i];
@@ -81,6 +81,15 @@ SE_DEV float row16_reduce_scatter(float (&v)[16]) {
   rs_round<4, 0x4e>(v, j & 2);    // quad_perm [2,3,0,1]
   rs_round<2, 0xb1>(v, j & 1);    // quad_perm [1,0,3,2]
   return v[0];
+}
+// the same for 8 values: three rounds within each half-row leave lanes j and j ^ 8 with the sums over their halves
+// of value j % 8, and one rotation by 8 adds the halves
+SE_DEV float row16_reduce_scatter(float (&v)[8]) {
+  const int j = threadIdx.x & 15;
+  rs_round<8, 0x141>(v, j & 4);
+  rs_round<4, 0x4e>(v, j & 2);
+  rs_round<2, 0xb1>(v, j & 1);
+  return v[0] + dpp_f<kRowRor8>(v[0]);
 }
 // lane N of each row of 16 lanes, in every lane of the row (DPP row_newbcast)
 template <int N>

@@ -119,12 +119,22 @@ SE_DEV void merge_stats(const ScoreArgs &a, int unit, int rg, float *s_mlog) {
 }
 
 
-constexpr int kSub = 64;  // keys per step of a wave
+// A wave's step is KB 16-key tiles: KB = 2 where the chunk's keys come from HBM (one row group), 4 where several
+// row groups read the same keys and mostly hit the L2.
+#ifndef SE_STREAM_NSET
+#define SE_STREAM_NSET 2
+#endif
+constexpr int kNSet = SE_STREAM_NSET;  // register sets of keys per wave (kNSet - 1 steps in flight)
+static_assert(kNSet >= 2, "the fused kernel keeps two steps in registers");
 
-// The lazy running max of pass 1: a row's reference m only moves (and its sum is rescaled) when a logit exceeds it
-// by more than kLazy / c in log2 units; until then the terms are exp2 of at most kLazy, which fp32 sums hold
-// exactly enough.
+// Pass 1 first sums exp2(s c) with no reference subtracted. A row whose chunk sum lies in [2^-80, 2^80] has every
+// term finite, and the terms flushed to zero (each below 2^-126, at most 2^15 of them) are under 2^-31 of the sum,
+// so the sum is as exact as one taken against the row's maximum. A chunk with a row outside that band (or with a
+// non-finite sum) is streamed again with a lazy running max: a row's reference m only moves (and its sum is
+// rescaled) when a logit exceeds it by more than kLazy / c in log2 units; until then the terms are exp2 of at most
+// kLazy, which fp32 sums hold exactly enough.
 constexpr float kLazy = 8.f;
+constexpr float kPlainLo = 0x1p-80f, kPlainHi = 0x1p80f;
 
 // max of four values that are finite or -inf: two v_max3_f32, without the NaN-quieting copies fmaxf would add.
 // Only for VALU results: inline asm is outside the compiler's hazard checks, and an MFMA result needs wait states
@@ -140,22 +150,26 @@ SE_DEV float max4(float a, float b, float c, float d) {
 // S^T = K Q^T per 16x16 tile: A = 16 keys x 32 dims, held in registers, B = 32 dims x 16 query rows, read from LDS.
 // Lane l receives query row l%16 and keys 4*(l/16)..+4 of the tile. K-step t covers dims 32t..32t+32 (lane group
 // h = l/16 holds dims 32t + 8h..+8), so each key load instruction reads 64 contiguous bytes of 16 rows.
-// Each wave streams its own 64-key steps of the chunk straight from global memory (the next step's loads in flight
-// while the current one is computed): K never passes through LDS and no barrier separates the steps, so the waves
-// of a SIMD drift apart and one wave's MFMAs run while another does its softmax work.
+// Each wave streams its own steps of the chunk straight from global memory (the next step's loads in flight while
+// the current one is computed): K never passes through LDS and no barrier separates the steps, so the waves of a
+// SIMD drift apart and one wave's MFMAs run while another does its softmax work. Where the keys come from HBM,
+// steps of 32 keys (two tiles) rather than 64 keep the wave's loads in smaller, more frequent batches, which the
+// memory system serves with less queueing, for twice the query-fragment reads from LDS per MFMA.
 constexpr int kStreamRows = 256;
 constexpr int kStreamQB = kStreamRows / 16;  // 16-row query blocks
 
-// one 64-key step of a wave: the K fragments of its four 16-key tiles and, per tile, the position of the key this
-// lane loads (tile row l%16; -1: outside the chunk or not resident)
+// one step of a wave: the K fragments of its 16-key tiles and, per tile, the position of the key this lane loads
+// (tile row l%16; -1: outside the chunk or not resident)
+template <int KB>
 struct KStep {
-  bf16x8 f[4][4];  // [key tile][k-step]
-  int pos[4];
+  bf16x8 f[KB][4];  // [key tile][k-step]
+  int pos[KB];
 };
 
 // the block-table entries and positions of a step's keys (loaded a step before the keys themselves)
+template <int KB>
 struct KAddr {
-  int blk[4], pos[4], page[4];
+  int blk[KB], pos[KB], page[KB];
 };
 
 // every load is issued unconditionally (indices clamped into the chunk), so none waits behind a branch
@@ -165,26 +179,26 @@ SE_DEV int page_of(const ScoreArgs &a, int slot) {
   return POW2 ? slot >> a.page_shift : slot / a.page;
 }
 
-template <bool POW2>
-SE_DEV void kaddr_load(const ScoreArgs &a, int b, int g, int c0, int c1, int step, KAddr &ad) {
+template <bool POW2, int KB>
+SE_DEV void kaddr_load(const ScoreArgs &a, int b, int g, int c0, int c1, int step, KAddr<KB> &ad) {
   const int lane = threadIdx.x & 63;
   const int32_t *bt = a.bt + (int64_t)b * a.max_blocks;
   const int32_t *pos = a.pos + ((int64_t)b * a.n_kv + g) * a.max_blocks * a.page;
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
-    const int key = min(c0 + step * kSub + kb * 16 + (lane & 15), c1 - 1);
+  for (int kb = 0; kb < KB; ++kb) {
+    const int key = min(c0 + step * 16 * KB + kb * 16 + (lane & 15), c1 - 1);
     ad.page[kb] = page_of<POW2>(a, key);
     ad.blk[kb] = bt[ad.page[kb]];
     ad.pos[kb] = pos[key];
   }
 }
 
-template <bool POW2>
-SE_DEV void kstep_fetch(const ScoreArgs &a, int g, int c0, int c1, int step, const KAddr &ad, KStep &ks) {
+template <bool POW2, int KB>
+SE_DEV void kstep_fetch(const ScoreArgs &a, int g, int c0, int c1, int step, const KAddr<KB> &ad, KStep<KB> &ks) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
-    const int key = c0 + step * kSub + kb * 16 + (lane & 15);
+  for (int kb = 0; kb < KB; ++kb) {
+    const int key = c0 + step * 16 * KB + kb * 16 + (lane & 15);
     const bool ok = (key < c1) & (ad.pos[kb] >= 0) & ((unsigned)ad.blk[kb] < (unsigned)a.num_blocks);
     const int keep = -(int)ok;  // all ones or zero: arithmetic instead of a select the compiler may branch on
     const int off = POW2 ? (key & (a.page - 1)) : key - ad.page[kb] * a.page;
@@ -207,34 +221,36 @@ SE_DEV bf16x8 q_frag(const char *s_q, int qb, int t) {
 
 // PRIO: the MFMAs are issued at raised wave priority, so that the other wave of the SIMD, in its softmax work, takes
 // the issue slots between them (pass 1, which holds its row statistics in registers, has no room for the change)
-template <bool PRIO = false>
-SE_DEV void stile(const KStep &ks, const char *s_q, int qb, floatx4 (&acc)[4]) {
+template <bool PRIO = false, int KB>
+SE_DEV void stile(const KStep<KB> &ks, const char *s_q, int qb, floatx4 (&acc)[KB]) {
   bf16x8 qf[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) qf[t] = q_frag(s_q, qb, t);
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb) acc[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int kb = 0; kb < KB; ++kb) acc[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
   if (PRIO) __builtin_amdgcn_s_setprio(2);
 #pragma unroll
   for (int t = 0; t < 4; ++t)
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) acc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ks.f[kb][t], qf[t], acc[kb], 0, 0, 0);
+    for (int kb = 0; kb < KB; ++kb) acc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ks.f[kb][t], qf[t], acc[kb], 0, 0, 0);
   if (PRIO) __builtin_amdgcn_s_setprio(0);
 }
 
 // max of 16 values that are VALU results (never MFMA results: the asm is outside the compiler's hazard checks,
 // and an MFMA result needs wait states before a VALU instruction may read it)
-SE_DEV float max16(const float (&x)[16]) {
+SE_DEV float maxv(const float (&x)[16]) {
   return fmaxf(fmaxf(max4(x[0], x[1], x[2], x[3]), max4(x[4], x[5], x[6], x[7])),
                fmaxf(max4(x[8], x[9], x[10], x[11]), max4(x[12], x[13], x[14], x[15])));
 }
+SE_DEV float maxv(const float (&x)[8]) { return fmaxf(max4(x[0], x[1], x[2], x[3]), max4(x[4], x[5], x[6], x[7])); }
 
 // keys of the lane's outputs that its query row may not see become -inf (the row's limit and the keys' positions
-// come from LDS: s_kp holds the positions of the wave's 64 keys of this step)
-SE_DEV void stream_mask(const int *s_kp, int lim, floatx4 (&acc)[4]) {
+// come from LDS: s_kp holds the positions of the wave's keys of this step)
+template <int KB>
+SE_DEV void stream_mask(const int *s_kp, int lim, floatx4 (&acc)[KB]) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb)
+  for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int p = s_kp[kb * 16 + (lane >> 4) * 4 + v];
@@ -245,9 +261,10 @@ SE_DEV void stream_mask(const int *s_kp, int lim, floatx4 (&acc)[4]) {
 // PASS 1: row statistics of the chunk; PASS 2: column sums with the merged statistics. PASS 3 (a unit's whole key
 // range in one chunk of at most two steps per wave): both, in one workgroup, with the keys kept in registers and
 // the row statistics merged in LDS.
-template <int PASS, int NW, bool POW2>
+template <int PASS, int NW, bool POW2, int KB>
 __global__ __launch_bounds__(NW * 64, 2) void window_stream(ScoreArgs a) {
   constexpr int NT = NW * 64;
+  constexpr int kKB = KB, kSub = 16 * KB;  // tiles and keys per step of a wave
   int chunk, rg, unit;
   xcd_item(chunk, rg, unit);
   const int b = unit / a.n_kv, g = unit % a.n_kv;
@@ -267,18 +284,32 @@ __global__ __launch_bounds__(NW * 64, 2) void window_stream(ScoreArgs a) {
   const int rows = min(kStreamRows, a.R * a.wq - rg * kStreamRows);
 
   // the wave's first step, and the addresses of its second, are in flight while the query rows are staged
-  KStep ka, kb2;
-  KAddr ad;
+  // kNSet register sets of keys (step j in ks[j % kNSet], its addresses in ad[j % kNSet]): the keys of the next
+  // kNSet - 1 steps are in flight while a step is computed
+  KStep<KB> ks[kNSet];
+  KAddr<KB> ad[kNSet];
   int s = __builtin_amdgcn_readfirstlane(wave);
-  // Pass 2 walks the chunk's steps last to first: the keys pass 1 read last are the likeliest still to be in the
-  // last-level cache. ph maps a wave's step order to the step it scores.
-  auto ph = [&](int x) { return PASS == 2 ? nsub - 1 - x : x; };
-  if (s < nsub) {
-    kaddr_load<POW2>(a, b, g, c0, c1, ph(s), ad);
-    kstep_fetch<POW2>(a, g, c0, c1, ph(s), ad, ka);
-    kaddr_load<POW2>(a, b, g, c0, c1, ph(min(s + NW, nsub - 1)), ad);
-    if (PASS == 3) kstep_fetch<POW2>(a, g, c0, c1, min(s + NW, nsub - 1), ad, kb2);
-  }
+  // ph maps a wave's step order to the step it scores. Each workgroup starts its walk at its own step (rot), so
+  // that the concurrent workgroups, whose chunks sit at large power-of-two strides in the pool, read from different
+  // memory banks at any moment. Pass 2 walks the same ring backwards from there: the keys pass 1 read last are the
+  // likeliest still to be in the last-level cache. The fused kernel (PASS 3) walks in order.
+  const int rot = PASS != 3 && nsub > 0 ? (unit * 7 + chunk * 5 + rg * 3) % nsub : 0;
+  auto ph = [&](int x) {
+    const int y = PASS == 2 ? rot - 1 - x : rot + x;
+    return y < 0 ? y + nsub : (y >= nsub ? y - nsub : y);
+  };
+  auto prime = [&]() __attribute__((always_inline)) {
+    if (s < nsub) {
+#pragma unroll
+      for (int p = 0; p < kNSet - 1; ++p) {
+        kaddr_load<POW2>(a, b, g, c0, c1, ph(min(s + p * NW, nsub - 1)), ad[p]);
+        kstep_fetch<POW2>(a, g, c0, c1, ph(min(s + p * NW, nsub - 1)), ad[p], ks[p]);
+      }
+      kaddr_load<POW2>(a, b, g, c0, c1, ph(min(s + (kNSet - 1) * NW, nsub - 1)), ad[kNSet - 1]);
+      if (PASS == 3 && kNSet == 2) kstep_fetch<POW2>(a, g, c0, c1, min(s + NW, nsub - 1), ad[1], ks[1]);
+    }
+  };
+  prime();
 
   if (threadIdx.x == 0) s_limmin = 0x7fffffff;
   const char *qbase = a.q + (((int64_t)b * a.n_kv + g) * a.R * a.wq + (int64_t)rg * kStreamRows) * 256;
@@ -308,9 +339,9 @@ __global__ __launch_bounds__(NW * 64, 2) void window_stream(ScoreArgs a) {
   const int nqb = (rows + 15) / 16;
   const float c = a.scale_log2;
 
-  // pass 1: per query block, the lane's running sum of exp2(s c - m c) over its keys, and -m c. The reference m
-  // starts at the first visible logit and afterwards only moves up, when a logit exceeds it by more than kLazy / c
-  // (the terms stay below 2^kLazy meanwhile, which fp32 sums hold exactly enough).
+  // pass 1: per query block, the lane's running sum of exp2(s c - m c) over its keys, and -m c (0 on the first,
+  // reference-free stream). On the lazy stream the reference m starts at the first visible logit and afterwards
+  // only moves up, when a logit exceeds it by more than kLazy / c.
   float st_l[kStreamQB], st_nmc[kStreamQB];
   // pass 2: per query block, the merged statistic of the lane's row (+inf: no such row)
   float ml[kStreamQB];
@@ -325,35 +356,36 @@ __global__ __launch_bounds__(NW * 64, 2) void window_stream(ScoreArgs a) {
     }
   }
 
-  auto step = [&](const KStep &ks, int sidx, auto pass_tag) {
+  auto step = [&](const KStep<KB> &ks, int sidx, auto pass_tag) __attribute__((always_inline)) {
     constexpr int P = decltype(pass_tag)::value;
-    int pmin = min(min(ks.pos[0], ks.pos[1]), min(ks.pos[2], ks.pos[3]));
-    int pmax = max(max(ks.pos[0], ks.pos[1]), max(ks.pos[2], ks.pos[3]));
+    int pmin = ks.pos[0], pmax = ks.pos[0];
+#pragma unroll
+    for (int kb = 1; kb < kKB; ++kb) pmin = min(pmin, ks.pos[kb]), pmax = max(pmax, ks.pos[kb]);
     const bool fast = __builtin_amdgcn_ballot_w64(!(pmin >= 0 && pmax <= limmin)) == 0;
     if (!fast) {
       if (lane < 16) {
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) s_kp[wave][kb * 16 + lane] = ks.pos[kb];
+        for (int kb = 0; kb < kKB; ++kb) s_kp[wave][kb * 16 + lane] = ks.pos[kb];
       }
       // LDS accesses of a wave complete in order; this keeps the compiler from moving the reads above the writes
       asm volatile("" ::: "memory");
     }
-    float col[16];
+    float col[4 * kKB];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) col[i] = 0.f;
+    for (int i = 0; i < 4 * kKB; ++i) col[i] = 0.f;
 #pragma unroll
     for (int qb = 0; qb < kStreamQB; ++qb) {
       if (qb < nqb) {  // uniform
-        floatx4 acc[4];
+        floatx4 acc[kKB];
         stile<P == 2>(ks, s_q, qb, acc);
         if (!fast) stream_mask(s_kp[wave], s_lim[qb * 16 + (lane & 15)], acc);
         if constexpr (P == 1) {
-          float t[16];  // s c - m c against the current reference
+          float t[4 * kKB];  // s c - m c against the current reference
 #pragma unroll
-          for (int kb = 0; kb < 4; ++kb)
+          for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
             for (int v = 0; v < 4; ++v) t[kb * 4 + v] = fmaf(acc[kb][v], c, st_nmc[qb]);
-          const float tm = max16(t);
+          const float tm = maxv(t);
           const bool first = st_l[qb] == 0.f;  // nothing visible yet: the reference is not set
           const bool mv = (tm > kLazy) | (first & (tm > -INFINITY));
           if (__builtin_amdgcn_ballot_w64(mv)) {
@@ -361,26 +393,34 @@ __global__ __launch_bounds__(NW * 64, 2) void window_stream(ScoreArgs a) {
               st_l[qb] = first ? 0.f : st_l[qb] * __builtin_amdgcn_exp2f(-tm);
               st_nmc[qb] -= tm;
 #pragma unroll
-              for (int i = 0; i < 16; ++i) t[i] -= tm;
+              for (int i = 0; i < 4 * kKB; ++i) t[i] -= tm;
             }
           }
           float sum = 0.f;
 #pragma unroll
-          for (int i = 0; i < 16; ++i) sum += __builtin_amdgcn_exp2f(t[i]);
+          for (int i = 0; i < 4 * kKB; ++i) sum += __builtin_amdgcn_exp2f(t[i]);
+          st_l[qb] += sum;
+        } else if constexpr (P == 4) {  // pass 1, reference-free: masked logits are -inf and add 0
+          float sum = 0.f;
+#pragma unroll
+          for (int kb = 0; kb < kKB; ++kb)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) sum += __builtin_amdgcn_exp2f(acc[kb][v] * c);
           st_l[qb] += sum;
         } else {
 #pragma unroll
-          for (int kb = 0; kb < 4; ++kb)
+          for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
             for (int v = 0; v < 4; ++v) col[kb * 4 + v] += __builtin_amdgcn_exp2f(fmaf(acc[kb][v], c, -ml[qb]));
         }
       }
     }
     if constexpr (P == 2) {
+      // lane j of a row ends with the total of value j % (4 kKB): key tile m / 4, output m % 4 of its lane group
       const float tot = row16_reduce_scatter(col);
-      const int j = lane & 15;
-      const int key = sidx * kSub + (j >> 2) * 16 + (lane >> 4) * 4 + (j & 3);
-      if (c0 + key < c1) {
+      const int j = lane & 15, m = j & (4 * kKB - 1);
+      const int key = sidx * kSub + (m >> 2) * 16 + (lane >> 4) * 4 + (m & 3);
+      if (j < 4 * kKB && c0 + key < c1) {
         const int idx = c0 + key - k0;
         if (a.nrg == 1) put_score(a, (int64_t)unit * a.score_stride + idx, tot);
         else a.colpart[((int64_t)unit * a.nrg + rg) * a.key_span + idx] = tot;
@@ -388,16 +428,12 @@ __global__ __launch_bounds__(NW * 64, 2) void window_stream(ScoreArgs a) {
     }
   };
 
-  // Two register sets: while a step is computed, the next one's keys load into the other set and the addresses
-  // of the one after are loaded (the wait for those addresses, a step later, also covers the keys in flight).
-  // The loads are unconditional: past the wave's last step they fetch that step again, unused, so that no path
-  // through the loop skips a wait (the compiler's wait counts would otherwise hold the MFMAs for the prefetch).
   using P1 = std::integral_constant<int, 1>;
   using P2 = std::integral_constant<int, 2>;
   if constexpr (PASS == 3) {
     // both passes over the wave's (at most two) steps, which stay in registers
-    if (s < nsub) step(ka, s, P1{});
-    if (s + NW < nsub) step(kb2, s + NW, P1{});
+    if (s < nsub) step(ks[0], s, P1{});
+    if (s + NW < nsub) step(ks[1], s + NW, P1{});
 #pragma unroll
     for (int qb = 0; qb < kStreamQB; ++qb) {
       const float mc = st_l[qb] > 0.f ? -st_nmc[qb] : -1e30f;  // this lane's m c (none: no visible key)
@@ -419,46 +455,91 @@ __global__ __launch_bounds__(NW * 64, 2) void window_stream(ScoreArgs a) {
     __syncthreads();
 #pragma unroll
     for (int qb = 0; qb < kStreamQB; ++qb) ml[qb] = s_ml3[qb * 16 + (lane & 15)];
-    if (s < nsub) step(ka, s, P2{});
-    if (s + NW < nsub) step(kb2, s + NW, P2{});
+    if (s < nsub) step(ks[0], s, P2{});
+    if (s + NW < nsub) step(ks[1], s + NW, P2{});
     return;
   }
   const int last = nsub - 1;
-  while (s < nsub) {
-    kstep_fetch<POW2>(a, g, c0, c1, ph(min(s + NW, last)), ad, kb2);
-    kaddr_load<POW2>(a, b, g, c0, c1, ph(min(s + 2 * NW, last)), ad);
-    step(ka, ph(s), std::integral_constant<int, PASS>{});
-    s += NW;
-    if (s >= nsub) break;
-    kstep_fetch<POW2>(a, g, c0, c1, ph(min(s + NW, last)), ad, ka);
-    kaddr_load<POW2>(a, b, g, c0, c1, ph(min(s + 2 * NW, last)), ad);
-    step(kb2, ph(s), std::integral_constant<int, PASS>{});
-    s += NW;
-  }
+  // Step j of the wave: first the addresses of step j + kNSet, then the keys of step j + kNSet - 1 (whose addresses
+  // came an iteration earlier, ahead of that iteration's keys, so waiting for them leaves the newer keys in flight),
+  // then step j itself. The loads are unconditional: past the wave's last step they fetch that step again, unused,
+  // so that no path through the loop skips a wait.
+  auto stream = [&](auto pass_tag) __attribute__((always_inline)) {
+    while (s < nsub) {
+#pragma unroll
+      for (int p = 0; p < kNSet; ++p) {
+        kaddr_load<POW2>(a, b, g, c0, c1, ph(min(s + kNSet * NW, last)), ad[p]);
+        kstep_fetch<POW2>(a, g, c0, c1, ph(min(s + (kNSet - 1) * NW, last)), ad[(p + kNSet - 1) % kNSet],
+                          ks[(p + kNSet - 1) % kNSet]);
+        step(ks[p], ph(s), pass_tag);
+        s += NW;
+        if (s >= nsub) break;
+      }
+    }
+  };
 
   if constexpr (PASS == 1) {
     // combine the four lanes of each row, then the waves, and write the chunk's (max, sum) per row (log2 domain)
-    __syncthreads();  // every wave is done with s_q: it holds the per-wave row statistics from here on
-    float2 *s_st = reinterpret_cast<float2 *>(s_q);  // [NW][kStreamRows]
+    float2 *s_st = reinterpret_cast<float2 *>(s_q);  // [NW][kStreamRows], once every wave is done with s_q
+    __shared__ int s_redo;
+    auto merge_out = [&](bool plain) __attribute__((always_inline)) {
+      __syncthreads();  // every wave is done with s_q (and has read s_redo)
+      if (threadIdx.x == 0) s_redo = 0;
 #pragma unroll
-    for (int qb = 0; qb < kStreamQB; ++qb) {
-      const float mc = st_l[qb] > 0.f ? -st_nmc[qb] : -1e30f;  // this lane's m c (none: no visible key)
-      const float mr = cross_row_max(mc);
-      const float lr = cross_row_sum(st_l[qb] * __builtin_amdgcn_exp2f(mc - mr));
-      if (lane < 16) s_st[wave * kStreamRows + qb * 16 + lane] = make_float2(mr, lr);
+      for (int qb = 0; qb < kStreamQB; ++qb) {
+        float mr, lr;
+        if (plain) {
+          mr = 0.f;
+          lr = cross_row_sum(st_l[qb]);
+        } else {
+          const float mc = st_l[qb] > 0.f ? -st_nmc[qb] : -1e30f;  // this lane's m c (none: no visible key)
+          mr = cross_row_max(mc);
+          lr = cross_row_sum(st_l[qb] * __builtin_amdgcn_exp2f(mc - mr));
+        }
+        if (lane < 16) s_st[wave * kStreamRows + qb * 16 + lane] = make_float2(mr, lr);
+      }
+      __syncthreads();
+      float *out = a.stats + ((((int64_t)unit * a.nrg + rg) * a.nkc + chunk) * a.rpg) * 2;
+      bool bad = false;
+      for (int r = threadIdx.x; r < kStreamRows; r += NT) {
+        float mm = -1e30f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) mm = fmaxf(mm, s_st[w * kStreamRows + r].x);
+        float ll = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) ll += s_st[w * kStreamRows + r].y * __builtin_amdgcn_exp2f(s_st[w * kStreamRows + r].x - mm);
+        out[r * 2] = mm;
+        out[r * 2 + 1] = ll;
+        bad |= plain && r < rows && !(ll >= kPlainLo && ll <= kPlainHi);
+      }
+      if (bad) s_redo = 1;
+      __syncthreads();
+      return s_redo != 0;
+    };
+    stream(std::integral_constant<int, 4>{});
+    if (merge_out(true)) {  // uniform, rare: a row sum outside the band; the chunk again, exactly
+#pragma unroll
+      for (int qb = 0; qb < kStreamQB; ++qb) st_l[qb] = 0.f, st_nmc[qb] = 0.f;
+      // the queries again (s_q held the statistics), and the wave's first step and the addresses of its second
+      __syncthreads();
+      int tid = threadIdx.x;
+      asm volatile("" : "+v"(tid));  // the addresses are computed again, not kept alive through the first stream
+#pragma unroll
+      for (int j = 0; j < kPieces; ++j) {
+        const int i = tid + j * NT, r = i >> 4, p = i & 15;
+        const bool in = r < rows;
+        const u32x4 v0 = ld16(qbase + (int64_t)(in ? i : (i & 15)) * 16);
+        const u32x4 v = {in ? v0.x : 0u, in ? v0.y : 0u, in ? v0.z : 0u, in ? v0.w : 0u};
+        *reinterpret_cast<u32x4 *>(s_q + r * 256 + ((p ^ (r & 15)) << 4)) = v;
+      }
+      s = __builtin_amdgcn_readfirstlane(wave);
+      prime();
+      __syncthreads();
+      stream(std::integral_constant<int, 1>{});
+      merge_out(false);
     }
-    __syncthreads();
-    float *out = a.stats + ((((int64_t)unit * a.nrg + rg) * a.nkc + chunk) * a.rpg) * 2;
-    for (int r = threadIdx.x; r < kStreamRows; r += NT) {
-      float mm = -1e30f;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) mm = fmaxf(mm, s_st[w * kStreamRows + r].x);
-      float ll = 0.f;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) ll += s_st[w * kStreamRows + r].y * __builtin_amdgcn_exp2f(s_st[w * kStreamRows + r].x - mm);
-      out[r * 2] = mm;
-      out[r * 2 + 1] = ll;
-    }
+  } else {
+    stream(std::integral_constant<int, PASS>{});
   }
 }
 
@@ -817,6 +898,7 @@ __global__ __launch_bounds__(kBidirNW * 64, bidir_wgs_per_cu<KT>()) void window_
 #endif
 constexpr int kStreamNW = SE_STREAM_NW;
 constexpr int kStreamWGs = SE_STREAM_WGS;  // workgroups a launch aims for (two per CU at NW = 4)
+constexpr int kFusedKeys = 2 * 64 * kStreamNW;  // key ranges the single-kernel path takes (two 64-key steps per wave)
 
 // ---- VALU path (fp32 inputs, or any d that fits) ---------------------------------------------------------------
 template <int DTYPE, int D>
@@ -913,10 +995,15 @@ __global__ void colsum_reduce(ScoreArgs a) {
   }
 }
 
+template <int PASS, int KB>
+void launch_stream_kb(const ScoreArgs &a, dim3 grid, hipStream_t st) {
+  if (a.page_shift >= 0) hipLaunchKernelGGL((window_stream<PASS, kStreamNW, true, KB>), grid, dim3(kStreamNW * 64), 0, st, a);
+  else hipLaunchKernelGGL((window_stream<PASS, kStreamNW, false, KB>), grid, dim3(kStreamNW * 64), 0, st, a);
+}
 template <int PASS>
-void launch_stream(const ScoreArgs &a, dim3 grid, hipStream_t st) {
-  if (a.page_shift >= 0) hipLaunchKernelGGL((window_stream<PASS, kStreamNW, true>), grid, dim3(kStreamNW * 64), 0, st, a);
-  else hipLaunchKernelGGL((window_stream<PASS, kStreamNW, false>), grid, dim3(kStreamNW * 64), 0, st, a);
+void launch_stream(const ScoreArgs &a, dim3 grid, int kb, hipStream_t st) {
+  if (kb == 2) launch_stream_kb<PASS, 2>(a, grid, st);
+  else launch_stream_kb<PASS, 4>(a, grid, st);
 }
 
 template <int KT>
@@ -945,6 +1032,7 @@ constexpr int kBidirWGs = SE_BIDIR_WGS;  // workgroups a launch aims for (two pe
 
 struct Plan {
   int nrg, nkc, kc, key_span, rpg, nw;  // nw: waves per MFMA workgroup (0: fp32 VALU path, -1: streaming)
+  int kb;                               // streaming: 16-key tiles per step of a wave (2 or 4)
   int bidir_kt;                         // > 0: the register-resident bidirectional kernel, key tiles per wave
   size_t stats_bytes, col_bytes;
 };
@@ -985,13 +1073,17 @@ Plan make_plan(const se_cache_t *c, const se_window_params_t *p) {
   const int max_slots = c->max_blocks * c->page;
   pl.key_span = p->mode == SE_SCORE_CAUSAL ? max_slots : p->window - p->protect;
   const int span64 = (pl.key_span + 63) / 64 * 64;
-  if (pl.nw < 0) {
-    // chunks of whole rounds of 64-key steps (one per wave) that give about kStreamWGs workgroups; a key range of
-    // at most two steps per wave stays one chunk (the single-kernel path)
+  pl.kb = 4;
+  if (pl.nw < 0 && pl.key_span <= kFusedKeys) {
+    // at most two 64-key steps per wave: one chunk, both passes in one kernel
+    pl.kc = (pl.key_span + 64 * kStreamNW - 1) / (64 * kStreamNW) * (64 * kStreamNW);
+  } else if (pl.nw < 0) {
+    // chunks of whole rounds of steps (one per wave) that give about kStreamWGs workgroups
+    pl.kb = pl.nrg == 1 ? 2 : 4;
     const long long groups = (long long)c->B * c->n_kv * pl.nrg;
     const long long per = (kStreamWGs + groups - 1) / groups;
-    const int round = kSub * kStreamNW;
-    long long kc = pl.key_span <= 2 * round ? pl.key_span : (pl.key_span + per - 1) / per;
+    const int round = 16 * pl.kb * kStreamNW;
+    long long kc = (pl.key_span + per - 1) / per;
     kc = (kc + round - 1) / round * round;
     pl.kc = (int)(kc < round ? round : (kc > 16384 ? 16384 : kc));
   } else {
@@ -1071,11 +1163,11 @@ extern "C" int32_t se_window_score(const se_cache_t *c, const void *q_win, const
   hipStream_t st = (hipStream_t)stream;
   if (pl.bidir_kt > 0) {
     se::launch_bidir(pl.bidir_kt, a, grid, st);
-  } else if (pl.nw < 0 && pl.nkc == 1 && (pl.key_span + se::kSub - 1) / se::kSub <= 2 * se::kStreamNW) {
-    se::launch_stream<3>(a, grid, st);
+  } else if (pl.nw < 0 && pl.key_span <= se::kFusedKeys) {
+    se::launch_stream_kb<3, 4>(a, grid, st);
   } else if (pl.nw < 0) {
-    se::launch_stream<1>(a, grid, st);
-    se::launch_stream<2>(a, grid, st);
+    se::launch_stream<1>(a, grid, pl.kb, st);
+    se::launch_stream<2>(a, grid, pl.kb, st);
   } else {
     hipLaunchKernelGGL((se::stats_valu<SE_DTYPE_F32, 64>), grid, dim3(se::kValuRows), 0, st, a);
     hipLaunchKernelGGL((se::colsum_valu<SE_DTYPE_F32, 64>), grid, dim3(se::kValuRows), 0, st, a);

@@ -168,6 +168,42 @@ def test_window_score_causal_bf16(N, page):
     np.testing.assert_allclose(got.sum(axis=2), 256.0, rtol=1e-5)
 
 
+@pytest.mark.parametrize("case,wq", [("overflow", 64), ("underflow", 64), ("overflow", 128), ("underflow", 128)])
+def test_window_score_causal_extreme_logits(case, wq):
+    """Logits whose row sums of exp2(s c) leave [2^-80, 2^80]: the reference-free first pass must hand those chunks
+    to the exact (running-max) pass. "overflow": the first 600 slots' keys scaled by 30, so only the chunks that
+    hold them overflow (the others stay reference-free); "underflow": every key shifted along one direction and the
+    queries against it, so every logit is near -900 and every row sum near 2^-104. wq = 128 gives two row groups
+    (the other step width of the streaming kernels)."""
+    banner(f"window causal bf16 extreme logits: {case} wq={wq}")
+    inp = snap_inputs(N=1500, wq=wq)
+    st = inp["cache"].copy()
+    k = W.bf16_bits_to_f32(st.k_pool).reshape(st.k_pool.shape).astype(np.float64)
+    q = W.bf16_bits_to_f32(inp["q_win"]).reshape(inp["q_win"].shape).astype(np.float64)
+    if case == "overflow":
+        page = st.page
+        for b in range(2):
+            for slot in range(600):
+                k[st.block_table[b, slot // page], :, slot % page, :] *= 30.0
+    else:
+        u = np.random.default_rng(11).standard_normal(128)
+        u /= np.linalg.norm(u)
+        k += 30.0 * u
+        q -= 30.0 * u
+    st.k_pool = W.to_storage(k, "bf16").reshape(st.k_pool.shape)
+    q_win = W.to_storage(q, "bf16").reshape(inp["q_win"].shape)
+    ref = oracle.window_score_causal(st, q_win, inp["q_pos"], inp["scale"])
+    dc = to_device(st, 8)
+    S = st.pos_map.shape[2]
+    scores = torch.zeros((2, 2, S), dtype=torch.float32, device=DEV)
+    se.se_window_score(dc, storage_tensor(q_win, "bf16"), i32(inp["q_pos"]), scores, scale=inp["scale"],
+                       mode=se.SE_SCORE_CAUSAL, n_query=wq)
+    got = scores.cpu().numpy()
+    assert np.isfinite(got).all()
+    assert_scores_close(got[:, :, :1500], ref[:, :, :1500], mass=np.full((2, 2), 4.0 * wq))
+    np.testing.assert_allclose(got.sum(axis=2), 4.0 * wq, rtol=1e-5)
+
+
 def test_window_score_causal_f32_c0():
     banner("window causal f32 (tiny workload, full size)")
     inp = W.gen_snapkv(W.C0, seed=0, threads=1)
