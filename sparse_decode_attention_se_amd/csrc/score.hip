@@ -222,10 +222,7 @@ SE_DEV bf16x8 q_frag(const char *s_q, int qb, int t) {
 // PRIO: the MFMAs are issued at raised wave priority, so that the other wave of the SIMD, in its softmax work, takes
 // the issue slots between them (pass 1, which holds its row statistics in registers, has no room for the change)
 template <bool PRIO = false, int KB>
-SE_DEV void stile(const KStep<KB> &ks, const char *s_q, int qb, floatx4 (&acc)[KB]) {
-  bf16x8 qf[4];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) qf[t] = q_frag(s_q, qb, t);
+SE_DEV void stile(const KStep<KB> &ks, const bf16x8 (&qf)[4], floatx4 (&acc)[KB]) {
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) acc[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
   if (PRIO) __builtin_amdgcn_s_setprio(2);
@@ -373,11 +370,26 @@ __global__ __launch_bounds__(NW * 64, 2) void window_stream(ScoreArgs a) {
     float col[4 * kKB];
 #pragma unroll
     for (int i = 0; i < 4 * kKB; ++i) col[i] = 0.f;
+    // Outside the (rare) lazy-reference stream, the query fragments of block qb + 1 are read from LDS while block
+    // qb's softmax work runs.
+    constexpr bool kAhead = P != 1;
+    bf16x8 qn[4];
+    if (kAhead) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) qn[t] = q_frag(s_q, 0, t);
+    }
 #pragma unroll
     for (int qb = 0; qb < kStreamQB; ++qb) {
       if (qb < nqb) {  // uniform
         floatx4 acc[kKB];
-        stile<P == 2>(ks, s_q, qb, acc);
+        bf16x8 qf[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) qf[t] = kAhead ? qn[t] : q_frag(s_q, qb, t);
+        stile<P == 2>(ks, qf, acc);
+        if (kAhead && qb + 1 < kStreamQB) {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) qn[t] = q_frag(s_q, qb + 1, t);
+        }
         if (!fast) stream_mask(s_kp[wave], s_lim[qb * 16 + (lane & 15)], acc);
         if constexpr (P == 1) {
           float t[4 * kKB];  // s c - m c against the current reference
