@@ -23,6 +23,17 @@ struct alignas(16) u32x4 {
   uint32_t x, y, z, w;
 };
 SE_DEV u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
+// a 16-byte load marked non-temporal, for data read once (streamed K and V rows): it does not displace what the
+// caches hold for later reads (partial results, maps, query rows)
+typedef unsigned int u32v4 __attribute__((ext_vector_type(4)));
+SE_DEV u32x4 ld16_stream(const void *p) {
+  return __builtin_bit_cast(u32x4, __builtin_nontemporal_load(reinterpret_cast<const u32v4 *>(p)));
+}
+// a 16-byte store marked non-temporal, for K and V rows written into the pools: they go to memory without being
+// kept in the caches, where the next kernel's streaming reads would otherwise meet them
+SE_DEV void st16_stream(void *p, const u32x4 &v) {
+  __builtin_nontemporal_store(__builtin_bit_cast(u32v4, v), reinterpret_cast<u32v4 *>(p));
+}
 SE_DEV void st16(void *p, const u32x4 &v) { *reinterpret_cast<u32x4 *>(p) = v; }
 
 // ---- wave reductions ------------------------------------------------------------------------------------------

@@ -127,8 +127,8 @@ SE_DEV void move_tile(const GatherArgs &a, int unit, const Tile &t, int nrows) {
     if (x >= total) continue;
     const int64_t so = t.soff[x / cpr];
     if (so < 0) continue;
-    kbuf[i] = ld16(a.k + so + (x % cpr) * 16);
-    vbuf[i] = ld16(a.v + so + (x % cpr) * 16);
+    kbuf[i] = ld16_stream(a.k + so + (x % cpr) * 16);
+    vbuf[i] = ld16_stream(a.v + so + (x % cpr) * 16);
   }
   if (ORDERED) __syncthreads();
   const int64_t base = (int64_t)unit * a.max_blocks * a.page;
@@ -139,8 +139,8 @@ SE_DEV void move_tile(const GatherArgs &a, int unit, const Tile &t, int nrows) {
     const int r = x / cpr, ch = x % cpr;
     const int64_t so = t.soff[r], dof = t.doff[r];
     if (so < 0) continue;
-    st16(a.k + dof + ch * 16, kbuf[i]);
-    st16(a.v + dof + ch * 16, vbuf[i]);
+    st16_stream(a.k + dof + ch * 16, kbuf[i]);
+    st16_stream(a.v + dof + ch * 16, vbuf[i]);
     if (ch == 0) {
       a.pos[base + t.dslot[r]] = t.pval[r];
       if (a.cum) a.cum[base + t.dslot[r]] = t.cval[r];
@@ -325,8 +325,8 @@ __global__ __launch_bounds__(kSmallThreads) void gather_small(GatherArgs a) {
     if (x >= total) continue;
     const int64_t so = s_soff[x / cpr];
     if (so < 0) continue;
-    kb[i] = ld16(a.k + so + (x % cpr) * 16);
-    vb[i] = ld16(a.v + so + (x % cpr) * 16);
+    kb[i] = ld16_stream(a.k + so + (x % cpr) * 16);
+    vb[i] = ld16_stream(a.v + so + (x % cpr) * 16);
   }
   __syncthreads();  // every source row of the unit is read before any destination row is written
 #pragma unroll
@@ -335,8 +335,8 @@ __global__ __launch_bounds__(kSmallThreads) void gather_small(GatherArgs a) {
     if (x >= total) continue;
     const int r = x / cpr, ch = x % cpr;
     if (s_soff[r] < 0) continue;
-    st16(a.k + s_doff[r] + ch * 16, kb[i]);
-    st16(a.v + s_doff[r] + ch * 16, vb[i]);
+    st16_stream(a.k + s_doff[r] + ch * 16, kb[i]);
+    st16_stream(a.v + s_doff[r] + ch * 16, vb[i]);
   }
   if (threadIdx.x < cnt) {
     a.pos[base + w0 + threadIdx.x] = s_pval[threadIdx.x];
@@ -676,9 +676,9 @@ __global__ __launch_bounds__(kCopyThreads) void append_copy(AppendArgs a) {
   const int row = a.dst_row[unit];
   if (row < 0) return;
   const int64_t src = (int64_t)unit * a.row_bytes + ch * 16, dst = (int64_t)row * a.row_bytes + ch * 16;
-  const u32x4 kr = ld16(a.k_new + src), vr = ld16(a.v_new + src);
-  st16(a.k + dst, kr);
-  st16(a.v + dst, vr);
+  const u32x4 kr = ld16_stream(a.k_new + src), vr = ld16_stream(a.v_new + src);
+  st16_stream(a.k + dst, kr);
+  st16_stream(a.v + dst, vr);
 }
 
 // ---- chunk append: T tokens per unit at the high-water slots -------------------------------------------------------
@@ -811,9 +811,9 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_write(ChunkArgs a) {
   const int blk = bt[slot / a.page];
   const int64_t src = ((int64_t)unit * a.T + t) * a.row_bytes + ch * 16;
   const int64_t dst = (((int64_t)blk * a.n_kv + g) * a.page + slot % a.page) * a.row_bytes + ch * 16;
-  const u32x4 kr = ld16(a.k_new + src), vr = ld16(a.v_new + src);
-  st16(a.k + dst, kr);
-  st16(a.v + dst, vr);
+  const u32x4 kr = ld16_stream(a.k_new + src), vr = ld16_stream(a.v_new + src);
+  st16_stream(a.k + dst, kr);
+  st16_stream(a.v + dst, vr);
   if (ch == 0) {
     a.pos[(int64_t)unit * cap + slot] = a.pos0[b] + t;
     if (a.cum) a.cum[(int64_t)unit * cap + slot] = 0.f;
