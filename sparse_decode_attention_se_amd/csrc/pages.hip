@@ -64,14 +64,27 @@ SE_DEV void build_page(const PagesArgs &a, int unit, int b, int g, int p, int cl
     const int32_t *pos = a.pos + (int64_t)unit * a.max_blocks * a.page + p * a.page;
     const char *tile = a.k + ((int64_t)blk * a.n_kv + g) * a.page * 256 + cl * 16;
     const int rows = min(a.page, n - p * a.page);
-    for (int i = 0; i < rows; ++i) {
-      if (pos[i] < 0) continue;
-      float x[EPL];
-      unpack<DTYPE>(ld16(tile + i * 256), x);
+    // eight rows at a time: their positions and key pieces all in flight (past the page's last row: that row
+    // again, not counted)
+    for (int i0 = 0; i0 < rows; i0 += 8) {
+      int pv[8];
+      u32x4 w[8];
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        lo[e] = fminf(lo[e], x[e]);
-        hi[e] = fmaxf(hi[e], x[e]);
+      for (int j = 0; j < 8; ++j) {
+        const int i = min(i0 + j, rows - 1);
+        pv[j] = pos[i];
+        w[j] = ld16_stream(tile + i * 256);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (i0 + j >= rows || pv[j] < 0) continue;
+        float x[EPL];
+        unpack<DTYPE>(w[j], x);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          lo[e] = fminf(lo[e], x[e]);
+          hi[e] = fmaxf(hi[e], x[e]);
+        }
       }
     }
   } else if (p * a.page < n) {
@@ -140,8 +153,8 @@ __global__ __launch_bounds__(kThreads) void pages_score(PagesArgs a) {
   float lo[EPL], hi[EPL];
   if (live) {
     const char *m = a.meta + ((int64_t)unit * a.max_blocks + p) * 2 * 256 + cl * 16;
-    unpack<DTYPE>(ld16(m), lo);
-    unpack<DTYPE>(ld16(m + 256), hi);
+    unpack<DTYPE>(ld16_stream(m), lo);  // read once per call: non-temporal
+    unpack<DTYPE>(ld16_stream(m + 256), hi);
   } else {
 #pragma unroll
     for (int e = 0; e < EPL; ++e) lo[e] = hi[e] = 0.f;
