@@ -226,12 +226,12 @@ __global__ __launch_bounds__(kThreads, SE_DECODE_WG_PER_CU) void decode_partial(
       const int vk = ik < lim ? s_row[w0 + ik] : -1;
       const char *kr = a.k + (int64_t)(vk >= 0 ? vk : 0) * RB + lrow * 16;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) kb[t] = ld16_stream(kr + t * 64);
+      for (int t = 0; t < 4; ++t) kb[t] = ld16(kr + t * 64);
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         const int i = it * 16 + lrow * 4 + u;
         const int v = i < lim ? s_row[w0 + i] : -1;
-        vb[u] = ld16_stream(a.v + (int64_t)(v >= 0 ? v : 0) * RB + cl * 16);
+        vb[u] = ld16(a.v + (int64_t)(v >= 0 ? v : 0) * RB + cl * 16);
         rv[u] = v;
       }
       return;
@@ -241,8 +241,8 @@ __global__ __launch_bounds__(kThreads, SE_DECODE_WG_PER_CU) void decode_partial(
       const int i = it * 16 + u * 4 + lrow;
       const int v = i < lim ? s_row[w0 + i] : -1;
       const int64_t off = (int64_t)(v >= 0 ? v : 0) * RB + cl * 16;
-      kb[u] = ld16_stream(a.k + off);
-      vb[u] = ld16_stream(a.v + off);
+      kb[u] = ld16(a.k + off);
+      vb[u] = ld16(a.v + off);
       rv[u] = v;
     }
   };
