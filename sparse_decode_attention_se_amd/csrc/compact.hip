@@ -139,8 +139,9 @@ SE_DEV void move_tile(const GatherArgs &a, int unit, const Tile &t, int nrows) {
     const int r = x / cpr, ch = x % cpr;
     const int64_t so = t.soff[r], dof = t.doff[r];
     if (so < 0) continue;
-    st16_stream(a.k + dof + ch * 16, kbuf[i]);
-    st16_stream(a.v + dof + ch * 16, vbuf[i]);
+    // plain stores: the decode that follows a compaction reads these rows, and finds them in the last-level cache
+    st16(a.k + dof + ch * 16, kbuf[i]);
+    st16(a.v + dof + ch * 16, vbuf[i]);
     if (ch == 0) {
       a.pos[base + t.dslot[r]] = t.pval[r];
       if (a.cum) a.cum[base + t.dslot[r]] = t.cval[r];
