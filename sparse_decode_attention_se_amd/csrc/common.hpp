@@ -24,8 +24,9 @@ struct alignas(16) u32x4 {
 };
 SE_DEV u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
 // A 16-byte load marked non-temporal, for data read once. A streaming read of 8 GiB reaches 7.09 TB/s with it
-// against 6.29 with plain loads, but the cache state it leaves can slow the kernels that follow (measured per
-// call on each workload: the split decode and the bidirectional scorer keep plain loads).
+// against 6.29 with plain loads, but it does not find what the last-level cache holds: data that a kernel of the
+// same step has just written or read (a compaction's moved rows, the scorer's region keys) is read with plain
+// loads (measured per call on each workload).
 typedef unsigned int u32v4 __attribute__((ext_vector_type(4)));
 SE_DEV u32x4 ld16_stream(const void *p) {
   return __builtin_bit_cast(u32x4, __builtin_nontemporal_load(reinterpret_cast<const u32v4 *>(p)));

@@ -123,6 +123,10 @@ constexpr int kMaxChunkRows = 1024;
 #define SE_DECODE_MIN_WGS 512
 #endif
 constexpr int kMinWGs = SE_DECODE_MIN_WGS;
+#ifndef SE_DECODE_HOT_ROWS
+#define SE_DECODE_HOT_ROWS 4096
+#endif
+constexpr int kHotRows = SE_DECODE_HOT_ROWS;  // a unit's most recent rows, read with plain loads
 
 template <int DTYPE, int R>
 __global__ __launch_bounds__(kThreads, SE_DECODE_WG_PER_CU) void decode_partial(DecodeArgs a) {
@@ -219,20 +223,33 @@ __global__ __launch_bounds__(kThreads, SE_DECODE_WG_PER_CU) void decode_partial(
   lim = lim < 0 ? 0 : (lim > per_wave ? per_wave : lim);
   const int nit = (lim + 15) / 16;
 
+  // Chunks away from the unit's most recent rows (which the step's other calls have just written or read, so
+  // that the last-level cache may hold them) stream their rows with non-temporal loads.
+  const bool cold = list != nullptr || row0 + a.chunk_rows <= n - kHotRows;
   auto load = [&](int it, u32x4 (&kb)[kUnroll], u32x4 (&vb)[kUnroll], int (&rv)[kUnroll]) {
     if constexpr (kMfma) {
       // K in the MFMA layout (key cl of the step, k-step t at byte 64 t); V of keys 4 lrow + u, slice cl
       const int ik = it * 16 + cl;
       const int vk = ik < lim ? s_row[w0 + ik] : -1;
       const char *kr = a.k + (int64_t)(vk >= 0 ? vk : 0) * RB + lrow * 16;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) kb[t] = ld16(kr + t * 64);
+      const char *vr[kUnroll];
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         const int i = it * 16 + lrow * 4 + u;
         const int v = i < lim ? s_row[w0 + i] : -1;
-        vb[u] = ld16(a.v + (int64_t)(v >= 0 ? v : 0) * RB + cl * 16);
+        vr[u] = a.v + (int64_t)(v >= 0 ? v : 0) * RB + cl * 16;
         rv[u] = v;
+      }
+      if (cold) {  // uniform
+#pragma unroll
+        for (int t = 0; t < 4; ++t) kb[t] = ld16_stream(kr + t * 64);
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) vb[u] = ld16_stream(vr[u]);
+      } else {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) kb[t] = ld16(kr + t * 64);
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) vb[u] = ld16(vr[u]);
       }
       return;
     }
