@@ -30,8 +30,8 @@ A step is one pass of the workload's hot path over its batch, with every input r
      both policies' compression share. --steps and --warmup do not apply (one period, after an untimed pass).
 
 Every workload but c4 changes its cache or would leave its working set in the 256 MB last-level cache between
-steps, so before each of its steps the cache is copied back from one pristine clone and 1 GiB is written to flush
-the last-level cache, outside the timed region; each step's wall time is taken between two device
+steps, so before each of its steps the cache is copied back from one pristine clone and 1 GiB is read to flush
+the last-level cache (leaving clean lines), outside the timed region; each step's wall time is taken between two device
 synchronisations. c4's eager steps run back to back on one evolving cache. Per-call times come from HIP events on the
 stream the calls are launched on. Every call reports index and capacity errors into one status word, checked
 after the warm-up and after the timed steps. For c1 and c2 the oracle is timed on the host first, on all cores
@@ -793,8 +793,9 @@ def require_clean_status(se, status, when):
 
 
 def flush_llc(buf):
-    """Write 1 GiB so that nothing a step reads is left in the 256 MB last-level cache."""
-    buf.fill_(0.0)
+    """Read 1 GiB so that nothing a step reads is left in the 256 MB last-level cache. A read leaves clean lines
+    behind: a write would leave 256 MB of dirty lines whose write-back the step's first large kernel would pay."""
+    buf.amax()
 
 
 def main():
@@ -859,7 +860,7 @@ def main():
     t0 = time.time()
     wl = SETUPS[args.workload](se, WF, W, dev, status, args.warmup + args.steps)
     cfg, alg = wl.cfg, wl.alg
-    flush = torch.empty(2**28, dtype=torch.float32, device=dev) if wl.restore else None
+    flush = torch.zeros(2**28, dtype=torch.float32, device=dev) if wl.restore else None
     torch.cuda.synchronize()
     log(f"{cfg.name}: inputs ready in {time.time() - t0:.1f} s, {torch.cuda.memory_allocated() / 2**30:.1f} GiB "
         f"resident")
@@ -986,7 +987,7 @@ def main():
     if getattr(wl, "graph", None) is not None and not args.eager:
         # the workload's whole loop as one captured graph, replayed on the restored cache after a flush: the line's
         # step time is the replay's per decode step
-        flush = torch.empty(2**28, dtype=torch.float32, device=dev)
+        flush = torch.zeros(2**28, dtype=torch.float32, device=dev)
         wl.graph_restore()
         torch.cuda.synchronize()
         graph = wl.graph()

@@ -206,12 +206,7 @@ SE_DEV void kstep_fetch(const ScoreArgs &a, int g, int c0, int c1, int step, con
     ks.pos[kb] = (ad.pos[kb] & keep) | ~keep;
     const char *src = a.k + (int64_t)row * 256 + (lane >> 4) * 16;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      // two-tile steps stream keys that one row group reads once per pass: non-temporal loads, which the memory
-      // system serves faster; four-tile steps (several row groups) keep the keys cached for the other groups
-      const u32x4 w = KB == 2 ? ld16_stream(src + t * 64) : ld16(src + t * 64);
-      ks.f[kb][t] = __builtin_bit_cast(bf16x8, w);
-    }
+    for (int t = 0; t < 4; ++t) ks.f[kb][t] = __builtin_bit_cast(bf16x8, ld16(src + t * 64));
   }
 }
 
