@@ -115,7 +115,7 @@ struct ViewMap {
 // Running maxima move only when a logit exceeds them by more than kLazy (log2 units): until then the weights are
 // exp2 of at most kLazy, which fp32 sums hold without loss, and the rescale of l and acc is skipped.
 constexpr float kLazy = 8.f;
-constexpr int kMaxChunkRows = 1024;
+constexpr int kMaxChunkRows = 2048;
 #ifndef SE_DECODE_WG_PER_CU
 #define SE_DECODE_WG_PER_CU 2  // occupancy hint of the split kernel (the compiler settles at three waves per SIMD)
 #endif
