@@ -18,7 +18,8 @@
 namespace se {
 namespace {
 
-constexpr int kThreads = 1024;
+// workgroup sizes: 1024 threads, or 256 for units of at most 1024 items (fewer waves to meet at each barrier)
+constexpr int kThreadsBig = 1024, kThreadsSmall = 256;
 
 SE_DEV uint32_t orderable(float f) {
   uint32_t u = __float_as_uint(f == 0.f ? 0.f : f);  // -0 == +0
@@ -35,11 +36,12 @@ struct TopkArgs {
   int32_t n_kv, page, max_slots, max_blocks, num_blocks;
 };
 
-// One workgroup per unit; item i lives in thread i % kThreads, register j = i / kThreads (coalesced loads).
-constexpr int kWaves = kThreads / 64;
+// One workgroup per unit; item i lives in thread i % NTH, register j = i / NTH (coalesced loads).
 
-// block-wide reductions (every thread gets the result); s_red holds kWaves values
+// block-wide reductions (every thread gets the result); s_red holds one value per wave
+template <int NTH>
 SE_DEV uint32_t block_min_u(uint32_t x, uint32_t *s_red) {
+  constexpr int kWaves = NTH / 64;
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) x = min(x, (uint32_t)__shfl_xor((int)x, o));
   __syncthreads();
@@ -49,7 +51,9 @@ SE_DEV uint32_t block_min_u(uint32_t x, uint32_t *s_red) {
   for (int w = 1; w < kWaves; ++w) x = min(x, s_red[w]);
   return x;
 }
+template <int NTH>
 SE_DEV uint32_t block_max_u(uint32_t x, uint32_t *s_red) {
+  constexpr int kWaves = NTH / 64;
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) x = max(x, (uint32_t)__shfl_xor((int)x, o));
   __syncthreads();
@@ -59,7 +63,9 @@ SE_DEV uint32_t block_max_u(uint32_t x, uint32_t *s_red) {
   for (int w = 1; w < kWaves; ++w) x = max(x, s_red[w]);
   return x;
 }
+template <int NTH>
 SE_DEV int block_sum_i(int x, uint32_t *s_red) {
+  constexpr int kWaves = NTH / 64;
   x = wave_sum_i(x);
   __syncthreads();
   if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = (uint32_t)x;
@@ -73,9 +79,10 @@ SE_DEV int block_sum_i(int x, uint32_t *s_red) {
 // return `want` is the number of items equal to T still to be taken (those above T are all taken). Radix select
 // over 8-bit digits of v - min, starting at the highest bit in which the items differ, so the first histogram
 // already spreads over many bins.
-template <int PER>
+template <int PER, int NTH>
 SE_DEV uint32_t radix_kth(const uint32_t (&v)[PER], uint32_t mask, int &want, uint32_t *s_hist, uint32_t *s_red,
                           int *s_res) {
+  constexpr int kThreads = NTH;
   uint32_t lo = 0xffffffffu, hi = 0;
 #pragma unroll
   for (int j = 0; j < PER; ++j)
@@ -83,8 +90,8 @@ SE_DEV uint32_t radix_kth(const uint32_t (&v)[PER], uint32_t mask, int &want, ui
       lo = min(lo, v[j]);
       hi = max(hi, v[j]);
     }
-  lo = block_min_u(lo, s_red);
-  hi = block_max_u(hi, s_red);
+  lo = block_min_u<NTH>(lo, s_red);
+  hi = block_max_u<NTH>(hi, s_red);
   if (lo >= hi) return hi;  // all equal
   int top = 32 - __clz(hi - lo);
   uint32_t prefix = 0;  // digits of (T - lo) above bit `top` found so far
@@ -135,8 +142,9 @@ SE_DEV uint32_t radix_kth(const uint32_t (&v)[PER], uint32_t mask, int &want, ui
   return lo + prefix;
 }
 
-template <int PER, bool ONE>  // ONE: k == 1, selected by one arg-max instead of radix passes
-__global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
+template <int PER, bool ONE, int NTH>  // ONE: k == 1, selected by one arg-max instead of radix passes
+__global__ __launch_bounds__(NTH) void topk_kernel(TopkArgs a) {
+  constexpr int kThreads = NTH, kWaves = NTH / 64;
   __shared__ uint32_t s_hist[256];
   __shared__ uint32_t s_red[kWaves];
   __shared__ int s_res[2];
@@ -187,7 +195,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
     mx = max(mx, pv[j]);
   }
   int limit = 0;
-  if (a.mode == SE_TOPK_SMALLEST) limit = (int)block_max_u((uint32_t)(mx + 1), s_red) - 1 - a.recent;
+  if (a.mode == SE_TOPK_SMALLEST) limit = (int)block_max_u<NTH>((uint32_t)(mx + 1), s_red) - 1 - a.recent;
 
   // range-restricted pruning: a bit per logical page of the items (pages from the one holding slot `base`) whose
   // block has references, in LDS (threads load block-table entries and counts cooperatively); an item looks up
@@ -243,7 +251,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
     }
     if (k) keep |= 1u << j;
   }
-  const int ncand = block_sum_i(ncand_local, s_red);
+  const int ncand = block_sum_i<NTH>(ncand_local, s_red);
 
   int want = a.k;
   if (a.mode == SE_TOPK_SMALLEST) {
@@ -261,7 +269,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
 #pragma unroll
     for (int j = 0; j < PER; ++j)
       if ((cand >> j) & 1u) bk = max(bk, key[j]);
-    bk = block_max_u(bk, s_red);
+    bk = block_max_u<NTH>(bk, s_red);
     auto tie_of = [&](int j) {
       const int i = j * kThreads + t;
       return page_unit ? (uint32_t)i : (a.mode == SE_TOPK_SMALLEST ? 0x7fffffffu - (uint32_t)pv[j] : (uint32_t)pv[j]);
@@ -270,13 +278,13 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
 #pragma unroll
     for (int j = 0; j < PER; ++j)
       if (((cand >> j) & 1u) && key[j] == bk) bt = min(bt, tie_of(j));
-    bt = block_min_u(bt, s_red);
+    bt = block_min_u<NTH>(bt, s_red);
 #pragma unroll
     for (int j = 0; j < PER; ++j)
       if (((cand >> j) & 1u) && key[j] == bk && tie_of(j) == bt) sel |= 1u << j;
   } else if (want > 0) {
     int w = want;
-    const uint32_t T = radix_kth<PER>(key, cand, w, s_hist, s_red, s_res);
+    const uint32_t T = radix_kth<PER, NTH>(key, cand, w, s_hist, s_red, s_res);
     uint32_t eq = 0;
     int n_eq_local = 0;
 #pragma unroll
@@ -288,7 +296,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
         ++n_eq_local;
       }
     }
-    const int n_eq = block_sum_i(n_eq_local, s_red);
+    const int n_eq = block_sum_i<NTH>(n_eq_local, s_red);
     if (n_eq == w) {
       sel |= eq;
     } else {
@@ -309,7 +317,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
         }
         inv[j] = ~tie;
       }
-      const uint32_t T2 = radix_kth<PER>(inv, eq, w, s_hist, s_red, s_res);
+      const uint32_t T2 = radix_kth<PER, NTH>(inv, eq, w, s_hist, s_red, s_res);
 #pragma unroll
       for (int j = 0; j < PER; ++j)
         if (((eq >> j) & 1u) && inv[j] >= T2) sel |= 1u << j;
@@ -430,19 +438,23 @@ extern "C" int32_t se_topk_select(const se_cache_t *c, const float *scores, cons
   a.max_slots = max_slots;
   const int units = c->B * c->n_kv;
   hipStream_t st = (hipStream_t)stream;
-  const int per = (n_items + se::kThreads - 1) / se::kThreads;
-  const dim3 grid(units), block(se::kThreads);
-#define SE_TOPK_LAUNCH(P)                                                                                      \
+  const dim3 grid(units);
+#define SE_TOPK_LAUNCH(P, N)                                                                                   \
   do {                                                                                                         \
-    if (p->k == 1) hipLaunchKernelGGL((se::topk_kernel<P, true>), grid, block, 0, st, a);                     \
-    else hipLaunchKernelGGL((se::topk_kernel<P, false>), grid, block, 0, st, a);                               \
+    if (p->k == 1) hipLaunchKernelGGL((se::topk_kernel<P, true, N>), grid, dim3(N), 0, st, a);                \
+    else hipLaunchKernelGGL((se::topk_kernel<P, false, N>), grid, dim3(N), 0, st, a);                          \
   } while (0)
-  if (per <= 1) SE_TOPK_LAUNCH(1);
-  else if (per <= 4) SE_TOPK_LAUNCH(4);
-  else if (per <= 8) SE_TOPK_LAUNCH(8);
-  else if (per <= 16) SE_TOPK_LAUNCH(16);
-  else if (per <= 32) SE_TOPK_LAUNCH(32);
-  else return SE_ERR_UNSUPPORTED;
+  if (n_items <= 4 * se::kThreadsSmall) {
+    if (n_items <= se::kThreadsSmall) SE_TOPK_LAUNCH(1, se::kThreadsSmall);
+    else SE_TOPK_LAUNCH(4, se::kThreadsSmall);
+  } else {
+    const int per = (n_items + se::kThreadsBig - 1) / se::kThreadsBig;
+    if (per <= 4) SE_TOPK_LAUNCH(4, se::kThreadsBig);
+    else if (per <= 8) SE_TOPK_LAUNCH(8, se::kThreadsBig);
+    else if (per <= 16) SE_TOPK_LAUNCH(16, se::kThreadsBig);
+    else if (per <= 32) SE_TOPK_LAUNCH(32, se::kThreadsBig);
+    else return SE_ERR_UNSUPPORTED;
+  }
 #undef SE_TOPK_LAUNCH
   return se_host::launch_status();
 }
