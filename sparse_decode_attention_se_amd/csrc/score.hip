@@ -5,9 +5,10 @@
 //     protected tail) with no mask; weights are summed the same way.
 //
 // Per (sequence, KV head) unit the R*Wq query rows of the group form a matrix Q and the keys a matrix K. The row
-// softmax needs each row's global max and sum before any weight can be added to a key, so the work is two passes
-// over QK^T: pass 1 streams K in chunks and keeps an online (max, sum) per row; pass 2 merges those, recomputes
-// QK^T and adds exp2(s - max - log2 sum) into per-key column sums. For bf16 (d = 128) QK^T runs on MFMA
+// softmax needs each row's global normaliser before any weight can be added to a key, so the work is two passes
+// over QK^T: pass 1 streams K in chunks and sums exp2(s) per row (with an exact running-max fallback for rows
+// whose sums leave a safe range); pass 2 merges the chunks' (reference, sum) pairs, recomputes QK^T and adds
+// exp2(s - ref - log2 sum) into per-key column sums. For bf16 (d = 128) QK^T runs on MFMA
 // (v_mfma_f32_16x16x32_bf16, fp32 accumulate); fp32 inputs use a plain VALU path. A workgroup covers up to 256
 // query rows and one key chunk; with several row groups, a last kernel sums their column sums. When one chunk holds
 // a unit's whole key range and every wave has at most two steps, a single kernel does both passes.
