@@ -127,6 +127,7 @@ constexpr int kMinWGs = SE_DECODE_MIN_WGS;
 #define SE_DECODE_HOT_ROWS 4096
 #endif
 constexpr int kHotRows = SE_DECODE_HOT_ROWS;  // a unit's most recent rows, read with plain loads
+constexpr int kUnitHotRows = 2048;              // the same for the single-workgroup decode
 
 template <int DTYPE, int R>
 __global__ __launch_bounds__(kThreads, SE_DECODE_WG_PER_CU) void decode_partial(DecodeArgs a) {
@@ -669,13 +670,23 @@ __global__ __launch_bounds__(kUnitThreads) void decode_unit(DecodeArgs a) {
 #pragma unroll
     for (int u = 0; u < U; ++u) rv[u] = __builtin_amdgcn_ds_bpermute((half * SR + u * 4 + lrow) * 4, vs);
   };
+  // waves whose rows end at least kUnitHotRows before the view's last row load non-temporally; the waves over the
+  // most recent rows load plain (measured: a mix streams faster than either kind alone)
+  const bool cold = wr1 <= rows - kUnitHotRows;  // uniform per wave
   auto load = [&](const int (&rv)[U + 1], u32x4 (&kb)[U], u32x4 (&vb)[U]) {
     if constexpr (kMfma) {
       const char *kr = a.k + (int64_t)(rv[U] >= 0 ? rv[U] : 0) * RB + lrow * 16;
+      if (cold) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) kb[t] = ld16_stream(kr + t * 64);
+        for (int t = 0; t < 4; ++t) kb[t] = ld16_stream(kr + t * 64);
 #pragma unroll
-      for (int u = 0; u < U; ++u) vb[u] = ld16_stream(a.v + (int64_t)(rv[u] >= 0 ? rv[u] : 0) * RB + cl * 16);
+        for (int u = 0; u < U; ++u) vb[u] = ld16_stream(a.v + (int64_t)(rv[u] >= 0 ? rv[u] : 0) * RB + cl * 16);
+      } else {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) kb[t] = ld16(kr + t * 64);
+#pragma unroll
+        for (int u = 0; u < U; ++u) vb[u] = ld16(a.v + (int64_t)(rv[u] >= 0 ? rv[u] : 0) * RB + cl * 16);
+      }
       return;
     }
 #pragma unroll
