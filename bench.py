@@ -34,7 +34,7 @@ steps, so before each of its steps the cache is copied back from one pristine cl
 the last-level cache (leaving clean lines), outside the timed region; each step's wall time is taken between two device
 synchronisations. c4's eager steps run back to back on one evolving cache. Per-call times come from HIP events on the
 stream the calls are launched on. Every call reports index and capacity errors into one status word, checked
-after the warm-up and after the timed steps. For c1 and c2 the oracle is timed on the host first, on all cores
+after the warm-up and after the timed steps. For c1 to c4 the oracle is timed on the host first, on all cores
 (one worker process per core) and on one core.
 """
 import argparse
@@ -50,6 +50,9 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+# workloads whose step the oracle is timed on (the CPU baseline), and how many of H2O's steps its sample cycles over
+ORACLE_WORKLOADS = ("c1", "c2", "c3", "c4")
+ORACLE_H2O_STEPS = 64
 
 
 def log(msg):
@@ -711,6 +714,25 @@ def _oracle_sample(workload, first, n_seq):
             return n_seq * cfg.window
 
         return run
+    if workload == "c3":
+        cfg = W.scaled(W.C3, B=n_seq)
+        inp = W.gen_quest(cfg, seed=0, threads=1, first=first)
+        return lambda: (P.quest_step(inp), n_seq * cfg.N)[1]
+    if workload == "c4":
+        # the workload's own inputs (1024 steps drawn); the sample cycles over its first ORACLE_H2O_STEPS steps,
+        # starting again from the initial cache after the last of them
+        cfg = W.scaled(W.C4, B=n_seq)
+        inp = W.gen_h2o(cfg, seed=0, threads=1, first=first)
+        state = {"cache": inp["cache"].copy(), "t": 0}
+
+        def run():
+            if state["t"] == ORACLE_H2O_STEPS:
+                state["cache"], state["t"] = inp["cache"].copy(), 0
+            state["cache"], _ = P.h2o_step(inp, state["cache"], state["t"])
+            state["t"] += 1
+            return n_seq * (cfg.budget + 1)
+
+        return run
     raise ValueError(workload)
 
 
@@ -772,7 +794,10 @@ def cpu_baseline(workload, n_seq, min_seconds, max_workers=16):
     one = _run_workers(ctx, workload, 1, n_seq, min_seconds)[0]
     what = {"c1": "the whole event (window scores, top-K, compaction, decode)",
             "c2": "the whole step (Kara's event: window scores, top-K, Token2Chunk, compaction; then append and "
-                  "decode)"}[workload]
+                  "decode)",
+            "c3": "the whole step (page metadata build, page scores, top pages, decode over them)",
+            "c4": f"decode steps (append, decode with cumulative scores, bottom-1, eviction) cycling over the first "
+                  f"{ORACLE_H2O_STEPS} of the workload's 1024"}[workload]
     return {
         "value": round(tokens / wall, 1), "unit": "KV tokens/s", "cores": n, "kind": "oracle",
         "sample": f"{n} worker processes (one per core of {avail} available, BLAS limited to one thread each), "
@@ -804,7 +829,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="c2", choices=sorted(SETUPS) + ["c8"])
-    ap.add_argument("--cpu-seqs", type=int, default=2, help="sequences per oracle worker in the CPU baseline")
+    ap.add_argument("--cpu-seqs", type=int, help="sequences per oracle worker in the CPU baseline (default: 1 for "
+                    "c3's 128K-token sequences, else 2)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle time for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true",
@@ -834,9 +860,10 @@ def main():
 
     # the host baseline first: its workers are forked, which must happen before anything touches the GPU
     cpu = None
-    if args.workload in ("c1", "c2") and not args.no_cpu_baseline:
+    if args.workload in ORACLE_WORKLOADS and not args.no_cpu_baseline:
         log(f"timing the oracle on the host ({host_cores()} cores available)")
-        cpu = cpu_baseline(args.workload, args.cpu_seqs, args.cpu_seconds)
+        n_seq = args.cpu_seqs or (1 if args.workload == "c3" else 2)
+        cpu = cpu_baseline(args.workload, n_seq, args.cpu_seconds)
         log(f"oracle: {cpu['value']:.0f} tokens/s on {cpu['cores']} cores, {cpu['single_core']['value']:.0f} on one")
 
     if args.calibrate_copy:

@@ -94,3 +94,26 @@ def test_every_workload_has_a_traffic_summary_for_its_dominant_call():
         # bytes, read and written are each rounded from the scaled counters
         assert abs(int(kv["bytes"]) - int(kv["read"]) - int(kv["written"])) <= 2 and int(kv["bytes"]) > 0
         assert len(kv["sources"]) == 16
+
+
+def test_oracle_samples_draw_the_workload_sequences_they_name():
+    # a CPU-baseline worker on sequences [first, first + n) generates exactly those sequences of the larger batch
+    import numpy as np
+
+    import workloads as W
+
+    for gen, cfg in ((W.gen_quest, W.scaled(W.C3, N=1024, top_pages=8)),
+                     (W.gen_h2o, W.scaled(W.C4, N=256, budget=256, recent=32, steps=3))):
+        whole = gen(W.scaled(cfg, B=3), seed=0, threads=1)
+        part = gen(W.scaled(cfg, B=1), seed=0, threads=1, first=2)
+        for key in ("q_dec", "q_steps", "k_new", "v_new"):
+            if key in whole:
+                axis = 1 if key in ("q_steps", "k_new", "v_new") else 0
+                assert np.array_equal(np.take(whole[key], [2], axis=axis), part[key]), key
+        for pool in ("k_pool", "v_pool"):
+            # the sequence's mapped blocks, through its block-table row in each cache
+            ta, tb = whole["cache"].block_table[2], part["cache"].block_table[0]
+            assert np.array_equal(ta >= 0, tb >= 0) and (ta >= 0).sum() > 0
+            a = getattr(whole["cache"], pool)[ta[ta >= 0]]
+            b = getattr(part["cache"], pool)[tb[tb >= 0]]
+            assert np.array_equal(a, b), pool

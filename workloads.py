@@ -497,23 +497,24 @@ def gen_h2o_prefill(cfg: H2OPrefill, seed: int = 0, threads: int = 8) -> dict:
     return dict(cfg=cfg, cache=c, k_all=k_all, v_all=v_all, q_all=q_all, q_dec=inp["q_dec"], scale=inp["scale"])
 
 
-def gen_quest(cfg: Quest, seed: int = 0, threads: int = 8) -> dict:
+def gen_quest(cfg: Quest, seed: int = 0, threads: int = 8, first: int = 0) -> dict:
     """Inputs of the Quest-style workload: a full cache with a fraction of pages shifted along the group's query
     direction, page metadata storage, and one decode query per sequence. With ``cfg.steps`` > 0 the cache has
     room for that many appended tokens, whose keys and values (``k_new``, ``v_new`` [steps][B][n_kv][d], i.i.d.
-    N(0,1)) are drawn from streams of their own, so the prompt's draws do not change."""
+    N(0,1)) are drawn from streams of their own, so the prompt's draws do not change. With ``first`` > 0 the B
+    sequences are those numbered ``first .. first + B - 1`` of a larger batch."""
     B, hq, hkv, d, N, page = cfg.B, cfg.hq, cfg.hkv, cfg.d, cfg.N, cfg.page
     max_blocks = -(-(N + cfg.steps) // page)
     cache = empty_cache(B, hkv, d, page, max_blocks, B * max_blocks, cfg.dtype, with_meta=True)
     nb = layout_initial(cache, N)
     r = hq // hkv
-    q64 = [_normal(seed, TAG_QDEC, b, (hq, d)) for b in range(B)]
+    q64 = [_normal(seed, TAG_QDEC, first + b, (hq, d)) for b in range(B)]
     q_dec = np.stack([to_storage(q, cfg.dtype) for q in q64])
     n_shift = int(round(cfg.shift_frac * nb))
 
     def fill(b):
-        k = _normal(seed, TAG_K, b, (hkv, N, d))
-        rs = rng_for(seed, TAG_SHIFT, b)
+        k = _normal(seed, TAG_K, first + b, (hkv, N, d))
+        rs = rng_for(seed, TAG_SHIFT, first + b)
         for g in range(hkv):
             pages = rs.choice(nb, size=n_shift, replace=False)
             direction = q64[b][g * r:(g + 1) * r].sum(axis=0)
@@ -521,25 +522,26 @@ def gen_quest(cfg: Quest, seed: int = 0, threads: int = 8) -> dict:
             for p in pages:
                 k[g, p * page:min((p + 1) * page, N), :] += cfg.shift * direction
         write_sequence(cache.k_pool, nb, b, to_storage(k, cfg.dtype), page)
-        v = _normal(seed, TAG_V, b, (hkv, N, d))
+        v = _normal(seed, TAG_V, first + b, (hkv, N, d))
         write_sequence(cache.v_pool, nb, b, to_storage(v, cfg.dtype), page)
 
     _pmap(fill, range(B), threads)
     out = dict(cfg=cfg, cache=cache, q_dec=q_dec, scale=1.0 / math.sqrt(d))
     if cfg.steps:
-        out["k_new"] = np.stack([to_storage(_normal(seed, TAG_KNEW, b, (cfg.steps, hkv, d)), cfg.dtype)
+        out["k_new"] = np.stack([to_storage(_normal(seed, TAG_KNEW, first + b, (cfg.steps, hkv, d)), cfg.dtype)
                                  for b in range(B)], axis=1)
-        out["v_new"] = np.stack([to_storage(_normal(seed, TAG_VNEW, b, (cfg.steps, hkv, d)), cfg.dtype)
+        out["v_new"] = np.stack([to_storage(_normal(seed, TAG_VNEW, first + b, (cfg.steps, hkv, d)), cfg.dtype)
                                  for b in range(B)], axis=1)
     return out
 
 
-def gen_h2o(cfg: H2O, seed: int = 0, threads: int = 8) -> dict:
+def gen_h2o(cfg: H2O, seed: int = 0, threads: int = 8, first: int = 0) -> dict:
     """Inputs of the H2O continuous-eviction workload.
 
     Keys of every token (initial context and the ``steps`` appended ones) carry a per-sequence Zipf key-norm
     scale: a seeded permutation gives token t the rank rho_t in 1..N+steps, the scale is rho_t^-zipf normalised
-    to unit RMS over the sequence, shared by all heads.
+    to unit RMS over the sequence, shared by all heads. With ``first`` > 0 the B sequences are those numbered
+    ``first .. first + B - 1`` of a larger batch.
     """
     B, hq, hkv, d, N, page = cfg.B, cfg.hq, cfg.hkv, cfg.d, cfg.N, cfg.page
     T = N + cfg.steps
@@ -553,21 +555,21 @@ def gen_h2o(cfg: H2O, seed: int = 0, threads: int = 8) -> dict:
     v_new = np.zeros((cfg.steps, B, hkv, d), sd)
 
     def fill(b):
-        k = _normal(seed, TAG_K, b, (hkv, T, d))
-        rank = rng_for(seed, TAG_ZIPF, b).permutation(T) + 1
+        k = _normal(seed, TAG_K, first + b, (hkv, T, d))
+        rank = rng_for(seed, TAG_ZIPF, first + b).permutation(T) + 1
         s = rank.astype(np.float64) ** (-cfg.zipf)
         s /= math.sqrt(float(np.mean(s * s)))
         k *= s[None, :, None]
         ks = to_storage(k, cfg.dtype)
         write_sequence(cache.k_pool, nb, b, np.ascontiguousarray(ks[:, :N]), page)
         k_new[:, b] = ks[:, N:].transpose(1, 0, 2)
-        v = to_storage(_normal(seed, TAG_V, b, (hkv, T, d)), cfg.dtype)
+        v = to_storage(_normal(seed, TAG_V, first + b, (hkv, T, d)), cfg.dtype)
         write_sequence(cache.v_pool, nb, b, np.ascontiguousarray(v[:, :N]), page)
         v_new[:, b] = v[:, N:].transpose(1, 0, 2)
 
     _pmap(fill, range(B), threads)
     q_steps = np.stack([np.stack([to_storage(x, cfg.dtype) for x in
-                                  _normal(seed, TAG_QDEC, b, (cfg.steps, hq, d))]) for b in range(B)], axis=1)
+                                  _normal(seed, TAG_QDEC, first + b, (cfg.steps, hq, d))]) for b in range(B)], axis=1)
     return dict(cfg=cfg, cache=cache, q_steps=q_steps, k_new=k_new, v_new=v_new, scale=1.0 / math.sqrt(d))
 
 
