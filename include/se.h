@@ -86,7 +86,9 @@ typedef struct se_cache {
  *   BIDIR: the window is the last `window` slots [w0, n_slots), w0 = n_slots - window, and the region its first
  *     window - protect slots. q_win [B][n_q][window][d] holds the queries of the window's tokens; q_pos is
  *     unused. Each query row is a softmax over the resident region slots (no mask);
- *     scores[(b*n_kv+g)*score_stride + (s - w0)] for s in the region.
+ *     scores[(b*n_kv+g)*score_stride + (s - w0)] for s in the region. A unit with n_slots < window raises
+ *     SE_DEV_INDEX and its scores are not written.
+ *   Nothing outside these entries is written.
  * accumulate != 0: every score is added to the value the output already holds instead of replacing it, so with
  *   scores = cum_score (score_stride = max_blocks * page) the causal scores of a prefill chunk's queries are added to
  *   H2O's cumulative scores (SparseEngine page, "What it is": H2O keeps cumulative attention scores).

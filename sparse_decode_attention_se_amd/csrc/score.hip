@@ -71,7 +71,10 @@ SE_DEV void key_range(const ScoreArgs &a, int unit, int &k0, int &k1, int &n) {
   } else {
     k0 = n - a.window;
     k1 = k0 + (a.window - a.protect);
-    if (k0 < 0) k0 = k1 = 0;
+    if (k0 < 0) {  // a window longer than the unit's slots: an index error, and nothing is scored
+      if (threadIdx.x == 0) raise(a.status, SE_DEV_INDEX);
+      k0 = k1 = 0;
+    }
   }
 }
 
