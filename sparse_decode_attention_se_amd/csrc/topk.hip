@@ -20,6 +20,9 @@ namespace {
 
 // workgroup sizes: 1024 threads, or 256 for units of at most 1024 items (fewer waves to meet at each barrier)
 constexpr int kThreadsBig = 1024, kThreadsSmall = 256;
+#ifndef SE_TOPK_ONE_THREADS
+#define SE_TOPK_ONE_THREADS 512  // workgroup size for k = 1 over more than 1024 items (fewer waves per barrier)
+#endif
 
 SE_DEV uint32_t orderable(float f) {
   uint32_t u = __float_as_uint(f == 0.f ? 0.f : f);  // -0 == +0
@@ -61,6 +64,22 @@ SE_DEV uint32_t block_max_u(uint32_t x, uint32_t *s_red) {
   __syncthreads();
   x = s_red[0];
   for (int w = 1; w < kWaves; ++w) x = max(x, s_red[w]);
+  return x;
+}
+template <int NTH>
+SE_DEV uint64_t block_max_u64(uint64_t x, uint64_t *s_red) {
+  constexpr int kWaves = NTH / 64;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)x, o), hi = (uint32_t)__shfl_xor((int)(uint32_t)(x >> 32), o);
+    const uint64_t y = ((uint64_t)hi << 32) | lo;
+    x = y > x ? y : x;
+  }
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  x = s_red[0];
+  for (int w = 1; w < kWaves; ++w) x = s_red[w] > x ? s_red[w] : x;
   return x;
 }
 template <int NTH>
@@ -147,6 +166,7 @@ __global__ __launch_bounds__(NTH) void topk_kernel(TopkArgs a) {
   constexpr int kThreads = NTH, kWaves = NTH / 64;
   __shared__ uint32_t s_hist[256];
   __shared__ uint32_t s_red[kWaves];
+  __shared__ uint64_t s_red64[ONE ? kWaves : 1];
   __shared__ int s_res[2];
   __shared__ int s_cnt[PER * kWaves];
   __shared__ uint32_t s_busy[(PER * kThreads + 31) / 32];  // range pruning: logical pages in busy blocks
@@ -251,37 +271,51 @@ __global__ __launch_bounds__(NTH) void topk_kernel(TopkArgs a) {
     }
     if (k) keep |= 1u << j;
   }
-  const int ncand = block_sum_i<NTH>(ncand_local, s_red);
+  // k = 1 needs no candidate count: its selection below finds nothing when there is no candidate
+  const int ncand = ONE ? 0 : block_sum_i<NTH>(ncand_local, s_red);
 
   int want = a.k;
   if (a.mode == SE_TOPK_SMALLEST) {
     const int over = a.ctx[unit] - a.budget;
     want = min(want, over < 0 ? 0 : over);
   }
-  want = min(want, ncand);
+  if (!ONE) want = min(want, ncand);
 
   uint32_t sel = 0;
-  if (want == ncand) {
+  uint64_t best = 0;  // k = 1: the chosen item's (key, complemented tie key); 0 when nothing is chosen
+  if (ONE) {
+    // one item (H2O evicts one per step): the largest key, then the smallest tie key among the items holding it,
+    // as the largest pair (key, ~tie key) in one reduction. Tie keys are below 2^31, so a candidate's pair is never 0.
+    if (want > 0) {
+      auto tie_of = [&](int j) {
+        const int i = j * kThreads + t;
+        return page_unit ? (uint32_t)i : (a.mode == SE_TOPK_SMALLEST ? 0x7fffffffu - (uint32_t)pv[j] : (uint32_t)pv[j]);
+      };
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const uint64_t v = ((uint64_t)key[j] << 32) | (uint32_t)~tie_of(j);
+        if (((cand >> j) & 1u) && v > best) best = v;
+      }
+      best = block_max_u64<NTH>(best, s_red64);
+#pragma unroll
+      for (int j = 0; j < PER; ++j)
+        if (((cand >> j) & 1u) && best != 0 && ((uint64_t)key[j] << 32 | (uint32_t)~tie_of(j)) == best) sel |= 1u << j;
+    }
+    if (a.mode == SE_TOPK_SMALLEST) {
+      // nothing is kept besides the chosen item: its thread writes it, with no ordering pass
+      if (best != 0 && a.out_stride < 1) {
+        if (t == 0) {
+          raise(a.status, SE_DEV_CAPACITY);
+          a.count[unit] = 0;
+        }
+        return;
+      }
+      if (sel) a.idx[(int64_t)unit * a.out_stride] = base + __builtin_ctz(sel) * kThreads + t;
+      if (t == 0) a.count[unit] = best != 0 ? 1 : 0;
+      return;
+    }
+  } else if (want == ncand) {
     sel = cand;
-  } else if (ONE) {
-    // one item (H2O evicts one per step): the largest key, then the smallest tie key among the items holding it
-    uint32_t bk = 0;
-#pragma unroll
-    for (int j = 0; j < PER; ++j)
-      if ((cand >> j) & 1u) bk = max(bk, key[j]);
-    bk = block_max_u<NTH>(bk, s_red);
-    auto tie_of = [&](int j) {
-      const int i = j * kThreads + t;
-      return page_unit ? (uint32_t)i : (a.mode == SE_TOPK_SMALLEST ? 0x7fffffffu - (uint32_t)pv[j] : (uint32_t)pv[j]);
-    };
-    uint32_t bt = 0xffffffffu;
-#pragma unroll
-    for (int j = 0; j < PER; ++j)
-      if (((cand >> j) & 1u) && key[j] == bk) bt = min(bt, tie_of(j));
-    bt = block_min_u<NTH>(bt, s_red);
-#pragma unroll
-    for (int j = 0; j < PER; ++j)
-      if (((cand >> j) & 1u) && key[j] == bk && tie_of(j) == bt) sel |= 1u << j;
   } else if (want > 0) {
     int w = want;
     const uint32_t T = radix_kth<PER, NTH>(key, cand, w, s_hist, s_red, s_res);
@@ -447,6 +481,13 @@ extern "C" int32_t se_topk_select(const se_cache_t *c, const float *scores, cons
   if (n_items <= 4 * se::kThreadsSmall) {
     if (n_items <= se::kThreadsSmall) SE_TOPK_LAUNCH(1, se::kThreadsSmall);
     else SE_TOPK_LAUNCH(4, se::kThreadsSmall);
+  } else if (SE_TOPK_ONE_THREADS != se::kThreadsBig && p->k == 1 && n_items <= 32 * SE_TOPK_ONE_THREADS) {
+    constexpr int N = SE_TOPK_ONE_THREADS;
+    const int per = (n_items + N - 1) / N;
+    if (per <= 4) hipLaunchKernelGGL((se::topk_kernel<4, true, N>), grid, dim3(N), 0, st, a);
+    else if (per <= 8) hipLaunchKernelGGL((se::topk_kernel<8, true, N>), grid, dim3(N), 0, st, a);
+    else if (per <= 16) hipLaunchKernelGGL((se::topk_kernel<16, true, N>), grid, dim3(N), 0, st, a);
+    else hipLaunchKernelGGL((se::topk_kernel<32, true, N>), grid, dim3(N), 0, st, a);
   } else {
     const int per = (n_items + se::kThreadsBig - 1) / se::kThreadsBig;
     if (per <= 4) SE_TOPK_LAUNCH(4, se::kThreadsBig);
