@@ -119,6 +119,33 @@ SE_DEV int wave_sum_i(int x) {
   return x;
 }
 
+// Exclusive prefix sum of v over the workgroup's NTH threads in thread order, and the total: a scan within each
+// wave by lane shifts, then the waves' totals through LDS (s_wsum: NTH / 64 ints). Two barriers; every thread of
+// the workgroup must call it, and s_wsum may be reused right after (the first barrier guards it).
+template <int NTH>
+SE_DEV int block_exscan(int v, int *s_wsum, int &total) {
+  constexpr int kWaves = NTH / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  __syncthreads();
+  if (lane == 63) s_wsum[wave] = incl;
+  __syncthreads();
+  int before = 0;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const int x = s_wsum[w];
+    before += w < wave ? x : 0;
+    total += x;
+  }
+  return before + incl - v;
+}
+
 SE_DEV bool blk_ok(int32_t blk, int32_t num_blocks) { return blk >= 0 && blk < num_blocks; }
 
 // ---- status ---------------------------------------------------------------------------------------------------

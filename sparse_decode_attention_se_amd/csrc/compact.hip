@@ -572,7 +572,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_plan(AppendArgs a) {
   __shared__ int s_slot[kMaxUnits];
   __shared__ int s_lb[kAppendMaxSeq];   // logical block sequence b lacks (-1 = none)
   __shared__ int s_pop[kAppendMaxSeq];  // free-stack index it pops from
-  __shared__ int s_scan[kAppendThreads];
+  __shared__ int s_wsum[kAppendThreads / 64];
   __shared__ int s_fail;
   const int units = a.B * a.n_kv;
   const int cap = a.max_blocks * a.page;
@@ -626,25 +626,19 @@ __global__ __launch_bounds__(kAppendThreads) void append_plan(AppendArgs a) {
     return;
   }
   for (int base = 0; base < a.B; base += kAppendThreads) {
-    int b = base + threadIdx.x;
-    int v = (b < a.B && s_lb[b] >= 0) ? 1 : 0;
-    s_scan[threadIdx.x] = v;
-    __syncthreads();
-    for (int off = 1; off < kAppendThreads; off <<= 1) {
-      int x = threadIdx.x >= off ? s_scan[threadIdx.x - off] : 0;
-      __syncthreads();
-      s_scan[threadIdx.x] += x;
-      __syncthreads();
-    }
+    const int b = base + threadIdx.x;
+    const int v = (b < a.B && s_lb[b] >= 0) ? 1 : 0;
+    int total;
+    const int before = block_exscan<kAppendThreads>(v, s_wsum, total);
     if (v) {
-      int idx = top0 - 1 - (carry + s_scan[threadIdx.x] - 1);
-      int blk = idx >= 0 ? a.free_blocks[idx] : -1;
+      const int idx = top0 - 1 - (carry + before);
+      const int blk = idx >= 0 ? a.free_blocks[idx] : -1;
       if (blk < 0 || blk >= a.num_blocks) atomicOr(&s_fail, 4);
       s_pop[b] = blk;
     }
-    carry += s_scan[kAppendThreads - 1];
-    __syncthreads();
+    carry += total;
   }
+  __syncthreads();  // s_fail and s_pop complete
   if (s_fail) {
     if (threadIdx.x == 0) raise(a.status, s_fail == 2 ? SE_DEV_INDEX : SE_DEV_CAPACITY);
     for (int unit = threadIdx.x; unit < units; unit += kAppendThreads) a.dst_row[unit] = -1;
@@ -708,7 +702,7 @@ SE_DEV int chunk_count(const ChunkArgs &a, int b) {
 __global__ __launch_bounds__(kAppendThreads) void chunk_plan(ChunkArgs a) {
   __shared__ int s_first[kAppendMaxSeq], s_last[kAppendMaxSeq], s_alloc[kAppendMaxSeq], s_need[kAppendMaxSeq];
   __shared__ int s_before[kAppendMaxSeq];
-  __shared__ int s_scan[kAppendThreads];
+  __shared__ int s_wsum[kAppendThreads / 64];
   __shared__ int s_fail;
   const int units = a.B * a.n_kv;
   const int cap = a.max_blocks * a.page;
@@ -762,17 +756,10 @@ __global__ __launch_bounds__(kAppendThreads) void chunk_plan(ChunkArgs a) {
   for (int base = 0; base < a.B; base += kAppendThreads) {
     const int b = base + threadIdx.x;
     const int v = b < a.B ? s_need[b] : 0;
-    s_scan[threadIdx.x] = v;
-    __syncthreads();
-    for (int off = 1; off < kAppendThreads; off <<= 1) {
-      const int x = threadIdx.x >= off ? s_scan[threadIdx.x - off] : 0;
-      __syncthreads();
-      s_scan[threadIdx.x] += x;
-      __syncthreads();
-    }
-    if (b < a.B) s_before[b] = carry + s_scan[threadIdx.x] - v;
-    carry += s_scan[kAppendThreads - 1];
-    __syncthreads();  // s_scan is rewritten by the next chunk of sequences
+    int total;
+    const int before = block_exscan<kAppendThreads>(v, s_wsum, total);
+    if (b < a.B) s_before[b] = carry + before;
+    carry += total;
   }
   if (threadIdx.x == 0 && carry > top0) s_fail |= 1;
   __syncthreads();

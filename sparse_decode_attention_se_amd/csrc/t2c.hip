@@ -39,7 +39,7 @@ __global__ __launch_bounds__(kThreads) void t2c_kernel(T2CArgs a) {
   int *s_gap_of = reinterpret_cast<int *>(s_prio + L);  // gap index of rank r
   short *s_size_of = reinterpret_cast<short *>(s_gap_of + L);  // its size
   unsigned char *s_fill = reinterpret_cast<unsigned char *>(s_size_of + L);
-  __shared__ int s_scan[kThreads];
+  __shared__ int s_wsum[kThreads / 64];
   __shared__ int s_m, s_bad, s_nq;
   const int unit = blockIdx.x, t = threadIdx.x;
   const int n = a.n_slots[unit];
@@ -111,15 +111,8 @@ __global__ __launch_bounds__(kThreads) void t2c_kernel(T2CArgs a) {
   const int per = (m + kThreads - 1) / kThreads;
   int mine = 0;
   for (int i = t * per; i < min(m, (t + 1) * per); ++i) mine += 1 + ((i < gaps && s_fill[i]) ? s_c[i + 1] - s_c[i] - 1 : 0);
-  s_scan[t] = mine;
-  __syncthreads();
-  for (int off = 1; off < kThreads; off <<= 1) {
-    int x = t >= off ? s_scan[t - off] : 0;
-    __syncthreads();
-    s_scan[t] += x;
-    __syncthreads();
-  }
-  const int expanded = s_scan[kThreads - 1];
+  int expanded;
+  const int before = block_exscan<kThreads>(mine, s_wsum, expanded);
   const int total = expanded + (cnt - m);
   if (total > a.out_stride) {
     if (t == 0) {
@@ -129,7 +122,7 @@ __global__ __launch_bounds__(kThreads) void t2c_kernel(T2CArgs a) {
     return;
   }
   int32_t *out = a.idx_out + (int64_t)unit * a.out_stride;
-  int o = s_scan[t] - mine;
+  int o = before;
   for (int i = t * per; i < min(m, (t + 1) * per); ++i) {
     out[o++] = s_c[i];
     if (i < gaps && s_fill[i])
