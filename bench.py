@@ -80,13 +80,14 @@ CALL_KERNELS = {
     "se_cache_append_chunk": ["chunk_plan", "chunk_write"],
     "se_page_bounds": ["pages_score", "pages_build"],
     "se_page_bounds_refresh": ["pages_refresh"],
+    "se_h2o_decode_evict": ["h2o_decode_unit"],
     "se_sparse_decode_attn": ["decode_partial", "decode_merge", "decode_cum", "decode_unit"],
 }
 CALL_SOURCES = {
     "se_window_score": "score.hip", "se_topk_select": "topk.hip", "se_token2chunk": "t2c.hip",
     "se_compact_evict": "compact.hip", "se_cache_append": "compact.hip", "se_cache_append_chunk": "compact.hip", "se_page_bounds": "pages.hip",
     "se_page_bounds_refresh": "pages.hip",
-    "se_sparse_decode_attn": "decode.hip",
+    "se_sparse_decode_attn": "decode.hip", "se_h2o_decode_evict": "decode.hip",
 }
 CSRC = os.path.join(ROOT, "sparse_decode_attention_se_amd", "csrc")
 
@@ -543,22 +544,17 @@ def setup_c4(se, WF, W, dev, status, steps):
         s = s % cfg.steps
         return [
             ("se_cache_append", lambda: se.se_cache_append(c, k_new[s], v_new[s], pos[s], status=status)),
-            ("se_sparse_decode_attn", lambda: se.se_sparse_decode_attn(c, q[s], h2o.out, scale=h2o.scale,
-                                                                       accumulate=True, status=status)),
-            ("se_topk_select", lambda: se.se_topk_select(c, c.cum_score, h2o.evict, h2o.evict_count,
-                                                         mode=se.SE_TOPK_SMALLEST, unit=se.SE_UNIT_SLOT, k=1,
-                                                         budget=cfg.budget, recent=cfg.recent, status=status)),
-            ("se_compact_evict", lambda: se.se_compact_evict(c, h2o.evict, h2o.evict_count,
-                                                             mode=se.SE_COMPACT_EVICT_SLOTS, status=status)),
+            ("se_h2o_decode_evict", lambda: se.se_h2o_decode_evict(c, q[s], h2o.out, h2o.evict, h2o.evict_count,
+                                                                   scale=h2o.scale, budget=cfg.budget,
+                                                                   recent=cfg.recent, status=status)),
         ]
 
     B, G, row = cfg.B, cfg.hkv, cfg.d * 2
     n = cfg.budget + 1
     alg = {
         "se_cache_append": {"bytes": 2 * B * G * row * 2},
-        "se_sparse_decode_attn": {"bytes": B * G * n * (2 * row + 4 + 8) + B * cfg.hq * cfg.d * (2 + 4)},
-        "se_topk_select": {"bytes": B * G * n * 8},
-        "se_compact_evict": {"bytes": B * G * 16},
+        # K and V rows, positions, cumulative scores read and written; queries and outputs; the eviction's writes
+        "se_h2o_decode_evict": {"bytes": B * G * n * (2 * row + 4 + 8) + B * cfg.hq * cfg.d * (2 + 4) + B * G * 28},
     }
     wl = Workload(cfg, B * n, alg, step)
 

@@ -273,6 +273,29 @@ int32_t se_sparse_decode_attn(se_cache_t *c, const void *q, const int32_t *sel_p
                               const se_decode_params_t *p, float *out, int32_t *status, void *ws, size_t ws_bytes,
                               se_stream_t stream);
 
+/* ---- H2O decode step: accumulate, then evict the lowest cumulative score ---------------------------------------
+ * SparseEngine page, "What it is": H2O keeps cumulative attention scores during generation and evicts physically by
+ * them. One call computes what these three calls in order compute, with the same results bit for bit:
+ *   se_sparse_decode_attn (every resident slot, accumulate != 0, max_slots = 0),
+ *   se_topk_select (SE_TOPK_SMALLEST, SE_UNIT_SLOT, k = 1, budget, recent, scores = cum_score,
+ *                   out_stride = 1) into evict_idx [B*n_kv] and evict_count [B*n_kv] (0 or 1),
+ *   se_compact_evict (SE_COMPACT_EVICT_SLOTS) of that list.
+ * When the unit's logits fit the single-workgroup decode (max_blocks * page * (n_q / n_kv) <= 38912 and
+ * max_blocks * page <= 9984), the choice and the eviction happen inside the decode's own workgroup, from the scores
+ * it has just updated (one launch instead of four); otherwise the three calls are made in turn. Needs cum_score and
+ * a slot stack (slot_cap > 0). Workspace: se_h2o_decode_evict_workspace_size bytes (0 on the single-workgroup path).
+ * Errors: those of the three calls.
+ */
+typedef struct {
+  float scale;
+  int32_t budget; /* evict only while ctx_len > budget */
+  int32_t recent; /* slots within `recent` positions of the newest resident one are never evicted */
+} se_h2o_params_t;
+
+size_t se_h2o_decode_evict_workspace_size(const se_cache_t *c, const se_h2o_params_t *p);
+int32_t se_h2o_decode_evict(se_cache_t *c, const void *q, const se_h2o_params_t *p, float *out, int32_t *evict_idx,
+                            int32_t *evict_count, int32_t *status, void *ws, size_t ws_bytes, se_stream_t stream);
+
 /* ---- decode attention without allocation -----------------------------------------------------------------------
  * For callers that cannot allocate device memory: code under HIP graph capture, tight serving loops, harnesses
  * that forbid hipMalloc. Computes exactly what se_sparse_decode_attn computes (the same kernels, the same

@@ -17,7 +17,7 @@ from ._lib import (SE_COMPACT_EVICT_SLOTS, SE_COMPACT_GATHER, SE_DEV_CAPACITY, S
 __all__ = [
     "DeviceCache", "SEError", "se_window_score", "se_topk_select", "se_token2chunk", "se_compact_evict",
     "se_cache_append", "se_cache_append_chunk", "se_page_bounds", "se_page_bounds_refresh", "se_sparse_decode_attn",
-    "se_sparse_decode_attn_noalloc", "se_status_read",
+    "se_sparse_decode_attn_noalloc", "se_h2o_decode_evict", "se_status_read",
     "se_version", "set_operand_checks", "SE_SCORE_CAUSAL", "SE_SCORE_BIDIR", "SE_TOPK_LARGEST", "SE_TOPK_SMALLEST", "SE_UNIT_SLOT",
     "SE_UNIT_PAGE", "SE_COMPACT_GATHER", "SE_COMPACT_EVICT_SLOTS", "SE_PAGES_BUILD", "SE_PAGES_SCORE",
     "SE_REFRESH_LAST_PAGE", "SE_REFRESH_FROM_PAGE", "SE_DEV_INDEX", "SE_DEV_CAPACITY",
@@ -351,6 +351,27 @@ def se_sparse_decode_attn(cache, q, out, *, scale, sel_pages=None, sel_count=Non
     _check("se_sparse_decode_attn", lib.se_sparse_decode_attn(C.byref(c), _ptr(q), _ptr(sel_pages), _ptr(sel_count),
                                                               C.byref(p), _ptr(out), _ptr(status), _ptr(ws), nb,
                                                               sp))
+
+
+def se_h2o_decode_evict(cache, q, out, evict_idx, evict_count, *, scale, budget, recent, status=None, stream=None):
+    """H2O's decode step after the append: accumulating decode over every resident slot, then the lowest
+    cumulative score outside the recent positions is evicted (evict_idx, evict_count: [B][n_kv] int32)."""
+    if _CHECKS[0]:
+        B, G, Hq, d, page, mb, nblk, pdt, dev = _dims(cache)
+        call = "se_h2o_decode_evict"
+        _need(call, "q", q, B * Hq * d, pdt, dev)
+        _need(call, "out", out, B * Hq * d, F32, dev)
+        _need(call, "evict_idx", evict_idx, B * G, I32, dev)
+        _need(call, "evict_count", evict_count, B * G, I32, dev)
+        _need(call, "status", status, 1, I32, dev, optional=True)
+    lib = _lib.load()
+    st, sp = _stream(stream)
+    c = cache.desc()
+    p = _lib.se_h2o_params_t(scale, budget, recent)
+    nb = lib.se_h2o_decode_evict_workspace_size(C.byref(c), C.byref(p))
+    ws = _workspace(nb, cache.device, stream)
+    _check("se_h2o_decode_evict", lib.se_h2o_decode_evict(C.byref(c), _ptr(q), C.byref(p), _ptr(out), _ptr(evict_idx),
+                                                          _ptr(evict_count), _ptr(status), _ptr(ws), nb, sp))
 
 
 def se_sparse_decode_attn_noalloc(cache, q, out, *, scale, sel_pages=None, sel_count=None, max_sel=0, max_slots=0,

@@ -58,6 +58,10 @@ class se_decode_params_t(C.Structure):
                 ("accumulate", I32)]
 
 
+class se_h2o_params_t(C.Structure):
+    _fields_ = [("scale", C.c_float), ("budget", I32), ("recent", I32)]
+
+
 EXPORTS = {
     "se_window_score_workspace_size": (C.c_size_t, [C.POINTER(se_cache_t), C.POINTER(se_window_params_t)]),
     "se_window_score": (I32, [C.POINTER(se_cache_t), P, P, C.POINTER(se_window_params_t), P, P, P, C.c_size_t, P]),
@@ -79,6 +83,9 @@ EXPORTS = {
                                     C.c_size_t, P]),
     "se_sparse_decode_attn_noalloc": (I32, [C.POINTER(se_cache_t), P, P, P, C.POINTER(se_decode_params_t), P, P,
                                             P]),
+    "se_h2o_decode_evict_workspace_size": (C.c_size_t, [C.POINTER(se_cache_t), C.POINTER(se_h2o_params_t)]),
+    "se_h2o_decode_evict": (I32, [C.POINTER(se_cache_t), P, C.POINTER(se_h2o_params_t), P, P, P, P, P, C.c_size_t,
+                                  P]),
     "se_status_read": (I32, [P, C.POINTER(I32), I32, P]),
     "se_error_string": (C.c_char_p, [I32]),
     "se_version": (C.c_char_p, []),

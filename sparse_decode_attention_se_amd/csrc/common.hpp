@@ -148,6 +148,12 @@ SE_DEV int block_exscan(int v, int *s_wsum, int &total) {
 
 SE_DEV bool blk_ok(int32_t blk, int32_t num_blocks) { return blk >= 0 && blk < num_blocks; }
 
+// fp32 -> u32 with the same order (unsigned comparison), -0 taken as +0: the selection keys of top-K
+SE_DEV uint32_t orderable(float f) {
+  uint32_t u = __float_as_uint(f == 0.f ? 0.f : f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
 // ---- status ---------------------------------------------------------------------------------------------------
 SE_DEV void raise(int32_t *status, int32_t bit) {
   if (status) atomicOr(status, bit);

@@ -81,6 +81,9 @@ struct DecodeArgs {
   int32_t *status;
   int32_t n_kv, page, max_blocks, num_blocks, sel_stride, rows_bound, chunk_rows, nchunk;
   float scale_log2;
+  // H2O's eviction inside decode_unit: the cache's mutable maps, the chosen slot and count per unit
+  int32_t *ev_pos, *ev_stack, *ev_top, *ev_ctx, *ev_idx, *ev_count;
+  int32_t ev_cap, ev_budget, ev_recent;
 };
 
 // number of view rows of a unit, and the slot of view row r (-1 if the row is not in the view)
@@ -592,8 +595,12 @@ constexpr int U = 4;   // wave-loads per lane-row and step: 16 rows (8 KiB of K 
 constexpr int UG = 4;  // rows per lane-row whose scores are live at once
 constexpr int NB = 4;  // K/V buffers: three steps in flight while one is computed
 
-template <int DTYPE, int R>
-__global__ __launch_bounds__(kUnitThreads) void decode_unit(DecodeArgs a) {
+// With EV, H2O's eviction follows in the same workgroup (se_h2o_decode_evict): from the scores just updated, the
+// resident slot with the lowest cumulative score among those at least `recent` positions below the newest resident
+// one (ties: the higher position) is freed when the unit holds more than `budget` tokens: the selection of top-K's
+// smallest mode with k = 1 and the slot eviction, on the same values.
+template <int DTYPE, int R, bool EV>
+SE_DEV void decode_unit_body(const DecodeArgs &a) {
   using V = Vec<DTYPE>;
   constexpr int EPL = V::EPL;
   constexpr int D = 16 * EPL;
@@ -609,6 +616,8 @@ __global__ __launch_bounds__(kUnitThreads) void decode_unit(DecodeArgs a) {
   __shared__ float s_lg[kUnitLdsFloats];
   __shared__ float s_ml[kUnitWaves][R][2];
   __shared__ float s_acc[R][D];
+  __shared__ int s_evmx[EV ? kUnitWaves : 1];
+  __shared__ uint64_t s_ev64[EV ? kUnitWaves : 1];
 
   u32x4 q[R];
 #pragma unroll
@@ -638,6 +647,12 @@ __global__ __launch_bounds__(kUnitThreads) void decode_unit(DecodeArgs a) {
   const int32_t *bt = a.bt + (int64_t)b * a.max_blocks;
   const int32_t *pos = a.pos + (int64_t)unit * cap;
   float *cum = a.cum + (int64_t)unit * cap;
+  // EV: the unit's token count and slot-stack top, which only this workgroup changes during the call
+  int ctxv = 0, topv = 0;
+  if constexpr (EV) {
+    ctxv = a.ev_ctx[unit];
+    topv = a.ev_top[unit];
+  }
 
   // Rows are resolved SUB at a time, lane i holding row wr0 + SUB k + i of sub-chunk k (pool row, or -1 when not
   // resident); a step takes its rows from that register with ds_bpermute. The block-table and position loads of
@@ -649,9 +664,11 @@ __global__ __launch_bounds__(kUnitThreads) void decode_unit(DecodeArgs a) {
     blk = bt[rr / a.page];
     ps = pos[rr];
   };
+  int mxp = -1;  // EV: the newest position among this lane's resolved rows
   auto res_make = [&](int k, int blk, int ps) {
     const int r = wr0 + SUB * k + lane;
     int v = -1;
+    if (EV && lane < SUB && r < wr1) mxp = max(mxp, ps);
     if (lane < SUB && r < wr1 && ps >= 0) {
       if (blk_ok(blk, a.num_blocks)) v = (blk * a.n_kv + g) * a.page + r % a.page;
       else bad = true;
@@ -928,12 +945,25 @@ __global__ __launch_bounds__(kUnitThreads) void decode_unit(DecodeArgs a) {
       m[3 % R] = row16_bcast<3 % R>(ml), l[3 % R] = row16_bcast<3 % R>(lsum);
     }
   }
-  // this thread's cumulative scores, loaded while the waves merge
+  // this thread's cumulative scores, loaded while the waves merge (with EV also its slots' positions, -1 past the
+  // view, and the unit's token count)
   float cv[kCum];
 #pragma unroll
   for (int k = 0; k < kCum; ++k) {
     const int r = k * kUnitThreads + threadIdx.x;
     cv[k] = cum[r < rows ? r : 0];
+  }
+  int pv[EV ? kCum : 1];
+  if constexpr (EV) {
+#pragma unroll
+    for (int k = 0; k < kCum; ++k) {
+      const int r = k * kUnitThreads + threadIdx.x;
+      const int p = pos[r < rows ? r : 0];
+      pv[k] = r < rows ? p : -1;
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) mxp = max(mxp, __shfl_xor(mxp, o));
+    if (lane == 0) s_evmx[wave] = mxp;  // published with the waves' statistics below
   }
 
   // merge the four lane-rows of each wave, then the waves: max and sum first, then acc one wave at a time
@@ -987,7 +1017,10 @@ __global__ __launch_bounds__(kUnitThreads) void decode_unit(DecodeArgs a) {
   float *out = a.out + (((int64_t)b * a.n_kv + g) * R) * D;
   for (int i = threadIdx.x; i < R * D; i += kUnitThreads) out[i] = s_acc[i / D][i % D] * iL[i / D];
 
-  // cum[slot] += the group's summed weight on the slot; free slots (logit -inf) keep their value
+  // cum[slot] += the group's summed weight on the slot; free slots (logit -inf) keep their value. With EV the
+  // stores wait until the eviction has been chosen from the new values (the chosen slot's score becomes 0), so no
+  // barrier below waits for them.
+  uint32_t inview = 0;  // bit k: slot k * kUnitThreads + threadIdx.x gets a new score
 #pragma unroll
   for (int k = 0; k < kCum; ++k) {
     const int r = k * kUnitThreads + threadIdx.x;
@@ -996,8 +1029,71 @@ __global__ __launch_bounds__(kUnitThreads) void decode_unit(DecodeArgs a) {
     float sum = 0.f;
 #pragma unroll
     for (int h = 0; h < R; ++h) sum += __builtin_amdgcn_exp2f(s_lg[r * R + h] - M[h]) * iL[h];
-    cum[r] = cv[k] + sum;
+    cv[k] += sum;
+    if constexpr (EV) inview |= 1u << k;
+    else cum[r] = cv[k];
   }
+  if constexpr (EV) {
+    // the newest resident position over every slot below n_slots (as in top-K), from the rows the waves resolved
+    int mx = -1;
+#pragma unroll
+    for (int w = 0; w < kUnitWaves; ++w) mx = max(mx, s_evmx[w]);
+    const int limit = mx - a.ev_recent;
+    // the largest (~key, ~tie key) pair, as top-K's k = 1 path packs it (a candidate's pair is never 0); 0 for
+    // slots that are not candidates
+    const bool over = ctxv - a.ev_budget > 0;
+    uint64_t pr[kCum];
+    uint64_t best = 0;
+#pragma unroll
+    for (int k = 0; k < kCum; ++k) {
+      const bool cand = over && pv[k] >= 0 && pv[k] <= limit;
+      pr[k] = cand ? ((uint64_t)~orderable(cv[k]) << 32) | (uint32_t)~(0x7fffffffu - (uint32_t)pv[k]) : 0;
+      best = pr[k] > best ? pr[k] : best;
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)best, o);
+      const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(best >> 32), o);
+      const uint64_t y = ((uint64_t)hi << 32) | lo;
+      best = y > best ? y : best;
+    }
+    if (lane == 0) s_ev64[wave] = best;
+    // only LDS is exchanged here: wait for this wave's LDS write, not for its global accesses, then meet
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+    for (int w = 0; w < kUnitWaves; ++w) best = s_ev64[w] > best ? s_ev64[w] : best;
+    // the chosen slot's thread frees it under the slot eviction's rules for one entry (a stack top outside
+    // [0, cap) raises SE_DEV_CAPACITY and changes nothing); every other new score is stored as it is
+    const bool room = topv >= 0 && topv < a.ev_cap;
+#pragma unroll
+    for (int k = 0; k < kCum; ++k) {
+      const int r = k * kUnitThreads + threadIdx.x;
+      const bool chosen = best != 0 && pr[k] == best;
+      if ((inview >> k) & 1u) cum[r] = chosen && room ? 0.f : cv[k];
+      if (!chosen) continue;
+      a.ev_idx[unit] = r;
+      if (!room) {
+        raise(a.status, SE_DEV_CAPACITY);
+      } else {
+        a.ev_pos[(int64_t)unit * cap + r] = -1;
+        if (!((inview >> k) & 1u)) cum[r] = 0.f;
+        a.ev_stack[(int64_t)unit * a.ev_cap + topv] = r;
+        a.ev_top[unit] = topv + 1;
+        a.ev_ctx[unit] = ctxv - 1;
+      }
+    }
+    if (threadIdx.x == 0) a.ev_count[unit] = best != 0 ? 1 : 0;
+  }
+}
+
+template <int DTYPE, int R>
+__global__ __launch_bounds__(kUnitThreads) void decode_unit(DecodeArgs a) {
+  decode_unit_body<DTYPE, R, false>(a);
+}
+// the same with H2O's bottom-1 eviction after the cumulative scores (se_h2o_decode_evict)
+template <int DTYPE, int R>
+__global__ __launch_bounds__(kUnitThreads) void h2o_decode_unit(DecodeArgs a) {
+  decode_unit_body<DTYPE, R, true>(a);
 }
 
 struct Plan {
@@ -1035,7 +1131,8 @@ Plan make_plan(const se_cache_t *c, const se_decode_params_t *p, int has_sel) {
 template <int DTYPE, int R>
 void launch(const DecodeArgs &a, int units, int nchunk, bool unit_path, hipStream_t st) {
   if (unit_path) {
-    hipLaunchKernelGGL((decode_unit<DTYPE, R>), dim3(units), dim3(kUnitThreads), 0, st, a);
+    if (a.ev_idx) hipLaunchKernelGGL((h2o_decode_unit<DTYPE, R>), dim3(units), dim3(kUnitThreads), 0, st, a);
+    else hipLaunchKernelGGL((decode_unit<DTYPE, R>), dim3(units), dim3(kUnitThreads), 0, st, a);
     return;
   }
   hipLaunchKernelGGL((decode_partial<DTYPE, R>), dim3(nchunk, units), dim3(kThreads), 0, st, a);
@@ -1069,9 +1166,15 @@ extern "C" size_t se_sparse_decode_attn_workspace_size(const se_cache_t *c, cons
 
 namespace {
 
+// H2O's eviction after an accumulating decode (se_h2o_decode_evict); null for a plain decode call
+struct EvictSpec {
+  int32_t budget, recent;
+  int32_t *idx, *count;
+};
+
 int32_t decode_call(se_cache_t *c, const void *q, const int32_t *sel_pages, const int32_t *sel_count,
                     const se_decode_params_t *p, float *out, int32_t *status, void *ws, size_t ws_bytes,
-                    se_stream_t stream) {
+                    se_stream_t stream, const EvictSpec *ev = nullptr) {
   int32_t rc = se_host::check_cache(c);
   if (rc != SE_OK) return rc;
   if (!q || !out || !p) return SE_ERR_NULL;
@@ -1113,10 +1216,36 @@ int32_t decode_call(se_cache_t *c, const void *q, const int32_t *sel_pages, cons
   a.chunk_rows = pl.chunk_rows;
   a.nchunk = pl.nchunk;
   a.scale_log2 = p->scale * 1.4426950408889634f;
+  const bool fused = ev && pl.unit_path;  // the eviction inside the single-workgroup decode
+  a.ev_pos = fused ? c->pos_map : nullptr;
+  a.ev_stack = fused ? c->slot_stack : nullptr;
+  a.ev_top = fused ? c->slot_top : nullptr;
+  a.ev_ctx = fused ? c->ctx_len : nullptr;
+  a.ev_idx = fused ? ev->idx : nullptr;
+  a.ev_count = fused ? ev->count : nullptr;
+  a.ev_cap = fused ? c->slot_cap : 0;
+  a.ev_budget = fused ? ev->budget : 0;
+  a.ev_recent = fused ? ev->recent : 0;
   const int R = c->n_q / c->n_kv;
   hipStream_t st = (hipStream_t)stream;
-  if (c->dtype == SE_DTYPE_BF16) return se::dispatch_r<SE_DTYPE_BF16>(R, a, pl.units, pl.nchunk, pl.unit_path, st);
-  return se::dispatch_r<SE_DTYPE_F32>(R, a, pl.units, pl.nchunk, pl.unit_path, st);
+  rc = c->dtype == SE_DTYPE_BF16 ? se::dispatch_r<SE_DTYPE_BF16>(R, a, pl.units, pl.nchunk, pl.unit_path, st)
+                                 : se::dispatch_r<SE_DTYPE_F32>(R, a, pl.units, pl.nchunk, pl.unit_path, st);
+  if (rc != SE_OK || !ev || fused) return rc;
+  // the view is too long for one workgroup's LDS: bottom-1 and the slot eviction as their own calls
+  se_topk_params_t tp{};
+  tp.mode = SE_TOPK_SMALLEST;
+  tp.unit = SE_UNIT_SLOT;
+  tp.k = 1;
+  tp.budget = ev->budget;
+  tp.recent = ev->recent;
+  tp.score_stride = c->max_blocks * c->page;
+  tp.out_stride = 1;
+  rc = se_topk_select(c, c->cum_score, &tp, ev->idx, ev->count, status, nullptr, 0, stream);
+  if (rc != SE_OK) return rc;
+  se_compact_params_t cp{};
+  cp.mode = SE_COMPACT_EVICT_SLOTS;
+  cp.idx_stride = 1;
+  return se_compact_evict(c, ev->idx, ev->count, &cp, status, nullptr, 0, stream);
 }
 
 }  // namespace
@@ -1125,6 +1254,34 @@ extern "C" int32_t se_sparse_decode_attn(se_cache_t *c, const void *q, const int
                                          const int32_t *sel_count, const se_decode_params_t *p, float *out,
                                          int32_t *status, void *ws, size_t ws_bytes, se_stream_t stream) {
   return decode_call(c, q, sel_pages, sel_count, p, out, status, ws, ws_bytes, stream);
+}
+
+namespace {
+se_decode_params_t h2o_decode_params(const se_h2o_params_t *p) {
+  se_decode_params_t d{};
+  d.scale = p->scale;
+  d.accumulate = 1;
+  return d;
+}
+}  // namespace
+
+extern "C" size_t se_h2o_decode_evict_workspace_size(const se_cache_t *c, const se_h2o_params_t *p) {
+  if (!p) return 0;
+  const se_decode_params_t d = h2o_decode_params(p);
+  return se_sparse_decode_attn_workspace_size(c, &d, 0);
+}
+
+extern "C" int32_t se_h2o_decode_evict(se_cache_t *c, const void *q, const se_h2o_params_t *p, float *out,
+                                       int32_t *evict_idx, int32_t *evict_count, int32_t *status, void *ws,
+                                       size_t ws_bytes, se_stream_t stream) {
+  int32_t rc = se_host::check_cache(c);
+  if (rc != SE_OK) return rc;
+  if (!p || !evict_idx || !evict_count) return SE_ERR_NULL;
+  if (!c->cum_score || !c->slot_stack || !c->slot_top || c->slot_cap <= 0) return SE_ERR_NULL;
+  if (p->budget < 0 || p->recent < 0) return SE_ERR_PARAM;
+  const se_decode_params_t d = h2o_decode_params(p);
+  const EvictSpec ev{p->budget, p->recent, evict_idx, evict_count};
+  return decode_call(c, q, nullptr, nullptr, &d, out, status, ws, ws_bytes, stream, &ev);
 }
 
 // ---- the allocation-free variant ------------------------------------------------------------------------------

@@ -24,11 +24,6 @@ constexpr int kThreadsBig = 1024, kThreadsSmall = 256;
 #define SE_TOPK_ONE_THREADS 512  // workgroup size for k = 1 over more than 1024 items (fewer waves per barrier)
 #endif
 
-SE_DEV uint32_t orderable(float f) {
-  uint32_t u = __float_as_uint(f == 0.f ? 0.f : f);  // -0 == +0
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
 struct TopkArgs {
   const float *scores;
   const int32_t *pos, *n_slots, *ctx;

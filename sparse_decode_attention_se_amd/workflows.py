@@ -12,8 +12,8 @@ import torch
 
 from . import (SE_COMPACT_EVICT_SLOTS, SE_COMPACT_GATHER, SE_PAGES_BUILD, SE_PAGES_SCORE, SE_REFRESH_FROM_PAGE,
                SE_REFRESH_LAST_PAGE, SE_SCORE_BIDIR, SE_SCORE_CAUSAL, SE_TOPK_LARGEST, SE_TOPK_SMALLEST, SE_UNIT_PAGE,
-               SE_UNIT_SLOT, se_cache_append, se_cache_append_chunk, se_compact_evict, se_page_bounds, se_page_bounds_refresh,
-               se_sparse_decode_attn, se_token2chunk, se_topk_select, se_window_score)
+               SE_UNIT_SLOT, se_cache_append, se_cache_append_chunk, se_compact_evict, se_h2o_decode_evict, se_page_bounds,
+               se_page_bounds_refresh, se_sparse_decode_attn, se_token2chunk, se_topk_select, se_window_score)
 
 
 def _dims(cache):
@@ -245,16 +245,24 @@ class DecodeStep:
 
 
 class H2OStep(DecodeStep):
-    """Append -> decode with cumulative scores -> evict the lowest score outside the recent positions."""
+    """Append -> decode with cumulative scores -> evict the lowest score outside the recent positions.
 
-    def __init__(self, cache, *, scale, budget, recent, status=None):
+    The last three are one call, se_h2o_decode_evict; with fused=False they are made as se_sparse_decode_attn,
+    se_topk_select and se_compact_evict (the same results)."""
+
+    def __init__(self, cache, *, scale, budget, recent, status=None, fused=True):
         super().__init__(cache, scale=scale, accumulate=True, status=status)
         B, G, S, d = _dims(cache)
-        self.budget, self.recent = budget, recent
+        self.budget, self.recent, self.fused = budget, recent, fused
         self.evict = torch.zeros((B, G, 1), dtype=torch.int32, device=cache.device)
         self.evict_count = torch.zeros((B, G), dtype=torch.int32, device=cache.device)
 
     def run(self, k_new, v_new, pos, q):
+        if self.fused:
+            se_cache_append(self.cache, k_new, v_new, pos, status=self.status)
+            se_h2o_decode_evict(self.cache, q, self.out, self.evict, self.evict_count, scale=self.scale,
+                                budget=self.budget, recent=self.recent, status=self.status)
+            return self.out
         super().run(k_new, v_new, pos, q)
         se_topk_select(self.cache, self.cache.cum_score, self.evict, self.evict_count, mode=SE_TOPK_SMALLEST,
                        unit=SE_UNIT_SLOT, k=1, budget=self.budget, recent=self.recent, status=self.status)

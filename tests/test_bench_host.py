@@ -82,7 +82,7 @@ def test_every_workload_has_a_traffic_summary_for_its_dominant_call():
     import workloads as W
 
     dominant = {"c1_snapkv_llama8b": "se_window_score", "c2_kara_qwen3_4b": "se_sparse_decode_attn",
-                "c3_quest_128k": "se_sparse_decode_attn", "c4_h2o": "se_sparse_decode_attn",
+                "c3_quest_128k": "se_sparse_decode_attn", "c4_h2o": "se_h2o_decode_evict",
                 "c5_quest_128k_append": "se_sparse_decode_attn", "c6_prune_llama8b": "se_window_score",
                 "c7_h2o_prefill_llama8b": "se_window_score", "c8_kvllm_policy_qwen3_4b": "se_sparse_decode_attn"}
     assert set(dominant) == {c.name for c in W.FULL.values()} - {W.C0.name}
