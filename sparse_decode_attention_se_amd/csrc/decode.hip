@@ -1039,17 +1039,24 @@ SE_DEV void decode_unit_body(const DecodeArgs &a) {
 #pragma unroll
     for (int w = 0; w < kUnitWaves; ++w) mx = max(mx, s_evmx[w]);
     const int limit = mx - a.ev_recent;
-    // the largest (~key, ~tie key) pair, as top-K's k = 1 path packs it (a candidate's pair is never 0); 0 for
-    // slots that are not candidates
+    // this thread's candidate with the lowest score (ties: the higher position), by float comparisons (scores are
+    // not NaN, and -0 equals +0 as in top-K's keys); then the largest (~key, ~tie key) pair over the workgroup,
+    // packed as top-K's k = 1 path packs it (a candidate's pair is never 0)
     const bool over = ctxv - a.ev_budget > 0;
-    uint64_t pr[kCum];
-    uint64_t best = 0;
+    float bv = 0.f;
+    int bp = -1, br = -1;
 #pragma unroll
     for (int k = 0; k < kCum; ++k) {
       const bool cand = over && pv[k] >= 0 && pv[k] <= limit;
-      pr[k] = cand ? ((uint64_t)~orderable(cv[k]) << 32) | (uint32_t)~(0x7fffffffu - (uint32_t)pv[k]) : 0;
-      best = pr[k] > best ? pr[k] : best;
+      const bool better = bp < 0 || cv[k] < bv || (cv[k] == bv && pv[k] > bp);
+      if (cand && better) {
+        bv = cv[k];
+        bp = pv[k];
+        br = k * kUnitThreads + threadIdx.x;
+      }
     }
+    const uint64_t mine = bp >= 0 ? ((uint64_t)~orderable(bv) << 32) | (uint32_t)~(0x7fffffffu - (uint32_t)bp) : 0;
+    uint64_t best = mine;
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) {
       const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)best, o);
@@ -1065,10 +1072,11 @@ SE_DEV void decode_unit_body(const DecodeArgs &a) {
     // the chosen slot's thread frees it under the slot eviction's rules for one entry (a stack top outside
     // [0, cap) raises SE_DEV_CAPACITY and changes nothing); every other new score is stored as it is
     const bool room = topv >= 0 && topv < a.ev_cap;
+    const int chosen_r = best != 0 && mine == best ? br : -1;  // this thread's slot, if it is the one chosen
 #pragma unroll
     for (int k = 0; k < kCum; ++k) {
       const int r = k * kUnitThreads + threadIdx.x;
-      const bool chosen = best != 0 && pr[k] == best;
+      const bool chosen = r == chosen_r;
       if ((inview >> k) & 1u) cum[r] = chosen && room ? 0.f : cv[k];
       if (!chosen) continue;
       a.ev_idx[unit] = r;
