@@ -240,8 +240,9 @@ class Workload:
         self.outputs = outputs or {}  # named device tensors a step writes besides the cache (for tests)
 
 
-def per_call_marks(wl, args, prepare, calls):
-    """[(start, end) event per call] for each of args.steps restored steps queued behind a device spin."""
+def per_call_marks(wl, args, prepare, calls, first):
+    """[(start, end) event per call] for each of args.steps steps (numbered from `first`; restored first when the
+    workload restores) queued behind a device spin."""
     import torch
 
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -252,13 +253,15 @@ def per_call_marks(wl, args, prepare, calls):
     cycles_per_ms = (1 << 22) / max(e0.elapsed_time(e1), 1e-3)
     spin_ms = 4.0
     marks = []
-    i = 0
+    i = tried = 0  # a retried step of an evolving cache takes the next step's inputs (its own were consumed)
     while i < args.steps:
         prepare()
         torch.cuda.synchronize()
         torch.cuda._sleep(int(spin_ms * cycles_per_ms))
         m = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in calls]
-        for (name, fn), (a, b) in zip(wl.step(args.warmup + i), m):
+        step = first + (i if wl.restore else tried)
+        tried += 1
+        for (name, fn), (a, b) in zip(wl.step(step), m):
             a.record()
             fn()
             b.record()
@@ -930,12 +933,14 @@ def main():
                 e1.record()
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t_start
-    if wl.restore and not args.eager:
-        # Per-call times: the restored steps again, each behind a device spin long enough that the host has queued
-        # the whole step before the first call starts, so that the events around each call see only device time
-        # (with small calls the device would otherwise wait for the host between them). A spin that ended before
-        # the host had queued the step is doubled and the step run again.
-        marks = per_call_marks(wl, args, prepare, calls)
+    if not args.eager:
+        # Per-call times: K more steps (the restored steps again, or the evolving cache's next steps), each behind
+        # a device spin long enough that the host has queued the whole step before the first call starts, so that
+        # the events around each call see only device time (with small calls the device would otherwise wait for
+        # the host between them). A spin that ended before the host had queued the step is doubled and the step
+        # run again.
+        marks = per_call_marks(wl, args, prepare, calls,
+                               args.warmup if wl.restore else args.warmup + args.steps)
     se.set_operand_checks(True)
     require_clean_status(se, status, "the timed steps")
     # per entry point: its time per step (summed over its calls when a step makes several, as C7's chunks do)
