@@ -67,6 +67,17 @@ def test_host_validation_without_device():
     assert lib.se_compact_evict(C.byref(c), 16, 16, C.byref(cp), None, None, 0, None) == _lib.SE_ERR_PARAM
     cp = _lib.se_compact_params_t(0, 0, 8)  # GATHER needs its small workspace
     assert lib.se_compact_evict(C.byref(c), 16, 16, C.byref(cp), None, None, 0, None) == _lib.SE_ERR_WORKSPACE
+    # H2O's fused step: needs the cumulative scores and a slot stack, and non-negative budget and recent
+    hp = _lib.se_h2o_params_t(0.1, 8, 4)
+    assert lib.se_h2o_decode_evict(C.byref(c), 16, C.byref(hp), 16, 16, 16, None, None, 0, None) == _lib.SE_ERR_NULL
+    c.cum_score = c.slot_stack = c.slot_top = 16
+    c.slot_cap = 4
+    assert lib.se_h2o_decode_evict(C.byref(c), 16, C.byref(hp), 16, None, 16, None, None, 0, None) == _lib.SE_ERR_NULL
+    hp = _lib.se_h2o_params_t(0.1, -1, 4)
+    assert lib.se_h2o_decode_evict(C.byref(c), 16, C.byref(hp), 16, 16, 16, None, None, 0, None) == _lib.SE_ERR_PARAM
+    # 64 slots per unit fit one workgroup's LDS: the fused path needs no workspace
+    hp = _lib.se_h2o_params_t(0.1, 8, 4)
+    assert lib.se_h2o_decode_evict_workspace_size(C.byref(c), C.byref(hp)) == 0
 
 
 def test_workspace_sizes_are_host_only():
