@@ -562,17 +562,19 @@ struct AppendArgs {
   int32_t B, n_kv, page, max_blocks, num_blocks, slot_cap, row_bytes;
 };
 
-constexpr int kAppendThreads = 1024;
+constexpr int kAppendThreads = 1024;  // plan workgroup; 256 threads when the call has at most 256 units or sequences
+constexpr int kAppendThreadsSmall = 256;
 constexpr int kMaxUnits = 4096;
 constexpr int kAppendMaxSeq = 2048;
 
 // Plan and maps, one workgroup: decide every slot and block first, then commit only if the whole call fits, and
 // hand each unit's destination pool row to append_copy through the workspace (-1: nothing to copy).
-__global__ __launch_bounds__(kAppendThreads) void append_plan(AppendArgs a) {
+template <int NTH>
+__global__ __launch_bounds__(NTH) void append_plan(AppendArgs a) {
   __shared__ int s_slot[kMaxUnits];
   __shared__ int s_lb[kAppendMaxSeq];   // logical block sequence b lacks (-1 = none)
   __shared__ int s_pop[kAppendMaxSeq];  // free-stack index it pops from
-  __shared__ int s_wsum[kAppendThreads / 64];
+  __shared__ int s_wsum[NTH / 64];
   __shared__ int s_fail;
   const int units = a.B * a.n_kv;
   const int cap = a.max_blocks * a.page;
@@ -580,7 +582,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_plan(AppendArgs a) {
   // loads that depend on nothing go out first: the free-stack top and each unit's high-water mark
   const int top0 = *a.free_top;
   __syncthreads();
-  for (int unit = threadIdx.x; unit < units; unit += kAppendThreads) {
+  for (int unit = threadIdx.x; unit < units; unit += NTH) {
     int top = a.slot_cap > 0 ? a.slot_top[unit] : 0;
     const int hw = a.n_slots[unit];
     if (top < 0 || top > a.slot_cap) {
@@ -599,12 +601,12 @@ __global__ __launch_bounds__(kAppendThreads) void append_plan(AppendArgs a) {
   // token per head can only enter one new block; heads that lack different blocks are an index error). One
   // thread per head; the sequence's answer is gathered with LDS min/max.
   __shared__ int s_lbmin[kAppendMaxSeq];
-  for (int b = threadIdx.x; b < a.B; b += kAppendThreads) {
+  for (int b = threadIdx.x; b < a.B; b += NTH) {
     s_lb[b] = -1;
     s_lbmin[b] = 0x7fffffff;
   }
   __syncthreads();
-  for (int unit = threadIdx.x; unit < units; unit += kAppendThreads) {
+  for (int unit = threadIdx.x; unit < units; unit += NTH) {
     const int b = unit / a.n_kv;
     const int lb = s_slot[unit] / a.page;
     const int cur = a.bt[(int64_t)b * a.max_blocks + lb];
@@ -615,21 +617,21 @@ __global__ __launch_bounds__(kAppendThreads) void append_plan(AppendArgs a) {
     }
   }
   __syncthreads();
-  for (int b = threadIdx.x; b < a.B; b += kAppendThreads)
+  for (int b = threadIdx.x; b < a.B; b += NTH)
     if (s_lb[b] >= 0 && s_lbmin[b] != s_lb[b]) atomicOr(&s_fail, 2);
   __syncthreads();
   // exclusive scan of the pops over sequences, in sequence order
   int carry = 0;
   if (top0 < 0 || top0 > a.num_blocks) {
     if (threadIdx.x == 0) raise(a.status, SE_DEV_CAPACITY);
-    for (int unit = threadIdx.x; unit < units; unit += kAppendThreads) a.dst_row[unit] = -1;
+    for (int unit = threadIdx.x; unit < units; unit += NTH) a.dst_row[unit] = -1;
     return;
   }
-  for (int base = 0; base < a.B; base += kAppendThreads) {
+  for (int base = 0; base < a.B; base += NTH) {
     const int b = base + threadIdx.x;
     const int v = (b < a.B && s_lb[b] >= 0) ? 1 : 0;
     int total;
-    const int before = block_exscan<kAppendThreads>(v, s_wsum, total);
+    const int before = block_exscan<NTH>(v, s_wsum, total);
     if (v) {
       const int idx = top0 - 1 - (carry + before);
       const int blk = idx >= 0 ? a.free_blocks[idx] : -1;
@@ -641,14 +643,14 @@ __global__ __launch_bounds__(kAppendThreads) void append_plan(AppendArgs a) {
   __syncthreads();  // s_fail and s_pop complete
   if (s_fail) {
     if (threadIdx.x == 0) raise(a.status, s_fail == 2 ? SE_DEV_INDEX : SE_DEV_CAPACITY);
-    for (int unit = threadIdx.x; unit < units; unit += kAppendThreads) a.dst_row[unit] = -1;
+    for (int unit = threadIdx.x; unit < units; unit += NTH) a.dst_row[unit] = -1;
     return;  // all or nothing: nothing was written
   }
-  for (int b = threadIdx.x; b < a.B; b += kAppendThreads)
+  for (int b = threadIdx.x; b < a.B; b += NTH)
     if (s_lb[b] >= 0) a.bt[(int64_t)b * a.max_blocks + s_lb[b]] = s_pop[b];
   __syncthreads();
   if (threadIdx.x == 0) *a.free_top = top0 - carry;
-  for (int unit = threadIdx.x; unit < units; unit += kAppendThreads) {
+  for (int unit = threadIdx.x; unit < units; unit += NTH) {
     int b = unit / a.n_kv;
     int slot = s_slot[unit];
     int top = a.slot_cap > 0 ? a.slot_top[unit] : 0;
@@ -699,10 +701,11 @@ SE_DEV int chunk_count(const ChunkArgs &a, int b) {
 // One workgroup: per sequence the logical blocks its heads' new slots [n, n + T) need beyond the allocated prefix;
 // pops for them in (sequence, logical block) order; then, only if everything fits, the commit: block table,
 // free-stack top, n_slots and ctx_len. chunk_write copies the rows afterwards.
-__global__ __launch_bounds__(kAppendThreads) void chunk_plan(ChunkArgs a) {
+template <int NTH>
+__global__ __launch_bounds__(NTH) void chunk_plan(ChunkArgs a) {
   __shared__ int s_first[kAppendMaxSeq], s_last[kAppendMaxSeq], s_alloc[kAppendMaxSeq], s_need[kAppendMaxSeq];
   __shared__ int s_before[kAppendMaxSeq];
-  __shared__ int s_wsum[kAppendThreads / 64];
+  __shared__ int s_wsum[NTH / 64];
   __shared__ int s_fail;
   const int units = a.B * a.n_kv;
   const int cap = a.max_blocks * a.page;
@@ -710,7 +713,7 @@ __global__ __launch_bounds__(kAppendThreads) void chunk_plan(ChunkArgs a) {
     s_fail = 0;
     *a.flag = 0;
   }
-  for (int b = threadIdx.x; b < a.B; b += kAppendThreads) {
+  for (int b = threadIdx.x; b < a.B; b += NTH) {
     s_first[b] = -1;
     s_last[b] = -1;
     s_alloc[b] = 0x7fffffff;
@@ -718,7 +721,7 @@ __global__ __launch_bounds__(kAppendThreads) void chunk_plan(ChunkArgs a) {
   __syncthreads();
   // blocks below the largest n / page of a sequence's heads hold resident slots, so they are allocated; its new
   // slots reach block (largest n + T - 1) / page
-  for (int unit = threadIdx.x; unit < units; unit += kAppendThreads) {
+  for (int unit = threadIdx.x; unit < units; unit += NTH) {
     const int n = a.n_slots[unit], b = unit / a.n_kv;
     const int tb = chunk_count(a, b);
     if (tb < 0 || n < 0 || n + tb > cap) {
@@ -733,7 +736,7 @@ __global__ __launch_bounds__(kAppendThreads) void chunk_plan(ChunkArgs a) {
   // the first unallocated table entry in each sequence's window [first, last] (allocated entries form a
   // prefix), over all (sequence, entry) pairs at once; a window spans at most `span` entries
   const int span = (a.T + a.page - 1) / a.page + 1;
-  for (int x = threadIdx.x; x < a.B * span; x += kAppendThreads) {
+  for (int x = threadIdx.x; x < a.B * span; x += NTH) {
     const int b = x / span, j = s_first[b] + x % span;
     if (s_first[b] < 0 || j > s_last[b]) continue;
     const int cur = a.bt[(int64_t)b * a.max_blocks + j];
@@ -741,7 +744,7 @@ __global__ __launch_bounds__(kAppendThreads) void chunk_plan(ChunkArgs a) {
     if (cur < 0) atomicMin(&s_alloc[b], j);
   }
   __syncthreads();
-  for (int b = threadIdx.x; b < a.B; b += kAppendThreads) {
+  for (int b = threadIdx.x; b < a.B; b += NTH) {
     const int l = s_last[b], al = s_alloc[b];
     s_need[b] = (l >= 0 && al <= l) ? l - al + 1 : 0;
   }
@@ -753,11 +756,11 @@ __global__ __launch_bounds__(kAppendThreads) void chunk_plan(ChunkArgs a) {
   }
   // exclusive scan of the needs over sequences: sequence b pops free_blocks[top0 - 1 - (s_before[b] + i)]
   int carry = 0;
-  for (int base = 0; base < a.B; base += kAppendThreads) {
+  for (int base = 0; base < a.B; base += NTH) {
     const int b = base + threadIdx.x;
     const int v = b < a.B ? s_need[b] : 0;
     int total;
-    const int before = block_exscan<kAppendThreads>(v, s_wsum, total);
+    const int before = block_exscan<NTH>(v, s_wsum, total);
     if (b < a.B) s_before[b] = carry + before;
     carry += total;
   }
@@ -767,10 +770,10 @@ __global__ __launch_bounds__(kAppendThreads) void chunk_plan(ChunkArgs a) {
     if (threadIdx.x == 0) raise(a.status, (s_fail & 2) ? SE_DEV_INDEX : SE_DEV_CAPACITY);
     return;  // all or nothing: nothing was written
   }
-  for (int b = threadIdx.x; b < a.B; b += kAppendThreads)
+  for (int b = threadIdx.x; b < a.B; b += NTH)
     for (int i = 0; i < s_need[b]; ++i)
       a.bt[(int64_t)b * a.max_blocks + s_alloc[b] + i] = a.free_blocks[top0 - 1 - (s_before[b] + i)];
-  for (int unit = threadIdx.x; unit < units; unit += kAppendThreads) {
+  for (int unit = threadIdx.x; unit < units; unit += NTH) {
     const int tb = chunk_count(a, unit / a.n_kv);
     a.n_slots[unit] += tb;
     a.ctx[unit] += tb;
@@ -945,7 +948,10 @@ extern "C" int32_t se_cache_append(se_cache_t *c, const void *k_new, const void 
   a.row_bytes = row_bytes;
   a.dst_row = (int32_t *)ws;
   hipStream_t st = (hipStream_t)stream;
-  hipLaunchKernelGGL(se::append_plan, dim3(1), dim3(se::kAppendThreads), 0, st, a);
+  if (c->B * c->n_kv <= se::kAppendThreadsSmall)
+    hipLaunchKernelGGL(se::append_plan<se::kAppendThreadsSmall>, dim3(1), dim3(se::kAppendThreadsSmall), 0, st, a);
+  else
+    hipLaunchKernelGGL(se::append_plan<se::kAppendThreads>, dim3(1), dim3(se::kAppendThreads), 0, st, a);
   const int pieces = c->B * c->n_kv * (row_bytes / 16);
   hipLaunchKernelGGL(se::append_copy, dim3((pieces + se::kCopyThreads - 1) / se::kCopyThreads), dim3(se::kCopyThreads),
                      0, st, a);
@@ -993,7 +999,10 @@ extern "C" int32_t se_cache_append_chunk(se_cache_t *c, const void *k_new, const
   a.row_bytes = row_bytes;
   a.T = T;
   hipStream_t st = (hipStream_t)stream;
-  hipLaunchKernelGGL(se::chunk_plan, dim3(1), dim3(se::kAppendThreads), 0, st, a);
+  if (c->B * c->n_kv <= se::kAppendThreadsSmall)
+    hipLaunchKernelGGL(se::chunk_plan<se::kAppendThreadsSmall>, dim3(1), dim3(se::kAppendThreadsSmall), 0, st, a);
+  else
+    hipLaunchKernelGGL(se::chunk_plan<se::kAppendThreads>, dim3(1), dim3(se::kAppendThreads), 0, st, a);
   const int rows = se::kChunkThreads / (row_bytes / 16);
   hipLaunchKernelGGL(se::chunk_write, dim3((T + rows - 1) / rows, c->B * c->n_kv), dim3(se::kChunkThreads), 0, st, a);
   return se_host::launch_status();
