@@ -650,6 +650,9 @@ __global__ __launch_bounds__(NTH) void append_plan(AppendArgs a) {
     if (s_lb[b] >= 0) a.bt[(int64_t)b * a.max_blocks + s_lb[b]] = s_pop[b];
   __syncthreads();
   if (threadIdx.x == 0) *a.free_top = top0 - carry;
+  // with few units (the 256-thread plan) the rows are copied here as well, with no second launch
+  constexpr bool kCopy = NTH == kAppendThreadsSmall;
+  __shared__ int s_dst[kCopy ? kAppendThreadsSmall : 1];
   for (int unit = threadIdx.x; unit < units; unit += NTH) {
     int b = unit / a.n_kv;
     int slot = s_slot[unit];
@@ -659,7 +662,20 @@ __global__ __launch_bounds__(NTH) void append_plan(AppendArgs a) {
     a.ctx[unit] += 1;
     if (a.cum) a.cum[(int64_t)unit * cap + slot] = 0.f;
     const int blk = a.bt[(int64_t)b * a.max_blocks + slot / a.page];
-    a.dst_row[unit] = (blk * a.n_kv + unit % a.n_kv) * a.page + slot % a.page;
+    const int row = (blk * a.n_kv + unit % a.n_kv) * a.page + slot % a.page;
+    a.dst_row[unit] = row;
+    if constexpr (kCopy) s_dst[unit] = row;
+  }
+  if constexpr (kCopy) {
+    __syncthreads();
+    const int cpr = a.row_bytes / 16;
+    for (int x = threadIdx.x; x < units * cpr; x += NTH) {
+      const int unit = x / cpr, ch = x % cpr;
+      const int64_t src = (int64_t)unit * a.row_bytes + ch * 16, dst = (int64_t)s_dst[unit] * a.row_bytes + ch * 16;
+      const u32x4 kr = ld16_stream(a.k_new + src), vr = ld16_stream(a.v_new + src);
+      st16_stream(a.k + dst, kr);
+      st16_stream(a.v + dst, vr);
+    }
   }
 }
 
@@ -952,9 +968,11 @@ extern "C" int32_t se_cache_append(se_cache_t *c, const void *k_new, const void 
     hipLaunchKernelGGL(se::append_plan<se::kAppendThreadsSmall>, dim3(1), dim3(se::kAppendThreadsSmall), 0, st, a);
   else
     hipLaunchKernelGGL(se::append_plan<se::kAppendThreads>, dim3(1), dim3(se::kAppendThreads), 0, st, a);
-  const int pieces = c->B * c->n_kv * (row_bytes / 16);
-  hipLaunchKernelGGL(se::append_copy, dim3((pieces + se::kCopyThreads - 1) / se::kCopyThreads), dim3(se::kCopyThreads),
-                     0, st, a);
+  if (c->B * c->n_kv > se::kAppendThreadsSmall) {  // the small plan copies the rows itself
+    const int pieces = c->B * c->n_kv * (row_bytes / 16);
+    hipLaunchKernelGGL(se::append_copy, dim3((pieces + se::kCopyThreads - 1) / se::kCopyThreads),
+                       dim3(se::kCopyThreads), 0, st, a);
+  }
   return se_host::launch_status();
 }
 
